@@ -1,0 +1,305 @@
+"""Decode-step benchmark of the low-bit KV cache on one MI355X.
+
+A step is one pass of the whole hot path over one batch: one decode-attention
+step over the packed cache + fp16 windows (split-K kernel + log-sum-exp
+merge), then the append-group quantize+pack of the full fp16 residual group
+(the cache's streaming update).  Inputs are seeded synthetic tensors already
+resident in HBM.  To measure HBM rather than the 256 MB Infinity Cache, the
+steps rotate over several independent copies of the packed cache (total well
+above the cache size).
+
+Prints one JSON line:  python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, vendor figure
+MALL_BYTES = 256 << 20       # MI355X Infinity Cache
+DEFAULT_WORKLOAD = "llama3_8b_t32k_2bit"
+
+
+# ----------------------------------------------------------------------------
+# algorithmic bytes (what the method itself must move)
+# ----------------------------------------------------------------------------
+
+def decode_bytes(w) -> int:
+    """Bytes one decode step must read/write: packed codes, fp16 scale+min per
+    group, Kitty high words + index, the fp16 sink/residual windows, q (fp16)
+    and the output (fp32).  Split-K partials are not counted."""
+    T, D, G, b = w.T, w.D, w.G, w.bits
+    per_head = (T * D * b // 8            # key codes
+                + (T // G) * D * 4        # key scale + min (fp16 each)
+                + T * D * b // 8          # value codes
+                + T * (D // G) * 4        # value scale + min
+                + (T * w.n_boost * 2 // 8 + (T // G) * D if w.n_boost else 0)  # Kitty
+                + (w.S + w.R) * D * 4)    # fp16 K and V windows
+    return w.heads * per_head + w.B * w.H_q * D * (2 + 4)
+
+
+def append_bytes(w) -> int:
+    """Bytes of the append-group quantize: read one fp16 group of K and V, write
+    its codes and metadata."""
+    G, D, b = w.G, w.D, w.bits
+    per_head = (2 * G * D * 2 + 2 * G * D * b // 8 + D * 4 + G * (D // G) * 4
+                + (G * w.n_boost * 2 // 8 + D if w.n_boost else 0))
+    return w.heads * per_head
+
+
+def avg_bits_per_element(bits: int, G: int, T: int, R: int) -> float:
+    """Average stored bits per K/V element of a cache with T quantized tokens
+    (codes + fp16 scale and min per group of G) and R fp16 residual tokens."""
+    quant = bits + 32.0 / G
+    return (quant * T + 16.0 * R) / (T + R)
+
+
+# ----------------------------------------------------------------------------
+
+def _host_info():
+    cores = os.cpu_count() or 1
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = cores
+    model = platform.processor() or "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=5).stdout
+        for ln in out.splitlines():
+            if ln.startswith("Model name:"):
+                model = ln.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return min(cores, aff), model
+
+
+def build_caches(w, n_copies, kvq, synth, torch):
+    cfg = kvq.QCfg(bits=w.bits, group=w.G, head_dim=w.D, n_boost=w.n_boost)
+    t_cap = w.T + w.G
+    c0 = kvq.Cache.empty(cfg, w.heads, t_cap)
+    hb = max(1, min(w.heads, (1 << 30) // max(1, w.T * w.D * 4)))  # ~1 GiB of source per batch
+    for h0 in range(0, w.heads, hb):
+        n = min(hb, w.heads - h0)
+        ks, vs = zip(*[synth.head_kv(w, h, "cuda") for h in range(h0, h0 + n)])
+        k, v = torch.stack(ks), torch.stack(vs)
+        kvq.kvq_quantize_pack(cfg, c0.heads_view(h0, n), 1, n, k, v, 0, w.T // w.G)
+        del k, v, ks, vs
+    torch.cuda.synchronize()
+    copies = [c0]
+    for _ in range(n_copies - 1):
+        copies.append(kvq.Cache(cfg, t_cap, w.heads,
+                                **{f: (None if getattr(c0, f) is None else getattr(c0, f).clone())
+                                   for f in kvq.Cache.FIELDS}))
+    torch.cuda.synchronize()
+    return cfg, copies
+
+
+def cpu_baseline(w, max_heads, threads):
+    """Time the oracle (as it stands) on a bounded sample of heads: one decode
+    step plus the append-group quantize of those heads; scale to the whole
+    workload."""
+    import numpy as np
+    import oracle
+    import synth
+
+    heads = list(range(min(max_heads, w.heads)))
+    heads = heads[: (len(heads) // w.H_kv) * w.H_kv] or heads[:1]
+    B = max(1, len(heads) // w.H_kv)
+    H_kv = min(w.H_kv, len(heads))
+    oc = oracle.empty_cache(w.bits, w.G, w.D, w.n_boost, w.T + w.G, len(heads))
+    ks, vs, kr, vr, kS, vS = [], [], [], [], [], []
+    for h in heads:
+        k, v = synth.head_kv(w, h, "cpu")
+        a, b, c, d = synth.head_windows(w, h, "cpu")
+        ks.append(synth.as_bits(k)), vs.append(synth.as_bits(v))
+        kS.append(synth.as_bits(a)), vS.append(synth.as_bits(b))
+        kr.append(synth.as_bits(c)), vr.append(synth.as_bits(d))
+    k_src, v_src = np.stack(ks), np.stack(vs)
+    del ks, vs
+    oracle.quantize_pack(oc, k_src, v_src, 0, w.T // w.G, n_threads=threads)
+    del k_src, v_src
+    q = synth.as_bits(synth.query(w, "cpu"))[:B, : H_kv * w.gqa]
+    kS, vS, kr, vr = (np.stack(x) for x in (kS, vS, kr, vr))
+    t0 = time.perf_counter()
+    oracle.decode_attention(oc, B, H_kv * w.gqa, H_kv, q, w.T, k_sink=kS if w.S else None,
+                            v_sink=vS if w.S else None, n_sink=w.S, k_res=kr, v_res=vr,
+                            n_res=w.R, n_threads=threads)
+    if w.R >= w.G:
+        oracle.quantize_pack(oc, kr, vr, w.T // w.G, 1, n_threads=threads)
+    dt = time.perf_counter() - t0
+    scale = w.heads / len(heads)
+    return {"value": dt * scale * 1e6, "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"{len(heads)} of {w.heads} kv heads (all their query heads), one "
+                      f"decode step + append quantize, {dt:.2f} s wall on {threads} threads, "
+                      f"scaled x{scale:g}"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0 = auto)")
+    ap.add_argument("--n-chunks", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=64)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (each box has "
+              "one GPU and the path is built for a single device).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import bit_kv_cache_amd as kvq
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    cache_bytes_one = None
+
+    # packed caches (rotated) -----------------------------------------------------
+    probe_cfg = kvq.QCfg(bits=w.bits, group=w.G, head_dim=w.D, n_boost=w.n_boost)
+    one = kvq.Cache.empty(probe_cfg, 1, w.T + w.G, device="meta").nbytes() * w.heads
+    cache_bytes_one = one
+    n_copies = args.copies or max(2, math.ceil(3 * MALL_BYTES / one) + 1)
+    n_copies = min(n_copies, 16)
+    cfg, copies = build_caches(w, n_copies, kvq, synth, torch)
+
+    # windows and query -------------------------------------------------------------
+    wins = [synth.head_windows(w, h, "cuda") for h in range(w.heads)]
+    k_sink = torch.stack([x[0] for x in wins])
+    v_sink = torch.stack([x[1] for x in wins])
+    k_res = torch.stack([x[2] for x in wins])
+    v_res = torch.stack([x[3] for x in wins])
+    del wins
+    q = synth.query(w, "cuda")
+    n_chunks, ws_bytes = kvq.kvq_decode_plan(cfg, w.B, w.H_q, w.H_kv, w.T,
+                                             args.n_chunks or w.min_chunks)
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    # raw ctypes arguments, built once (keeps host launch overhead low)
+    lib = kvq._lib
+    c_cfg = cfg.c()
+    c_caches = [c.c() for c in copies]
+    sink = kvq.window(k_sink, v_sink, w.S)
+    res = kvq.window(k_res, v_res, w.R)
+    sink_p = ctypes.byref(sink) if sink is not None else None
+    res_p = ctypes.byref(res) if res is not None else None
+    append = w.R >= w.G
+    g_app = w.T // w.G
+
+    def decode(i):
+        st = lib.kvq_decode_attention(ctypes.byref(c_cfg), ctypes.byref(c_caches[i % n_copies]),
+                                      w.B, w.H_q, w.H_kv, q.data_ptr(), w.T, sink_p, res_p,
+                                      ctypes.c_float(0.0), n_chunks, ws.data_ptr(), ws_bytes,
+                                      out.data_ptr(), sp)
+        if st:
+            raise kvq.KvqError(st, "kvq_decode_attention")
+
+    def quant(i):
+        if not append:
+            return
+        st = lib.kvq_quantize_pack(ctypes.byref(c_cfg), ctypes.byref(c_caches[i % n_copies]),
+                                   1, w.heads, k_res.data_ptr(), v_res.data_ptr(),
+                                   k_res.stride(0), g_app, 1, sp)
+        if st:
+            raise kvq.KvqError(st, "kvq_quantize_pack")
+
+    for i in range(args.warmup):
+        decode(i)
+        quant(i)
+    torch.cuda.synchronize()
+
+    # timed region: whole steps -------------------------------------------------------
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        decode(i)
+        quant(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations on the launch stream (HIP events around each call) ---------
+    n_k = min(args.steps, 100)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
+    torch.cuda.synchronize()
+    for i in range(n_k):
+        ev[i][0].record(stream)
+        decode(i)
+        ev[i][1].record(stream)
+        quant(i)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    app_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    dec_avg = sum(dec_ms) / n_k
+    app_avg = sum(app_ms) / n_k
+
+    alg = decode_bytes(w)
+    achieved = alg / (dec_avg * 1e-3) / 1e9
+    step_bytes = alg + (append_bytes(w) if append else 0)
+    eff_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    result = {
+        "metric": "decode-attn us/step + effective HBM GB/s (% of peak), 2-bit, Llama-3-8B "
+                  "shape 32K" if w.name == DEFAULT_WORKLOAD else f"decode-attn us/step ({w.name})",
+        "value": round(ms_per_step * 1e3, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"u{w.bits} codes, fp32 math",
+        "data": "synthetic (seeded; K outlier channels, see synth/)",
+        "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "D": w.D,
+                   "T": w.T, "R": w.R, "S": w.S, "bits": w.bits, "G": w.G,
+                   "n_boost": w.n_boost, "n_chunks": n_chunks, "cache_copies": n_copies,
+                   "cache_bytes_per_copy": cache_bytes_one, "step": "decode + append-group "
+                   "quantize" if append else "decode"},
+        "effective_GBps": round(eff_gbps, 1),
+        "effective_frac_of_peak": round(eff_gbps / HBM_PEAK_GBPS, 4),
+        "decode_us": {"avg": round(dec_avg * 1e3, 3), "p10": round(dec_ms[n_k // 10] * 1e3, 3),
+                      "p90": round(dec_ms[(9 * n_k) // 10] * 1e3, 3)},
+        "append_quant_us": round(app_avg * 1e3, 3) if append else None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "kvq_decode_attention (split-K + merge)",
+                     "algorithmic_bytes": alg},
+    }
+    if not args.no_cpu_baseline:
+        cores, model = _host_info()
+        cb = cpu_baseline(w, args.cpu_heads, cores)
+        cb["cpu_model"] = model
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

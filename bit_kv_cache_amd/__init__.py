@@ -1,0 +1,227 @@
+"""Python binding of libkvq: low-bit KV cache + decode attention on MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libkvq.so`` (C ABI in ``include/kvq.h``).  torch provides device memory and
+streams.  The functions keep the C names (``kvq_quantize_pack``,
+``kvq_decode_attention``, ``kvq_dequantize``, ...) and take torch tensors;
+a non-OK status raises ``KvqError``.  If the library is not built, importing
+this package raises immediately -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libkvq.so is not built ({LIB_PATH}); run `python -m bit_kv_cache_amd._build` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_ALIGN, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = (
+    0, -1, -2, -3, -4, -5)
+
+EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
+            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_dequantize")
+
+
+class kvq_qcfg(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("n_boost", ctypes.c_int32)]
+
+
+class kvq_cache(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("k_min", ctypes.c_void_p), ("k_hi", ctypes.c_void_p),
+                ("k_bidx", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("v_min", ctypes.c_void_p),
+                ("t_cap", ctypes.c_int64)]
+
+
+class kvq_window(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("n", ctypes.c_int32), ("cap", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_lib.kvq_status_string.argtypes = [ctypes.c_int]
+_lib.kvq_status_string.restype = ctypes.c_char_p
+_lib.kvq_quantize_pack.argtypes = [_P, _P, _i32, _i32, _P, _P, _i64, _i64, _i64, _P]
+_lib.kvq_quantize_pack.restype = ctypes.c_int
+_lib.kvq_decode_plan.argtypes = [_P, _i32, _i32, _i32, _i64, _i32, _P, _P]
+_lib.kvq_decode_plan.restype = ctypes.c_int
+_lib.kvq_decode_workspace_bytes.argtypes = [_P, _i32, _i32, _i32, _i64, _i32]
+_lib.kvq_decode_workspace_bytes.restype = _sz
+_lib.kvq_decode_attention.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32,
+                                      _P, _sz, _P, _P]
+_lib.kvq_decode_attention.restype = ctypes.c_int
+_lib.kvq_dequantize.argtypes = [_P, _P, _i32, _i32, _i64, _i64, _P, _P, _P]
+_lib.kvq_dequantize.restype = ctypes.c_int
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kvq_status_string(status)}")
+
+
+def kvq_status_string(status: int) -> str:
+    return _lib.kvq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != KVQ_OK:
+        raise KvqError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return stream
+
+
+# ----------------------------------------------------------------- containers
+
+@dataclass
+class QCfg:
+    bits: int = 2
+    group: int = 128
+    head_dim: int = 128
+    n_boost: int = 0
+
+    def c(self) -> kvq_qcfg:
+        return kvq_qcfg(self.bits, self.group, self.head_dim, self.n_boost)
+
+
+@dataclass
+class Cache:
+    """Packed cache tensors (layout in include/kvq.h).  ``heads`` = B*H_kv."""
+    cfg: QCfg
+    t_cap: int
+    heads: int
+    k_codes: torch.Tensor
+    k_scale: torch.Tensor
+    k_min: torch.Tensor
+    k_hi: torch.Tensor | None
+    k_bidx: torch.Tensor | None
+    v_codes: torch.Tensor
+    v_scale: torch.Tensor
+    v_min: torch.Tensor
+
+    FIELDS = ("k_codes", "k_scale", "k_min", "k_hi", "k_bidx", "v_codes", "v_scale", "v_min")
+
+    @staticmethod
+    def empty(cfg: QCfg, heads: int, t_cap: int, device="cuda") -> "Cache":
+        fpi = 32 // cfg.bits
+        D, G, T, H = cfg.head_dim, cfg.group, t_cap, heads
+        z = dict(device=device)
+        return Cache(
+            cfg, t_cap, heads,
+            k_codes=torch.zeros((H, T, D // fpi), dtype=torch.int32, **z),
+            k_scale=torch.zeros((H, T // G, D), dtype=torch.int16, **z),
+            k_min=torch.zeros((H, T // G, D), dtype=torch.int16, **z),
+            k_hi=torch.zeros((H, T, cfg.n_boost // 16), dtype=torch.int32, **z)
+            if cfg.n_boost else None,
+            k_bidx=torch.zeros((H, T // G, D), dtype=torch.uint8, **z) if cfg.n_boost else None,
+            v_codes=torch.zeros((H, T // fpi, D), dtype=torch.int32, **z),
+            v_scale=torch.zeros((H, T, D // G), dtype=torch.int16, **z),
+            v_min=torch.zeros((H, T, D // G), dtype=torch.int16, **z),
+        )
+
+    def heads_view(self, h0: int, n: int) -> "Cache":
+        """The cache restricted to heads [h0, h0+n) (same storage)."""
+        sl = {f: (None if getattr(self, f) is None else getattr(self, f)[h0:h0 + n])
+              for f in self.FIELDS}
+        return Cache(self.cfg, self.t_cap, n, **sl)
+
+    def nbytes(self) -> int:
+        return sum(getattr(self, f).numel() * getattr(self, f).element_size()
+                   for f in self.FIELDS if getattr(self, f) is not None)
+
+    def c(self) -> kvq_cache:
+        return kvq_cache(*[_ptr(getattr(self, f)) for f in self.FIELDS], self.t_cap)
+
+
+def window(k: torch.Tensor | None, v: torch.Tensor | None, n: int) -> kvq_window | None:
+    """fp16 window ``[heads][cap][D]`` with the first ``n`` rows valid."""
+    if k is None or n == 0:
+        return None
+    return kvq_window(_ptr(k), _ptr(v), int(n), int(k.shape[1]))
+
+
+# ----------------------------------------------------------------- entry points
+
+def kvq_quantize_pack(cfg: QCfg, cache: Cache, B: int, H_kv: int, k_src: torch.Tensor,
+                      v_src: torch.Tensor, first_group: int, n_groups: int,
+                      src_head_stride: int | None = None, stream=None) -> None:
+    """fp16 sources ``[B*H_kv][>= n_groups*G][D]`` -> groups [first, first+n)."""
+    if src_head_stride is None:
+        src_head_stride = k_src.stride(0)
+    c_cfg, c_cache = cfg.c(), cache.c()
+    _check(_lib.kvq_quantize_pack(ctypes.byref(c_cfg), ctypes.byref(c_cache), B, H_kv,
+                                  _ptr(k_src), _ptr(v_src), src_head_stride, first_group,
+                                  n_groups, _stream(stream)), "kvq_quantize_pack")
+
+
+def kvq_decode_plan(cfg: QCfg, B: int, H_q: int, H_kv: int, n_quant_tokens: int,
+                    n_chunks: int = 0):
+    """(chunks per head, workspace bytes)."""
+    nc, ws = ctypes.c_int32(0), ctypes.c_size_t(0)
+    c_cfg = cfg.c()
+    _check(_lib.kvq_decode_plan(ctypes.byref(c_cfg), B, H_q, H_kv, n_quant_tokens, n_chunks,
+                                ctypes.byref(nc), ctypes.byref(ws)), "kvq_decode_plan")
+    return nc.value, ws.value
+
+
+def kvq_decode_workspace_bytes(cfg: QCfg, B: int, H_q: int, H_kv: int, n_quant_tokens: int,
+                               n_chunks: int = 0) -> int:
+    c_cfg = cfg.c()
+    return int(_lib.kvq_decode_workspace_bytes(ctypes.byref(c_cfg), B, H_q, H_kv,
+                                               n_quant_tokens, n_chunks))
+
+
+def kvq_decode_attention(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int,
+                         q: torch.Tensor, n_quant_tokens: int, sink: kvq_window | None,
+                         res: kvq_window | None, out: torch.Tensor, workspace: torch.Tensor,
+                         sm_scale: float = 0.0, n_chunks: int = 0, stream=None) -> None:
+    c_cfg, c_cache = cfg.c(), cache.c()
+    _check(_lib.kvq_decode_attention(
+        ctypes.byref(c_cfg), ctypes.byref(c_cache), B, H_q, H_kv, _ptr(q), n_quant_tokens,
+        ctypes.byref(sink) if sink is not None else None,
+        ctypes.byref(res) if res is not None else None, float(sm_scale), int(n_chunks),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_dequantize(cfg: QCfg, cache: Cache, B: int, H_kv: int, first_group: int,
+                   n_groups: int, k_out: torch.Tensor, v_out: torch.Tensor,
+                   stream=None) -> None:
+    c_cfg, c_cache = cfg.c(), cache.c()
+    _check(_lib.kvq_dequantize(ctypes.byref(c_cfg), ctypes.byref(c_cache), B, H_kv,
+                               first_group, n_groups, _ptr(k_out), _ptr(v_out),
+                               _stream(stream)), "kvq_dequantize")
+
+
+def raw_call(name: str, *args) -> int:
+    """Call a C entry point with raw ctypes arguments (status returned, not
+    raised).  For tests of the argument checks."""
+    return getattr(_lib, name)(*args)

@@ -1,0 +1,330 @@
+// Split-K decode attention over the packed low-bit cache + fp16 windows,
+// and the log-sum-exp merge of the partial results.
+//
+// Each block owns one (batch, kv head) and one "part": a chunk of quantized
+// groups, or (last part) the fp16 sink + residual windows.  It keeps, for
+// every query head of the kv head's GQA group, the online-softmax state
+// (running max m, running sum l, accumulator acc[D]) in the log2 domain and
+// writes it to the workspace; the merge kernel combines the parts:
+//   M = max_p m_p,  O = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+//
+// This kernel dequantizes in registers (code*scale + min in fp32, the same
+// value the cache defines, KIVI page Step 4) and forms q.k and p.v on the
+// vector ALUs.
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBlockTok = 128;   // tokens per processing block
+constexpr float kNegInf = -__builtin_inff();
+
+struct SoftmaxState {
+  float m[kMaxGqa];
+  float l[kMaxGqa];
+};
+
+template <int GQA>
+struct Lds {
+  float q[GQA][kD];                      // query * sm * log2(e)
+  float ks[kBlockTok / 32][kD];          // key scale / min per (group in block, channel)
+  float km[kBlockTok / 32][kD];
+  int kb[kBlockTok / 32][kD];            // Kitty boosted row per (group in block, channel)
+  float vs[kBlockTok * 4];               // value scale / min per (token, channel group)
+  float vm[kBlockTok * 4];
+  float part[2][GQA][kBlockTok];         // q.k partial sums of the two channel halves
+  float p[GQA][kBlockTok];               // logits, then probabilities
+  float m[GQA], l[GQA], alpha[GQA];
+  float acc[GQA][kD];                    // final combine of the two token halves
+};
+
+// ------------------------------------------------------------------ softmax
+// Block-wide online softmax update over the nt logits in lds.p.
+template <int GQA>
+__device__ void softmax_block(Lds<GQA>& s, int nt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int h = wave; h < GQA; h += kThreads / 64) {
+    float mx = kNegInf;
+    for (int t = lane; t < nt; t += 64) mx = fmaxf(mx, s.p[h][t]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float m_old = s.m[h];
+    const float m_new = fmaxf(m_old, mx);
+    float sum = 0.f;
+    for (int t = lane; t < nt; t += 64) {
+      const float e = exp2f(s.p[h][t] - m_new);
+      s.p[h][t] = e;
+      sum += e;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0) {
+      const float alpha = exp2f(m_old - m_new);   // 0 when m_old == -inf
+      s.alpha[h] = alpha;
+      s.l[h] = s.l[h] * alpha + sum;
+      s.m[h] = m_new;
+    }
+  }
+}
+
+// --------------------------------------------------------- quantized block
+// Tokens [t0, t0+nt) of head `head`, nt a multiple of G, nt <= kBlockTok.
+template <int BITS, int G, int GQA>
+__device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int64_t t0, int nt,
+                            float (&acc)[GQA]) {
+  constexpr int FPI = 32 / BITS;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  constexpr int WPT = kD / FPI;
+  constexpr int NCG = kD / G;
+  const int tid = threadIdx.x;
+  const int64_t g0 = t0 / G;
+  const int ng = nt / G;
+
+  // stage per-group key scale/min (and Kitty rows), per-token value scale/min
+  for (int i = tid; i < ng * kD; i += kThreads) {
+    const int gl = i / kD, d = i % kD;
+    const int64_t off = (head * (a.c.t_cap / G) + g0 + gl) * kD + d;
+    s.ks[gl][d] = h2f(a.c.k_scale[off]);
+    s.km[gl][d] = h2f(a.c.k_min[off]);
+    if (a.n_boost > 0) s.kb[gl][d] = a.c.k_bidx[off];
+  }
+  for (int i = tid; i < nt * NCG; i += kThreads) {
+    const int64_t off = (head * a.c.t_cap + t0) * NCG + i;
+    s.vs[i] = h2f(a.c.v_scale[off]);
+    s.vm[i] = h2f(a.c.v_min[off]);
+  }
+  __syncthreads();
+
+  // q.k: thread (token t, channel half)
+  {
+    const int t = tid & (kBlockTok - 1), half = tid >> 7;
+    if (t < nt) {
+      const int gl = t / G;
+      const uint32_t* kw = a.c.k_codes + (head * a.c.t_cap + t0 + t) * WPT + half * (WPT / 2);
+      uint32_t hw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (a.n_boost > 0) {
+        const uint32_t* hp = a.c.k_hi + (head * a.c.t_cap + t0 + t) * (a.n_boost / 16);
+        for (int w = 0; w < a.n_boost / 16; ++w) hw[w] = hp[w];
+      }
+      float dot[GQA];
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) dot[h] = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPT / 2; ++w) {
+        const uint32_t word = kw[w];
+#pragma unroll
+        for (int j = 0; j < FPI; ++j) {
+          const int c = half * (kD / 2) + w * FPI + j;
+          uint32_t q = (word >> (BITS * j)) & MASK;
+          if (a.n_boost > 0) {
+            const int r = s.kb[gl][c];
+            if (r < a.n_boost) q |= ((hw[r >> 4] >> (2 * (r & 15))) & 3u) << 2;
+          }
+          const float x = fmaf((float)q, s.ks[gl][c], s.km[gl][c]);
+#pragma unroll
+          for (int h = 0; h < GQA; ++h) dot[h] = fmaf(s.q[h][c], x, dot[h]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) s.part[half][h][t] = dot[h];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < GQA * nt; i += kThreads) {
+    const int h = i / nt, t = i % nt;
+    s.p[h][t] = s.part[0][h][t] + s.part[1][h][t];
+  }
+  __syncthreads();
+  softmax_block<GQA>(s, nt);
+  __syncthreads();
+
+  // p.v: thread (channel d, token half)
+  {
+    const int d = tid & (kD - 1), half = tid >> 7;
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) acc[h] *= s.alpha[h];
+    const int tb = half * (kBlockTok / 2);
+    const int te = min(nt, tb + kBlockTok / 2);
+    const uint32_t* vw = a.c.v_codes + (head * (a.c.t_cap / FPI)) * kD + d;
+    for (int tw = tb; tw < te; tw += FPI) {
+      const uint32_t word = vw[((t0 + tw) / FPI) * kD];
+#pragma unroll
+      for (int j = 0; j < FPI; ++j) {
+        const int t = tw + j;
+        const uint32_t q = (word >> (BITS * j)) & MASK;
+        const int pi = t * NCG + d / G;
+        const float x = fmaf((float)q, s.vs[pi], s.vm[pi]);
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) acc[h] = fmaf(s.p[h][t], x, acc[h]);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------ fp16 window
+// Window tokens [u0, u0+nt) of the concatenation sink | residual.
+template <int GQA>
+__device__ void window_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int u0, int nt,
+                             float (&acc)[GQA]) {
+  const int tid = threadIdx.x;
+  auto krow = [&](int u) -> const uint16_t* {
+    return u < a.n_sink ? a.k_sink + (head * a.sink_cap + u) * kD
+                        : a.k_res + (head * a.res_cap + (u - a.n_sink)) * kD;
+  };
+  auto vrow = [&](int u) -> const uint16_t* {
+    return u < a.n_sink ? a.v_sink + (head * a.sink_cap + u) * kD
+                        : a.v_res + (head * a.res_cap + (u - a.n_sink)) * kD;
+  };
+  {
+    const int t = tid & (kBlockTok - 1), half = tid >> 7;
+    if (t < nt) {
+      const uint16_t* k = krow(u0 + t) + half * (kD / 2);
+      float dot[GQA];
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) dot[h] = 0.f;
+      for (int c = 0; c < kD / 2; ++c) {
+        const float x = h2f(k[c]);
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) dot[h] = fmaf(s.q[h][half * (kD / 2) + c], x, dot[h]);
+      }
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) s.part[half][h][t] = dot[h];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < GQA * nt; i += kThreads) {
+    const int h = i / nt, t = i % nt;
+    s.p[h][t] = s.part[0][h][t] + s.part[1][h][t];
+  }
+  __syncthreads();
+  softmax_block<GQA>(s, nt);
+  __syncthreads();
+  {
+    const int d = tid & (kD - 1), half = tid >> 7;
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) acc[h] *= s.alpha[h];
+    const int tb = half * (kBlockTok / 2);
+    const int te = min(nt, tb + kBlockTok / 2);
+    for (int t = tb; t < te; ++t) {
+      const float x = h2f(vrow(u0 + t)[d]);
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) acc[h] = fmaf(s.p[h][t], x, acc[h]);
+    }
+  }
+  __syncthreads();
+}
+
+// grid: (n_chunks + 1, B * H_kv); part n_chunks is the fp16 windows
+template <int BITS, int G, int GQA>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
+  __shared__ Lds<GQA> s;
+  const int tid = threadIdx.x;
+  const int part = blockIdx.x;
+  const int64_t head = blockIdx.y;
+  const int64_t b = head / a.H_kv, hk = head % a.H_kv;
+  const int n_parts = a.n_chunks + 1;
+
+  for (int i = tid; i < GQA * kD; i += kThreads) {
+    const int h = i / kD, d = i % kD;
+    s.q[h][d] = h2f(a.q[((b * a.H_q) + hk * GQA + h) * kD + d]) * a.qscale;
+  }
+  if (tid < GQA) {
+    s.m[tid] = kNegInf;
+    s.l[tid] = 0.f;
+  }
+  __syncthreads();
+
+  float acc[GQA];
+#pragma unroll
+  for (int h = 0; h < GQA; ++h) acc[h] = 0.f;
+
+  if (part < a.n_chunks) {
+    const int64_t gb = (int64_t)part * a.groups_per_chunk;
+    const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
+    for (int64_t g = gb; g < ge; g += kBlockTok / G) {
+      const int ng = (int)min<int64_t>(kBlockTok / G, ge - g);
+      quant_block<BITS, G, GQA>(a, s, head, g * G, ng * G, acc);
+    }
+  } else {
+    const int n_win = a.n_sink + a.n_res;
+    for (int u = 0; u < n_win; u += kBlockTok)
+      window_block<GQA>(a, s, head, u, min(kBlockTok, n_win - u), acc);
+  }
+
+  // combine the two token halves and write (m, l, acc)
+  const int d = tid & (kD - 1), half = tid >> 7;
+  if (half) {
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) s.acc[h][d] = acc[h];
+  }
+  __syncthreads();
+  if (!half) {
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) {
+      float* w = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + part) * (kD + 2);
+      w[2 + d] = acc[h] + s.acc[h][d];
+      if (d == 0) {
+        w[0] = s.m[h];
+        w[1] = s.l[h];
+      }
+    }
+  }
+}
+
+// grid: B * H_q blocks of kD threads
+__global__ __launch_bounds__(kD) void merge_kernel(DecodeArgs a) {
+  const int64_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const int n_parts = a.n_chunks + 1;
+  const float* w = a.ws + bh * n_parts * (kD + 2);
+  float M = kNegInf;
+  for (int p = 0; p < n_parts; ++p)
+    if (w[p * (kD + 2) + 1] > 0.f) M = fmaxf(M, w[p * (kD + 2)]);
+  float L = 0.f, o = 0.f;
+  for (int p = 0; p < n_parts; ++p) {
+    const float* wp = w + p * (kD + 2);
+    if (wp[1] > 0.f) {
+      const float f = exp2f(wp[0] - M);
+      L = fmaf(wp[1], f, L);
+      o = fmaf(wp[2 + d], f, o);
+    }
+  }
+  a.out[bh * kD + d] = (L > 0.f) ? o / L : 0.f;
+}
+
+template <int BITS, int G>
+hipError_t decode_bg(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.n_chunks + 1), (unsigned)(a.B * a.H_kv));
+  switch (a.gqa) {
+    case 1: decode_valu_kernel<BITS, G, 1><<<grid, kThreads, 0, st>>>(a); break;
+    case 2: decode_valu_kernel<BITS, G, 2><<<grid, kThreads, 0, st>>>(a); break;
+    case 4: decode_valu_kernel<BITS, G, 4><<<grid, kThreads, 0, st>>>(a); break;
+    case 8: decode_valu_kernel<BITS, G, 8><<<grid, kThreads, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  merge_kernel<<<(unsigned)(a.B * a.H_q), kD, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t decode_bits(int group, const DecodeArgs& a, hipStream_t st) {
+  switch (group) {
+    case 32: return decode_bg<BITS, 32>(a, st);
+    case 64: return decode_bg<BITS, 64>(a, st);
+    case 128: return decode_bg<BITS, 128>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(int bits, int group, const DecodeArgs& a, hipStream_t st) {
+  return bits == 2 ? decode_bits<2>(group, a, st) : decode_bits<4>(group, a, st);
+}
+
+}  // namespace kvq

@@ -1,0 +1,209 @@
+// Host side of the libkvq C ABI: argument validation (pure host code, run
+// before anything touches the GPU), split planning and kernel launch.
+
+#include <math.h>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+using kvq::kD;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every entry point.
+kvq_status check_cfg(const kvq_qcfg* cfg) {
+  if (!cfg) return KVQ_ERR_ARG;
+  if (cfg->bits == 8 || (cfg->head_dim > 0 && cfg->head_dim != kD))
+    return KVQ_ERR_UNSUPPORTED;
+  if (cfg->bits != 2 && cfg->bits != 4) return KVQ_ERR_ARG;
+  if (cfg->head_dim != kD) return KVQ_ERR_ARG;
+  const int fpi = 32 / cfg->bits;
+  if (cfg->group <= 0 || cfg->group % fpi || kD % cfg->group) return KVQ_ERR_ARG;
+  if (cfg->group != 32 && cfg->group != 64 && cfg->group != 128) return KVQ_ERR_UNSUPPORTED;
+  if (cfg->n_boost < 0 || cfg->n_boost > kD || cfg->n_boost % 16) return KVQ_ERR_ARG;
+  if (cfg->n_boost > 0 && cfg->bits != 2) return KVQ_ERR_ARG;
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_qcfg* cfg, const kvq_cache* c) {
+  if (!c) return KVQ_ERR_ARG;
+  if (c->t_cap <= 0 || c->t_cap % cfg->group) return KVQ_ERR_ARG;
+  if (!c->k_codes || !c->k_scale || !c->k_min || !c->v_codes || !c->v_scale || !c->v_min)
+    return KVQ_ERR_ARG;
+  if (cfg->n_boost > 0 && (!c->k_hi || !c->k_bidx)) return KVQ_ERR_ARG;
+  if (!aligned16(c->k_codes) || !aligned16(c->k_scale) || !aligned16(c->k_min) ||
+      !aligned16(c->v_codes) || !aligned16(c->v_scale) || !aligned16(c->v_min))
+    return KVQ_ERR_ALIGN;
+  if (cfg->n_boost > 0 && (!aligned16(c->k_hi) || !aligned16(c->k_bidx))) return KVQ_ERR_ALIGN;
+  return KVQ_OK;
+}
+
+kvq::CacheArgs cache_args(const kvq_cache* c) {
+  return {reinterpret_cast<uint32_t*>(c->k_codes), c->k_scale, c->k_min,
+          reinterpret_cast<uint32_t*>(c->k_hi), c->k_bidx,
+          reinterpret_cast<uint32_t*>(c->v_codes), c->v_scale, c->v_min, c->t_cap};
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+// Chunks per head: enough blocks to give every compute unit several, each
+// chunk at least one group; an explicit request is honoured up to one chunk
+// per group.
+int32_t plan_chunks(int64_t heads, int64_t n_groups, int32_t req) {
+  if (n_groups <= 0) return 0;
+  int64_t n;
+  if (req > 0) {
+    n = req;
+  } else {
+    const int64_t target_blocks = 1024;  // 256 CUs x 4
+    n = (target_blocks + heads - 1) / heads;
+  }
+  if (n > n_groups) n = n_groups;
+  if (n < 1) n = 1;
+  return (int32_t)n;
+}
+
+kvq_status check_window(const kvq_window* w) {
+  if (!w) return KVQ_OK;
+  if (w->n < 0 || w->cap < 0 || w->n > w->cap) return KVQ_ERR_ARG;
+  if (w->n > 0 && (!w->k || !w->v)) return KVQ_ERR_ARG;
+  if (w->n > 0 && (!aligned16(w->k) || !aligned16(w->v))) return KVQ_ERR_ALIGN;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_ARG: return "KVQ_ERR_ARG: invalid argument";
+    case KVQ_ERR_ALIGN: return "KVQ_ERR_ALIGN: device pointer not 16-byte aligned";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: configuration not built";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE: workspace missing or too small";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP: kernel launch failed";
+  }
+  return "kvq: unknown status";
+}
+
+kvq_status kvq_quantize_pack(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                             int32_t H_kv, const uint16_t* k_src, const uint16_t* v_src,
+                             int64_t src_head_stride, int64_t first_group, int64_t n_groups,
+                             void* stream) {
+  kvq_status st = check_cfg(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if (B <= 0 || H_kv <= 0) return KVQ_ERR_ARG;
+  if (first_group < 0 || n_groups < 0) return KVQ_ERR_ARG;
+  const int64_t G = cfg->group;
+  if ((first_group + n_groups) * G > cache->t_cap) return KVQ_ERR_ARG;
+  if (n_groups == 0) return KVQ_OK;
+  if (!k_src || !v_src) return KVQ_ERR_ARG;
+  if (src_head_stride < n_groups * G * kD) return KVQ_ERR_ARG;
+  if (!aligned16(k_src) || !aligned16(v_src) || (src_head_stride * 2) % 16)
+    return KVQ_ERR_ALIGN;
+  const int64_t heads = (int64_t)B * H_kv;
+  if (heads * n_groups > 0x7FFFFFFF) return KVQ_ERR_ARG;
+  kvq::QuantArgs a{cache_args(cache), k_src,    v_src, src_head_stride, first_group,
+                   n_groups,          (int32_t)heads, cfg->n_boost};
+  return hip_status(
+      kvq::launch_quantize(cfg->bits, cfg->group, a, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t H_kv,
+                           int64_t n_quant_tokens, int32_t n_chunks_req, int32_t* n_chunks,
+                           size_t* ws_bytes) {
+  kvq_status st = check_cfg(cfg);
+  if (st != KVQ_OK) return st;
+  if (B <= 0 || H_kv <= 0 || H_q <= 0 || H_q % H_kv) return KVQ_ERR_ARG;
+  const int32_t gqa = H_q / H_kv;
+  if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KVQ_ERR_UNSUPPORTED;
+  if (n_quant_tokens < 0 || n_quant_tokens % cfg->group || n_chunks_req < 0)
+    return KVQ_ERR_ARG;
+  const int64_t heads = (int64_t)B * H_kv;
+  if (heads > 65535) return KVQ_ERR_ARG;  // one grid row per (batch, kv head)
+  const int32_t n = plan_chunks(heads, n_quant_tokens / cfg->group, n_chunks_req);
+  if (n_chunks) *n_chunks = n;
+  if (ws_bytes) *ws_bytes = (size_t)B * H_q * (size_t)(n + 1) * (kD + 2) * sizeof(float);
+  return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t H_kv,
+                                  int64_t n_quant_tokens, int32_t n_chunks_req) {
+  size_t ws = 0;
+  if (kvq_decode_plan(cfg, B, H_q, H_kv, n_quant_tokens, n_chunks_req, nullptr, &ws) != KVQ_OK)
+    return 0;
+  return ws;
+}
+
+kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                                int32_t H_q, int32_t H_kv, const uint16_t* q,
+                                int64_t n_quant_tokens, const kvq_window* sink,
+                                const kvq_window* res, float sm_scale, int32_t n_chunks,
+                                void* workspace, size_t ws_bytes, float* out, void* stream) {
+  int32_t nc = 0;
+  size_t need = 0;
+  kvq_status st = kvq_decode_plan(cfg, B, H_q, H_kv, n_quant_tokens, n_chunks, &nc, &need);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if (n_quant_tokens > cache->t_cap) return KVQ_ERR_ARG;
+  if ((st = check_window(sink)) != KVQ_OK) return st;
+  if ((st = check_window(res)) != KVQ_OK) return st;
+  if (!q || !out) return KVQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (!(sm_scale > 0.f)) sm_scale = 1.0f / sqrtf((float)kD);
+
+  kvq::DecodeArgs a{};
+  a.c = cache_args(cache);
+  a.q = q;
+  a.B = B;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.gqa = H_q / H_kv;
+  a.n_boost = cfg->n_boost;
+  a.n_groups = n_quant_tokens / cfg->group;
+  a.n_chunks = nc;
+  a.groups_per_chunk = nc > 0 ? (int32_t)((a.n_groups + nc - 1) / nc) : 0;
+  if (sink && sink->n > 0) {
+    a.k_sink = sink->k;
+    a.v_sink = sink->v;
+    a.n_sink = sink->n;
+    a.sink_cap = sink->cap;
+  }
+  if (res && res->n > 0) {
+    a.k_res = res->k;
+    a.v_res = res->v;
+    a.n_res = res->n;
+    a.res_cap = res->cap;
+  }
+  a.qscale = sm_scale * 1.4426950408889634f;
+  a.ws = static_cast<float*>(workspace);
+  a.out = out;
+  return hip_status(kvq::launch_decode(cfg->bits, cfg->group, a, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_dequantize(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_kv,
+                          int64_t first_group, int64_t n_groups, float* k_out, float* v_out,
+                          void* stream) {
+  kvq_status st = check_cfg(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
+  if (B <= 0 || H_kv <= 0 || first_group < 0 || n_groups < 0) return KVQ_ERR_ARG;
+  if ((first_group + n_groups) * cfg->group > cache->t_cap) return KVQ_ERR_ARG;
+  if (n_groups == 0) return KVQ_OK;
+  if (!k_out || !v_out) return KVQ_ERR_ARG;
+  if (!aligned16(k_out) || !aligned16(v_out)) return KVQ_ERR_ALIGN;
+  const int64_t heads = (int64_t)B * H_kv;
+  if (heads * n_groups * cfg->group * kD / 256 > 0x7FFFFFFF) return KVQ_ERR_ARG;
+  kvq::DequantArgs a{cache_args(cache), k_out, v_out, first_group, n_groups, (int32_t)heads,
+                     cfg->n_boost};
+  return hip_status(
+      kvq::launch_dequantize(cfg->bits, cfg->group, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

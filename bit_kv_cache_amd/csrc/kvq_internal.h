@@ -1,0 +1,90 @@
+// Internal declarations shared by the libkvq HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kD = 128;          // head dimension the kernels are built for
+constexpr int kMaxGqa = 8;       // query heads per kv head
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default mode).
+__device__ __forceinline__ uint16_t f2h(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Total order key of a finite fp16 value (-0 < +0), and its inverse.
+__device__ __forceinline__ uint32_t order_key(uint16_t h) {
+  return (h & 0x8000u) ? (0x7FFFu - (h & 0x7FFFu)) : (0x8000u + h);
+}
+__device__ __forceinline__ uint16_t from_order_key(uint32_t k) {
+  return (k < 0x8000u) ? (uint16_t)(0x8000u | (0x7FFFu - k)) : (uint16_t)(k - 0x8000u);
+}
+
+// ---------------------------------------------------------------- launch args
+
+struct CacheArgs {
+  uint32_t* k_codes;
+  uint16_t* k_scale;
+  uint16_t* k_min;
+  uint32_t* k_hi;
+  uint8_t* k_bidx;
+  uint32_t* v_codes;
+  uint16_t* v_scale;
+  uint16_t* v_min;
+  int64_t t_cap;
+};
+
+struct QuantArgs {
+  CacheArgs c;
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  int64_t src_head_stride;
+  int64_t first_group;
+  int64_t n_groups;
+  int32_t n_heads;
+  int32_t n_boost;
+};
+
+struct DequantArgs {
+  CacheArgs c;
+  float* k_out;
+  float* v_out;
+  int64_t first_group;
+  int64_t n_groups;
+  int32_t n_heads;
+  int32_t n_boost;
+};
+
+struct DecodeArgs {
+  CacheArgs c;
+  const uint16_t* q;       // [B][H_q][D] fp16
+  int32_t B, H_q, H_kv, gqa;
+  int32_t n_boost;
+  int64_t n_groups;        // quantized groups per head
+  int32_t n_chunks;        // token chunks per head (parts 0..n_chunks-1)
+  int32_t groups_per_chunk;
+  const uint16_t* k_sink;
+  const uint16_t* v_sink;
+  int32_t n_sink, sink_cap;
+  const uint16_t* k_res;
+  const uint16_t* v_res;
+  int32_t n_res, res_cap;
+  float qscale;            // sm_scale * log2(e): logits kept in the log2 domain
+  float* ws;               // partials [B][H_q][n_chunks+1][D+2]
+  float* out;              // [B][H_q][D]
+};
+
+// Each launcher returns the hipError_t of its launch (hipGetLastError).
+hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s);
+hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStream_t s);
+hipError_t launch_decode(int bits, int group, const DecodeArgs& a, hipStream_t s);
+
+}  // namespace kvq

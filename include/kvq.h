@@ -1,0 +1,178 @@
+/*
+ * kvq.h -- C ABI of libkvq, a low-bit KV cache for single-query decode
+ * attention on AMD Instinct MI355X (gfx950).
+ *
+ * What it computes
+ *  - KIVI-style asymmetric min-max group quantization (KIVI page, Step 1):
+ *    for a group x of G values, mn = min x, scale = fp16((max x - mn)/(2^bits-1)),
+ *    code = round(clamp((x - mn)/scale, 0, 2^bits-1)).  Keys are grouped per
+ *    channel over G consecutive tokens, values per token over G consecutive
+ *    channels (KIVI page, Step 1: K per-channel, V per-token).
+ *  - Packing 32/bits codes per 32-bit word, code j at bits [bits*j, bits*j+bits)
+ *    (KIVI page, Step 2 `pack_tensor`; unpack in Step 4).
+ *  - Optional Kitty channel-wise precision boost (Kitty page, sections 3.2,
+ *    4.1, 4.2): per key group the n_boost channels with the largest range use
+ *    4-bit codes, stored as a dense tensor of every channel's low two bits, a
+ *    compact tensor of the boosted channels' high two bits and a per-channel
+ *    index (sentinel = n_boost); dequantization is (lo | hi << 2)*scale + min.
+ *  - Single-query decode attention softmax(q K^T * sm) V (BitDecoding page,
+ *    section II) over: an fp16 sink window (Kitty page, section 3.1), the
+ *    quantized tokens (dequantized on chip), and an fp16 residual window of
+ *    the most recent tokens (KIVI page, Step 3), split over token chunks with
+ *    an fp32 log-sum-exp merge.
+ *
+ * Arithmetic contract (identical on every path, checked against a CPU oracle)
+ *  - quantizer: fp32 range max-min, IEEE fp32 division by 2^bits-1, scale
+ *    rounded to fp16 (nearest even); codes divide by the stored fp16 scale in
+ *    IEEE fp32, clamp, then round half to even; max == min (or a scale that
+ *    underflows fp16) stores scale 0 and codes 0.  min/max use the order
+ *    -0 < +0.  Packed words, scales, mins, high words and indices are
+ *    bit-exact.
+ *  - dequantized value: fp32 code*scale + min (one rounding).
+ *  - attention: fp32, output fp32; max-abs error vs an fp64 reference over
+ *    the same dequantized cache within 2e-3 for the documented inputs.
+ *
+ * Cache layout (device memory owned by the caller).  head = b*H_kv + h,
+ * fpi = 32/bits, D = head_dim, G = group, t_cap = token capacity per head:
+ *    k_codes  [head][t_cap][D/fpi]       key codes packed along channels:
+ *                                        word (t,w) holds channels w*fpi+j
+ *    k_scale, k_min [head][t_cap/G][D]   fp16 bits per (group, channel)
+ *    k_hi     [head][t_cap][n_boost/16]  Kitty: word (t,w) holds the high two
+ *                                        bits of boosted rows w*16+j
+ *    k_bidx   [head][t_cap/G][D] uint8   Kitty: boosted row of channel d
+ *                                        (ascending channel order) or n_boost
+ *    v_codes  [head][t_cap/fpi][D]       value codes packed along tokens:
+ *                                        word (w,d) holds tokens w*fpi+j
+ *    v_scale, v_min [head][t_cap][D/G]   fp16 bits per (token, channel group)
+ *  Keys are packed along the channel axis and values along the token axis:
+ *  the contraction axis of q.K^T and p.V, so one word feeds one lane's
+ *  matrix-core operand directly.
+ *
+ * Conventions
+ *  - fp16 data is passed as raw uint16_t bit patterns.
+ *  - All pointers except `cfg`/`cache`/window structs themselves are device
+ *    pointers, 16-byte aligned (else KVQ_ERR_ALIGN).
+ *  - `stream` is a hipStream_t (NULL = default stream).  Calls are
+ *    asynchronous; nothing synchronizes the host.
+ *  - The library allocates no memory and keeps no state between calls.
+ *  - Every argument is validated before anything is launched; on error
+ *    nothing is launched or written.  A failed launch returns KVQ_ERR_HIP.
+ *  - Non-finite inputs give undefined results.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,         /* bad size, null pointer, out-of-range index */
+  KVQ_ERR_ALIGN = -2,       /* a device pointer is not 16-byte aligned */
+  KVQ_ERR_UNSUPPORTED = -3, /* legal for the method, not built (bits 8, D != 128) */
+  KVQ_ERR_WORKSPACE = -4,   /* workspace missing or too small */
+  KVQ_ERR_HIP = -5          /* a kernel launch failed */
+} kvq_status;
+
+/* Quantization configuration.
+ *  bits: 2 or 4 (8 is a legal packing width on the KIVI page and returns
+ *        KVQ_ERR_UNSUPPORTED).
+ *  group: G, one of 32, 64, 128; must divide head_dim.
+ *  head_dim: D, 128.
+ *  n_boost: 0 (plain KIVI) or, with bits == 2, a multiple of 16 up to D
+ *        (Kitty boost; 16 of 128 channels is the 12.5% "Kitty" setting). */
+typedef struct kvq_qcfg {
+  int32_t bits;
+  int32_t group;
+  int32_t head_dim;
+  int32_t n_boost;
+} kvq_qcfg;
+
+/* Packed cache, layout above.  k_hi / k_bidx may be NULL when n_boost == 0.
+ * t_cap must be a positive multiple of G. */
+typedef struct kvq_cache {
+  int32_t* k_codes;
+  uint16_t* k_scale;
+  uint16_t* k_min;
+  int32_t* k_hi;
+  uint8_t* k_bidx;
+  int32_t* v_codes;
+  uint16_t* v_scale;
+  uint16_t* v_min;
+  int64_t t_cap;
+} kvq_cache;
+
+/* An fp16 window of full-precision tokens (sink or residual): k and v are
+ * [head][cap][D] fp16, the first n rows of each head are valid.  k/v may be
+ * NULL when n == 0. */
+typedef struct kvq_window {
+  const uint16_t* k;
+  const uint16_t* v;
+  int32_t n;
+  int32_t cap;
+} kvq_window;
+
+/* Human-readable name of a status code (static storage). */
+const char* kvq_status_string(kvq_status s);
+
+/* Quantize and pack groups [first_group, first_group + n_groups) of every
+ * head (KIVI page Steps 1-2; Kitty page section 4.1 when n_boost > 0).
+ *  k_src, v_src: fp16 [B*H_kv][>= n_groups*G][D]; head i starts at element
+ *      i*src_head_stride.  Typically the residual window (append one full
+ *      group after a decode step, Kitty page section 4.3 stage 3) or a
+ *      prefill slab (n_groups > 1).
+ *  Writes codes, scales, mins (and Kitty high words / indices) of those
+ *  groups only.  Requires (first_group + n_groups)*G <= t_cap and
+ *  src_head_stride >= n_groups*G*D.  n_groups == 0 is a no-op. */
+kvq_status kvq_quantize_pack(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                             int32_t H_kv, const uint16_t* k_src, const uint16_t* v_src,
+                             int64_t src_head_stride, int64_t first_group, int64_t n_groups,
+                             void* stream);
+
+/* Split plan of a decode step: the number of token chunks per head
+ * (n_chunks_req > 0 is honoured up to one chunk per group; 0 picks a count
+ * that fills the GPU) and the workspace size in bytes it needs. */
+kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t H_kv,
+                           int64_t n_quant_tokens, int32_t n_chunks_req, int32_t* n_chunks,
+                           size_t* ws_bytes);
+
+/* Workspace bytes of kvq_decode_attention for the same arguments (0 on a bad
+ * argument).  Partials are fp32 (m, l, acc[D]) per (batch, query head, part),
+ * part = chunk or the fp16 windows. */
+size_t kvq_decode_workspace_bytes(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t H_kv,
+                                  int64_t n_quant_tokens, int32_t n_chunks_req);
+
+/* One decode step: for batch b and query head h (kv head h / (H_q/H_kv)),
+ *   out[b][h] = softmax(sm * q[b][h] . K^T) V
+ * over the sink window, the first n_quant_tokens cached tokens and the
+ * residual window (which holds the current token).
+ *  q: fp16 [B][H_q][D].  out: fp32 [B][H_q][D].
+ *  n_quant_tokens: multiple of G, 0 <= n_quant_tokens <= t_cap.
+ *  sink, res: may be NULL (no tokens).
+ *  sm_scale <= 0 selects 1/sqrt(D).
+ *  n_chunks: token chunks per head for split-K (0 = automatic); see
+ *      kvq_decode_plan.  workspace: device memory of at least
+ *      kvq_decode_workspace_bytes(...) bytes, 16-byte aligned.
+ *  H_q / H_kv must be 1..8. */
+kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                                int32_t H_q, int32_t H_kv, const uint16_t* q,
+                                int64_t n_quant_tokens, const kvq_window* sink,
+                                const kvq_window* res, float sm_scale, int32_t n_chunks,
+                                void* workspace, size_t ws_bytes, float* out, void* stream);
+
+/* Dequantize groups [first_group, first_group + n_groups) of every head to
+ * fp32 [B*H_kv][n_groups*G][D] (value = code*scale + min; Kitty page
+ * Algorithm 1 for boosted key channels).  For checking the packed cache. */
+kvq_status kvq_dequantize(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_kv,
+                          int64_t first_group, int64_t n_groups, float* k_out, float* v_out,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

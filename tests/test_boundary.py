@@ -1,0 +1,125 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/kvq.h declares, and rejects bad arguments before launching
+anything (only calls that must fail validation are made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+kvq = pytest.importorskip("bit_kv_cache_amd")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert names == sorted(kvq.EXPORTED)
+    lib = ctypes.CDLL(kvq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert kvq.kvq_status_string(s).startswith("KVQ_")
+    assert "unknown" in kvq.kvq_status_string(7)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _cfg(bits=2, group=128, D=128, nb=0):
+    return kvq.kvq_qcfg(bits, group, D, nb)
+
+
+def _cache(t_cap=1024, align=0, hi=FAKE):
+    p = FAKE + align
+    return kvq.kvq_cache(p, p, p, hi, hi, p, p, p, t_cap)
+
+
+def _quant(cfg, cache, B=1, H=1, k=FAKE, v=FAKE, stride=128 * 128, fg=0, ng=1):
+    return kvq.raw_call("kvq_quantize_pack", ctypes.byref(cfg) if cfg else None,
+                        ctypes.byref(cache) if cache else None, B, H, k, v, stride, fg, ng, None)
+
+
+@pytest.mark.parametrize("cfg,want", [
+    (_cfg(bits=3), kvq.KVQ_ERR_ARG),
+    (_cfg(bits=8), kvq.KVQ_ERR_UNSUPPORTED),
+    (_cfg(D=64), kvq.KVQ_ERR_UNSUPPORTED),
+    (_cfg(group=48), kvq.KVQ_ERR_ARG),
+    (_cfg(group=8), kvq.KVQ_ERR_ARG),
+    (_cfg(group=0), kvq.KVQ_ERR_ARG),
+    (_cfg(nb=8), kvq.KVQ_ERR_ARG),
+    (_cfg(bits=4, nb=16), kvq.KVQ_ERR_ARG),
+    (_cfg(nb=144), kvq.KVQ_ERR_ARG),
+])
+def test_quantize_rejects_bad_config(cfg, want):
+    assert _quant(cfg, _cache()) == want
+
+
+def test_quantize_rejects_bad_arguments():
+    cfg = _cfg()
+    assert _quant(None, _cache()) == kvq.KVQ_ERR_ARG
+    assert _quant(cfg, None) == kvq.KVQ_ERR_ARG
+    assert _quant(cfg, _cache(t_cap=100)) == kvq.KVQ_ERR_ARG        # not a multiple of G
+    assert _quant(cfg, _cache(align=4)) == kvq.KVQ_ERR_ALIGN
+    assert _quant(cfg, _cache(), B=0) == kvq.KVQ_ERR_ARG
+    assert _quant(cfg, _cache(), fg=-1) == kvq.KVQ_ERR_ARG
+    assert _quant(cfg, _cache(t_cap=256), fg=1, ng=2) == kvq.KVQ_ERR_ARG   # past t_cap
+    assert _quant(cfg, _cache(), k=None) == kvq.KVQ_ERR_ARG
+    assert _quant(cfg, _cache(), stride=100) == kvq.KVQ_ERR_ARG
+    assert _quant(cfg, _cache(), k=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+    assert _quant(_cfg(nb=16), _cache(hi=None)) == kvq.KVQ_ERR_ARG
+
+
+def test_quantize_zero_groups_is_noop():
+    assert _quant(_cfg(), _cache(), ng=0) == kvq.KVQ_OK
+
+
+def _decode(cfg=None, cache=None, B=1, Hq=4, Hkv=1, q=FAKE, nq=1024, sink=None, res=None,
+            nchunks=0, ws=FAKE, ws_bytes=1 << 30, out=FAKE):
+    cfg = cfg or _cfg()
+    cache = cache or _cache()
+    return kvq.raw_call("kvq_decode_attention", ctypes.byref(cfg), ctypes.byref(cache), B, Hq,
+                        Hkv, q, nq, ctypes.byref(sink) if sink else None,
+                        ctypes.byref(res) if res else None, ctypes.c_float(0.0), nchunks, ws,
+                        ws_bytes, out, None)
+
+
+def test_decode_rejects_bad_arguments():
+    assert _decode(Hq=6, Hkv=4) == kvq.KVQ_ERR_ARG            # H_q not a multiple of H_kv
+    assert _decode(Hq=16, Hkv=1) == kvq.KVQ_ERR_UNSUPPORTED   # group of 16 query heads
+    assert _decode(Hq=3, Hkv=1) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _decode(nq=100) == kvq.KVQ_ERR_ARG                 # not a multiple of G
+    assert _decode(nq=2048) == kvq.KVQ_ERR_ARG                # past t_cap
+    assert _decode(nq=-128) == kvq.KVQ_ERR_ARG
+    assert _decode(nchunks=-1) == kvq.KVQ_ERR_ARG
+    assert _decode(q=None) == kvq.KVQ_ERR_ARG
+    assert _decode(out=FAKE + 8) == kvq.KVQ_ERR_ALIGN
+    assert _decode(ws=None) == kvq.KVQ_ERR_WORKSPACE
+    assert _decode(ws_bytes=16) == kvq.KVQ_ERR_WORKSPACE
+    assert _decode(res=kvq.kvq_window(FAKE, FAKE, 5, 4)) == kvq.KVQ_ERR_ARG    # n > cap
+    assert _decode(res=kvq.kvq_window(None, FAKE, 5, 8)) == kvq.KVQ_ERR_ARG
+    assert _decode(sink=kvq.kvq_window(FAKE + 2, FAKE, 1, 8)) == kvq.KVQ_ERR_ALIGN
+
+
+def test_decode_plan():
+    cfg = kvq.QCfg(bits=2, group=128)
+    # auto: ~1024 blocks over the heads, at most one chunk per group
+    assert kvq.kvq_decode_plan(cfg, 8, 32, 8, 32768)[0] == 16
+    assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 1 << 20)[0] == 128
+    assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 1 << 20, 256)[0] == 256
+    assert kvq.kvq_decode_plan(cfg, 1, 1, 1, 512)[0] == 4
+    assert kvq.kvq_decode_plan(cfg, 1, 1, 1, 0)[0] == 0
+    nc, ws = kvq.kvq_decode_plan(cfg, 8, 32, 8, 32768)
+    assert ws >= 8 * 32 * (nc + 1) * 130 * 4
+    assert kvq.kvq_decode_workspace_bytes(cfg, 8, 32, 8, 32768) == ws
+    assert kvq.kvq_decode_workspace_bytes(kvq.QCfg(bits=3), 8, 32, 8, 32768) == 0

@@ -1,0 +1,165 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds.
+
+Packed words, scales, mins, Kitty high words / indices and dequantized
+values must be bit-exact; attention outputs within max-abs 2e-3 of the
+oracle's fp64 attention over the same dequantized cache."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import (TOL, assert_cache_equal, gpu_decode, gpu_quantize, make_inputs,
+                         max_err, oracle_decode, oracle_quantize, qcfg)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+# (workload, overrides) -- shapes of the five workloads, shrunk in tokens (and
+# batch where needed) so that the oracle runs in seconds; each spans many
+# tiles and chunks and includes ragged chunk tails.
+CASES = {
+    "tiny": (W["tiny_t512_g32_2bit"], {}),
+    "llama_2bit": (W["llama3_8b_t32k_2bit"], dict(B=2, T=19 * 128)),
+    "llama_4bit": (W["llama3_8b_t8k_b32_4bit"], dict(B=2, T=11 * 128)),
+    "kitty": (W["kitty_t128k_h64_boost16"], dict(B=1, T=9 * 128)),
+    "long_splitk": (W["long_t1m_2bit_splitk"], dict(T=64 * 128)),
+    "g64_gqa2": (synth.shrink(W["llama3_8b_t32k_2bit"], H_q=16, G=64, T=23 * 64, B=1), {}),
+    "g32_4bit_gqa8": (synth.shrink(W["llama3_8b_t8k_b32_4bit"], H_q=64, G=32, T=40 * 32, B=1,
+                                   R=32, S=5), {}),
+    "kitty_boost32": (synth.shrink(W["kitty_t128k_h64_boost16"], n_boost=32, H_q=32, G=64,
+                                   T=6 * 64, R=64), {}),
+}
+
+
+def _w(name):
+    w, kw = CASES[name]
+    return synth.shrink(w, **kw) if kw else w
+
+
+@pytest.fixture(scope="module")
+def built():
+    import bit_kv_cache_amd  # noqa: F401  (fails loudly when the library is missing)
+    assert torch.cuda.is_available()
+    return True
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_quantize_and_dequantize_bit_exact(built, name):
+    import bit_kv_cache_amd as kvq
+    w = _w(name)
+    inp = make_inputs(w)
+    gc = gpu_quantize(w, inp)
+    oc = oracle_quantize(w, inp)
+    torch.cuda.synchronize()
+    assert_cache_equal(gc, oc, tokens=w.T)
+    # dequantized values
+    n = len(inp["heads"])
+    ng = w.T // w.G
+    ko = torch.empty((n, w.T, w.D), dtype=torch.float32, device="cuda")
+    vo = torch.empty_like(ko)
+    kvq.kvq_dequantize(qcfg(w), gc, 1, n, 0, ng, ko, vo)
+    kr, vr = oracle.dequantize(oc, 0, ng)
+    assert np.array_equal(ko.cpu().numpy().view(np.uint32), kr.view(np.uint32))
+    assert np.array_equal(vo.cpu().numpy().view(np.uint32), vr.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_matches_oracle(built, name):
+    w = _w(name)
+    inp = make_inputs(w)
+    gc = gpu_quantize(w, inp)
+    oc = oracle_quantize(w, inp)
+    ref = oracle_decode(w, oc, inp, w.T)
+    ng = w.T // w.G
+    for n_chunks in sorted({0, 1, 3, max(1, ng // 2), ng, ng + 5, w.min_chunks}):
+        out = gpu_decode(w, gc, inp, w.T, n_chunks=n_chunks)
+        err = max_err(out, ref)
+        assert err <= TOL, f"{name} n_chunks={n_chunks}: max-abs {err:.3g}"
+
+
+def test_append_group_matches_oracle(built):
+    """Decode step, then quantize the full residual group into the next group
+    slot (streaming append), then decode again with an empty residual."""
+    import bit_kv_cache_amd as kvq
+    for name in ("llama_2bit", "llama_4bit", "kitty"):
+        w = _w(name)
+        w = synth.shrink(w, R=w.G)
+        inp = make_inputs(w)
+        t_cap = w.T + w.G
+        gc = gpu_quantize(w, inp, t_cap)
+        oc = oracle_quantize(w, inp, t_cap)
+        n = len(inp["heads"])
+        kvq.kvq_quantize_pack(qcfg(w), gc, 1, n, inp["k_res"], inp["v_res"], w.T // w.G, 1)
+        oracle.quantize_pack(oc, synth.as_bits(inp["k_res"]), synth.as_bits(inp["v_res"]),
+                             w.T // w.G, 1)
+        torch.cuda.synchronize()
+        assert_cache_equal(gc, oc, tokens=t_cap)
+        out = gpu_decode(w, gc, inp, t_cap, n_res=0)
+        ref = oracle_decode(w, oc, inp, t_cap, n_res=0)
+        assert max_err(out, ref) <= TOL, name
+
+
+@pytest.mark.parametrize("name", ["llama_2bit", "kitty", "g32_4bit_gqa8"])
+def test_decode_edge_cases(built, name):
+    w = _w(name)
+    inp = make_inputs(w)
+    gc = gpu_quantize(w, inp)
+    oc = oracle_quantize(w, inp)
+    # no quantized tokens: every token in the fp16 windows
+    assert max_err(gpu_decode(w, gc, inp, 0), oracle_decode(w, oc, inp, 0)) <= TOL
+    # no windows at all
+    out = gpu_decode(w, gc, inp, w.T, n_res=0, n_sink=0)
+    assert max_err(out, oracle_decode(w, oc, inp, w.T, n_res=0, n_sink=0)) <= TOL
+    # a single quantized group, one residual token
+    out = gpu_decode(w, gc, inp, w.G, n_res=1, n_sink=0)
+    assert max_err(out, oracle_decode(w, oc, inp, w.G, n_res=1, n_sink=0)) <= TOL
+    # ragged: a prefix of the groups, odd window counts
+    n_q = (w.T // w.G // 2 + 1) * w.G
+    out = gpu_decode(w, gc, inp, n_q, n_chunks=3, n_res=min(w.R, 17), n_sink=min(w.S, 3))
+    ref = oracle_decode(w, oc, inp, n_q, n_res=min(w.R, 17), n_sink=min(w.S, 3))
+    assert max_err(out, ref) <= TOL
+
+
+def test_no_tokens_gives_zero(built):
+    w = _w("llama_2bit")
+    inp = make_inputs(w)
+    gc = gpu_quantize(w, inp)
+    out = gpu_decode(w, gc, inp, 0, n_res=0, n_sink=0)
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_decode_deterministic(built):
+    w = _w("llama_2bit")
+    inp = make_inputs(w)
+    gc = gpu_quantize(w, inp)
+    a = gpu_decode(w, gc, inp, w.T)
+    b = gpu_decode(w, gc, inp, w.T)
+    assert torch.equal(a, b)
+    # quantizing twice writes identical bits
+    gc2 = gpu_quantize(w, inp)
+    torch.cuda.synchronize()
+    for f in ("k_codes", "k_scale", "k_min", "v_codes", "v_scale", "v_min"):
+        assert torch.equal(getattr(gc, f), getattr(gc2, f)), f
+
+
+def test_head_view_and_stream(built):
+    """Quantizing head slices on a side stream equals one bulk call."""
+    import bit_kv_cache_amd as kvq
+    w = _w("llama_4bit")
+    inp = make_inputs(w)
+    bulk = gpu_quantize(w, inp)
+    part = kvq.Cache.empty(qcfg(w), len(inp["heads"]), w.T + w.G)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for h0 in range(0, len(inp["heads"]), 5):
+            n = min(5, len(inp["heads"]) - h0)
+            kvq.kvq_quantize_pack(qcfg(w), part.heads_view(h0, n), 1, n, inp["k"][h0:h0 + n],
+                                  inp["v"][h0:h0 + n], 0, w.T // w.G, stream=s)
+    s.synchronize()
+    for f in ("k_codes", "k_scale", "k_min", "v_codes", "v_scale", "v_min"):
+        assert torch.equal(getattr(bulk, f), getattr(part, f)), f
