@@ -2,72 +2,23 @@
 // and the log-sum-exp merge of the partial results.
 //
 // Each block owns one (batch, kv head) and one "part": a chunk of quantized
-// groups, or (last part) the fp16 sink + residual windows.  It keeps, for
+// groups, or the fp16 sink + residual windows (workspace slot n_chunks).  It keeps, for
 // every query head of the kv head's GQA group, the online-softmax state
 // (running max m, running sum l, accumulator acc[D]) in the log2 domain and
 // writes it to the workspace; the merge kernel combines the parts:
 //   M = max_p m_p,  O = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
 //
-// This kernel dequantizes in registers (code*scale + min in fp32, the same
-// value the cache defines, KIVI page Step 4) and forms q.k and p.v on the
-// vector ALUs.
+// The kernel here dequantizes in registers (code*scale + min in fp32, the
+// same value the cache defines, KIVI page Step 4) and forms q.k and p.v on
+// the vector ALUs.  It serves MHA and small query groups, group sizes 32/64
+// and the Kitty boost; GQA groups of 4 or 8 with G = 128 go to the matrix-core
+// kernel (decode_mfma.hip).  Both write the same partials.
 
 #include "kvq_internal.h"
+#include "decode_common.h"
 
 namespace kvq {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kBlockTok = 128;   // tokens per processing block
-constexpr float kNegInf = -__builtin_inff();
-
-struct SoftmaxState {
-  float m[kMaxGqa];
-  float l[kMaxGqa];
-};
-
-template <int GQA>
-struct Lds {
-  float q[GQA][kD];                      // query * sm * log2(e)
-  float ks[kBlockTok / 32][kD];          // key scale / min per (group in block, channel)
-  float km[kBlockTok / 32][kD];
-  int kb[kBlockTok / 32][kD];            // Kitty boosted row per (group in block, channel)
-  float vs[kBlockTok * 4];               // value scale / min per (token, channel group)
-  float vm[kBlockTok * 4];
-  float part[2][GQA][kBlockTok];         // q.k partial sums of the two channel halves
-  float p[GQA][kBlockTok];               // logits, then probabilities
-  float m[GQA], l[GQA], alpha[GQA];
-  float acc[GQA][kD];                    // final combine of the two token halves
-};
-
-// ------------------------------------------------------------------ softmax
-// Block-wide online softmax update over the nt logits in lds.p.
-template <int GQA>
-__device__ void softmax_block(Lds<GQA>& s, int nt) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int h = wave; h < GQA; h += kThreads / 64) {
-    float mx = kNegInf;
-    for (int t = lane; t < nt; t += 64) mx = fmaxf(mx, s.p[h][t]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float m_old = s.m[h];
-    const float m_new = fmaxf(m_old, mx);
-    float sum = 0.f;
-    for (int t = lane; t < nt; t += 64) {
-      const float e = exp2f(s.p[h][t] - m_new);
-      s.p[h][t] = e;
-      sum += e;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-    if (lane == 0) {
-      const float alpha = exp2f(m_old - m_new);   // 0 when m_old == -inf
-      s.alpha[h] = alpha;
-      s.l[h] = s.l[h] * alpha + sum;
-      s.m[h] = m_new;
-    }
-  }
-}
 
 // --------------------------------------------------------- quantized block
 // Tokens [t0, t0+nt) of head `head`, nt a multiple of G, nt <= kBlockTok.
@@ -164,59 +115,6 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
   __syncthreads();
 }
 
-// ------------------------------------------------------------ fp16 window
-// Window tokens [u0, u0+nt) of the concatenation sink | residual.
-template <int GQA>
-__device__ void window_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int u0, int nt,
-                             float (&acc)[GQA]) {
-  const int tid = threadIdx.x;
-  auto krow = [&](int u) -> const uint16_t* {
-    return u < a.n_sink ? a.k_sink + (head * a.sink_cap + u) * kD
-                        : a.k_res + (head * a.res_cap + (u - a.n_sink)) * kD;
-  };
-  auto vrow = [&](int u) -> const uint16_t* {
-    return u < a.n_sink ? a.v_sink + (head * a.sink_cap + u) * kD
-                        : a.v_res + (head * a.res_cap + (u - a.n_sink)) * kD;
-  };
-  {
-    const int t = tid & (kBlockTok - 1), half = tid >> 7;
-    if (t < nt) {
-      const uint16_t* k = krow(u0 + t) + half * (kD / 2);
-      float dot[GQA];
-#pragma unroll
-      for (int h = 0; h < GQA; ++h) dot[h] = 0.f;
-      for (int c = 0; c < kD / 2; ++c) {
-        const float x = h2f(k[c]);
-#pragma unroll
-        for (int h = 0; h < GQA; ++h) dot[h] = fmaf(s.q[h][half * (kD / 2) + c], x, dot[h]);
-      }
-#pragma unroll
-      for (int h = 0; h < GQA; ++h) s.part[half][h][t] = dot[h];
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < GQA * nt; i += kThreads) {
-    const int h = i / nt, t = i % nt;
-    s.p[h][t] = s.part[0][h][t] + s.part[1][h][t];
-  }
-  __syncthreads();
-  softmax_block<GQA>(s, nt);
-  __syncthreads();
-  {
-    const int d = tid & (kD - 1), half = tid >> 7;
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) acc[h] *= s.alpha[h];
-    const int tb = half * (kBlockTok / 2);
-    const int te = min(nt, tb + kBlockTok / 2);
-    for (int t = tb; t < te; ++t) {
-      const float x = h2f(vrow(u0 + t)[d]);
-#pragma unroll
-      for (int h = 0; h < GQA; ++h) acc[h] = fmaf(s.p[h][t], x, acc[h]);
-    }
-  }
-  __syncthreads();
-}
-
 // grid: (n_chunks + 1, B * H_kv); part n_chunks is the fp16 windows
 template <int BITS, int G, int GQA>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
@@ -225,8 +123,6 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   const int part = blockIdx.x;
   const int64_t head = blockIdx.y;
   const int64_t b = head / a.H_kv, hk = head % a.H_kv;
-  const int n_parts = a.n_chunks + 1;
-
   for (int i = tid; i < GQA * kD; i += kThreads) {
     const int h = i / kD, d = i % kD;
     s.q[h][d] = h2f(a.q[((b * a.H_q) + hk * GQA + h) * kD + d]) * a.qscale;
@@ -254,24 +150,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       window_block<GQA>(a, s, head, u, min(kBlockTok, n_win - u), acc);
   }
 
-  // combine the two token halves and write (m, l, acc)
-  const int d = tid & (kD - 1), half = tid >> 7;
-  if (half) {
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) s.acc[h][d] = acc[h];
-  }
-  __syncthreads();
-  if (!half) {
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) {
-      float* w = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + part) * (kD + 2);
-      w[2 + d] = acc[h] + s.acc[h][d];
-      if (d == 0) {
-        w[0] = s.m[h];
-        w[1] = s.l[h];
-      }
-    }
-  }
+  write_partial<GQA>(a, s, b, hk, part, acc);
 }
 
 // grid: B * H_q blocks of kD threads
@@ -305,9 +184,6 @@ hipError_t decode_bg(const DecodeArgs& a, hipStream_t st) {
     case 8: decode_valu_kernel<BITS, G, 8><<<grid, kThreads, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  merge_kernel<<<(unsigned)(a.B * a.H_q), kD, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -324,7 +200,14 @@ hipError_t decode_bits(int group, const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode(int bits, int group, const DecodeArgs& a, hipStream_t st) {
-  return bits == 2 ? decode_bits<2>(group, a, st) : decode_bits<4>(group, a, st);
+  hipError_t e;
+  if (mfma_decode_supported(bits, group, a.gqa, a.n_boost))
+    e = launch_decode_mfma(bits, a, st);
+  else
+    e = bits == 2 ? decode_bits<2>(group, a, st) : decode_bits<4>(group, a, st);
+  if (e != hipSuccess) return e;
+  merge_kernel<<<(unsigned)(a.B * a.H_q), kD, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace kvq

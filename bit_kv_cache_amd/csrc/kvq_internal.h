@@ -86,5 +86,7 @@ struct DecodeArgs {
 hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStream_t s);
 hipError_t launch_decode(int bits, int group, const DecodeArgs& a, hipStream_t s);
+bool mfma_decode_supported(int bits, int group, int gqa, int n_boost);
+hipError_t launch_decode_mfma(int bits, const DecodeArgs& a, hipStream_t s);
 
 }  // namespace kvq

@@ -32,6 +32,8 @@ CASES = {
                                    R=32, S=5), {}),
     "kitty_boost32": (synth.shrink(W["kitty_t128k_h64_boost16"], n_boost=32, H_q=32, G=64,
                                    T=6 * 64, R=64), {}),
+    "gqa8_2bit": (synth.shrink(W["llama3_8b_t32k_2bit"], H_q=64, B=1, T=13 * 128, S=7), {}),
+    "gqa8_4bit": (synth.shrink(W["llama3_8b_t8k_b32_4bit"], H_q=64, B=1, T=10 * 128), {}),
 }
 
 
@@ -163,3 +165,25 @@ def test_head_view_and_stream(built):
     s.synchronize()
     for f in ("k_codes", "k_scale", "k_min", "v_codes", "v_scale", "v_min"):
         assert torch.equal(getattr(bulk, f), getattr(part, f)), f
+
+
+@pytest.mark.parametrize("name", ["llama_2bit", "llama_4bit", "gqa8_2bit"])
+@pytest.mark.parametrize("qk,vs", [(4.0, 1 / 16), (1 / 8, 8.0), (1.0, 1 / 1024)])
+def test_decode_scaled_inputs(built, name, qk, vs):
+    """Inputs scaled away from N(0,1): sharper / flatter softmax, large and tiny
+    value scales (exercises the per-group operand exponents)."""
+    w = _w(name)
+    inp = make_inputs(w)
+    for key in ("k", "k_res", "k_sink", "q"):
+        if inp[key] is not None:
+            inp[key] = (inp[key].float() * qk).half()
+    for key in ("v", "v_res", "v_sink"):
+        if inp[key] is not None:
+            inp[key] = (inp[key].float() * vs).half()
+    gc = gpu_quantize(w, inp)
+    oc = oracle_quantize(w, inp)
+    torch.cuda.synchronize()
+    assert_cache_equal(gc, oc, tokens=w.T)
+    ref = oracle_decode(w, oc, inp, w.T)
+    err = max_err(gpu_decode(w, gc, inp, w.T), ref)
+    assert err <= TOL * max(1.0, vs), f"max-abs {err:.3g}"
