@@ -193,7 +193,7 @@ def main(argv=None):
     q = synth.query(w, "cuda")
     n_chunks, ws_bytes = kvq.kvq_decode_plan(cfg, w.B, w.H_q, w.H_kv, w.T,
                                              args.n_chunks or w.min_chunks)
-    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(ws_bytes // 4, dtype=torch.float32, device="cuda")   # counters start at 0
     out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -289,7 +289,7 @@ def main(argv=None):
         "append_quant_us": round(app_avg * 1e3, 3) if append else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "kvq_decode_attention (split-K + merge)",
+                     "traffic": None, "kernel": "kvq_decode_attention",
                      "algorithmic_bytes": alg},
     }
     if not args.no_cpu_baseline:

@@ -153,25 +153,64 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   write_partial<GQA>(a, s, b, hk, part, acc);
 }
 
-// grid: B * H_q blocks of kD threads
-__global__ __launch_bounds__(kD) void merge_kernel(DecodeArgs a) {
+// Log-sum-exp merge of the parts: one block per (batch, query head).
+// Parts' (m, l) are read in parallel (one per thread), the weights
+// 2^(m_p - M) / L go to LDS, then each thread sums one channel over the parts
+// with its loads batched.
+constexpr int kMergeThreads = 256;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+  __shared__ float s_w[1024];
+  __shared__ float s_red[kMergeThreads / 64];
   const int64_t bh = blockIdx.x;
-  const int d = threadIdx.x;
-  const int n_parts = a.n_chunks + 1;
-  const float* w = a.ws + bh * n_parts * (kD + 2);
-  float M = kNegInf;
-  for (int p = 0; p < n_parts; ++p)
-    if (w[p * (kD + 2) + 1] > 0.f) M = fmaxf(M, w[p * (kD + 2)]);
-  float L = 0.f, o = 0.f;
-  for (int p = 0; p < n_parts; ++p) {
-    const float* wp = w + p * (kD + 2);
-    if (wp[1] > 0.f) {
-      const float f = exp2f(wp[0] - M);
-      L = fmaf(wp[1], f, L);
-      o = fmaf(wp[2 + d], f, o);
-    }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int np = a.n_parts;
+  const float* w = a.ws + bh * (int64_t)np * (kD + 2);
+  // block max of the non-empty parts
+  float mx = kNegInf;
+  for (int p = tid; p < np; p += kMergeThreads) {
+    const float l = w[p * (kD + 2) + 1];
+    const float m = w[p * (kD + 2)];
+    s_w[p] = l > 0.f ? m : kNegInf;
+    mx = fmaxf(mx, s_w[p]);
   }
-  a.out[bh * kD + d] = (L > 0.f) ? o / L : 0.f;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  float M = s_red[0];
+#pragma unroll
+  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, s_red[i]);
+  __syncthreads();
+  // weights and their l-weighted sum
+  float L = 0.f;
+  for (int p = tid; p < np; p += kMergeThreads) {
+    const float f = s_w[p] == kNegInf ? 0.f : exp2f(s_w[p] - M);
+    s_w[p] = f;
+    L = fmaf(w[p * (kD + 2) + 1], f, L);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+  if (lane == 0) s_red[wave] = L;
+  __syncthreads();
+  float Ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMergeThreads / 64; ++i) Ls += s_red[i];
+  // numerators: thread (channel d, part phase), batched independent loads
+  const int d = tid & (kD - 1), ph = tid >> 7;
+  float o = 0.f;
+  int p = ph;
+  for (; p + 14 < np; p += 16) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = w[(p + 2 * j) * (kD + 2) + 2 + d];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o = fmaf(v[j], s_w[p + 2 * j], o);
+  }
+  for (; p < np; p += 2) o = fmaf(w[p * (kD + 2) + 2 + d], s_w[p], o);
+  __syncthreads();
+  if (ph) s_w[d] = o;   // s_w is free again: park the odd-phase sums
+  __syncthreads();
+  if (!ph) a.out[bh * kD + d] = Ls > 0.f ? (o + s_w[d]) / Ls : 0.f;
 }
 
 template <int BITS, int G>
@@ -200,13 +239,11 @@ hipError_t decode_bits(int group, const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode(int bits, int group, const DecodeArgs& a, hipStream_t st) {
-  hipError_t e;
-  if (mfma_decode_supported(bits, group, a.gqa, a.n_boost))
-    e = launch_decode_mfma(bits, a, st);
-  else
-    e = bits == 2 ? decode_bits<2>(group, a, st) : decode_bits<4>(group, a, st);
+  const hipError_t e = mfma_decode_supported(bits, group, a.gqa, a.n_boost)
+                           ? launch_decode_mfma(bits, a, st)
+                           : (bits == 2 ? decode_bits<2>(group, a, st) : decode_bits<4>(group, a, st));
   if (e != hipSuccess) return e;
-  merge_kernel<<<(unsigned)(a.B * a.H_q), kD, 0, st>>>(a);
+  merge_kernel<<<(unsigned)(a.B * a.H_q), kMergeThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -119,7 +119,7 @@ __device__ void write_partial(const DecodeArgs& a, Lds<GQA>& s, int64_t b, int64
                               const float (&acc)[GQA]) {
   const int tid = threadIdx.x;
   const int d = tid & (kD - 1), half = tid >> 7;
-  const int n_parts = a.n_chunks + 1;
+  const int n_parts = a.n_parts;
   if (half) {
 #pragma unroll
     for (int h = 0; h < GQA; ++h) s.acc[h][d] = acc[h];

@@ -23,10 +23,16 @@
 //  * sum_d q_d mn_d (keys) is one more MFMA per group; sum_t p_t mn_t
 //    (values) is a per-head scalar kept beside the accumulator.
 //
-// Work split: block = 4 waves on one (batch, kv head) and one chunk of groups;
-// each wave owns whole groups (round robin), keeps its own online softmax
-// state, and the 4 waves are merged at the end of the chunk.  Part 0 of each
-// head is the fp16 sink + residual window (vector ALU path).
+// Work split: block = 4 waves on one (batch, kv head) and one chunk of groups
+// plus a slice of the fp16 sink/residual window (so every block carries the
+// same load and the grid runs in one round of resident blocks).  Each wave
+// owns whole groups (round robin) with its own online softmax state and
+// software-pipelined loads (the next group's keys load during q.K^T's
+// successors, its values during p.V's).  At the chunk end the waves and the
+// window slice merge in LDS and the block writes its partial (m, l, acc); the
+// log-sum-exp merge kernel combines the chunks.
+
+#include <type_traits>
 
 #include "kvq_internal.h"
 #include "decode_common.h"
@@ -113,6 +119,77 @@ __device__ __forceinline__ float wave_max16(float v) {  // over the 16 lanes of 
   return fmaxf(v, __shfl_xor(v, 8));
 }
 
+
+template <int BITS>
+struct KeyLoad {
+  static constexpr int KW = BITS == 2 ? 2 : 4;   // key words per lane per tile
+  uint32_t kw[8][KW];                           // 8 tiles of 16 tokens
+  u32x4 kmin[4];                                // key minima, natural order (bias MFMA)
+  u32x2 ks[2];                                  // key scales of the A-prep chunk
+};
+
+template <int BITS>
+struct ValueLoad {
+  static constexpr int VR = BITS == 2 ? 2 : 4;   // value word rows per lane group
+  u32x4 vw[VR][2];
+  u32x2 vs[2], vm[2];                           // value scale / min of the P' chunk
+};
+
+// Offset (elements) of the two 4-element runs of an A-prep chunk.
+template <int BITS>
+__device__ __forceinline__ int run_stride() { return BITS == 2 ? 8 : 4; }
+
+template <int BITS>
+__device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int64_t g, int n,
+                                          int kq, int pc, int pkq, KeyLoad<BITS>& L) {
+  constexpr int WPT = kD / (32 / BITS);
+  const uint32_t* kb = reinterpret_cast<const uint32_t*>(a.c.k_codes) +
+                       (head * a.c.t_cap + g * kG + n) * WPT + KeyLoad<BITS>::KW * kq;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    if (BITS == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(kb + 16 * t * WPT);
+      L.kw[t][0] = v[0];
+      L.kw[t][1] = v[1];
+    } else {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(kb + 16 * t * WPT);
+#pragma unroll
+      for (int i = 0; i < KeyLoad<BITS>::KW; ++i) L.kw[t][i] = v[i];
+    }
+  }
+  const int64_t kmeta = (head * (a.c.t_cap / kG) + g) * kD;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    L.kmin[c] = *reinterpret_cast<const u32x4*>(a.c.k_min + kmeta + 32 * c + 8 * kq);
+  const int base = chunk_index<BITS>(pc, pkq, 0);
+  L.ks[0] = *reinterpret_cast<const u32x2*>(a.c.k_scale + kmeta + base);
+  L.ks[1] = *reinterpret_cast<const u32x2*>(a.c.k_scale + kmeta + base + run_stride<BITS>());
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_values(const DecodeArgs& a, int64_t head, int64_t g, int n,
+                                            int kq, int pc, int pkq, ValueLoad<BITS>& L) {
+  constexpr int FPI = 32 / BITS;
+  constexpr int VR = ValueLoad<BITS>::VR;
+  const uint32_t* vb = reinterpret_cast<const uint32_t*>(a.c.v_codes) +
+                       (head * (a.c.t_cap / FPI) + g * (kG / FPI) + VR * kq) * kD + 4 * n;
+#pragma unroll
+  for (int i = 0; i < VR; ++i)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) L.vw[i][e] = *reinterpret_cast<const u32x4*>(vb + i * kD + 64 * e);
+  const int64_t t0 = head * a.c.t_cap + g * kG + chunk_index<BITS>(pc, pkq, 0);
+  L.vs[0] = *reinterpret_cast<const u32x2*>(a.c.v_scale + t0);
+  L.vs[1] = *reinterpret_cast<const u32x2*>(a.c.v_scale + t0 + run_stride<BITS>());
+  L.vm[0] = *reinterpret_cast<const u32x2*>(a.c.v_min + t0);
+  L.vm[1] = *reinterpret_cast<const u32x2*>(a.c.v_min + t0 + run_stride<BITS>());
+}
+
+// fp16 element e (= 2r + half) of an A-prep chunk from its two 4-element runs
+__device__ __forceinline__ float chunk_elem(const u32x2 (&run)[2], int e) {
+  const uint32_t w = run[e & 1][(e >> 1) >> 1];
+  return h2f((uint16_t)(((e >> 1) & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
+
 template <int GQA>
 struct WaveLds {
   static constexpr int ROWS = 2 * GQA;             // A rows: (head, hi/lo)
@@ -120,7 +197,6 @@ struct WaveLds {
   u32x4 av[4][4][ROWS];                            // value A operand [c][kq][row]
   float p[GQA][kG];                                // probabilities of the group
   float alpha[GQA];
-  float m[GQA];
 };
 
 template <int GQA>
@@ -130,19 +206,26 @@ struct MergeLds {
 };
 
 template <int GQA>
-union MfmaLds {
-  struct {
-    WaveLds<GQA> w[kWaves];
-    u32x4 zero;
-  } main;
-  MergeLds<GQA> merge;
-  Lds<GQA> window;
+struct WindowResult {
+  float acc[GQA][kD];
+  float m[GQA], l[GQA];
+};
+
+template <int GQA>
+struct MfmaLds {
+  union {
+    struct {
+      WaveLds<GQA> w[kWaves];
+      u32x4 zero;
+    } main;
+    MergeLds<GQA> merge;
+    Lds<GQA> window;
+  } u;
+  WindowResult<GQA> win;
 };
 
 template <int BITS, int GQA>
 __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int FPI = 32 / BITS;
-  constexpr int WPT = kD / FPI;          // key words per token
   constexpr int TPC = GQA == 4 ? 2 : 1;  // tiles per QK accumulator (row slots)
   constexpr int NFRAG = 8 / TPC;         // QK accumulators per group
   constexpr int NH = GQA / 4;            // A-prep heads per lane (1 or 2)
@@ -151,51 +234,67 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kq = lane >> 4;   // operand lane coordinates
+  const int chunk = blockIdx.x;
   const int64_t head = blockIdx.y;
   const int64_t b = head / a.H_kv, hk = head % a.H_kv;
-  const int n_parts = a.n_chunks + 1;
+  const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
 
-  // ---------------------------------------------------------------- fp16 windows
-  if (blockIdx.x == 0) {
-    Lds<GQA>& s = sh.window;
-    for (int i = tid; i < GQA * kD; i += kThreadsM) {
-      const int h = i / kD, d = i % kD;
-      s.q[h][d] = h2f(a.q[((b * a.H_q) + hk * GQA + h) * kD + d]) * a.qscale;
-    }
-    if (tid < GQA) {
-      s.m[tid] = kNegInfM;
-      s.l[tid] = 0.f;
+  // ---------------------------------------------------------------- window slice
+  {
+    const int n_win = a.n_sink + a.n_res;
+    const int wpc = (n_win + a.n_chunks - 1) / a.n_chunks;
+    const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
+    Lds<GQA>& s = sh.u.window;
+    if (u1 > u0) {
+      for (int i = tid; i < GQA * kD; i += kThreadsM) s.q[i / kD][i % kD] = h2f(qrow[i]) * a.qscale;
+      if (tid < GQA) {
+        s.m[tid] = kNegInfM;
+        s.l[tid] = 0.f;
+      }
+      __syncthreads();
+      float acc[GQA];
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) acc[h] = 0.f;
+      for (int u = u0; u < u1; u += kBlockTok)
+        window_block<GQA>(a, s, head, u, min(kBlockTok, u1 - u), acc);
+      const int d = tid & (kD - 1), half = tid >> 7;
+      if (half) {
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) sh.win.acc[h][d] = acc[h];
+      }
+      __syncthreads();
+      if (!half) {
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) sh.win.acc[h][d] += acc[h];
+      }
+      if (tid < GQA) {
+        sh.win.m[tid] = s.m[tid];
+        sh.win.l[tid] = s.l[tid];
+      }
+    } else if (tid < GQA) {
+      sh.win.m[tid] = kNegInfM;
+      sh.win.l[tid] = 0.f;
     }
     __syncthreads();
-    float acc[GQA];
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) acc[h] = 0.f;
-    const int n_win = a.n_sink + a.n_res;
-    for (int u = 0; u < n_win; u += kBlockTok)
-      window_block<GQA>(a, s, head, u, min(kBlockTok, n_win - u), acc);
-    write_partial<GQA>(a, s, b, hk, a.n_chunks, acc);
-    return;
   }
 
-  // ---------------------------------------------------------------- quantized chunk
-  const int chunk = blockIdx.x - 1;
+  // ---------------------------------------------------------------- quantized groups
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
   const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
-  WaveLds<GQA>& L = sh.main.w[wave];
-  if (tid == 0) sh.main.zero = u32x4{0u, 0u, 0u, 0u};
+  WaveLds<GQA>& L = sh.u.main.w[wave];
+  if (tid == 0) sh.u.main.zero = u32x4{0u, 0u, 0u, 0u};
 
-  // query in the log2 domain, this wave's A-prep heads and chunk
-  const int ph = lane >> 4;                 // A-prep head (plus 4 for the second)
-  const int pc = lane & 3, pkq = (lane >> 2) & 3;   // A-prep chunk (c, kq)
+  // this lane's A-prep heads and chunk (c, kq)
+  const int ph = lane >> 4;
+  const int pc = lane & 3, pkq = (lane >> 2) & 3;
   float qhat[NH][8];                        // q * sm * log2e * 2^(24 - offset)
   float qmax = 0.f;
 #pragma unroll
   for (int j = 0; j < NH; ++j) {
-    const int h = ph + 4 * j;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int ch = chunk_index<BITS>(pc, pkq, e);
-      const float qv = h2f(a.q[((b * a.H_q) + hk * GQA + h) * kD + ch]) * a.qscale;
+      const float qv = h2f(qrow[(ph + 4 * j) * kD + ch]) * a.qscale;
       qhat[j][e] = qv * exp2i(24 - code_offset<BITS>(ch));
       qmax = fmaxf(qmax, fabsf(qhat[j][e]));
     }
@@ -213,17 +312,17 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
     for (int c = 0; c < 4; ++c) {
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = h2f(a.q[((b * a.H_q) + hk * GQA + h) * kD + 32 * c + 8 * kq + e]) * a.qscale;
+      for (int e = 0; e < 8; ++e) v[e] = h2f(qrow[h * kD + 32 * c + 8 * kq + e]) * a.qscale;
       u32x4 hi, lo;
       split_hilo(v, hi, lo);
       abias[c] = hl ? lo : hi;
     }
   }
 
-  // per-wave online softmax state: this lane's QK heads hA, hB
+  // per-wave online softmax state: this lane's QK heads hA, hA + 1
   const int rq = lane >> 4;
   const int hA = GQA == 4 ? 2 * (rq & 1) : 2 * rq;
+  const bool pv_rows = GQA == 8 || rq < 2;  // lanes holding real p.V rows
   float m_run[2] = {kNegInfM, kNegInfM};
   float l_part[2] = {0.f, 0.f};
   float mterm[NH];                          // sum_t p_t * value min, A-prep heads
@@ -233,57 +332,26 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
   f32x4 acc[8];                             // p.V accumulators, 8 channel blocks
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int m_row = lane & 15;
   __syncthreads();
 
-  const uint32_t* kw_base = reinterpret_cast<const uint32_t*>(a.c.k_codes);
-  for (int64_t g = gb + wave; g < ge; g += kWaves) {
-    // ---- loads
-    const int64_t tok0 = head * a.c.t_cap + g * kG;
-    uint32_t kwords[8][BITS == 2 ? 2 : 4];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t* p = kw_base + (tok0 + 16 * t + n) * WPT + (BITS == 2 ? 2 : 4) * kq;
-      if (BITS == 2) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-        kwords[t][0] = v[0];
-        kwords[t][1] = v[1];
-      } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-        for (int i = 0; i < (BITS == 2 ? 2 : 4); ++i) kwords[t][i] = v[i];
-      }
-    }
-    constexpr int VR = BITS == 2 ? 2 : 4;   // value word rows per lane group
-    u32x4 vwords[VR][2];
-    {
-      const uint32_t* vb = reinterpret_cast<const uint32_t*>(a.c.v_codes) +
-                           (head * (a.c.t_cap / FPI) + g * (kG / FPI) + VR * kq) * kD + 4 * n;
-#pragma unroll
-      for (int i = 0; i < VR; ++i)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          vwords[i][e] = *reinterpret_cast<const u32x4*>(vb + i * kD + 64 * e);
-    }
-    const int64_t kmeta = (head * (a.c.t_cap / kG) + g) * kD;
-    u32x4 kmin[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      kmin[c] = *reinterpret_cast<const u32x4*>(a.c.k_min + kmeta + 32 * c + 8 * kq);
-    // key scales of the A-prep chunk, value scale/min of the P' chunk
-    float ks[8];
-    uint16_t vsb[8], vmb[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = chunk_index<BITS>(pc, pkq, e);
-      ks[e] = h2f(a.c.k_scale[kmeta + i]);
-      vsb[e] = a.c.v_scale[head * a.c.t_cap + g * kG + i];
-      vmb[e] = a.c.v_min[head * a.c.t_cap + g * kG + i];
-    }
+  KeyLoad<BITS> kl;
+  ValueLoad<BITS> vl;
+  // One group of this wave.  With PREFETCH the next group's keys are fetched
+  // right after q.K^T and its values right after p.V (unconditionally, so the
+  // wait counters stay exact); the wave's last group runs without.
+  auto group_step = [&](int64_t g, auto prefetch_tag) {
+    constexpr bool PREFETCH = decltype(prefetch_tag)::value;
+    const int64_t gn = g + kWaves;
 
-    // ---- key A operand: (q s) 2^(24-offset) 2^-E_K, hi/lo rows, via LDS
+    // ---- key A operand: (q s) 2^(24-offset) 2^-E_K as hi/lo rows, via LDS
+    float ks[8];
     float smax = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) smax = fmaxf(smax, ks[e]);
+    for (int e = 0; e < 8; ++e) {
+      ks[e] = chunk_elem(kl.ks, e);
+      smax = fmaxf(smax, ks[e]);
+    }
     smax = wave_max16(smax);
     const int e_k = e_q + ceil_exp(smax) - 15;
     const float sk = exp2i(max(-126, min(127, -e_k)));
@@ -302,15 +370,14 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- bias: sum_d q_d mn_d per head (natural channel order)
+    // ---- bias: sum_d q_d mn_d per head
     f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) cb = mfma(abias[c], kmin[c], cb);
+    for (int c = 0; c < 4; ++c) cb = mfma(abias[c], kl.kmin[c], cb);
     const float biasA = cb[0] + cb[1], biasB = cb[2] + cb[3];
 
     // ---- q.K^T
     const float ek = exp2i(max(-126, min(127, e_k)));
-    const int m_row = lane & 15;
     float logit[NFRAG][2];
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
@@ -323,17 +390,17 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
           u32x4 bq;
           if (BITS == 2) {
             u32x4 q0, q1;
-            conv2(kwords[t][c >> 1], q0, q1);
+            conv2(kl.kw[t][c >> 1], q0, q1);
             bq = (c & 1) ? q1 : q0;
           } else {
-            bq = conv4(kwords[t][c]);
+            bq = conv4(kl.kw[t][c]);
           }
           u32x4 aq;
           if (TPC == 1) {
             aq = L.ak[c][kq][m_row];
           } else {
             const bool mine = (m_row >> 3) == slot;
-            aq = mine ? L.ak[c][kq][m_row & 7] : sh.main.zero;
+            aq = mine ? L.ak[c][kq][m_row & 7] : sh.u.main.zero;
           }
           cq = mfma(aq, bq, cq);
         }
@@ -341,9 +408,11 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
       logit[f][0] = fmaf(cq[0] + cq[1], ek, biasA);
       logit[f][1] = fmaf(cq[2] + cq[3], ek, biasB);
     }
+    // the key registers are free: fetch the next group's keys
+    if (PREFETCH) load_keys<BITS>(a, head, gn, n, kq, pc, pkq, kl);
 
     // ---- online softmax over the group (per head, this wave)
-    float mx[2];
+    float alpha[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       float v = logit[0][j];
@@ -351,12 +420,7 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
       for (int f = 1; f < NFRAG; ++f) v = fmaxf(v, logit[f][j]);
       v = wave_max16(v);
       if (GQA == 4) v = fmaxf(v, __shfl_xor(v, 32));
-      mx[j] = v;
-    }
-    float alpha[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float m_new = fmaxf(m_run[j], mx[j]);
+      const float m_new = fmaxf(m_run[j], v);
       alpha[j] = exp2f(m_run[j] - m_new);
       m_run[j] = m_new;
       float sum = 0.f;
@@ -369,7 +433,7 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
       }
       l_part[j] = l_part[j] * alpha[j] + sum;
     }
-    if (n == 0 && (GQA == 8 || rq < 2)) {
+    if (n == 0 && pv_rows) {
       L.alpha[hA] = alpha[0];
       L.alpha[hA + 1] = alpha[1];
     }
@@ -377,17 +441,17 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- value A operand: p s_t 2^(24-offset) 2^-E_V, hi/lo rows, via LDS
+    // ---- value A operand: p s_t 2^(24-offset) 2^-E_V as hi/lo rows, via LDS
     float vs[8];
     float vmax = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      vs[e] = h2f(vsb[e]);
+      vs[e] = chunk_elem(vl.vs, e);
       vmax = fmaxf(vmax, vs[e]);
     }
     vmax = wave_max16(vmax);
     const int e_v_new = max(e_v, ceil_exp(vmax) + 9);
-    const float vshift = exp2i(max(-126, min(127, e_v - e_v_new)));   // 0 on the first group
+    const float vshift = exp2i(max(-126, min(127, e_v - e_v_new)));
     const float sv = exp2i(max(-126, min(127, -e_v_new)));
     e_v = e_v_new;
 #pragma unroll
@@ -401,7 +465,7 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
         const int t = chunk_index<BITS>(pc, pkq, e);
         const float p = L.p[h][t];
         v[e] = p * vs[e] * exp2i(24 - code_offset<BITS>(t)) * sv;
-        mt = fmaf(p, h2f(vmb[e]), mt);
+        mt = fmaf(p, chunk_elem(vl.vm, e), mt);
       }
       mterm[j] = fmaf(mterm[j], al, mt);
       u32x4 hi, lo;
@@ -415,10 +479,8 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
 
     // ---- rescale the p.V accumulators (alpha and the exponent change)
     {
-      const bool real_rows = GQA == 8 || rq < 2;
-      const int h0 = GQA == 4 ? 2 * rq : 2 * rq;
-      const float f0 = real_rows ? L.alpha[h0] * vshift : 0.f;
-      const float f1 = real_rows ? L.alpha[h0 + 1] * vshift : 0.f;
+      const float f0 = pv_rows ? L.alpha[2 * rq] * vshift : 0.f;
+      const float f1 = pv_rows ? L.alpha[2 * rq + 1] * vshift : 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         acc[i][0] *= f0;
@@ -432,7 +494,7 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
     u32x4 apv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      apv[c] = (m_row < 2 * GQA) ? L.av[c][kq][m_row] : sh.main.zero;
+      apv[c] = (m_row < 2 * GQA) ? L.av[c][kq][m_row] : sh.u.main.zero;
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       const int e = blk >> 2, comp = blk & 3;
@@ -441,22 +503,30 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
         u32x4 bv;
         if (BITS == 2) {
           u32x4 q0, q1;
-          conv2(vwords[c >> 1][e][comp], q0, q1);
+          conv2(vl.vw[c >> 1][e][comp], q0, q1);
           bv = (c & 1) ? q1 : q0;
         } else {
-          bv = conv4(vwords[c][e][comp]);
+          bv = conv4(vl.vw[c][e][comp]);
         }
         acc[blk] = mfma(apv[c], bv, acc[blk]);
       }
     }
+    // the value registers are free: fetch the next group's values
+    if (PREFETCH) load_values<BITS>(a, head, gn, n, kq, pc, pkq, vl);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  int64_t g = gb + wave;
+  if (g < ge) {
+    load_keys<BITS>(a, head, g, n, kq, pc, pkq, kl);
+    load_values<BITS>(a, head, g, n, kq, pc, pkq, vl);
+    for (; g + kWaves < ge; g += kWaves) group_step(g, std::true_type{});
+    group_step(g, std::false_type{});
   }
 
-  // ---------------------------------------------------------------- merge waves
-  // per-head totals of this wave
-  float lsum[2], msave[2] = {m_run[0], m_run[1]};
+  // ---------------------------------------------------------------- block merge
+  float lsum[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float v = l_part[j];
@@ -478,10 +548,10 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
     mtsum[j] = v;
   }
   __syncthreads();   // the per-wave buffers are reused for the merge below
-  MergeLds<GQA>& M = sh.merge;
-  if (n == 0 && (GQA == 8 || rq < 2)) {
-    M.m[wave][hA] = msave[0];
-    M.m[wave][hA + 1] = msave[1];
+  MergeLds<GQA>& M = sh.u.merge;
+  if (n == 0 && pv_rows) {
+    M.m[wave][hA] = m_run[0];
+    M.m[wave][hA + 1] = m_run[1];
     M.l[wave][hA] = lsum[0];
     M.l[wave][hA + 1] = lsum[1];
   }
@@ -490,27 +560,30 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
     for (int j = 0; j < NH; ++j) M.mt[wave][ph + 4 * j] = mtsum[j];
   }
   __syncthreads();
-  {
-    const bool real_rows = GQA == 8 || rq < 2;
-    if (real_rows) {
-      const int h0 = 2 * rq;
-      const float ev = exp2i(max(-126, min(127, e_v)));
+  if (pv_rows) {
+    const int h0 = 2 * rq;
+    const float ev = exp2i(max(-126, min(127, e_v)));
 #pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
-        const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
-        M.num[wave][h0][d] = fmaf(acc[blk][0] + acc[blk][1], ev, M.mt[wave][h0]);
-        M.num[wave][h0 + 1][d] = fmaf(acc[blk][2] + acc[blk][3], ev, M.mt[wave][h0 + 1]);
-      }
+    for (int blk = 0; blk < 8; ++blk) {
+      const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
+      M.num[wave][h0][d] = fmaf(acc[blk][0] + acc[blk][1], ev, M.mt[wave][h0]);
+      M.num[wave][h0 + 1][d] = fmaf(acc[blk][2] + acc[blk][3], ev, M.mt[wave][h0 + 1]);
     }
   }
   __syncthreads();
+  const int n_parts = a.n_parts;
   for (int i = tid; i < GQA * kD; i += kThreadsM) {
     const int h = i / kD, d = i % kD;
-    float mm = kNegInfM;
+    float mm = sh.win.l[h] > 0.f ? sh.win.m[h] : kNegInfM;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
       if (M.l[w][h] > 0.f) mm = fmaxf(mm, M.m[w][h]);
     float num = 0.f, den = 0.f;
+    if (sh.win.l[h] > 0.f) {
+      const float f = exp2f(sh.win.m[h] - mm);
+      num = sh.win.acc[h][d] * f;
+      den = sh.win.l[h] * f;
+    }
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
       if (M.l[w][h] > 0.f) {
@@ -525,16 +598,13 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
       wp[1] = den;
     }
   }
+
 }
 
 }  // namespace
 
-bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
-  return group == kG && (gqa == 4 || gqa == 8) && n_boost == 0 && (bits == 2 || bits == 4);
-}
-
 hipError_t launch_decode_mfma(int bits, const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)(a.n_chunks + 1), (unsigned)(a.B * a.H_kv));
+  const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
   if (bits == 2) {
     if (a.gqa == 4) decode_mfma_kernel<2, 4><<<grid, kThreadsM, 0, st>>>(a);
     else decode_mfma_kernel<2, 8><<<grid, kThreadsM, 0, st>>>(a);

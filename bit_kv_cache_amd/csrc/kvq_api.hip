@@ -48,21 +48,36 @@ kvq::CacheArgs cache_args(const kvq_cache* c) {
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
-// Chunks per head: enough blocks to give every compute unit several, each
-// chunk at least one group; an explicit request is honoured up to one chunk
-// per group.
-int32_t plan_chunks(int64_t heads, int64_t n_groups, int32_t req) {
-  if (n_groups <= 0) return 0;
+// Chunks per head.  Vector-ALU kernel: enough blocks to give every compute
+// unit several (the fp16 windows are one more block per head).  Matrix-core
+// kernel: the resident block slots divided over the heads, so the grid runs
+// in a single round (windows are spread over the chunks; at least one chunk).
+// An explicit request is honoured up to one chunk per group (and 1023).
+constexpr int64_t kMaxChunks = 1023;  // the merge kernel holds <= 1024 part weights
+
+int32_t plan_chunks(bool mfma, int64_t heads, int64_t n_groups, int32_t req) {
   int64_t n;
   if (req > 0) {
     n = req;
+  } else if (mfma) {
+    n = kvq::kMfmaResidentBlocks / heads;
   } else {
     const int64_t target_blocks = 1024;  // 256 CUs x 4
     n = (target_blocks + heads - 1) / heads;
   }
   if (n > n_groups) n = n_groups;
-  if (n < 1) n = 1;
+  if (n > kMaxChunks) n = kMaxChunks;
+  if (n < 1) n = mfma ? 1 : (n_groups > 0 ? 1 : 0);
   return (int32_t)n;
+}
+
+size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Workspace: fp32 partials [B][H_q][parts][D+2].  Parts are the chunks, plus
+// the fp16-window part on the vector-ALU kernel (the matrix-core kernel
+// spreads the windows over its chunks).
+size_t partial_bytes(int64_t B, int64_t H_q, int64_t parts) {
+  return align16((size_t)B * H_q * parts * (kD + 2) * sizeof(float));
 }
 
 kvq_status check_window(const kvq_window* w) {
@@ -125,9 +140,10 @@ kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t 
     return KVQ_ERR_ARG;
   const int64_t heads = (int64_t)B * H_kv;
   if (heads > 65535) return KVQ_ERR_ARG;  // one grid row per (batch, kv head)
-  const int32_t n = plan_chunks(heads, n_quant_tokens / cfg->group, n_chunks_req);
+  const bool mfma = kvq::mfma_decode_supported(cfg->bits, cfg->group, gqa, cfg->n_boost);
+  const int32_t n = plan_chunks(mfma, heads, n_quant_tokens / cfg->group, n_chunks_req);
   if (n_chunks) *n_chunks = n;
-  if (ws_bytes) *ws_bytes = (size_t)B * H_q * (size_t)(n + 1) * (kD + 2) * sizeof(float);
+  if (ws_bytes) *ws_bytes = partial_bytes(B, H_q, mfma ? n : n + 1);
   return KVQ_OK;
 }
 
@@ -183,6 +199,7 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
   }
   a.qscale = sm_scale * 1.4426950408889634f;
   a.ws = static_cast<float*>(workspace);
+  a.n_parts = kvq::mfma_decode_supported(cfg->bits, cfg->group, a.gqa, cfg->n_boost) ? nc : nc + 1;
   a.out = out;
   return hip_status(kvq::launch_decode(cfg->bits, cfg->group, a, static_cast<hipStream_t>(stream)));
 }

@@ -78,15 +78,24 @@ struct DecodeArgs {
   const uint16_t* v_res;
   int32_t n_res, res_cap;
   float qscale;            // sm_scale * log2(e): logits kept in the log2 domain
-  float* ws;               // partials [B][H_q][n_chunks+1][D+2]
+  int32_t n_parts;         // partials per (batch, query head)
+  float* ws;               // partials [B][H_q][n_parts][D+2]
   float* out;              // [B][H_q][D]
 };
+
+// The matrix-core decode kernel serves GQA groups of 4 or 8 heads with G = 128
+// and plain (non-boosted) codes; everything else takes the vector-ALU kernel.
+inline bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
+  return group == 128 && (gqa == 4 || gqa == 8) && n_boost == 0 && (bits == 2 || bits == 4);
+}
+// Resident blocks of the matrix-core kernel on MI355X: 256 CUs x 2 blocks of
+// 4 waves (<= 256 VGPRs per lane -> 2 waves per SIMD).
+constexpr int kMfmaResidentBlocks = 256 * 2;
 
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
 hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStream_t s);
 hipError_t launch_decode(int bits, int group, const DecodeArgs& a, hipStream_t s);
-bool mfma_decode_supported(int bits, int group, int gqa, int n_boost);
 hipError_t launch_decode_mfma(int bits, const DecodeArgs& a, hipStream_t s);
 
 }  // namespace kvq

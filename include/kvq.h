@@ -134,15 +134,16 @@ kvq_status kvq_quantize_pack(const kvq_qcfg* cfg, const kvq_cache* cache, int32_
                              void* stream);
 
 /* Split plan of a decode step: the number of token chunks per head
- * (n_chunks_req > 0 is honoured up to one chunk per group; 0 picks a count
- * that fills the GPU) and the workspace size in bytes it needs. */
+ * (n_chunks_req > 0 is honoured up to one chunk per group and at most 1023;
+ * 0 picks a count that fills the GPU) and the workspace size in bytes it needs. */
 kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t H_kv,
                            int64_t n_quant_tokens, int32_t n_chunks_req, int32_t* n_chunks,
                            size_t* ws_bytes);
 
 /* Workspace bytes of kvq_decode_attention for the same arguments (0 on a bad
- * argument).  Partials are fp32 (m, l, acc[D]) per (batch, query head, part),
- * part = chunk or the fp16 windows. */
+ * argument): fp32 partials (m, l, acc[D]) per (batch, query head, part).  The
+ * contents need no initialization; calls that share a workspace must not
+ * overlap in time. */
 size_t kvq_decode_workspace_bytes(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t H_kv,
                                   int64_t n_quant_tokens, int32_t n_chunks_req);
 

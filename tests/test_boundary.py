@@ -113,13 +113,19 @@ def test_decode_rejects_bad_arguments():
 
 def test_decode_plan():
     cfg = kvq.QCfg(bits=2, group=128)
-    # auto: ~1024 blocks over the heads, at most one chunk per group
-    assert kvq.kvq_decode_plan(cfg, 8, 32, 8, 32768)[0] == 16
-    assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 1 << 20)[0] == 128
+    # matrix-core path (GQA 4/8, G 128): 512 resident blocks over the heads
+    assert kvq.kvq_decode_plan(cfg, 8, 32, 8, 32768)[0] == 8
+    assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 1 << 20)[0] == 64
     assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 1 << 20, 256)[0] == 256
+    assert kvq.kvq_decode_plan(cfg, 32, 32, 8, 8192)[0] == 2
+    assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 0)[0] == 1      # windows only: one chunk
+    nc, ws = kvq.kvq_decode_plan(cfg, 8, 32, 8, 32768)
+    assert ws >= 8 * 32 * nc * 130 * 4
+    # vector-ALU path (MHA): ~1024 blocks, at most one chunk per group
     assert kvq.kvq_decode_plan(cfg, 1, 1, 1, 512)[0] == 4
     assert kvq.kvq_decode_plan(cfg, 1, 1, 1, 0)[0] == 0
-    nc, ws = kvq.kvq_decode_plan(cfg, 8, 32, 8, 32768)
-    assert ws >= 8 * 32 * (nc + 1) * 130 * 4
+    assert kvq.kvq_decode_plan(kvq.QCfg(bits=2, group=64), 8, 32, 8, 32768)[0] == 16
     assert kvq.kvq_decode_workspace_bytes(cfg, 8, 32, 8, 32768) == ws
+    nc, ws = kvq.kvq_decode_plan(cfg, 1, 1, 1, 512)
+    assert ws >= (nc + 1) * 130 * 4
     assert kvq.kvq_decode_workspace_bytes(kvq.QCfg(bits=3), 8, 32, 8, 32768) == 0
