@@ -55,13 +55,13 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c) {
                                                 __builtin_bit_cast(half8, b), c, 0, 0, 0);
 }
 
-// 2-bit word (codes 0..15 at bits 2i) -> two operand quads.  Element pairs
-// (lo half, hi half): j=0..7 -> codes (j, j+8) at in-half bit offset
-// p(j) = {0,2,4,6,8,0,2,4}; quad q0 holds j = 0..3, quad q1 holds j = 4..7.
-__device__ __forceinline__ void conv2(uint32_t w, u32x4& q0, u32x4& q1) {
+// 2-bit word (codes 0..15 at bits 2i) -> operand quad q (0 or 1).  Element
+// pairs (lo half, hi half) j = 0..7 hold codes (j, j+8) at in-half bit
+// offset p(j) = {0,2,4,6,8,0,2,4}; quad 0 holds j = 0..3, quad 1 j = 4..7.
+__device__ __forceinline__ u32x4 conv2_q(uint32_t w, int q) {
+  if (q == 0) return u32x4{w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u};
   const uint32_t s = w >> 10;
-  q0 = u32x4{w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u};
-  q1 = u32x4{w & 0x03000300u, s & 0x00030003u, s & 0x000C000Cu, s & 0x00300030u};
+  return u32x4{w & 0x03000300u, s & 0x00030003u, s & 0x000C000Cu, s & 0x00300030u};
 }
 
 // 4-bit word (codes 0..7 at bits 4i) -> one operand quad: pair r holds codes
@@ -112,13 +112,33 @@ __device__ __forceinline__ void split_hilo(const float (&v)[8], u32x4& hi, u32x4
   }
 }
 
-__device__ __forceinline__ float wave_max16(float v) {  // over the 16 lanes of a row
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  return fmaxf(v, __shfl_xor(v, 8));
+// DPP lane moves (VALU, no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
 }
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadXor2 = 0x4E, kQuadXor1 = 0xB1;
 
+// max / sum over the 16 lanes of a row (every lane gets the result)
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<kRowRor8>(v));
+  v = fmaxf(v, dpp<kRowRor4>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  return fmaxf(v, dpp<kQuadXor1>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<kRowRor8>(v);
+  v += dpp<kRowRor4>(v);
+  v += dpp<kQuadXor2>(v);
+  return v + dpp<kQuadXor1>(v);
+}
+// value of lane l ^ 32 (gfx950 v_permlane32_swap)
+__device__ __forceinline__ float xor32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 template <int BITS>
 struct KeyLoad {
@@ -139,49 +159,64 @@ struct ValueLoad {
 template <int BITS>
 __device__ __forceinline__ int run_stride() { return BITS == 2 ? 8 : 4; }
 
+// Per-lane byte offsets of a wave's loads inside one group (uniform bases
+// come from the group index; lane offsets stay 32-bit).
 template <int BITS>
-__device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int64_t g, int n,
-                                          int kq, int pc, int pkq, KeyLoad<BITS>& L) {
+struct LaneOffsets {
+  uint32_t kw;      // key words of tile 0 (tile t adds 16 * t * WPT * 4)
+  uint32_t kmeta;   // key scale run 0 inside the group's [D] row
+  uint32_t kmin;    // key minima of K-step 0 (natural order) inside that row
+  uint32_t vw;      // value words (row VR*kq, channel 4n)
+  uint32_t vmeta;   // value scale/min run 0 inside the group's [G] tokens
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int64_t g,
+                                          const LaneOffsets<BITS>& o, KeyLoad<BITS>& L) {
   constexpr int WPT = kD / (32 / BITS);
-  const uint32_t* kb = reinterpret_cast<const uint32_t*>(a.c.k_codes) +
-                       (head * a.c.t_cap + g * kG + n) * WPT + KeyLoad<BITS>::KW * kq;
+  const char* kb = reinterpret_cast<const char*>(a.c.k_codes) +
+                   (head * a.c.t_cap + g * kG) * WPT * 4 + o.kw;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     if (BITS == 2) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(kb + 16 * t * WPT);
+      const u32x2 v = *reinterpret_cast<const u32x2*>(kb + 16 * t * WPT * 4);
       L.kw[t][0] = v[0];
       L.kw[t][1] = v[1];
     } else {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(kb + 16 * t * WPT);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(kb + 16 * t * WPT * 4);
 #pragma unroll
       for (int i = 0; i < KeyLoad<BITS>::KW; ++i) L.kw[t][i] = v[i];
     }
   }
-  const int64_t kmeta = (head * (a.c.t_cap / kG) + g) * kD;
+  const char* km = reinterpret_cast<const char*>(a.c.k_min) +
+                   (head * (a.c.t_cap / kG) + g) * kD * 2 + o.kmin;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    L.kmin[c] = *reinterpret_cast<const u32x4*>(a.c.k_min + kmeta + 32 * c + 8 * kq);
-  const int base = chunk_index<BITS>(pc, pkq, 0);
-  L.ks[0] = *reinterpret_cast<const u32x2*>(a.c.k_scale + kmeta + base);
-  L.ks[1] = *reinterpret_cast<const u32x2*>(a.c.k_scale + kmeta + base + run_stride<BITS>());
+  for (int c = 0; c < 4; ++c) L.kmin[c] = *reinterpret_cast<const u32x4*>(km + 64 * c);
+  const char* ks = reinterpret_cast<const char*>(a.c.k_scale) +
+                   (head * (a.c.t_cap / kG) + g) * kD * 2 + o.kmeta;
+  L.ks[0] = *reinterpret_cast<const u32x2*>(ks);
+  L.ks[1] = *reinterpret_cast<const u32x2*>(ks + 2 * run_stride<BITS>());
 }
 
 template <int BITS>
-__device__ __forceinline__ void load_values(const DecodeArgs& a, int64_t head, int64_t g, int n,
-                                            int kq, int pc, int pkq, ValueLoad<BITS>& L) {
+__device__ __forceinline__ void load_values(const DecodeArgs& a, int64_t head, int64_t g,
+                                            const LaneOffsets<BITS>& o, ValueLoad<BITS>& L) {
   constexpr int FPI = 32 / BITS;
   constexpr int VR = ValueLoad<BITS>::VR;
-  const uint32_t* vb = reinterpret_cast<const uint32_t*>(a.c.v_codes) +
-                       (head * (a.c.t_cap / FPI) + g * (kG / FPI) + VR * kq) * kD + 4 * n;
+  const char* vb = reinterpret_cast<const char*>(a.c.v_codes) +
+                   (head * (a.c.t_cap / FPI) + g * (kG / FPI)) * kD * 4 + o.vw;
 #pragma unroll
   for (int i = 0; i < VR; ++i)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) L.vw[i][e] = *reinterpret_cast<const u32x4*>(vb + i * kD + 64 * e);
-  const int64_t t0 = head * a.c.t_cap + g * kG + chunk_index<BITS>(pc, pkq, 0);
-  L.vs[0] = *reinterpret_cast<const u32x2*>(a.c.v_scale + t0);
-  L.vs[1] = *reinterpret_cast<const u32x2*>(a.c.v_scale + t0 + run_stride<BITS>());
-  L.vm[0] = *reinterpret_cast<const u32x2*>(a.c.v_min + t0);
-  L.vm[1] = *reinterpret_cast<const u32x2*>(a.c.v_min + t0 + run_stride<BITS>());
+    for (int e = 0; e < 2; ++e)
+      L.vw[i][e] = *reinterpret_cast<const u32x4*>(vb + (i * kD + 64 * e) * 4);
+  const int64_t t0 = (head * a.c.t_cap + g * kG) * 2;
+  const char* vs = reinterpret_cast<const char*>(a.c.v_scale) + t0 + o.vmeta;
+  const char* vm = reinterpret_cast<const char*>(a.c.v_min) + t0 + o.vmeta;
+  L.vs[0] = *reinterpret_cast<const u32x2*>(vs);
+  L.vs[1] = *reinterpret_cast<const u32x2*>(vs + 2 * run_stride<BITS>());
+  L.vm[0] = *reinterpret_cast<const u32x2*>(vm);
+  L.vm[1] = *reinterpret_cast<const u32x2*>(vm + 2 * run_stride<BITS>());
 }
 
 // fp16 element e (= 2r + half) of an A-prep chunk from its two 4-element runs
@@ -197,6 +232,7 @@ struct WaveLds {
   u32x4 av[4][4][ROWS];                            // value A operand [c][kq][row]
   float p[GQA][kG];                                // probabilities of the group
   float alpha[GQA];
+  f32x4 qhat[GQA / 4][64][2];                      // scaled query of the A-prep lanes
 };
 
 template <int GQA>
@@ -222,17 +258,19 @@ struct MfmaLds {
     Lds<GQA> window;
   } u;
   WindowResult<GQA> win;
+  u32x4 bias_a[4][4][16];                          // bias A operand [c][kq][row]
 };
 
 template <int BITS, int GQA>
-__global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreadsM, kMfmaBlocksPerCU<GQA>) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int TPC = GQA == 4 ? 2 : 1;  // tiles per QK accumulator (row slots)
   constexpr int NFRAG = 8 / TPC;         // QK accumulators per group
   constexpr int NH = GQA / 4;            // A-prep heads per lane (1 or 2)
   __shared__ MfmaLds<GQA> sh;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, kq = lane >> 4;   // operand lane coordinates
   const int chunk = blockIdx.x;
   const int64_t head = blockIdx.y;
@@ -287,36 +325,36 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
   // this lane's A-prep heads and chunk (c, kq)
   const int ph = lane >> 4;
   const int pc = lane & 3, pkq = (lane >> 2) & 3;
-  float qhat[NH][8];                        // q * sm * log2e * 2^(24 - offset)
+  // q * sm * log2e * 2^(24 - offset) of this lane's A-prep elements, in LDS
   float qmax = 0.f;
 #pragma unroll
   for (int j = 0; j < NH; ++j) {
+    float qh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int ch = chunk_index<BITS>(pc, pkq, e);
       const float qv = h2f(qrow[(ph + 4 * j) * kD + ch]) * a.qscale;
-      qhat[j][e] = qv * exp2i(24 - code_offset<BITS>(ch));
-      qmax = fmaxf(qmax, fabsf(qhat[j][e]));
+      qh[e] = qv * exp2i(24 - code_offset<BITS>(ch));
+      qmax = fmaxf(qmax, fabsf(qh[e]));
     }
+    L.qhat[j][lane][0] = f32x4{qh[0], qh[1], qh[2], qh[3]};
+    L.qhat[j][lane][1] = f32x4{qh[4], qh[5], qh[6], qh[7]};
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, o));
   const int e_q = ceil_exp(qmax);
 
-  // bias operand: hi/lo of q*sm*log2e in natural channel order, rows (head, hi/lo)
-  u32x4 abias[4];
+  // bias operand: hi/lo of q*sm*log2e in natural channel order, rows (head,
+  // hi/lo); built once per block in LDS (wave w builds K-step w)
   {
-    const int m = lane & 15;
+    const int m = lane & 15, c = wave;
     const int h = (m % (2 * GQA)) >> 1, hl = m & 1;
+    float v[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = h2f(qrow[h * kD + 32 * c + 8 * kq + e]) * a.qscale;
-      u32x4 hi, lo;
-      split_hilo(v, hi, lo);
-      abias[c] = hl ? lo : hi;
-    }
+    for (int e = 0; e < 8; ++e) v[e] = h2f(qrow[h * kD + 32 * c + 8 * kq + e]) * a.qscale;
+    u32x4 hi, lo;
+    split_hilo(v, hi, lo);
+    sh.bias_a[c][kq][m] = hl ? lo : hi;
   }
 
   // per-wave online softmax state: this lane's QK heads hA, hA + 1
@@ -333,8 +371,30 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int m_row = lane & 15;
+  // LDS address of this lane's A operand chunk (K-step 0), per row slot; lanes
+  // whose rows are unused in a slot read the zero block instead
+  const u32x4* ak_ptr[TPC];
+  int ak_step[TPC];                         // K-step stride (0 on the zero block)
+#pragma unroll
+  for (int slot = 0; slot < TPC; ++slot) {
+    const bool mine = TPC == 1 || (m_row >> 3) == slot;
+    ak_ptr[slot] = mine ? &L.ak[0][kq][TPC == 1 ? m_row : (m_row & 7)] : &sh.u.main.zero;
+    ak_step[slot] = mine ? 4 * WaveLds<GQA>::ROWS : 0;
+  }
+  const bool av_mine = m_row < 2 * GQA;
+  const u32x4* av_ptr = av_mine ? &L.av[0][kq][m_row] : &sh.u.main.zero;
+  const int av_step = av_mine ? 4 * WaveLds<GQA>::ROWS : 0;
   __syncthreads();
 
+  LaneOffsets<BITS> lo;
+  {
+    constexpr int WPT = kD / (32 / BITS);
+    lo.kw = (uint32_t)((n * WPT + KeyLoad<BITS>::KW * kq) * 4);
+    lo.kmeta = (uint32_t)(chunk_index<BITS>(pc, pkq, 0) * 2);
+    lo.vw = (uint32_t)((ValueLoad<BITS>::VR * kq * kD + 4 * n) * 4);
+    lo.vmeta = lo.kmeta;
+    lo.kmin = (uint32_t)(8 * kq * 2);
+  }
   KeyLoad<BITS> kl;
   ValueLoad<BITS> vl;
   // One group of this wave.  With PREFETCH the next group's keys are fetched
@@ -352,14 +412,16 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
       ks[e] = chunk_elem(kl.ks, e);
       smax = fmaxf(smax, ks[e]);
     }
-    smax = wave_max16(smax);
+    smax = row_max16(smax);
     const int e_k = e_q + ceil_exp(smax) - 15;
     const float sk = exp2i(max(-126, min(127, -e_k)));
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
+      const f32x4 q0 = L.qhat[j][lane][0], q1 = L.qhat[j][lane][1];
+      const float qh[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = qhat[j][e] * ks[e] * sk;
+      for (int e = 0; e < 8; ++e) v[e] = qh[e] * ks[e] * sk;
       u32x4 hi, lo;
       split_hilo(v, hi, lo);
       const int h = ph + 4 * j;
@@ -370,46 +432,40 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- bias: sum_d q_d mn_d per head
+    // ---- bias: sum_d q_d mn_d per head (key minima in natural channel order)
     f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) cb = mfma(abias[c], kl.kmin[c], cb);
+    for (int c = 0; c < 4; ++c) cb = mfma(sh.bias_a[c][kq][m_row], kl.kmin[c], cb);
     const float biasA = cb[0] + cb[1], biasB = cb[2] + cb[3];
 
     // ---- q.K^T
     const float ek = exp2i(max(-126, min(127, e_k)));
     float logit[NFRAG][2];
+    {
+      f32x4 cq[NFRAG];
 #pragma unroll
-    for (int f = 0; f < NFRAG; ++f) {
-      f32x4 cq = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < NFRAG; ++f) cq[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int slot = 0; slot < TPC; ++slot) {
-        const int t = f * TPC + slot;
+      for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          u32x4 bq;
-          if (BITS == 2) {
-            u32x4 q0, q1;
-            conv2(kl.kw[t][c >> 1], q0, q1);
-            bq = (c & 1) ? q1 : q0;
-          } else {
-            bq = conv4(kl.kw[t][c]);
+        for (int slot = 0; slot < TPC; ++slot) {
+          const u32x4 aq = *(ak_ptr[slot] + c * ak_step[slot]);
+#pragma unroll
+          for (int f = 0; f < NFRAG; ++f) {
+            const int t = f * TPC + slot;
+            const u32x4 bq = BITS == 2 ? conv2_q(kl.kw[t][c >> 1], c & 1) : conv4(kl.kw[t][c]);
+            cq[f] = mfma(aq, bq, cq[f]);
           }
-          u32x4 aq;
-          if (TPC == 1) {
-            aq = L.ak[c][kq][m_row];
-          } else {
-            const bool mine = (m_row >> 3) == slot;
-            aq = mine ? L.ak[c][kq][m_row & 7] : sh.u.main.zero;
-          }
-          cq = mfma(aq, bq, cq);
         }
       }
-      logit[f][0] = fmaf(cq[0] + cq[1], ek, biasA);
-      logit[f][1] = fmaf(cq[2] + cq[3], ek, biasB);
+#pragma unroll
+      for (int f = 0; f < NFRAG; ++f) {
+        logit[f][0] = fmaf(cq[f][0] + cq[f][1], ek, biasA);
+        logit[f][1] = fmaf(cq[f][2] + cq[f][3], ek, biasB);
+      }
     }
     // the key registers are free: fetch the next group's keys
-    if (PREFETCH) load_keys<BITS>(a, head, gn, n, kq, pc, pkq, kl);
+    if (PREFETCH) load_keys<BITS>(a, head, gn, lo, kl);
 
     // ---- online softmax over the group (per head, this wave)
     float alpha[2];
@@ -418,8 +474,8 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
       float v = logit[0][j];
 #pragma unroll
       for (int f = 1; f < NFRAG; ++f) v = fmaxf(v, logit[f][j]);
-      v = wave_max16(v);
-      if (GQA == 4) v = fmaxf(v, __shfl_xor(v, 32));
+      v = row_max16(v);
+      if (GQA == 4) v = fmaxf(v, xor32(v));
       const float m_new = fmaxf(m_run[j], v);
       alpha[j] = exp2f(m_run[j] - m_new);
       m_run[j] = m_new;
@@ -449,7 +505,7 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
       vs[e] = chunk_elem(vl.vs, e);
       vmax = fmaxf(vmax, vs[e]);
     }
-    vmax = wave_max16(vmax);
+    vmax = row_max16(vmax);
     const int e_v_new = max(e_v, ceil_exp(vmax) + 9);
     const float vshift = exp2i(max(-126, min(127, e_v - e_v_new)));
     const float sv = exp2i(max(-126, min(127, -e_v_new)));
@@ -481,46 +537,38 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
     {
       const float f0 = pv_rows ? L.alpha[2 * rq] * vshift : 0.f;
       const float f1 = pv_rows ? L.alpha[2 * rq + 1] * vshift : 0.f;
+      if (!__all((f0 == 1.f && f1 == 1.f) || !pv_rows)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[i][0] *= f0;
-        acc[i][1] *= f0;
-        acc[i][2] *= f1;
-        acc[i][3] *= f1;
+        for (int i = 0; i < 8; ++i) {
+          acc[i][0] *= f0;
+          acc[i][1] *= f0;
+          acc[i][2] *= f1;
+          acc[i][3] *= f1;
+        }
       }
     }
 
     // ---- p.V
-    u32x4 apv[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      apv[c] = (m_row < 2 * GQA) ? L.av[c][kq][m_row] : sh.u.main.zero;
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 apv = *(av_ptr + c * av_step);
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-      const int e = blk >> 2, comp = blk & 3;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 bv;
-        if (BITS == 2) {
-          u32x4 q0, q1;
-          conv2(vl.vw[c >> 1][e][comp], q0, q1);
-          bv = (c & 1) ? q1 : q0;
-        } else {
-          bv = conv4(vl.vw[c][e][comp]);
-        }
-        acc[blk] = mfma(apv[c], bv, acc[blk]);
+      for (int blk = 0; blk < 8; ++blk) {
+        const int e = blk >> 2, comp = blk & 3;
+        const u32x4 bv = BITS == 2 ? conv2_q(vl.vw[c >> 1][e][comp], c & 1) : conv4(vl.vw[c][e][comp]);
+        acc[blk] = mfma(apv, bv, acc[blk]);
       }
     }
     // the value registers are free: fetch the next group's values
-    if (PREFETCH) load_values<BITS>(a, head, gn, n, kq, pc, pkq, vl);
+    if (PREFETCH) load_values<BITS>(a, head, gn, lo, vl);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   int64_t g = gb + wave;
   if (g < ge) {
-    load_keys<BITS>(a, head, g, n, kq, pc, pkq, kl);
-    load_values<BITS>(a, head, g, n, kq, pc, pkq, vl);
+    load_keys<BITS>(a, head, g, lo, kl);
+    load_values<BITS>(a, head, g, lo, vl);
     for (; g + kWaves < ge; g += kWaves) group_step(g, std::true_type{});
     group_step(g, std::false_type{});
   }
@@ -529,23 +577,14 @@ __global__ __launch_bounds__(kThreadsM, 2) void decode_mfma_kernel(DecodeArgs a)
   float lsum[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    float v = l_part[j];
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    if (GQA == 4) v += __shfl_xor(v, 32);
+    float v = row_sum16(l_part[j]);
+    if (GQA == 4) v += xor32(v);
     lsum[j] = v;
   }
   float mtsum[NH];
 #pragma unroll
   for (int j = 0; j < NH; ++j) {
-    float v = mterm[j];
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    mtsum[j] = v;
+    mtsum[j] = row_sum16(mterm[j]);
   }
   __syncthreads();   // the per-wave buffers are reused for the merge below
   MergeLds<GQA>& M = sh.u.merge;

@@ -88,9 +88,14 @@ struct DecodeArgs {
 inline bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
   return group == 128 && (gqa == 4 || gqa == 8) && n_boost == 0 && (bits == 2 || bits == 4);
 }
-// Resident blocks of the matrix-core kernel on MI355X: 256 CUs x 2 blocks of
-// 4 waves (<= 256 VGPRs per lane -> 2 waves per SIMD).
-constexpr int kMfmaResidentBlocks = 256 * 2;
+// Resident blocks (of 4 waves) per CU of the matrix-core kernel: GQA-4
+// variants fit 3 waves per SIMD (<= 168 VGPRs), GQA-8 variants 2 (LDS).
+template <int GQA>
+constexpr int kMfmaBlocksPerCU = GQA == 4 ? 2 : 2;
+constexpr int kCUs = 256;  // MI355X
+inline int mfma_resident_blocks(int gqa) {
+  return kCUs * (gqa == 4 ? kMfmaBlocksPerCU<4> : kMfmaBlocksPerCU<8>);
+}
 
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
 hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s);

@@ -12,6 +12,11 @@
 // rounded division), fp16 scale rounded to nearest even, codes divide by the
 // stored scale, clamp, then round half to even (v_rndne_f32); min/max by the
 // total order -0 < +0.  No floating-point contraction in this file.
+//
+// Work split: every (head, group) is cut into 4 key slices of 32 channels and
+// up to 4 value slices of whole packed words of tokens, one block each, so a
+// one-group append over 64 heads already fills the GPU.  Kitty keys need the ranking of all channels
+// of a group, so with n_boost > 0 one block quantizes the whole key group.
 
 #include "kvq_internal.h"
 
@@ -21,6 +26,7 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSlices = 4;
 
 __device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float maxq) {
   if (s == 0.0f) return 0u;
@@ -29,159 +35,255 @@ __device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float
   return (uint32_t)__builtin_rintf(y);
 }
 
-// One block quantizes one (head, group) of keys (blockIdx.y == 0) or values
-// (blockIdx.y == 1).  The fp16 source tile [G][D] is staged in LDS.
+__device__ __forceinline__ uint32_t wave_min(uint32_t v, int width) {
+  for (int o = 1; o < width; o <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v, int width) {
+  for (int o = 1; o < width; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// Keys, channels [32*slice, 32*slice+32) of one group (plain KIVI).
 template <int BITS, int G>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+__device__ void quantize_keys_slice(const QuantArgs& a, int64_t head, int64_t gi, int slice) {
   constexpr int FPI = 32 / BITS;
   constexpr uint32_t MASK = (1u << BITS) - 1u;
   constexpr int WPT = kD / FPI;          // key words per token
-  __shared__ uint16_t tile[G * kD];
-  __shared__ float s_mn[kD];             // keys: per channel; values: per (token, chan group)
-  __shared__ float s_sc[kD];
-  __shared__ float s_mq[kD];             // keys: maxq of each channel (3 or 15 with boost)
-  __shared__ float s_rng[kD];
-  __shared__ int s_flag[kD];             // keys: channel is boosted (Kitty)
-  __shared__ int s_chan_of_row[kD];
-  __shared__ uint32_t s_red[2][kD];
-
+  constexpr int CH = kD / kSlices;       // 32 channels
+  constexpr int SW = CH / FPI;           // words per token in this slice
+  __shared__ uint16_t tile[G][CH + 2];   // +2: odd row pitch in dwords
+  __shared__ uint32_t red[2][8][CH];
+  __shared__ float s_mn[CH], s_sc[CH];
   const int tid = threadIdx.x;
-  const int64_t blk = blockIdx.x;
-  const int64_t head = blk / a.n_groups;
-  const int64_t gi = blk % a.n_groups;          // group index inside the source
-  const int64_t g = a.first_group + gi;         // group index in the cache
-  const bool is_v = blockIdx.y != 0;
-  const uint16_t* src = (is_v ? a.v_src : a.k_src) + head * a.src_head_stride + gi * G * kD;
+  const int64_t g = a.first_group + gi;
+  const uint16_t* src = a.k_src + head * a.src_head_stride + gi * G * kD + slice * CH;
+  // stage: each row contributes 64 bytes (4 x 16 B)
+  for (int i = tid; i < G * 4; i += kThreads) {
+    const int t = i >> 2, q = i & 3;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + t * kD + 8 * q);
+    uint32_t* d = reinterpret_cast<uint32_t*>(&tile[t][8 * q]);
+    d[0] = v.x, d[1] = v.y, d[2] = v.z, d[3] = v.w;
+  }
+  __syncthreads();
+  // min/max per channel: 8 token parts of G/8
+  {
+    const int c = tid & (CH - 1), part = tid >> 5;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int t = part * (G / 8); t < (part + 1) * (G / 8); ++t) {
+      const uint32_t k = order_key(tile[t][c]);
+      lo = min(lo, k);
+      hi = max(hi, k);
+    }
+    red[0][part][c] = lo;
+    red[1][part][c] = hi;
+  }
+  __syncthreads();
+  if (tid < CH) {
+    uint32_t lo = red[0][0][tid], hi = red[1][0][tid];
+#pragma unroll
+    for (int p = 1; p < 8; ++p) {
+      lo = min(lo, red[0][p][tid]);
+      hi = max(hi, red[1][p][tid]);
+    }
+    const float mn = h2f(from_order_key(lo));
+    const float mx = h2f(from_order_key(hi));
+    const uint16_t sh = f2h((mx - mn) / (float)MASK);
+    const int64_t m_off = (head * (a.c.t_cap / G) + g) * kD + slice * CH + tid;
+    a.c.k_scale[m_off] = sh;
+    a.c.k_min[m_off] = from_order_key(lo);
+    s_mn[tid] = mn;
+    s_sc[tid] = h2f(sh);
+  }
+  __syncthreads();
+  // codes, packed along channels: word (t, w) holds channels w*FPI + j
+  uint32_t* kw = a.c.k_codes + (head * a.c.t_cap + g * G) * WPT + slice * SW;
+  for (int i = tid; i < G * SW; i += kThreads) {
+    const int t = i / SW, w = i % SW;
+    uint32_t word = 0u;
+#pragma unroll
+    for (int j = 0; j < FPI; ++j) {
+      const int c = w * FPI + j;
+      word |= quant_code(h2f(tile[t][c]), s_mn[c], s_sc[c], (float)MASK) << (BITS * j);
+    }
+    kw[t * WPT + w] = word;
+  }
+}
 
-  // stage the tile: 16-byte loads
+// Keys of one whole group with the Kitty boost (2-bit, n_boost > 0).
+template <int G>
+__device__ void quantize_keys_kitty(const QuantArgs& a, int64_t head, int64_t gi) {
+  constexpr int BITS = 2, FPI = 16, WPT = kD / FPI;
+  constexpr uint32_t MASK = 3u;
+  __shared__ uint16_t tile[G * kD];
+  __shared__ float s_mn[kD], s_sc[kD], s_mq[kD], s_rng[kD];
+  __shared__ int s_flag[kD], s_chan_of_row[kD];
+  __shared__ uint32_t s_red[2][kD];
+  const int tid = threadIdx.x;
+  const int64_t g = a.first_group + gi;
+  const int nb = a.n_boost;
+  const uint16_t* src = a.k_src + head * a.src_head_stride + gi * G * kD;
   {
     const uint4* s4 = reinterpret_cast<const uint4*>(src);
     uint4* t4 = reinterpret_cast<uint4*>(tile);
     for (int i = tid; i < G * kD / 8; i += kThreads) t4[i] = s4[i];
   }
   __syncthreads();
-
-  if (!is_v) {
-    // ---- keys: min/max per channel over G tokens (two threads per channel)
-    const int d = tid & (kD - 1), half = tid >> 7;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int j = half * (G / 2); j < (half + 1) * (G / 2); ++j) {
-      const uint32_t k = order_key(tile[j * kD + d]);
-      lo = min(lo, k);
-      hi = max(hi, k);
+  const int d = tid & (kD - 1), half = tid >> 7;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int j = half * (G / 2); j < (half + 1) * (G / 2); ++j) {
+    const uint32_t k = order_key(tile[j * kD + d]);
+    lo = min(lo, k);
+    hi = max(hi, k);
+  }
+  if (half) {
+    s_red[0][d] = lo;
+    s_red[1][d] = hi;
+  }
+  __syncthreads();
+  if (!half) {
+    lo = min(lo, s_red[0][d]);
+    hi = max(hi, s_red[1][d]);
+    const float mn = h2f(from_order_key(lo));
+    s_mn[d] = mn;
+    s_rng[d] = h2f(from_order_key(hi)) - mn;
+  }
+  __syncthreads();
+  if (!half) {
+    // rank by range, ties to the lower channel
+    const float r = s_rng[d];
+    int rank = 0;
+    for (int c = 0; c < kD; ++c) {
+      const float rc = s_rng[c];
+      rank += (rc > r) || (rc == r && c < d);
     }
-    if (half) {
-      s_red[0][d] = lo;
-      s_red[1][d] = hi;
+    s_flag[d] = rank < nb;
+  }
+  __syncthreads();
+  if (!half) {
+    int row = nb;  // sentinel: not boosted
+    if (s_flag[d]) {
+      row = 0;  // boosted rows ascend with the channel index
+      for (int c = 0; c < d; ++c) row += s_flag[c];
     }
-    __syncthreads();
-    const int nb = a.n_boost;
-    if (!half) {
-      lo = min(lo, s_red[0][d]);
-      hi = max(hi, s_red[1][d]);
-      const float mn = h2f(from_order_key(lo));
-      const float mx = h2f(from_order_key(hi));
-      s_mn[d] = mn;
-      s_rng[d] = mx - mn;
-    }
-    __syncthreads();
-    if (!half && nb > 0) {
-      // Kitty: rank by range, ties to the lower channel
-      const float r = s_rng[d];
-      int rank = 0;
-      for (int c = 0; c < kD; ++c) {
-        const float rc = s_rng[c];
-        rank += (rc > r) || (rc == r && c < d);
-      }
-      s_flag[d] = rank < nb;
-    }
-    __syncthreads();
-    if (!half) {
-      int row = nb;  // sentinel: not boosted
-      if (nb > 0 && s_flag[d]) {
-        row = 0;  // boosted rows ascend with the channel index
-        for (int c = 0; c < d; ++c) row += s_flag[c];
-      }
-      const float maxq = (row < nb) ? 15.0f : (float)MASK;
-      const uint16_t sh = f2h(s_rng[d] / maxq);
-      const int64_t m_off = (head * (a.c.t_cap / G) + g) * kD + d;
-      a.c.k_scale[m_off] = sh;
-      a.c.k_min[m_off] = from_order_key(lo);
-      if (nb > 0) a.c.k_bidx[m_off] = (uint8_t)row;
-      s_sc[d] = h2f(sh);
-      s_mq[d] = maxq;
-      if (row < nb) s_chan_of_row[row] = d;
-    }
-    __syncthreads();
-    // ---- codes, packed along channels: word (t, w) holds channels w*FPI + j
-    uint32_t* kw = a.c.k_codes + (head * a.c.t_cap + g * G) * WPT;
-    for (int i = tid; i < G * WPT; i += kThreads) {
-      const int t = i / WPT, w = i % WPT;
-      uint32_t word = 0u;
+    const float maxq = (row < nb) ? 15.0f : (float)MASK;
+    const uint16_t sh = f2h(s_rng[d] / maxq);
+    const int64_t m_off = (head * (a.c.t_cap / G) + g) * kD + d;
+    a.c.k_scale[m_off] = sh;
+    a.c.k_min[m_off] = from_order_key(lo);
+    a.c.k_bidx[m_off] = (uint8_t)row;
+    s_sc[d] = h2f(sh);
+    s_mq[d] = maxq;
+    if (row < nb) s_chan_of_row[row] = d;
+  }
+  __syncthreads();
+  uint32_t* kw = a.c.k_codes + (head * a.c.t_cap + g * G) * WPT;
+  for (int i = tid; i < G * WPT; i += kThreads) {
+    const int t = i / WPT, w = i % WPT;
+    uint32_t word = 0u;
 #pragma unroll
-      for (int j = 0; j < FPI; ++j) {
-        const int c = w * FPI + j;
-        const uint32_t q = quant_code(h2f(tile[t * kD + c]), s_mn[c], s_sc[c], s_mq[c]);
-        word |= (q & MASK) << (BITS * j);
-      }
-      kw[i] = word;
+    for (int j = 0; j < FPI; ++j) {
+      const int c = w * FPI + j;
+      const uint32_t q = quant_code(h2f(tile[t * kD + c]), s_mn[c], s_sc[c], s_mq[c]);
+      word |= (q & MASK) << (BITS * j);
     }
-    if (nb > 0) {
-      // Kitty high two bits of the boosted rows, 16 rows per word
-      const int hpt = nb / 16;
-      uint32_t* hw = a.c.k_hi + (head * a.c.t_cap + g * G) * hpt;
-      for (int i = tid; i < G * hpt; i += kThreads) {
-        const int t = i / hpt, w = i % hpt;
-        uint32_t word = 0u;
-        for (int j = 0; j < 16; ++j) {
-          const int c = s_chan_of_row[w * 16 + j];
-          const uint32_t q = quant_code(h2f(tile[t * kD + c]), s_mn[c], s_sc[c], 15.0f);
-          word |= (q >> 2) << (2 * j);
-        }
-        hw[i] = word;
-      }
+    kw[i] = word;
+  }
+  // high two bits of the boosted rows, 16 rows per word
+  const int hpt = nb / 16;
+  uint32_t* hw = a.c.k_hi + (head * a.c.t_cap + g * G) * hpt;
+  for (int i = tid; i < G * hpt; i += kThreads) {
+    const int t = i / hpt, w = i % hpt;
+    uint32_t word = 0u;
+    for (int j = 0; j < 16; ++j) {
+      const int c = s_chan_of_row[w * 16 + j];
+      const uint32_t q = quant_code(h2f(tile[t * kD + c]), s_mn[c], s_sc[c], 15.0f);
+      word |= (q >> 2) << (2 * j);
     }
-  } else {
-    // ---- values: per token, per channel group of G channels
-    constexpr int NCG = kD / G;            // channel groups per token
-    constexpr int PAIRS = G * NCG;         // (token, channel group) pairs == kD
-    static_assert(PAIRS == kD, "one pair per LDS slot");
-    const int p = tid >> 1, half = tid & 1;
+    hw[i] = word;
+  }
+}
+
+// Value slices per group: whole packed words (FPI tokens) per slice.
+template <int BITS, int G>
+constexpr int kValueSlices = (G / (32 / BITS)) < kSlices ? (G / (32 / BITS)) : kSlices;
+
+// Values, tokens [slice*NT, (slice+1)*NT) of one group: per token, per
+// channel group of G channels; codes packed along tokens.
+template <int BITS, int G>
+__device__ void quantize_values_slice(const QuantArgs& a, int64_t head, int64_t gi, int slice) {
+  constexpr int FPI = 32 / BITS;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  constexpr int NT = G / kValueSlices<BITS, G>;   // tokens in this slice (multiple of FPI)
+  constexpr int NCG = kD / G;            // channel groups per token
+  constexpr int TPP = kThreads / (NT * NCG);   // threads per (token, channel group)
+  __shared__ uint16_t tile[NT][kD + 2];
+  __shared__ float s_mn[NT * NCG], s_sc[NT * NCG];
+  static_assert(FPI <= NT && NT % FPI == 0, "whole words per slice");
+  static_assert(TPP >= 1 && (TPP & (TPP - 1)) == 0 && G % TPP == 0, "thread split");
+  const int tid = threadIdx.x;
+  const int64_t g = a.first_group + gi;
+  const int t_base = slice * NT;
+  const uint16_t* src = a.v_src + head * a.src_head_stride + (gi * G + t_base) * kD;
+  for (int i = tid; i < NT * kD / 8; i += kThreads) {
+    const int t = i / (kD / 8), q = i % (kD / 8);
+    const uint4 v = *reinterpret_cast<const uint4*>(src + t * kD + 8 * q);
+    uint32_t* d = reinterpret_cast<uint32_t*>(&tile[t][8 * q]);
+    d[0] = v.x, d[1] = v.y, d[2] = v.z, d[3] = v.w;
+  }
+  __syncthreads();
+  {
+    const int p = tid / TPP, part = tid % TPP;   // p = token * NCG + channel group
     const int t = p / NCG, cg = p % NCG;
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int j = half * (G / 2); j < (half + 1) * (G / 2); ++j) {
-      const uint32_t k = order_key(tile[t * kD + cg * G + j]);
+    for (int j = part * (G / TPP); j < (part + 1) * (G / TPP); ++j) {
+      const uint32_t k = order_key(tile[t][cg * G + j]);
       lo = min(lo, k);
       hi = max(hi, k);
     }
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, 1));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, 1));
-    if (!half) {
+    lo = wave_min(lo, TPP);
+    hi = wave_max(hi, TPP);
+    if (part == 0) {
       const float mn = h2f(from_order_key(lo));
       const float mx = h2f(from_order_key(hi));
       const uint16_t sh = f2h((mx - mn) / (float)MASK);
-      const int64_t m_off = (head * a.c.t_cap + g * G + t) * NCG + cg;
+      const int64_t m_off = (head * a.c.t_cap + g * G + t_base + t) * NCG + cg;
       a.c.v_scale[m_off] = sh;
       a.c.v_min[m_off] = from_order_key(lo);
       s_mn[p] = mn;
       s_sc[p] = h2f(sh);
     }
-    __syncthreads();
-    // codes, packed along tokens: word (w, d) holds tokens w*FPI + j
-    uint32_t* vw = a.c.v_codes + (head * (a.c.t_cap / FPI) + g * (G / FPI)) * kD;
-    for (int i = tid; i < (G / FPI) * kD; i += kThreads) {
-      const int w = i / kD, d = i % kD;
-      const int cgd = d / G;
-      uint32_t word = 0u;
+  }
+  __syncthreads();
+  uint32_t* vw = a.c.v_codes + (head * (a.c.t_cap / FPI) + (g * G + t_base) / FPI) * kD;
+  for (int i = tid; i < (NT / FPI) * kD; i += kThreads) {
+    const int w = i / kD, d = i % kD;
+    const int cgd = d / G;
+    uint32_t word = 0u;
 #pragma unroll
-      for (int j = 0; j < FPI; ++j) {
-        const int tt = w * FPI + j;
-        const int pp = tt * NCG + cgd;
-        const uint32_t q = quant_code(h2f(tile[tt * kD + d]), s_mn[pp], s_sc[pp], (float)MASK);
-        word |= q << (BITS * j);
-      }
-      vw[i] = word;
+    for (int j = 0; j < FPI; ++j) {
+      const int tt = w * FPI + j;
+      const int pp = tt * NCG + cgd;
+      word |= quant_code(h2f(tile[tt][d]), s_mn[pp], s_sc[pp], (float)MASK) << (BITS * j);
     }
+    vw[i] = word;
+  }
+}
+
+// grid: (heads * n_groups, 2 * kSlices): y < kSlices key slices (Kitty: the
+// whole key group in y == 0), then value slices
+template <int BITS, int G, bool KITTY>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  const int64_t blk = blockIdx.x;
+  const int64_t head = blk / a.n_groups;
+  const int64_t gi = blk % a.n_groups;
+  const int y = blockIdx.y;
+  if (y >= kSlices) {
+    if (y - kSlices < kValueSlices<BITS, G>) quantize_values_slice<BITS, G>(a, head, gi, y - kSlices);
+  } else if constexpr (KITTY) {
+    if (y == 0) quantize_keys_kitty<G>(a, head, gi);
+  } else {
+    quantize_keys_slice<BITS, G>(a, head, gi, y);
   }
 }
 
@@ -224,13 +326,13 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   }
 }
 
-template <int BITS>
+template <int BITS, bool KITTY>
 hipError_t quantize_bits(int group, const QuantArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.n_heads * a.n_groups), 2);
+  const dim3 grid((unsigned)(a.n_heads * a.n_groups), 2 * kSlices);
   switch (group) {
-    case 32: quantize_kernel<BITS, 32><<<grid, kThreads, 0, s>>>(a); break;
-    case 64: quantize_kernel<BITS, 64><<<grid, kThreads, 0, s>>>(a); break;
-    case 128: quantize_kernel<BITS, 128><<<grid, kThreads, 0, s>>>(a); break;
+    case 32: quantize_kernel<BITS, 32, KITTY><<<grid, kThreads, 0, s>>>(a); break;
+    case 64: quantize_kernel<BITS, 64, KITTY><<<grid, kThreads, 0, s>>>(a); break;
+    case 128: quantize_kernel<BITS, 128, KITTY><<<grid, kThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -253,7 +355,9 @@ hipError_t dequantize_bits(int group, const DequantArgs& a, hipStream_t s) {
 
 hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s) {
   if (a.n_groups == 0 || a.n_heads == 0) return hipSuccess;
-  return bits == 2 ? quantize_bits<2>(group, a, s) : quantize_bits<4>(group, a, s);
+  if (bits == 2)
+    return a.n_boost > 0 ? quantize_bits<2, true>(group, a, s) : quantize_bits<2, false>(group, a, s);
+  return quantize_bits<4, false>(group, a, s);
 }
 
 hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStream_t s) {
