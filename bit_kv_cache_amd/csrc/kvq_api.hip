@@ -3,7 +3,7 @@
 
 #include <math.h>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 #include "kvq_internal.h"
 
 namespace {
