@@ -67,6 +67,86 @@ def avg_bits_per_element(bits: int, G: int, T: int, R: int) -> float:
 
 
 # ----------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters (FETCH_SIZE / WRITE_SIZE, KiB per
+# dispatch), scaled by what the same counters read for a plain copy of known
+# size.  The figures live in a text file under profiles/ together with a hash
+# of the kernel sources they were taken from; a changed source voids them.
+# ----------------------------------------------------------------------------
+
+CALIB_COPY_BYTES = 1 << 30
+SPLIT_KERNEL = "decode_mfma_kernel"
+COPY_KERNEL = "bitwise_not"       # the calibration pass: dst = ~src over 1 GiB of int32
+
+
+def kernel_source_hash() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bit_kv_cache_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_decode_mfma_{workload}.txt")
+
+
+def _counter_means(csv_path, counter):
+    import csv
+    per = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            for key in (SPLIT_KERNEL, COPY_KERNEL):
+                if key in r["Kernel_Name"]:
+                    per.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, command: str) -> dict:
+    """Turn the two counter runs into bytes per launch of the split-K kernel."""
+    fm, fn = _counter_means(fetch_csv, "FETCH_SIZE")
+    wm, wn = _counter_means(write_csv, "WRITE_SIZE")
+    f_scale = CALIB_COPY_BYTES / (fm[COPY_KERNEL] * 1024)
+    w_scale = CALIB_COPY_BYTES / (wm[COPY_KERNEL] * 1024)
+    fetch = fm[SPLIT_KERNEL] * 1024 * f_scale
+    write = wm[SPLIT_KERNEL] * 1024 * w_scale
+    rec = {"workload": workload, "source_hash": kernel_source_hash(),
+           "fetch_bytes": round(fetch), "write_bytes": round(write),
+           "traffic_bytes": round(fetch + write),
+           "raw_fetch_kib": round(fm[SPLIT_KERNEL], 1), "raw_write_kib": round(wm[SPLIT_KERNEL], 1),
+           "copy_fetch_kib": round(fm[COPY_KERNEL], 1), "copy_write_kib": round(wm[COPY_KERNEL], 1),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "dispatches": {"fetch": fn, "write": wn}}
+    with open(traffic_file(workload), "w") as fh:
+        fh.write(f"# HBM traffic per launch of {SPLIT_KERNEL}, workload {workload}\n")
+        fh.write(f"# counters: {command}\n")
+        fh.write(f"# scale = {CALIB_COPY_BYTES} B copied / counter reading of the copy kernel\n")
+        for k, v in rec.items():
+            fh.write(f"{k}: {json.dumps(v)}\n")
+    return rec
+
+
+def read_traffic(workload: str):
+    """Bytes per launch from the committed counter file, or None when absent or
+    taken from other kernel sources."""
+    try:
+        rec = {}
+        with open(traffic_file(workload)) as fh:
+            for ln in fh:
+                if ln.startswith("#") or ":" not in ln:
+                    continue
+                k, v = ln.split(":", 1)
+                rec[k.strip()] = json.loads(v)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes")
+
 
 def _host_info():
     cores = os.cpu_count() or 1
@@ -106,10 +186,10 @@ def build_caches(w, n_copies, kvq, synth, torch):
     return cfg, copies
 
 
-def cpu_baseline(w, max_heads, threads):
-    """Time the oracle (as it stands) on a bounded sample of heads: one decode
-    step plus the append-group quantize of those heads; scale to the whole
-    workload."""
+def cpu_baseline(w, max_heads, threads, min_seconds=10.0):
+    """Time the oracle (as it stands) on a bounded sample of heads: decode steps
+    plus the append-group quantize of those heads, repeated until at least
+    ``min_seconds`` of wall time; scale the mean step to the whole workload."""
     import numpy as np
     import oracle
     import synth
@@ -132,18 +212,24 @@ def cpu_baseline(w, max_heads, threads):
     del k_src, v_src
     q = synth.as_bits(synth.query(w, "cpu"))[:B, : H_kv * w.gqa]
     kS, vS, kr, vr = (np.stack(x) for x in (kS, vS, kr, vr))
+    reps = 0
     t0 = time.perf_counter()
-    oracle.decode_attention(oc, B, H_kv * w.gqa, H_kv, q, w.T, k_sink=kS if w.S else None,
-                            v_sink=vS if w.S else None, n_sink=w.S, k_res=kr, v_res=vr,
-                            n_res=w.R, n_threads=threads)
-    if w.R >= w.G:
-        oracle.quantize_pack(oc, kr, vr, w.T // w.G, 1, n_threads=threads)
-    dt = time.perf_counter() - t0
+    while True:
+        oracle.decode_attention(oc, B, H_kv * w.gqa, H_kv, q, w.T, k_sink=kS if w.S else None,
+                                v_sink=vS if w.S else None, n_sink=w.S, k_res=kr, v_res=vr,
+                                n_res=w.R, n_threads=threads)
+        if w.R >= w.G:
+            oracle.quantize_pack(oc, kr, vr, w.T // w.G, 1, n_threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     scale = w.heads / len(heads)
-    return {"value": dt * scale * 1e6, "unit": "us/step", "cores": threads, "kind": "oracle",
-            "sample": f"{len(heads)} of {w.heads} kv heads (all their query heads), one "
-                      f"decode step + append quantize, {dt:.2f} s wall on {threads} threads, "
-                      f"scaled x{scale:g}"}
+    return {"value": round(dt / reps * scale * 1e6, 1), "unit": "us/step", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(heads)} of {w.heads} kv heads (all their query heads); {reps} "
+                      f"repetitions of one decode step + append quantize in {dt:.1f} s wall "
+                      f"on {threads} threads; mean step scaled x{scale:g}"}
 
 
 def main(argv=None):
@@ -155,8 +241,17 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0 = auto)")
     ap.add_argument("--n-chunks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--cpu-heads", type=int, default=1 << 20, help="kv heads the oracle runs")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the run, stream 1 GiB in and 1 GiB out 5 times (counter scale)")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "CMD"),
+                    help="write the profiles/ traffic file from two counter runs and exit")
     args = ap.parse_args(argv)
+
+    if args.write_traffic:
+        print(json.dumps(write_traffic(args.workload, *args.write_traffic)))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (each box has "
@@ -193,7 +288,7 @@ def main(argv=None):
     q = synth.query(w, "cuda")
     n_chunks, ws_bytes = kvq.kvq_decode_plan(cfg, w.B, w.H_q, w.H_kv, w.T,
                                              args.n_chunks or w.min_chunks)
-    ws = torch.zeros(ws_bytes // 4, dtype=torch.float32, device="cuda")   # counters start at 0
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
     out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -209,13 +304,25 @@ def main(argv=None):
     append = w.R >= w.G
     g_app = w.T // w.G
 
-    def decode(i):
-        st = lib.kvq_decode_attention(ctypes.byref(c_cfg), ctypes.byref(c_caches[i % n_copies]),
-                                      w.B, w.H_q, w.H_kv, q.data_ptr(), w.T, sink_p, res_p,
-                                      ctypes.c_float(0.0), n_chunks, ws.data_ptr(), ws_bytes,
-                                      out.data_ptr(), sp)
+    n_parts = ctypes.c_int32(0)
+
+    def partials(i):
+        st = lib.kvq_decode_partials(ctypes.byref(c_cfg), ctypes.byref(c_caches[i % n_copies]),
+                                     w.B, w.H_q, w.H_kv, q.data_ptr(), w.T, sink_p, res_p,
+                                     ctypes.c_float(0.0), n_chunks, ws.data_ptr(), ws_bytes,
+                                     ctypes.byref(n_parts), sp)
         if st:
-            raise kvq.KvqError(st, "kvq_decode_attention")
+            raise kvq.KvqError(st, "kvq_decode_partials")
+
+    def merge():
+        st = lib.kvq_decode_merge(w.B, w.H_q, n_parts.value, ws.data_ptr(), ws_bytes,
+                                  out.data_ptr(), sp)
+        if st:
+            raise kvq.KvqError(st, "kvq_decode_merge")
+
+    def decode(i):
+        partials(i)
+        merge()
 
     def quant(i):
         if not append:
@@ -242,24 +349,32 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel durations on the launch stream (HIP events around each call) ---------
+    # per-kernel durations on the launch stream (HIP events between the launches)
     n_k = min(args.steps, 100)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_k)]
     torch.cuda.synchronize()
     for i in range(n_k):
         ev[i][0].record(stream)
-        decode(i)
+        partials(i)
         ev[i][1].record(stream)
-        quant(i)
+        merge()
         ev[i][2].record(stream)
+        quant(i)
+        ev[i][3].record(stream)
     torch.cuda.synchronize()
-    dec_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    app_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
-    dec_avg = sum(dec_ms) / n_k
-    app_avg = sum(app_ms) / n_k
+
+    def stats(a, b):
+        ms = sorted(e[a].elapsed_time(e[b]) for e in ev)
+        return sum(ms) / n_k, ms
+
+    part_avg, part_ms = stats(0, 1)
+    merge_avg, _ = stats(1, 2)
+    dec_avg, dec_ms = stats(0, 2)
+    app_avg, _ = stats(2, 3)
 
     alg = decode_bytes(w)
-    achieved = alg / (dec_avg * 1e-3) / 1e9
+    alg_split = alg - w.B * w.H_q * w.D * 4   # the split-K kernel does not write O
+    achieved = alg_split / (part_avg * 1e-3) / 1e9
     step_bytes = alg + (append_bytes(w) if append else 0)
     eff_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
@@ -285,19 +400,30 @@ def main(argv=None):
         "effective_GBps": round(eff_gbps, 1),
         "effective_frac_of_peak": round(eff_gbps / HBM_PEAK_GBPS, 4),
         "decode_us": {"avg": round(dec_avg * 1e3, 3), "p10": round(dec_ms[n_k // 10] * 1e3, 3),
-                      "p90": round(dec_ms[(9 * n_k) // 10] * 1e3, 3)},
+                      "p90": round(dec_ms[(9 * n_k) // 10] * 1e3, 3),
+                      "split_kernel_avg": round(part_avg * 1e3, 3),
+                      "merge_kernel_avg": round(merge_avg * 1e3, 3)},
         "append_quant_us": round(app_avg * 1e3, 3) if append else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "kvq_decode_attention",
-                     "algorithmic_bytes": alg},
+                     "traffic": read_traffic(w.name),
+                     "kernel": "split-K decode kernel (kvq_decode_partials)",
+                     "algorithmic_bytes": alg_split,
+                     "kernel_avg_us": round(part_avg * 1e3, 3)},
     }
     if not args.no_cpu_baseline:
         cores, model = _host_info()
-        cb = cpu_baseline(w, args.cpu_heads, cores)
+        cb = cpu_baseline(w, args.cpu_heads, cores, args.cpu_seconds)
         cb["cpu_model"] = model
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
+    if args.calib_copy:
+        src = torch.zeros(CALIB_COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
     return 0
 
 

@@ -30,7 +30,8 @@ KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_ALIGN, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_
     0, -1, -2, -3, -4, -5)
 
 EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
-            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_dequantize")
+            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_partials",
+            "kvq_decode_merge", "kvq_dequantize")
 
 
 class kvq_qcfg(ctypes.Structure):
@@ -64,6 +65,11 @@ _lib.kvq_decode_workspace_bytes.restype = _sz
 _lib.kvq_decode_attention.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32,
                                       _P, _sz, _P, _P]
 _lib.kvq_decode_attention.restype = ctypes.c_int
+_lib.kvq_decode_partials.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32,
+                                     _P, _sz, _P, _P]
+_lib.kvq_decode_partials.restype = ctypes.c_int
+_lib.kvq_decode_merge.argtypes = [_i32, _i32, _i32, _P, _sz, _P, _P]
+_lib.kvq_decode_merge.restype = ctypes.c_int
 _lib.kvq_dequantize.argtypes = [_P, _P, _i32, _i32, _i64, _i64, _P, _P, _P]
 _lib.kvq_dequantize.restype = ctypes.c_int
 
@@ -210,6 +216,29 @@ def kvq_decode_attention(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int,
         ctypes.byref(res) if res is not None else None, float(sm_scale), int(n_chunks),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
         _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_decode_partials(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int,
+                        q: torch.Tensor, n_quant_tokens: int, sink: kvq_window | None,
+                        res: kvq_window | None, workspace: torch.Tensor, sm_scale: float = 0.0,
+                        n_chunks: int = 0, stream=None) -> int:
+    """Split-K phase only; returns the number of parts per (batch, query head)."""
+    c_cfg, c_cache = cfg.c(), cache.c()
+    n_parts = ctypes.c_int32(0)
+    _check(_lib.kvq_decode_partials(
+        ctypes.byref(c_cfg), ctypes.byref(c_cache), B, H_q, H_kv, _ptr(q), n_quant_tokens,
+        ctypes.byref(sink) if sink is not None else None,
+        ctypes.byref(res) if res is not None else None, float(sm_scale), int(n_chunks),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), ctypes.byref(n_parts),
+        _stream(stream)), "kvq_decode_partials")
+    return n_parts.value
+
+
+def kvq_decode_merge(B: int, H_q: int, n_parts: int, workspace: torch.Tensor,
+                     out: torch.Tensor, stream=None) -> None:
+    _check(_lib.kvq_decode_merge(B, H_q, n_parts, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _ptr(out),
+                                 _stream(stream)), "kvq_decode_merge")
 
 
 def kvq_dequantize(cfg: QCfg, cache: Cache, B: int, H_kv: int, first_group: int,

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 // with its loads batched.
 constexpr int kMergeThreads = 256;
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
-  __shared__ float s_w[1024];
+  __shared__ float s_w[kMaxParts];
   __shared__ float s_red[kMergeThreads / 64];
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -238,11 +238,13 @@ hipError_t decode_bits(int group, const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_decode(int bits, int group, const DecodeArgs& a, hipStream_t st) {
-  const hipError_t e = mfma_decode_supported(bits, group, a.gqa, a.n_boost)
-                           ? launch_decode_mfma(bits, a, st)
-                           : (bits == 2 ? decode_bits<2>(group, a, st) : decode_bits<4>(group, a, st));
-  if (e != hipSuccess) return e;
+hipError_t launch_decode_partials(int bits, int group, const DecodeArgs& a, hipStream_t st) {
+  return mfma_decode_supported(bits, group, a.gqa, a.n_boost)
+             ? launch_decode_mfma(bits, a, st)
+             : (bits == 2 ? decode_bits<2>(group, a, st) : decode_bits<4>(group, a, st));
+}
+
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t st) {
   merge_kernel<<<(unsigned)(a.B * a.H_q), kMergeThreads, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -53,7 +53,7 @@ kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_
 // kernel: the resident block slots divided over the heads, so the grid runs
 // in a single round (windows are spread over the chunks; at least one chunk).
 // An explicit request is honoured up to one chunk per group (and 1023).
-constexpr int64_t kMaxChunks = 1023;  // the merge kernel holds <= 1024 part weights
+constexpr int64_t kMaxChunks = kvq::kMaxParts - 1;  // plus the window part
 
 int32_t plan_chunks(bool mfma, int gqa, int64_t heads, int64_t n_groups, int32_t req) {
   int64_t n;
@@ -155,11 +155,17 @@ size_t kvq_decode_workspace_bytes(const kvq_qcfg* cfg, int32_t B, int32_t H_q, i
   return ws;
 }
 
-kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
-                                int32_t H_q, int32_t H_kv, const uint16_t* q,
-                                int64_t n_quant_tokens, const kvq_window* sink,
-                                const kvq_window* res, float sm_scale, int32_t n_chunks,
-                                void* workspace, size_t ws_bytes, float* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates a decode call and fills the launch arguments (shared by the
+// one-call and the two-phase entry points).
+kvq_status prepare_decode(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,
+                          int32_t H_kv, const uint16_t* q, int64_t n_quant_tokens,
+                          const kvq_window* sink, const kvq_window* res, float sm_scale,
+                          int32_t n_chunks, void* workspace, size_t ws_bytes,
+                          kvq::DecodeArgs* a) {
   int32_t nc = 0;
   size_t need = 0;
   kvq_status st = kvq_decode_plan(cfg, B, H_q, H_kv, n_quant_tokens, n_chunks, &nc, &need);
@@ -168,40 +174,95 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
   if (n_quant_tokens > cache->t_cap) return KVQ_ERR_ARG;
   if ((st = check_window(sink)) != KVQ_OK) return st;
   if ((st = check_window(res)) != KVQ_OK) return st;
-  if (!q || !out) return KVQ_ERR_ARG;
-  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  if (!q) return KVQ_ERR_ARG;
+  if (!aligned16(q)) return KVQ_ERR_ALIGN;
   if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
   if (!(sm_scale > 0.f)) sm_scale = 1.0f / sqrtf((float)kD);
 
-  kvq::DecodeArgs a{};
-  a.c = cache_args(cache);
-  a.q = q;
-  a.B = B;
-  a.H_q = H_q;
-  a.H_kv = H_kv;
-  a.gqa = H_q / H_kv;
-  a.n_boost = cfg->n_boost;
-  a.n_groups = n_quant_tokens / cfg->group;
-  a.n_chunks = nc;
-  a.groups_per_chunk = nc > 0 ? (int32_t)((a.n_groups + nc - 1) / nc) : 0;
+  *a = kvq::DecodeArgs{};
+  a->c = cache_args(cache);
+  a->q = q;
+  a->B = B;
+  a->H_q = H_q;
+  a->H_kv = H_kv;
+  a->gqa = H_q / H_kv;
+  a->n_boost = cfg->n_boost;
+  a->n_groups = n_quant_tokens / cfg->group;
+  a->n_chunks = nc;
+  a->groups_per_chunk = nc > 0 ? (int32_t)((a->n_groups + nc - 1) / nc) : 0;
   if (sink && sink->n > 0) {
-    a.k_sink = sink->k;
-    a.v_sink = sink->v;
-    a.n_sink = sink->n;
-    a.sink_cap = sink->cap;
+    a->k_sink = sink->k;
+    a->v_sink = sink->v;
+    a->n_sink = sink->n;
+    a->sink_cap = sink->cap;
   }
   if (res && res->n > 0) {
-    a.k_res = res->k;
-    a.v_res = res->v;
-    a.n_res = res->n;
-    a.res_cap = res->cap;
+    a->k_res = res->k;
+    a->v_res = res->v;
+    a->n_res = res->n;
+    a->res_cap = res->cap;
   }
-  a.qscale = sm_scale * 1.4426950408889634f;
-  a.ws = static_cast<float*>(workspace);
-  a.n_parts = kvq::mfma_decode_supported(cfg->bits, cfg->group, a.gqa, cfg->n_boost) ? nc : nc + 1;
+  a->qscale = sm_scale * 1.4426950408889634f;
+  a->ws = static_cast<float*>(workspace);
+  a->n_parts = kvq::mfma_decode_supported(cfg->bits, cfg->group, a->gqa, cfg->n_boost) ? nc
+                                                                                     : nc + 1;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                                int32_t H_q, int32_t H_kv, const uint16_t* q,
+                                int64_t n_quant_tokens, const kvq_window* sink,
+                                const kvq_window* res, float sm_scale, int32_t n_chunks,
+                                void* workspace, size_t ws_bytes, float* out, void* stream) {
+  kvq::DecodeArgs a;
+  kvq_status st = prepare_decode(cfg, cache, B, H_q, H_kv, q, n_quant_tokens, sink, res,
+                                 sm_scale, n_chunks, workspace, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!out) return KVQ_ERR_ARG;
+  if (!aligned16(out)) return KVQ_ERR_ALIGN;
   a.out = out;
-  return hip_status(kvq::launch_decode(cfg->bits, cfg->group, a, static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s))) != KVQ_OK)
+    return st;
+  return hip_status(kvq::launch_merge(a, s));
+}
+
+kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                               int32_t H_q, int32_t H_kv, const uint16_t* q,
+                               int64_t n_quant_tokens, const kvq_window* sink,
+                               const kvq_window* res, float sm_scale, int32_t n_chunks,
+                               void* workspace, size_t ws_bytes, int32_t* n_parts,
+                               void* stream) {
+  kvq::DecodeArgs a;
+  kvq_status st = prepare_decode(cfg, cache, B, H_q, H_kv, q, n_quant_tokens, sink, res,
+                                 sm_scale, n_chunks, workspace, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!n_parts) return KVQ_ERR_ARG;
+  *n_parts = a.n_parts;
+  return hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_merge(int32_t B, int32_t H_q, int32_t n_parts, const float* workspace,
+                            size_t ws_bytes, float* out, void* stream) {
+  if (B <= 0 || H_q <= 0 || n_parts <= 0 || n_parts > kvq::kMaxParts) return KVQ_ERR_ARG;
+  if ((int64_t)B * H_q > 0x7FFFFFFF) return KVQ_ERR_ARG;
+  if (!workspace || ws_bytes < (size_t)B * H_q * n_parts * (kD + 2) * sizeof(float))
+    return KVQ_ERR_WORKSPACE;
+  if (!out) return KVQ_ERR_ARG;
+  if (!aligned16(workspace) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  kvq::DecodeArgs a{};
+  a.B = B;
+  a.H_q = H_q;
+  a.n_parts = n_parts;
+  a.ws = const_cast<float*>(workspace);
+  a.out = out;
+  return hip_status(kvq::launch_merge(a, static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_dequantize(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_kv,

@@ -8,6 +8,7 @@ namespace kvq {
 
 constexpr int kD = 128;          // head dimension the kernels are built for
 constexpr int kMaxGqa = 8;       // query heads per kv head
+constexpr int kMaxParts = 1024;  // partials per (batch, query head) the merge accepts
 
 // ---------------------------------------------------------------- device helpers
 
@@ -88,10 +89,9 @@ struct DecodeArgs {
 inline bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
   return group == 128 && (gqa == 4 || gqa == 8) && n_boost == 0 && (bits == 2 || bits == 4);
 }
-// Resident blocks (of 4 waves) per CU of the matrix-core kernel: GQA-4
-// variants fit 3 waves per SIMD (<= 168 VGPRs), GQA-8 variants 2 (LDS).
+// Resident blocks (of 4 waves) per CU of the matrix-core kernel.
 template <int GQA>
-constexpr int kMfmaBlocksPerCU = GQA == 4 ? 2 : 2;
+constexpr int kMfmaBlocksPerCU = 2;
 constexpr int kCUs = 256;  // MI355X
 inline int mfma_resident_blocks(int gqa) {
   return kCUs * (gqa == 4 ? kMfmaBlocksPerCU<4> : kMfmaBlocksPerCU<8>);
@@ -100,7 +100,8 @@ inline int mfma_resident_blocks(int gqa) {
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
 hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStream_t s);
-hipError_t launch_decode(int bits, int group, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_partials(int bits, int group, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma(int bits, const DecodeArgs& a, hipStream_t s);
 
 }  // namespace kvq

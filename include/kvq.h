@@ -165,6 +165,36 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
                                 const kvq_window* res, float sm_scale, int32_t n_chunks,
                                 void* workspace, size_t ws_bytes, float* out, void* stream);
 
+/* The two phases of kvq_decode_attention, for callers that combine partial
+ * results of several calls (for example a sequence split across devices, each
+ * holding a token range of the same heads) or time the phases apart.
+ *
+ * kvq_decode_partials: the split-K phase (same arguments as
+ * kvq_decode_attention, no output).  Writes, for every batch b, query head h
+ * and part p < *n_parts, the fp32 record
+ *     workspace[((b*H_q + h)*n_parts + p)*(D+2) + {0, 1, 2..D+1}]
+ *         = m, l, acc[0..D-1]
+ * of one token range (BitDecoding page, section II; the combination rule is
+ * the log-sum-exp merge): with x_t = sm*log2(e)*(q . k_t) over the range's
+ * tokens, m = max x_t, l = sum 2^(x_t - m), acc = sum 2^(x_t - m) v_t.  An
+ * empty range has l = 0 (m is then meaningless).  *n_parts receives the
+ * number of parts per (b, h): the chunk count of kvq_decode_plan, plus one
+ * window part when GQA is 1 or 2, or G != 128, or n_boost > 0.
+ *
+ * kvq_decode_merge: out[b][h] = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
+ * over the parts with l_p > 0 (M the largest such m_p); 0 when every part is
+ * empty.  Reads workspace laid out as above with 1 <= n_parts <= 1024 and
+ * ws_bytes >= B*H_q*n_parts*(D+2)*4. */
+kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                               int32_t H_q, int32_t H_kv, const uint16_t* q,
+                               int64_t n_quant_tokens, const kvq_window* sink,
+                               const kvq_window* res, float sm_scale, int32_t n_chunks,
+                               void* workspace, size_t ws_bytes, int32_t* n_parts,
+                               void* stream);
+
+kvq_status kvq_decode_merge(int32_t B, int32_t H_q, int32_t n_parts, const float* workspace,
+                            size_t ws_bytes, float* out, void* stream);
+
 /* Dequantize groups [first_group, first_group + n_groups) of every head to
  * fp32 [B*H_kv][n_groups*G][D] (value = code*scale + min; Kitty page
  * Algorithm 1 for boosted key channels).  For checking the packed cache. */

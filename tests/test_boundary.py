@@ -130,3 +130,30 @@ def test_decode_plan():
     nc, ws = kvq.kvq_decode_plan(cfg, 1, 1, 1, 512)
     assert ws >= (nc + 1) * 130 * 4
     assert kvq.kvq_decode_workspace_bytes(kvq.QCfg(bits=3), 8, 32, 8, 32768) == 0
+
+
+def test_merge_rejects_bad_arguments():
+    m = lambda B=1, H=4, n=8, ws=FAKE, wsb=1 << 20, out=FAKE: kvq.raw_call(
+        "kvq_decode_merge", B, H, n, ws, wsb, out, None)
+    assert m(n=0) == kvq.KVQ_ERR_ARG
+    assert m(n=1025) == kvq.KVQ_ERR_ARG
+    assert m(B=0) == kvq.KVQ_ERR_ARG
+    assert m(ws=None) == kvq.KVQ_ERR_WORKSPACE
+    assert m(wsb=4 * 8 * 130 * 4 - 4) == kvq.KVQ_ERR_WORKSPACE
+    assert m(out=None) == kvq.KVQ_ERR_ARG
+    assert m(out=FAKE + 4) == kvq.KVQ_ERR_ALIGN
+
+
+def test_partials_reject_bad_arguments():
+    def p(n_parts=True, **kw):
+        cfg, cache = _cfg(), _cache()
+        nq = kw.get("nq", 1024)
+        out = ctypes.c_int32(0)
+        return kvq.raw_call("kvq_decode_partials", ctypes.byref(cfg), ctypes.byref(cache), 1, 4,
+                            1, kw.get("q", FAKE), nq, None, None, ctypes.c_float(0.0), 0,
+                            kw.get("ws", FAKE), 1 << 30,
+                            ctypes.byref(out) if n_parts else None, None)
+    assert p(n_parts=False) == kvq.KVQ_ERR_ARG
+    assert p(nq=100) == kvq.KVQ_ERR_ARG
+    assert p(q=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+    assert p(ws=None) == kvq.KVQ_ERR_WORKSPACE

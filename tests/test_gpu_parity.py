@@ -187,3 +187,54 @@ def test_decode_scaled_inputs(built, name, qk, vs):
     ref = oracle_decode(w, oc, inp, w.T)
     err = max_err(gpu_decode(w, gc, inp, w.T), ref)
     assert err <= TOL * max(1.0, vs), f"max-abs {err:.3g}"
+
+
+def _partials(w, cache, inp, n_quant, sink, res, n_chunks=0):
+    import bit_kv_cache_amd as kvq
+    B = len(inp["heads"]) // w.H_kv
+    _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), B, w.H_q, w.H_kv, n_quant, n_chunks)
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    n_parts = kvq.kvq_decode_partials(qcfg(w), cache, B, w.H_q, w.H_kv, inp["q"][:B].contiguous(),
+                                      n_quant, sink, res, ws, n_chunks=n_chunks)
+    return ws[: B * w.H_q * n_parts * (w.D + 2)].view(B * w.H_q, n_parts, w.D + 2)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama_2bit", "kitty", "gqa8_4bit"])
+def test_partials_then_merge_equals_one_call(built, name):
+    import bit_kv_cache_amd as kvq
+    w = _w(name)
+    inp = make_inputs(w)
+    gc = gpu_quantize(w, inp)
+    one = gpu_decode(w, gc, inp, w.T)
+    parts = _partials(w, gc, inp, w.T, kvq.window(inp["k_sink"], inp["v_sink"], w.S),
+                      kvq.window(inp["k_res"], inp["v_res"], w.R))
+    B = len(inp["heads"]) // w.H_kv
+    out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_merge(B, w.H_q, parts.shape[1], parts.contiguous(), out)
+    assert torch.equal(out, one)
+
+
+@pytest.mark.parametrize("name", ["llama_2bit", "kitty"])
+def test_token_split_across_calls_merges_to_whole(built, name):
+    """Two token ranges of the same heads in separate caches (as on two devices
+    that each hold part of a sequence): concatenated partials, one merge,
+    equal the oracle over the whole sequence."""
+    import bit_kv_cache_amd as kvq
+    w = _w(name)
+    inp = make_inputs(w)
+    n_groups = w.T // w.G
+    g1 = n_groups // 3
+    first = dict(inp, k=inp["k"][:, : g1 * w.G].contiguous(), v=inp["v"][:, : g1 * w.G].contiguous())
+    second = dict(inp, k=inp["k"][:, g1 * w.G:].contiguous(), v=inp["v"][:, g1 * w.G:].contiguous())
+    ca = gpu_quantize(synth.shrink(w, T=g1 * w.G), first)
+    cb = gpu_quantize(synth.shrink(w, T=(n_groups - g1) * w.G), second)
+    pa = _partials(w, ca, inp, g1 * w.G, kvq.window(inp["k_sink"], inp["v_sink"], w.S), None)
+    pb = _partials(w, cb, inp, (n_groups - g1) * w.G, None,
+                   kvq.window(inp["k_res"], inp["v_res"], w.R), n_chunks=3)
+    parts = torch.cat([pa, pb], dim=1).contiguous()
+    B = len(inp["heads"]) // w.H_kv
+    out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_merge(B, w.H_q, parts.shape[1], parts, out)
+    ref = oracle_decode(w, oracle_quantize(w, inp), inp, w.T)
+    err = max_err(out, ref)
+    assert err <= TOL, f"max-abs {err:.3g}"
