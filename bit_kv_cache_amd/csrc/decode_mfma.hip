@@ -35,7 +35,6 @@
 #include <type_traits>
 
 #include "kvq_internal.h"
-#include "decode_common.h"
 
 namespace kvq {
 namespace {
@@ -140,6 +139,13 @@ __device__ __forceinline__ float xor32(float v) {
   return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// Streaming loads: every cache byte is read once per step, so the loads are
+// non-temporal (no reuse expected in the caches).
+template <typename T>
+__device__ __forceinline__ T ldnt(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
+
 template <int BITS>
 struct KeyLoad {
   static constexpr int KW = BITS == 2 ? 2 : 4;   // key words per lane per tile
@@ -179,11 +185,11 @@ __device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     if (BITS == 2) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(kb + 16 * t * WPT * 4);
+      const u32x2 v = ldnt<u32x2>(kb + 16 * t * WPT * 4);
       L.kw[t][0] = v[0];
       L.kw[t][1] = v[1];
     } else {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(kb + 16 * t * WPT * 4);
+      const u32x4 v = ldnt<u32x4>(kb + 16 * t * WPT * 4);
 #pragma unroll
       for (int i = 0; i < KeyLoad<BITS>::KW; ++i) L.kw[t][i] = v[i];
     }
@@ -191,11 +197,11 @@ __device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int
   const char* km = reinterpret_cast<const char*>(a.c.k_min) +
                    (head * (a.c.t_cap / kG) + g) * kD * 2 + o.kmin;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) L.kmin[c] = *reinterpret_cast<const u32x4*>(km + 64 * c);
+  for (int c = 0; c < 4; ++c) L.kmin[c] = ldnt<u32x4>(km + 64 * c);
   const char* ks = reinterpret_cast<const char*>(a.c.k_scale) +
                    (head * (a.c.t_cap / kG) + g) * kD * 2 + o.kmeta;
-  L.ks[0] = *reinterpret_cast<const u32x2*>(ks);
-  L.ks[1] = *reinterpret_cast<const u32x2*>(ks + 2 * run_stride<BITS>());
+  L.ks[0] = ldnt<u32x2>(ks);
+  L.ks[1] = ldnt<u32x2>(ks + 2 * run_stride<BITS>());
 }
 
 template <int BITS>
@@ -209,14 +215,14 @@ __device__ __forceinline__ void load_values(const DecodeArgs& a, int64_t head, i
   for (int i = 0; i < VR; ++i)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      L.vw[i][e] = *reinterpret_cast<const u32x4*>(vb + (i * kD + 64 * e) * 4);
+      L.vw[i][e] = ldnt<u32x4>(vb + (i * kD + 64 * e) * 4);
   const int64_t t0 = (head * a.c.t_cap + g * kG) * 2;
   const char* vs = reinterpret_cast<const char*>(a.c.v_scale) + t0 + o.vmeta;
   const char* vm = reinterpret_cast<const char*>(a.c.v_min) + t0 + o.vmeta;
-  L.vs[0] = *reinterpret_cast<const u32x2*>(vs);
-  L.vs[1] = *reinterpret_cast<const u32x2*>(vs + 2 * run_stride<BITS>());
-  L.vm[0] = *reinterpret_cast<const u32x2*>(vm);
-  L.vm[1] = *reinterpret_cast<const u32x2*>(vm + 2 * run_stride<BITS>());
+  L.vs[0] = ldnt<u32x2>(vs);
+  L.vs[1] = ldnt<u32x2>(vs + 2 * run_stride<BITS>());
+  L.vm[0] = ldnt<u32x2>(vm);
+  L.vm[1] = ldnt<u32x2>(vm + 2 * run_stride<BITS>());
 }
 
 // fp16 element e (= 2r + half) of an A-prep chunk from its two 4-element runs
@@ -228,8 +234,14 @@ __device__ __forceinline__ float chunk_elem(const u32x2 (&run)[2], int e) {
 template <int GQA>
 struct WaveLds {
   static constexpr int ROWS = 2 * GQA;             // A rows: (head, hi/lo)
-  u32x4 ak[4][4][ROWS];                            // key A operand [c][kq][row]
-  u32x4 av[4][4][ROWS];                            // value A operand [c][kq][row]
+  union {
+    struct {
+      u32x4 ak[4][4][ROWS];                        // key A operand [c][kq][row]
+      u32x4 av[4][4][ROWS];                        // value A operand [c][kq][row]
+    } op;
+    uint32_t vt[kD][8];                            // fp16 window tile, transposed:
+                                                   // [channel][token pair]
+  };
   float p[GQA][kG];                                // probabilities of the group
   float alpha[GQA];
   f32x4 qhat[GQA / 4][64][2];                      // scaled query of the A-prep lanes
@@ -242,12 +254,6 @@ struct MergeLds {
 };
 
 template <int GQA>
-struct WindowResult {
-  float acc[GQA][kD];
-  float m[GQA], l[GQA];
-};
-
-template <int GQA>
 struct MfmaLds {
   union {
     struct {
@@ -255,9 +261,7 @@ struct MfmaLds {
       u32x4 zero;
     } main;
     MergeLds<GQA> merge;
-    Lds<GQA> window;
   } u;
-  WindowResult<GQA> win;
   u32x4 bias_a[4][4][16];                          // bias A operand [c][kq][row]
 };
 
@@ -277,54 +281,35 @@ __global__ __launch_bounds__(kThreadsM, kMfmaBlocksPerCU<GQA>) void decode_mfma_
   const int64_t b = head / a.H_kv, hk = head % a.H_kv;
   const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
 
-  // ---------------------------------------------------------------- window slice
+  // ---------------------------------------------------------------- first loads
+  // The wave's first group is requested before anything else, so its latency
+  // overlaps the window slice and the operand set-up below.
+  const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
+  const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
+  const int ph = lane >> 4;
+  const int pc = lane & 3, pkq = (lane >> 2) & 3;
+  LaneOffsets<BITS> lo;
   {
-    const int n_win = a.n_sink + a.n_res;
-    const int wpc = (n_win + a.n_chunks - 1) / a.n_chunks;
-    const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
-    Lds<GQA>& s = sh.u.window;
-    if (u1 > u0) {
-      for (int i = tid; i < GQA * kD; i += kThreadsM) s.q[i / kD][i % kD] = h2f(qrow[i]) * a.qscale;
-      if (tid < GQA) {
-        s.m[tid] = kNegInfM;
-        s.l[tid] = 0.f;
-      }
-      __syncthreads();
-      float acc[GQA];
-#pragma unroll
-      for (int h = 0; h < GQA; ++h) acc[h] = 0.f;
-      for (int u = u0; u < u1; u += kBlockTok)
-        window_block<GQA>(a, s, head, u, min(kBlockTok, u1 - u), acc);
-      const int d = tid & (kD - 1), half = tid >> 7;
-      if (half) {
-#pragma unroll
-        for (int h = 0; h < GQA; ++h) sh.win.acc[h][d] = acc[h];
-      }
-      __syncthreads();
-      if (!half) {
-#pragma unroll
-        for (int h = 0; h < GQA; ++h) sh.win.acc[h][d] += acc[h];
-      }
-      if (tid < GQA) {
-        sh.win.m[tid] = s.m[tid];
-        sh.win.l[tid] = s.l[tid];
-      }
-    } else if (tid < GQA) {
-      sh.win.m[tid] = kNegInfM;
-      sh.win.l[tid] = 0.f;
-    }
-    __syncthreads();
+    constexpr int WPT = kD / (32 / BITS);
+    lo.kw = (uint32_t)((n * WPT + KeyLoad<BITS>::KW * kq) * 4);
+    lo.kmeta = (uint32_t)(chunk_index<BITS>(pc, pkq, 0) * 2);
+    lo.vw = (uint32_t)((ValueLoad<BITS>::VR * kq * kD + 4 * n) * 4);
+    lo.vmeta = lo.kmeta;
+    lo.kmin = (uint32_t)(8 * kq * 2);
+  }
+  KeyLoad<BITS> kl;
+  ValueLoad<BITS> vl;
+  int64_t g = gb + wave;
+  if (g < ge) {
+    load_keys<BITS>(a, head, g, lo, kl);
+    load_values<BITS>(a, head, g, lo, vl);
   }
 
   // ---------------------------------------------------------------- quantized groups
-  const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
-  const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
   WaveLds<GQA>& L = sh.u.main.w[wave];
   if (tid == 0) sh.u.main.zero = u32x4{0u, 0u, 0u, 0u};
 
-  // this lane's A-prep heads and chunk (c, kq)
-  const int ph = lane >> 4;
-  const int pc = lane & 3, pkq = (lane >> 2) & 3;
+  // this lane's A-prep heads (ph, ph + 4) and chunk (pc, pkq)
   // q * sm * log2e * 2^(24 - offset) of this lane's A-prep elements, in LDS
   float qmax = 0.f;
 #pragma unroll
@@ -378,25 +363,14 @@ __global__ __launch_bounds__(kThreadsM, kMfmaBlocksPerCU<GQA>) void decode_mfma_
 #pragma unroll
   for (int slot = 0; slot < TPC; ++slot) {
     const bool mine = TPC == 1 || (m_row >> 3) == slot;
-    ak_ptr[slot] = mine ? &L.ak[0][kq][TPC == 1 ? m_row : (m_row & 7)] : &sh.u.main.zero;
+    ak_ptr[slot] = mine ? &L.op.ak[0][kq][TPC == 1 ? m_row : (m_row & 7)] : &sh.u.main.zero;
     ak_step[slot] = mine ? 4 * WaveLds<GQA>::ROWS : 0;
   }
   const bool av_mine = m_row < 2 * GQA;
-  const u32x4* av_ptr = av_mine ? &L.av[0][kq][m_row] : &sh.u.main.zero;
+  const u32x4* av_ptr = av_mine ? &L.op.av[0][kq][m_row] : &sh.u.main.zero;
   const int av_step = av_mine ? 4 * WaveLds<GQA>::ROWS : 0;
   __syncthreads();
 
-  LaneOffsets<BITS> lo;
-  {
-    constexpr int WPT = kD / (32 / BITS);
-    lo.kw = (uint32_t)((n * WPT + KeyLoad<BITS>::KW * kq) * 4);
-    lo.kmeta = (uint32_t)(chunk_index<BITS>(pc, pkq, 0) * 2);
-    lo.vw = (uint32_t)((ValueLoad<BITS>::VR * kq * kD + 4 * n) * 4);
-    lo.vmeta = lo.kmeta;
-    lo.kmin = (uint32_t)(8 * kq * 2);
-  }
-  KeyLoad<BITS> kl;
-  ValueLoad<BITS> vl;
   // One group of this wave.  With PREFETCH the next group's keys are fetched
   // right after q.K^T and its values right after p.V (unconditionally, so the
   // wait counters stay exact); the wave's last group runs without.
@@ -425,8 +399,8 @@ __global__ __launch_bounds__(kThreadsM, kMfmaBlocksPerCU<GQA>) void decode_mfma_
       u32x4 hi, lo;
       split_hilo(v, hi, lo);
       const int h = ph + 4 * j;
-      L.ak[pc][pkq][2 * h] = hi;
-      L.ak[pc][pkq][2 * h + 1] = lo;
+      L.op.ak[pc][pkq][2 * h] = hi;
+      L.op.ak[pc][pkq][2 * h + 1] = lo;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -526,8 +500,8 @@ __global__ __launch_bounds__(kThreadsM, kMfmaBlocksPerCU<GQA>) void decode_mfma_
       mterm[j] = fmaf(mterm[j], al, mt);
       u32x4 hi, lo;
       split_hilo(v, hi, lo);
-      L.av[pc][pkq][2 * h] = hi;
-      L.av[pc][pkq][2 * h + 1] = lo;
+      L.op.av[pc][pkq][2 * h] = hi;
+      L.op.av[pc][pkq][2 * h + 1] = lo;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -565,12 +539,115 @@ __global__ __launch_bounds__(kThreadsM, kMfmaBlocksPerCU<GQA>) void decode_mfma_
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  int64_t g = gb + wave;
   if (g < ge) {
-    load_keys<BITS>(a, head, g, lo, kl);
-    load_values<BITS>(a, head, g, lo, vl);
     for (; g + kWaves < ge; g += kWaves) group_step(g, std::true_type{});
     group_step(g, std::false_type{});
+  }
+
+  // ---------------------------------------------------------------- fp16 window
+  // Window tokens [u0, u1) of sink | residual belong to this block (every
+  // block takes an equal slice).  Wave w takes 16-token tiles w, w + 4, ...:
+  // q.K^T on the matrix core with the raw fp16 keys as B (natural channel
+  // order, the bias operand as A), the same online softmax, and p.V through an
+  // LDS transpose of the fp16 values into a natural-scale accumulator.
+  f32x4 wacc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) wacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    const int n_win = a.n_sink + a.n_res;
+    const int wpc = (n_win + a.n_chunks - 1) / a.n_chunks;
+    const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
+    auto row = [&](const uint16_t* sink, const uint16_t* res, int u) -> const uint16_t* {
+      return u < a.n_sink ? sink + (head * a.sink_cap + u) * kD
+                          : res + (head * a.res_cap + (u - a.n_sink)) * kD;
+    };
+    for (int u = u0 + 16 * wave; u < u1; u += 16 * kWaves) {
+      const int nt = min(16, u1 - u);
+      // keys of token n (rows past the tile end repeat its last token)
+      const uint16_t* kr = row(a.k_sink, a.k_res, u + min(n, nt - 1));
+      u32x4 kv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kv[c] = *reinterpret_cast<const u32x4*>(kr + 32 * c + 8 * kq);
+      // values: lane (token pair j, 16-channel group cg) -> vt[channel][j]
+      {
+        const int j = lane & 7, cg = lane >> 3;
+        const uint16_t* r0 = row(a.v_sink, a.v_res, u + min(2 * j, nt - 1)) + 16 * cg;
+        const uint16_t* r1 = row(a.v_sink, a.v_res, u + min(2 * j + 1, nt - 1)) + 16 * cg;
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(r0);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(r0 + 8);
+        const u32x4 y0 = *reinterpret_cast<const u32x4*>(r1);
+        const u32x4 y1 = *reinterpret_cast<const u32x4*>(r1 + 8);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t x = q < 4 ? x0[q] : x1[q - 4];
+          const uint32_t y = q < 4 ? y0[q] : y1[q - 4];
+          L.vt[16 * cg + 2 * q][j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+          L.vt[16 * cg + 2 * q + 1][j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+        }
+      }
+      f32x4 cw = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cw = mfma(sh.bias_a[c][kq][m_row], kv[c], cw);
+      // rows 8..15 repeat rows 0..7 when GQA == 4
+      const bool valid = n < nt && (GQA == 8 || rq < 2);
+      float alpha[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float lg = valid ? cw[2 * j] + cw[2 * j + 1] : kNegInfM;
+        float v = row_max16(lg);
+        if (GQA == 4) v = fmaxf(v, xor32(v));
+        const float m_new = fmaxf(m_run[j], v);   // finite: the tile has a valid token
+        alpha[j] = exp2f(m_run[j] - m_new);
+        m_run[j] = m_new;
+        const float p = valid ? exp2f(lg - m_new) : 0.f;
+        if (GQA == 8 || rq < 2) L.p[hA + j][n] = p;
+        l_part[j] = fmaf(l_part[j], alpha[j], p);
+      }
+      if (n == 0 && pv_rows) {
+        L.alpha[hA] = alpha[0];
+        L.alpha[hA + 1] = alpha[1];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < NH; ++j) mterm[j] *= L.alpha[ph + 4 * j];
+      {
+        const float f0 = pv_rows ? L.alpha[2 * rq] : 0.f;
+        const float f1 = pv_rows ? L.alpha[2 * rq + 1] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          acc[i][0] *= f0;
+          acc[i][1] *= f0;
+          acc[i][2] *= f1;
+          acc[i][3] *= f1;
+          wacc[i][0] *= f0;
+          wacc[i][1] *= f0;
+          wacc[i][2] *= f1;
+          wacc[i][3] *= f1;
+        }
+      }
+      // A = p (hi/lo rows), tokens 8kq..8kq+7 of the tile (kq < 2)
+      u32x4 apw = u32x4{0u, 0u, 0u, 0u};
+      if (m_row < 2 * GQA && kq < 2) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = L.p[m_row >> 1][8 * kq + e];
+        u32x4 hi, lo;
+        split_hilo(v, hi, lo);
+        apw = (m_row & 1) ? lo : hi;
+      }
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
+        const u32x4 bv = kq < 2 ? *reinterpret_cast<const u32x4*>(&L.vt[d][4 * kq])
+                                : u32x4{0u, 0u, 0u, 0u};
+        wacc[blk] = mfma(apw, bv, wacc[blk]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   }
 
   // ---------------------------------------------------------------- block merge
@@ -605,24 +682,21 @@ __global__ __launch_bounds__(kThreadsM, kMfmaBlocksPerCU<GQA>) void decode_mfma_
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
-      M.num[wave][h0][d] = fmaf(acc[blk][0] + acc[blk][1], ev, M.mt[wave][h0]);
-      M.num[wave][h0 + 1][d] = fmaf(acc[blk][2] + acc[blk][3], ev, M.mt[wave][h0 + 1]);
+      M.num[wave][h0][d] = fmaf(acc[blk][0] + acc[blk][1], ev, M.mt[wave][h0]) +
+                           (wacc[blk][0] + wacc[blk][1]);
+      M.num[wave][h0 + 1][d] = fmaf(acc[blk][2] + acc[blk][3], ev, M.mt[wave][h0 + 1]) +
+                               (wacc[blk][2] + wacc[blk][3]);
     }
   }
   __syncthreads();
   const int n_parts = a.n_parts;
   for (int i = tid; i < GQA * kD; i += kThreadsM) {
     const int h = i / kD, d = i % kD;
-    float mm = sh.win.l[h] > 0.f ? sh.win.m[h] : kNegInfM;
+    float mm = kNegInfM;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
       if (M.l[w][h] > 0.f) mm = fmaxf(mm, M.m[w][h]);
     float num = 0.f, den = 0.f;
-    if (sh.win.l[h] > 0.f) {
-      const float f = exp2f(sh.win.m[h] - mm);
-      num = sh.win.acc[h][d] * f;
-      den = sh.win.l[h] * f;
-    }
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
       if (M.l[w][h] > 0.f) {
