@@ -1,0 +1,659 @@
+// Split-K decode attention for 2-bit codes on gfx950 matrix cores, GQA query
+// groups of 4 or 8 heads, group size 128, head dim 128.
+//
+// The query heads that share a kv head form a dense contraction with the kv
+// tile (BitDecoding page, section V.A), so q.K^T and p.V run on
+// v_mfma_scale_f32_16x16x128_f8f6f4 with
+//
+//  * B = the packed 2-bit codes as fp4 (e2m1).  A code c in the low two bits
+//    of a nibble whose high bits are clear is the fp4 value c/2, so one AND
+//    with 0x33333333 turns a 32-bit word of 16 codes into 8 operand nibbles
+//    (the even codes) and a shift plus AND gives the odd ones.  Keys are
+//    packed along channels and values along tokens, the contraction axes, so
+//    a lane's two words are its 32 contraction elements with no shuffle.
+//  * A = the dequantization scales folded into the query / the probabilities
+//    (KIVI page Step 4, x = code*scale + min spread over the dot product):
+//        q.k_t = sum_d (q_d s_d) code_td + sum_d q_d mn_d
+//        p.v_d = sum_t (p_t s_t) code_td + sum_t p_t mn_t
+//    Each A value is scaled by a power of two per group to below 2^8 and
+//    written as the sum of fp8 (e4m3) digits, each the round-to-nearest fp8
+//    value of the remaining residual (about four significant bits per
+//    digit).  The digits are A rows of the same head, so one MFMA per 16
+//    tokens (or 16 channels) serves four heads and the output rows of a head
+//    are summed afterwards.  Values (p s_t) take four digits: their error is
+//    relative to the output.  Keys take five (the fifth in a second MFMA):
+//    logits reach tens of log2 units where outlier channels meet large
+//    queries, and softmax needs them to about 1e-4 absolute.
+//  * sum_d q_d mn_d is a vector-ALU dot product in the A-prep lanes; sum_t
+//    p_t mn_t is a per-head scalar kept beside the accumulator.
+//
+// Lane roles (n = lane & 15, r = lane >> 4): lane (n, r) prepares A values of
+// head r (and r + 4) for channels / tokens 8n..8n+7, and holds the logits and
+// probabilities of the same head for tokens 8n..8n+7 of the group (column n
+// of tile t is token 8n + t), so the probabilities become p.V operands
+// without leaving the lane.  Matrix-core outputs land in lane (n, r) as the
+// four digit rows of head r.
+//
+// Work split: block = 4 waves on one (batch, kv head) and one chunk of groups
+// plus an equal slice of the fp16 sink/residual window; each wave owns whole
+// groups (round robin) with its own online softmax and software-pipelined
+// loads; the window slice runs as 16-token fp16 tiles at the end; the waves
+// merge in LDS and the block writes its partial (m, l, acc).
+
+#include <type_traits>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int kG = 128;          // tokens per group
+constexpr int kWaves = 4;
+constexpr int kThreadsF = 64 * kWaves;
+constexpr int kWpt = kD / 16;     // 2-bit key words per token (8)
+constexpr uint32_t kNib = 0x33333333u;
+constexpr float kNegInfF = -__builtin_inff();
+#ifndef KVQ_KEY_DIGITS
+#define KVQ_KEY_DIGITS 4
+#endif
+constexpr int kKeyDigits = KVQ_KEY_DIGITS;   // fp8 digits of the key-side A values
+
+// ------------------------------------------------------------------ helpers
+
+// A: fp8 e4m3 (format 0) with E8M0 row scale `sa` (the same in every lane of
+// a row), B: fp4 e2m1 (format 4) with unit scale (127)
+__device__ __forceinline__ f32x4 mfma_f8f4(const v8i& a, const v8i& b, f32x4 c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, 127);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+// fp4 B operand from the two words holding contraction elements 32r..32r+15
+// (w0) and 32r+16..32r+31 (w1): nibble j of the operand is element
+// 16*(j/16) + 2*(j%8) + (j/8)%2 of the lane's 32.
+__device__ __forceinline__ v8i fp4_operand(uint32_t w0, uint32_t w1) {
+  return v8i{(int)(w0 & kNib), (int)((w0 >> 2) & kNib), (int)(w1 & kNib),
+             (int)((w1 >> 2) & kNib), 0, 0, 0, 0};
+}
+
+__device__ __forceinline__ float h2f_lo(uint32_t w) { return h2f((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float h2f_hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+
+__device__ __forceinline__ float exp2i(int e) {  // 2^e for e in [-126, 127]
+  return __builtin_bit_cast(float, (uint32_t)(max(-126, min(127, e)) + 127) << 23);
+}
+
+// smallest e with x < 2^e for finite x >= 0 (x == 0 -> -126)
+__device__ __forceinline__ int ceil_exp(float x) {
+  const int b = (int)((__builtin_bit_cast(uint32_t, x) >> 23) & 0xFF);
+  return b == 0 ? -126 : b - 126;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, true));
+}
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadXor2 = 0x4E, kQuadXor1 = 0xB1;
+
+// max / sum over the 16 lanes of a row (every lane of the row gets it)
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<kRowRor8>(v));
+  v = fmaxf(v, dpp<kRowRor4>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  return fmaxf(v, dpp<kQuadXor1>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<kRowRor8>(v);
+  v += dpp<kRowRor4>(v);
+  v += dpp<kQuadXor2>(v);
+  return v + dpp<kQuadXor1>(v);
+}
+
+// ND fp8 digits of four values (x0..x3 -> bytes 0..3 of each digit word).
+// Digit k is the nearest fp8 value of 16^k times what digits 0..k-1 left
+// over (a scaled conversion), so each digit adds about four significant bits
+// and no residual sinks into the fp8 subnormal range; the matrix-core row of
+// digit k carries the block scale 2^-4k that undoes the factor.
+template <int ND>
+__device__ __forceinline__ void fp8_digits(float x0, float x1, float x2, float x3,
+                                           uint32_t (&d)[ND]) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int k = 0; k < ND; ++k) {
+    const float sc = __builtin_bit_cast(float, (uint32_t)(127 - 4 * k) << 23);   // 2^-4k
+    v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, x0, x1, sc, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x2, x3, sc, true);
+    const int wi = __builtin_bit_cast(int, w);
+    d[k] = (uint32_t)wi;
+    if (k < ND - 1) {
+      const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wi, sc, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wi, sc, true);
+      x0 -= lo[0];
+      x1 -= lo[1];
+      x2 -= hi[0];
+      x3 -= hi[1];
+    }
+  }
+}
+
+// Byte offset, inside one [16 rows][4 lane groups][32 B] A-operand tile, of
+// the four even-numbered elements of octet o (items 8o, 8o+2, 8o+4, 8o+6)
+// for row 0; the odd ones sit 8 bytes further.  The B operand's element
+// order (fp4_operand) and the f8f6f4 instruction's A byte order fix it: A
+// byte i of lane group g is contraction element 16g + (i%16) + 64(i/16).
+__device__ __forceinline__ uint32_t a_offset(int o) {
+  const int g = o >> 2, w = (o >> 1) & 1;
+  const int ga = 2 * (g & 1) + w;
+  const int i0 = 16 * (g >> 1) + 4 * (o & 1);
+  return (uint32_t)(ga * 32 + i0);
+}
+
+template <int GQA>
+struct WaveLdsF {
+  static constexpr int NH = GQA / 4;
+  union {
+    struct {
+      uint8_t ak[NH][16][4][32];                  // q.K^T A operand [half][row][g][byte]
+      uint8_t ak5[16][4][32];                     // fifth key digit: row 4r + half
+      uint8_t av[NH][16][4][32];                  // p.V A operand
+    } op;
+    uint32_t vt[kD][8];                           // fp16 window tile, [channel][token pair]
+  };
+  float p[GQA][16];                               // window-tile probabilities
+};
+
+template <int GQA>
+struct MergeLdsF {
+  float num[kWaves][GQA][kD];
+  float m[kWaves][GQA], l[kWaves][GQA];
+};
+
+template <int GQA>
+struct LdsF {
+  union {
+    WaveLdsF<GQA> w[kWaves];
+    MergeLdsF<GQA> merge;
+  } u;
+  u32x4 win_a[GQA / 4][4][4][16];                 // window q.K^T A: [half][c][kq][row]
+};
+
+struct Prefetch {
+  uint32_t kw[8][2];     // key words: tile t, token 8n + t, words 2r, 2r + 1
+  u32x4 ks, kmin;        // key scale / min of channels 8n..8n+7
+  u32x4 vw[2][2];        // value words: rows 2r, 2r + 1; channels 4n.. and 64 + 4n..
+  u32x4 vs, vmn;         // value scale / min of tokens 8n..8n+7
+};
+
+template <typename T>
+__device__ __forceinline__ T ldnt(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
+
+__device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int64_t g, int n,
+                                          int r, Prefetch& f) {
+  const char* kb = reinterpret_cast<const char*>(a.c.k_codes) +
+                   ((head * a.c.t_cap + g * kG + 8 * n) * kWpt + 2 * r) * 4;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const u32x2 v = ldnt<u32x2>(kb + t * kWpt * 4);
+    f.kw[t][0] = v[0];
+    f.kw[t][1] = v[1];
+  }
+  const int64_t mo = ((head * (a.c.t_cap / kG) + g) * kD + 8 * n) * 2;
+  f.ks = ldnt<u32x4>(reinterpret_cast<const char*>(a.c.k_scale) + mo);
+  f.kmin = ldnt<u32x4>(reinterpret_cast<const char*>(a.c.k_min) + mo);
+}
+
+__device__ __forceinline__ void load_values(const DecodeArgs& a, int64_t head, int64_t g, int n,
+                                            int r, Prefetch& f) {
+  const char* vb = reinterpret_cast<const char*>(a.c.v_codes) +
+                   ((head * (a.c.t_cap / 16) + g * (kG / 16) + 2 * r) * kD + 4 * n) * 4;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) f.vw[q][hb] = ldnt<u32x4>(vb + (q * kD + 64 * hb) * 4);
+  const int64_t to = (head * a.c.t_cap + g * kG + 8 * n) * 2;
+  f.vs = ldnt<u32x4>(reinterpret_cast<const char*>(a.c.v_scale) + to);
+  f.vmn = ldnt<u32x4>(reinterpret_cast<const char*>(a.c.v_min) + to);
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 8 fp16 of a u32x4 as floats
+__device__ __forceinline__ void unpack8(const u32x4& v, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = h2f_lo(v[i]);
+    x[2 * i + 1] = h2f_hi(v[i]);
+  }
+}
+
+// Digits of 8 values (items 8o..8o+7): digits 0..3 into rows 4*hr..4*hr+3 of
+// an A tile; with ND == 5 the fifth digit into row `row5` of a second tile.
+template <int ND>
+__device__ __forceinline__ void write_digits(uint8_t (*tile)[4][32], int hr, uint32_t off,
+                                             const float (&x)[8], uint8_t (*tile5)[4][32],
+                                             int row5) {
+  uint32_t de[ND], dodd[ND];
+  fp8_digits<ND>(x[0], x[2], x[4], x[6], de);
+  fp8_digits<ND>(x[1], x[3], x[5], x[7], dodd);
+  uint8_t* base = &tile[4 * hr][0][0] + off;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    *reinterpret_cast<uint32_t*>(base + k * 128) = de[k];
+    *reinterpret_cast<uint32_t*>(base + k * 128 + 8) = dodd[k];
+  }
+  if (ND == 5) {
+    uint8_t* b5 = &tile5[row5][0][0] + off;
+    *reinterpret_cast<uint32_t*>(b5) = de[ND - 1];
+    *reinterpret_cast<uint32_t*>(b5 + 8) = dodd[ND - 1];
+  }
+}
+
+__device__ __forceinline__ v8i read_a(const uint8_t (*tile)[4][32], int m, int g) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(&tile[m][g][0]);
+  const u32x4 lo = p[0], hi = p[1];
+  return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <int GQA>
+__global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a) {
+  constexpr int NH = GQA / 4;    // heads per lane (r and r + 4)
+  __shared__ LdsF<GQA> sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, r = lane >> 4;
+  const int chunk = blockIdx.x;
+  const int64_t head = blockIdx.y;
+  const int64_t b = head / a.H_kv, hk = head % a.H_kv;
+  const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
+
+  // ---------------------------------------------------------------- first loads
+  const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
+  const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
+  Prefetch pf;
+  int64_t g = gb + wave;
+  if (g < ge) {
+    load_keys(a, head, g, n, r, pf);
+    load_values(a, head, g, n, r, pf);
+  }
+
+  // ---------------------------------------------------------------- query
+  // qv[j][e] = q[r + 4j][8n + e] * sm * log2(e) * 2^(8 - e_q), |qv| < 2^8
+  float qv[NH][8];
+  float qmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + (r + 4 * j) * kD + 8 * n);
+    unpack8(raw, qv[j]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[j][e] *= a.qscale;
+      qmax = fmaxf(qmax, fabsf(qv[j][e]));
+    }
+  }
+  qmax = row_max16(qmax);
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+  const int e_q = ceil_exp(qmax);
+  {
+    const float qs = exp2i(8 - e_q);
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[j][e] *= qs;
+  }
+  const float q_unscale = exp2i(e_q - 8);
+
+  // window q.K^T operand: rows 4h' + {hi, lo, 0, 0} of head 4H + h', K-step
+  // c = wave (channels 32c + 8kq + e), natural channel order
+  const int n_win = a.n_sink + a.n_res;
+  const int wpc = n_win > 0 ? (n_win + a.n_chunks - 1) / a.n_chunks : 0;
+  const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
+  if (u1 > u0) {
+    const int m = lane & 15, kq = lane >> 4, c = wave;
+#pragma unroll
+    for (int H = 0; H < NH; ++H) {
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      if ((m & 3) < 2) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + (4 * H + (m >> 2)) * kD +
+                                                          32 * c + 8 * kq);
+        float v[8];
+        unpack8(raw, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = v[2 * i] * a.qscale, x1 = v[2 * i + 1] * a.qscale;
+          const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+          const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]);
+          val[i] = __builtin_bit_cast(uint32_t, (m & 1) ? l : h);
+        }
+      }
+      sh.win_a[H][c][kq][m] = val;
+    }
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- groups
+  WaveLdsF<GQA>& L = sh.u.w[wave];
+  const uint32_t a_off = a_offset(n);
+  const int sa_digit = 127 - 4 * (lane & 3);   // A row m = lane & 15 holds digit m % 4
+  constexpr int kSa5 = 127 - 16;
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(&L.op.ak5[0][0][0]);
+    z[2 * lane] = u32x4{0u, 0u, 0u, 0u};
+    z[2 * lane + 1] = u32x4{0u, 0u, 0u, 0u};
+  }
+  float m_run[NH], l_part[NH], mterm[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    m_run[j] = kNegInfF;
+    l_part[j] = 0.f;
+    mterm[j] = 0.f;
+  }
+  int e_v = -1000;                 // running value-side exponent
+  f32x4 acc[NH][8];                // p.V: [head half][channel block], 4 digit rows
+#pragma unroll
+  for (int H = 0; H < NH; ++H)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto group_step = [&](auto prefetch_tag) {
+    constexpr bool PREFETCH = decltype(prefetch_tag)::value;
+    const int64_t gn = g + kWaves;
+
+    // ---- key A operand: digits of q s 2^(8 - e_q - e_s); bias q . mn
+    float ks[8], km[8];
+    unpack8(pf.ks, ks);
+    unpack8(pf.kmin, km);
+    float smax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) smax = fmaxf(smax, ks[e]);
+    smax = row_max16(smax);
+    const int e_s = ceil_exp(smax);
+    const float sk = exp2i(-e_s);
+    float bias[NH];
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      float x[8];
+      float bsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = qv[j][e] * (ks[e] * sk);
+        bsum = fmaf(qv[j][e], km[e], bsum);
+      }
+      bias[j] = row_sum16(bsum) * q_unscale;
+      write_digits<kKeyDigits>(L.op.ak[j], r, a_off, x, L.op.ak5, 4 * r + j);
+    }
+    wave_sync();
+
+    // ---- q.K^T: one MFMA per 16-token tile and head half
+    float logit[NH][8];
+    {
+      const float ek = exp2i(e_q - 8 + e_s + 1);   // fp4 codes are c/2
+      const v8i a5 = kKeyDigits == 5 ? read_a(L.op.ak5, lane & 15, lane >> 4) : v8i{};
+      v8i aq[NH];
+#pragma unroll
+      for (int H = 0; H < NH; ++H) aq[H] = read_a(L.op.ak[H], lane & 15, lane >> 4);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const v8i bk = fp4_operand(pf.kw[t][0], pf.kw[t][1]);
+        const f32x4 c5 = kKeyDigits == 5 ? mfma_f8f4(a5, bk, f32x4{0.f, 0.f, 0.f, 0.f}, kSa5)
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int H = 0; H < NH; ++H) {
+          const f32x4 c = mfma_f8f4(aq[H], bk, f32x4{0.f, 0.f, 0.f, 0.f}, sa_digit);
+          logit[H][t] = fmaf(((c[0] + c[1]) + (c[2] + c[3])) + c5[H], ek, bias[H]);
+        }
+      }
+    }
+    if (PREFETCH) load_keys(a, head, gn, n, r, pf);
+
+    // ---- online softmax (lane: head r + 4H, tokens 8n..8n+7)
+    float alpha[NH];
+    float p[NH][8];
+#pragma unroll
+    for (int H = 0; H < NH; ++H) {
+      float v = logit[H][0];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) v = fmaxf(v, logit[H][t]);
+      v = row_max16(v);
+      const float m_new = fmaxf(m_run[H], v);
+      alpha[H] = exp2f(m_run[H] - m_new);
+      m_run[H] = m_new;
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        p[H][t] = exp2f(logit[H][t] - m_new);
+        sum += p[H][t];
+      }
+      l_part[H] = fmaf(l_part[H], alpha[H], sum);
+    }
+
+    // ---- value A operand: digits of p s_t 2^(8 - e_v); min term
+    float vs[8], vm[8];
+    unpack8(pf.vs, vs);
+    unpack8(pf.vmn, vm);
+    float vmax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, vs[e]);
+    vmax = row_max16(vmax);
+    const int e_v_new = max(e_v, ceil_exp(vmax));
+    const float vshift = exp2i(e_v - e_v_new);
+    const float sv = exp2i(8 - e_v_new);
+    e_v = e_v_new;
+#pragma unroll
+    for (int H = 0; H < NH; ++H) {
+      float x[8];
+      float mt = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = p[H][e] * (vs[e] * sv);
+        mt = fmaf(p[H][e], vm[e], mt);
+      }
+      mterm[H] = fmaf(mterm[H], alpha[H], mt);
+      write_digits<4>(L.op.av[H], r, a_off, x, nullptr, 0);
+    }
+    wave_sync();
+
+    // ---- rescale the accumulators (alpha and the exponent change)
+    {
+      bool same = true;
+#pragma unroll
+      for (int H = 0; H < NH; ++H) same = same && alpha[H] * vshift == 1.f;
+      if (!__all(same)) {
+#pragma unroll
+        for (int H = 0; H < NH; ++H) {
+          const float f = alpha[H] * vshift;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[H][i] *= f;
+        }
+      }
+    }
+
+    // ---- p.V: one MFMA per 16-channel block and head half
+#pragma unroll
+    for (int H = 0; H < NH; ++H) {
+      const v8i apv = read_a(L.op.av[H], lane & 15, lane >> 4);
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const int hb = blk >> 2, comp = blk & 3;
+        acc[H][blk] = mfma_f8f4(apv, fp4_operand(pf.vw[0][hb][comp], pf.vw[1][hb][comp]),
+                                acc[H][blk], sa_digit);
+      }
+    }
+    if (PREFETCH) load_values(a, head, gn, n, r, pf);
+    wave_sync();
+  };
+
+  if (g < ge) {
+    for (; g + kWaves < ge; g += kWaves) group_step(std::true_type{});
+    group_step(std::false_type{});
+  }
+
+  // ---------------------------------------------------------------- fp16 window
+  // Window tokens [u0, u1) of sink | residual; wave w takes 16-token tiles
+  // w, w + 4, ...: q.K^T on fp16 matrix cores (raw keys as B), the same
+  // online softmax, p.V through an LDS transpose of the fp16 values into a
+  // natural-scale accumulator.
+  f32x4 wacc[NH][8];
+#pragma unroll
+  for (int H = 0; H < NH; ++H)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wacc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    const int kq = lane >> 4, m_row = lane & 15;
+    auto row = [&](const uint16_t* sink, const uint16_t* res, int u) -> const uint16_t* {
+      return u < a.n_sink ? sink + (head * a.sink_cap + u) * kD
+                          : res + (head * a.res_cap + (u - a.n_sink)) * kD;
+    };
+    for (int u = u0 + 16 * wave; u < u1; u += 16 * kWaves) {
+      const int nt = min(16, u1 - u);
+      // keys of token n (rows past the tile end repeat its last token)
+      const uint16_t* kr = row(a.k_sink, a.k_res, u + min(n, nt - 1));
+      u32x4 kv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kv[c] = *reinterpret_cast<const u32x4*>(kr + 32 * c + 8 * kq);
+      // values: lane (token pair j, 16-channel group cg) -> vt[channel][j]
+      {
+        const int j = lane & 7, cg = lane >> 3;
+        const uint16_t* r0 = row(a.v_sink, a.v_res, u + min(2 * j, nt - 1)) + 16 * cg;
+        const uint16_t* r1 = row(a.v_sink, a.v_res, u + min(2 * j + 1, nt - 1)) + 16 * cg;
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(r0);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(r0 + 8);
+        const u32x4 y0 = *reinterpret_cast<const u32x4*>(r1);
+        const u32x4 y1 = *reinterpret_cast<const u32x4*>(r1 + 8);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t x = q < 4 ? x0[q] : x1[q - 4];
+          const uint32_t y = q < 4 ? y0[q] : y1[q - 4];
+          L.vt[16 * cg + 2 * q][j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+          L.vt[16 * cg + 2 * q + 1][j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+        }
+      }
+      const bool valid = n < nt;
+      float alpha[NH];
+#pragma unroll
+      for (int H = 0; H < NH; ++H) {
+        f32x4 cw = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cw = mfma_f16(sh.win_a[H][c][kq][m_row], kv[c], cw);
+        const float lg = valid ? cw[0] + cw[1] : kNegInfF;
+        const float v = row_max16(lg);
+        const float m_new = fmaxf(m_run[H], v);   // finite: the tile has a valid token
+        alpha[H] = exp2f(m_run[H] - m_new);
+        m_run[H] = m_new;
+        const float pw = valid ? exp2f(lg - m_new) : 0.f;
+        L.p[r + 4 * H][n] = pw;
+        l_part[H] = fmaf(l_part[H], alpha[H], pw);
+        mterm[H] *= alpha[H];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          acc[H][i] *= alpha[H];
+          wacc[H][i] *= alpha[H];
+        }
+      }
+      wave_sync();
+#pragma unroll
+      for (int H = 0; H < NH; ++H) {
+        // A = p (rows 4h' + {hi, lo, 0, 0}), tokens 8kq..8kq+7 of the tile (kq < 2)
+        u32x4 apw = u32x4{0u, 0u, 0u, 0u};
+        if ((m_row & 3) < 2 && kq < 2) {
+          const float* pp = &L.p[4 * H + (m_row >> 2)][8 * kq];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x0 = pp[2 * i], x1 = pp[2 * i + 1];
+            const auto hi = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+            const auto lo = __builtin_amdgcn_cvt_pkrtz(x0 - (float)hi[0], x1 - (float)hi[1]);
+            apw[i] = __builtin_bit_cast(uint32_t, (m_row & 1) ? lo : hi);
+          }
+        }
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+          const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
+          const u32x4 bv = kq < 2 ? *reinterpret_cast<const u32x4*>(&L.vt[d][4 * kq])
+                                  : u32x4{0u, 0u, 0u, 0u};
+          wacc[H][blk] = mfma_f16(apw, bv, wacc[H][blk]);
+        }
+      }
+      wave_sync();
+    }
+  }
+
+  // ---------------------------------------------------------------- block merge
+  float lsum[NH], mtsum[NH];
+#pragma unroll
+  for (int H = 0; H < NH; ++H) {
+    lsum[H] = row_sum16(l_part[H]);
+    mtsum[H] = row_sum16(mterm[H]);
+  }
+  __syncthreads();   // the per-wave buffers are reused for the merge below
+  MergeLdsF<GQA>& M = sh.u.merge;
+  const float ev = exp2i(e_v - 8 + 1);   // p.V digits carry 2^(8 - e_v), codes are c/2
+#pragma unroll
+  for (int H = 0; H < NH; ++H) {
+    const int h = r + 4 * H;
+    if (n == 0) {
+      M.m[wave][h] = m_run[H];
+      M.l[wave][h] = lsum[H];
+    }
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
+      const f32x4 v = acc[H][blk];
+      M.num[wave][h][d] = fmaf((v[0] + v[1]) + (v[2] + v[3]), ev, mtsum[H]) +
+                          (wacc[H][blk][0] + wacc[H][blk][1]);
+    }
+  }
+  __syncthreads();
+  const int n_parts = a.n_parts;
+  for (int i = tid; i < GQA * kD; i += kThreadsF) {
+    const int h = i / kD, d = i % kD;
+    float mm = kNegInfF;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (M.l[w][h] > 0.f) mm = fmaxf(mm, M.m[w][h]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (M.l[w][h] > 0.f) {
+        const float f = exp2f(M.m[w][h] - mm);
+        num = fmaf(M.num[w][h][d], f, num);
+        den = fmaf(M.l[w][h], f, den);
+      }
+    float* wp = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + chunk) * (kD + 2);
+    wp[2 + d] = num;
+    if (d == 0) {
+      wp[0] = mm;
+      wp[1] = den;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
+  if (a.gqa == 4) decode_f8f4_kernel<4><<<grid, kThreadsF, 0, st>>>(a);
+  else decode_f8f4_kernel<8><<<grid, kThreadsF, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -719,8 +719,7 @@ __global__ __launch_bounds__(kThreadsM, kMfmaBlocksPerCU<GQA>) void decode_mfma_
 hipError_t launch_decode_mfma(int bits, const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
   if (bits == 2) {
-    if (a.gqa == 4) decode_mfma_kernel<2, 4><<<grid, kThreadsM, 0, st>>>(a);
-    else decode_mfma_kernel<2, 8><<<grid, kThreadsM, 0, st>>>(a);
+    return launch_decode_f8f4(a, st);   // fp8 x fp4 matrix cores
   } else {
     if (a.gqa == 4) decode_mfma_kernel<4, 4><<<grid, kThreadsM, 0, st>>>(a);
     else decode_mfma_kernel<4, 8><<<grid, kThreadsM, 0, st>>>(a);

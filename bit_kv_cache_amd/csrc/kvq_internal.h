@@ -103,5 +103,6 @@ hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStrea
 hipError_t launch_decode_partials(int bits, int group, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma(int bits, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace kvq
