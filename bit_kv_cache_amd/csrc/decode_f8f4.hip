@@ -20,27 +20,24 @@
 //    value of the remaining residual (about four significant bits per
 //    digit).  The digits are A rows of the same head, so one MFMA per 16
 //    tokens (or 16 channels) serves four heads and the output rows of a head
-//    are summed afterwards.  Values (p s_t) take four digits: their error is
-//    relative to the output.  Keys take five (the fifth in a second MFMA):
-//    logits reach tens of log2 units where outlier channels meet large
-//    queries, and softmax needs them to about 1e-4 absolute.
+//    are summed afterwards.  Four digits carry about 16 bits; each digit's
+//    conversion is scaled by 2^-4k (undone by the MFMA's per-row E8M0 block
+//    scale) so small residuals never fall into fp8's subnormal range.
 //  * sum_d q_d mn_d is a vector-ALU dot product in the A-prep lanes; sum_t
 //    p_t mn_t is a per-head scalar kept beside the accumulator.
 //
 // Lane roles (n = lane & 15, r = lane >> 4): lane (n, r) prepares A values of
-// head r (and r + 4) for channels / tokens 8n..8n+7, and holds the logits and
-// probabilities of the same head for tokens 8n..8n+7 of the group (column n
-// of tile t is token 8n + t), so the probabilities become p.V operands
-// without leaving the lane.  Matrix-core outputs land in lane (n, r) as the
-// four digit rows of head r.
+// head r (and r + 4) for channels / tokens 8n..8n+7, and holds the logits of
+// the same head for tokens 16t + n (column n of tile t, so each key load
+// instruction reads 512 contiguous bytes); the probabilities pass through a
+// small LDS transpose to the lanes that prepare the p.V operand.
+// Matrix-core outputs land in lane (n, r) as the four digit rows of head r.
 //
 // Work split: block = 4 waves on one (batch, kv head) and one chunk of groups
 // plus an equal slice of the fp16 sink/residual window; each wave owns whole
 // groups (round robin) with its own online softmax and software-pipelined
 // loads; the window slice runs as 16-token fp16 tiles at the end; the waves
 // merge in LDS and the block writes its partial (m, l, acc).
-
-#include <type_traits>
 
 #include "kvq_internal.h"
 
@@ -60,10 +57,7 @@ constexpr int kThreadsF = 64 * kWaves;
 constexpr int kWpt = kD / 16;     // 2-bit key words per token (8)
 constexpr uint32_t kNib = 0x33333333u;
 constexpr float kNegInfF = -__builtin_inff();
-#ifndef KVQ_KEY_DIGITS
-#define KVQ_KEY_DIGITS 4
-#endif
-constexpr int kKeyDigits = KVQ_KEY_DIGITS;   // fp8 digits of the key-side A values
+constexpr int kDigits = 4;        // fp8 digits of an A value
 
 // ------------------------------------------------------------------ helpers
 
@@ -101,9 +95,13 @@ __device__ __forceinline__ int ceil_exp(float x) {
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                                 0xF, 0xF, true));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                              0xF, true));
 }
+
+// 2^x with the hardware instruction (results below 2^-126 flush to zero,
+// which softmax weights can afford)
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kQuadXor2 = 0x4E, kQuadXor1 = 0xB1;
 
 // max / sum over the 16 lanes of a row (every lane of the row gets it)
@@ -113,6 +111,24 @@ __device__ __forceinline__ float row_max16(float v) {
   v = fmaxf(v, dpp<kQuadXor2>(v));
   return fmaxf(v, dpp<kQuadXor1>(v));
 }
+__device__ __forceinline__ uint32_t row_max16u(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kRowRor8, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kRowRor4, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor2, 0xF, 0xF, true));
+  return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, true));
+}
+
+// Largest of 8 non-negative fp16 values (as bits: their order as unsigned
+// integers is their numeric order), over the 16 lanes of the row, returned
+// as the smallest e with every value < 2^e (-14 for subnormal or zero).
+__device__ __forceinline__ int row_exp_f16(const u32x4& v) {
+  const uint32_t lo = max(max(v[0] & 0xFFFFu, v[1] & 0xFFFFu), max(v[2] & 0xFFFFu, v[3] & 0xFFFFu));
+  const uint32_t hi = max(max(v[0] >> 16, v[1] >> 16), max(v[2] >> 16, v[3] >> 16));
+  const uint32_t top = row_max16u(max(lo, hi));
+  const int ef = (int)(top >> 10);                 // biased fp16 exponent
+  return (ef == 0 ? 1 : ef) - 14;
+}
+
 __device__ __forceinline__ float row_sum16(float v) {
   v += dpp<kRowRor8>(v);
   v += dpp<kRowRor4>(v);
@@ -120,23 +136,23 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v + dpp<kQuadXor1>(v);
 }
 
-// ND fp8 digits of four values (x0..x3 -> bytes 0..3 of each digit word).
-// Digit k is the nearest fp8 value of 16^k times what digits 0..k-1 left
-// over (a scaled conversion), so each digit adds about four significant bits
-// and no residual sinks into the fp8 subnormal range; the matrix-core row of
-// digit k carries the block scale 2^-4k that undoes the factor.
-template <int ND>
-__device__ __forceinline__ void fp8_digits(float x0, float x1, float x2, float x3,
-                                           uint32_t (&d)[ND]) {
+// Four fp8 digits of four values (x0..x3 -> bytes 0..3 of each digit word).
+// Digit k is the nearest fp8 value of what digits 0..k-1 left over, divided
+// by 2^(eb - 4k) (a scaled conversion), so each digit adds about four
+// significant bits and no residual sinks into the fp8 subnormal range; the
+// matrix-core row of digit k carries the block scale 2^-4k, so the rows of a
+// value add up to x / 2^eb.
+__device__ __forceinline__ void fp8_digits(float x0, float x1, float x2, float x3, int eb,
+                                           uint32_t (&d)[kDigits]) {
   typedef short v2s __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int k = 0; k < ND; ++k) {
-    const float sc = __builtin_bit_cast(float, (uint32_t)(127 - 4 * k) << 23);   // 2^-4k
+  for (int k = 0; k < kDigits; ++k) {
+    const float sc = exp2i(eb - 4 * k);
     v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, x0, x1, sc, false);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x2, x3, sc, true);
     const int wi = __builtin_bit_cast(int, w);
     d[k] = (uint32_t)wi;
-    if (k < ND - 1) {
+    if (k < kDigits - 1) {
       const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wi, sc, false);
       const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wi, sc, true);
       x0 -= lo[0];
@@ -147,9 +163,9 @@ __device__ __forceinline__ void fp8_digits(float x0, float x1, float x2, float x
   }
 }
 
-// Byte offset, inside one [16 rows][4 lane groups][32 B] A-operand tile, of
-// the four even-numbered elements of octet o (items 8o, 8o+2, 8o+4, 8o+6)
-// for row 0; the odd ones sit 8 bytes further.  The B operand's element
+// Byte offset, inside row 0 of an A-operand tile (4 lane groups x 32 B), of
+// the four even-numbered elements of octet o (items 8o, 8o+2, 8o+4, 8o+6);
+// the odd ones sit 8 bytes further.  The B operand's element
 // order (fp4_operand) and the f8f6f4 instruction's A byte order fix it: A
 // byte i of lane group g is contraction element 16g + (i%16) + 64(i/16).
 __device__ __forceinline__ uint32_t a_offset(int o) {
@@ -159,18 +175,25 @@ __device__ __forceinline__ uint32_t a_offset(int o) {
   return (uint32_t)(ga * 32 + i0);
 }
 
+// A-operand tile: 16 rows of 4 lane groups x 32 bytes, rows padded to 144
+// bytes so the 16 rows a 128-bit read touches fall in different LDS banks.
+constexpr int kRowBytes = 144;
+typedef uint8_t ATile[16][kRowBytes];
+
 template <int GQA>
 struct WaveLdsF {
   static constexpr int NH = GQA / 4;
   union {
     struct {
-      uint8_t ak[NH][16][4][32];                  // q.K^T A operand [half][row][g][byte]
-      uint8_t ak5[16][4][32];                     // fifth key digit: row 4r + half
-      uint8_t av[NH][16][4][32];                  // p.V A operand
+      ATile ak[NH];                               // q.K^T A operand [half][row][g*32 + byte]
+      ATile av[NH];                               // p.V A operand
     } op;
-    uint32_t vt[kD][8];                           // fp16 window tile, [channel][token pair]
+    uint32_t vt[kD][12];                          // fp16 window tile, [channel][token pair]
+                                                  // (rows padded to 48 bytes)
   };
   float p[GQA][16];                               // window-tile probabilities
+  float pt[GQA][kG + 4];                          // group probabilities [head][token]
+                                                  // (rows padded: 4 heads, 4 banks apart)
 };
 
 template <int GQA>
@@ -189,7 +212,7 @@ struct LdsF {
 };
 
 struct Prefetch {
-  uint32_t kw[8][2];     // key words: tile t, token 8n + t, words 2r, 2r + 1
+  uint32_t kw[8][2];     // key words: tile t, token 16t + n, words 2r, 2r + 1
   u32x4 ks, kmin;        // key scale / min of channels 8n..8n+7
   u32x4 vw[2][2];        // value words: rows 2r, 2r + 1; channels 4n.. and 64 + 4n..
   u32x4 vs, vmn;         // value scale / min of tokens 8n..8n+7
@@ -203,10 +226,10 @@ __device__ __forceinline__ T ldnt(const char* p) {
 __device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int64_t g, int n,
                                           int r, Prefetch& f) {
   const char* kb = reinterpret_cast<const char*>(a.c.k_codes) +
-                   ((head * a.c.t_cap + g * kG + 8 * n) * kWpt + 2 * r) * 4;
+                   ((head * a.c.t_cap + g * kG + n) * kWpt + 2 * r) * 4;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const u32x2 v = ldnt<u32x2>(kb + t * kWpt * 4);
+    const u32x2 v = ldnt<u32x2>(kb + 16 * t * kWpt * 4);
     f.kw[t][0] = v[0];
     f.kw[t][1] = v[1];
   }
@@ -228,9 +251,12 @@ __device__ __forceinline__ void load_values(const DecodeArgs& a, int64_t head, i
   f.vmn = ldnt<u32x4>(reinterpret_cast<const char*>(a.c.v_min) + to);
 }
 
+// Orders this wave's LDS writes before its later LDS reads of other lanes'
+// data (the hardware executes one wave's LDS operations in order; this keeps
+// the compiler from moving the accesses across each other, while other
+// instructions may still be scheduled across it).
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
@@ -243,37 +269,30 @@ __device__ __forceinline__ void unpack8(const u32x4& v, float (&x)[8]) {
   }
 }
 
-// Digits of 8 values (items 8o..8o+7): digits 0..3 into rows 4*hr..4*hr+3 of
-// an A tile; with ND == 5 the fifth digit into row `row5` of a second tile.
-template <int ND>
-__device__ __forceinline__ void write_digits(uint8_t (*tile)[4][32], int hr, uint32_t off,
-                                             const float (&x)[8], uint8_t (*tile5)[4][32],
-                                             int row5) {
-  uint32_t de[ND], dodd[ND];
-  fp8_digits<ND>(x[0], x[2], x[4], x[6], de);
-  fp8_digits<ND>(x[1], x[3], x[5], x[7], dodd);
-  uint8_t* base = &tile[4 * hr][0][0] + off;
+// Digits of 8 values (items 8o..8o+7) over 2^eb into rows 4*hr..4*hr+3 of an
+// A tile.
+__device__ __forceinline__ void write_digits(ATile& tile, int hr, uint32_t off,
+                                             const float (&x)[8], int eb) {
+  uint32_t de[kDigits], dodd[kDigits];
+  fp8_digits(x[0], x[2], x[4], x[6], eb, de);
+  fp8_digits(x[1], x[3], x[5], x[7], eb, dodd);
+  uint8_t* base = &tile[4 * hr][0] + off;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    *reinterpret_cast<uint32_t*>(base + k * 128) = de[k];
-    *reinterpret_cast<uint32_t*>(base + k * 128 + 8) = dodd[k];
-  }
-  if (ND == 5) {
-    uint8_t* b5 = &tile5[row5][0][0] + off;
-    *reinterpret_cast<uint32_t*>(b5) = de[ND - 1];
-    *reinterpret_cast<uint32_t*>(b5 + 8) = dodd[ND - 1];
+  for (int k = 0; k < kDigits; ++k) {
+    *reinterpret_cast<uint32_t*>(base + k * kRowBytes) = de[k];
+    *reinterpret_cast<uint32_t*>(base + k * kRowBytes + 8) = dodd[k];
   }
 }
 
-__device__ __forceinline__ v8i read_a(const uint8_t (*tile)[4][32], int m, int g) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(&tile[m][g][0]);
+__device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(&tile[m][32 * g]);
   const u32x4 lo = p[0], hi = p[1];
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
 template <int GQA>
-__global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_f8f4_kernel(DecodeArgs a) {
   constexpr int NH = GQA / 4;    // heads per lane (r and r + 4)
   __shared__ LdsF<GQA> sh;
 
@@ -289,12 +308,21 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a)
   // ---------------------------------------------------------------- first loads
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
   const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
-  Prefetch pf;
+  // Two prefetch buffers: a wave's groups alternate between them, and the
+  // loads for group g + 8 are issued while group g computes, so a group's
+  // data has a whole iteration to arrive.  Loads are issued unconditionally
+  // (exact wait counts); past the chunk end they read group 0 of head 0,
+  // which every such load shares, instead of new memory.
+  Prefetch pfa, pfb;
   int64_t g = gb + wave;
-  if (g < ge) {
-    load_keys(a, head, g, n, r, pf);
-    load_values(a, head, g, n, r, pf);
-  }
+  auto fetch = [&](int64_t gi, Prefetch& f) {
+    const bool in = gi < ge;
+    const int64_t hh = in ? head : 0, gg = in ? gi : 0;
+    load_keys(a, hh, gg, n, r, f);
+    load_values(a, hh, gg, n, r, f);
+  };
+  fetch(g, pfa);
+  fetch(g + kWaves, pfb);
 
   // ---------------------------------------------------------------- query
   // qv[j][e] = q[r + 4j][8n + e] * sm * log2(e) * 2^(8 - e_q), |qv| < 2^8
@@ -355,12 +383,6 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a)
   WaveLdsF<GQA>& L = sh.u.w[wave];
   const uint32_t a_off = a_offset(n);
   const int sa_digit = 127 - 4 * (lane & 3);   // A row m = lane & 15 holds digit m % 4
-  constexpr int kSa5 = 127 - 16;
-  {
-    u32x4* z = reinterpret_cast<u32x4*>(&L.op.ak5[0][0][0]);
-    z[2 * lane] = u32x4{0u, 0u, 0u, 0u};
-    z[2 * lane + 1] = u32x4{0u, 0u, 0u, 0u};
-  }
   float m_run[NH], l_part[NH], mterm[NH];
 #pragma unroll
   for (int j = 0; j < NH; ++j) {
@@ -375,60 +397,69 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto group_step = [&](auto prefetch_tag) {
-    constexpr bool PREFETCH = decltype(prefetch_tag)::value;
-    const int64_t gn = g + kWaves;
+  // The loop is software-pipelined over a wave's groups: while group g's
+  // softmax, value operand and p.V run, the key operand and q.K^T matrix
+  // products of group g + 4 are already issued, so the two dependency chains
+  // interleave.  Buffer parity: group g's data sits in pfa or pfb; its keys
+  // are consumed one iteration before its values.
+  int e_s_n = 0;                 // key exponent of the group whose q.K^T is in flight
+  float bias_n[NH];              // its q . key-min terms
+  f32x4 cq[NH][8];               // its q.K^T digit rows, per tile
+  auto clamp_group = [&](int64_t gi, int64_t& hh, int64_t& gg) {
+    const bool in = gi < ge;
+    hh = in ? head : 0;
+    gg = in ? gi : 0;
+  };
 
-    // ---- key A operand: digits of q s 2^(8 - e_q - e_s); bias q . mn
-    float ks[8], km[8];
-    unpack8(pf.ks, ks);
-    unpack8(pf.kmin, km);
-    float smax = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) smax = fmaxf(smax, ks[e]);
-    smax = row_max16(smax);
-    const int e_s = ceil_exp(smax);
-    const float sk = exp2i(-e_s);
-    float bias[NH];
+  // key A operand of the group in pf, its q.K^T MFMAs; pf then receives the
+  // keys of group gk + 8
+  auto qk_issue = [&](Prefetch& pf, int64_t gk) {
+    e_s_n = row_exp_f16(pf.ks);
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
       float x[8];
       float bsum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = qv[j][e] * (ks[e] * sk);
-        bsum = fmaf(qv[j][e], km[e], bsum);
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = fmaf(qv[j][2 * i], h2f_lo(pf.ks[i]), 0.f);
+        x[2 * i + 1] = fmaf(qv[j][2 * i + 1], h2f_hi(pf.ks[i]), 0.f);
+        bsum = fmaf(qv[j][2 * i], h2f_lo(pf.kmin[i]), bsum);
+        bsum = fmaf(qv[j][2 * i + 1], h2f_hi(pf.kmin[i]), bsum);
       }
-      bias[j] = row_sum16(bsum) * q_unscale;
-      write_digits<kKeyDigits>(L.op.ak[j], r, a_off, x, L.op.ak5, 4 * r + j);
+      bias_n[j] = row_sum16(bsum) * q_unscale;
+      write_digits(L.op.ak[j], r, a_off, x, e_s_n);
     }
     wave_sync();
-
-    // ---- q.K^T: one MFMA per 16-token tile and head half
-    float logit[NH][8];
-    {
-      const float ek = exp2i(e_q - 8 + e_s + 1);   // fp4 codes are c/2
-      const v8i a5 = kKeyDigits == 5 ? read_a(L.op.ak5, lane & 15, lane >> 4) : v8i{};
-      v8i aq[NH];
+    v8i aq[NH];
 #pragma unroll
-      for (int H = 0; H < NH; ++H) aq[H] = read_a(L.op.ak[H], lane & 15, lane >> 4);
+    for (int H = 0; H < NH; ++H) aq[H] = read_a(L.op.ak[H], lane & 15, lane >> 4);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const v8i bk = fp4_operand(pf.kw[t][0], pf.kw[t][1]);
-        const f32x4 c5 = kKeyDigits == 5 ? mfma_f8f4(a5, bk, f32x4{0.f, 0.f, 0.f, 0.f}, kSa5)
-                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t) {
+      const v8i bk = fp4_operand(pf.kw[t][0], pf.kw[t][1]);
 #pragma unroll
-        for (int H = 0; H < NH; ++H) {
-          const f32x4 c = mfma_f8f4(aq[H], bk, f32x4{0.f, 0.f, 0.f, 0.f}, sa_digit);
-          logit[H][t] = fmaf(((c[0] + c[1]) + (c[2] + c[3])) + c5[H], ek, bias[H]);
-        }
-      }
+      for (int H = 0; H < NH; ++H)
+        cq[H][t] = mfma_f8f4(aq[H], bk, f32x4{0.f, 0.f, 0.f, 0.f}, sa_digit);
     }
-    if (PREFETCH) load_keys(a, head, gn, n, r, pf);
+    int64_t hh, gg;
+    clamp_group(gk + 2 * kWaves, hh, gg);
+    load_keys(a, hh, gg, n, r, pf);
+  };
 
-    // ---- online softmax (lane: head r + 4H, tokens 8n..8n+7)
+  // logits of the group whose q.K^T was issued last
+  auto qk_finish = [&](float (&logit)[NH][8]) {
+    const float ek = exp2i(e_q - 8 + e_s_n + 1);   // fp4 codes are c/2
+#pragma unroll
+    for (int H = 0; H < NH; ++H)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        logit[H][t] =
+            fmaf((cq[H][t][0] + cq[H][t][1]) + (cq[H][t][2] + cq[H][t][3]), ek, bias_n[H]);
+  };
+
+  // softmax, value A operand and p.V of the group in pf; pf then receives
+  // the values of group gv + 8
+  auto pv_step = [&](Prefetch& pf, int64_t gv, const float (&logit)[NH][8]) {
     float alpha[NH];
-    float p[NH][8];
 #pragma unroll
     for (int H = 0; H < NH; ++H) {
       float v = logit[H][0];
@@ -436,44 +467,51 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a)
       for (int t = 1; t < 8; ++t) v = fmaxf(v, logit[H][t]);
       v = row_max16(v);
       const float m_new = fmaxf(m_run[H], v);
-      alpha[H] = exp2f(m_run[H] - m_new);
+      alpha[H] = fexp2(m_run[H] - m_new);
       m_run[H] = m_new;
       float sum = 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        p[H][t] = exp2f(logit[H][t] - m_new);
-        sum += p[H][t];
+        const float pe = fexp2(logit[H][t] - m_new);   // token 16t + n
+        L.pt[r + 4 * H][16 * t + n] = pe;
+        sum += pe;
       }
       l_part[H] = fmaf(l_part[H], alpha[H], sum);
     }
-
-    // ---- value A operand: digits of p s_t 2^(8 - e_v); min term
-    float vs[8], vm[8];
-    unpack8(pf.vs, vs);
-    unpack8(pf.vmn, vm);
-    float vmax = 0.f;
+    wave_sync();
+    float p[NH][8];                // tokens 8n..8n+7 of head r + 4H
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, vs[e]);
-    vmax = row_max16(vmax);
-    const int e_v_new = max(e_v, ceil_exp(vmax));
+    for (int H = 0; H < NH; ++H) {
+      const f32x4* pp = reinterpret_cast<const f32x4*>(&L.pt[r + 4 * H][8 * n]);
+      const f32x4 p0 = pp[0], p1 = pp[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[H][e] = p0[e];
+        p[H][4 + e] = p1[e];
+      }
+    }
+
+    // value A operand: digits of p s_t 2^(8 - e_v); min term
+    const int e_v_new = max(e_v, row_exp_f16(pf.vs));
     const float vshift = exp2i(e_v - e_v_new);
-    const float sv = exp2i(8 - e_v_new);
     e_v = e_v_new;
 #pragma unroll
     for (int H = 0; H < NH; ++H) {
       float x[8];
       float mt = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = p[H][e] * (vs[e] * sv);
-        mt = fmaf(p[H][e], vm[e], mt);
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = fmaf(p[H][2 * i], h2f_lo(pf.vs[i]), 0.f);
+        x[2 * i + 1] = fmaf(p[H][2 * i + 1], h2f_hi(pf.vs[i]), 0.f);
+        mt = fmaf(p[H][2 * i], h2f_lo(pf.vmn[i]), mt);
+        mt = fmaf(p[H][2 * i + 1], h2f_hi(pf.vmn[i]), mt);
       }
       mterm[H] = fmaf(mterm[H], alpha[H], mt);
-      write_digits<4>(L.op.av[H], r, a_off, x, nullptr, 0);
+      write_digits(L.op.av[H], r, a_off, x, e_v - 8);
     }
     wave_sync();
 
-    // ---- rescale the accumulators (alpha and the exponent change)
+    // rescale the accumulators (alpha and the exponent change)
     {
       bool same = true;
 #pragma unroll
@@ -488,7 +526,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a)
       }
     }
 
-    // ---- p.V: one MFMA per 16-channel block and head half
+    // p.V: one MFMA per 16-channel block and head half
 #pragma unroll
     for (int H = 0; H < NH; ++H) {
       const v8i apv = read_a(L.op.av[H], lane & 15, lane >> 4);
@@ -499,13 +537,27 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a)
                                 acc[H][blk], sa_digit);
       }
     }
-    if (PREFETCH) load_values(a, head, gn, n, r, pf);
-    wave_sync();
+    int64_t hh, gg;
+    clamp_group(gv + 2 * kWaves, hh, gg);
+    load_values(a, hh, gg, n, r, pf);
   };
 
   if (g < ge) {
-    for (; g + kWaves < ge; g += kWaves) group_step(std::true_type{});
-    group_step(std::false_type{});
+    float logit[NH][8];
+    qk_issue(pfa, g);
+    qk_finish(logit);
+    for (;;) {
+      qk_issue(pfb, g + kWaves);     // next group's keys (a dummy past the end)
+      pv_step(pfa, g, logit);
+      qk_finish(logit);
+      g += kWaves;
+      if (g >= ge) break;
+      qk_issue(pfa, g + kWaves);
+      pv_step(pfb, g, logit);
+      qk_finish(logit);
+      g += kWaves;
+      if (g >= ge) break;
+    }
   }
 
   // ---------------------------------------------------------------- fp16 window
@@ -558,9 +610,9 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a)
         const float lg = valid ? cw[0] + cw[1] : kNegInfF;
         const float v = row_max16(lg);
         const float m_new = fmaxf(m_run[H], v);   // finite: the tile has a valid token
-        alpha[H] = exp2f(m_run[H] - m_new);
+        alpha[H] = fexp2(m_run[H] - m_new);
         m_run[H] = m_new;
-        const float pw = valid ? exp2f(lg - m_new) : 0.f;
+        const float pw = valid ? fexp2(lg - m_new) : 0.f;
         L.p[r + 4 * H][n] = pw;
         l_part[H] = fmaf(l_part[H], alpha[H], pw);
         mterm[H] *= alpha[H];
@@ -634,7 +686,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_f8f4_kernel(DecodeArgs a)
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
       if (M.l[w][h] > 0.f) {
-        const float f = exp2f(M.m[w][h] - mm);
+        const float f = fexp2(M.m[w][h] - mm);
         num = fmaf(M.num[w][h][d], f, num);
         den = fmaf(M.l[w][h], f, den);
       }

@@ -266,7 +266,7 @@ struct MfmaLds {
 };
 
 template <int BITS, int GQA>
-__global__ __launch_bounds__(kThreadsM, kMfmaBlocksPerCU<GQA>) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int TPC = GQA == 4 ? 2 : 1;  // tiles per QK accumulator (row slots)
   constexpr int NFRAG = 8 / TPC;         // QK accumulators per group
   constexpr int NH = GQA / 4;            // A-prep heads per lane (1 or 2)

@@ -55,12 +55,12 @@ kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_
 // An explicit request is honoured up to one chunk per group (and 1023).
 constexpr int64_t kMaxChunks = kvq::kMaxParts - 1;  // plus the window part
 
-int32_t plan_chunks(bool mfma, int gqa, int64_t heads, int64_t n_groups, int32_t req) {
+int32_t plan_chunks(bool mfma, int bits, int gqa, int64_t heads, int64_t n_groups, int32_t req) {
   int64_t n;
   if (req > 0) {
     n = req;
   } else if (mfma) {
-    n = kvq::mfma_resident_blocks(gqa) / heads;
+    n = kvq::mfma_resident_blocks(bits, gqa) / heads;
   } else {
     const int64_t target_blocks = 1024;  // 256 CUs x 4
     n = (target_blocks + heads - 1) / heads;
@@ -141,7 +141,7 @@ kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t 
   const int64_t heads = (int64_t)B * H_kv;
   if (heads > 65535) return KVQ_ERR_ARG;  // one grid row per (batch, kv head)
   const bool mfma = kvq::mfma_decode_supported(cfg->bits, cfg->group, gqa, cfg->n_boost);
-  const int32_t n = plan_chunks(mfma, gqa, heads, n_quant_tokens / cfg->group, n_chunks_req);
+  const int32_t n = plan_chunks(mfma, cfg->bits, gqa, heads, n_quant_tokens / cfg->group, n_chunks_req);
   if (n_chunks) *n_chunks = n;
   if (ws_bytes) *ws_bytes = partial_bytes(B, H_q, mfma ? n : n + 1);
   return KVQ_OK;

@@ -89,13 +89,11 @@ struct DecodeArgs {
 inline bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
   return group == 128 && (gqa == 4 || gqa == 8) && n_boost == 0 && (bits == 2 || bits == 4);
 }
-// Resident blocks (of 4 waves) per CU of the matrix-core kernel.
-template <int GQA>
-constexpr int kMfmaBlocksPerCU = 2;
+// Resident blocks (of 4 waves) per CU of the matrix-core kernels (their
+// register use allows two waves per SIMD).
+constexpr int mfma_blocks_per_cu(int, int) { return 2; }
 constexpr int kCUs = 256;  // MI355X
-inline int mfma_resident_blocks(int gqa) {
-  return kCUs * (gqa == 4 ? kMfmaBlocksPerCU<4> : kMfmaBlocksPerCU<8>);
-}
+inline int mfma_resident_blocks(int bits, int gqa) { return kCUs * mfma_blocks_per_cu(bits, gqa); }
 
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
 hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s);
