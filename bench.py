@@ -74,8 +74,16 @@ def avg_bits_per_element(bits: int, G: int, T: int, R: int) -> float:
 # ----------------------------------------------------------------------------
 
 CALIB_COPY_BYTES = 1 << 30
-SPLIT_KERNEL = "decode_mfma_kernel"
 COPY_KERNEL = "bitwise_not"       # the calibration pass: dst = ~src over 1 GiB of int32
+
+
+def split_kernel(w) -> str:
+    """Name of the split-K kernel the library launches for this workload (the
+    dispatch rule of the library: matrix cores for GQA 4/8, G 128, no boost;
+    fp8 x fp4 for 2-bit codes, fp16 for 4-bit)."""
+    if w.G == 128 and w.gqa in (4, 8) and w.n_boost == 0:
+        return "decode_f8f4_kernel" if w.bits == 2 else "decode_mfma_kernel"
+    return "decode_valu_kernel"
 
 
 def kernel_source_hash() -> str:
@@ -89,40 +97,41 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"hbm_traffic_decode_mfma_{workload}.txt")
+def traffic_file(w) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{split_kernel(w)}_{w.name}.txt")
 
 
-def _counter_means(csv_path, counter):
+def _counter_means(csv_path, counter, kernel):
     import csv
     per = {}
     with open(csv_path) as fh:
         for r in csv.DictReader(fh):
             if r["Counter_Name"] != counter:
                 continue
-            for key in (SPLIT_KERNEL, COPY_KERNEL):
+            for key in (kernel, COPY_KERNEL):
                 if key in r["Kernel_Name"]:
                     per.setdefault(key, []).append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
-def write_traffic(workload: str, fetch_csv: str, write_csv: str, command: str) -> dict:
+def write_traffic(w, fetch_csv: str, write_csv: str, command: str) -> dict:
     """Turn the two counter runs into bytes per launch of the split-K kernel."""
-    fm, fn = _counter_means(fetch_csv, "FETCH_SIZE")
-    wm, wn = _counter_means(write_csv, "WRITE_SIZE")
+    kern = split_kernel(w)
+    fm, fn = _counter_means(fetch_csv, "FETCH_SIZE", kern)
+    wm, wn = _counter_means(write_csv, "WRITE_SIZE", kern)
     f_scale = CALIB_COPY_BYTES / (fm[COPY_KERNEL] * 1024)
     w_scale = CALIB_COPY_BYTES / (wm[COPY_KERNEL] * 1024)
-    fetch = fm[SPLIT_KERNEL] * 1024 * f_scale
-    write = wm[SPLIT_KERNEL] * 1024 * w_scale
-    rec = {"workload": workload, "source_hash": kernel_source_hash(),
+    fetch = fm[kern] * 1024 * f_scale
+    write = wm[kern] * 1024 * w_scale
+    rec = {"workload": w.name, "kernel": kern, "source_hash": kernel_source_hash(),
            "fetch_bytes": round(fetch), "write_bytes": round(write),
            "traffic_bytes": round(fetch + write),
-           "raw_fetch_kib": round(fm[SPLIT_KERNEL], 1), "raw_write_kib": round(wm[SPLIT_KERNEL], 1),
+           "raw_fetch_kib": round(fm[kern], 1), "raw_write_kib": round(wm[kern], 1),
            "copy_fetch_kib": round(fm[COPY_KERNEL], 1), "copy_write_kib": round(wm[COPY_KERNEL], 1),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "dispatches": {"fetch": fn, "write": wn}}
-    with open(traffic_file(workload), "w") as fh:
-        fh.write(f"# HBM traffic per launch of {SPLIT_KERNEL}, workload {workload}\n")
+    with open(traffic_file(w), "w") as fh:
+        fh.write(f"# HBM traffic per launch of {kern}, workload {w.name}\n")
         fh.write(f"# counters: {command}\n")
         fh.write(f"# scale = {CALIB_COPY_BYTES} B copied / counter reading of the copy kernel\n")
         for k, v in rec.items():
@@ -130,12 +139,12 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, command: str) -
     return rec
 
 
-def read_traffic(workload: str):
+def read_traffic(w):
     """Bytes per launch from the committed counter file, or None when absent or
     taken from other kernel sources."""
     try:
         rec = {}
-        with open(traffic_file(workload)) as fh:
+        with open(traffic_file(w)) as fh:
             for ln in fh:
                 if ln.startswith("#") or ":" not in ln:
                     continue
@@ -250,7 +259,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.write_traffic:
-        print(json.dumps(write_traffic(args.workload, *args.write_traffic)))
+        import synth
+        print(json.dumps(write_traffic(synth.WORKLOADS[args.workload], *args.write_traffic)))
         return 0
 
     if args.gpus != 1:
@@ -406,8 +416,8 @@ def main(argv=None):
         "append_quant_us": round(app_avg * 1e3, 3) if append else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": read_traffic(w.name),
-                     "kernel": "split-K decode kernel (kvq_decode_partials)",
+                     "traffic": read_traffic(w),
+                     "kernel": f"{split_kernel(w)} (split-K phase, kvq_decode_partials)",
                      "algorithmic_bytes": alg_split,
                      "kernel_avg_us": round(part_avg * 1e3, 3)},
     }

@@ -153,6 +153,40 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   write_partial<GQA>(a, s, b, hk, part, acc);
 }
 
+// Log-sum-exp merge of up to NPM parts: one block per (batch, query head),
+// one thread per channel.  Every load is issued up front (part indices past
+// the count re-read the last part and get weight 0), so the merge costs one
+// memory round trip.
+template <int NPM>
+__global__ __launch_bounds__(kD) void merge_small_kernel(DecodeArgs a) {
+  const int64_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const int np = a.n_parts;
+  const float* w = a.ws + bh * (int64_t)np * (kD + 2);
+  float m[NPM], l[NPM], v[NPM];
+#pragma unroll
+  for (int j = 0; j < NPM; ++j) {
+    const float* wp = w + (int64_t)min(j, np - 1) * (kD + 2);
+    m[j] = wp[0];
+    l[j] = wp[1];
+    v[j] = wp[2 + d];
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int j = 0; j < NPM; ++j)
+    if (j < np && l[j] > 0.f) M = fmaxf(M, m[j]);
+  // weights select rather than branch, so the loads stay unconditional (an
+  // excluded part's values are finite: empty parts hold zeros)
+  float L = 0.f, o = 0.f;
+#pragma unroll
+  for (int j = 0; j < NPM; ++j) {
+    const float f = (j < np && l[j] > 0.f) ? exp2f(m[j] - M) : 0.f;
+    L = fmaf(l[j], f, L);
+    o = fmaf(v[j], f, o);
+  }
+  a.out[bh * kD + d] = L > 0.f ? o / L : 0.f;
+}
+
 // Log-sum-exp merge of the parts: one block per (batch, query head).
 // Parts' (m, l) are read in parallel (one per thread), the weights
 // 2^(m_p - M) / L go to LDS, then each thread sums one channel over the parts
@@ -245,7 +279,11 @@ hipError_t launch_decode_partials(int bits, int group, const DecodeArgs& a, hipS
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st) {
-  merge_kernel<<<(unsigned)(a.B * a.H_q), kMergeThreads, 0, st>>>(a);
+  const unsigned blocks = (unsigned)(a.B * a.H_q);
+  if (a.n_parts <= 8) merge_small_kernel<8><<<blocks, kD, 0, st>>>(a);
+  else if (a.n_parts <= 16) merge_small_kernel<16><<<blocks, kD, 0, st>>>(a);
+  else if (a.n_parts <= 32) merge_small_kernel<32><<<blocks, kD, 0, st>>>(a);
+  else merge_kernel<<<blocks, kMergeThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

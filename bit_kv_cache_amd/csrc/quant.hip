@@ -35,6 +35,23 @@ __device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float
   return (uint32_t)__builtin_rintf(y);
 }
 
+// The same code with the quotient taken as (x - mn) * rs, rs = 1/s rounded,
+// falling back to the IEEE quotient near a rounding tie.  Exact: the range
+// fits (x - mn)/s <= 1.5 maxq <= 22.5 (s is the fp16-rounded range/maxq, at
+// least 2^-24 when nonzero), so the product and the IEEE quotient differ by
+// at most a few ulps of 32 (< 2^-17), and round-half-even of two values that
+// close differs only when a half-integer lies within 2^-16 of them; the clamp
+// bounds are integers and cannot change that.
+__device__ __forceinline__ uint32_t quant_code_rcp(float x, float mn, float s, float rs,
+                                                   float maxq) {
+  if (s == 0.0f) return 0u;
+  const float dlt = x - mn;
+  float y = dlt * rs;
+  if (__builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-16f) y = dlt / s;
+  y = fminf(fmaxf(y, 0.0f), maxq);
+  return (uint32_t)__builtin_rintf(y);
+}
+
 __device__ __forceinline__ uint32_t wave_min(uint32_t v, int width) {
   for (int o = 1; o < width; o <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
   return v;
@@ -54,7 +71,7 @@ __device__ void quantize_keys_slice(const QuantArgs& a, int64_t head, int64_t gi
   constexpr int SW = CH / FPI;           // words per token in this slice
   __shared__ uint16_t tile[G][CH + 2];   // +2: odd row pitch in dwords
   __shared__ uint32_t red[2][8][CH];
-  __shared__ float s_mn[CH], s_sc[CH];
+  __shared__ float s_mn[CH], s_sc[CH], s_rs[CH];
   const int tid = threadIdx.x;
   const int64_t g = a.first_group + gi;
   const uint16_t* src = a.k_src + head * a.src_head_stride + gi * G * kD + slice * CH;
@@ -94,6 +111,7 @@ __device__ void quantize_keys_slice(const QuantArgs& a, int64_t head, int64_t gi
     a.c.k_min[m_off] = from_order_key(lo);
     s_mn[tid] = mn;
     s_sc[tid] = h2f(sh);
+    s_rs[tid] = 1.0f / h2f(sh);
   }
   __syncthreads();
   // codes, packed along channels: word (t, w) holds channels w*FPI + j
@@ -104,7 +122,8 @@ __device__ void quantize_keys_slice(const QuantArgs& a, int64_t head, int64_t gi
 #pragma unroll
     for (int j = 0; j < FPI; ++j) {
       const int c = w * FPI + j;
-      word |= quant_code(h2f(tile[t][c]), s_mn[c], s_sc[c], (float)MASK) << (BITS * j);
+      word |= quant_code_rcp(h2f(tile[t][c]), s_mn[c], s_sc[c], s_rs[c], (float)MASK)
+              << (BITS * j);
     }
     kw[t * WPT + w] = word;
   }
@@ -218,7 +237,7 @@ __device__ void quantize_values_slice(const QuantArgs& a, int64_t head, int64_t 
   constexpr int NCG = kD / G;            // channel groups per token
   constexpr int TPP = kThreads / (NT * NCG);   // threads per (token, channel group)
   __shared__ uint16_t tile[NT][kD + 2];
-  __shared__ float s_mn[NT * NCG], s_sc[NT * NCG];
+  __shared__ float s_mn[NT * NCG], s_sc[NT * NCG], s_rs[NT * NCG];
   static_assert(FPI <= NT && NT % FPI == 0, "whole words per slice");
   static_assert(TPP >= 1 && (TPP & (TPP - 1)) == 0 && G % TPP == 0, "thread split");
   const int tid = threadIdx.x;
@@ -252,6 +271,7 @@ __device__ void quantize_values_slice(const QuantArgs& a, int64_t head, int64_t 
       a.c.v_min[m_off] = from_order_key(lo);
       s_mn[p] = mn;
       s_sc[p] = h2f(sh);
+      s_rs[p] = 1.0f / h2f(sh);
     }
   }
   __syncthreads();
@@ -264,7 +284,8 @@ __device__ void quantize_values_slice(const QuantArgs& a, int64_t head, int64_t 
     for (int j = 0; j < FPI; ++j) {
       const int tt = w * FPI + j;
       const int pp = tt * NCG + cgd;
-      word |= quant_code(h2f(tile[tt][d]), s_mn[pp], s_sc[pp], (float)MASK) << (BITS * j);
+      word |= quant_code_rcp(h2f(tile[tt][d]), s_mn[pp], s_sc[pp], s_rs[pp], (float)MASK)
+              << (BITS * j);
     }
     vw[i] = word;
   }

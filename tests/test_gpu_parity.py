@@ -238,3 +238,35 @@ def test_token_split_across_calls_merges_to_whole(built, name):
     ref = oracle_decode(w, oracle_quantize(w, inp), inp, w.T)
     err = max_err(out, ref)
     assert err <= TOL, f"max-abs {err:.3g}"
+
+
+def test_quantize_rounding_ties_bit_exact(built):
+    """Groups whose quotients (x - min)/scale land exactly on, and one fp16 step
+    either side of, half-integers: the GPU's code rounding (including its
+    reciprocal fast path) must equal the oracle's IEEE division + RNE."""
+    import bit_kv_cache_amd as kvq
+    for bits in (2, 4):
+        w = synth.shrink(W["llama3_8b_t32k_2bit"], B=1, H_kv=2, H_q=8, T=4 * 128, bits=bits)
+        maxq = (1 << bits) - 1
+        gen = torch.Generator().manual_seed(77 + bits)
+        n = w.heads * w.T * w.D
+        # multiples of 1/2 in [0, maxq]: with min 0 and max maxq the scale is 1
+        half = torch.randint(0, 2 * maxq + 1, (n,), generator=gen).float() * 0.5
+        x = half.half()
+        # nudge a third of them by one fp16 step up or down
+        bits16 = x.view(torch.int16)
+        sel = torch.randint(0, 3, (n,), generator=gen)
+        bits16 = torch.where((sel == 1) & (x > 0), bits16 + 1, bits16)
+        bits16 = torch.where((sel == 2) & (x > 0), bits16 - 1, bits16)
+        x = bits16.view(torch.float16).view(w.heads, w.T, w.D).clone()
+        # pin min and max of every key group (channel) and value group (token)
+        x[:, 0::128, :] = 0.0
+        x[:, 1::128, :] = float(maxq)
+        x[:, :, 0] = 0.0
+        x[:, :, 1] = float(maxq)
+        inp = make_inputs(w)
+        inp["k"], inp["v"] = x.cuda(), x.flip(1).contiguous().cuda()
+        gc = gpu_quantize(w, inp)
+        oc = oracle_quantize(w, inp)
+        torch.cuda.synchronize()
+        assert_cache_equal(gc, oc, tokens=w.T)
