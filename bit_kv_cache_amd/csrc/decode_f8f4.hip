@@ -306,6 +306,56 @@ __global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_
   const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
 
   // ---------------------------------------------------------------- first loads
+  // Issue order matters: vector-memory loads complete in issue order, so the
+  // query and the first fp16 window tile are requested before the groups'
+  // prefetches, and the window work below waits only for them.
+  u32x4 qraw[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j)
+    qraw[j] = *reinterpret_cast<const u32x4*>(qrow + (r + 4 * j) * kD + 8 * n);
+
+  // This block's slice [u0, u1) of the fp16 window (sink | residual); wave w
+  // takes 16-token tiles w, w + 4, ...
+  const int n_win = a.n_sink + a.n_res;
+  const int wpc = n_win > 0 ? (n_win + a.n_chunks - 1) / a.n_chunks : 0;
+  const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
+  const int kq = lane >> 4, m_row = lane & 15;
+  u32x4 wq[NH];                      // window q.K^T A operand (see below)
+  if (u1 > u0) {
+    const int c = wave;
+#pragma unroll
+    for (int H = 0; H < NH; ++H)
+      wq[H] = (m_row & 3) < 2 ? *reinterpret_cast<const u32x4*>(
+                                    qrow + (4 * H + (m_row >> 2)) * kD + 32 * c + 8 * kq)
+                              : u32x4{0u, 0u, 0u, 0u};
+  }
+  auto win_row = [&](const uint16_t* sink, const uint16_t* res, int u) -> const uint16_t* {
+    return u < a.n_sink ? sink + (head * a.sink_cap + u) * kD
+                        : res + (head * a.res_cap + (u - a.n_sink)) * kD;
+  };
+  // one window tile: keys of token n (rows past the tile end repeat its last
+  // token) and the values of token pair (lane & 7), 16-channel group lane >> 3
+  struct WinTile {
+    u32x4 k[4];
+    u32x4 v[4];
+  };
+  auto load_win = [&](int u, WinTile& t) {
+    const int nt = min(16, u1 - u);
+    const uint16_t* kr = win_row(a.k_sink, a.k_res, u + min(n, nt - 1));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t.k[c] = *reinterpret_cast<const u32x4*>(kr + 32 * c + 8 * kq);
+    const int j = lane & 7, cg = lane >> 3;
+    const uint16_t* r0 = win_row(a.v_sink, a.v_res, u + min(2 * j, nt - 1)) + 16 * cg;
+    const uint16_t* r1 = win_row(a.v_sink, a.v_res, u + min(2 * j + 1, nt - 1)) + 16 * cg;
+    t.v[0] = *reinterpret_cast<const u32x4*>(r0);
+    t.v[1] = *reinterpret_cast<const u32x4*>(r0 + 8);
+    t.v[2] = *reinterpret_cast<const u32x4*>(r1);
+    t.v[3] = *reinterpret_cast<const u32x4*>(r1 + 8);
+  };
+  const int u_first = u0 + 16 * wave;
+  WinTile wt;
+  if (u_first < u1) load_win(u_first, wt);
+
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
   const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
   // Two prefetch buffers: a wave's groups alternate between them, and the
@@ -330,8 +380,7 @@ __global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_
   float qmax = 0.f;
 #pragma unroll
   for (int j = 0; j < NH; ++j) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + (r + 4 * j) * kD + 8 * n);
-    unpack8(raw, qv[j]);
+    unpack8(qraw[j], qv[j]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qv[j][e] *= a.qscale;
@@ -353,36 +402,27 @@ __global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_
 
   // window q.K^T operand: rows 4h' + {hi, lo, 0, 0} of head 4H + h', K-step
   // c = wave (channels 32c + 8kq + e), natural channel order
-  const int n_win = a.n_sink + a.n_res;
-  const int wpc = n_win > 0 ? (n_win + a.n_chunks - 1) / a.n_chunks : 0;
-  const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
   if (u1 > u0) {
-    const int m = lane & 15, kq = lane >> 4, c = wave;
 #pragma unroll
     for (int H = 0; H < NH; ++H) {
       u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if ((m & 3) < 2) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + (4 * H + (m >> 2)) * kD +
-                                                          32 * c + 8 * kq);
+      if ((m_row & 3) < 2) {
         float v[8];
-        unpack8(raw, v);
+        unpack8(wq[H], v);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float x0 = v[2 * i] * a.qscale, x1 = v[2 * i + 1] * a.qscale;
           const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
           const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]);
-          val[i] = __builtin_bit_cast(uint32_t, (m & 1) ? l : h);
+          val[i] = __builtin_bit_cast(uint32_t, (m_row & 1) ? l : h);
         }
       }
-      sh.win_a[H][c][kq][m] = val;
+      sh.win_a[H][wave][kq][m_row] = val;
     }
   }
   __syncthreads();
 
-  // ---------------------------------------------------------------- groups
   WaveLdsF<GQA>& L = sh.u.w[wave];
-  const uint32_t a_off = a_offset(n);
-  const int sa_digit = 127 - 4 * (lane & 3);   // A row m = lane & 15 holds digit m % 4
   float m_run[NH], l_part[NH], mterm[NH];
 #pragma unroll
   for (int j = 0; j < NH; ++j) {
@@ -390,6 +430,89 @@ __global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_
     l_part[j] = 0.f;
     mterm[j] = 0.f;
   }
+
+  // ---------------------------------------------------------------- fp16 window
+  // Window tiles first (their data was requested before the groups'): q.K^T
+  // on fp16 matrix cores (raw keys as B), the online softmax, p.V through an
+  // LDS transpose of the fp16 values into a natural-scale accumulator, which
+  // is then reduced to the lane's channels (wsum, rescaled with the softmax
+  // from here on).
+  float wsum[NH][8];
+#pragma unroll
+  for (int H = 0; H < NH; ++H)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wsum[H][i] = 0.f;
+  if (u_first < u1) {
+    f32x4 wacc[NH][8];
+#pragma unroll
+    for (int H = 0; H < NH; ++H)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wacc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = u_first; u < u1; u += 16 * kWaves) {
+      if (u != u_first) load_win(u, wt);
+      const int nt = min(16, u1 - u);
+      {
+        const int j = lane & 7, cg = lane >> 3;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t x = q < 4 ? wt.v[0][q] : wt.v[1][q - 4];
+          const uint32_t y = q < 4 ? wt.v[2][q] : wt.v[3][q - 4];
+          L.vt[16 * cg + 2 * q][j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+          L.vt[16 * cg + 2 * q + 1][j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+        }
+      }
+      const bool valid = n < nt;
+      float alpha[NH];
+#pragma unroll
+      for (int H = 0; H < NH; ++H) {
+        f32x4 cw = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cw = mfma_f16(sh.win_a[H][c][kq][m_row], wt.k[c], cw);
+        const float lg = valid ? cw[0] + cw[1] : kNegInfF;
+        const float v = row_max16(lg);
+        const float m_new = fmaxf(m_run[H], v);   // finite: the tile has a valid token
+        alpha[H] = fexp2(m_run[H] - m_new);
+        m_run[H] = m_new;
+        const float pw = valid ? fexp2(lg - m_new) : 0.f;
+        L.p[r + 4 * H][n] = pw;
+        l_part[H] = fmaf(l_part[H], alpha[H], pw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wacc[H][i] *= alpha[H];
+      }
+      wave_sync();
+#pragma unroll
+      for (int H = 0; H < NH; ++H) {
+        // A = p (rows 4h' + {hi, lo, 0, 0}), tokens 8kq..8kq+7 of the tile (kq < 2)
+        u32x4 apw = u32x4{0u, 0u, 0u, 0u};
+        if ((m_row & 3) < 2 && kq < 2) {
+          const float* pp = &L.p[4 * H + (m_row >> 2)][8 * kq];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x0 = pp[2 * i], x1 = pp[2 * i + 1];
+            const auto hi = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+            const auto lo = __builtin_amdgcn_cvt_pkrtz(x0 - (float)hi[0], x1 - (float)hi[1]);
+            apw[i] = __builtin_bit_cast(uint32_t, (m_row & 1) ? lo : hi);
+          }
+        }
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+          const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
+          const u32x4 bv = kq < 2 ? *reinterpret_cast<const u32x4*>(&L.vt[d][4 * kq])
+                                  : u32x4{0u, 0u, 0u, 0u};
+          wacc[H][blk] = mfma_f16(apw, bv, wacc[H][blk]);
+        }
+      }
+      wave_sync();
+    }
+#pragma unroll
+    for (int H = 0; H < NH; ++H)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wsum[H][i] = wacc[H][i][0] + wacc[H][i][1];
+  }
+
+  // ---------------------------------------------------------------- groups
+  const uint32_t a_off = a_offset(n);
+  const int sa_digit = 127 - 4 * (lane & 3);   // A row m = lane & 15 holds digit m % 4
   int e_v = -1000;                 // running value-side exponent
   f32x4 acc[NH][8];                // p.V: [head half][channel block], 4 digit rows
 #pragma unroll
@@ -521,7 +644,10 @@ __global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_
         for (int H = 0; H < NH; ++H) {
           const float f = alpha[H] * vshift;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[H][i] *= f;
+          for (int i = 0; i < 8; ++i) {
+            acc[H][i] *= f;
+            wsum[H][i] *= alpha[H];
+          }
         }
       }
     }
@@ -560,95 +686,6 @@ __global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_
     }
   }
 
-  // ---------------------------------------------------------------- fp16 window
-  // Window tokens [u0, u1) of sink | residual; wave w takes 16-token tiles
-  // w, w + 4, ...: q.K^T on fp16 matrix cores (raw keys as B), the same
-  // online softmax, p.V through an LDS transpose of the fp16 values into a
-  // natural-scale accumulator.
-  f32x4 wacc[NH][8];
-#pragma unroll
-  for (int H = 0; H < NH; ++H)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) wacc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  {
-    const int kq = lane >> 4, m_row = lane & 15;
-    auto row = [&](const uint16_t* sink, const uint16_t* res, int u) -> const uint16_t* {
-      return u < a.n_sink ? sink + (head * a.sink_cap + u) * kD
-                          : res + (head * a.res_cap + (u - a.n_sink)) * kD;
-    };
-    for (int u = u0 + 16 * wave; u < u1; u += 16 * kWaves) {
-      const int nt = min(16, u1 - u);
-      // keys of token n (rows past the tile end repeat its last token)
-      const uint16_t* kr = row(a.k_sink, a.k_res, u + min(n, nt - 1));
-      u32x4 kv[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kv[c] = *reinterpret_cast<const u32x4*>(kr + 32 * c + 8 * kq);
-      // values: lane (token pair j, 16-channel group cg) -> vt[channel][j]
-      {
-        const int j = lane & 7, cg = lane >> 3;
-        const uint16_t* r0 = row(a.v_sink, a.v_res, u + min(2 * j, nt - 1)) + 16 * cg;
-        const uint16_t* r1 = row(a.v_sink, a.v_res, u + min(2 * j + 1, nt - 1)) + 16 * cg;
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(r0);
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(r0 + 8);
-        const u32x4 y0 = *reinterpret_cast<const u32x4*>(r1);
-        const u32x4 y1 = *reinterpret_cast<const u32x4*>(r1 + 8);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t x = q < 4 ? x0[q] : x1[q - 4];
-          const uint32_t y = q < 4 ? y0[q] : y1[q - 4];
-          L.vt[16 * cg + 2 * q][j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
-          L.vt[16 * cg + 2 * q + 1][j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
-        }
-      }
-      const bool valid = n < nt;
-      float alpha[NH];
-#pragma unroll
-      for (int H = 0; H < NH; ++H) {
-        f32x4 cw = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) cw = mfma_f16(sh.win_a[H][c][kq][m_row], kv[c], cw);
-        const float lg = valid ? cw[0] + cw[1] : kNegInfF;
-        const float v = row_max16(lg);
-        const float m_new = fmaxf(m_run[H], v);   // finite: the tile has a valid token
-        alpha[H] = fexp2(m_run[H] - m_new);
-        m_run[H] = m_new;
-        const float pw = valid ? fexp2(lg - m_new) : 0.f;
-        L.p[r + 4 * H][n] = pw;
-        l_part[H] = fmaf(l_part[H], alpha[H], pw);
-        mterm[H] *= alpha[H];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          acc[H][i] *= alpha[H];
-          wacc[H][i] *= alpha[H];
-        }
-      }
-      wave_sync();
-#pragma unroll
-      for (int H = 0; H < NH; ++H) {
-        // A = p (rows 4h' + {hi, lo, 0, 0}), tokens 8kq..8kq+7 of the tile (kq < 2)
-        u32x4 apw = u32x4{0u, 0u, 0u, 0u};
-        if ((m_row & 3) < 2 && kq < 2) {
-          const float* pp = &L.p[4 * H + (m_row >> 2)][8 * kq];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x0 = pp[2 * i], x1 = pp[2 * i + 1];
-            const auto hi = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-            const auto lo = __builtin_amdgcn_cvt_pkrtz(x0 - (float)hi[0], x1 - (float)hi[1]);
-            apw[i] = __builtin_bit_cast(uint32_t, (m_row & 1) ? lo : hi);
-          }
-        }
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-          const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
-          const u32x4 bv = kq < 2 ? *reinterpret_cast<const u32x4*>(&L.vt[d][4 * kq])
-                                  : u32x4{0u, 0u, 0u, 0u};
-          wacc[H][blk] = mfma_f16(apw, bv, wacc[H][blk]);
-        }
-      }
-      wave_sync();
-    }
-  }
-
   // ---------------------------------------------------------------- block merge
   float lsum[NH], mtsum[NH];
 #pragma unroll
@@ -670,8 +707,7 @@ __global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_
     for (int blk = 0; blk < 8; ++blk) {
       const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
       const f32x4 v = acc[H][blk];
-      M.num[wave][h][d] = fmaf((v[0] + v[1]) + (v[2] + v[3]), ev, mtsum[H]) +
-                          (wacc[H][blk][0] + wacc[H][blk][1]);
+      M.num[wave][h][d] = fmaf((v[0] + v[1]) + (v[2] + v[3]), ev, mtsum[H]) + wsum[H][blk];
     }
   }
   __syncthreads();
