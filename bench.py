@@ -377,10 +377,26 @@ def main(argv=None):
         ms = sorted(e[a].elapsed_time(e[b]) for e in ev)
         return sum(ms) / n_k, ms
 
-    part_avg, part_ms = stats(0, 1)
-    merge_avg, _ = stats(1, 2)
+    part_iso, part_ms = stats(0, 1)
+    merge_iso, _ = stats(1, 2)
     dec_avg, dec_ms = stats(0, 2)
-    app_avg, _ = stats(2, 3)
+    app_iso, _ = stats(2, 3)
+
+    # average launch duration of each kernel alone, back to back on the
+    # stream (one event pair around n_k launches: no event between launches)
+    def back_to_back(fn):
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for i in range(n_k):
+            fn(i)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) / n_k
+
+    part_avg = back_to_back(partials)
+    merge_avg = back_to_back(lambda i: merge())
+    app_avg = back_to_back(quant) if append else 0.0
 
     alg = decode_bytes(w)
     alg_split = alg - w.B * w.H_q * w.D * 4   # the split-K kernel does not write O
@@ -412,7 +428,12 @@ def main(argv=None):
         "decode_us": {"avg": round(dec_avg * 1e3, 3), "p10": round(dec_ms[n_k // 10] * 1e3, 3),
                       "p90": round(dec_ms[(9 * n_k) // 10] * 1e3, 3),
                       "split_kernel_avg": round(part_avg * 1e3, 3),
-                      "merge_kernel_avg": round(merge_avg * 1e3, 3)},
+                      "merge_kernel_avg": round(merge_avg * 1e3, 3),
+                      "split_kernel_isolated_avg": round(part_iso * 1e3, 3),
+                      "merge_kernel_isolated_avg": round(merge_iso * 1e3, 3),
+                      "timing": "*_avg: n launches back to back between two HIP events on the "
+                                "launch stream; *_isolated_avg: an event pair around every "
+                                "launch"},
         "append_quant_us": round(app_avg * 1e3, 3) if append else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -52,7 +52,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kG = 128;          // tokens per group
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;        // one block per CU (two waves per SIMD): 7 consumers, 1 loader
+constexpr int kConsumers = kWaves - 1;
+constexpr int kLoader = kWaves - 1;
 constexpr int kThreadsF = 64 * kWaves;
 constexpr int kWpt = kD / 16;     // 2-bit key words per token (8)
 constexpr uint32_t kNib = 0x33333333u;
@@ -180,6 +182,8 @@ __device__ __forceinline__ uint32_t a_offset(int o) {
 constexpr int kRowBytes = 144;
 typedef uint8_t ATile[16][kRowBytes];
 
+// ------------------------------------------------------------------ LDS
+
 template <int GQA>
 struct WaveLdsF {
   static constexpr int NH = GQA / 4;
@@ -202,53 +206,80 @@ struct MergeLdsF {
   float m[kWaves][GQA], l[kWaves][GQA];
 };
 
+// Ring of group records filled by the loader wave: slot layout (bytes)
+//   [0, 4096)      key words of the 128 tokens, as in the cache (token-major)
+//   [4096, 8192)   value words, 8 rows of 128 channels, as in the cache
+//   [8192, 8448)   key scale of the 128 channels (fp16), then key min,
+//   [8704, 8960)   value scale of the 128 tokens, then value min
+constexpr int kSlotBytes = 9216;
+constexpr int kSlotV = 4096, kSlotKs = 8192, kSlotKm = 8448, kSlotVs = 8704, kSlotVm = 8960;
+template <int GQA>
+constexpr int ring_slots() { return GQA == 4 ? 8 : 5; }
+// groups the loader keeps in flight (at most ring_slots; 9 loads per group,
+// and the vector-memory counter holds at most 63)
+template <int GQA>
+constexpr int in_flight() { return ring_slots<GQA>() - 1; }
+
 template <int GQA>
 struct LdsF {
+  static constexpr int R = ring_slots<GQA>();
   union {
-    WaveLdsF<GQA> w[kWaves];
+    WaveLdsF<GQA> w[kConsumers];
     MergeLdsF<GQA> merge;
   } u;
   u32x4 win_a[GQA / 4][4][4][16];                 // window q.K^T A: [half][c][kq][row]
+  alignas(16) uint8_t ring[R][kSlotBytes];
+  int ready[R];     // the chunk-relative group a slot holds once its data has arrived
+  int empty[R];     // the group a slot may receive next (its previous one was copied out)
+  int next_group;   // next group a consumer claims
+  int stalled;      // a wait ran past its spin limit
 };
 
-struct Prefetch {
+struct Operands {
   uint32_t kw[8][2];     // key words: tile t, token 16t + n, words 2r, 2r + 1
   u32x4 ks, kmin;        // key scale / min of channels 8n..8n+7
   u32x4 vw[2][2];        // value words: rows 2r, 2r + 1; channels 4n.. and 64 + 4n..
   u32x4 vs, vmn;         // value scale / min of tokens 8n..8n+7
 };
 
+// One 1 KB wave-wide copy from global memory into LDS: lane i's 16 bytes at
+// gptr land at LDS byte address lds + 16 i.  Written as an instruction
+// rather than the compiler builtin because the compiler makes every later
+// LDS access wait for all such copies in flight, which would serialize the
+// loader; the loader waits for its copies itself (loader_wait).
+__device__ __forceinline__ void dma_1k(uint32_t lds, const void* gptr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(lds)
+               : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory loads are in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
 template <typename T>
-__device__ __forceinline__ T ldnt(const char* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+__device__ __forceinline__ T lds_load(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int64_t g, int n,
-                                          int r, Prefetch& f) {
-  const char* kb = reinterpret_cast<const char*>(a.c.k_codes) +
-                   ((head * a.c.t_cap + g * kG + n) * kWpt + 2 * r) * 4;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const u32x2 v = ldnt<u32x2>(kb + 16 * t * kWpt * 4);
-    f.kw[t][0] = v[0];
-    f.kw[t][1] = v[1];
+// Spin (with sleeps) until *p == want; false if the spin limit ran out (the
+// caller then stops, so every wave always reaches the end of the kernel).
+constexpr uint32_t kSpinLimit = 1u << 20;
+__device__ __forceinline__ bool spin_until(const int* p, int want) {
+  for (uint32_t i = 0; i < kSpinLimit; ++i) {
+    if (lds_load(p) == want) return true;
+    __builtin_amdgcn_s_sleep(1);
   }
-  const int64_t mo = ((head * (a.c.t_cap / kG) + g) * kD + 8 * n) * 2;
-  f.ks = ldnt<u32x4>(reinterpret_cast<const char*>(a.c.k_scale) + mo);
-  f.kmin = ldnt<u32x4>(reinterpret_cast<const char*>(a.c.k_min) + mo);
-}
-
-__device__ __forceinline__ void load_values(const DecodeArgs& a, int64_t head, int64_t g, int n,
-                                            int r, Prefetch& f) {
-  const char* vb = reinterpret_cast<const char*>(a.c.v_codes) +
-                   ((head * (a.c.t_cap / 16) + g * (kG / 16) + 2 * r) * kD + 4 * n) * 4;
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) f.vw[q][hb] = ldnt<u32x4>(vb + (q * kD + 64 * hb) * 4);
-  const int64_t to = (head * a.c.t_cap + g * kG + 8 * n) * 2;
-  f.vs = ldnt<u32x4>(reinterpret_cast<const char*>(a.c.v_scale) + to);
-  f.vmn = ldnt<u32x4>(reinterpret_cast<const char*>(a.c.v_min) + to);
+  return false;
 }
 
 // Orders this wave's LDS writes before its later LDS reads of other lanes'
@@ -291,411 +322,474 @@ __device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
+
+// ------------------------------------------------------------------ kernel
+
 template <int GQA>
-__global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_f8f4_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a) {
   constexpr int NH = GQA / 4;    // heads per lane (r and r + 4)
+  constexpr int R = ring_slots<GQA>();
+  constexpr int DF = in_flight<GQA>();
   __shared__ LdsF<GQA> sh;
 
+  // Every launch argument the first phase needs, fetched in one round trip
+  // (the compiler would otherwise load each one just before its first use,
+  // serializing several kernel-argument reads at the start of every wave).
+  asm volatile("" ::"s"(a.c.k_codes), "s"(a.c.v_codes), "s"(a.c.k_scale), "s"(a.c.k_min),
+               "s"(a.c.v_scale), "s"(a.c.v_min), "s"(a.c.t_cap), "s"(a.groups_per_chunk),
+               "s"(a.n_groups), "s"(a.H_kv), "s"(a.H_q), "s"(a.q), "s"(a.qscale), "s"(a.n_sink), "s"(a.n_res), "s"(a.k_sink),
+               "s"(a.v_sink), "s"(a.k_res), "s"(a.v_res), "s"(a.sink_cap), "s"(a.res_cap),
+               "s"(a.n_chunks));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, r = lane >> 4;
   const int chunk = blockIdx.x;
-  const int64_t head = blockIdx.y;
-  const int64_t b = head / a.H_kv, hk = head % a.H_kv;
+  const int head32 = blockIdx.y;                 // < 65536 (checked on the host)
+  const int64_t head = head32;
+  const int b32 = head32 / a.H_kv, hk32 = head32 - b32 * a.H_kv;   // 32-bit division
+  const int64_t b = b32, hk = hk32;
   const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
-
-  // ---------------------------------------------------------------- first loads
-  // Issue order matters: vector-memory loads complete in issue order, so the
-  // query and the first fp16 window tile are requested before the groups'
-  // prefetches, and the window work below waits only for them.
-  u32x4 qraw[NH];
-#pragma unroll
-  for (int j = 0; j < NH; ++j)
-    qraw[j] = *reinterpret_cast<const u32x4*>(qrow + (r + 4 * j) * kD + 8 * n);
-
-  // This block's slice [u0, u1) of the fp16 window (sink | residual); wave w
-  // takes 16-token tiles w, w + 4, ...
-  const int n_win = a.n_sink + a.n_res;
-  const int wpc = n_win > 0 ? (n_win + a.n_chunks - 1) / a.n_chunks : 0;
-  const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
-  const int kq = lane >> 4, m_row = lane & 15;
-  u32x4 wq[NH];                      // window q.K^T A operand (see below)
-  if (u1 > u0) {
-    const int c = wave;
-#pragma unroll
-    for (int H = 0; H < NH; ++H)
-      wq[H] = (m_row & 3) < 2 ? *reinterpret_cast<const u32x4*>(
-                                    qrow + (4 * H + (m_row >> 2)) * kD + 32 * c + 8 * kq)
-                              : u32x4{0u, 0u, 0u, 0u};
-  }
-  auto win_row = [&](const uint16_t* sink, const uint16_t* res, int u) -> const uint16_t* {
-    return u < a.n_sink ? sink + (head * a.sink_cap + u) * kD
-                        : res + (head * a.res_cap + (u - a.n_sink)) * kD;
-  };
-  // one window tile: keys of token n (rows past the tile end repeat its last
-  // token) and the values of token pair (lane & 7), 16-channel group lane >> 3
-  struct WinTile {
-    u32x4 k[4];
-    u32x4 v[4];
-  };
-  auto load_win = [&](int u, WinTile& t) {
-    const int nt = min(16, u1 - u);
-    const uint16_t* kr = win_row(a.k_sink, a.k_res, u + min(n, nt - 1));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) t.k[c] = *reinterpret_cast<const u32x4*>(kr + 32 * c + 8 * kq);
-    const int j = lane & 7, cg = lane >> 3;
-    const uint16_t* r0 = win_row(a.v_sink, a.v_res, u + min(2 * j, nt - 1)) + 16 * cg;
-    const uint16_t* r1 = win_row(a.v_sink, a.v_res, u + min(2 * j + 1, nt - 1)) + 16 * cg;
-    t.v[0] = *reinterpret_cast<const u32x4*>(r0);
-    t.v[1] = *reinterpret_cast<const u32x4*>(r0 + 8);
-    t.v[2] = *reinterpret_cast<const u32x4*>(r1);
-    t.v[3] = *reinterpret_cast<const u32x4*>(r1 + 8);
-  };
-  const int u_first = u0 + 16 * wave;
-  WinTile wt;
-  if (u_first < u1) load_win(u_first, wt);
-
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
-  const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
-  // Two prefetch buffers: a wave's groups alternate between them, and the
-  // loads for group g + 8 are issued while group g computes, so a group's
-  // data has a whole iteration to arrive.  Loads are issued unconditionally
-  // (exact wait counts); past the chunk end they read group 0 of head 0,
-  // which every such load shares, instead of new memory.
-  Prefetch pfa, pfb;
-  int64_t g = gb + wave;
-  auto fetch = [&](int64_t gi, Prefetch& f) {
-    const bool in = gi < ge;
-    const int64_t hh = in ? head : 0, gg = in ? gi : 0;
-    load_keys(a, hh, gg, n, r, f);
-    load_values(a, hh, gg, n, r, f);
-  };
-  fetch(g, pfa);
-  fetch(g + kWaves, pfb);
+  const int ngc = (int)max<int64_t>(0, min<int64_t>(a.n_groups, gb + a.groups_per_chunk) - gb);
 
-  // ---------------------------------------------------------------- query
-  // qv[j][e] = q[r + 4j][8n + e] * sm * log2(e) * 2^(8 - e_q), |qv| < 2^8
-  float qv[NH][8];
-  float qmax = 0.f;
-#pragma unroll
-  for (int j = 0; j < NH; ++j) {
-    unpack8(qraw[j], qv[j]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qv[j][e] *= a.qscale;
-      qmax = fmaxf(qmax, fabsf(qv[j][e]));
-    }
+  if (tid < R) {
+    sh.ready[tid] = -1;
+    sh.empty[tid] = tid;
   }
-  qmax = row_max16(qmax);
-  qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
-  qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
-  const int e_q = ceil_exp(qmax);
-  {
-    const float qs = exp2i(8 - e_q);
-#pragma unroll
-    for (int j = 0; j < NH; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[j][e] *= qs;
-  }
-  const float q_unscale = exp2i(e_q - 8);
-
-  // window q.K^T operand: rows 4h' + {hi, lo, 0, 0} of head 4H + h', K-step
-  // c = wave (channels 32c + 8kq + e), natural channel order
-  if (u1 > u0) {
-#pragma unroll
-    for (int H = 0; H < NH; ++H) {
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if ((m_row & 3) < 2) {
-        float v[8];
-        unpack8(wq[H], v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x0 = v[2 * i] * a.qscale, x1 = v[2 * i + 1] * a.qscale;
-          const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-          const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]);
-          val[i] = __builtin_bit_cast(uint32_t, (m_row & 1) ? l : h);
-        }
-      }
-      sh.win_a[H][wave][kq][m_row] = val;
-    }
+  if (tid == 0) {
+    sh.next_group = 0;
+    sh.stalled = 0;
   }
   __syncthreads();
 
-  WaveLdsF<GQA>& L = sh.u.w[wave];
+  // per-wave online-softmax state (the loader's stays empty)
   float m_run[NH], l_part[NH], mterm[NH];
+  float wsum[NH][8];                 // fp16-window p.V, channels of this lane
+  f32x4 acc[NH][8];                  // quantized p.V: [head half][channel block], 4 digit rows
+  int e_v = -1000;                   // running value-side exponent of acc
 #pragma unroll
-  for (int j = 0; j < NH; ++j) {
-    m_run[j] = kNegInfF;
-    l_part[j] = 0.f;
-    mterm[j] = 0.f;
+  for (int H = 0; H < NH; ++H) {
+    m_run[H] = kNegInfF;
+    l_part[H] = 0.f;
+    mterm[H] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wsum[H][i] = 0.f;
+      acc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
 
-  // ---------------------------------------------------------------- fp16 window
-  // Window tiles first (their data was requested before the groups'): q.K^T
-  // on fp16 matrix cores (raw keys as B), the online softmax, p.V through an
-  // LDS transpose of the fp16 values into a natural-scale accumulator, which
-  // is then reduced to the lane's channels (wsum, rescaled with the softmax
-  // from here on).
-  float wsum[NH][8];
-#pragma unroll
-  for (int H = 0; H < NH; ++H)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) wsum[H][i] = 0.f;
-  if (u_first < u1) {
-    f32x4 wacc[NH][8];
-#pragma unroll
-    for (int H = 0; H < NH; ++H)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wacc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int u = u_first; u < u1; u += 16 * kWaves) {
-      if (u != u_first) load_win(u, wt);
-      const int nt = min(16, u1 - u);
-      {
-        const int j = lane & 7, cg = lane >> 3;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t x = q < 4 ? wt.v[0][q] : wt.v[1][q - 4];
-          const uint32_t y = q < 4 ? wt.v[2][q] : wt.v[3][q - 4];
-          L.vt[16 * cg + 2 * q][j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
-          L.vt[16 * cg + 2 * q + 1][j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
-        }
+  if (wave == kLoader) {
+    // ---------------------------------------------------------- loader wave
+    // Copies the chunk's groups, in order, into the ring (group j -> slot
+    // j % R) with DF groups in flight, and publishes each one once its data
+    // is in LDS.  A slot is refilled only after a consumer copied its
+    // previous group out (empty[s] == j).
+    const int sub = lane & 15, part = lane >> 4;
+    const char* kp = reinterpret_cast<const char*>(a.c.k_codes) +
+                     (head * a.c.t_cap + gb * kG) * (kWpt * 4) + 16 * lane;
+    const char* vp = reinterpret_cast<const char*>(a.c.v_codes) +
+                     (head * (a.c.t_cap / 16) + gb * (kG / 16)) * (kD * 4) + 16 * lane;
+    // metadata lanes: key scale, key min, value scale, value min (256 B each)
+    const uint16_t* marr = part == 0 ? a.c.k_scale : part == 1 ? a.c.k_min
+                         : part == 2 ? a.c.v_scale : a.c.v_min;
+    const int64_t m0 = part < 2 ? (head * (a.c.t_cap / kG) + gb) * kD : head * a.c.t_cap + gb * kG;
+    const char* mp = reinterpret_cast<const char*>(marr + m0) + 16 * sub;
+    // LDS byte address of the ring (address-space cast of the generic pointer)
+    const uint32_t ring0 =
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)(&sh.ring[0][0]));
+    bool ok = true;
+    for (int j = 0; j < ngc; ++j) {
+      const int s = j % R;
+      if (!spin_until(&sh.empty[s], j)) {
+        ok = false;
+        break;
       }
-      const bool valid = n < nt;
+      asm volatile("" ::: "memory");
+      const uint32_t sl = __builtin_amdgcn_readfirstlane(ring0 + s * kSlotBytes);
+      const int64_t jo = j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma_1k(sl + 1024 * i, kp + jo * 4096 + 1024 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma_1k(sl + kSlotV + 1024 * i, vp + jo * 4096 + 1024 * i);
+      dma_1k(sl + kSlotKs, mp + jo * 256);
+      if (j >= DF - 1) {
+        vm_wait<9 * (DF - 1)>();     // group j - DF + 1 has landed
+        if (lane == 0) lds_store(&sh.ready[(j - DF + 1) % R], j - DF + 1);
+      }
+    }
+    vm_wait<0>();
+    if (ok) {
+      for (int j = max(0, ngc - DF + 1); j < ngc; ++j)
+        if (lane == 0) lds_store(&sh.ready[j % R], j);
+    } else if (lane == 0) {
+      lds_store(&sh.stalled, 1);
+    }
+  } else {
+    // ---------------------------------------------------------- consumer waves
+    // query, then this wave's first fp16 window tile (requested first, so
+    // the window work waits only for them)
+    u32x4 qraw[NH];
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+      qraw[j] = *reinterpret_cast<const u32x4*>(qrow + (r + 4 * j) * kD + 8 * n);
+
+    // This block's slice [u0, u1) of the fp16 window (sink | residual);
+    // consumer w takes 16-token tiles w, w + kConsumers, ...
+    const int n_win = a.n_sink + a.n_res;
+    const int wpc = n_win > 0 ? (n_win + a.n_chunks - 1) / a.n_chunks : 0;
+    const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
+    const int kq = lane >> 4, m_row = lane & 15;
+    const int u_first = u0 + 16 * wave;
+    auto win_row = [&](const uint16_t* sink, const uint16_t* res, int u) -> const uint16_t* {
+      return u < a.n_sink ? sink + (head * a.sink_cap + u) * kD
+                          : res + (head * a.res_cap + (u - a.n_sink)) * kD;
+    };
+    // one window tile: keys of token n (rows past the tile end repeat its
+    // last token) and the values of token pair (lane & 7), 16-channel group
+    // lane >> 3
+    struct WinTile {
+      u32x4 k[4];
+      u32x4 v[4];
+    };
+    auto load_win = [&](int u, WinTile& t) {
+      const int nt = min(16, u1 - u);
+      const uint16_t* kr = win_row(a.k_sink, a.k_res, u + min(n, nt - 1));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) t.k[c] = *reinterpret_cast<const u32x4*>(kr + 32 * c + 8 * kq);
+      const int j = lane & 7, cg = lane >> 3;
+      const uint16_t* r0 = win_row(a.v_sink, a.v_res, u + min(2 * j, nt - 1)) + 16 * cg;
+      const uint16_t* r1 = win_row(a.v_sink, a.v_res, u + min(2 * j + 1, nt - 1)) + 16 * cg;
+      t.v[0] = *reinterpret_cast<const u32x4*>(r0);
+      t.v[1] = *reinterpret_cast<const u32x4*>(r0 + 8);
+      t.v[2] = *reinterpret_cast<const u32x4*>(r1);
+      t.v[3] = *reinterpret_cast<const u32x4*>(r1 + 8);
+    };
+    // window q.K^T A operand of this wave: rows 4h' + {hi, lo, 0, 0} of head
+    // 4H + h', K-step c (channels 32c + 8kq + e), natural channel order
+    u32x4 wq[NH][4];
+    WinTile wt;
+    if (u_first < u1) {
+#pragma unroll
+      for (int H = 0; H < NH; ++H)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          wq[H][c] = (m_row & 3) < 2 ? *reinterpret_cast<const u32x4*>(
+                                           qrow + (4 * H + (m_row >> 2)) * kD + 32 * c + 8 * kq)
+                                     : u32x4{0u, 0u, 0u, 0u};
+      load_win(u_first, wt);
+    }
+
+    // qv[j][e] = q[r + 4j][8n + e] * sm * log2(e) * 2^(8 - e_q), |qv| < 2^8
+    float qv[NH][8];
+    float qmax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      unpack8(qraw[j], qv[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qv[j][e] *= a.qscale;
+        qmax = fmaxf(qmax, fabsf(qv[j][e]));
+      }
+    }
+    qmax = row_max16(qmax);
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+    const int e_q = ceil_exp(qmax);
+    {
+      const float qs = exp2i(8 - e_q);
+#pragma unroll
+      for (int j = 0; j < NH; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[j][e] *= qs;
+    }
+    const float q_unscale = exp2i(e_q - 8);
+
+    WaveLdsF<GQA>& L = sh.u.w[wave];
+
+    // ------------------------------------------------------ fp16 window
+    // q.K^T on fp16 matrix cores (raw keys as B), the online softmax, p.V
+    // through an LDS transpose of the fp16 values into a natural-scale
+    // accumulator, reduced to the lane's channels (wsum, rescaled with the
+    // softmax from here on).
+    if (u_first < u1) {
+#pragma unroll
+      for (int H = 0; H < NH; ++H)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u32x4 val = u32x4{0u, 0u, 0u, 0u};
+          if ((m_row & 3) < 2) {
+            float v[8];
+            unpack8(wq[H][c], v);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x0 = v[2 * i] * a.qscale, x1 = v[2 * i + 1] * a.qscale;
+              const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+              const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]);
+              val[i] = __builtin_bit_cast(uint32_t, (m_row & 1) ? l : h);
+            }
+          }
+          wq[H][c] = val;
+        }
+      f32x4 wacc[NH][8];
+#pragma unroll
+      for (int H = 0; H < NH; ++H)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wacc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = u_first; u < u1; u += 16 * kConsumers) {
+        if (u != u_first) load_win(u, wt);
+        const int nt = min(16, u1 - u);
+        {
+          const int j = lane & 7, cg = lane >> 3;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t x = q < 4 ? wt.v[0][q] : wt.v[1][q - 4];
+            const uint32_t y = q < 4 ? wt.v[2][q] : wt.v[3][q - 4];
+            L.vt[16 * cg + 2 * q][j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+            L.vt[16 * cg + 2 * q + 1][j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+          }
+        }
+        const bool valid = n < nt;
+#pragma unroll
+        for (int H = 0; H < NH; ++H) {
+          f32x4 cw = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) cw = mfma_f16(wq[H][c], wt.k[c], cw);
+          const float lg = valid ? cw[0] + cw[1] : kNegInfF;
+          const float v = row_max16(lg);
+          const float m_new = fmaxf(m_run[H], v);   // finite: the tile has a valid token
+          const float alpha = fexp2(m_run[H] - m_new);
+          m_run[H] = m_new;
+          const float pw = valid ? fexp2(lg - m_new) : 0.f;
+          L.p[r + 4 * H][n] = pw;
+          l_part[H] = fmaf(l_part[H], alpha, pw);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wacc[H][i] *= alpha;
+        }
+        wave_sync();
+#pragma unroll
+        for (int H = 0; H < NH; ++H) {
+          // A = p (rows 4h' + {hi, lo, 0, 0}), tokens 8kq..8kq+7 of the tile (kq < 2)
+          u32x4 apw = u32x4{0u, 0u, 0u, 0u};
+          if ((m_row & 3) < 2 && kq < 2) {
+            const float* pp = &L.p[4 * H + (m_row >> 2)][8 * kq];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x0 = pp[2 * i], x1 = pp[2 * i + 1];
+              const auto hi = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+              const auto lo = __builtin_amdgcn_cvt_pkrtz(x0 - (float)hi[0], x1 - (float)hi[1]);
+              apw[i] = __builtin_bit_cast(uint32_t, (m_row & 1) ? lo : hi);
+            }
+          }
+#pragma unroll
+          for (int blk = 0; blk < 8; ++blk) {
+            const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
+            const u32x4 bv = kq < 2 ? *reinterpret_cast<const u32x4*>(&L.vt[d][4 * kq])
+                                    : u32x4{0u, 0u, 0u, 0u};
+            wacc[H][blk] = mfma_f16(apw, bv, wacc[H][blk]);
+          }
+        }
+        wave_sync();
+      }
+#pragma unroll
+      for (int H = 0; H < NH; ++H)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wsum[H][i] = wacc[H][i][0] + wacc[H][i][1];
+    }
+
+    // ------------------------------------------------------ groups
+    const uint32_t a_off = a_offset(n);
+    const int sa_digit = 127 - 4 * (lane & 3);   // A row m = lane & 15 holds digit m % 4
+    int e_s = 0;                   // key exponent of the current group
+    float bias[NH];                // its q . key-min terms
+    f32x4 cq[NH][8];               // its q.K^T digit rows, per tile
+
+    // copy group j's operands out of ring slot s (then the slot is free)
+    auto read_slot = [&](int s, Operands& f) {
+      const uint8_t* sp = &sh.ring[s][0];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(sp + 512 * t + 32 * n + 8 * r);
+        f.kw[t][0] = v[0];
+        f.kw[t][1] = v[1];
+      }
+      f.ks = *reinterpret_cast<const u32x4*>(sp + kSlotKs + 16 * n);
+      f.kmin = *reinterpret_cast<const u32x4*>(sp + kSlotKm + 16 * n);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          f.vw[q][hb] = *reinterpret_cast<const u32x4*>(sp + kSlotV + (2 * r + q) * 512 +
+                                                         (64 * hb + 4 * n) * 4);
+      f.vs = *reinterpret_cast<const u32x4*>(sp + kSlotVs + 16 * n);
+      f.vmn = *reinterpret_cast<const u32x4*>(sp + kSlotVm + 16 * n);
+    };
+
+    // key A operand of the group and its q.K^T matrix products
+    auto qk_issue = [&](const Operands& pf) {
+      e_s = row_exp_f16(pf.ks);
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        float x[8];
+        float bsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = fmaf(qv[j][2 * i], h2f_lo(pf.ks[i]), 0.f);
+          x[2 * i + 1] = fmaf(qv[j][2 * i + 1], h2f_hi(pf.ks[i]), 0.f);
+          bsum = fmaf(qv[j][2 * i], h2f_lo(pf.kmin[i]), bsum);
+          bsum = fmaf(qv[j][2 * i + 1], h2f_hi(pf.kmin[i]), bsum);
+        }
+        bias[j] = row_sum16(bsum) * q_unscale;
+        write_digits(L.op.ak[j], r, a_off, x, e_s);
+      }
+      wave_sync();
+      v8i aq[NH];
+#pragma unroll
+      for (int H = 0; H < NH; ++H) aq[H] = read_a(L.op.ak[H], lane & 15, lane >> 4);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const v8i bk = fp4_operand(pf.kw[t][0], pf.kw[t][1]);
+#pragma unroll
+        for (int H = 0; H < NH; ++H)
+          cq[H][t] = mfma_f8f4(aq[H], bk, f32x4{0.f, 0.f, 0.f, 0.f}, sa_digit);
+      }
+    };
+
+    // logits of the group, softmax, value A operand and p.V
+    auto pv_step = [&](const Operands& pf) {
+      float logit[NH][8];
+      const float ek = exp2i(e_q - 8 + e_s + 1);   // fp4 codes are c/2
+#pragma unroll
+      for (int H = 0; H < NH; ++H)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          logit[H][t] =
+              fmaf((cq[H][t][0] + cq[H][t][1]) + (cq[H][t][2] + cq[H][t][3]), ek, bias[H]);
       float alpha[NH];
 #pragma unroll
       for (int H = 0; H < NH; ++H) {
-        f32x4 cw = f32x4{0.f, 0.f, 0.f, 0.f};
+        float v = logit[H][0];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) cw = mfma_f16(sh.win_a[H][c][kq][m_row], wt.k[c], cw);
-        const float lg = valid ? cw[0] + cw[1] : kNegInfF;
-        const float v = row_max16(lg);
-        const float m_new = fmaxf(m_run[H], v);   // finite: the tile has a valid token
+        for (int t = 1; t < 8; ++t) v = fmaxf(v, logit[H][t]);
+        v = row_max16(v);
+        const float m_new = fmaxf(m_run[H], v);
         alpha[H] = fexp2(m_run[H] - m_new);
         m_run[H] = m_new;
-        const float pw = valid ? fexp2(lg - m_new) : 0.f;
-        L.p[r + 4 * H][n] = pw;
-        l_part[H] = fmaf(l_part[H], alpha[H], pw);
+        float sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wacc[H][i] *= alpha[H];
+        for (int t = 0; t < 8; ++t) {
+          const float pe = fexp2(logit[H][t] - m_new);   // token 16t + n
+          L.pt[r + 4 * H][16 * t + n] = pe;
+          sum += pe;
+        }
+        l_part[H] = fmaf(l_part[H], alpha[H], sum);
       }
       wave_sync();
+      float p[NH][8];                // tokens 8n..8n+7 of head r + 4H
 #pragma unroll
       for (int H = 0; H < NH; ++H) {
-        // A = p (rows 4h' + {hi, lo, 0, 0}), tokens 8kq..8kq+7 of the tile (kq < 2)
-        u32x4 apw = u32x4{0u, 0u, 0u, 0u};
-        if ((m_row & 3) < 2 && kq < 2) {
-          const float* pp = &L.p[4 * H + (m_row >> 2)][8 * kq];
+        const f32x4* pp = reinterpret_cast<const f32x4*>(&L.pt[r + 4 * H][8 * n]);
+        const f32x4 p0 = pp[0], p1 = pp[1];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x0 = pp[2 * i], x1 = pp[2 * i + 1];
-            const auto hi = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-            const auto lo = __builtin_amdgcn_cvt_pkrtz(x0 - (float)hi[0], x1 - (float)hi[1]);
-            apw[i] = __builtin_bit_cast(uint32_t, (m_row & 1) ? lo : hi);
-          }
+        for (int e = 0; e < 4; ++e) {
+          p[H][e] = p0[e];
+          p[H][4 + e] = p1[e];
         }
+      }
+
+      // value A operand: digits of p s_t 2^(8 - e_v); min term
+      const int e_v_new = max(e_v, row_exp_f16(pf.vs));
+      const float vshift = exp2i(e_v - e_v_new);
+      e_v = e_v_new;
 #pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-          const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
-          const u32x4 bv = kq < 2 ? *reinterpret_cast<const u32x4*>(&L.vt[d][4 * kq])
-                                  : u32x4{0u, 0u, 0u, 0u};
-          wacc[H][blk] = mfma_f16(apw, bv, wacc[H][blk]);
+      for (int H = 0; H < NH; ++H) {
+        float x[8];
+        float mt = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = fmaf(p[H][2 * i], h2f_lo(pf.vs[i]), 0.f);
+          x[2 * i + 1] = fmaf(p[H][2 * i + 1], h2f_hi(pf.vs[i]), 0.f);
+          mt = fmaf(p[H][2 * i], h2f_lo(pf.vmn[i]), mt);
+          mt = fmaf(p[H][2 * i + 1], h2f_hi(pf.vmn[i]), mt);
         }
+        mterm[H] = fmaf(mterm[H], alpha[H], mt);
+        write_digits(L.op.av[H], r, a_off, x, e_v - 8);
       }
       wave_sync();
-    }
-#pragma unroll
-    for (int H = 0; H < NH; ++H)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wsum[H][i] = wacc[H][i][0] + wacc[H][i][1];
-  }
 
-  // ---------------------------------------------------------------- groups
-  const uint32_t a_off = a_offset(n);
-  const int sa_digit = 127 - 4 * (lane & 3);   // A row m = lane & 15 holds digit m % 4
-  int e_v = -1000;                 // running value-side exponent
-  f32x4 acc[NH][8];                // p.V: [head half][channel block], 4 digit rows
+      // rescale the accumulators (alpha and the exponent change)
+      {
+        bool same = true;
 #pragma unroll
-  for (int H = 0; H < NH; ++H)
+        for (int H = 0; H < NH; ++H) same = same && alpha[H] * vshift == 1.f;
+        if (!__all(same)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // The loop is software-pipelined over a wave's groups: while group g's
-  // softmax, value operand and p.V run, the key operand and q.K^T matrix
-  // products of group g + 4 are already issued, so the two dependency chains
-  // interleave.  Buffer parity: group g's data sits in pfa or pfb; its keys
-  // are consumed one iteration before its values.
-  int e_s_n = 0;                 // key exponent of the group whose q.K^T is in flight
-  float bias_n[NH];              // its q . key-min terms
-  f32x4 cq[NH][8];               // its q.K^T digit rows, per tile
-  auto clamp_group = [&](int64_t gi, int64_t& hh, int64_t& gg) {
-    const bool in = gi < ge;
-    hh = in ? head : 0;
-    gg = in ? gi : 0;
-  };
-
-  // key A operand of the group in pf, its q.K^T MFMAs; pf then receives the
-  // keys of group gk + 8
-  auto qk_issue = [&](Prefetch& pf, int64_t gk) {
-    e_s_n = row_exp_f16(pf.ks);
+          for (int H = 0; H < NH; ++H) {
+            const float f = alpha[H] * vshift;
 #pragma unroll
-    for (int j = 0; j < NH; ++j) {
-      float x[8];
-      float bsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = fmaf(qv[j][2 * i], h2f_lo(pf.ks[i]), 0.f);
-        x[2 * i + 1] = fmaf(qv[j][2 * i + 1], h2f_hi(pf.ks[i]), 0.f);
-        bsum = fmaf(qv[j][2 * i], h2f_lo(pf.kmin[i]), bsum);
-        bsum = fmaf(qv[j][2 * i + 1], h2f_hi(pf.kmin[i]), bsum);
-      }
-      bias_n[j] = row_sum16(bsum) * q_unscale;
-      write_digits(L.op.ak[j], r, a_off, x, e_s_n);
-    }
-    wave_sync();
-    v8i aq[NH];
-#pragma unroll
-    for (int H = 0; H < NH; ++H) aq[H] = read_a(L.op.ak[H], lane & 15, lane >> 4);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const v8i bk = fp4_operand(pf.kw[t][0], pf.kw[t][1]);
-#pragma unroll
-      for (int H = 0; H < NH; ++H)
-        cq[H][t] = mfma_f8f4(aq[H], bk, f32x4{0.f, 0.f, 0.f, 0.f}, sa_digit);
-    }
-    int64_t hh, gg;
-    clamp_group(gk + 2 * kWaves, hh, gg);
-    load_keys(a, hh, gg, n, r, pf);
-  };
-
-  // logits of the group whose q.K^T was issued last
-  auto qk_finish = [&](float (&logit)[NH][8]) {
-    const float ek = exp2i(e_q - 8 + e_s_n + 1);   // fp4 codes are c/2
-#pragma unroll
-    for (int H = 0; H < NH; ++H)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        logit[H][t] =
-            fmaf((cq[H][t][0] + cq[H][t][1]) + (cq[H][t][2] + cq[H][t][3]), ek, bias_n[H]);
-  };
-
-  // softmax, value A operand and p.V of the group in pf; pf then receives
-  // the values of group gv + 8
-  auto pv_step = [&](Prefetch& pf, int64_t gv, const float (&logit)[NH][8]) {
-    float alpha[NH];
-#pragma unroll
-    for (int H = 0; H < NH; ++H) {
-      float v = logit[H][0];
-#pragma unroll
-      for (int t = 1; t < 8; ++t) v = fmaxf(v, logit[H][t]);
-      v = row_max16(v);
-      const float m_new = fmaxf(m_run[H], v);
-      alpha[H] = fexp2(m_run[H] - m_new);
-      m_run[H] = m_new;
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float pe = fexp2(logit[H][t] - m_new);   // token 16t + n
-        L.pt[r + 4 * H][16 * t + n] = pe;
-        sum += pe;
-      }
-      l_part[H] = fmaf(l_part[H], alpha[H], sum);
-    }
-    wave_sync();
-    float p[NH][8];                // tokens 8n..8n+7 of head r + 4H
-#pragma unroll
-    for (int H = 0; H < NH; ++H) {
-      const f32x4* pp = reinterpret_cast<const f32x4*>(&L.pt[r + 4 * H][8 * n]);
-      const f32x4 p0 = pp[0], p1 = pp[1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[H][e] = p0[e];
-        p[H][4 + e] = p1[e];
-      }
-    }
-
-    // value A operand: digits of p s_t 2^(8 - e_v); min term
-    const int e_v_new = max(e_v, row_exp_f16(pf.vs));
-    const float vshift = exp2i(e_v - e_v_new);
-    e_v = e_v_new;
-#pragma unroll
-    for (int H = 0; H < NH; ++H) {
-      float x[8];
-      float mt = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = fmaf(p[H][2 * i], h2f_lo(pf.vs[i]), 0.f);
-        x[2 * i + 1] = fmaf(p[H][2 * i + 1], h2f_hi(pf.vs[i]), 0.f);
-        mt = fmaf(p[H][2 * i], h2f_lo(pf.vmn[i]), mt);
-        mt = fmaf(p[H][2 * i + 1], h2f_hi(pf.vmn[i]), mt);
-      }
-      mterm[H] = fmaf(mterm[H], alpha[H], mt);
-      write_digits(L.op.av[H], r, a_off, x, e_v - 8);
-    }
-    wave_sync();
-
-    // rescale the accumulators (alpha and the exponent change)
-    {
-      bool same = true;
-#pragma unroll
-      for (int H = 0; H < NH; ++H) same = same && alpha[H] * vshift == 1.f;
-      if (!__all(same)) {
-#pragma unroll
-        for (int H = 0; H < NH; ++H) {
-          const float f = alpha[H] * vshift;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            acc[H][i] *= f;
-            wsum[H][i] *= alpha[H];
+            for (int i = 0; i < 8; ++i) {
+              acc[H][i] *= f;
+              wsum[H][i] *= alpha[H];
+            }
           }
         }
       }
+
+      // p.V: one MFMA per 16-channel block and head half
+#pragma unroll
+      for (int H = 0; H < NH; ++H) {
+        const v8i apv = read_a(L.op.av[H], lane & 15, lane >> 4);
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+          const int hb = blk >> 2, comp = blk & 3;
+          acc[H][blk] = mfma_f8f4(apv, fp4_operand(pf.vw[0][hb][comp], pf.vw[1][hb][comp]),
+                                  acc[H][blk], sa_digit);
+        }
+      }
+    };
+
+    // Consumers claim the chunk's groups in order from a block counter and
+    // take each from the ring as soon as the loader has published it.
+    for (;;) {
+      int jl = 0;
+      if (lane == 0) jl = atomicAdd(&sh.next_group, 1);
+      const int j = __builtin_amdgcn_readlane(jl, 0);
+      if (j >= ngc) break;
+      const int s = j % R;
+      if (!spin_until(&sh.ready[s], j)) {
+        if (lane == 0) lds_store(&sh.stalled, 1);
+        break;
+      }
+      asm volatile("" ::: "memory");
+      Operands pf;
+      read_slot(s, pf);
+      asm volatile("" ::: "memory");
+      // this wave's LDS reads complete in order before its next LDS write
+      if (lane == 0) lds_store(&sh.empty[s], j + R);
+      qk_issue(pf);
+      pv_step(pf);
     }
 
-    // p.V: one MFMA per 16-channel block and head half
+    // fold the digit rows of the quantized p.V into the lane's channels
+    const float ev = exp2i(e_v - 8 + 1);   // p.V digits carry 2^(8 - e_v), codes are c/2
 #pragma unroll
     for (int H = 0; H < NH; ++H) {
-      const v8i apv = read_a(L.op.av[H], lane & 15, lane >> 4);
+      const float mts = row_sum16(mterm[H]);
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
-        const int hb = blk >> 2, comp = blk & 3;
-        acc[H][blk] = mfma_f8f4(apv, fp4_operand(pf.vw[0][hb][comp], pf.vw[1][hb][comp]),
-                                acc[H][blk], sa_digit);
+        const f32x4 v = acc[H][blk];
+        wsum[H][blk] += fmaf((v[0] + v[1]) + (v[2] + v[3]), ev, mts);
       }
-    }
-    int64_t hh, gg;
-    clamp_group(gv + 2 * kWaves, hh, gg);
-    load_values(a, hh, gg, n, r, pf);
-  };
-
-  if (g < ge) {
-    float logit[NH][8];
-    qk_issue(pfa, g);
-    qk_finish(logit);
-    for (;;) {
-      qk_issue(pfb, g + kWaves);     // next group's keys (a dummy past the end)
-      pv_step(pfa, g, logit);
-      qk_finish(logit);
-      g += kWaves;
-      if (g >= ge) break;
-      qk_issue(pfa, g + kWaves);
-      pv_step(pfb, g, logit);
-      qk_finish(logit);
-      g += kWaves;
-      if (g >= ge) break;
     }
   }
 
   // ---------------------------------------------------------------- block merge
-  float lsum[NH], mtsum[NH];
+  float lsum[NH];
 #pragma unroll
-  for (int H = 0; H < NH; ++H) {
-    lsum[H] = row_sum16(l_part[H]);
-    mtsum[H] = row_sum16(mterm[H]);
-  }
+  for (int H = 0; H < NH; ++H) lsum[H] = row_sum16(l_part[H]);
   __syncthreads();   // the per-wave buffers are reused for the merge below
   MergeLdsF<GQA>& M = sh.u.merge;
-  const float ev = exp2i(e_v - 8 + 1);   // p.V digits carry 2^(8 - e_v), codes are c/2
 #pragma unroll
   for (int H = 0; H < NH; ++H) {
     const int h = r + 4 * H;
@@ -706,12 +800,12 @@ __global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
-      const f32x4 v = acc[H][blk];
-      M.num[wave][h][d] = fmaf((v[0] + v[1]) + (v[2] + v[3]), ev, mtsum[H]) + wsum[H][blk];
+      M.num[wave][h][d] = wsum[H][blk];
     }
   }
   __syncthreads();
   const int n_parts = a.n_parts;
+  const bool stalled = lds_load(&sh.stalled) != 0;
   for (int i = tid; i < GQA * kD; i += kThreadsF) {
     const int h = i / kD, d = i % kD;
     float mm = kNegInfF;
@@ -726,6 +820,7 @@ __global__ __launch_bounds__(kThreadsF, mfma_blocks_per_cu(2, GQA)) void decode_
         num = fmaf(M.num[w][h][d], f, num);
         den = fmaf(M.l[w][h], f, den);
       }
+    if (stalled) num = den = __builtin_nanf("");   // a wait ran out: poison the result
     float* wp = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + chunk) * (kD + 2);
     wp[2 + d] = num;
     if (d == 0) {

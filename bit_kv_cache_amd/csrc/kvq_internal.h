@@ -89,9 +89,9 @@ struct DecodeArgs {
 inline bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
   return group == 128 && (gqa == 4 || gqa == 8) && n_boost == 0 && (bits == 2 || bits == 4);
 }
-// Resident blocks (of 4 waves) per CU of the matrix-core kernels (their
-// register use allows two waves per SIMD).
-constexpr int mfma_blocks_per_cu(int, int) { return 2; }
+// Resident blocks per CU of the matrix-core kernels: two waves per SIMD,
+// as one block of 8 waves (2-bit, fp8 x fp4 kernel) or two of 4 (4-bit).
+constexpr int mfma_blocks_per_cu(int bits, int) { return bits == 2 ? 1 : 2; }
 constexpr int kCUs = 256;  // MI355X
 inline int mfma_resident_blocks(int bits, int gqa) { return kCUs * mfma_blocks_per_cu(bits, gqa); }
 

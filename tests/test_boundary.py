@@ -113,12 +113,14 @@ def test_decode_rejects_bad_arguments():
 
 def test_decode_plan():
     cfg = kvq.QCfg(bits=2, group=128)
-    # matrix-core path (GQA 4/8, G 128): resident blocks (2 per CU) over the heads
-    assert kvq.kvq_decode_plan(cfg, 8, 32, 8, 32768)[0] == 8
-    assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 1 << 20)[0] == 64
+    # matrix-core path (GQA 4/8, G 128): resident blocks over the heads -- one
+    # 8-wave block per CU for 2-bit codes, two 4-wave blocks per CU for 4-bit
+    assert kvq.kvq_decode_plan(cfg, 8, 32, 8, 32768)[0] == 4
+    assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 1 << 20)[0] == 32
     assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 1 << 20, 256)[0] == 256
-    assert kvq.kvq_decode_plan(cfg, 32, 32, 8, 8192)[0] == 2
-    assert kvq.kvq_decode_plan(cfg, 16, 64, 8, 131072)[0] == 4
+    assert kvq.kvq_decode_plan(cfg, 32, 32, 8, 8192)[0] == 1
+    assert kvq.kvq_decode_plan(cfg, 16, 64, 8, 131072)[0] == 2
+    assert kvq.kvq_decode_plan(kvq.QCfg(bits=4, group=128), 32, 32, 8, 8192)[0] == 2
     assert kvq.kvq_decode_plan(cfg, 1, 32, 8, 0)[0] == 1      # windows only: one chunk
     nc, ws = kvq.kvq_decode_plan(cfg, 8, 32, 8, 32768)
     assert ws >= 8 * 32 * nc * 130 * 4

@@ -134,13 +134,16 @@ def test_no_tokens_gives_zero(built):
     assert torch.count_nonzero(out).item() == 0
 
 
-def test_decode_deterministic(built):
+def test_decode_repeatable(built):
+    """Repeated decode steps agree to fp32 summation order: the 2-bit
+    matrix-core kernel hands groups to waves dynamically, so which wave sums
+    which group (and the last bits of the sums) can change between calls."""
     w = _w("llama_2bit")
     inp = make_inputs(w)
     gc = gpu_quantize(w, inp)
     a = gpu_decode(w, gc, inp, w.T)
     b = gpu_decode(w, gc, inp, w.T)
-    assert torch.equal(a, b)
+    assert (a - b).abs().max().item() <= 1e-6
     # quantizing twice writes identical bits
     gc2 = gpu_quantize(w, inp)
     torch.cuda.synchronize()
@@ -211,7 +214,9 @@ def test_partials_then_merge_equals_one_call(built, name):
     B = len(inp["heads"]) // w.H_kv
     out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
     kvq.kvq_decode_merge(B, w.H_q, parts.shape[1], parts.contiguous(), out)
-    assert torch.equal(out, one)
+    # same kernels and chunking; equal up to the summation order of the
+    # dynamically scheduled 2-bit kernel
+    assert (out - one).abs().max().item() <= 1e-6
 
 
 @pytest.mark.parametrize("name", ["llama_2bit", "kitty"])
