@@ -343,9 +343,18 @@ def main(argv=None):
         if st:
             raise kvq.KvqError(st, "kvq_quantize_pack")
 
+    def step(i):
+        # one whole step: decode + append of the full residual group, one call
+        # (the append runs inside the split-K launch where the path fuses it)
+        st = lib.kvq_decode_step(ctypes.byref(c_cfg), ctypes.byref(c_caches[i % n_copies]),
+                                 w.B, w.H_q, w.H_kv, q.data_ptr(), w.T, sink_p, res_p,
+                                 ctypes.c_float(0.0), n_chunks, ws.data_ptr(), ws_bytes,
+                                 out.data_ptr(), 1 if append else 0, sp)
+        if st:
+            raise kvq.KvqError(st, "kvq_decode_step")
+
     for i in range(args.warmup):
-        decode(i)
-        quant(i)
+        step(i)
     torch.cuda.synchronize()
 
     # timed region: whole steps -------------------------------------------------------
@@ -353,11 +362,20 @@ def main(argv=None):
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # the same step as three launches (decode partials, merge, quantize), for context
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
         decode(i)
         quant(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_unfused = e0.elapsed_time(e1) / args.steps
 
     # per-kernel durations on the launch stream (HIP events between the launches)
     n_k = min(args.steps, 100)
@@ -422,7 +440,7 @@ def main(argv=None):
                    "T": w.T, "R": w.R, "S": w.S, "bits": w.bits, "G": w.G,
                    "n_boost": w.n_boost, "n_chunks": n_chunks, "cache_copies": n_copies,
                    "cache_bytes_per_copy": cache_bytes_one, "step": "decode + append-group "
-                   "quantize" if append else "decode"},
+                   "quantize (kvq_decode_step)" if append else "decode (kvq_decode_step)"},
         "effective_GBps": round(eff_gbps, 1),
         "effective_frac_of_peak": round(eff_gbps / HBM_PEAK_GBPS, 4),
         "decode_us": {"avg": round(dec_avg * 1e3, 3), "p10": round(dec_ms[n_k // 10] * 1e3, 3),
@@ -435,6 +453,7 @@ def main(argv=None):
                                 "launch stream; *_isolated_avg: an event pair around every "
                                 "launch"},
         "append_quant_us": round(app_avg * 1e3, 3) if append else None,
+        "step_unfused_us": round(ms_unfused * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": read_traffic(w),

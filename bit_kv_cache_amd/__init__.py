@@ -30,8 +30,8 @@ KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_ALIGN, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_
     0, -1, -2, -3, -4, -5)
 
 EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
-            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_partials",
-            "kvq_decode_merge", "kvq_dequantize")
+            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_step",
+            "kvq_decode_partials", "kvq_decode_merge", "kvq_dequantize")
 
 
 class kvq_qcfg(ctypes.Structure):
@@ -65,6 +65,9 @@ _lib.kvq_decode_workspace_bytes.restype = _sz
 _lib.kvq_decode_attention.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32,
                                       _P, _sz, _P, _P]
 _lib.kvq_decode_attention.restype = ctypes.c_int
+_lib.kvq_decode_step.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32, _P,
+                                 _sz, _P, _i32, _P]
+_lib.kvq_decode_step.restype = ctypes.c_int
 _lib.kvq_decode_partials.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32,
                                      _P, _sz, _P, _P]
 _lib.kvq_decode_partials.restype = ctypes.c_int
@@ -216,6 +219,21 @@ def kvq_decode_attention(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int,
         ctypes.byref(res) if res is not None else None, float(sm_scale), int(n_chunks),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
         _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_decode_step(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int, q: torch.Tensor,
+                    n_quant_tokens: int, sink: kvq_window | None, res: kvq_window | None,
+                    out: torch.Tensor, workspace: torch.Tensor, append: bool,
+                    sm_scale: float = 0.0, n_chunks: int = 0, stream=None) -> None:
+    """Decode step + (when ``append``) the residual group quantized into group
+    ``n_quant_tokens / G`` in the same launch where the path supports it."""
+    c_cfg, c_cache = cfg.c(), cache.c()
+    _check(_lib.kvq_decode_step(
+        ctypes.byref(c_cfg), ctypes.byref(c_cache), B, H_q, H_kv, _ptr(q), n_quant_tokens,
+        ctypes.byref(sink) if sink is not None else None,
+        ctypes.byref(res) if res is not None else None, float(sm_scale), int(n_chunks),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        1 if append else 0, _stream(stream)), "kvq_decode_step")
 
 
 def kvq_decode_partials(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int,

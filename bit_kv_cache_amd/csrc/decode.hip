@@ -16,6 +16,7 @@
 
 #include "kvq_internal.h"
 #include "decode_common.h"
+#include "merge_common.h"
 
 namespace kvq {
 namespace {
@@ -154,37 +155,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // Log-sum-exp merge of up to NPM parts: one block per (batch, query head),
-// one thread per channel.  Every load is issued up front (part indices past
-// the count re-read the last part and get weight 0), so the merge costs one
-// memory round trip.
+// one thread per channel.
 template <int NPM>
 __global__ __launch_bounds__(kD) void merge_small_kernel(DecodeArgs a) {
-  const int64_t bh = blockIdx.x;
-  const int d = threadIdx.x;
-  const int np = a.n_parts;
-  const float* w = a.ws + bh * (int64_t)np * (kD + 2);
-  float m[NPM], l[NPM], v[NPM];
-#pragma unroll
-  for (int j = 0; j < NPM; ++j) {
-    const float* wp = w + (int64_t)min(j, np - 1) * (kD + 2);
-    m[j] = wp[0];
-    l[j] = wp[1];
-    v[j] = wp[2 + d];
-  }
-  float M = kNegInf;
-#pragma unroll
-  for (int j = 0; j < NPM; ++j)
-    if (j < np && l[j] > 0.f) M = fmaxf(M, m[j]);
-  // weights select rather than branch, so the loads stay unconditional (an
-  // excluded part's values are finite: empty parts hold zeros)
-  float L = 0.f, o = 0.f;
-#pragma unroll
-  for (int j = 0; j < NPM; ++j) {
-    const float f = (j < np && l[j] > 0.f) ? exp2f(m[j] - M) : 0.f;
-    L = fmaf(l[j], f, L);
-    o = fmaf(v[j], f, o);
-  }
-  a.out[bh * kD + d] = L > 0.f ? o / L : 0.f;
+  merge_row<NPM>(a.ws, a.n_parts, a.out, blockIdx.x, threadIdx.x);
 }
 
 // Log-sum-exp merge of the parts: one block per (batch, query head).

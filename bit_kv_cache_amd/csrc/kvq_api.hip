@@ -232,6 +232,34 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
   return hip_status(kvq::launch_merge(a, s));
 }
 
+kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,
+                           int32_t H_kv, const uint16_t* q, int64_t n_quant_tokens,
+                           const kvq_window* sink, const kvq_window* res, float sm_scale,
+                           int32_t n_chunks, void* workspace, size_t ws_bytes, float* out,
+                           int32_t append, void* stream) {
+  kvq::DecodeArgs a;
+  kvq_status st = prepare_decode(cfg, cache, B, H_q, H_kv, q, n_quant_tokens, sink, res,
+                                 sm_scale, n_chunks, workspace, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!out) return KVQ_ERR_ARG;
+  if (!aligned16(out)) return KVQ_ERR_ALIGN;
+  const int64_t G = cfg->group;
+  if (append) {
+    // the residual holds the full group that becomes group n_quant_tokens / G
+    if (!res || res->n < G || n_quant_tokens + G > cache->t_cap) return KVQ_ERR_ARG;
+    if ((int64_t)H_kv * B * 8 + (int64_t)B * H_q > 0x7FFFFFFF) return KVQ_ERR_ARG;
+  }
+  a.out = out;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s))) != KVQ_OK)
+    return st;
+  if (!append) return hip_status(kvq::launch_merge(a, s));
+  const int64_t heads = (int64_t)B * H_kv;
+  const kvq::QuantArgs qa{cache_args(cache), res->k,          res->v,   (int64_t)res->cap * kD,
+                          n_quant_tokens / G, 1,              (int32_t)heads, cfg->n_boost};
+  return hip_status(kvq::launch_merge_append(cfg->bits, cfg->group, a, qa, s));
+}
+
 kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
                                int32_t H_q, int32_t H_kv, const uint16_t* q,
                                int64_t n_quant_tokens, const kvq_window* sink,

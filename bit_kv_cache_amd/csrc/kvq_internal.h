@@ -100,6 +100,12 @@ hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t 
 hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStream_t s);
 hipError_t launch_decode_partials(int bits, int group, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+// The merge of a decode step and the quantize of an appended group (both
+// small, latency-bound) as one launch; separate launches when the step has
+// more than kMergeAppendParts parts.
+constexpr int kMergeAppendParts = 32;
+hipError_t launch_merge_append(int bits, int group, const DecodeArgs& d, const QuantArgs& q,
+                               hipStream_t s);
 hipError_t launch_decode_mfma(int bits, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t s);
 

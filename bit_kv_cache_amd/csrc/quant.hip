@@ -19,6 +19,8 @@
 // of a group, so with n_boost > 0 one block quantizes the whole key group.
 
 #include "kvq_internal.h"
+#include "quant_common.h"
+#include "merge_common.h"
 
 #pragma clang fp contract(off)
 
@@ -31,23 +33,6 @@ constexpr int kSlices = 4;
 __device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float maxq) {
   if (s == 0.0f) return 0u;
   float y = (x - mn) / s;
-  y = fminf(fmaxf(y, 0.0f), maxq);
-  return (uint32_t)__builtin_rintf(y);
-}
-
-// The same code with the quotient taken as (x - mn) * rs, rs = 1/s rounded,
-// falling back to the IEEE quotient near a rounding tie.  Exact: the range
-// fits (x - mn)/s <= 1.5 maxq <= 22.5 (s is the fp16-rounded range/maxq, at
-// least 2^-24 when nonzero), so the product and the IEEE quotient differ by
-// at most a few ulps of 32 (< 2^-17), and round-half-even of two values that
-// close differs only when a half-integer lies within 2^-16 of them; the clamp
-// bounds are integers and cannot change that.
-__device__ __forceinline__ uint32_t quant_code_rcp(float x, float mn, float s, float rs,
-                                                   float maxq) {
-  if (s == 0.0f) return 0u;
-  const float dlt = x - mn;
-  float y = dlt * rs;
-  if (__builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-16f) y = dlt / s;
   y = fminf(fmaxf(y, 0.0f), maxq);
   return (uint32_t)__builtin_rintf(y);
 }
@@ -308,6 +293,32 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   }
 }
 
+// The merge of a decode step and the quantize of the group it appends, in
+// one launch: blocks [0, n_merge) merge two (batch, query head) rows each
+// (threads 0..127 and 128..255, one channel per thread); the blocks after
+// them are the quantize kernel's (group, slice) blocks.  The two jobs share
+// no memory (partials and output vs. residual rows and one cache group).
+template <int BITS, int G, bool KITTY, int NPM>
+__global__ __launch_bounds__(kThreads) void merge_append_kernel(DecodeArgs d, QuantArgs a,
+                                                               int n_merge) {
+  const int blk = blockIdx.x;
+  if (blk < n_merge) {
+    const int64_t bh = 2 * (int64_t)blk + (threadIdx.x >> 7);
+    if (bh < (int64_t)d.B * d.H_q) merge_row<NPM>(d.ws, d.n_parts, d.out, bh, threadIdx.x & 127);
+    return;
+  }
+  const int qb = blk - n_merge;
+  const int64_t head = qb / (2 * kSlices);   // one group: (head, slice)
+  const int y = qb % (2 * kSlices);
+  if (y >= kSlices) {
+    if (y - kSlices < kValueSlices<BITS, G>) quantize_values_slice<BITS, G>(a, head, 0, y - kSlices);
+  } else if constexpr (KITTY) {
+    if (y == 0) quantize_keys_kitty<G>(a, head, 0);
+  } else {
+    quantize_keys_slice<BITS, G>(a, head, 0, y);
+  }
+}
+
 // Dequantize: one thread per (token, channel) of keys and values.
 template <int BITS, int G>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
@@ -372,7 +383,39 @@ hipError_t dequantize_bits(int group, const DequantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BITS, bool KITTY, int NPM>
+hipError_t merge_append_bits(int group, const DecodeArgs& d, const QuantArgs& a, hipStream_t s) {
+  const int n_merge = (int)(((int64_t)d.B * d.H_q + 1) / 2);
+  const dim3 grid((unsigned)(n_merge + a.n_heads * 2 * kSlices));
+  switch (group) {
+    case 32: merge_append_kernel<BITS, 32, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge); break;
+    case 64: merge_append_kernel<BITS, 64, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge); break;
+    case 128: merge_append_kernel<BITS, 128, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int BITS, bool KITTY>
+hipError_t merge_append_parts(int group, const DecodeArgs& d, const QuantArgs& a, hipStream_t s) {
+  if (d.n_parts <= 8) return merge_append_bits<BITS, KITTY, 8>(group, d, a, s);
+  if (d.n_parts <= 16) return merge_append_bits<BITS, KITTY, 16>(group, d, a, s);
+  return merge_append_bits<BITS, KITTY, kMergeAppendParts>(group, d, a, s);
+}
+
 }  // namespace
+
+hipError_t launch_merge_append(int bits, int group, const DecodeArgs& d, const QuantArgs& a,
+                               hipStream_t s) {
+  if (d.n_parts > kMergeAppendParts || a.n_groups != 1) {
+    const hipError_t e = launch_merge(d, s);
+    return e != hipSuccess ? e : launch_quantize(bits, group, a, s);
+  }
+  if (bits == 2)
+    return a.n_boost > 0 ? merge_append_parts<2, true>(group, d, a, s)
+                         : merge_append_parts<2, false>(group, d, a, s);
+  return merge_append_parts<4, false>(group, d, a, s);
+}
 
 hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s) {
   if (a.n_groups == 0 || a.n_heads == 0) return hipSuccess;

@@ -1,0 +1,46 @@
+// Device helpers of the min-max group quantizer shared by the quantize kernel
+// and the decode kernel's fused append (not installed).
+#pragma once
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+// Code of x in a group with min mn and stored scale s (rs = 1/s rounded):
+// round-half-even(clamp((x - mn)/s, 0, maxq)) with the IEEE fp32 quotient
+// (KIVI page, Step 1).  The quotient is taken as (x - mn) * rs, falling
+// back to the IEEE division near a rounding tie.  Exact: the range fits
+// (x - mn)/s <= 1.5 maxq <= 22.5 (s is the fp16-rounded range/maxq, at least
+// 2^-24 when nonzero), so the product and the IEEE quotient differ by at most
+// a few ulps of 32 (< 2^-17), and round-half-even of two values that close
+// differs only when a half-integer lies within 2^-16 of them; the clamp
+// bounds are integers and cannot change that.  s == 0 (max == min, or a
+// range whose scale underflows fp16) gives code 0.
+__device__ __forceinline__ uint32_t quant_code_rcp(float x, float mn, float s, float rs,
+                                                   float maxq) {
+#pragma clang fp contract(off)
+  if (s == 0.0f) return 0u;
+  const float dlt = x - mn;
+  float y = dlt * rs;
+  if (__builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-16f) y = dlt / s;
+  y = fminf(fmaxf(y, 0.0f), maxq);
+  return (uint32_t)__builtin_rintf(y);
+}
+
+// Exact code by the IEEE quotient (the reference form of quant_code_rcp).
+__device__ __forceinline__ uint32_t quant_code_div(float x, float mn, float s, float maxq) {
+#pragma clang fp contract(off)
+  if (s == 0.0f) return 0u;
+  float y = (x - mn) / s;
+  y = fminf(fmaxf(y, 0.0f), maxq);
+  return (uint32_t)__builtin_rintf(y);
+}
+
+// fp16 scale of a group from its min and max: fp16((max - min)/maxq), the
+// subtraction and division in IEEE fp32, both rounded to nearest even.
+__device__ __forceinline__ uint16_t group_scale(float mn, float mx, float maxq) {
+#pragma clang fp contract(off)
+  return f2h((mx - mn) / maxq);
+}
+
+}  // namespace kvq

@@ -165,6 +165,24 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
                                 const kvq_window* res, float sm_scale, int32_t n_chunks,
                                 void* workspace, size_t ws_bytes, float* out, void* stream);
 
+/* One decode step with the streaming append: the attention of
+ * kvq_decode_attention (same arguments and result) and, when append != 0, the
+ * quantize + pack of the first G rows of the residual window of every head
+ * into cache group n_quant_tokens / G -- the residual group that has filled
+ * up (KIVI page, Step 3; Kitty page, section 4.3, stage 3), whose tokens this
+ * step still attends to in fp16.  The cache contents equal those of
+ * kvq_quantize_pack(cfg, cache, B, H_kv, res->k, res->v, res->cap * D,
+ * n_quant_tokens / G, 1), bit for bit.  The quantization runs in the same
+ * launch as the log-sum-exp merge (two launches per step instead of three;
+ * separate launches when the step has more than 32 parts).
+ *  append != 0 requires res->n >= G and n_quant_tokens + G <= t_cap
+ *  (else KVQ_ERR_ARG, nothing launched). */
+kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,
+                           int32_t H_kv, const uint16_t* q, int64_t n_quant_tokens,
+                           const kvq_window* sink, const kvq_window* res, float sm_scale,
+                           int32_t n_chunks, void* workspace, size_t ws_bytes, float* out,
+                           int32_t append, void* stream);
+
 /* The two phases of kvq_decode_attention, for callers that combine partial
  * results of several calls (for example a sequence split across devices, each
  * holding a token range of the same heads) or time the phases apart.

@@ -3,8 +3,8 @@ benchmark times (the library's automatic chunk plan, or the workload's
 minimum chunk count), checked on sampled heads.
 
 Every head of the full cache is quantized on the GPU and one decode step runs
-over all of them in a single launch; the full residual group is then appended
-(the benchmark's step).  The oracle regenerates the sampled heads' seeded
+over all of them, appending the full residual group into the cache (the
+benchmark's step, kvq_decode_step).  The oracle regenerates the sampled heads' seeded
 inputs and recomputes just those heads: their packed codes, scales, mins (and
 Kitty high words / indices) must be bit-exact over every token slot, and their
 query heads' attention outputs within max-abs 2e-3 of the oracle's fp64
@@ -69,13 +69,11 @@ def test_full_size_sampled_heads(built, name):
         assert n_chunks >= w.min_chunks
     ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
     out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
-    kvq.kvq_decode_attention(cfg, cache, w.B, w.H_q, w.H_kv, q, w.T,
-                             kvq.window(k_sink, v_sink, w.S), kvq.window(k_res, v_res, w.R),
-                             out, ws, n_chunks=w.min_chunks)
-    # then the append of the full residual group (when the window holds one)
+    # the benchmark's step: decode + append of the full residual group (when
+    # the window holds one) in one call
     append = w.R >= w.G
-    if append:
-        kvq.kvq_quantize_pack(cfg, cache, 1, w.heads, k_res, v_res, w.T // w.G, 1)
+    kvq.kvq_decode_step(cfg, cache, w.B, w.H_q, w.H_kv, q, w.T, kvq.window(k_sink, v_sink, w.S),
+                        kvq.window(k_res, v_res, w.R), out, ws, append, n_chunks=w.min_chunks)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
 

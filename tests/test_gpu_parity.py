@@ -275,3 +275,51 @@ def test_quantize_rounding_ties_bit_exact(built):
         oc = oracle_quantize(w, inp)
         torch.cuda.synchronize()
         assert_cache_equal(gc, oc, tokens=w.T)
+
+
+@pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "long_splitk", "llama_4bit", "kitty"])
+def test_decode_step_with_append(built, name):
+    """kvq_decode_step(append): the attention equals the oracle over the
+    quantized tokens + the full fp16 residual group, and the residual group
+    lands in cache group T/G bit-exact (quantized in the merge's launch, or
+    in launches of their own past 32 parts)."""
+    import bit_kv_cache_amd as kvq
+    w = _w(name)
+    w = synth.shrink(w, R=w.G)
+    inp = make_inputs(w)
+    t_cap = w.T + w.G
+    gc = gpu_quantize(w, inp, t_cap)
+    oc = oracle_quantize(w, inp, t_cap)
+    B = len(inp["heads"]) // w.H_kv
+    for n_chunks in (0, 3):
+        _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), B, w.H_q, w.H_kv, w.T, n_chunks)
+        ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+        out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+        kvq.kvq_decode_step(qcfg(w), gc, B, w.H_q, w.H_kv, inp["q"][:B].contiguous(), w.T,
+                            kvq.window(inp["k_sink"], inp["v_sink"], w.S),
+                            kvq.window(inp["k_res"], inp["v_res"], w.R), out, ws, True,
+                            n_chunks=n_chunks)
+        ref = oracle_decode(w, oc, inp, w.T)
+        err = max_err(out, ref)
+        assert err <= TOL, f"{name} n_chunks={n_chunks}: max-abs {err:.3g}"
+    oracle.quantize_pack(oc, synth.as_bits(inp["k_res"]), synth.as_bits(inp["v_res"]),
+                         w.T // w.G, 1)
+    torch.cuda.synchronize()
+    assert_cache_equal(gc, oc, tokens=t_cap)
+    # the next step reads the appended group like any other
+    out = gpu_decode(w, gc, inp, t_cap, n_res=0)
+    assert max_err(out, oracle_decode(w, oc, inp, t_cap, n_res=0)) <= TOL
+
+
+def test_decode_step_append_rejects_short_residual(built):
+    import bit_kv_cache_amd as kvq
+    w = _w("llama_2bit")
+    inp = make_inputs(w)
+    gc = gpu_quantize(w, inp)
+    B = len(inp["heads"]) // w.H_kv
+    _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), B, w.H_q, w.H_kv, w.T, 0)
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_decode_step(qcfg(w), gc, B, w.H_q, w.H_kv, inp["q"][:B].contiguous(), w.T, None,
+                            kvq.window(inp["k_res"], inp["v_res"], w.G - 1), out, ws, True)
