@@ -211,24 +211,31 @@ struct MergeLdsF {
 //   [4096, 8192)   value words, 8 rows of 128 channels, as in the cache
 //   [8192, 8448)   key scale of the 128 channels (fp16), then key min,
 //   [8704, 8960)   value scale of the 128 tokens, then value min
-constexpr int kSlotBytes = 9216;
+// and with the Kitty boost (16 boosted key channels per group)
+//   [9216, 9728)   high-bits word of each token (boosted rows 0..15)
+//   [9728, 9856)   boosted row of each channel (16 = not boosted), then pad
 constexpr int kSlotV = 4096, kSlotKs = 8192, kSlotKm = 8448, kSlotVs = 8704, kSlotVm = 8960;
+constexpr int kSlotHi = 9216, kSlotBidx = 9728;
+template <bool KITTY>
+constexpr int slot_bytes() { return KITTY ? 10240 : 9216; }
+template <bool KITTY>
+constexpr int dma_per_group() { return KITTY ? 10 : 9; }
 template <int GQA>
-constexpr int ring_slots() { return GQA == 4 ? 8 : 5; }
-// groups the loader keeps in flight (at most ring_slots; 9 loads per group,
-// and the vector-memory counter holds at most 63)
+constexpr int ring_slots() { return GQA == 4 ? 8 : 6; }
+// groups the loader keeps in flight (at most ring_slots; the vector-memory
+// counter holds at most 63 copies)
 template <int GQA>
 constexpr int in_flight() { return ring_slots<GQA>() - 1; }
+static_assert(10 * (ring_slots<4>() - 2) < 64 && 10 * (ring_slots<8>() - 2) < 64, "vmcnt range");
 
-template <int GQA>
+template <int GQA, bool KITTY>
 struct LdsF {
   static constexpr int R = ring_slots<GQA>();
   union {
     WaveLdsF<GQA> w[kConsumers];
     MergeLdsF<GQA> merge;
   } u;
-  u32x4 win_a[GQA / 4][4][4][16];                 // window q.K^T A: [half][c][kq][row]
-  alignas(16) uint8_t ring[R][kSlotBytes];
+  alignas(16) uint8_t ring[R][slot_bytes<KITTY>()];
   int ready[R];     // the chunk-relative group a slot holds once its data has arrived
   int empty[R];     // the group a slot may receive next (its previous one was copied out)
   int next_group;   // next group a consumer claims
@@ -237,6 +244,7 @@ struct LdsF {
 
 struct Operands {
   uint32_t kw[8][2];     // key words: tile t, token 16t + n, words 2r, 2r + 1
+  uint32_t hw[8];        // Kitty: high-bits word of token 16t + n
   u32x4 ks, kmin;        // key scale / min of channels 8n..8n+7
   u32x4 vw[2][2];        // value words: rows 2r, 2r + 1; channels 4n.. and 64 + 4n..
   u32x4 vs, vmn;         // value scale / min of tokens 8n..8n+7
@@ -325,12 +333,14 @@ __device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
 
 // ------------------------------------------------------------------ kernel
 
-template <int GQA>
+template <int GQA, bool KITTY>
 __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a) {
   constexpr int NH = GQA / 4;    // heads per lane (r and r + 4)
   constexpr int R = ring_slots<GQA>();
   constexpr int DF = in_flight<GQA>();
-  __shared__ LdsF<GQA> sh;
+  constexpr int SB = slot_bytes<KITTY>();
+  constexpr int NDMA = dma_per_group<KITTY>();
+  __shared__ LdsF<GQA, KITTY> sh;
 
   // Every launch argument the first phase needs, fetched in one round trip
   // (the compiler would otherwise load each one just before its first use,
@@ -396,6 +406,13 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
                          : part == 2 ? a.c.v_scale : a.c.v_min;
     const int64_t m0 = part < 2 ? (head * (a.c.t_cap / kG) + gb) * kD : head * a.c.t_cap + gb * kG;
     const char* mp = reinterpret_cast<const char*>(marr + m0) + 16 * sub;
+    // Kitty lanes: 0..31 the group's 128 high-bits words, 32..39 its 128
+    // boosted-row bytes (40..63 repeat them into the pad)
+    const char* xp = lane < 32 ? reinterpret_cast<const char*>(a.c.k_hi) +
+                                     (head * a.c.t_cap + gb * kG) * 4 + 16 * lane
+                               : reinterpret_cast<const char*>(a.c.k_bidx) +
+                                     (head * (a.c.t_cap / kG) + gb) * kD + 16 * ((lane - 32) & 7);
+    const int64_t xstep = lane < 32 ? kG * 4 : kD;
     // LDS byte address of the ring (address-space cast of the generic pointer)
     const uint32_t ring0 =
         (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)(&sh.ring[0][0]));
@@ -407,15 +424,16 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
         break;
       }
       asm volatile("" ::: "memory");
-      const uint32_t sl = __builtin_amdgcn_readfirstlane(ring0 + s * kSlotBytes);
+      const uint32_t sl = __builtin_amdgcn_readfirstlane(ring0 + s * SB);
       const int64_t jo = j;
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_1k(sl + 1024 * i, kp + jo * 4096 + 1024 * i);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_1k(sl + kSlotV + 1024 * i, vp + jo * 4096 + 1024 * i);
       dma_1k(sl + kSlotKs, mp + jo * 256);
+      if constexpr (KITTY) dma_1k(sl + kSlotHi, xp + jo * xstep);
       if (j >= DF - 1) {
-        vm_wait<9 * (DF - 1)>();     // group j - DF + 1 has landed
+        vm_wait<NDMA * (DF - 1)>();     // group j - DF + 1 has landed
         if (lane == 0) lds_store(&sh.ready[(j - DF + 1) % R], j - DF + 1);
       }
     }
@@ -605,6 +623,24 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
     float bias[NH];                // its q . key-min terms
     f32x4 cq[NH][8];               // its q.K^T digit rows, per tile
 
+    // Kitty.  The high-bits word of a token (2 bits per boosted row j,
+    // rows ascending with the channel index) is the B operand of an extra
+    // product; lane group g holds rows 8 (g % 2) + 2i in nibble i and rows
+    // 8 (g % 2) + 2i + 1 in nibble 16 + i (i < 4), which pair with A bytes
+    // 0..3 of lane groups 2 (g % 2) and 2 (g % 2) + 1 (fp4_operand, a_offset).
+    // So A lane group ga, byte i must hold the q.K^T digit byte of the channel
+    // of row 8 (ga / 2) + 2i + ga % 2; every other A byte is 0.  ktab (16 bytes
+    // in the row padding of the first key tile) maps A byte 4 ga + i to that
+    // channel's byte position in an A-tile row.
+    uint8_t* const ktab = &L.op.ak[0][0][128];
+    auto chan_pos = [](int c) -> uint32_t {
+      return a_offset(c >> 3) + 8 * (c & 1) + ((c & 7) >> 1);
+    };
+    const uint32_t kpos0 = chan_pos(lane), kpos1 = chan_pos(64 + lane);
+    auto ktab_slot = [](uint32_t j) -> uint32_t {
+      return 8 * (j >> 3) + 4 * (j & 1) + ((j & 7) >> 1);
+    };
+
     // copy group j's operands out of ring slot s (then the slot is free)
     auto read_slot = [&](int s, Operands& f) {
       const uint8_t* sp = &sh.ring[s][0];
@@ -624,6 +660,15 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
                                                          (64 * hb + 4 * n) * 4);
       f.vs = *reinterpret_cast<const u32x4*>(sp + kSlotVs + 16 * n);
       f.vmn = *reinterpret_cast<const u32x4*>(sp + kSlotVm + 16 * n);
+      if constexpr (KITTY) {
+        // rows 8 (r % 2) .. 8 (r % 2) + 7 of token 16t + n
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          f.hw[t] = *reinterpret_cast<const uint16_t*>(sp + kSlotHi + 4 * (16 * t + n) + 2 * (r & 1));
+        const uint32_t j0 = sp[kSlotBidx + lane], j1 = sp[kSlotBidx + 64 + lane];
+        if (j0 < 16) ktab[ktab_slot(j0)] = (uint8_t)kpos0;
+        if (j1 < 16) ktab[ktab_slot(j1)] = (uint8_t)kpos1;
+      }
     };
 
     // key A operand of the group and its q.K^T matrix products
@@ -653,6 +698,28 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
 #pragma unroll
         for (int H = 0; H < NH; ++H)
           cq[H][t] = mfma_f8f4(aq[H], bk, f32x4{0.f, 0.f, 0.f, 0.f}, sa_digit);
+      }
+      if constexpr (KITTY) {
+        // high bits: the codes are lo + 4 hi, so q.k gains 4 sum_j a_j hi_j
+        // over the boosted rows j (block scale x4 on the digit rows)
+        const uint32_t pw = *reinterpret_cast<const uint32_t*>(ktab + 4 * (lane >> 4));
+        const uint32_t p0 = pw & 0xFFu, p1 = (pw >> 8) & 0xFFu, p2 = (pw >> 16) & 0xFFu,
+                       p3 = pw >> 24;
+        v8i ah[NH];
+#pragma unroll
+        for (int H = 0; H < NH; ++H) {
+          const uint8_t* row = &L.op.ak[H][lane & 15][0];
+          const uint32_t dw = (uint32_t)row[p0] | ((uint32_t)row[p1] << 8) |
+                              ((uint32_t)row[p2] << 16) | ((uint32_t)row[p3] << 24);
+          ah[H] = v8i{(int)dw, 0, 0, 0, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const v8i bh = v8i{(int)(pf.hw[t] & kNib), 0, (int)((pf.hw[t] >> 2) & kNib), 0,
+                             0, 0, 0, 0};
+#pragma unroll
+          for (int H = 0; H < NH; ++H) cq[H][t] = mfma_f8f4(ah[H], bh, cq[H][t], sa_digit + 2);
+        }
       }
     };
 
@@ -834,8 +901,13 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
 
 hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
-  if (a.gqa == 4) decode_f8f4_kernel<4><<<grid, kThreadsF, 0, st>>>(a);
-  else decode_f8f4_kernel<8><<<grid, kThreadsF, 0, st>>>(a);
+  if (a.n_boost > 0) {
+    if (a.gqa == 4) decode_f8f4_kernel<4, true><<<grid, kThreadsF, 0, st>>>(a);
+    else decode_f8f4_kernel<8, true><<<grid, kThreadsF, 0, st>>>(a);
+  } else {
+    if (a.gqa == 4) decode_f8f4_kernel<4, false><<<grid, kThreadsF, 0, st>>>(a);
+    else decode_f8f4_kernel<8, false><<<grid, kThreadsF, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

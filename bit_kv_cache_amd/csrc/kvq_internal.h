@@ -84,10 +84,12 @@ struct DecodeArgs {
   float* out;              // [B][H_q][D]
 };
 
-// The matrix-core decode kernel serves GQA groups of 4 or 8 heads with G = 128
-// and plain (non-boosted) codes; everything else takes the vector-ALU kernel.
+// The matrix-core decode kernels serve GQA groups of 4 or 8 heads with
+// G = 128: 2-bit codes plain or with the 16-channel Kitty boost, 4-bit codes
+// plain; everything else takes the vector-ALU kernel.
 inline bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
-  return group == 128 && (gqa == 4 || gqa == 8) && n_boost == 0 && (bits == 2 || bits == 4);
+  return group == 128 && (gqa == 4 || gqa == 8) &&
+         ((bits == 2 && (n_boost == 0 || n_boost == 16)) || (bits == 4 && n_boost == 0));
 }
 // Resident blocks per CU of the matrix-core kernels: two waves per SIMD,
 // as one block of 8 waves (2-bit, fp8 x fp4 kernel) or two of 4 (4-bit).

@@ -30,6 +30,7 @@ CASES = {
     "g64_gqa2": (synth.shrink(W["llama3_8b_t32k_2bit"], H_q=16, G=64, T=23 * 64, B=1), {}),
     "g32_4bit_gqa8": (synth.shrink(W["llama3_8b_t8k_b32_4bit"], H_q=64, G=32, T=40 * 32, B=1,
                                    R=32, S=5), {}),
+    "kitty_gqa4": (synth.shrink(W["kitty_t128k_h64_boost16"], H_q=32, B=1, T=7 * 128, S=5), {}),
     "kitty_boost32": (synth.shrink(W["kitty_t128k_h64_boost16"], n_boost=32, H_q=32, G=64,
                                    T=6 * 64, R=64), {}),
     "gqa8_2bit": (synth.shrink(W["llama3_8b_t32k_2bit"], H_q=64, B=1, T=13 * 128, S=7), {}),
