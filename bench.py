@@ -79,10 +79,14 @@ COPY_KERNEL = "bitwise_not"       # the calibration pass: dst = ~src over 1 GiB 
 
 def split_kernel(w) -> str:
     """Name of the split-K kernel the library launches for this workload (the
-    dispatch rule of the library: matrix cores for GQA 4/8, G 128, no boost;
-    fp8 x fp4 for 2-bit codes, fp16 for 4-bit)."""
-    if w.G == 128 and w.gqa in (4, 8) and w.n_boost == 0:
-        return "decode_f8f4_kernel" if w.bits == 2 else "decode_mfma_kernel"
+    dispatch rule of the library: matrix cores for GQA 4/8 and G 128, fp8 x fp4
+    for 2-bit codes, plain or with the 16-channel Kitty boost, fp16 for plain
+    4-bit codes; the vector-ALU kernel otherwise)."""
+    if w.G == 128 and w.gqa in (4, 8):
+        if w.bits == 2 and w.n_boost in (0, 16):
+            return "decode_f8f4_kernel"
+        if w.bits == 4 and w.n_boost == 0:
+            return "decode_mfma_kernel"
     return "decode_valu_kernel"
 
 

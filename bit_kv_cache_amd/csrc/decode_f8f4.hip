@@ -33,11 +33,22 @@
 // small LDS transpose to the lanes that prepare the p.V operand.
 // Matrix-core outputs land in lane (n, r) as the four digit rows of head r.
 //
-// Work split: block = 4 waves on one (batch, kv head) and one chunk of groups
-// plus an equal slice of the fp16 sink/residual window; each wave owns whole
-// groups (round robin) with its own online softmax and software-pipelined
-// loads; the window slice runs as 16-token fp16 tiles at the end; the waves
-// merge in LDS and the block writes its partial (m, l, acc).
+// Kitty boost (Kitty page, 3.2 and 4.2): a boosted key channel's code is
+// lo + 4 hi; the dense words carry lo, so the high bits add 4 sum_j a_j hi_j
+// over the 16 boosted rows, one more scaled product per 16-token tile whose
+// B operand is the token's high-bits word and whose A operand gathers the
+// boosted channels' digit bytes.
+//
+// Work split: block = 8 waves on one (batch, kv head) and one chunk of
+// groups, one block per CU.  Wave 7 is the loader: it copies each group's
+// record (key words, value words, scales and mins, Kitty high bits and
+// boosted rows) straight from HBM into an LDS ring with asynchronous
+// global-to-LDS loads, several groups in flight, and publishes a slot once
+// its data has landed.  Waves 0..6 consume: each claims the next group with
+// an LDS counter, copies the operands out of the slot (freeing it) and runs
+// both products with its own online softmax.  The block's equal slice of
+// the fp16 sink/residual window runs first, as 16-token fp16 tiles.  The
+// waves merge in LDS and the block writes its partial (m, l, acc).
 
 #include "kvq_internal.h"
 
