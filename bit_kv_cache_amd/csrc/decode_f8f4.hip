@@ -63,10 +63,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kG = 128;          // tokens per group
-constexpr int kWaves = 8;        // one block per CU (two waves per SIMD): 7 consumers, 1 loader
-constexpr int kConsumers = kWaves - 1;
-constexpr int kLoader = kWaves - 1;
-constexpr int kThreadsF = 64 * kWaves;
+// One block per CU: 8 waves (two per SIMD), the last the loader, the
+// others consumers.
+template <int GQA, bool KITTY>
+constexpr int block_waves() { return 8; }
 constexpr int kWpt = kD / 16;     // 2-bit key words per token (8)
 constexpr uint32_t kNib = 0x33333333u;
 constexpr float kNegInfF = -__builtin_inff();
@@ -203,18 +203,18 @@ struct WaveLdsF {
       ATile ak[NH];                               // q.K^T A operand [half][row][g*32 + byte]
       ATile av[NH];                               // p.V A operand
     } op;
-    uint32_t vt[kD][12];                          // fp16 window tile, [channel][token pair]
-                                                  // (rows padded to 48 bytes)
+    uint32_t vt[kD][10];                          // fp16 window tile, [channel][token pair]
+                                                  // (rows padded to 40 bytes)
   };
   float p[GQA][16];                               // window-tile probabilities
   float pt[GQA][kG + 4];                          // group probabilities [head][token]
                                                   // (rows padded: 4 heads, 4 banks apart)
 };
 
-template <int GQA>
+template <int GQA, int NW>
 struct MergeLdsF {
-  float num[kWaves][GQA][kD];
-  float m[kWaves][GQA], l[kWaves][GQA];
+  float num[NW][GQA][kD];
+  float m[NW][GQA], l[NW][GQA];
 };
 
 // Ring of group records filled by the loader wave: slot layout (bytes)
@@ -231,23 +231,28 @@ template <bool KITTY>
 constexpr int slot_bytes() { return KITTY ? 10240 : 9216; }
 template <bool KITTY>
 constexpr int dma_per_group() { return KITTY ? 10 : 9; }
-template <int GQA>
-constexpr int ring_slots() { return GQA == 4 ? 8 : 6; }
-// groups the loader keeps in flight (at most ring_slots; the vector-memory
-// counter holds at most 63 copies)
-template <int GQA>
-constexpr int in_flight() { return ring_slots<GQA>() - 1; }
-static_assert(10 * (ring_slots<4>() - 2) < 64 && 10 * (ring_slots<8>() - 2) < 64, "vmcnt range");
+template <int GQA, bool KITTY>
+constexpr int ring_slots() { return GQA == 4 ? (KITTY ? 10 : 12) : 6; }
+// groups the loader keeps in flight: fewer than ring_slots, and (DF - 1)
+// groups of copies (plus each group's flag copy) within the vector-memory
+// counter's 63
+template <int GQA, bool KITTY>
+constexpr int in_flight() {
+  return ring_slots<GQA, KITTY>() - 1 < 63 / (dma_per_group<KITTY>() + 1) + 1
+             ? ring_slots<GQA, KITTY>() - 1
+             : 63 / (dma_per_group<KITTY>() + 1) + 1;
+}
 
 template <int GQA, bool KITTY>
 struct LdsF {
-  static constexpr int R = ring_slots<GQA>();
+  static constexpr int R = ring_slots<GQA, KITTY>();
+  static constexpr int NW = block_waves<GQA, KITTY>();
   union {
-    WaveLdsF<GQA> w[kConsumers];
-    MergeLdsF<GQA> merge;
+    WaveLdsF<GQA> w[NW - 1];
+    MergeLdsF<GQA, NW> merge;
   } u;
   alignas(16) uint8_t ring[R][slot_bytes<KITTY>()];
-  int ready[R];     // the chunk-relative group a slot holds once its data has arrived
+  int ready[R];     // chunk-relative group (mod kSeqLen) a slot holds once its data has arrived
   int empty[R];     // the group a slot may receive next (its previous one was copied out)
   int next_group;   // next group a consumer claims
   int stalled;      // a wait ran past its spin limit
@@ -271,6 +276,25 @@ __device__ __forceinline__ void dma_1k(uint32_t lds, const void* gptr) {
                "s"(lds)
                : "memory");
 }
+
+// One 4-byte copy from global memory into LDS byte address lds (issued by
+// one lane): the ready flag of a ring slot.
+__device__ __forceinline__ void dma_flag(uint32_t lds, const void* gptr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
+               "s"(lds)
+               : "memory");
+}
+
+// Sequence table 0, 1, ..., kSeqLen - 1 in global memory: the values the
+// ring's ready flags are copied from.
+constexpr int kSeqLen = 4096;
+struct SeqTable {
+  int v[kSeqLen];
+  constexpr SeqTable() : v() {
+    for (int i = 0; i < kSeqLen; ++i) v[i] = i;
+  }
+};
+__device__ constexpr SeqTable kSeq{};
 
 // Wait until at most N of this wave's vector-memory loads are in flight
 // (they complete in issue order).
@@ -345,10 +369,15 @@ __device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
 // ------------------------------------------------------------------ kernel
 
 template <int GQA, bool KITTY>
-__global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8f4_kernel(DecodeArgs a) {
   constexpr int NH = GQA / 4;    // heads per lane (r and r + 4)
-  constexpr int R = ring_slots<GQA>();
-  constexpr int DF = in_flight<GQA>();
+  constexpr int R = ring_slots<GQA, KITTY>();
+  constexpr int DF = in_flight<GQA, KITTY>();
+  constexpr int kWaves = block_waves<GQA, KITTY>();
+  constexpr int kConsumers = kWaves - 1, kLoader = kWaves - 1;
+  constexpr int kThreadsF = 64 * kWaves;
+  static_assert((dma_per_group<KITTY>() + 1) * (DF - 1) < 64, "vmcnt range");
+  static_assert(R < kSeqLen, "ready tags must not repeat within the ring");
   constexpr int SB = slot_bytes<KITTY>();
   constexpr int NDMA = dma_per_group<KITTY>();
   __shared__ LdsF<GQA, KITTY> sh;
@@ -427,6 +456,16 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
     // LDS byte address of the ring (address-space cast of the generic pointer)
     const uint32_t ring0 =
         (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)(&sh.ring[0][0]));
+    // Group j goes to slot j % R with at most DF groups in flight.  Its
+    // last copy is a 4-byte one from the sequence table into ready[j % R]:
+    // copies land in issue order, so the slot shows j (mod kSeqLen) only
+    // once the whole group is in LDS, with no publishing step in between.
+    const uint32_t ready0 =
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) int*)(&sh.ready[0]));
+    // Blocks walk their chunks from different starting groups so that the
+    // blocks streaming at the same time do not all sit at the same offsets
+    // of their heads (and on the same memory channels).
+    const int rot = ngc > 0 ? (int)((head32 * 37 + chunk * 17) % ngc) : 0;
     bool ok = true;
     for (int j = 0; j < ngc; ++j) {
       const int s = j % R;
@@ -436,25 +475,19 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
       }
       asm volatile("" ::: "memory");
       const uint32_t sl = __builtin_amdgcn_readfirstlane(ring0 + s * SB);
-      const int64_t jo = j;
+      const int64_t jo = j + rot < ngc ? j + rot : j + rot - ngc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_1k(sl + 1024 * i, kp + jo * 4096 + 1024 * i);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_1k(sl + kSlotV + 1024 * i, vp + jo * 4096 + 1024 * i);
       dma_1k(sl + kSlotKs, mp + jo * 256);
       if constexpr (KITTY) dma_1k(sl + kSlotHi, xp + jo * xstep);
-      if (j >= DF - 1) {
-        vm_wait<NDMA * (DF - 1)>();     // group j - DF + 1 has landed
-        if (lane == 0) lds_store(&sh.ready[(j - DF + 1) % R], j - DF + 1);
-      }
+      if (lane == 0)
+        dma_flag(__builtin_amdgcn_readfirstlane(ready0 + 4 * s), kSeq.v + (j & (kSeqLen - 1)));
+      if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
     }
     vm_wait<0>();
-    if (ok) {
-      for (int j = max(0, ngc - DF + 1); j < ngc; ++j)
-        if (lane == 0) lds_store(&sh.ready[j % R], j);
-    } else if (lane == 0) {
-      lds_store(&sh.stalled, 1);
-    }
+    if (!ok && lane == 0) lds_store(&sh.stalled, 1);
   } else {
     // ---------------------------------------------------------- consumer waves
     // query, then this wave's first fp16 window tile (requested first, so
@@ -614,8 +647,12 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
 #pragma unroll
           for (int blk = 0; blk < 8; ++blk) {
             const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
-            const u32x4 bv = kq < 2 ? *reinterpret_cast<const u32x4*>(&L.vt[d][4 * kq])
-                                    : u32x4{0u, 0u, 0u, 0u};
+            u32x4 bv = u32x4{0u, 0u, 0u, 0u};
+            if (kq < 2) {   // rows are 8-byte aligned: two 8-byte reads
+              const u32x2 b0 = *reinterpret_cast<const u32x2*>(&L.vt[d][4 * kq]);
+              const u32x2 b1 = *reinterpret_cast<const u32x2*>(&L.vt[d][4 * kq + 2]);
+              bv = u32x4{b0[0], b0[1], b1[0], b1[1]};
+            }
             wacc[H][blk] = mfma_f16(apw, bv, wacc[H][blk]);
           }
         }
@@ -835,7 +872,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
       const int j = __builtin_amdgcn_readlane(jl, 0);
       if (j >= ngc) break;
       const int s = j % R;
-      if (!spin_until(&sh.ready[s], j)) {
+      if (!spin_until(&sh.ready[s], j & (kSeqLen - 1))) {
         if (lane == 0) lds_store(&sh.stalled, 1);
         break;
       }
@@ -867,7 +904,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
 #pragma unroll
   for (int H = 0; H < NH; ++H) lsum[H] = row_sum16(l_part[H]);
   __syncthreads();   // the per-wave buffers are reused for the merge below
-  MergeLdsF<GQA>& M = sh.u.merge;
+  MergeLdsF<GQA, kWaves>& M = sh.u.merge;
 #pragma unroll
   for (int H = 0; H < NH; ++H) {
     const int h = r + 4 * H;
@@ -913,11 +950,11 @@ __global__ __launch_bounds__(kThreadsF, 1) void decode_f8f4_kernel(DecodeArgs a)
 hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
   if (a.n_boost > 0) {
-    if (a.gqa == 4) decode_f8f4_kernel<4, true><<<grid, kThreadsF, 0, st>>>(a);
-    else decode_f8f4_kernel<8, true><<<grid, kThreadsF, 0, st>>>(a);
+    if (a.gqa == 4) decode_f8f4_kernel<4, true><<<grid, 64 * block_waves<4, true>(), 0, st>>>(a);
+    else decode_f8f4_kernel<8, true><<<grid, 64 * block_waves<8, true>(), 0, st>>>(a);
   } else {
-    if (a.gqa == 4) decode_f8f4_kernel<4, false><<<grid, kThreadsF, 0, st>>>(a);
-    else decode_f8f4_kernel<8, false><<<grid, kThreadsF, 0, st>>>(a);
+    if (a.gqa == 4) decode_f8f4_kernel<4, false><<<grid, 64 * block_waves<4, false>(), 0, st>>>(a);
+    else decode_f8f4_kernel<8, false><<<grid, 64 * block_waves<8, false>(), 0, st>>>(a);
   }
   return hipGetLastError();
 }
