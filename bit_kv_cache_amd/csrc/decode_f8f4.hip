@@ -374,7 +374,8 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   constexpr int R = ring_slots<GQA, KITTY>();
   constexpr int DF = in_flight<GQA, KITTY>();
   constexpr int kWaves = block_waves<GQA, KITTY>();
-  constexpr int kConsumers = kWaves - 1, kLoader = kWaves - 1;
+  // wave 0 is the loader (the first wave of a block to start), 1.. consume
+  constexpr int kConsumers = kWaves - 1, kLoader = 0;
   constexpr int kThreadsF = 64 * kWaves;
   static_assert((dma_per_group<KITTY>() + 1) * (DF - 1) < 64, "vmcnt range");
   static_assert(R < kSeqLen, "ready tags must not repeat within the ring");
@@ -389,7 +390,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
                "s"(a.c.v_scale), "s"(a.c.v_min), "s"(a.c.t_cap), "s"(a.groups_per_chunk),
                "s"(a.n_groups), "s"(a.H_kv), "s"(a.H_q), "s"(a.q), "s"(a.qscale), "s"(a.n_sink), "s"(a.n_res), "s"(a.k_sink),
                "s"(a.v_sink), "s"(a.k_res), "s"(a.v_res), "s"(a.sink_cap), "s"(a.res_cap),
-               "s"(a.n_chunks));
+               "s"(a.n_chunks), "s"(a.ws), "s"(a.n_parts));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -403,15 +404,9 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
   const int ngc = (int)max<int64_t>(0, min<int64_t>(a.n_groups, gb + a.groups_per_chunk) - gb);
 
-  if (tid < R) {
-    sh.ready[tid] = -1;
-    sh.empty[tid] = tid;
-  }
-  if (tid == 0) {
-    sh.next_group = 0;
-    sh.stalled = 0;
-  }
-  __syncthreads();
+  // The loader wave sets up the ring's flags, starts its first copies and
+  // only then meets the other waves at the block barrier; consumers run
+  // their fp16 window tiles before it.  Each wave passes it exactly once.
 
   // per-wave online-softmax state (the loader's stays empty)
   float m_run[NH], l_part[NH], mterm[NH];
@@ -432,6 +427,16 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
 
   if (wave == kLoader) {
     // ---------------------------------------------------------- loader wave
+    if (tid < R) {
+      sh.ready[tid] = -1;
+      sh.empty[tid] = tid;
+    }
+    if (tid == 0) {
+      sh.next_group = 0;
+      sh.stalled = 0;
+    }
+    // the flags are written before any copy can land on them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // Copies the chunk's groups, in order, into the ring (group j -> slot
     // j % R) with DF groups in flight, and publishes each one once its data
     // is in LDS.  A slot is refilled only after a consumer copied its
@@ -466,9 +471,13 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     // blocks streaming at the same time do not all sit at the same offsets
     // of their heads (and on the same memory channels).
     const int rot = ngc > 0 ? (int)((head32 * 37 + chunk * 17) % ngc) : 0;
-    bool ok = true;
+    bool ok = true, met = false;
     for (int j = 0; j < ngc; ++j) {
       const int s = j % R;
+      if (j == DF - 1) {   // the first DF - 1 groups are on their way
+        __syncthreads();
+        met = true;
+      }
       if (!spin_until(&sh.empty[s], j)) {
         ok = false;
         break;
@@ -486,6 +495,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
         dma_flag(__builtin_amdgcn_readfirstlane(ready0 + 4 * s), kSeq.v + (j & (kSeqLen - 1)));
       if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
     }
+    if (!met) __syncthreads();
     vm_wait<0>();
     if (!ok && lane == 0) lds_store(&sh.stalled, 1);
   } else {
@@ -503,7 +513,8 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     const int wpc = n_win > 0 ? (n_win + a.n_chunks - 1) / a.n_chunks : 0;
     const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
     const int kq = lane >> 4, m_row = lane & 15;
-    const int u_first = u0 + 16 * wave;
+    const int cw = wave - 1;   // consumer index
+    const int u_first = u0 + 16 * cw;
     auto win_row = [&](const uint16_t* sink, const uint16_t* res, int u) -> const uint16_t* {
       return u < a.n_sink ? sink + (head * a.sink_cap + u) * kD
                           : res + (head * a.res_cap + (u - a.n_sink)) * kD;
@@ -568,7 +579,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     }
     const float q_unscale = exp2i(e_q - 8);
 
-    WaveLdsF<GQA>& L = sh.u.w[wave];
+    WaveLdsF<GQA>& L = sh.u.w[cw];
 
     // ------------------------------------------------------ fp16 window
     // q.K^T on fp16 matrix cores (raw keys as B), the online softmax, p.V
@@ -864,6 +875,8 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       }
     };
 
+    __syncthreads();   // the loader has set up the ring's flags
+
     // Consumers claim the chunk's groups in order from a block counter and
     // take each from the ring as soon as the loader has published it.
     for (;;) {
@@ -923,18 +936,25 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   const bool stalled = lds_load(&sh.stalled) != 0;
   for (int i = tid; i < GQA * kD; i += kThreadsF) {
     const int h = i / kD, d = i % kD;
+    // every wave's record read up front; empty ones (l = 0) are skipped by
+    // selects, not branches, so the reads overlap
+    float mw[kWaves], lw[kWaves], nw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = M.m[w][h];
+      lw[w] = M.l[w][h];
+      nw[w] = M.num[w][h][d];
+    }
     float mm = kNegInfF;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (M.l[w][h] > 0.f) mm = fmaxf(mm, M.m[w][h]);
+    for (int w = 0; w < kWaves; ++w) mm = lw[w] > 0.f ? fmaxf(mm, mw[w]) : mm;
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (M.l[w][h] > 0.f) {
-        const float f = fexp2(M.m[w][h] - mm);
-        num = fmaf(M.num[w][h][d], f, num);
-        den = fmaf(M.l[w][h], f, den);
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fexp2(mw[w] - mm);
+      num = lw[w] > 0.f ? fmaf(nw[w], f, num) : num;
+      den = lw[w] > 0.f ? fmaf(lw[w], f, den) : den;
+    }
     if (stalled) num = den = __builtin_nanf("");   // a wait ran out: poison the result
     float* wp = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + chunk) * (kD + 2);
     wp[2 + d] = num;

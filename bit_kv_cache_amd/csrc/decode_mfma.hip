@@ -692,18 +692,25 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
   const int n_parts = a.n_parts;
   for (int i = tid; i < GQA * kD; i += kThreadsM) {
     const int h = i / kD, d = i % kD;
+    // every wave's record read up front; empty ones (l = 0) are skipped by
+    // selects, not branches, so the reads overlap
+    float mw[kWaves], lw[kWaves], nw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = M.m[w][h];
+      lw[w] = M.l[w][h];
+      nw[w] = M.num[w][h][d];
+    }
     float mm = kNegInfM;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (M.l[w][h] > 0.f) mm = fmaxf(mm, M.m[w][h]);
+    for (int w = 0; w < kWaves; ++w) mm = lw[w] > 0.f ? fmaxf(mm, mw[w]) : mm;
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (M.l[w][h] > 0.f) {
-        const float f = exp2f(M.m[w][h] - mm);
-        num = fmaf(M.num[w][h][d], f, num);
-        den = fmaf(M.l[w][h], f, den);
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = exp2f(mw[w] - mm);
+      num = lw[w] > 0.f ? fmaf(nw[w], f, num) : num;
+      den = lw[w] > 0.f ? fmaf(lw[w], f, den) : den;
+    }
     float* wp = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + chunk) * (kD + 2);
     wp[2 + d] = num;
     if (d == 0) {
