@@ -1,10 +1,11 @@
 """Decode-step benchmark of the low-bit KV cache on one MI355X.
 
 A step is one pass of the whole hot path over one batch: one decode-attention
-step over the packed cache + fp16 windows (split-K kernel + log-sum-exp
-merge), then the append-group quantize+pack of the full fp16 residual group
-(the cache's streaming update).  Inputs are seeded synthetic tensors already
-resident in HBM.  To measure HBM rather than the 256 MB Infinity Cache, the
+step over the packed cache + fp16 windows (split-K, log-sum-exp merge) and
+the append-group quantize+pack of the full fp16 residual group (the cache's
+streaming update), as one kvq_decode_step call.  For plain 2-bit codes with
+4..8 chunks per head the library runs that step as a single kernel launch.
+Inputs are seeded synthetic tensors already resident in HBM.  To measure HBM rather than the 256 MB Infinity Cache, the
 steps rotate over several independent copies of the packed cache (total well
 above the cache size).
 
@@ -88,6 +89,24 @@ def split_kernel(w) -> str:
         if w.bits == 4 and w.n_boost == 0:
             return "decode_mfma_kernel"
     return "decode_valu_kernel"
+
+
+def fused_step(w, n_chunks: int) -> bool:
+    """Whether the library runs a step with append as one launch (its dispatch
+    rule: the 2-bit matrix-core kernel, plain codes, 4..8 chunks per head)."""
+    return split_kernel(w) == "decode_f8f4_kernel" and w.n_boost == 0 and 4 <= n_chunks <= 8
+
+
+def launches_per_step(w, n_chunks: int, append: bool) -> int:
+    """Kernel launches of one kvq_decode_step call (the library's dispatch)."""
+    mfma = split_kernel(w) != "decode_valu_kernel"
+    n_parts = n_chunks if mfma else n_chunks + 1
+    in_launch_merge = split_kernel(w) == "decode_f8f4_kernel" and n_parts <= 8
+    if append:
+        if fused_step(w, n_chunks):
+            return 1
+        return 2 if n_parts <= 32 else 3
+    return 1 if in_launch_merge else 2
 
 
 def kernel_source_hash() -> str:
@@ -249,7 +268,8 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first (about 20 ms: the clocks reach their steady state)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0 = auto)")
     ap.add_argument("--n-chunks", type=int, default=0)
@@ -258,6 +278,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the run, stream 1 GiB in and 1 GiB out 5 times (counter scale)")
+    ap.add_argument("--profile-step", action="store_true",
+                    help="launch only the warm-up and timed steps (counter runs), then exit")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "CMD"),
                     help="write the profiles/ traffic file from two counter runs and exit")
     args = ap.parse_args(argv)
@@ -302,7 +324,7 @@ def main(argv=None):
     q = synth.query(w, "cuda")
     n_chunks, ws_bytes = kvq.kvq_decode_plan(cfg, w.B, w.H_q, w.H_kv, w.T,
                                              args.n_chunks or w.min_chunks)
-    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    ws = kvq.decode_workspace(ws_bytes)
     out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -370,6 +392,12 @@ def main(argv=None):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
+    if args.profile_step:
+        print(json.dumps({"profile_step": w.name, "steps": args.steps,
+                          "ms_per_step": round(ms_per_step, 5)}), flush=True)
+        if args.calib_copy:
+            calib_copy(torch)
+        return 0
 
     # the same step as three launches (decode partials, merge, quantize), for context
     torch.cuda.synchronize()
@@ -402,7 +430,6 @@ def main(argv=None):
     part_iso, part_ms = stats(0, 1)
     merge_iso, _ = stats(1, 2)
     dec_avg, dec_ms = stats(0, 2)
-    app_iso, _ = stats(2, 3)
 
     # average launch duration of each kernel alone, back to back on the
     # stream (one event pair around n_k launches: no event between launches)
@@ -416,15 +443,35 @@ def main(argv=None):
         torch.cuda.synchronize()
         return b0.elapsed_time(b1) / n_k
 
+    def attention(i):
+        st = lib.kvq_decode_step(ctypes.byref(c_cfg), ctypes.byref(c_caches[i % n_copies]),
+                                 w.B, w.H_q, w.H_kv, q.data_ptr(), w.T, sink_p, res_p,
+                                 ctypes.c_float(0.0), n_chunks, ws.data_ptr(), ws_bytes,
+                                 out.data_ptr(), 0, sp)
+        if st:
+            raise kvq.KvqError(st, "kvq_decode_step")
+
+    step_avg = back_to_back(step)
+    attn_avg = back_to_back(attention)
     part_avg = back_to_back(partials)
     merge_avg = back_to_back(lambda i: merge())
     app_avg = back_to_back(quant) if append else 0.0
 
     alg = decode_bytes(w)
-    alg_split = alg - w.B * w.H_q * w.D * 4   # the split-K kernel does not write O
-    achieved = alg_split / (part_avg * 1e-3) / 1e9
+    alg_split = alg - w.B * w.H_q * w.D * 4   # the split-K phase does not write O
     step_bytes = alg + (append_bytes(w) if append else 0)
     eff_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    one_launch = append and fused_step(w, n_chunks)
+    split_gbps = alg_split / (part_avg * 1e-3) / 1e9
+    if one_launch:
+        # the step is one launch of the split-K kernel that also quantizes the
+        # appended group and merges: its bytes are the whole step's
+        dom_kernel = f"{split_kernel(w)} (whole step in one launch: split-K, append, merge)"
+        dom_bytes, dom_avg = step_bytes, step_avg
+    else:
+        dom_kernel = f"{split_kernel(w)} (split-K phase, kvq_decode_partials)"
+        dom_bytes, dom_avg = alg_split, part_avg
+    achieved = dom_bytes / (dom_avg * 1e-3) / 1e9
 
     result = {
         "metric": "decode-attn us/step + effective HBM GB/s (% of peak), 2-bit, Llama-3-8B "
@@ -444,26 +491,35 @@ def main(argv=None):
                    "T": w.T, "R": w.R, "S": w.S, "bits": w.bits, "G": w.G,
                    "n_boost": w.n_boost, "n_chunks": n_chunks, "cache_copies": n_copies,
                    "cache_bytes_per_copy": cache_bytes_one, "step": "decode + append-group "
-                   "quantize (kvq_decode_step)" if append else "decode (kvq_decode_step)"},
+                   "quantize (kvq_decode_step)" if append else "decode (kvq_decode_step)",
+                   "launches_per_step": launches_per_step(w, n_chunks, append)},
         "effective_GBps": round(eff_gbps, 1),
         "effective_frac_of_peak": round(eff_gbps / HBM_PEAK_GBPS, 4),
-        "decode_us": {"avg": round(dec_avg * 1e3, 3), "p10": round(dec_ms[n_k // 10] * 1e3, 3),
-                      "p90": round(dec_ms[(9 * n_k) // 10] * 1e3, 3),
+        "step_bytes": step_bytes,
+        "decode_us": {"step_avg": round(step_avg * 1e3, 3),
+                      "step_without_append_avg": round(attn_avg * 1e3, 3),
                       "split_kernel_avg": round(part_avg * 1e3, 3),
                       "merge_kernel_avg": round(merge_avg * 1e3, 3),
+                      "split_plus_merge_isolated_avg": round(dec_avg * 1e3, 3),
+                      "split_plus_merge_p10": round(dec_ms[n_k // 10] * 1e3, 3),
+                      "split_plus_merge_p90": round(dec_ms[(9 * n_k) // 10] * 1e3, 3),
                       "split_kernel_isolated_avg": round(part_iso * 1e3, 3),
                       "merge_kernel_isolated_avg": round(merge_iso * 1e3, 3),
                       "timing": "*_avg: n launches back to back between two HIP events on the "
-                                "launch stream; *_isolated_avg: an event pair around every "
+                                "launch stream; *_isolated_*: an event pair around every "
                                 "launch"},
         "append_quant_us": round(app_avg * 1e3, 3) if append else None,
-        "step_unfused_us": round(ms_unfused * 1e3, 3),
+        "step_as_three_launches_us": round(ms_unfused * 1e3, 3),
+        "split_phase": {"kernel": f"{split_kernel(w)} (kvq_decode_partials)",
+                        "algorithmic_bytes": alg_split, "avg_us": round(part_avg * 1e3, 3),
+                        "GBps": round(split_gbps, 1),
+                        "frac": round(split_gbps / HBM_PEAK_GBPS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": read_traffic(w),
-                     "kernel": f"{split_kernel(w)} (split-K phase, kvq_decode_partials)",
-                     "algorithmic_bytes": alg_split,
-                     "kernel_avg_us": round(part_avg * 1e3, 3)},
+                     "kernel": dom_kernel,
+                     "algorithmic_bytes": dom_bytes,
+                     "kernel_avg_us": round(dom_avg * 1e3, 3)},
     }
     if not args.no_cpu_baseline:
         cores, model = _host_info()
@@ -472,13 +528,19 @@ def main(argv=None):
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
     if args.calib_copy:
-        src = torch.zeros(CALIB_COPY_BYTES // 4, dtype=torch.int32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            torch.bitwise_not(src, out=dst)
-        torch.cuda.synchronize()
+        calib_copy(torch)
     return 0
+
+
+def calib_copy(torch):
+    """1 GiB in and 1 GiB out, 5 times: the reference the traffic counters are
+    scaled by."""
+    src = torch.zeros(CALIB_COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -28,6 +28,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_ALIGN, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
+# arrival counters at the start of a decode workspace (zero between calls)
+KVQ_WS_COUNTER_BYTES = 262144
 
 EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_step",
@@ -199,6 +201,19 @@ def kvq_decode_plan(cfg: QCfg, B: int, H_q: int, H_kv: int, n_quant_tokens: int,
     _check(_lib.kvq_decode_plan(ctypes.byref(c_cfg), B, H_q, H_kv, n_quant_tokens, n_chunks,
                                 ctypes.byref(nc), ctypes.byref(ws)), "kvq_decode_plan")
     return nc.value, ws.value
+
+
+def decode_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A decode workspace of ``nbytes`` (from ``kvq_decode_plan``), allocated
+    zeroed as the counter bytes at its start require."""
+    return torch.zeros((nbytes + 3) // 4, dtype=torch.float32, device=device)
+
+
+def workspace_records(workspace: torch.Tensor, rows: int, n_parts: int, D: int = 128):
+    """The partial records ``[rows][n_parts][D+2]`` (m, l, acc) that follow the
+    counter bytes of a workspace (a view)."""
+    off = KVQ_WS_COUNTER_BYTES // 4
+    return workspace[off: off + rows * n_parts * (D + 2)].view(rows, n_parts, D + 2)
 
 
 def kvq_decode_workspace_bytes(cfg: QCfg, B: int, H_q: int, H_kv: int, n_quant_tokens: int,

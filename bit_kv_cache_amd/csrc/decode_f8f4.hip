@@ -51,6 +51,8 @@
 // waves merge in LDS and the block writes its partial (m, l, acc).
 
 #include "kvq_internal.h"
+#include "merge_common.h"
+#include "quant_common.h"
 
 namespace kvq {
 namespace {
@@ -256,6 +258,8 @@ struct LdsF {
   int empty[R];     // the group a slot may receive next (its previous one was copied out)
   int next_group;   // next group a consumer claims
   int stalled;      // a wait ran past its spin limit
+  int last;         // this block is the last of its head to finish (in-launch merge)
+  int next_item;    // next append item a consumer claims
 };
 
 struct Operands {
@@ -316,10 +320,13 @@ __device__ __forceinline__ void lds_store(T* p, T v) {
 
 // Spin (with sleeps) until *p == want; false if the spin limit ran out (the
 // caller then stops, so every wave always reaches the end of the kernel).
+// The flag is compared as a wave-uniform (scalar) value: a per-lane compare
+// would let the compiler treat the loop exit as divergent and restructure
+// the caller's loop so that lanes run different iterations.
 constexpr uint32_t kSpinLimit = 1u << 20;
 __device__ __forceinline__ bool spin_until(const int* p, int want) {
   for (uint32_t i = 0; i < kSpinLimit; ++i) {
-    if (lds_load(p) == want) return true;
+    if (__builtin_amdgcn_readfirstlane(lds_load(p)) == want) return true;
     __builtin_amdgcn_s_sleep(1);
   }
   return false;
@@ -366,6 +373,198 @@ __device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
 }
 
 
+// ------------------------------------------------------------------ fused append
+//
+// With DecodeArgs::append the block also quantizes its share of the group
+// that has filled the residual window (rows 0..127 of the head's residual
+// buffer) into cache group n_groups: slice s = chunk of four (key channels
+// [32 s, 32 s + 32), value tokens [32 s, 32 s + 32)), with the arithmetic of
+// the quantize kernel (KIVI page, Steps 1-2): min and max by the total order
+// -0 < +0, scale fp16((max - min)/3), codes by quant_code_rcp.  The slice is
+// four self-contained items (16 key channels, or 16 value tokens, each with
+// its own statistics and whole packed words) that the first consumer waves
+// past the block barrier claim, while the first groups are still on their
+// way.  The appended group lies past
+// every group the launch reads.
+constexpr int kAppWpt = kD / 16;   // 2-bit key words per token
+constexpr int kAppItems = 4;       // items per slice
+
+// min / max (as order keys) of the fp16 value e of a u32x4 of 8 halves
+__device__ __forceinline__ uint32_t half_key(const u32x4& v, int e) {
+  return order_key((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+}
+__device__ __forceinline__ uint16_t half_of(const u32x4& v, int e) {
+  return (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+}
+
+// Item k of slice s.  k < 2: key channels c0 = 32 s + 16 k .. c0 + 15 over
+// the 128 tokens, one packed word per token (lane: tokens lane / 2 + 32 i,
+// channels c0 + 8 (lane % 2) ..); k >= 2: value tokens t0 = 32 s + 16 (k - 2)
+// .. t0 + 15 over the 128 channels, one packed word per channel (lane: tokens
+// t0 + lane / 16 + 4 i, channels 8 (lane % 16) ..).
+__device__ __forceinline__ void append_item_load(const DecodeArgs& a, int64_t head, int s, int k,
+                                                 int lane, u32x4 (&x)[4]) {
+  if (k < 2) {
+    const uint16_t* src = a.k_res + head * a.res_cap * kD + 32 * s + 16 * k + 8 * (lane & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] = *reinterpret_cast<const u32x4*>(src + ((lane >> 1) + 32 * i) * kD);
+  } else {
+    const uint16_t* src =
+        a.v_res + (head * a.res_cap + 32 * s + 16 * (k - 2) + (lane >> 4)) * kD + 8 * (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const u32x4*>(src + 4 * i * kD);
+  }
+}
+
+__device__ __forceinline__ void append_item(const DecodeArgs& a, int64_t head, int s, int k,
+                                            int lane, const u32x4 (&x)[4]) {
+  const int64_t g = a.n_groups;
+  if (k < 2) {
+    const int c0 = 32 * s + 16 * k, q = lane & 1;
+    // per channel over the 128 tokens: the lane's 4, then the 32 lanes with
+    // the same q
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = half_key(x[0], e);
+      hi[e] = lo[e];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        lo[e] = min(lo[e], half_key(x[i], e));
+        hi[e] = max(hi[e], half_key(x[i], e));
+      }
+    }
+#pragma unroll
+    for (int o = 2; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] = min(lo[e], (uint32_t)__shfl_xor((int)lo[e], o));
+        hi[e] = max(hi[e], (uint32_t)__shfl_xor((int)hi[e], o));
+      }
+    float mn[8], sc[8], rs[8];
+    uint32_t shw[4], mnw[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t l16 = from_order_key(lo[e]);
+      const uint16_t sh = group_scale(h2f(l16), h2f(from_order_key(hi[e])), 3.0f);
+      mn[e] = h2f(l16);
+      sc[e] = h2f(sh);
+      rs[e] = 1.0f / sc[e];
+      if (e & 1) {
+        shw[e >> 1] |= (uint32_t)sh << 16;
+        mnw[e >> 1] |= (uint32_t)l16 << 16;
+      } else {
+        shw[e >> 1] = sh;
+        mnw[e >> 1] = l16;
+      }
+    }
+    if (lane < 2) {
+      const int64_t m_off = (head * (a.c.t_cap / kG) + g) * kD + c0 + 8 * q;
+      *reinterpret_cast<u32x4*>(a.c.k_scale + m_off) = u32x4{shw[0], shw[1], shw[2], shw[3]};
+      *reinterpret_cast<u32x4*>(a.c.k_min + m_off) = u32x4{mnw[0], mnw[1], mnw[2], mnw[3]};
+    }
+    // codes: channels c0 + 8 q + e at bits 2 (8 q + e) of the token's word
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t part = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        part |= quant_code_rcp(h2f(half_of(x[i], e)), mn[e], sc[e], rs[e], 3.0f)
+                << (2 * (8 * q + e));
+      const uint32_t word = part | (uint32_t)__shfl_xor((int)part, 1);
+      if (q == 0) {
+        const int t = (lane >> 1) + 32 * i;
+        a.c.k_codes[(head * a.c.t_cap + g * kG + t) * kAppWpt + 2 * s + k] = word;
+      }
+    }
+  } else {
+    const int t0 = 32 * s + 16 * (k - 2), r = lane >> 4, q = lane & 15;
+    // per token over the 128 channels: the lane's 8, then the 16 lanes with
+    // the same r
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = half_key(x[i], 0);
+      hi[i] = lo[i];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) {
+        lo[i] = min(lo[i], half_key(x[i], e));
+        hi[i] = max(hi[i], half_key(x[i], e));
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = min(lo[i], (uint32_t)__shfl_xor((int)lo[i], o));
+        hi[i] = max(hi[i], (uint32_t)__shfl_xor((int)hi[i], o));
+      }
+    float mn[4], sc[4], rs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t l16 = from_order_key(lo[i]);
+      const uint16_t sh = group_scale(h2f(l16), h2f(from_order_key(hi[i])), 3.0f);
+      mn[i] = h2f(l16);
+      sc[i] = h2f(sh);
+      rs[i] = 1.0f / sc[i];
+      if (q == 0) {
+        const int64_t m_off = head * a.c.t_cap + g * kG + t0 + r + 4 * i;
+        a.c.v_scale[m_off] = sh;
+        a.c.v_min[m_off] = l16;
+      }
+    }
+    // codes: token t0 + r + 4 i at bits 2 (r + 4 i) of the channel's word
+    uint32_t wd[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t part = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part |= quant_code_rcp(h2f(half_of(x[i], e)), mn[i], sc[i], rs[i], 3.0f)
+                << (2 * (r + 4 * i));
+      part |= (uint32_t)__shfl_xor((int)part, 16);
+      wd[e] = part | (uint32_t)__shfl_xor((int)part, 32);
+    }
+    if (r == 0) {
+      uint32_t* dst = a.c.v_codes + (head * (a.c.t_cap / 16) + (g * kG + t0) / 16) * kD + 8 * q;
+      *reinterpret_cast<u32x4*>(dst) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      *reinterpret_cast<u32x4*>(dst + 4) = u32x4{wd[4], wd[5], wd[6], wd[7]};
+    }
+  }
+}
+
+// ------------------------------------------------------------------ in-launch merge
+
+// After a block has written its partial records (device-scope stores): its
+// arrival on the head's counter, and, in the last block of the head to
+// arrive, the log-sum-exp merge of the head's query rows into the output.
+// No block waits for another, so the order in which blocks run is free.  The
+// last block resets the counter, leaving it zero for the next call.
+template <int GQA>
+__device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int64_t b, int64_t hk,
+                                                int head32, int& last_flag) {
+  // this thread's stores have completed (they are visible device-wide)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(a.counters + head32, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == a.n_chunks - 1;
+    if (last) __hip_atomic_store(a.counters + head32, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = last;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  const int np = a.n_parts;
+  for (int i = threadIdx.x; i < GQA * kD; i += blockDim.x) {
+    const int64_t bh = b * a.H_q + hk * GQA + i / kD;
+    const int d = i % kD;
+    if (np <= 4) merge_row<4, true>(a.ws, np, a.out, bh, d);
+    else merge_row<8, true>(a.ws, np, a.out, bh, d);
+  }
+}
+
 // ------------------------------------------------------------------ kernel
 
 template <int GQA, bool KITTY>
@@ -403,6 +602,8 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
   const int ngc = (int)max<int64_t>(0, min<int64_t>(a.n_groups, gb + a.groups_per_chunk) - gb);
+  // slice of the appended group this block quantizes (-1: none)
+  const int app_slice = (!KITTY && a.append && chunk < 4) ? chunk : -1;
 
   // The loader wave sets up the ring's flags, starts its first copies and
   // only then meets the other waves at the block barrier; consumers run
@@ -434,6 +635,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     if (tid == 0) {
       sh.next_group = 0;
       sh.stalled = 0;
+      sh.next_item = 0;
     }
     // the flags are written before any copy can land on them
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -506,6 +708,9 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
 #pragma unroll
     for (int j = 0; j < NH; ++j)
       qraw[j] = *reinterpret_cast<const u32x4*>(qrow + (r + 4 * j) * kD + 8 * n);
+    // The append's items, one on each of the last kAppItems consumers: the
+    // loads go out now, the arithmetic runs after the block barrier (the
+    // other consumers take the fp16 window tiles and the first groups).
 
     // This block's slice [u0, u1) of the fp16 window (sink | residual);
     // consumer w takes 16-token tiles w, w + kConsumers, ...
@@ -876,9 +1081,24 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     };
 
     __syncthreads();   // the loader has set up the ring's flags
+    // the append's items first (the waves that get here first take them)
+    if (app_slice >= 0) {
+      for (;;) {
+        int kl = 0;
+        if (lane == 0) kl = atomicAdd(&sh.next_item, 1);
+        const int k = __builtin_amdgcn_readlane(kl, 0);
+        if (k >= kAppItems) break;
+        u32x4 app_x[4];
+        append_item_load(a, head, app_slice, k, lane, app_x);
+        append_item(a, head, app_slice, k, lane, app_x);
+      }
+    }
 
     // Consumers claim the chunk's groups in order from a block counter and
     // take each from the ring as soon as the loader has published it.
+    // Only the claim branches on the lane; every store in the loop is made
+    // by all lanes with the same value (a lane-divergent store at the end of
+    // the body lets the compiler split the wave across iterations).
     for (;;) {
       int jl = 0;
       if (lane == 0) jl = atomicAdd(&sh.next_group, 1);
@@ -886,7 +1106,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       if (j >= ngc) break;
       const int s = j % R;
       if (!spin_until(&sh.ready[s], j & (kSeqLen - 1))) {
-        if (lane == 0) lds_store(&sh.stalled, 1);
+        lds_store(&sh.stalled, 1);
         break;
       }
       asm volatile("" ::: "memory");
@@ -894,7 +1114,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       read_slot(s, pf);
       asm volatile("" ::: "memory");
       // this wave's LDS reads complete in order before its next LDS write
-      if (lane == 0) lds_store(&sh.empty[s], j + R);
+      lds_store(&sh.empty[s], j + R);
       qk_issue(pf);
       pv_step(pf);
     }
@@ -957,12 +1177,22 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     }
     if (stalled) num = den = __builtin_nanf("");   // a wait ran out: poison the result
     float* wp = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + chunk) * (kD + 2);
-    wp[2 + d] = num;
-    if (d == 0) {
-      wp[0] = mm;
-      wp[1] = den;
+    if (a.counters) {
+      // read by another block of this launch: device-scope stores
+      __hip_atomic_store(wp + 2 + d, num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        __hip_atomic_store(wp, mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(wp + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      wp[2 + d] = num;
+      if (d == 0) {
+        wp[0] = mm;
+        wp[1] = den;
+      }
     }
   }
+  if (a.counters) merge_in_launch<GQA>(a, b, hk, head32, sh.last);
 }
 
 }  // namespace

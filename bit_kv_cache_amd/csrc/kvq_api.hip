@@ -80,6 +80,11 @@ size_t partial_bytes(int64_t B, int64_t H_q, int64_t parts) {
   return align16((size_t)B * H_q * parts * (kD + 2) * sizeof(float));
 }
 
+// Workspace: arrival counters (zero between calls), then the partials.
+size_t workspace_bytes(int64_t B, int64_t H_q, int64_t parts) {
+  return kvq::kCounterBytes + partial_bytes(B, H_q, parts);
+}
+
 kvq_status check_window(const kvq_window* w) {
   if (!w) return KVQ_OK;
   if (w->n < 0 || w->cap < 0 || w->n > w->cap) return KVQ_ERR_ARG;
@@ -143,7 +148,7 @@ kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t 
   const bool mfma = kvq::mfma_decode_supported(cfg->bits, cfg->group, gqa, cfg->n_boost);
   const int32_t n = plan_chunks(mfma, cfg->bits, gqa, heads, n_quant_tokens / cfg->group, n_chunks_req);
   if (n_chunks) *n_chunks = n;
-  if (ws_bytes) *ws_bytes = partial_bytes(B, H_q, mfma ? n : n + 1);
+  if (ws_bytes) *ws_bytes = workspace_bytes(B, H_q, mfma ? n : n + 1);
   return KVQ_OK;
 }
 
@@ -204,10 +209,25 @@ kvq_status prepare_decode(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
     a->res_cap = res->cap;
   }
   a->qscale = sm_scale * 1.4426950408889634f;
-  a->ws = static_cast<float*>(workspace);
+  a->ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kvq::kCounterBytes);
   a->n_parts = kvq::mfma_decode_supported(cfg->bits, cfg->group, a->gqa, cfg->n_boost) ? nc
                                                                                      : nc + 1;
+  a->counters = nullptr;
+  a->append = 0;
   return KVQ_OK;
+}
+
+// The decode step with its merge: one launch where the kernel merges in
+// place, else the split-K launch and the merge launch.
+kvq_status decode_and_merge(const kvq_qcfg* cfg, kvq::DecodeArgs& a, void* workspace,
+                            hipStream_t s) {
+  if (kvq::fused_merge_supported(cfg->bits, cfg->group, a.gqa, cfg->n_boost, a.n_parts)) {
+    a.counters = static_cast<int32_t*>(workspace);
+    return hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s));
+  }
+  kvq_status st = hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s));
+  if (st != KVQ_OK) return st;
+  return hip_status(kvq::launch_merge(a, s));
 }
 
 }  // namespace
@@ -226,10 +246,7 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
   if (!out) return KVQ_ERR_ARG;
   if (!aligned16(out)) return KVQ_ERR_ALIGN;
   a.out = out;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s))) != KVQ_OK)
-    return st;
-  return hip_status(kvq::launch_merge(a, s));
+  return decode_and_merge(cfg, a, workspace, static_cast<hipStream_t>(stream));
 }
 
 kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,
@@ -251,9 +268,16 @@ kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t 
   }
   a.out = out;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!append) return decode_and_merge(cfg, a, workspace, s);
+  if (kvq::fused_append_supported(cfg->bits, cfg->group, a.gqa, cfg->n_boost, a.n_parts,
+                                  a.n_chunks)) {
+    // one launch: split-K, the append's quantize and the merge
+    a.counters = static_cast<int32_t*>(workspace);
+    a.append = 1;
+    return hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s));
+  }
   if ((st = hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s))) != KVQ_OK)
     return st;
-  if (!append) return hip_status(kvq::launch_merge(a, s));
   const int64_t heads = (int64_t)B * H_kv;
   const kvq::QuantArgs qa{cache_args(cache), res->k,          res->v,   (int64_t)res->cap * kD,
                           n_quant_tokens / G, 1,              (int32_t)heads, cfg->n_boost};
@@ -280,7 +304,7 @@ kvq_status kvq_decode_merge(int32_t B, int32_t H_q, int32_t n_parts, const float
                             size_t ws_bytes, float* out, void* stream) {
   if (B <= 0 || H_q <= 0 || n_parts <= 0 || n_parts > kvq::kMaxParts) return KVQ_ERR_ARG;
   if ((int64_t)B * H_q > 0x7FFFFFFF) return KVQ_ERR_ARG;
-  if (!workspace || ws_bytes < (size_t)B * H_q * n_parts * (kD + 2) * sizeof(float))
+  if (!workspace || ws_bytes < kvq::kCounterBytes + (size_t)B * H_q * n_parts * (kD + 2) * sizeof(float))
     return KVQ_ERR_WORKSPACE;
   if (!out) return KVQ_ERR_ARG;
   if (!aligned16(workspace) || !aligned16(out)) return KVQ_ERR_ALIGN;
@@ -288,7 +312,8 @@ kvq_status kvq_decode_merge(int32_t B, int32_t H_q, int32_t n_parts, const float
   a.B = B;
   a.H_q = H_q;
   a.n_parts = n_parts;
-  a.ws = const_cast<float*>(workspace);
+  a.ws = reinterpret_cast<float*>(
+      const_cast<char*>(reinterpret_cast<const char*>(workspace)) + kvq::kCounterBytes);
   a.out = out;
   return hip_status(kvq::launch_merge(a, static_cast<hipStream_t>(stream)));
 }

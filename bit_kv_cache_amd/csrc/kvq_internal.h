@@ -82,7 +82,20 @@ struct DecodeArgs {
   int32_t n_parts;         // partials per (batch, query head)
   float* ws;               // partials [B][H_q][n_parts][D+2]
   float* out;              // [B][H_q][D]
+  // Arrival counters, one per (batch, kv head), zero on entry; non-null when
+  // the split-K kernel merges in the same launch (the last block of a head to
+  // finish merges its parts and resets the counter).
+  int32_t* counters;
+  // Nonzero: the split-K kernel also quantizes rows 0..G-1 of every head's
+  // residual window into cache group n_groups (the streaming append).
+  int32_t append;
 };
+
+// Bytes of arrival counters at the start of a decode workspace (one int per
+// (batch, kv head) for up to 65536 of them); the partials follow.
+constexpr size_t kCounterBytes = 65536 * sizeof(int32_t);
+// Parts the in-launch merge accepts (more take the merge kernel).
+constexpr int kFusedMergeParts = 8;
 
 // The matrix-core decode kernels serve GQA groups of 4 or 8 heads with
 // G = 128: 2-bit codes plain or with the 16-channel Kitty boost, 4-bit codes
@@ -90,6 +103,19 @@ struct DecodeArgs {
 inline bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
   return group == 128 && (gqa == 4 || gqa == 8) &&
          ((bits == 2 && (n_boost == 0 || n_boost == 16)) || (bits == 4 && n_boost == 0));
+}
+// The 2-bit matrix-core kernel merges its parts in the same launch when a
+// head has at most kFusedMergeParts of them.
+inline bool fused_merge_supported(int bits, int group, int gqa, int n_boost, int n_parts) {
+  return bits == 2 && mfma_decode_supported(bits, group, gqa, n_boost) &&
+         n_parts <= kFusedMergeParts;
+}
+// The same kernel also runs the append of a full residual group (plain
+// 2-bit codes, at least 4 chunks: chunk c quantizes slice c of 4).
+inline bool fused_append_supported(int bits, int group, int gqa, int n_boost, int n_parts,
+                                   int n_chunks) {
+  return fused_merge_supported(bits, group, gqa, n_boost, n_parts) && n_boost == 0 &&
+         n_chunks >= 4;
 }
 // Resident blocks per CU of the matrix-core kernels: two waves per SIMD,
 // as one block of 8 waves (2-bit, fp8 x fp4 kernel) or two of 4 (4-bit).

@@ -12,16 +12,27 @@ namespace kvq {
 // part is empty).  Up to NPM parts; every load is issued up front (indices
 // past the count re-read the last part and get weight 0), so the merge costs
 // one memory round trip.
-template <int NPM>
+//
+// COHERENT: the partials were written by other blocks of the same launch
+// (possibly on other XCDs, whose L2 caches are not coherent with this one):
+// read them with device-scope relaxed atomic loads, which the writers paired
+// with device-scope stores.
+template <int NPM, bool COHERENT = false>
 __device__ __forceinline__ void merge_row(const float* ws, int np, float* out, int64_t bh, int d) {
   const float* w = ws + bh * (int64_t)np * (kD + 2);
+  auto ld = [](const float* p) -> float {
+    if constexpr (COHERENT)
+      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      return *p;
+  };
   float m[NPM], l[NPM], v[NPM];
 #pragma unroll
   for (int j = 0; j < NPM; ++j) {
     const float* wp = w + (int64_t)min(j, np - 1) * (kD + 2);
-    m[j] = wp[0];
-    l[j] = wp[1];
-    v[j] = wp[2 + d];
+    m[j] = ld(wp);
+    l[j] = ld(wp + 1);
+    v[j] = ld(wp + 2 + d);
   }
   float M = -__builtin_inff();
 #pragma unroll

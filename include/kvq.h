@@ -140,10 +140,17 @@ kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t 
                            int64_t n_quant_tokens, int32_t n_chunks_req, int32_t* n_chunks,
                            size_t* ws_bytes);
 
+/* Decode workspace layout: KVQ_WS_COUNTER_BYTES of int32 arrival counters
+ * (one per (batch, kv head)), then the fp32 partial records.  The counter
+ * bytes must be zero when a workspace is first used (allocate it zeroed);
+ * every call leaves them zero, so a workspace stays valid across calls and
+ * configurations.  The records need no initialization.  Calls that share a
+ * workspace must not overlap in time. */
+#define KVQ_WS_COUNTER_BYTES 262144
+
 /* Workspace bytes of kvq_decode_attention for the same arguments (0 on a bad
- * argument): fp32 partials (m, l, acc[D]) per (batch, query head, part).  The
- * contents need no initialization; calls that share a workspace must not
- * overlap in time. */
+ * argument): the counter bytes plus fp32 partials (m, l, acc[D]) per (batch,
+ * query head, part). */
 size_t kvq_decode_workspace_bytes(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t H_kv,
                                   int64_t n_quant_tokens, int32_t n_chunks_req);
 
@@ -157,8 +164,13 @@ size_t kvq_decode_workspace_bytes(const kvq_qcfg* cfg, int32_t B, int32_t H_q, i
  *  sm_scale <= 0 selects 1/sqrt(D).
  *  n_chunks: token chunks per head for split-K (0 = automatic); see
  *      kvq_decode_plan.  workspace: device memory of at least
- *      kvq_decode_workspace_bytes(...) bytes, 16-byte aligned.
- *  H_q / H_kv must be 1..8. */
+ *      kvq_decode_workspace_bytes(...) bytes, 16-byte aligned, counter bytes
+ *      zero (layout above).
+ *  H_q / H_kv must be 1..8.
+ *  2-bit codes with G = 128, GQA 4 or 8 and at most 8 parts per head run
+ *  as one launch: the last block of each head to finish merges the head's
+ *  partial records (device-scope stores and loads, one arrival counter per
+ *  head); other configurations launch the merge separately. */
 kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
                                 int32_t H_q, int32_t H_kv, const uint16_t* q,
                                 int64_t n_quant_tokens, const kvq_window* sink,
@@ -172,9 +184,11 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
  * up (KIVI page, Step 3; Kitty page, section 4.3, stage 3), whose tokens this
  * step still attends to in fp16.  The cache contents equal those of
  * kvq_quantize_pack(cfg, cache, B, H_kv, res->k, res->v, res->cap * D,
- * n_quant_tokens / G, 1), bit for bit.  The quantization runs in the same
- * launch as the log-sum-exp merge (two launches per step instead of three;
- * separate launches when the step has more than 32 parts).
+ * n_quant_tokens / G, 1), bit for bit.  Plain 2-bit codes with G = 128,
+ * GQA 4 or 8 and 4 to 8 chunks run the whole step as one launch (each of the
+ * first four blocks of a head quantizes a quarter of the group, the last
+ * block to finish merges); otherwise the quantization shares the merge's
+ * launch (separate launches past 32 parts).
  *  append != 0 requires res->n >= G and n_quant_tokens + G <= t_cap
  *  (else KVQ_ERR_ARG, nothing launched). */
 kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,
@@ -189,8 +203,8 @@ kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t 
  *
  * kvq_decode_partials: the split-K phase (same arguments as
  * kvq_decode_attention, no output).  Writes, for every batch b, query head h
- * and part p < *n_parts, the fp32 record
- *     workspace[((b*H_q + h)*n_parts + p)*(D+2) + {0, 1, 2..D+1}]
+ * and part p < *n_parts, the fp32 record (rec = workspace + counter bytes)
+ *     rec[((b*H_q + h)*n_parts + p)*(D+2) + {0, 1, 2..D+1}]
  *         = m, l, acc[0..D-1]
  * of one token range (BitDecoding page, section II; the combination rule is
  * the log-sum-exp merge): with x_t = sm*log2(e)*(q . k_t) over the range's
@@ -202,7 +216,8 @@ kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t 
  * kvq_decode_merge: out[b][h] = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
  * over the parts with l_p > 0 (M the largest such m_p); 0 when every part is
  * empty.  Reads workspace laid out as above with 1 <= n_parts <= 1024 and
- * ws_bytes >= B*H_q*n_parts*(D+2)*4. */
+ * ws_bytes >= KVQ_WS_COUNTER_BYTES + B*H_q*n_parts*(D+2)*4.  Neither call
+ * touches the counter bytes. */
 kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
                                int32_t H_q, int32_t H_kv, const uint16_t* q,
                                int64_t n_quant_tokens, const kvq_window* sink,

@@ -86,7 +86,7 @@ def gpu_decode(w, cache, inp, n_quant, n_chunks=0, n_res=None, n_sink=None, stre
     n_res = w.R if n_res is None else n_res
     n_sink = w.S if n_sink is None else n_sink
     _, ws_bytes = kvq.kvq_decode_plan(cfg, B, w.H_q, w.H_kv, n_quant, n_chunks)
-    ws = torch.zeros(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    ws = kvq.decode_workspace(ws_bytes)
     out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
     q = inp["q"][:B].contiguous()
     kvq.kvq_decode_attention(cfg, cache, B, w.H_q, w.H_kv, q, n_quant,

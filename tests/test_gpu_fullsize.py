@@ -67,7 +67,7 @@ def test_full_size_sampled_heads(built, name):
     n_chunks, ws_bytes = kvq.kvq_decode_plan(cfg, w.B, w.H_q, w.H_kv, w.T, w.min_chunks)
     if w.min_chunks:
         assert n_chunks >= w.min_chunks
-    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    ws = kvq.decode_workspace(ws_bytes)
     out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
     # the benchmark's step: decode + append of the full residual group (when
     # the window holds one) in one call

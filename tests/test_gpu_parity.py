@@ -205,10 +205,22 @@ def _partials(w, cache, inp, n_quant, sink, res, n_chunks=0):
     import bit_kv_cache_amd as kvq
     B = len(inp["heads"]) // w.H_kv
     _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), B, w.H_q, w.H_kv, n_quant, n_chunks)
-    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    ws = kvq.decode_workspace(ws_bytes)
     n_parts = kvq.kvq_decode_partials(qcfg(w), cache, B, w.H_q, w.H_kv, inp["q"][:B].contiguous(),
                                       n_quant, sink, res, ws, n_chunks=n_chunks)
-    return ws[: B * w.H_q * n_parts * (w.D + 2)].view(B * w.H_q, n_parts, w.D + 2)
+    return kvq.workspace_records(ws, B * w.H_q, n_parts, w.D)
+
+
+def _merge(parts, B, H_q):
+    """kvq_decode_merge over records [B*H_q][n_parts][D+2] placed in a fresh
+    workspace."""
+    import bit_kv_cache_amd as kvq
+    rows, n_parts, d2 = parts.shape
+    ws = kvq.decode_workspace(kvq.KVQ_WS_COUNTER_BYTES + parts.numel() * 4)
+    kvq.workspace_records(ws, rows, n_parts, d2 - 2).copy_(parts)
+    out = torch.empty((B, H_q, d2 - 2), dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_merge(B, H_q, n_parts, ws, out)
+    return out
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama_2bit", "kitty", "gqa8_4bit"])
@@ -221,8 +233,7 @@ def test_partials_then_merge_equals_one_call(built, name):
     parts = _partials(w, gc, inp, w.T, kvq.window(inp["k_sink"], inp["v_sink"], w.S),
                       kvq.window(inp["k_res"], inp["v_res"], w.R))
     B = len(inp["heads"]) // w.H_kv
-    out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
-    kvq.kvq_decode_merge(B, w.H_q, parts.shape[1], parts.contiguous(), out)
+    out = _merge(parts, B, w.H_q)
     # same kernels and chunking; equal up to the dynamic scheduling of the
     # 2-bit kernel (REPEAT_TOL)
     assert (out - one).abs().max().item() <= REPEAT_TOL
@@ -245,13 +256,43 @@ def test_token_split_across_calls_merges_to_whole(built, name):
     pa = _partials(w, ca, inp, g1 * w.G, kvq.window(inp["k_sink"], inp["v_sink"], w.S), None)
     pb = _partials(w, cb, inp, (n_groups - g1) * w.G, None,
                    kvq.window(inp["k_res"], inp["v_res"], w.R), n_chunks=3)
-    parts = torch.cat([pa, pb], dim=1).contiguous()
+    parts = torch.cat([pa, pb], dim=1)
     B = len(inp["heads"]) // w.H_kv
-    out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
-    kvq.kvq_decode_merge(B, w.H_q, parts.shape[1], parts, out)
+    out = _merge(parts, B, w.H_q)
     ref = oracle_decode(w, oracle_quantize(w, inp), inp, w.T)
     err = max_err(out, ref)
     assert err <= TOL, f"max-abs {err:.3g}"
+
+
+@pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "kitty_gqa4", "kitty"])
+def test_in_launch_merge_shared_workspace(built, name):
+    """The 2-bit kernel merges in its own launch (the last block of a head
+    reads the other blocks' records).  Consecutive calls on one workspace
+    with different queries and chunk counts: every output matches the oracle
+    (a record left over from an earlier call would not), and the arrival
+    counters are zero after every call."""
+    import bit_kv_cache_amd as kvq
+    w = _w(name)
+    inp = make_inputs(w)
+    gc = gpu_quantize(w, inp)
+    oc = oracle_quantize(w, inp)
+    B = len(inp["heads"]) // w.H_kv
+    ws = kvq.decode_workspace(max(kvq.kvq_decode_plan(qcfg(w), B, w.H_q, w.H_kv, w.T, n)[1]
+                                  for n in (0, 1, 3, 7, 32)))
+    counters = ws[: kvq.KVQ_WS_COUNTER_BYTES // 4].view(torch.int32)
+    sink = kvq.window(inp["k_sink"], inp["v_sink"], w.S)
+    res = kvq.window(inp["k_res"], inp["v_res"], w.R)
+    for i, (n_chunks, qs) in enumerate([(0, 1.0), (3, -0.5), (7, 2.0), (1, 1.5), (32, 0.75),
+                                        (0, -1.25)]):
+        q = (inp["q"][:B].float() * qs).half().contiguous()
+        out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+        kvq.kvq_decode_attention(qcfg(w), gc, B, w.H_q, w.H_kv, q, w.T, sink, res, out, ws,
+                                 n_chunks=n_chunks)
+        torch.cuda.synchronize()
+        assert int(counters.abs().sum().item()) == 0, f"call {i}: counters left non-zero"
+        ref = oracle_decode(w, oc, dict(inp, q=q), w.T)
+        err = max_err(out, ref)
+        assert err <= TOL, f"call {i} (n_chunks={n_chunks}, q x{qs}): max-abs {err:.3g}"
 
 
 def test_quantize_rounding_ties_bit_exact(built):
@@ -290,31 +331,32 @@ def test_quantize_rounding_ties_bit_exact(built):
 def test_decode_step_with_append(built, name):
     """kvq_decode_step(append): the attention equals the oracle over the
     quantized tokens + the full fp16 residual group, and the residual group
-    lands in cache group T/G bit-exact (quantized in the merge's launch, or
-    in launches of their own past 32 parts)."""
+    lands in cache group T/G bit-exact.  Chunk counts 4..8 take the one-launch
+    path for plain 2-bit codes (split-K, append and merge in one kernel);
+    others quantize in the merge's launch, or in launches of their own."""
     import bit_kv_cache_amd as kvq
     w = _w(name)
     w = synth.shrink(w, R=w.G)
     inp = make_inputs(w)
     t_cap = w.T + w.G
-    gc = gpu_quantize(w, inp, t_cap)
     oc = oracle_quantize(w, inp, t_cap)
+    ref = oracle_decode(w, oc, inp, w.T)
+    oracle.quantize_pack(oc, synth.as_bits(inp["k_res"]), synth.as_bits(inp["v_res"]),
+                         w.T // w.G, 1)
     B = len(inp["heads"]) // w.H_kv
-    for n_chunks in (0, 3):
+    for n_chunks in (0, 3, 4, 7):
+        gc = gpu_quantize(w, inp, t_cap)   # a fresh cache: each append is checked alone
         _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), B, w.H_q, w.H_kv, w.T, n_chunks)
-        ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+        ws = kvq.decode_workspace(ws_bytes)
         out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
         kvq.kvq_decode_step(qcfg(w), gc, B, w.H_q, w.H_kv, inp["q"][:B].contiguous(), w.T,
                             kvq.window(inp["k_sink"], inp["v_sink"], w.S),
                             kvq.window(inp["k_res"], inp["v_res"], w.R), out, ws, True,
                             n_chunks=n_chunks)
-        ref = oracle_decode(w, oc, inp, w.T)
+        torch.cuda.synchronize()
         err = max_err(out, ref)
         assert err <= TOL, f"{name} n_chunks={n_chunks}: max-abs {err:.3g}"
-    oracle.quantize_pack(oc, synth.as_bits(inp["k_res"]), synth.as_bits(inp["v_res"]),
-                         w.T // w.G, 1)
-    torch.cuda.synchronize()
-    assert_cache_equal(gc, oc, tokens=t_cap)
+        assert_cache_equal(gc, oc, tokens=t_cap)
     # the next step reads the appended group like any other
     out = gpu_decode(w, gc, inp, t_cap, n_res=0)
     assert max_err(out, oracle_decode(w, oc, inp, t_cap, n_res=0)) <= TOL
@@ -327,7 +369,7 @@ def test_decode_step_append_rejects_short_residual(built):
     gc = gpu_quantize(w, inp)
     B = len(inp["heads"]) // w.H_kv
     _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), B, w.H_q, w.H_kv, w.T, 0)
-    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    ws = kvq.decode_workspace(ws_bytes)
     out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
     with pytest.raises(kvq.KvqError):
         kvq.kvq_decode_step(qcfg(w), gc, B, w.H_q, w.H_kv, inp["q"][:B].contiguous(), w.T, None,
