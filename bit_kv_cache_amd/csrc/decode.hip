@@ -249,7 +249,9 @@ hipError_t decode_bits(int group, const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_decode_partials(int bits, int group, const DecodeArgs& a, hipStream_t st) {
   return mfma_decode_supported(bits, group, a.gqa, a.n_boost)
              ? launch_decode_mfma(bits, a, st)
-             : (bits == 2 ? decode_bits<2>(group, a, st) : decode_bits<4>(group, a, st));
+             : (bits == 2   ? decode_bits<2>(group, a, st)
+                : bits == 4 ? decode_bits<4>(group, a, st)
+                            : decode_bits<8>(group, a, st));
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st) {

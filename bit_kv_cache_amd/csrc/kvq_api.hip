@@ -15,9 +15,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Checks shared by every entry point.
 kvq_status check_cfg(const kvq_qcfg* cfg) {
   if (!cfg) return KVQ_ERR_ARG;
-  if (cfg->bits == 8 || (cfg->head_dim > 0 && cfg->head_dim != kD))
-    return KVQ_ERR_UNSUPPORTED;
-  if (cfg->bits != 2 && cfg->bits != 4) return KVQ_ERR_ARG;
+  if (cfg->head_dim > 0 && cfg->head_dim != kD) return KVQ_ERR_UNSUPPORTED;
+  if (cfg->bits != 2 && cfg->bits != 4 && cfg->bits != 8) return KVQ_ERR_ARG;
   if (cfg->head_dim != kD) return KVQ_ERR_ARG;
   const int fpi = 32 / cfg->bits;
   if (cfg->group <= 0 || cfg->group % fpi || kD % cfg->group) return KVQ_ERR_ARG;

@@ -414,6 +414,7 @@ hipError_t launch_merge_append(int bits, int group, const DecodeArgs& d, const Q
   if (bits == 2)
     return a.n_boost > 0 ? merge_append_parts<2, true>(group, d, a, s)
                          : merge_append_parts<2, false>(group, d, a, s);
+  if (bits == 8) return merge_append_parts<8, false>(group, d, a, s);
   return merge_append_parts<4, false>(group, d, a, s);
 }
 
@@ -421,11 +422,13 @@ hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t 
   if (a.n_groups == 0 || a.n_heads == 0) return hipSuccess;
   if (bits == 2)
     return a.n_boost > 0 ? quantize_bits<2, true>(group, a, s) : quantize_bits<2, false>(group, a, s);
+  if (bits == 8) return quantize_bits<8, false>(group, a, s);
   return quantize_bits<4, false>(group, a, s);
 }
 
 hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStream_t s) {
   if (a.n_groups == 0 || a.n_heads == 0) return hipSuccess;
+  if (bits == 8) return dequantize_bits<8>(group, a, s);
   return bits == 2 ? dequantize_bits<2>(group, a, s) : dequantize_bits<4>(group, a, s);
 }
 

@@ -10,10 +10,13 @@ namespace kvq {
 // round-half-even(clamp((x - mn)/s, 0, maxq)) with the IEEE fp32 quotient
 // (KIVI page, Step 1).  The quotient is taken as (x - mn) * rs, falling
 // back to the IEEE division near a rounding tie.  Exact: the range fits
-// (x - mn)/s <= 1.5 maxq <= 22.5 (s is the fp16-rounded range/maxq, at least
-// 2^-24 when nonzero), so the product and the IEEE quotient differ by at most
-// a few ulps of 32 (< 2^-17), and round-half-even of two values that close
-// differs only when a half-integer lies within 2^-16 of them; the clamp
+// (x - mn)/s <= 1.5 maxq (s is the fp16-rounded range/maxq, at least 2^-24
+// when nonzero).  The product is within a relative 2^-23 of the true
+// quotient and the IEEE quotient within half an ulp of it, so the two differ
+// by less than 2^-18 for maxq <= 15 (quotients <= 22.5) and less than 2^-14
+// for maxq = 255 (quotients <= 383); round-half-even of two values that close
+// differs only when a half-integer lies between them, so the fallback window
+// is 2^-16 for 2- and 4-bit codes and 2^-12 for 8-bit ones.  The clamp
 // bounds are integers and cannot change that.  s == 0 (max == min, or a
 // range whose scale underflows fp16) gives code 0.
 __device__ __forceinline__ uint32_t quant_code_rcp(float x, float mn, float s, float rs,
@@ -22,7 +25,8 @@ __device__ __forceinline__ uint32_t quant_code_rcp(float x, float mn, float s, f
   if (s == 0.0f) return 0u;
   const float dlt = x - mn;
   float y = dlt * rs;
-  if (__builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-16f) y = dlt / s;
+  const float win = maxq > 15.0f ? 0x1p-12f : 0x1p-16f;
+  if (__builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < win) y = dlt / s;
   y = fminf(fmaxf(y, 0.0f), maxq);
   return (uint32_t)__builtin_rintf(y);
 }

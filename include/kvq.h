@@ -73,14 +73,14 @@ typedef enum kvq_status {
   KVQ_OK = 0,
   KVQ_ERR_ARG = -1,         /* bad size, null pointer, out-of-range index */
   KVQ_ERR_ALIGN = -2,       /* a device pointer is not 16-byte aligned */
-  KVQ_ERR_UNSUPPORTED = -3, /* legal for the method, not built (bits 8, D != 128) */
+  KVQ_ERR_UNSUPPORTED = -3, /* legal for the method, not built (D != 128, G not 32/64/128, ...) */
   KVQ_ERR_WORKSPACE = -4,   /* workspace missing or too small */
   KVQ_ERR_HIP = -5          /* a kernel launch failed */
 } kvq_status;
 
 /* Quantization configuration.
- *  bits: 2 or 4 (8 is a legal packing width on the KIVI page and returns
- *        KVQ_ERR_UNSUPPORTED).
+ *  bits: 2, 4 or 8 (the KIVI page's packing widths).  8-bit codes take the
+ *        vector-ALU decode kernel.
  *  group: G, one of 32, 64, 128; must divide head_dim.
  *  head_dim: D, 128.
  *  n_boost: 0 (plain KIVI) or, with bits == 2, a multiple of 16 up to D

@@ -52,7 +52,8 @@ def _quant(cfg, cache, B=1, H=1, k=FAKE, v=FAKE, stride=128 * 128, fg=0, ng=1):
 
 @pytest.mark.parametrize("cfg,want", [
     (_cfg(bits=3), kvq.KVQ_ERR_ARG),
-    (_cfg(bits=8), kvq.KVQ_ERR_UNSUPPORTED),
+    (_cfg(bits=1), kvq.KVQ_ERR_ARG),
+    (_cfg(bits=8, nb=16), kvq.KVQ_ERR_ARG),        # the boost is for 2-bit codes
     (_cfg(D=64), kvq.KVQ_ERR_UNSUPPORTED),
     (_cfg(group=48), kvq.KVQ_ERR_ARG),
     (_cfg(group=8), kvq.KVQ_ERR_ARG),

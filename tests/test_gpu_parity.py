@@ -35,6 +35,10 @@ CASES = {
                                    T=6 * 64, R=64), {}),
     "gqa8_2bit": (synth.shrink(W["llama3_8b_t32k_2bit"], H_q=64, B=1, T=13 * 128, S=7), {}),
     "gqa8_4bit": (synth.shrink(W["llama3_8b_t8k_b32_4bit"], H_q=64, B=1, T=10 * 128), {}),
+    # 8-bit codes (the KIVI page's widest packing): the vector-ALU kernel
+    "llama_8bit": (W["llama3_8b_t8k_b32_4bit"], dict(B=2, T=11 * 128, bits=8)),
+    "g32_8bit_gqa2": (synth.shrink(W["llama3_8b_t32k_2bit"], bits=8, H_q=16, G=32, T=23 * 32,
+                                   B=1, R=32, S=3), {}),
 }
 
 
@@ -88,7 +92,7 @@ def test_append_group_matches_oracle(built):
     """Decode step, then quantize the full residual group into the next group
     slot (streaming append), then decode again with an empty residual."""
     import bit_kv_cache_amd as kvq
-    for name in ("llama_2bit", "llama_4bit", "kitty"):
+    for name in ("llama_2bit", "llama_4bit", "kitty", "llama_8bit"):
         w = _w(name)
         w = synth.shrink(w, R=w.G)
         inp = make_inputs(w)
@@ -300,7 +304,7 @@ def test_quantize_rounding_ties_bit_exact(built):
     either side of, half-integers: the GPU's code rounding (including its
     reciprocal fast path) must equal the oracle's IEEE division + RNE."""
     import bit_kv_cache_amd as kvq
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         w = synth.shrink(W["llama3_8b_t32k_2bit"], B=1, H_kv=2, H_q=8, T=4 * 128, bits=bits)
         maxq = (1 << bits) - 1
         gen = torch.Generator().manual_seed(77 + bits)
@@ -327,7 +331,8 @@ def test_quantize_rounding_ties_bit_exact(built):
         assert_cache_equal(gc, oc, tokens=w.T)
 
 
-@pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "long_splitk", "llama_4bit", "kitty"])
+@pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "long_splitk", "llama_4bit", "kitty",
+                                  "llama_8bit"])
 def test_decode_step_with_append(built, name):
     """kvq_decode_step(append): the attention equals the oracle over the
     quantized tokens + the full fp16 residual group, and the residual group
