@@ -46,7 +46,8 @@ class kvq_cache(ctypes.Structure):
                 ("k_min", ctypes.c_void_p), ("k_hi", ctypes.c_void_p),
                 ("k_bidx", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
                 ("v_scale", ctypes.c_void_p), ("v_min", ctypes.c_void_p),
-                ("t_cap", ctypes.c_int64)]
+                ("t_cap", ctypes.c_int64), ("page_table", ctypes.c_void_p),
+                ("pt_stride", ctypes.c_int64)]
 
 
 class kvq_window(ctypes.Structure):
@@ -125,7 +126,9 @@ class QCfg:
 
 @dataclass
 class Cache:
-    """Packed cache tensors (layout in include/kvq.h).  ``heads`` = B*H_kv."""
+    """Packed cache tensors (layout in include/kvq.h).  ``heads`` = B*H_kv.
+    With ``page_table`` (int32 ``[heads][pt_stride]``) the tensors are a pool
+    of ``t_cap / G`` one-group pages (``Cache.pool``)."""
     cfg: QCfg
     t_cap: int
     heads: int
@@ -137,6 +140,7 @@ class Cache:
     v_codes: torch.Tensor
     v_scale: torch.Tensor
     v_min: torch.Tensor
+    page_table: torch.Tensor | None = None
 
     FIELDS = ("k_codes", "k_scale", "k_min", "k_hi", "k_bidx", "v_codes", "v_scale", "v_min")
 
@@ -158,8 +162,21 @@ class Cache:
             v_min=torch.zeros((H, T, D // G), dtype=torch.int16, **z),
         )
 
+    @staticmethod
+    def pool(cfg: QCfg, n_pages: int, page_table: torch.Tensor, device="cuda") -> "Cache":
+        """A paged cache: ``n_pages`` one-group pages, and the page of group g
+        of head h at ``page_table[h][g]`` (int32 ``[heads][max_groups]``)."""
+        c = Cache.empty(cfg, 1, n_pages * cfg.group, device=device)
+        c.heads = int(page_table.shape[0])
+        c.page_table = page_table.to(torch.int32).contiguous()
+        return c
+
     def heads_view(self, h0: int, n: int) -> "Cache":
         """The cache restricted to heads [h0, h0+n) (same storage)."""
+        if self.page_table is not None:
+            return Cache(self.cfg, self.t_cap, n,
+                         **{f: getattr(self, f) for f in self.FIELDS},
+                         page_table=self.page_table[h0:h0 + n])
         sl = {f: (None if getattr(self, f) is None else getattr(self, f)[h0:h0 + n])
               for f in self.FIELDS}
         return Cache(self.cfg, self.t_cap, n, **sl)
@@ -169,7 +186,9 @@ class Cache:
                    for f in self.FIELDS if getattr(self, f) is not None)
 
     def c(self) -> kvq_cache:
-        return kvq_cache(*[_ptr(getattr(self, f)) for f in self.FIELDS], self.t_cap)
+        pt = self.page_table
+        return kvq_cache(*[_ptr(getattr(self, f)) for f in self.FIELDS], self.t_cap,
+                         _ptr(pt), 0 if pt is None else int(pt.stride(0)))
 
 
 def window(k: torch.Tensor | None, v: torch.Tensor | None, n: int) -> kvq_window | None:

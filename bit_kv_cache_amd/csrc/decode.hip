@@ -34,16 +34,25 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
   const int64_t g0 = t0 / G;
   const int ng = nt / G;
 
-  // stage per-group key scale/min (and Kitty rows), per-token value scale/min
+  // the block (page) of each group, then per-group key scale/min (and Kitty
+  // rows) and per-token value scale/min
+  if (tid < ng) {
+    const int64_t blk = group_block(a.c, head, g0 + tid, G);
+    s.gblk[tid] = blk;
+    if (blk < 0) s.bad = 1;
+  }
+  __syncthreads();
+  if (s.bad) return;   // a page outside the pool: the part is poisoned
   for (int i = tid; i < ng * kD; i += kThreads) {
     const int gl = i / kD, d = i % kD;
-    const int64_t off = (head * (a.c.t_cap / G) + g0 + gl) * kD + d;
+    const int64_t off = s.gblk[gl] * kD + d;
     s.ks[gl][d] = h2f(a.c.k_scale[off]);
     s.km[gl][d] = h2f(a.c.k_min[off]);
     if (a.n_boost > 0) s.kb[gl][d] = a.c.k_bidx[off];
   }
   for (int i = tid; i < nt * NCG; i += kThreads) {
-    const int64_t off = (head * a.c.t_cap + t0) * NCG + i;
+    const int t = i / NCG;
+    const int64_t off = (s.gblk[t / G] * G + t % G) * NCG + i % NCG;
     s.vs[i] = h2f(a.c.v_scale[off]);
     s.vm[i] = h2f(a.c.v_min[off]);
   }
@@ -54,10 +63,11 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
     const int t = tid & (kBlockTok - 1), half = tid >> 7;
     if (t < nt) {
       const int gl = t / G;
-      const uint32_t* kw = a.c.k_codes + (head * a.c.t_cap + t0 + t) * WPT + half * (WPT / 2);
+      const int64_t tb = s.gblk[gl] * G + t % G;   // the token's row in the block layout
+      const uint32_t* kw = a.c.k_codes + tb * WPT + half * (WPT / 2);
       uint32_t hw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (a.n_boost > 0) {
-        const uint32_t* hp = a.c.k_hi + (head * a.c.t_cap + t0 + t) * (a.n_boost / 16);
+        const uint32_t* hp = a.c.k_hi + tb * (a.n_boost / 16);
         for (int w = 0; w < a.n_boost / 16; ++w) hw[w] = hp[w];
       }
       float dot[GQA];
@@ -99,9 +109,9 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
     for (int h = 0; h < GQA; ++h) acc[h] *= s.alpha[h];
     const int tb = half * (kBlockTok / 2);
     const int te = min(nt, tb + kBlockTok / 2);
-    const uint32_t* vw = a.c.v_codes + (head * (a.c.t_cap / FPI)) * kD + d;
+    const uint32_t* vw = a.c.v_codes + d;
     for (int tw = tb; tw < te; tw += FPI) {
-      const uint32_t word = vw[((t0 + tw) / FPI) * kD];
+      const uint32_t word = vw[((s.gblk[tw / G] * G + tw % G) / FPI) * kD];
 #pragma unroll
       for (int j = 0; j < FPI; ++j) {
         const int t = tw + j;
@@ -132,6 +142,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     s.m[tid] = kNegInf;
     s.l[tid] = 0.f;
   }
+  if (tid == 0) s.bad = 0;
   __syncthreads();
 
   float acc[GQA];
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   if (part < a.n_chunks) {
     const int64_t gb = (int64_t)part * a.groups_per_chunk;
     const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
-    for (int64_t g = gb; g < ge; g += kBlockTok / G) {
+    for (int64_t g = gb; g < ge && !s.bad; g += kBlockTok / G) {
       const int ng = (int)min<int64_t>(kBlockTok / G, ge - g);
       quant_block<BITS, G, GQA>(a, s, head, g * G, ng * G, acc);
     }

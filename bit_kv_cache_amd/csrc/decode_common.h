@@ -28,6 +28,8 @@ struct Lds {
   float p[GQA][kBlockTok];               // logits, then probabilities
   float m[GQA], l[GQA], alpha[GQA];
   float acc[GQA][kD];                    // final combine of the two token halves
+  int64_t gblk[kBlockTok / 32];          // cache block (page) of each group in the block
+  int bad;                               // a group's page lies outside the pool
 };
 
 // ------------------------------------------------------------------ softmax
@@ -129,10 +131,11 @@ __device__ void write_partial(const DecodeArgs& a, Lds<GQA>& s, int64_t b, int64
 #pragma unroll
     for (int h = 0; h < GQA; ++h) {
       float* w = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + part) * (kD + 2);
-      w[2 + d] = acc[h] + s.acc[h][d];
+      // a bad page poisons the part: l = 1 keeps it in the merge, acc NaN
+      w[2 + d] = s.bad ? __builtin_nanf("") : acc[h] + s.acc[h][d];
       if (d == 0) {
-        w[0] = s.m[h];
-        w[1] = s.l[h];
+        w[0] = s.bad ? 0.f : s.m[h];
+        w[1] = s.bad ? 1.f : s.l[h];
       }
     }
   }

@@ -419,7 +419,8 @@ __device__ __forceinline__ void append_item_load(const DecodeArgs& a, int64_t he
 
 __device__ __forceinline__ void append_item(const DecodeArgs& a, int64_t head, int s, int k,
                                             int lane, const u32x4 (&x)[4]) {
-  const int64_t g = a.n_groups;
+  const int64_t blk = group_block(a.c, head, a.n_groups, kG);   // the appended group's block
+  if (blk < 0) return;   // a page outside the pool: nothing is written
   if (k < 2) {
     const int c0 = 32 * s + 16 * k, q = lane & 1;
     // per channel over the 128 tokens: the lane's 4, then the 32 lanes with
@@ -460,7 +461,7 @@ __device__ __forceinline__ void append_item(const DecodeArgs& a, int64_t head, i
       }
     }
     if (lane < 2) {
-      const int64_t m_off = (head * (a.c.t_cap / kG) + g) * kD + c0 + 8 * q;
+      const int64_t m_off = blk * kD + c0 + 8 * q;
       *reinterpret_cast<u32x4*>(a.c.k_scale + m_off) = u32x4{shw[0], shw[1], shw[2], shw[3]};
       *reinterpret_cast<u32x4*>(a.c.k_min + m_off) = u32x4{mnw[0], mnw[1], mnw[2], mnw[3]};
     }
@@ -475,7 +476,7 @@ __device__ __forceinline__ void append_item(const DecodeArgs& a, int64_t head, i
       const uint32_t word = part | (uint32_t)__shfl_xor((int)part, 1);
       if (q == 0) {
         const int t = (lane >> 1) + 32 * i;
-        a.c.k_codes[(head * a.c.t_cap + g * kG + t) * kAppWpt + 2 * s + k] = word;
+        a.c.k_codes[(blk * kG + t) * kAppWpt + 2 * s + k] = word;
       }
     }
   } else {
@@ -509,7 +510,7 @@ __device__ __forceinline__ void append_item(const DecodeArgs& a, int64_t head, i
       sc[i] = h2f(sh);
       rs[i] = 1.0f / sc[i];
       if (q == 0) {
-        const int64_t m_off = head * a.c.t_cap + g * kG + t0 + r + 4 * i;
+        const int64_t m_off = blk * kG + t0 + r + 4 * i;
         a.c.v_scale[m_off] = sh;
         a.c.v_min[m_off] = l16;
       }
@@ -527,7 +528,7 @@ __device__ __forceinline__ void append_item(const DecodeArgs& a, int64_t head, i
       wd[e] = part | (uint32_t)__shfl_xor((int)part, 32);
     }
     if (r == 0) {
-      uint32_t* dst = a.c.v_codes + (head * (a.c.t_cap / 16) + (g * kG + t0) / 16) * kD + 8 * q;
+      uint32_t* dst = a.c.v_codes + (blk * (kG / 16) + t0 / 16) * kD + 8 * q;
       *reinterpret_cast<u32x4*>(dst) = u32x4{wd[0], wd[1], wd[2], wd[3]};
       *reinterpret_cast<u32x4*>(dst + 4) = u32x4{wd[4], wd[5], wd[6], wd[7]};
     }
@@ -644,22 +645,30 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     // is in LDS.  A slot is refilled only after a consumer copied its
     // previous group out (empty[s] == j).
     const int sub = lane & 15, part = lane >> 4;
-    const char* kp = reinterpret_cast<const char*>(a.c.k_codes) +
-                     (head * a.c.t_cap + gb * kG) * (kWpt * 4) + 16 * lane;
-    const char* vp = reinterpret_cast<const char*>(a.c.v_codes) +
-                     (head * (a.c.t_cap / 16) + gb * (kG / 16)) * (kD * 4) + 16 * lane;
+    // Every array is a sequence of one-group blocks: the group with block
+    // index blk has its key words at k_codes + 4096 blk bytes, its value words
+    // at v_codes + 4096 blk, its scales and mins at + 256 blk in each of the
+    // four arrays (Kitty: high-bits words + 512 blk, boosted rows + 128 blk).
+    const char* kp = reinterpret_cast<const char*>(a.c.k_codes) + 16 * lane;
+    const char* vp = reinterpret_cast<const char*>(a.c.v_codes) + 16 * lane;
     // metadata lanes: key scale, key min, value scale, value min (256 B each)
     const uint16_t* marr = part == 0 ? a.c.k_scale : part == 1 ? a.c.k_min
                          : part == 2 ? a.c.v_scale : a.c.v_min;
-    const int64_t m0 = part < 2 ? (head * (a.c.t_cap / kG) + gb) * kD : head * a.c.t_cap + gb * kG;
-    const char* mp = reinterpret_cast<const char*>(marr + m0) + 16 * sub;
+    const char* mp = reinterpret_cast<const char*>(marr) + 16 * sub;
     // Kitty lanes: 0..31 the group's 128 high-bits words, 32..39 its 128
     // boosted-row bytes (40..63 repeat them into the pad)
-    const char* xp = lane < 32 ? reinterpret_cast<const char*>(a.c.k_hi) +
-                                     (head * a.c.t_cap + gb * kG) * 4 + 16 * lane
-                               : reinterpret_cast<const char*>(a.c.k_bidx) +
-                                     (head * (a.c.t_cap / kG) + gb) * kD + 16 * ((lane - 32) & 7);
+    const char* xp = lane < 32 ? reinterpret_cast<const char*>(a.c.k_hi) + 16 * lane
+                               : reinterpret_cast<const char*>(a.c.k_bidx) + 16 * ((lane - 32) & 7);
     const int64_t xstep = lane < 32 ? kG * 4 : kD;
+    // block of the chunk's group gb + jo: head-major, or the page table's entry
+    // (read through the constant address space: scalar loads, which the
+    // vector-memory counter the copies rely on does not see)
+    const int64_t blk0 = head * (a.c.t_cap / kG) + gb;
+    const int64_t pool = a.c.t_cap / kG;
+    typedef __attribute__((address_space(4))) const int32_t* PagePtr;
+    const PagePtr pt = a.c.pages ? (PagePtr)(uintptr_t)(a.c.pages + head * a.c.pt_stride + gb)
+                                 : (PagePtr) nullptr;
+    bool bad_page = false;
     // LDS byte address of the ring (address-space cast of the generic pointer)
     const uint32_t ring0 =
         (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)(&sh.ring[0][0]));
@@ -687,19 +696,27 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       asm volatile("" ::: "memory");
       const uint32_t sl = __builtin_amdgcn_readfirstlane(ring0 + s * SB);
       const int64_t jo = j + rot < ngc ? j + rot : j + rot - ngc;
+      int64_t blk = blk0 + jo;
+      if (pt) {
+        blk = pt[jo];
+        if (blk < 0 || blk >= pool) {   // a page outside the pool: copy block 0, poison
+          bad_page = true;
+          blk = 0;
+        }
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma_1k(sl + 1024 * i, kp + jo * 4096 + 1024 * i);
+      for (int i = 0; i < 4; ++i) dma_1k(sl + 1024 * i, kp + blk * 4096 + 1024 * i);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma_1k(sl + kSlotV + 1024 * i, vp + jo * 4096 + 1024 * i);
-      dma_1k(sl + kSlotKs, mp + jo * 256);
-      if constexpr (KITTY) dma_1k(sl + kSlotHi, xp + jo * xstep);
+      for (int i = 0; i < 4; ++i) dma_1k(sl + kSlotV + 1024 * i, vp + blk * 4096 + 1024 * i);
+      dma_1k(sl + kSlotKs, mp + blk * 256);
+      if constexpr (KITTY) dma_1k(sl + kSlotHi, xp + blk * xstep);
       if (lane == 0)
         dma_flag(__builtin_amdgcn_readfirstlane(ready0 + 4 * s), kSeq.v + (j & (kSeqLen - 1)));
       if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
     }
     if (!met) __syncthreads();
     vm_wait<0>();
-    if (!ok && lane == 0) lds_store(&sh.stalled, 1);
+    if ((!ok || bad_page) && lane == 0) lds_store(&sh.stalled, 1);
   } else {
     // ---------------------------------------------------------- consumer waves
     // query, then this wave's first fp16 window tile (requested first, so
@@ -1175,7 +1192,11 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       num = lw[w] > 0.f ? fmaf(nw[w], f, num) : num;
       den = lw[w] > 0.f ? fmaf(lw[w], f, den) : den;
     }
-    if (stalled) num = den = __builtin_nanf("");   // a wait ran out: poison the result
+    if (stalled) {   // a wait ran out or a page was bad: poison the part (l = 1 keeps
+      num = __builtin_nanf("");   // it in the merge, acc NaN)
+      den = 1.f;
+      mm = 0.f;
+    }
     float* wp = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + chunk) * (kD + 2);
     if (a.counters) {
       // read by another block of this launch: device-scope stores

@@ -176,12 +176,12 @@ struct LaneOffsets {
   uint32_t vmeta;   // value scale/min run 0 inside the group's [G] tokens
 };
 
+// blk: the group's block (page) in the cache arrays
 template <int BITS>
-__device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int64_t g,
+__device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t blk,
                                           const LaneOffsets<BITS>& o, KeyLoad<BITS>& L) {
   constexpr int WPT = kD / (32 / BITS);
-  const char* kb = reinterpret_cast<const char*>(a.c.k_codes) +
-                   (head * a.c.t_cap + g * kG) * WPT * 4 + o.kw;
+  const char* kb = reinterpret_cast<const char*>(a.c.k_codes) + blk * kG * WPT * 4 + o.kw;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     if (BITS == 2) {
@@ -194,29 +194,26 @@ __device__ __forceinline__ void load_keys(const DecodeArgs& a, int64_t head, int
       for (int i = 0; i < KeyLoad<BITS>::KW; ++i) L.kw[t][i] = v[i];
     }
   }
-  const char* km = reinterpret_cast<const char*>(a.c.k_min) +
-                   (head * (a.c.t_cap / kG) + g) * kD * 2 + o.kmin;
+  const char* km = reinterpret_cast<const char*>(a.c.k_min) + blk * kD * 2 + o.kmin;
 #pragma unroll
   for (int c = 0; c < 4; ++c) L.kmin[c] = ldnt<u32x4>(km + 64 * c);
-  const char* ks = reinterpret_cast<const char*>(a.c.k_scale) +
-                   (head * (a.c.t_cap / kG) + g) * kD * 2 + o.kmeta;
+  const char* ks = reinterpret_cast<const char*>(a.c.k_scale) + blk * kD * 2 + o.kmeta;
   L.ks[0] = ldnt<u32x2>(ks);
   L.ks[1] = ldnt<u32x2>(ks + 2 * run_stride<BITS>());
 }
 
 template <int BITS>
-__device__ __forceinline__ void load_values(const DecodeArgs& a, int64_t head, int64_t g,
+__device__ __forceinline__ void load_values(const DecodeArgs& a, int64_t blk,
                                             const LaneOffsets<BITS>& o, ValueLoad<BITS>& L) {
   constexpr int FPI = 32 / BITS;
   constexpr int VR = ValueLoad<BITS>::VR;
-  const char* vb = reinterpret_cast<const char*>(a.c.v_codes) +
-                   (head * (a.c.t_cap / FPI) + g * (kG / FPI)) * kD * 4 + o.vw;
+  const char* vb = reinterpret_cast<const char*>(a.c.v_codes) + blk * (kG / FPI) * kD * 4 + o.vw;
 #pragma unroll
   for (int i = 0; i < VR; ++i)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
       L.vw[i][e] = ldnt<u32x4>(vb + (i * kD + 64 * e) * 4);
-  const int64_t t0 = (head * a.c.t_cap + g * kG) * 2;
+  const int64_t t0 = blk * kG * 2;
   const char* vs = reinterpret_cast<const char*>(a.c.v_scale) + t0 + o.vmeta;
   const char* vm = reinterpret_cast<const char*>(a.c.v_min) + t0 + o.vmeta;
   L.vs[0] = ldnt<u32x2>(vs);
@@ -263,6 +260,7 @@ struct MfmaLds {
     MergeLds<GQA> merge;
   } u;
   u32x4 bias_a[4][4][16];                          // bias A operand [c][kq][row]
+  int bad;                                         // a group's page lies outside the pool
 };
 
 template <int BITS, int GQA>
@@ -299,15 +297,27 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
   }
   KeyLoad<BITS> kl;
   ValueLoad<BITS> vl;
+  // a group's block (page); a page outside the pool reads block 0 and
+  // poisons the block's result
+  bool bad_page = false;
+  auto blk_of = [&](int64_t gg) -> int64_t {
+    const int64_t bk = group_block(a.c, head, gg, kG);
+    bad_page = bad_page || bk < 0;
+    return bk < 0 ? 0 : bk;
+  };
   int64_t g = gb + wave;
   if (g < ge) {
-    load_keys<BITS>(a, head, g, lo, kl);
-    load_values<BITS>(a, head, g, lo, vl);
+    const int64_t blk = blk_of(g);
+    load_keys<BITS>(a, blk, lo, kl);
+    load_values<BITS>(a, blk, lo, vl);
   }
 
   // ---------------------------------------------------------------- quantized groups
   WaveLds<GQA>& L = sh.u.main.w[wave];
-  if (tid == 0) sh.u.main.zero = u32x4{0u, 0u, 0u, 0u};
+  if (tid == 0) {
+    sh.u.main.zero = u32x4{0u, 0u, 0u, 0u};
+    sh.bad = 0;
+  }
 
   // this lane's A-prep heads (ph, ph + 4) and chunk (pc, pkq)
   // q * sm * log2e * 2^(24 - offset) of this lane's A-prep elements, in LDS
@@ -439,7 +449,8 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
       }
     }
     // the key registers are free: fetch the next group's keys
-    if (PREFETCH) load_keys<BITS>(a, head, gn, lo, kl);
+    const int64_t blk_n = PREFETCH ? blk_of(gn) : 0;
+    if (PREFETCH) load_keys<BITS>(a, blk_n, lo, kl);
 
     // ---- online softmax over the group (per head, this wave)
     float alpha[2];
@@ -534,7 +545,7 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
       }
     }
     // the value registers are free: fetch the next group's values
-    if (PREFETCH) load_values<BITS>(a, head, gn, lo, vl);
+    if (PREFETCH) load_values<BITS>(a, blk_n, lo, vl);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -663,6 +674,7 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
   for (int j = 0; j < NH; ++j) {
     mtsum[j] = row_sum16(mterm[j]);
   }
+  if (bad_page) sh.bad = 1;
   __syncthreads();   // the per-wave buffers are reused for the merge below
   MergeLds<GQA>& M = sh.u.merge;
   if (n == 0 && pv_rows) {
@@ -710,6 +722,11 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
       const float f = exp2f(mw[w] - mm);
       num = lw[w] > 0.f ? fmaf(nw[w], f, num) : num;
       den = lw[w] > 0.f ? fmaf(lw[w], f, den) : den;
+    }
+    if (sh.bad) {   // poisoned: l = 1 keeps the part in the merge, acc NaN
+      num = __builtin_nanf("");
+      den = 1.f;
+      mm = 0.f;
     }
     float* wp = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + chunk) * (kD + 2);
     wp[2 + d] = num;

@@ -36,13 +36,22 @@ kvq_status check_cache(const kvq_qcfg* cfg, const kvq_cache* c) {
       !aligned16(c->v_codes) || !aligned16(c->v_scale) || !aligned16(c->v_min))
     return KVQ_ERR_ALIGN;
   if (cfg->n_boost > 0 && (!aligned16(c->k_hi) || !aligned16(c->k_bidx))) return KVQ_ERR_ALIGN;
+  if (c->page_table && (c->pt_stride <= 0 || (reinterpret_cast<uintptr_t>(c->page_table) & 3u)))
+    return c->pt_stride <= 0 ? KVQ_ERR_ARG : KVQ_ERR_ALIGN;
   return KVQ_OK;
 }
 
 kvq::CacheArgs cache_args(const kvq_cache* c) {
   return {reinterpret_cast<uint32_t*>(c->k_codes), c->k_scale, c->k_min,
           reinterpret_cast<uint32_t*>(c->k_hi), c->k_bidx,
-          reinterpret_cast<uint32_t*>(c->v_codes), c->v_scale, c->v_min, c->t_cap};
+          reinterpret_cast<uint32_t*>(c->v_codes), c->v_scale, c->v_min, c->t_cap,
+          c->page_table, c->page_table ? c->pt_stride : 0};
+}
+
+// The groups [0, end_group) of every head must be addressable: in a
+// contiguous cache within t_cap, in a paged one within the table's rows.
+bool groups_fit(const kvq_cache* c, int64_t G, int64_t end_group) {
+  return c->page_table ? end_group <= c->pt_stride : end_group * G <= c->t_cap;
 }
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
@@ -118,7 +127,7 @@ kvq_status kvq_quantize_pack(const kvq_qcfg* cfg, const kvq_cache* cache, int32_
   if (B <= 0 || H_kv <= 0) return KVQ_ERR_ARG;
   if (first_group < 0 || n_groups < 0) return KVQ_ERR_ARG;
   const int64_t G = cfg->group;
-  if ((first_group + n_groups) * G > cache->t_cap) return KVQ_ERR_ARG;
+  if (!groups_fit(cache, G, first_group + n_groups)) return KVQ_ERR_ARG;
   if (n_groups == 0) return KVQ_OK;
   if (!k_src || !v_src) return KVQ_ERR_ARG;
   if (src_head_stride < n_groups * G * kD) return KVQ_ERR_ARG;
@@ -175,7 +184,7 @@ kvq_status prepare_decode(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
   kvq_status st = kvq_decode_plan(cfg, B, H_q, H_kv, n_quant_tokens, n_chunks, &nc, &need);
   if (st != KVQ_OK) return st;
   if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
-  if (n_quant_tokens > cache->t_cap) return KVQ_ERR_ARG;
+  if (!groups_fit(cache, cfg->group, n_quant_tokens / cfg->group)) return KVQ_ERR_ARG;
   if ((st = check_window(sink)) != KVQ_OK) return st;
   if ((st = check_window(res)) != KVQ_OK) return st;
   if (!q) return KVQ_ERR_ARG;
@@ -262,7 +271,7 @@ kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t 
   const int64_t G = cfg->group;
   if (append) {
     // the residual holds the full group that becomes group n_quant_tokens / G
-    if (!res || res->n < G || n_quant_tokens + G > cache->t_cap) return KVQ_ERR_ARG;
+    if (!res || res->n < G || !groups_fit(cache, G, n_quant_tokens / G + 1)) return KVQ_ERR_ARG;
     if ((int64_t)H_kv * B * 8 + (int64_t)B * H_q > 0x7FFFFFFF) return KVQ_ERR_ARG;
   }
   a.out = out;
@@ -324,7 +333,7 @@ kvq_status kvq_dequantize(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
   if (st != KVQ_OK) return st;
   if ((st = check_cache(cfg, cache)) != KVQ_OK) return st;
   if (B <= 0 || H_kv <= 0 || first_group < 0 || n_groups < 0) return KVQ_ERR_ARG;
-  if ((first_group + n_groups) * cfg->group > cache->t_cap) return KVQ_ERR_ARG;
+  if (!groups_fit(cache, cfg->group, first_group + n_groups)) return KVQ_ERR_ARG;
   if (n_groups == 0) return KVQ_OK;
   if (!k_out || !v_out) return KVQ_ERR_ARG;
   if (!aligned16(k_out) || !aligned16(v_out)) return KVQ_ERR_ALIGN;

@@ -41,7 +41,19 @@ struct CacheArgs {
   uint16_t* v_scale;
   uint16_t* v_min;
   int64_t t_cap;
+  const int32_t* pages;   // NULL: contiguous; else [heads][pt_stride] page of each group
+  int64_t pt_stride;
 };
+
+// Block index of group g of head `head` in every cache array (the arrays are
+// sequences of one-group blocks): head-major in a contiguous cache, the page
+// table's entry in a paged one.  Returns -1 for a page outside the pool.
+__device__ __forceinline__ int64_t group_block(const CacheArgs& c, int64_t head, int64_t g,
+                                               int G) {
+  if (!c.pages) return head * (c.t_cap / G) + g;
+  const int64_t p = c.pages[head * c.pt_stride + g];
+  return (p >= 0 && p < c.t_cap / G) ? p : -1;
+}
 
 struct QuantArgs {
   CacheArgs c;

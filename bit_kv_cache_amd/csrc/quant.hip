@@ -58,7 +58,8 @@ __device__ void quantize_keys_slice(const QuantArgs& a, int64_t head, int64_t gi
   __shared__ uint32_t red[2][8][CH];
   __shared__ float s_mn[CH], s_sc[CH], s_rs[CH];
   const int tid = threadIdx.x;
-  const int64_t g = a.first_group + gi;
+  const int64_t gb = group_block(a.c, head, a.first_group + gi, G);   // the group's block (page)
+  if (gb < 0) return;                     // a page outside the pool: nothing is written
   const uint16_t* src = a.k_src + head * a.src_head_stride + gi * G * kD + slice * CH;
   // stage: each row contributes 64 bytes (4 x 16 B)
   for (int i = tid; i < G * 4; i += kThreads) {
@@ -91,7 +92,7 @@ __device__ void quantize_keys_slice(const QuantArgs& a, int64_t head, int64_t gi
     const float mn = h2f(from_order_key(lo));
     const float mx = h2f(from_order_key(hi));
     const uint16_t sh = f2h((mx - mn) / (float)MASK);
-    const int64_t m_off = (head * (a.c.t_cap / G) + g) * kD + slice * CH + tid;
+    const int64_t m_off = gb * kD + slice * CH + tid;
     a.c.k_scale[m_off] = sh;
     a.c.k_min[m_off] = from_order_key(lo);
     s_mn[tid] = mn;
@@ -100,7 +101,7 @@ __device__ void quantize_keys_slice(const QuantArgs& a, int64_t head, int64_t gi
   }
   __syncthreads();
   // codes, packed along channels: word (t, w) holds channels w*FPI + j
-  uint32_t* kw = a.c.k_codes + (head * a.c.t_cap + g * G) * WPT + slice * SW;
+  uint32_t* kw = a.c.k_codes + gb * G * WPT + slice * SW;
   for (int i = tid; i < G * SW; i += kThreads) {
     const int t = i / SW, w = i % SW;
     uint32_t word = 0u;
@@ -124,7 +125,8 @@ __device__ void quantize_keys_kitty(const QuantArgs& a, int64_t head, int64_t gi
   __shared__ int s_flag[kD], s_chan_of_row[kD];
   __shared__ uint32_t s_red[2][kD];
   const int tid = threadIdx.x;
-  const int64_t g = a.first_group + gi;
+  const int64_t gb = group_block(a.c, head, a.first_group + gi, G);
+  if (gb < 0) return;
   const int nb = a.n_boost;
   const uint16_t* src = a.k_src + head * a.src_head_stride + gi * G * kD;
   {
@@ -172,7 +174,7 @@ __device__ void quantize_keys_kitty(const QuantArgs& a, int64_t head, int64_t gi
     }
     const float maxq = (row < nb) ? 15.0f : (float)MASK;
     const uint16_t sh = f2h(s_rng[d] / maxq);
-    const int64_t m_off = (head * (a.c.t_cap / G) + g) * kD + d;
+    const int64_t m_off = gb * kD + d;
     a.c.k_scale[m_off] = sh;
     a.c.k_min[m_off] = from_order_key(lo);
     a.c.k_bidx[m_off] = (uint8_t)row;
@@ -181,7 +183,7 @@ __device__ void quantize_keys_kitty(const QuantArgs& a, int64_t head, int64_t gi
     if (row < nb) s_chan_of_row[row] = d;
   }
   __syncthreads();
-  uint32_t* kw = a.c.k_codes + (head * a.c.t_cap + g * G) * WPT;
+  uint32_t* kw = a.c.k_codes + gb * G * WPT;
   for (int i = tid; i < G * WPT; i += kThreads) {
     const int t = i / WPT, w = i % WPT;
     uint32_t word = 0u;
@@ -195,7 +197,7 @@ __device__ void quantize_keys_kitty(const QuantArgs& a, int64_t head, int64_t gi
   }
   // high two bits of the boosted rows, 16 rows per word
   const int hpt = nb / 16;
-  uint32_t* hw = a.c.k_hi + (head * a.c.t_cap + g * G) * hpt;
+  uint32_t* hw = a.c.k_hi + gb * G * hpt;
   for (int i = tid; i < G * hpt; i += kThreads) {
     const int t = i / hpt, w = i % hpt;
     uint32_t word = 0u;
@@ -226,7 +228,8 @@ __device__ void quantize_values_slice(const QuantArgs& a, int64_t head, int64_t 
   static_assert(FPI <= NT && NT % FPI == 0, "whole words per slice");
   static_assert(TPP >= 1 && (TPP & (TPP - 1)) == 0 && G % TPP == 0, "thread split");
   const int tid = threadIdx.x;
-  const int64_t g = a.first_group + gi;
+  const int64_t gb = group_block(a.c, head, a.first_group + gi, G);
+  if (gb < 0) return;
   const int t_base = slice * NT;
   const uint16_t* src = a.v_src + head * a.src_head_stride + (gi * G + t_base) * kD;
   for (int i = tid; i < NT * kD / 8; i += kThreads) {
@@ -251,7 +254,7 @@ __device__ void quantize_values_slice(const QuantArgs& a, int64_t head, int64_t 
       const float mn = h2f(from_order_key(lo));
       const float mx = h2f(from_order_key(hi));
       const uint16_t sh = f2h((mx - mn) / (float)MASK);
-      const int64_t m_off = (head * a.c.t_cap + g * G + t_base + t) * NCG + cg;
+      const int64_t m_off = (gb * G + t_base + t) * NCG + cg;
       a.c.v_scale[m_off] = sh;
       a.c.v_min[m_off] = from_order_key(lo);
       s_mn[p] = mn;
@@ -260,7 +263,7 @@ __device__ void quantize_values_slice(const QuantArgs& a, int64_t head, int64_t 
     }
   }
   __syncthreads();
-  uint32_t* vw = a.c.v_codes + (head * (a.c.t_cap / FPI) + (g * G + t_base) / FPI) * kD;
+  uint32_t* vw = a.c.v_codes + ((gb * G + t_base) / FPI) * kD;
   for (int i = tid; i < (NT / FPI) * kD; i += kThreads) {
     const int w = i / kD, d = i % kD;
     const int cgd = d / G;
@@ -332,16 +335,21 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   const int64_t i = (idx / kD) % n_tok;
   const int64_t head = idx / (kD * n_tok);
   const int64_t t = a.first_group * G + i;
-  const int64_t g = t / G;
+  const int64_t gb = group_block(a.c, head, t / G, G);
+  if (gb < 0) {   // a page outside the pool
+    a.k_out[idx] = a.v_out[idx] = __builtin_nanf("");
+    return;
+  }
+  const int64_t tb = gb * G + t % G;   // the token's row in the block layout
   // key
   {
-    const uint32_t w = a.c.k_codes[(head * a.c.t_cap + t) * (kD / FPI) + d / FPI];
+    const uint32_t w = a.c.k_codes[tb * (kD / FPI) + d / FPI];
     uint32_t q = (w >> (BITS * (d % FPI))) & MASK;
-    const int64_t m_off = (head * (a.c.t_cap / G) + g) * kD + d;
+    const int64_t m_off = gb * kD + d;
     if (a.n_boost > 0) {
       const int r = a.c.k_bidx[m_off];
       if (r < a.n_boost) {
-        const uint32_t hw = a.c.k_hi[(head * a.c.t_cap + t) * (a.n_boost / 16) + r / 16];
+        const uint32_t hw = a.c.k_hi[tb * (a.n_boost / 16) + r / 16];
         q |= ((hw >> (2 * (r % 16))) & 3u) << 2;
       }
     }
@@ -350,9 +358,9 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   }
   // value
   {
-    const uint32_t w = a.c.v_codes[(head * (a.c.t_cap / FPI) + t / FPI) * kD + d];
+    const uint32_t w = a.c.v_codes[(tb / FPI) * kD + d];
     const uint32_t q = (w >> (BITS * (t % FPI))) & MASK;
-    const int64_t m_off = (head * a.c.t_cap + t) * (kD / G) + d / G;
+    const int64_t m_off = tb * (kD / G) + d / G;
     const float prod = (float)q * h2f(a.c.v_scale[m_off]);
     a.v_out[idx] = prod + h2f(a.c.v_min[m_off]);
   }

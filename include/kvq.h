@@ -47,6 +47,17 @@
  *  Keys are packed along the channel axis and values along the token axis:
  *  the contraction axis of q.K^T and p.V, so one word feeds one lane's
  *  matrix-core operand directly.
+ *  Every array above is a sequence of per-group blocks: group g of head h is
+ *  block h*(t_cap/G) + g.
+ *
+ * Paged layout (Kitty page, section 4.1: a page holds one group of tokens;
+ * PagedAttention-style serving).  With cache.page_table != NULL the arrays
+ * are a pool of t_cap/G one-group pages laid out as the blocks above, and
+ * group g of head h lives in page page_table[h*pt_stride + g].  Every call
+ * reads (and the quantize calls write) only the table entries of the groups
+ * it touches; an entry outside [0, t_cap/G) is never dereferenced: the
+ * quantize calls skip that group and the decode calls return NaN for that
+ * head's query rows.
  *
  * Conventions
  *  - fp16 data is passed as raw uint16_t bit patterns.
@@ -93,7 +104,10 @@ typedef struct kvq_qcfg {
 } kvq_qcfg;
 
 /* Packed cache, layout above.  k_hi / k_bidx may be NULL when n_boost == 0.
- * t_cap must be a positive multiple of G. */
+ * t_cap must be a positive multiple of G.
+ *  page_table: NULL (contiguous: t_cap tokens per head) or device int32
+ *      [heads][pt_stride] (paged: t_cap/G pages in the pool); pt_stride must
+ *      cover every group a call touches. */
 typedef struct kvq_cache {
   int32_t* k_codes;
   uint16_t* k_scale;
@@ -104,6 +118,8 @@ typedef struct kvq_cache {
   uint16_t* v_scale;
   uint16_t* v_min;
   int64_t t_cap;
+  const int32_t* page_table;
+  int64_t pt_stride;
 } kvq_cache;
 
 /* An fp16 window of full-precision tokens (sink or residual): k and v are

@@ -42,7 +42,7 @@ def _cfg(bits=2, group=128, D=128, nb=0):
 
 def _cache(t_cap=1024, align=0, hi=FAKE):
     p = FAKE + align
-    return kvq.kvq_cache(p, p, p, hi, hi, p, p, p, t_cap)
+    return kvq.kvq_cache(p, p, p, hi, hi, p, p, p, t_cap, None, 0)
 
 
 def _quant(cfg, cache, B=1, H=1, k=FAKE, v=FAKE, stride=128 * 128, fg=0, ng=1):
@@ -64,6 +64,22 @@ def _quant(cfg, cache, B=1, H=1, k=FAKE, v=FAKE, stride=128 * 128, fg=0, ng=1):
 ])
 def test_quantize_rejects_bad_config(cfg, want):
     assert _quant(cfg, _cache()) == want
+
+
+def test_paged_cache_validation():
+    """A page table needs a positive row stride, 4-byte alignment, and rows long
+    enough for every group a call touches (checked before any launch)."""
+    cfg = _cfg()
+    def paged(stride, table=FAKE, t_cap=1024):
+        return kvq.kvq_cache(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, t_cap, table, stride)
+    assert _quant(cfg, paged(0)) == kvq.KVQ_ERR_ARG
+    assert _quant(cfg, paged(-4)) == kvq.KVQ_ERR_ARG
+    assert _quant(cfg, paged(8, table=FAKE + 2)) == kvq.KVQ_ERR_ALIGN
+    assert _quant(cfg, paged(4), fg=3, ng=2) == kvq.KVQ_ERR_ARG      # group 4 past the rows
+    # the pool size (t_cap) does not bound group indices in a paged cache
+    assert _quant(cfg, paged(64, t_cap=256), fg=40, ng=1, k=None) == kvq.KVQ_ERR_ARG  # k checked
+    # decode: the quantized groups must fit the rows
+    assert _decode(cache=paged(4), nq=5 * 128) == kvq.KVQ_ERR_ARG
 
 
 def test_quantize_rejects_bad_arguments():
