@@ -33,7 +33,8 @@ KVQ_WS_COUNTER_BYTES = 262144
 
 EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_step",
-            "kvq_decode_partials", "kvq_decode_merge", "kvq_dequantize")
+            "kvq_decode_partials", "kvq_decode_merge", "kvq_dequantize",
+            "kvq_decode_attention_ragged", "kvq_decode_partials_ragged")
 
 
 class kvq_qcfg(ctypes.Structure):
@@ -76,6 +77,12 @@ _lib.kvq_decode_partials.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P,
 _lib.kvq_decode_partials.restype = ctypes.c_int
 _lib.kvq_decode_merge.argtypes = [_i32, _i32, _i32, _P, _sz, _P, _P]
 _lib.kvq_decode_merge.restype = ctypes.c_int
+_lib.kvq_decode_attention_ragged.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _P, _P,
+                                             _f32, _i32, _P, _sz, _P, _P]
+_lib.kvq_decode_attention_ragged.restype = ctypes.c_int
+_lib.kvq_decode_partials_ragged.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _P, _P,
+                                            _f32, _i32, _P, _sz, _P, _P]
+_lib.kvq_decode_partials_ragged.restype = ctypes.c_int
 _lib.kvq_dequantize.argtypes = [_P, _P, _i32, _i32, _i64, _i64, _P, _P, _P]
 _lib.kvq_dequantize.restype = ctypes.c_int
 
@@ -284,6 +291,24 @@ def kvq_decode_partials(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int,
         _ptr(workspace), workspace.numel() * workspace.element_size(), ctypes.byref(n_parts),
         _stream(stream)), "kvq_decode_partials")
     return n_parts.value
+
+
+def kvq_decode_attention_ragged(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int,
+                                q: torch.Tensor, n_quant_tokens: int,
+                                sink: kvq_window | None, res: kvq_window | None,
+                                seq_quant: torch.Tensor | None, seq_res: torch.Tensor | None,
+                                out: torch.Tensor, workspace: torch.Tensor,
+                                sm_scale: float = 0.0, n_chunks: int = 0, stream=None) -> None:
+    """Decode with per-sequence lengths (device int32 ``[B]`` tensors or None);
+    ``n_quant_tokens`` is the batch's maximum."""
+    c_cfg, c_cache = cfg.c(), cache.c()
+    _check(_lib.kvq_decode_attention_ragged(
+        ctypes.byref(c_cfg), ctypes.byref(c_cache), B, H_q, H_kv, _ptr(q), n_quant_tokens,
+        ctypes.byref(sink) if sink is not None else None,
+        ctypes.byref(res) if res is not None else None, _ptr(seq_quant), _ptr(seq_res),
+        float(sm_scale), int(n_chunks), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)),
+        "kvq_decode_attention_ragged")
 
 
 def kvq_decode_merge(B: int, H_q: int, n_parts: int, workspace: torch.Tensor,

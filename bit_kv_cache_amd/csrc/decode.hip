@@ -151,13 +151,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
   if (part < a.n_chunks) {
     const int64_t gb = (int64_t)part * a.groups_per_chunk;
-    const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
+    const int64_t ge = min<int64_t>(seq_groups(a, b, G), gb + a.groups_per_chunk);
     for (int64_t g = gb; g < ge && !s.bad; g += kBlockTok / G) {
       const int ng = (int)min<int64_t>(kBlockTok / G, ge - g);
       quant_block<BITS, G, GQA>(a, s, head, g * G, ng * G, acc);
     }
   } else {
-    const int n_win = a.n_sink + a.n_res;
+    const int n_win = a.n_sink + seq_res(a, b);
     for (int u = 0; u < n_win; u += kBlockTok)
       window_block<GQA>(a, s, head, u, min(kBlockTok, n_win - u), acc);
   }

@@ -602,7 +602,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   const int64_t b = b32, hk = hk32;
   const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
-  const int ngc = (int)max<int64_t>(0, min<int64_t>(a.n_groups, gb + a.groups_per_chunk) - gb);
+  const int ngc = (int)max<int64_t>(0, min<int64_t>(seq_groups(a, b, kG), gb + a.groups_per_chunk) - gb);
   // slice of the appended group this block quantizes (-1: none)
   const int app_slice = (!KITTY && a.append && chunk < 4) ? chunk : -1;
 
@@ -731,7 +731,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
 
     // This block's slice [u0, u1) of the fp16 window (sink | residual);
     // consumer w takes 16-token tiles w, w + kConsumers, ...
-    const int n_win = a.n_sink + a.n_res;
+    const int n_win = a.n_sink + seq_res(a, b);
     const int wpc = n_win > 0 ? (n_win + a.n_chunks - 1) / a.n_chunks : 0;
     const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
     const int kq = lane >> 4, m_row = lane & 15;

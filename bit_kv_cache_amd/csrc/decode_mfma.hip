@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
   // The wave's first group is requested before anything else, so its latency
   // overlaps the window slice and the operand set-up below.
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
-  const int64_t ge = min<int64_t>(a.n_groups, gb + a.groups_per_chunk);
+  const int64_t ge = min<int64_t>(seq_groups(a, b, kG), gb + a.groups_per_chunk);
   const int ph = lane >> 4;
   const int pc = lane & 3, pkq = (lane >> 2) & 3;
   LaneOffsets<BITS> lo;
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
 #pragma unroll
   for (int i = 0; i < 8; ++i) wacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
-    const int n_win = a.n_sink + a.n_res;
+    const int n_win = a.n_sink + seq_res(a, b);
     const int wpc = (n_win + a.n_chunks - 1) / a.n_chunks;
     const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
     auto row = [&](const uint16_t* sink, const uint16_t* res, int u) -> const uint16_t* {

@@ -222,6 +222,8 @@ kvq_status prepare_decode(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
                                                                                      : nc + 1;
   a->counters = nullptr;
   a->append = 0;
+  a->seq_quant = nullptr;
+  a->seq_res = nullptr;
   return KVQ_OK;
 }
 
@@ -304,6 +306,48 @@ kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int3
   if (st != KVQ_OK) return st;
   if (!n_parts) return KVQ_ERR_ARG;
   *n_parts = a.n_parts;
+  return hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_attention_ragged(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                                       int32_t H_q, int32_t H_kv, const uint16_t* q,
+                                       int64_t n_quant_tokens, const kvq_window* sink,
+                                       const kvq_window* res, const int32_t* seq_quant_tokens,
+                                       const int32_t* seq_res_tokens, float sm_scale,
+                                       int32_t n_chunks, void* workspace, size_t ws_bytes,
+                                       float* out, void* stream) {
+  kvq::DecodeArgs a;
+  kvq_status st = prepare_decode(cfg, cache, B, H_q, H_kv, q, n_quant_tokens, sink, res,
+                                 sm_scale, n_chunks, workspace, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!out) return KVQ_ERR_ARG;
+  if (!aligned16(out)) return KVQ_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(seq_quant_tokens) | reinterpret_cast<uintptr_t>(seq_res_tokens)) & 3u)
+    return KVQ_ERR_ALIGN;
+  a.out = out;
+  a.seq_quant = seq_quant_tokens;
+  a.seq_res = seq_res_tokens;
+  return decode_and_merge(cfg, a, workspace, static_cast<hipStream_t>(stream));
+}
+
+kvq_status kvq_decode_partials_ragged(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                                      int32_t H_q, int32_t H_kv, const uint16_t* q,
+                                      int64_t n_quant_tokens, const kvq_window* sink,
+                                      const kvq_window* res, const int32_t* seq_quant_tokens,
+                                      const int32_t* seq_res_tokens, float sm_scale,
+                                      int32_t n_chunks, void* workspace, size_t ws_bytes,
+                                      int32_t* n_parts, void* stream) {
+  kvq::DecodeArgs a;
+  kvq_status st = prepare_decode(cfg, cache, B, H_q, H_kv, q, n_quant_tokens, sink, res,
+                                 sm_scale, n_chunks, workspace, ws_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!n_parts) return KVQ_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(seq_quant_tokens) | reinterpret_cast<uintptr_t>(seq_res_tokens)) & 3u)
+    return KVQ_ERR_ALIGN;
+  *n_parts = a.n_parts;
+  a.seq_quant = seq_quant_tokens;
+  a.seq_res = seq_res_tokens;
   return hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a,
                                                 static_cast<hipStream_t>(stream)));
 }

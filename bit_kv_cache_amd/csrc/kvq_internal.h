@@ -101,7 +101,27 @@ struct DecodeArgs {
   // Nonzero: the split-K kernel also quantizes rows 0..G-1 of every head's
   // residual window into cache group n_groups (the streaming append).
   int32_t append;
+  // Per-sequence lengths (device int32 [B], or NULL for the uniform n_groups *
+  // G / n_res): quantized tokens and residual tokens of sequence b.
+  const int32_t* seq_quant;
+  const int32_t* seq_res;
 };
+
+// Quantized groups and residual tokens of sequence b: the per-sequence
+// lengths when given (read as scalar loads, clamped into [0, n_groups] and
+// [0, n_res] so no value can move an access past the planned range), else the
+// launch's uniform ones.
+typedef __attribute__((address_space(4))) const int32_t* ConstI32;
+__device__ __forceinline__ int64_t seq_groups(const DecodeArgs& a, int64_t b, int G) {
+  if (!a.seq_quant) return a.n_groups;
+  const int64_t n = ((ConstI32)(uintptr_t)a.seq_quant)[b] / G;
+  return n < 0 ? 0 : (n > a.n_groups ? a.n_groups : n);
+}
+__device__ __forceinline__ int seq_res(const DecodeArgs& a, int64_t b) {
+  if (!a.seq_res) return a.n_res;
+  const int n = ((ConstI32)(uintptr_t)a.seq_res)[b];
+  return n < 0 ? 0 : (n > a.n_res ? a.n_res : n);
+}
 
 // Bytes of arrival counters at the start of a decode workspace (one int per
 // (batch, kv head) for up to 65536 of them); the partials follow.

@@ -244,6 +244,32 @@ kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int3
 kvq_status kvq_decode_merge(int32_t B, int32_t H_q, int32_t n_parts, const float* workspace,
                             size_t ws_bytes, float* out, void* stream);
 
+/* Ragged batches: kvq_decode_attention and kvq_decode_partials where sequence
+ * b attends to its own number of cached and residual tokens (serving with
+ * sequences of different lengths, typically with a paged cache).
+ *  seq_quant_tokens: device int32 [B] or NULL: quantized tokens of sequence b
+ *      (rounded down to a multiple of G, clamped into [0, n_quant_tokens]);
+ *      n_quant_tokens is the batch's maximum and sizes the split-K plan.
+ *  seq_res_tokens: device int32 [B] or NULL: residual tokens of sequence b
+ *      (clamped into [0, res->n]).
+ * Everything else as in the uniform calls; the clamps keep every access
+ * inside the uniform call's range whatever the arrays hold. */
+kvq_status kvq_decode_attention_ragged(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                                       int32_t H_q, int32_t H_kv, const uint16_t* q,
+                                       int64_t n_quant_tokens, const kvq_window* sink,
+                                       const kvq_window* res, const int32_t* seq_quant_tokens,
+                                       const int32_t* seq_res_tokens, float sm_scale,
+                                       int32_t n_chunks, void* workspace, size_t ws_bytes,
+                                       float* out, void* stream);
+
+kvq_status kvq_decode_partials_ragged(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                                      int32_t H_q, int32_t H_kv, const uint16_t* q,
+                                      int64_t n_quant_tokens, const kvq_window* sink,
+                                      const kvq_window* res, const int32_t* seq_quant_tokens,
+                                      const int32_t* seq_res_tokens, float sm_scale,
+                                      int32_t n_chunks, void* workspace, size_t ws_bytes,
+                                      int32_t* n_parts, void* stream);
+
 /* Dequantize groups [first_group, first_group + n_groups) of every head to
  * fp32 [B*H_kv][n_groups*G][D] (value = code*scale + min; Kitty page
  * Algorithm 1 for boosted key channels).  For checking the packed cache. */

@@ -82,6 +82,20 @@ def test_paged_cache_validation():
     assert _decode(cache=paged(4), nq=5 * 128) == kvq.KVQ_ERR_ARG
 
 
+def test_ragged_decode_validation():
+    """The per-sequence length arrays must be 4-byte aligned; everything else is
+    validated as in the uniform call (nothing is launched on an error)."""
+    def rag(sq=None, sr=None, out=FAKE, Hq=4):
+        cfg, cache = _cfg(), _cache()
+        return kvq.raw_call("kvq_decode_attention_ragged", ctypes.byref(cfg), ctypes.byref(cache),
+                            1, Hq, 1, FAKE, 1024, None, None, sq, sr, ctypes.c_float(0.0), 0,
+                            FAKE, 1 << 30, out, None)
+    assert rag(sq=FAKE + 2) == kvq.KVQ_ERR_ALIGN
+    assert rag(sr=FAKE + 1) == kvq.KVQ_ERR_ALIGN
+    assert rag(out=None) == kvq.KVQ_ERR_ARG
+    assert rag(Hq=6) == kvq.KVQ_ERR_UNSUPPORTED     # a GQA group of 6 is not built
+
+
 def test_quantize_rejects_bad_arguments():
     cfg = _cfg()
     assert _quant(None, _cache()) == kvq.KVQ_ERR_ARG

@@ -157,3 +157,56 @@ def test_paged_bad_entry_poisons_only_its_head(built, name):
             ref = oracle_decode(w, oracle_quantize(w, inp), inp, w.T).reshape(n, w.gqa, w.D)
             err = float(np.max(np.abs(o[good].cpu().numpy().astype(np.float64) - ref[good])))
             assert err <= TOL, (bad_page, n_chunks, err)
+
+
+def _seq_inputs(inp, b, H_kv):
+    """The inputs of sequence b alone (its kv heads and query rows)."""
+    hs = slice(b * H_kv, (b + 1) * H_kv)
+    out = {k: (v[hs] if torch.is_tensor(v) and k != "q" else v) for k, v in inp.items()}
+    out["q"] = inp["q"][b:b + 1]
+    out["heads"] = inp["heads"][hs]
+    return out
+
+
+@pytest.mark.parametrize("name", CASES)
+@pytest.mark.parametrize("paged", [False, True])
+def test_ragged_batch(built, name, paged):
+    """Sequences of different lengths in one call: sequence b attends to its
+    first seq_quant[b] cached tokens and seq_res[b] residual tokens; each
+    matches the oracle run on that sequence alone.  One sequence has no
+    cached tokens, one a length that is not a multiple of G (rounded down)."""
+    import bit_kv_cache_amd as kvq
+    w = synth.shrink(_w(name), B=3)
+    inp = make_inputs(w)
+    n = len(inp["heads"])
+    ng = w.T // w.G
+    cfg = qcfg(w)
+    if paged:
+        table, n_pages = _table(n, ng, extra=5, seed=23)
+        cache = kvq.Cache.pool(cfg, n_pages, table.cuda())
+    else:
+        cache = kvq.Cache.empty(cfg, n, w.T)
+    kvq.kvq_quantize_pack(cfg, cache, w.B, w.H_kv, inp["k"], inp["v"], 0, ng)
+    seq_quant = [w.T, (ng // 2) * w.G + w.G // 3, 0]
+    seq_res = [w.R, w.R // 3, max(1, w.R // 2)]
+    sq = torch.tensor(seq_quant, dtype=torch.int32, device="cuda")
+    sr = torch.tensor(seq_res, dtype=torch.int32, device="cuda")
+    sink = kvq.window(inp["k_sink"], inp["v_sink"], w.S)
+    res = kvq.window(inp["k_res"], inp["v_res"], w.R)
+    refs = []
+    for b in range(w.B):
+        wb = synth.shrink(w, B=1)
+        ib = _seq_inputs(inp, b, w.H_kv)
+        nq = (seq_quant[b] // w.G) * w.G
+        ocb = oracle_quantize(wb, ib, w.T + w.G)
+        refs.append(oracle_decode(wb, ocb, ib, nq, n_res=seq_res[b]))
+    for n_chunks in (0, 3, 4):
+        _, ws_bytes = kvq.kvq_decode_plan(cfg, w.B, w.H_q, w.H_kv, w.T, n_chunks)
+        ws = kvq.decode_workspace(ws_bytes)
+        out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+        kvq.kvq_decode_attention_ragged(cfg, cache, w.B, w.H_q, w.H_kv, inp["q"].contiguous(), w.T,
+                                        sink, res, sq, sr, out, ws, n_chunks=n_chunks)
+        torch.cuda.synchronize()
+        for b in range(w.B):
+            err = max_err(out[b:b + 1], refs[b])
+            assert err <= TOL, f"{name} paged={paged} n_chunks={n_chunks} seq {b}: {err:.3g}"
