@@ -521,6 +521,9 @@ def main(argv=None):
                      "algorithmic_bytes": dom_bytes,
                      "kernel_avg_us": round(dom_avg * 1e3, 3)},
     }
+    sr = stream_read_ceiling(kvq, torch, alg_split, n_copies, stream)
+    result["stream_read"] = sr
+    result["roofline"]["frac_of_stream_read"] = round(achieved / sr["GBps"], 4)
     if not args.no_cpu_baseline:
         cores, model = _host_info()
         cb = cpu_baseline(w, args.cpu_heads, cores, args.cpu_seconds)
@@ -530,6 +533,45 @@ def main(argv=None):
     if args.calib_copy:
         calib_copy(torch)
     return 0
+
+
+def stream_read_ceiling(kvq, torch, nbytes, n_copies, stream, reps=50):
+    """The bandwidth a plain read reaches over the same bytes as the split-K
+    phase, rotating over as many independent copies as the caches: the best
+    of a sweep over grid size, workgroup size and load kind."""
+    nbytes = (nbytes + 15) // 16 * 16
+    bufs = [torch.full((nbytes // 4,), i, dtype=torch.int32, device="cuda")
+            for i in range(n_copies)]
+    sink = torch.zeros(8192 * 1024, dtype=torch.int32, device="cuda")
+    best = None
+    for mode in (0, 1):
+        for threads in (256, 512, 1024):
+            for blocks in (256, 512, 1024, 2048, 4096, 8192):
+                run = lambda i: kvq.kvq_stream_read(bufs[i % n_copies], sink, blocks, threads,
+                                                    mode, stream=stream)
+                for i in range(2 * n_copies):
+                    run(i)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for i in range(reps):
+                    run(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / reps * 1e3
+                if best is None or us < best[0]:
+                    best = (us, blocks, threads, mode)
+    us, blocks, threads, mode = best
+    gbps = nbytes / (us * 1e-6) / 1e9
+    del bufs, sink
+    return {"kernel": "stream_read_kernel (kvq_stream_read)", "bytes": nbytes,
+            "avg_us": round(us, 3), "GBps": round(gbps, 1),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "best_config": {"blocks": blocks, "threads": threads,
+                            "loads": "non-temporal" if mode else "ordinary"},
+            "sweep": "blocks 256..8192 x threads 256/512/1024 x ordinary/non-temporal loads, "
+                     f"{reps} launches back to back per point"}
 
 
 def calib_copy(torch):

@@ -34,7 +34,7 @@ KVQ_WS_COUNTER_BYTES = 262144
 EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_step",
             "kvq_decode_partials", "kvq_decode_merge", "kvq_dequantize",
-            "kvq_decode_attention_ragged", "kvq_decode_partials_ragged")
+            "kvq_decode_attention_ragged", "kvq_decode_partials_ragged", "kvq_stream_read")
 
 
 class kvq_qcfg(ctypes.Structure):
@@ -84,6 +84,8 @@ _lib.kvq_decode_partials_ragged.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, 
                                             _f32, _i32, _P, _sz, _P, _P]
 _lib.kvq_decode_partials_ragged.restype = ctypes.c_int
 _lib.kvq_dequantize.argtypes = [_P, _P, _i32, _i32, _i64, _i64, _P, _P, _P]
+_lib.kvq_stream_read.argtypes = [_P, _sz, _P, _i32, _i32, _i32, _P]
+_lib.kvq_stream_read.restype = ctypes.c_int
 _lib.kvq_dequantize.restype = ctypes.c_int
 
 
@@ -325,6 +327,16 @@ def kvq_dequantize(cfg: QCfg, cache: Cache, B: int, H_kv: int, first_group: int,
     _check(_lib.kvq_dequantize(ctypes.byref(c_cfg), ctypes.byref(c_cache), B, H_kv,
                                first_group, n_groups, _ptr(k_out), _ptr(v_out),
                                _stream(stream)), "kvq_dequantize")
+
+
+def kvq_stream_read(src: torch.Tensor, sink: torch.Tensor, blocks: int, threads: int,
+                    mode: int = 0, stream=None) -> None:
+    """Read every byte of ``src`` once (a measurement aid: the bandwidth a
+    plain read reaches); ``sink`` holds at least blocks*threads int32."""
+    if sink.numel() < blocks * threads:
+        raise ValueError("sink smaller than blocks*threads words")
+    _check(_lib.kvq_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                blocks, threads, mode, _stream(stream)), "kvq_stream_read")
 
 
 def raw_call(name: str, *args) -> int:

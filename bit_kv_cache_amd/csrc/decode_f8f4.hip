@@ -69,7 +69,6 @@ constexpr int kG = 128;          // tokens per group
 // others consumers.
 template <int GQA, bool KITTY>
 constexpr int block_waves() { return 8; }
-constexpr int kWpt = kD / 16;     // 2-bit key words per token (8)
 constexpr uint32_t kNib = 0x33333333u;
 constexpr float kNegInfF = -__builtin_inff();
 constexpr int kDigits = 4;        // fp8 digits of an A value
@@ -274,9 +273,10 @@ struct Operands {
 // gptr land at LDS byte address lds + 16 i.  Written as an instruction
 // rather than the compiler builtin because the compiler makes every later
 // LDS access wait for all such copies in flight, which would serialize the
-// loader; the loader waits for its copies itself (loader_wait).
+// loader; the loader waits for its copies itself (loader_wait).  The cache
+// is read once per step: the copies are marked non-temporal (streaming).
 __device__ __forceinline__ void dma_1k(uint32_t lds, const void* gptr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr),
                "s"(lds)
                : "memory");
 }

@@ -277,6 +277,19 @@ kvq_status kvq_dequantize(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
                           int64_t first_group, int64_t n_groups, float* k_out, float* v_out,
                           void* stream);
 
+/* Measurement aid, not part of the method: read `bytes` bytes at `src` once
+ * (16-byte loads, `blocks` workgroups of `threads` lanes, each workgroup a
+ * contiguous slice) and write nothing but a word that depends on every byte
+ * into `sink` when it equals an improbable value.  Timing it over the same
+ * bytes as a decode step gives the bandwidth that a plain read reaches on the
+ * chip, the practical ceiling of the decode kernels, which stream every byte
+ * of the cache once.  mode 0: ordinary loads; mode 1: non-temporal loads.
+ * src 16-byte aligned and bytes a multiple of 16 (else KVQ_ERR_ALIGN);
+ * threads a multiple of 64 in [64, 1024], blocks in [1, 2^20], sink holding
+ * blocks*threads words (else KVQ_ERR_ARG). */
+kvq_status kvq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                           int32_t threads, int32_t mode, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

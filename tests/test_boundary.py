@@ -190,3 +190,18 @@ def test_partials_reject_bad_arguments():
     assert p(nq=100) == kvq.KVQ_ERR_ARG
     assert p(q=FAKE + 2) == kvq.KVQ_ERR_ALIGN
     assert p(ws=None) == kvq.KVQ_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, 1024, FAKE, 256, 256, 0), kvq.KVQ_ERR_ARG),
+    ((FAKE, 1024, None, 256, 256, 0), kvq.KVQ_ERR_ARG),
+    ((FAKE + 4, 1024, FAKE, 256, 256, 0), kvq.KVQ_ERR_ALIGN),
+    ((FAKE, 1000, FAKE, 256, 256, 0), kvq.KVQ_ERR_ALIGN),
+    ((FAKE, 1024, FAKE, 256, 96, 0), kvq.KVQ_ERR_ARG),
+    ((FAKE, 1024, FAKE, 256, 2048, 0), kvq.KVQ_ERR_ARG),
+    ((FAKE, 1024, FAKE, 0, 256, 0), kvq.KVQ_ERR_ARG),
+    ((FAKE, 1024, FAKE, (1 << 20) + 1, 256, 0), kvq.KVQ_ERR_ARG),
+    ((FAKE, 1024, FAKE, 256, 256, 2), kvq.KVQ_ERR_ARG),
+])
+def test_stream_read_validation(args, want):
+    assert kvq.raw_call("kvq_stream_read", *args, None) == want
