@@ -75,7 +75,7 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
       for (int h = 0; h < GQA; ++h) dot[h] = 0.f;
 #pragma unroll
       for (int w = 0; w < WPT / 2; ++w) {
-        const uint32_t word = kw[w];
+        const uint32_t word = __builtin_nontemporal_load(kw + w);   // read once per step
 #pragma unroll
         for (int j = 0; j < FPI; ++j) {
           const int c = half * (kD / 2) + w * FPI + j;
@@ -111,7 +111,8 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
     const int te = min(nt, tb + kBlockTok / 2);
     const uint32_t* vw = a.c.v_codes + d;
     for (int tw = tb; tw < te; tw += FPI) {
-      const uint32_t word = vw[((s.gblk[tw / G] * G + tw % G) / FPI) * kD];
+      const uint32_t word =
+          __builtin_nontemporal_load(vw + ((s.gblk[tw / G] * G + tw % G) / FPI) * kD);
 #pragma unroll
       for (int j = 0; j < FPI; ++j) {
         const int t = tw + j;

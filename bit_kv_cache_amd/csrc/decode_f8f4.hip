@@ -40,11 +40,11 @@
 // boosted channels' digit bytes.
 //
 // Work split: block = 8 waves on one (batch, kv head) and one chunk of
-// groups, one block per CU.  Wave 7 is the loader: it copies each group's
+// groups, one block per CU.  Wave 0 is the loader: it copies each group's
 // record (key words, value words, scales and mins, Kitty high bits and
 // boosted rows) straight from HBM into an LDS ring with asynchronous
 // global-to-LDS loads, several groups in flight, and publishes a slot once
-// its data has landed.  Waves 0..6 consume: each claims the next group with
+// its data has landed.  Waves 1..7 consume: each claims the next group with
 // an LDS counter, copies the operands out of the slot (freeing it) and runs
 // both products with its own online softmax.  The block's equal slice of
 // the fp16 sink/residual window runs first, as 16-token fp16 tiles.  The
@@ -65,7 +65,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kG = 128;          // tokens per group
-// One block per CU: 8 waves (two per SIMD), the last the loader, the
+// One block per CU: 8 waves (two per SIMD), the first the loader, the
 // others consumers.
 template <int GQA, bool KITTY>
 constexpr int block_waves() { return 8; }
@@ -606,9 +606,11 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   // slice of the appended group this block quantizes (-1: none)
   const int app_slice = (!KITTY && a.append && chunk < 4) ? chunk : -1;
 
-  // The loader wave sets up the ring's flags, starts its first copies and
-  // only then meets the other waves at the block barrier; consumers run
-  // their fp16 window tiles before it.  Each wave passes it exactly once.
+  // The loader wave sets up the ring's flags and meets the other waves at the
+  // block barrier before its first copy; past it, the loader waits for
+  // nothing but free ring slots (consumers run their fp16 window tiles after
+  // the barrier, while the first groups are on their way).  Each wave passes
+  // it exactly once.
 
   // per-wave online-softmax state (the loader's stays empty)
   float m_run[NH], l_part[NH], mterm[NH];
@@ -640,6 +642,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     }
     // the flags are written before any copy can land on them
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
     // Copies the chunk's groups, in order, into the ring (group j -> slot
     // j % R) with DF groups in flight, and publishes each one once its data
     // is in LDS.  A slot is refilled only after a consumer copied its
@@ -682,13 +685,9 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     // blocks streaming at the same time do not all sit at the same offsets
     // of their heads (and on the same memory channels).
     const int rot = ngc > 0 ? (int)((head32 * 37 + chunk * 17) % ngc) : 0;
-    bool ok = true, met = false;
+    bool ok = true;
     for (int j = 0; j < ngc; ++j) {
       const int s = j % R;
-      if (j == DF - 1) {   // the first DF - 1 groups are on their way
-        __syncthreads();
-        met = true;
-      }
       if (!spin_until(&sh.empty[s], j)) {
         ok = false;
         break;
@@ -714,21 +713,17 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
         dma_flag(__builtin_amdgcn_readfirstlane(ready0 + 4 * s), kSeq.v + (j & (kSeqLen - 1)));
       if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
     }
-    if (!met) __syncthreads();
     vm_wait<0>();
     if ((!ok || bad_page) && lane == 0) lds_store(&sh.stalled, 1);
   } else {
     // ---------------------------------------------------------- consumer waves
+    __syncthreads();   // the loader has set up the ring's flags
     // query, then this wave's first fp16 window tile (requested first, so
     // the window work waits only for them)
     u32x4 qraw[NH];
 #pragma unroll
     for (int j = 0; j < NH; ++j)
       qraw[j] = *reinterpret_cast<const u32x4*>(qrow + (r + 4 * j) * kD + 8 * n);
-    // The append's items, one on each of the last kAppItems consumers: the
-    // loads go out now, the arithmetic runs after the block barrier (the
-    // other consumers take the fp16 window tiles and the first groups).
-
     // This block's slice [u0, u1) of the fp16 window (sink | residual);
     // consumer w takes 16-token tiles w, w + kConsumers, ...
     const int n_win = a.n_sink + seq_res(a, b);
@@ -1097,7 +1092,6 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       }
     };
 
-    __syncthreads();   // the loader has set up the ring's flags
     // the append's items first (the waves that get here first take them)
     if (app_slice >= 0) {
       for (;;) {
