@@ -72,15 +72,15 @@ def _load():
     lib.oracle_quantize_group.argtypes = [P, i64, i64, i32, P, P, P]
     lib.oracle_pack.argtypes = [P, i64, i32, P]
     lib.oracle_unpack.argtypes = [P, i64, i32, P]
-    lib.oracle_quantize_pack.argtypes = [i32, i32, i32, i32, i64] + [P] * 8 + [
+    lib.oracle_quantize_pack.argtypes = [i32, i32, i32, i32, i32, i32, i64] + [P] * 8 + [
         i64, P, P, i64, i64, i64, i32]
     lib.oracle_quantize_pack.restype = i32
-    lib.oracle_dequantize.argtypes = [i32, i32, i32, i32, i64] + [P] * 8 + [
+    lib.oracle_dequantize.argtypes = [i32, i32, i32, i32, i32, i32, i64] + [P] * 8 + [
         i64, i64, i64, P, P, i32]
     lib.oracle_dequantize.restype = i32
     lib.oracle_attention_fp64.argtypes = [P, P, P, i64, i32, f64, P]
     lib.oracle_attention_split_merge.argtypes = [P, P, P, i64, i32, f64, i64, P]
-    lib.oracle_decode_attention.argtypes = [i32, i32, i32, i32, i64] + [P] * 8 + [
+    lib.oracle_decode_attention.argtypes = [i32, i32, i32, i32, i32, i32, i64] + [P] * 8 + [
         i32, i32, i32, P, i64, P, P, i32, i32, P, P, i32, i32, f64, P, i32]
     lib.oracle_decode_attention.restype = i32
     _lib = lib
@@ -180,20 +180,34 @@ class Cache:
     v_words: np.ndarray
     v_scale: np.ndarray
     v_min: np.ndarray
+    v_bits: int = 0       # value code width (0: the key width)
+    score: int = 0        # Kitty channel importance: 0 range, 1 mean |x|
+
+    @property
+    def vb(self) -> int:
+        return self.v_bits or self.bits
 
     @property
     def fpi(self) -> int:
+        """Key codes per word."""
         return 32 // self.bits
 
+    @property
+    def v_fpi(self) -> int:
+        """Value codes per word."""
+        return 32 // self.vb
+
     def _args(self):
-        return [self.bits, self.group, self.head_dim, self.n_boost, self.t_cap,
+        return [self.bits, self.vb, self.group, self.head_dim, self.n_boost, self.score,
+                self.t_cap,
                 _ptr(self.k_words), _ptr(self.k_scale), _ptr(self.k_min), _ptr(self.k_hi),
                 _ptr(self.k_bidx), _ptr(self.v_words), _ptr(self.v_scale), _ptr(self.v_min)]
 
 
 def empty_cache(bits: int, group: int, head_dim: int, n_boost: int, t_cap: int,
-                n_heads: int) -> Cache:
-    fpi = 32 // bits
+                n_heads: int, v_bits: int = 0, score: int = 0) -> Cache:
+    """Key codes of ``bits`` bits, value codes of ``v_bits`` (0: the same)."""
+    fpi, v_fpi = 32 // bits, 32 // (v_bits or bits)
     H, T, D, G = n_heads, t_cap, head_dim, group
     return Cache(
         bits, group, head_dim, n_boost, t_cap, n_heads,
@@ -202,9 +216,10 @@ def empty_cache(bits: int, group: int, head_dim: int, n_boost: int, t_cap: int,
         k_min=np.zeros((H, T // G, D), np.uint16),
         k_hi=np.zeros((H, T, n_boost // 16), np.uint32) if n_boost else None,
         k_bidx=np.zeros((H, T // G, D), np.uint8) if n_boost else None,
-        v_words=np.zeros((H, T // fpi, D), np.uint32),
+        v_words=np.zeros((H, T // v_fpi, D), np.uint32),
         v_scale=np.zeros((H, T, D // G), np.uint16),
         v_min=np.zeros((H, T, D // G), np.uint16),
+        v_bits=v_bits, score=score,
     )
 
 

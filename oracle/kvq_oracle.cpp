@@ -36,7 +36,10 @@
 //    page's least-significant-first bit order;
 //  * Kitty channel choice: the n_boost channels with the largest per-group
 //    range (ties to the lower channel), boosted rows stored in ascending
-//    channel order, sentinel = n_boost;
+//    channel order, sentinel = n_boost; or, by choice, the largest mean
+//    magnitude over the group's tokens (section 3.2's heuristic, its T read
+//    as the tokens being quantized: the page quantizes a full page at once);
+//  * key and value code widths may differ (section 3.1's K2V4 and K4V2);
 //  * attention covers sink + quantized + residual tokens, sm_scale defaults
 //    to 1/sqrt(D), query head h reads kv head h / (H_q/H_kv).
 //
@@ -193,18 +196,20 @@ void oracle_unpack(const uint32_t* words, int64_t n_codes, int32_t bits, uint8_t
 }
 
 // ---------------------------------------------------------------------------
-// The packed cache.  Per head (head = b*H_kv + h_kv), t_cap token slots:
+// The packed cache.  Per head (head = b*H_kv + h_kv), t_cap token slots; keys
+// and values may use different code widths (Kitty page, section 3.1: K2V4
+// and K4V2), fpi = 32/bits for keys and v_fpi = 32/v_bits for values:
 //   K words  [t_cap][D/fpi]     word (t,w): channels w*fpi+j of token t
 //   K scale  [t_cap/G][D] fp16  K min [t_cap/G][D] fp16
 //   K hi     [t_cap][n_boost/16] word (t,w): high bits of boosted rows w*16+j
 //   K bidx   [t_cap/G][D] u8    boosted row of channel d, or n_boost
-//   V words  [t_cap/fpi][D]     word (w,d): tokens w*fpi+j of channel d
+//   V words  [t_cap/v_fpi][D]   word (w,d): tokens w*v_fpi+j of channel d
 //   V scale  [t_cap][D/G] fp16  V min [t_cap][D/G] fp16
 // ---------------------------------------------------------------------------
 
 struct Layout {
-  int32_t bits, G, D, n_boost;
-  int64_t t_cap, fpi;
+  int32_t bits, v_bits, G, D, n_boost, score;
+  int64_t t_cap, fpi, v_fpi;
   uint32_t* k_words;
   uint16_t* k_scale;
   uint16_t* k_min;
@@ -220,19 +225,32 @@ struct Layout {
     return (hd * t_cap + t) * (n_boost / 16) + w;
   }
   int64_t vw(int64_t hd, int64_t w, int64_t d) const {
-    return (hd * (t_cap / fpi) + w) * D + d;
+    return (hd * (t_cap / v_fpi) + w) * D + d;
   }
   int64_t vm(int64_t hd, int64_t t, int64_t c) const { return (hd * t_cap + t) * (D / G) + c; }
 };
 
-static int check_cfg(int32_t bits, int32_t G, int32_t D, int32_t n_boost, int64_t t_cap) {
-  if (bits != 2 && bits != 4 && bits != 8) return -1;
-  const int32_t fpi = 32 / bits;
-  if (G <= 0 || D <= 0 || G % fpi || D % fpi || D % G || t_cap % G) return -1;
+// score: how the Kitty boost ranks key channels (0: range over the group,
+// 1: mean magnitude over the group's tokens).
+static int check_cfg(int32_t bits, int32_t v_bits, int32_t G, int32_t D, int32_t n_boost,
+                     int32_t score, int64_t t_cap) {
+  if (G <= 0 || D <= 0 || D % G || t_cap % G) return -1;
+  for (const int32_t b : {bits, v_bits}) {
+    if (b != 2 && b != 4 && b != 8) return -1;
+    if (G % (32 / b) || D % (32 / b)) return -1;
+  }
   if (n_boost < 0 || n_boost > D || n_boost % 16) return -1;
-  if (n_boost > 0 && bits != 2) return -1;
+  if (n_boost > 0 && (bits != 2 || v_bits != 2)) return -1;   // Kitty: K2 boosted, V2
+  if (score != 0 && score != 1) return -1;
   return 0;
 }
+
+#define LAYOUT(bits, v_bits, G, D, n_boost, score, t_cap)                                  \
+  Layout L{bits, v_bits, G, D, n_boost, score, t_cap, 32 / (bits), 32 / (v_bits),            \
+           const_cast<uint32_t*>(k_words), const_cast<uint16_t*>(k_scale),                  \
+           const_cast<uint16_t*>(k_min), const_cast<uint32_t*>(k_hi),                       \
+           const_cast<uint8_t*>(k_bidx), const_cast<uint32_t*>(v_words),                    \
+           const_cast<uint16_t*>(v_scale), const_cast<uint16_t*>(v_min)}
 
 // Quantize + pack one key group of one head: rows src[j*D + d], j < G.
 static void quantize_key_group(const Layout& L, int64_t hd, int64_t g, const uint16_t* src) {
@@ -244,13 +262,29 @@ static void quantize_key_group(const Layout& L, int64_t hd, int64_t g, const uin
     oracle_group_minmax(src + d, G, D, &mn[d], &mx[d]);
     range[d] = oracle_group_range(mn[d], mx[d]);
   }
-  // Kitty: the n_boost channels of largest range get 4-bit codes.
+  // Kitty: the n_boost most important channels get 4-bit codes (ties to the
+  // lower channel).  Importance is the channel's range over the group, or
+  // (score 1) its mean magnitude over the group's tokens (Kitty page, section
+  // 3.2, the magnitude heuristic s_i), ranked by the sum of |x|: the same
+  // order, G being common to every channel, and exact in fp64 (each |x| is a
+  // multiple of 2^-24 below 2^16, and G <= D = 128 of them need at most 47
+  // significant bits).
+  std::vector<double> imp(D);
+  for (int32_t d = 0; d < D; ++d) {
+    if (L.score == 0) {
+      imp[d] = range[d];
+    } else {
+      double sum = 0.0;
+      for (int32_t j = 0; j < G; ++j) sum += std::fabs(oracle_f16_to_f64(src[j * D + d]));
+      imp[d] = sum;
+    }
+  }
   std::vector<int32_t> row(D, L.n_boost);
   if (L.n_boost > 0) {
     std::vector<int32_t> order(D);
     for (int32_t d = 0; d < D; ++d) order[d] = d;
     std::stable_sort(order.begin(), order.end(),
-                     [&](int32_t a, int32_t b) { return range[a] > range[b]; });
+                     [&](int32_t a, int32_t b) { return imp[a] > imp[b]; });
     std::vector<int32_t> chosen(order.begin(), order.begin() + L.n_boost);
     std::sort(chosen.begin(), chosen.end());
     for (int32_t r = 0; r < L.n_boost; ++r) row[chosen[r]] = r;
@@ -288,18 +322,18 @@ static void quantize_value_group(const Layout& L, int64_t hd, int64_t g, const u
     const int64_t t = g * G + j;
     for (int32_t c = 0; c < D / G; ++c) {
       uint16_t mn, s;
-      oracle_quantize_group(src + (size_t)j * D + c * G, G, 1, L.bits, &mn, &s,
+      oracle_quantize_group(src + (size_t)j * D + c * G, G, 1, L.v_bits, &mn, &s,
                             &codes[(size_t)j * D + c * G]);
       L.v_scale[L.vm(hd, t, c)] = s;
       L.v_min[L.vm(hd, t, c)] = mn;
     }
   }
-  std::vector<uint8_t> col(L.fpi);
+  std::vector<uint8_t> col(L.v_fpi);
   for (int32_t d = 0; d < D; ++d)
-    for (int64_t w0 = 0; w0 < G / L.fpi; ++w0) {
-      for (int64_t j = 0; j < L.fpi; ++j) col[j] = codes[(size_t)(w0 * L.fpi + j) * D + d];
-      const int64_t w = (g * G) / L.fpi + w0;
-      oracle_pack(col.data(), L.fpi, L.bits, &L.v_words[L.vw(hd, w, d)]);
+    for (int64_t w0 = 0; w0 < G / L.v_fpi; ++w0) {
+      for (int64_t j = 0; j < L.v_fpi; ++j) col[j] = codes[(size_t)(w0 * L.v_fpi + j) * D + d];
+      const int64_t w = (g * G) / L.v_fpi + w0;
+      oracle_pack(col.data(), L.v_fpi, L.v_bits, &L.v_words[L.vw(hd, w, d)]);
     }
 }
 
@@ -309,16 +343,16 @@ static void run_heads(int64_t n_heads, int32_t n_threads,
 // Quantize groups [first_group, first_group + n_groups) of every head from
 // fp16 sources laid out [head][n_groups*G][D] with the given head stride
 // (elements).  Returns 0, or -1 on a bad configuration.
-int oracle_quantize_pack(int32_t bits, int32_t G, int32_t D, int32_t n_boost, int64_t t_cap,
+int oracle_quantize_pack(int32_t bits, int32_t v_bits, int32_t G, int32_t D, int32_t n_boost,
+                         int32_t score, int64_t t_cap,
                          uint32_t* k_words, uint16_t* k_scale, uint16_t* k_min, uint32_t* k_hi,
                          uint8_t* k_bidx, uint32_t* v_words, uint16_t* v_scale, uint16_t* v_min,
                          int64_t n_heads, const uint16_t* k_src, const uint16_t* v_src,
                          int64_t src_head_stride, int64_t first_group, int64_t n_groups,
                          int32_t n_threads) {
-  if (check_cfg(bits, G, D, n_boost, t_cap)) return -1;
+  if (check_cfg(bits, v_bits, G, D, n_boost, score, t_cap)) return -1;
   if (first_group < 0 || n_groups < 0 || (first_group + n_groups) * G > t_cap) return -1;
-  Layout L{bits, G, D, n_boost, t_cap, 32 / bits, k_words, k_scale, k_min, k_hi,
-           k_bidx, v_words, v_scale, v_min};
+  LAYOUT(bits, v_bits, G, D, n_boost, score, t_cap);
   run_heads(n_heads, n_threads, [&](int64_t hd) {
     for (int64_t i = 0; i < n_groups; ++i) {
       const int64_t g = first_group + i;
@@ -347,27 +381,24 @@ static float key_at(const Layout& L, int64_t hd, int64_t t, int32_t d) {
 }
 
 static float value_at(const Layout& L, int64_t hd, int64_t t, int32_t d) {
-  const uint32_t w = L.v_words[L.vw(hd, t / L.fpi, d)];
-  const int32_t q = (int32_t)((w >> (L.bits * (t % L.fpi))) & ((1u << L.bits) - 1u));
+  const uint32_t w = L.v_words[L.vw(hd, t / L.v_fpi, d)];
+  const int32_t q = (int32_t)((w >> (L.v_bits * (t % L.v_fpi))) & ((1u << L.v_bits) - 1u));
   const int64_t c = d / L.G;
   return oracle_dequant(q, L.v_scale[L.vm(hd, t, c)], L.v_min[L.vm(hd, t, c)]);
 }
 
 // fp32 dequantized K and V of groups [first_group, first_group+n_groups),
 // written [head][n_groups*G][D].
-int oracle_dequantize(int32_t bits, int32_t G, int32_t D, int32_t n_boost, int64_t t_cap,
+int oracle_dequantize(int32_t bits, int32_t v_bits, int32_t G, int32_t D, int32_t n_boost,
+                      int32_t score, int64_t t_cap,
                       const uint32_t* k_words, const uint16_t* k_scale, const uint16_t* k_min,
                       const uint32_t* k_hi, const uint8_t* k_bidx, const uint32_t* v_words,
                       const uint16_t* v_scale, const uint16_t* v_min, int64_t n_heads,
                       int64_t first_group, int64_t n_groups, float* k_out, float* v_out,
                       int32_t n_threads) {
-  if (check_cfg(bits, G, D, n_boost, t_cap)) return -1;
+  if (check_cfg(bits, v_bits, G, D, n_boost, score, t_cap)) return -1;
   if (first_group < 0 || n_groups < 0 || (first_group + n_groups) * G > t_cap) return -1;
-  Layout L{bits, G, D, n_boost, t_cap, 32 / bits,
-           const_cast<uint32_t*>(k_words), const_cast<uint16_t*>(k_scale),
-           const_cast<uint16_t*>(k_min), const_cast<uint32_t*>(k_hi),
-           const_cast<uint8_t*>(k_bidx), const_cast<uint32_t*>(v_words),
-           const_cast<uint16_t*>(v_scale), const_cast<uint16_t*>(v_min)};
+  LAYOUT(bits, v_bits, G, D, n_boost, score, t_cap);
   const int64_t n_tok = n_groups * G;
   run_heads(n_heads, n_threads, [&](int64_t hd) {
     for (int64_t i = 0; i < n_tok; ++i) {
@@ -451,7 +482,8 @@ void oracle_attention_split_merge(const double* q, const double* K, const double
 // (dequantized as above), and n_res fp16 residual rows; its kv head is
 // h / (H_q / H_kv).  Windows are [head][cap][D] fp16 (either may be null
 // when its count is 0).  sm <= 0 selects 1/sqrt(D).  out: [B][H_q][D] fp64.
-int oracle_decode_attention(int32_t bits, int32_t G, int32_t D, int32_t n_boost, int64_t t_cap,
+int oracle_decode_attention(int32_t bits, int32_t v_bits, int32_t G, int32_t D, int32_t n_boost,
+                            int32_t score, int64_t t_cap,
                             const uint32_t* k_words, const uint16_t* k_scale,
                             const uint16_t* k_min, const uint32_t* k_hi, const uint8_t* k_bidx,
                             const uint32_t* v_words, const uint16_t* v_scale,
@@ -460,15 +492,11 @@ int oracle_decode_attention(int32_t bits, int32_t G, int32_t D, int32_t n_boost,
                             const uint16_t* v_sink, int32_t n_sink, int32_t sink_cap,
                             const uint16_t* k_res, const uint16_t* v_res, int32_t n_res,
                             int32_t res_cap, double sm, double* out, int32_t n_threads) {
-  if (check_cfg(bits, G, D, n_boost, t_cap)) return -1;
+  if (check_cfg(bits, v_bits, G, D, n_boost, score, t_cap)) return -1;
   if (B <= 0 || H_kv <= 0 || H_q % H_kv || n_quant < 0 || n_quant % G || n_quant > t_cap)
     return -1;
   if (n_sink < 0 || n_sink > sink_cap || n_res < 0 || n_res > res_cap) return -1;
-  Layout L{bits, G, D, n_boost, t_cap, 32 / bits,
-           const_cast<uint32_t*>(k_words), const_cast<uint16_t*>(k_scale),
-           const_cast<uint16_t*>(k_min), const_cast<uint32_t*>(k_hi),
-           const_cast<uint8_t*>(k_bidx), const_cast<uint32_t*>(v_words),
-           const_cast<uint16_t*>(v_scale), const_cast<uint16_t*>(v_min)};
+  LAYOUT(bits, v_bits, G, D, n_boost, score, t_cap);
   if (sm <= 0.0) sm = 1.0 / std::sqrt((double)D);
   const int32_t gq = H_q / H_kv;
   run_heads((int64_t)B * H_kv, n_threads, [&](int64_t hd) {

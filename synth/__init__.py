@@ -40,6 +40,8 @@ class Workload:
     seed: int
     min_chunks: int = 0   # smallest split-K chunk count per head the workload asks for
     note: str = ""
+    v_bits: int = 0       # value code width (0: the key width)
+    boost_score: int = 0  # Kitty channel importance: 0 range, 1 mean |x|
 
     @property
     def heads(self) -> int:

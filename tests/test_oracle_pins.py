@@ -340,6 +340,119 @@ def test_kitty_boosted_set_is_top_range():
                 assert (c.k_min[hd, g, d], c.k_scale[hd, g, d]) == (m, s)
 
 
+def _boosted(c, hd, g, nb):
+    return list(np.nonzero(c.k_bidx[hd, g] < nb)[0])
+
+
+def test_kitty_magnitude_score_hand_group():
+    """Kitty page, section 3.2: with the magnitude score the boosted channels
+    are those of largest mean |x| over the group, not of largest range.
+    Channels 0..15 are one spike of 1000 among zeros (range 1000, mean |x|
+    1000/128); channels 16..23 are constant 50, channels 24..31 constant -60
+    (range 0, mean |x| 50 and 60); the rest lie in (-1, 1)."""
+    rng = np.random.default_rng(12)
+    D, G, nb = 128, 128, 16
+    k = (rng.random((1, G, D)) * 1.8 - 0.9).astype(np.float32)
+    k[0, :, :16] = 0.0
+    k[0, 5, :16] = 1000.0
+    k[0, :, 16:24] = 50.0
+    k[0, :, 24:32] = -60.0
+    kb = k.astype(np.float16).view(np.uint16)
+    vb = np.zeros_like(kb)
+    by_range = oracle.empty_cache(2, G, D, nb, G, 1)
+    oracle.quantize_pack(by_range, kb, vb, 0, 1)
+    assert _boosted(by_range, 0, 0, nb) == list(range(16))
+    by_mag = oracle.empty_cache(2, G, D, nb, G, 1, score=1)
+    oracle.quantize_pack(by_mag, kb, vb, 0, 1)
+    assert _boosted(by_mag, 0, 0, nb) == list(range(16, 32))
+    assert list(by_mag.k_bidx[0, 0, 16:32]) == list(range(16))
+    # a constant channel has scale 0 and decodes to its value exactly
+    kk, _ = oracle.dequantize(by_mag, 0, 1)
+    assert np.all(kk[0, :, 16:24] == 50.0) and np.all(kk[0, :, 24:32] == -60.0)
+
+
+def test_kitty_magnitude_score_ties_and_sign():
+    """Equal sums of |x| tie to the lower channel whatever the signs; a
+    negative channel counts by its magnitude."""
+    D, G, nb = 128, 64, 16
+    k = np.ones((1, G, D), np.float32)
+    k[0, ::2, :] = -1.0                      # every channel: mean |x| = 1
+    k[0, :, 100] = -3.0                      # largest magnitude, all negative
+    kb = k.astype(np.float16).view(np.uint16)
+    c = oracle.empty_cache(2, G, D, nb, G, 1, score=1)
+    oracle.quantize_pack(c, kb, np.zeros_like(kb), 0, 1)
+    assert _boosted(c, 0, 0, nb) == list(range(15)) + [100]
+
+
+def test_kitty_magnitude_score_brute_force():
+    """Random groups: the boosted set equals the top n_boost channels by the
+    sum of |x| (exact rationals here), ties to the lower channel; with
+    n_boost = D both scores give the plain 4-bit cache."""
+    rng = np.random.default_rng(13)
+    D, G, T, heads = 128, 32, 128, 2
+    k, v = _rand_src(rng, heads, T, D, [(7, 12.0), (64, 9.0)])
+    for nb in (16, 32):
+        c = oracle.empty_cache(2, G, D, nb, T, heads, score=1)
+        oracle.quantize_pack(c, k, v, 0, T // G)
+        for hd in range(heads):
+            for g in range(T // G):
+                blk = k[hd, g * G:(g + 1) * G]
+                sums = [sum(Fraction(abs(float(x))) for x in blk[:, d].view(np.float16))
+                        for d in range(D)]
+                order = sorted(range(D), key=lambda d: (-sums[d], d))
+                assert _boosted(c, hd, g, nb) == sorted(order[:nb])
+    full = oracle.empty_cache(2, G, D, D, T, heads, score=1)
+    oracle.quantize_pack(full, k, v, 0, T // G)
+    p4 = oracle.empty_cache(4, G, D, 0, T, heads)
+    oracle.quantize_pack(p4, k, v, 0, T // G)
+    assert np.array_equal(oracle.dequantize(full, 0, T // G)[0], oracle.dequantize(p4, 0, T // G)[0])
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 4), (4, 2), (2, 8)])
+def test_mixed_widths_equal_their_uniform_parts(kb, vb):
+    """Kitty page, section 3.1 (K2V4, K4V2): keys of a mixed cache are the
+    uniform kb-bit cache's keys and its values the uniform vb-bit cache's
+    values, word for word and after dequantization; decode over it equals
+    attention over those dequantized keys and values."""
+    rng = np.random.default_rng(14)
+    D, G, T, heads = 128, 128, 256, 2
+    k, v = _rand_src(rng, heads, T, D, [(3, 15.0)])
+    mix = oracle.empty_cache(kb, G, D, 0, T, heads, v_bits=vb)
+    oracle.quantize_pack(mix, k, v, 0, T // G)
+    ck = oracle.empty_cache(kb, G, D, 0, T, heads)
+    oracle.quantize_pack(ck, k, v, 0, T // G)
+    cv = oracle.empty_cache(vb, G, D, 0, T, heads)
+    oracle.quantize_pack(cv, k, v, 0, T // G)
+    assert mix.v_words.shape == (heads, T * vb // 32, D)
+    for f in ("k_words", "k_scale", "k_min"):
+        assert np.array_equal(getattr(mix, f), getattr(ck, f)), f
+    for f in ("v_words", "v_scale", "v_min"):
+        assert np.array_equal(getattr(mix, f), getattr(cv, f)), f
+    km, vm = oracle.dequantize(mix, 0, T // G)
+    assert np.array_equal(km, oracle.dequantize(ck, 0, T // G)[0])
+    assert np.array_equal(vm, oracle.dequantize(cv, 0, T // G)[1])
+    q = rng.standard_normal((1, 4, D)).astype(np.float16).view(np.uint16)
+    out = oracle.decode_attention(mix, 1, 4, 2, q, T)
+    sm = 1.0 / math.sqrt(D)
+    for h in range(4):
+        ref = oracle.attention_fp64(q[0, h].view(np.float16).astype(np.float64),
+                                    km[h // 2].astype(np.float64), vm[h // 2].astype(np.float64), sm)
+        assert np.allclose(out[0, h], ref, rtol=0, atol=1e-12)
+
+
+def test_mixed_widths_reject_bad_configurations():
+    """A value width that does not divide the group into whole words, or a
+    Kitty boost with values wider than 2 bits, is refused."""
+    rng = np.random.default_rng(15)
+    k, v = _rand_src(rng, 1, 64, 128)
+    with pytest.raises(ValueError):
+        c = oracle.empty_cache(2, 64, 128, 16, 64, 1, v_bits=4)
+        c.k_hi = np.zeros((1, 64, 1), np.uint32)
+        oracle.quantize_pack(c, k, v, 0, 1)
+    with pytest.raises(ValueError):
+        oracle.quantize_pack(oracle.empty_cache(2, 64, 128, 0, 64, 1, v_bits=3), k, v, 0, 1)
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------
