@@ -39,7 +39,8 @@ EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
 
 class kvq_qcfg(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("n_boost", ctypes.c_int32)]
+                ("head_dim", ctypes.c_int32), ("n_boost", ctypes.c_int32),
+                ("v_bits", ctypes.c_int32), ("boost_score", ctypes.c_int32)]
 
 
 class kvq_cache(ctypes.Structure):
@@ -128,9 +129,16 @@ class QCfg:
     group: int = 128
     head_dim: int = 128
     n_boost: int = 0
+    v_bits: int = 0        # value code width (0: the key width)
+    boost_score: int = 0   # Kitty channel importance: 0 range, 1 mean |x|
+
+    @property
+    def vb(self) -> int:
+        return self.v_bits or self.bits
 
     def c(self) -> kvq_qcfg:
-        return kvq_qcfg(self.bits, self.group, self.head_dim, self.n_boost)
+        return kvq_qcfg(self.bits, self.group, self.head_dim, self.n_boost, self.v_bits,
+                        self.boost_score)
 
 
 @dataclass
@@ -155,7 +163,7 @@ class Cache:
 
     @staticmethod
     def empty(cfg: QCfg, heads: int, t_cap: int, device="cuda") -> "Cache":
-        fpi = 32 // cfg.bits
+        fpi, v_fpi = 32 // cfg.bits, 32 // cfg.vb
         D, G, T, H = cfg.head_dim, cfg.group, t_cap, heads
         z = dict(device=device)
         return Cache(
@@ -166,7 +174,7 @@ class Cache:
             k_hi=torch.zeros((H, T, cfg.n_boost // 16), dtype=torch.int32, **z)
             if cfg.n_boost else None,
             k_bidx=torch.zeros((H, T // G, D), dtype=torch.uint8, **z) if cfg.n_boost else None,
-            v_codes=torch.zeros((H, T // fpi, D), dtype=torch.int32, **z),
+            v_codes=torch.zeros((H, T // v_fpi, D), dtype=torch.int32, **z),
             v_scale=torch.zeros((H, T, D // G), dtype=torch.int16, **z),
             v_min=torch.zeros((H, T, D // G), dtype=torch.int16, **z),
         )

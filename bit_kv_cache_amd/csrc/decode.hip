@@ -23,11 +23,12 @@ namespace {
 
 // --------------------------------------------------------- quantized block
 // Tokens [t0, t0+nt) of head `head`, nt a multiple of G, nt <= kBlockTok.
-template <int BITS, int G, int GQA>
+// BITS: key code width, VB: value code width.
+template <int BITS, int VB, int G, int GQA>
 __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int64_t t0, int nt,
                             float (&acc)[GQA]) {
-  constexpr int FPI = 32 / BITS;
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  constexpr int FPI = 32 / BITS, VFPI = 32 / VB;
+  constexpr uint32_t MASK = (1u << BITS) - 1u, VMASK = (1u << VB) - 1u;
   constexpr int WPT = kD / FPI;
   constexpr int NCG = kD / G;
   const int tid = threadIdx.x;
@@ -110,13 +111,13 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
     const int tb = half * (kBlockTok / 2);
     const int te = min(nt, tb + kBlockTok / 2);
     const uint32_t* vw = a.c.v_codes + d;
-    for (int tw = tb; tw < te; tw += FPI) {
+    for (int tw = tb; tw < te; tw += VFPI) {
       const uint32_t word =
-          __builtin_nontemporal_load(vw + ((s.gblk[tw / G] * G + tw % G) / FPI) * kD);
+          __builtin_nontemporal_load(vw + ((s.gblk[tw / G] * G + tw % G) / VFPI) * kD);
 #pragma unroll
-      for (int j = 0; j < FPI; ++j) {
+      for (int j = 0; j < VFPI; ++j) {
         const int t = tw + j;
-        const uint32_t q = (word >> (BITS * j)) & MASK;
+        const uint32_t q = (word >> (VB * j)) & VMASK;
         const int pi = t * NCG + d / G;
         const float x = fmaf((float)q, s.vs[pi], s.vm[pi]);
 #pragma unroll
@@ -128,7 +129,7 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
 }
 
 // grid: (n_chunks + 1, B * H_kv); part n_chunks is the fp16 windows
-template <int BITS, int G, int GQA>
+template <int BITS, int VB, int G, int GQA>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   __shared__ Lds<GQA> s;
   const int tid = threadIdx.x;
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     const int64_t ge = min<int64_t>(seq_groups(a, b, G), gb + a.groups_per_chunk);
     for (int64_t g = gb; g < ge && !s.bad; g += kBlockTok / G) {
       const int ng = (int)min<int64_t>(kBlockTok / G, ge - g);
-      quant_block<BITS, G, GQA>(a, s, head, g * G, ng * G, acc);
+      quant_block<BITS, VB, G, GQA>(a, s, head, g * G, ng * G, acc);
     }
   } else {
     const int n_win = a.n_sink + seq_res(a, b);
@@ -233,37 +234,48 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   if (!ph) a.out[bh * kD + d] = Ls > 0.f ? (o + s_w[d]) / Ls : 0.f;
 }
 
-template <int BITS, int G>
+template <int BITS, int VB, int G>
 hipError_t decode_bg(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.n_chunks + 1), (unsigned)(a.B * a.H_kv));
   switch (a.gqa) {
-    case 1: decode_valu_kernel<BITS, G, 1><<<grid, kThreads, 0, st>>>(a); break;
-    case 2: decode_valu_kernel<BITS, G, 2><<<grid, kThreads, 0, st>>>(a); break;
-    case 4: decode_valu_kernel<BITS, G, 4><<<grid, kThreads, 0, st>>>(a); break;
-    case 8: decode_valu_kernel<BITS, G, 8><<<grid, kThreads, 0, st>>>(a); break;
+    case 1: decode_valu_kernel<BITS, VB, G, 1><<<grid, kThreads, 0, st>>>(a); break;
+    case 2: decode_valu_kernel<BITS, VB, G, 2><<<grid, kThreads, 0, st>>>(a); break;
+    case 4: decode_valu_kernel<BITS, VB, G, 4><<<grid, kThreads, 0, st>>>(a); break;
+    case 8: decode_valu_kernel<BITS, VB, G, 8><<<grid, kThreads, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int BITS>
+// equal widths for every group size, the mixed pairs for G = 128 only
+template <int BITS, int VB>
 hipError_t decode_bits(int group, const DecodeArgs& a, hipStream_t st) {
-  switch (group) {
-    case 32: return decode_bg<BITS, 32>(a, st);
-    case 64: return decode_bg<BITS, 64>(a, st);
-    case 128: return decode_bg<BITS, 128>(a, st);
-    default: return hipErrorInvalidValue;
+  if constexpr (VB != BITS) {
+    return group == 128 ? decode_bg<BITS, VB, 128>(a, st) : hipErrorInvalidValue;
+  } else {
+    switch (group) {
+      case 32: return decode_bg<BITS, VB, 32>(a, st);
+      case 64: return decode_bg<BITS, VB, 64>(a, st);
+      case 128: return decode_bg<BITS, VB, 128>(a, st);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_partials(int bits, int group, const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode_partials(int bits, int v_bits, int group, const DecodeArgs& a,
+                                  hipStream_t st) {
+  if (bits != v_bits) {
+    if (bits == 2 && v_bits == 4) return decode_bits<2, 4>(group, a, st);
+    if (bits == 4 && v_bits == 2) return decode_bits<4, 2>(group, a, st);
+    return hipErrorInvalidValue;
+  }
   return mfma_decode_supported(bits, group, a.gqa, a.n_boost)
              ? launch_decode_mfma(bits, a, st)
-             : (bits == 2   ? decode_bits<2>(group, a, st)
-                : bits == 4 ? decode_bits<4>(group, a, st)
-                            : decode_bits<8>(group, a, st));
+             : (bits == 2   ? decode_bits<2, 2>(group, a, st)
+                : bits == 4 ? decode_bits<4, 4>(group, a, st)
+                            : decode_bits<8, 8>(group, a, st));
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st) {

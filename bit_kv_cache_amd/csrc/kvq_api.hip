@@ -12,6 +12,12 @@ using kvq::kD;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Value code width (0 in the configuration: the key width).
+int vbits(const kvq_qcfg* cfg) { return cfg->v_bits ? cfg->v_bits : cfg->bits; }
+// The code width the matrix-core and fused kernels are chosen by: the key
+// width when keys and values share it, else 0 (no such kernel).
+int same_bits(const kvq_qcfg* cfg) { return vbits(cfg) == cfg->bits ? cfg->bits : 0; }
+
 // Checks shared by every entry point.
 kvq_status check_cfg(const kvq_qcfg* cfg) {
   if (!cfg) return KVQ_ERR_ARG;
@@ -23,6 +29,15 @@ kvq_status check_cfg(const kvq_qcfg* cfg) {
   if (cfg->group != 32 && cfg->group != 64 && cfg->group != 128) return KVQ_ERR_UNSUPPORTED;
   if (cfg->n_boost < 0 || cfg->n_boost > kD || cfg->n_boost % 16) return KVQ_ERR_ARG;
   if (cfg->n_boost > 0 && cfg->bits != 2) return KVQ_ERR_ARG;
+  const int vb = vbits(cfg);
+  if (vb != 2 && vb != 4 && vb != 8) return KVQ_ERR_ARG;
+  if (cfg->group % (32 / vb)) return KVQ_ERR_ARG;
+  if (cfg->n_boost > 0 && vb != 2) return KVQ_ERR_ARG;   // Kitty values are 2-bit
+  if (cfg->boost_score != 0 && cfg->boost_score != 1) return KVQ_ERR_ARG;
+  if (vb != cfg->bits) {   // the mixed widths built: K2V4 and K4V2 with G = 128
+    if (!((cfg->bits == 2 && vb == 4) || (cfg->bits == 4 && vb == 2))) return KVQ_ERR_UNSUPPORTED;
+    if (cfg->group != 128) return KVQ_ERR_UNSUPPORTED;
+  }
   return KVQ_OK;
 }
 
@@ -135,10 +150,11 @@ kvq_status kvq_quantize_pack(const kvq_qcfg* cfg, const kvq_cache* cache, int32_
     return KVQ_ERR_ALIGN;
   const int64_t heads = (int64_t)B * H_kv;
   if (heads * n_groups > 0x7FFFFFFF) return KVQ_ERR_ARG;
-  kvq::QuantArgs a{cache_args(cache), k_src,    v_src, src_head_stride, first_group,
-                   n_groups,          (int32_t)heads, cfg->n_boost};
-  return hip_status(
-      kvq::launch_quantize(cfg->bits, cfg->group, a, static_cast<hipStream_t>(stream)));
+  kvq::QuantArgs a{cache_args(cache), k_src,          v_src,        src_head_stride,
+                   first_group,       n_groups,       (int32_t)heads, cfg->n_boost,
+                   cfg->boost_score};
+  return hip_status(kvq::launch_quantize(cfg->bits, vbits(cfg), cfg->group, a,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t H_kv,
@@ -153,7 +169,7 @@ kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t 
     return KVQ_ERR_ARG;
   const int64_t heads = (int64_t)B * H_kv;
   if (heads > 65535) return KVQ_ERR_ARG;  // one grid row per (batch, kv head)
-  const bool mfma = kvq::mfma_decode_supported(cfg->bits, cfg->group, gqa, cfg->n_boost);
+  const bool mfma = kvq::mfma_decode_supported(same_bits(cfg), cfg->group, gqa, cfg->n_boost);
   const int32_t n = plan_chunks(mfma, cfg->bits, gqa, heads, n_quant_tokens / cfg->group, n_chunks_req);
   if (n_chunks) *n_chunks = n;
   if (ws_bytes) *ws_bytes = workspace_bytes(B, H_q, mfma ? n : n + 1);
@@ -218,8 +234,9 @@ kvq_status prepare_decode(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
   }
   a->qscale = sm_scale * 1.4426950408889634f;
   a->ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kvq::kCounterBytes);
-  a->n_parts = kvq::mfma_decode_supported(cfg->bits, cfg->group, a->gqa, cfg->n_boost) ? nc
-                                                                                     : nc + 1;
+  a->n_parts = kvq::mfma_decode_supported(same_bits(cfg), cfg->group, a->gqa, cfg->n_boost)
+                    ? nc
+                    : nc + 1;
   a->counters = nullptr;
   a->append = 0;
   a->seq_quant = nullptr;
@@ -231,11 +248,12 @@ kvq_status prepare_decode(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
 // place, else the split-K launch and the merge launch.
 kvq_status decode_and_merge(const kvq_qcfg* cfg, kvq::DecodeArgs& a, void* workspace,
                             hipStream_t s) {
-  if (kvq::fused_merge_supported(cfg->bits, cfg->group, a.gqa, cfg->n_boost, a.n_parts)) {
+  if (kvq::fused_merge_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_parts)) {
     a.counters = static_cast<int32_t*>(workspace);
-    return hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s));
+    return hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s));
   }
-  kvq_status st = hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s));
+  kvq_status st =
+      hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s));
   if (st != KVQ_OK) return st;
   return hip_status(kvq::launch_merge(a, s));
 }
@@ -279,19 +297,21 @@ kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t 
   a.out = out;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!append) return decode_and_merge(cfg, a, workspace, s);
-  if (kvq::fused_append_supported(cfg->bits, cfg->group, a.gqa, cfg->n_boost, a.n_parts,
+  if (kvq::fused_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_parts,
                                   a.n_chunks)) {
     // one launch: split-K, the append's quantize and the merge
     a.counters = static_cast<int32_t*>(workspace);
     a.append = 1;
-    return hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s));
+    return hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s));
   }
-  if ((st = hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a, s))) != KVQ_OK)
+  if ((st = hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s))) !=
+      KVQ_OK)
     return st;
   const int64_t heads = (int64_t)B * H_kv;
-  const kvq::QuantArgs qa{cache_args(cache), res->k,          res->v,   (int64_t)res->cap * kD,
-                          n_quant_tokens / G, 1,              (int32_t)heads, cfg->n_boost};
-  return hip_status(kvq::launch_merge_append(cfg->bits, cfg->group, a, qa, s));
+  const kvq::QuantArgs qa{cache_args(cache), res->k,         res->v,       (int64_t)res->cap * kD,
+                          n_quant_tokens / G, 1,             (int32_t)heads, cfg->n_boost,
+                          cfg->boost_score};
+  return hip_status(kvq::launch_merge_append(cfg->bits, vbits(cfg), cfg->group, a, qa, s));
 }
 
 kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
@@ -306,7 +326,7 @@ kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int3
   if (st != KVQ_OK) return st;
   if (!n_parts) return KVQ_ERR_ARG;
   *n_parts = a.n_parts;
-  return hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a,
+  return hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a,
                                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -348,7 +368,7 @@ kvq_status kvq_decode_partials_ragged(const kvq_qcfg* cfg, const kvq_cache* cach
   *n_parts = a.n_parts;
   a.seq_quant = seq_quant_tokens;
   a.seq_res = seq_res_tokens;
-  return hip_status(kvq::launch_decode_partials(cfg->bits, cfg->group, a,
+  return hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a,
                                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -385,8 +405,8 @@ kvq_status kvq_dequantize(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
   if (heads * n_groups * cfg->group * kD / 256 > 0x7FFFFFFF) return KVQ_ERR_ARG;
   kvq::DequantArgs a{cache_args(cache), k_out, v_out, first_group, n_groups, (int32_t)heads,
                      cfg->n_boost};
-  return hip_status(
-      kvq::launch_dequantize(cfg->bits, cfg->group, a, static_cast<hipStream_t>(stream)));
+  return hip_status(kvq::launch_dequantize(cfg->bits, vbits(cfg), cfg->group, a,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

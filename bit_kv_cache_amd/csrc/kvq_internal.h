@@ -64,6 +64,7 @@ struct QuantArgs {
   int64_t n_groups;
   int32_t n_heads;
   int32_t n_boost;
+  int32_t boost_score;   // Kitty channel importance: 0 range, 1 mean |x|
 };
 
 struct DequantArgs {
@@ -156,16 +157,20 @@ constexpr int kCUs = 256;  // MI355X
 inline int mfma_resident_blocks(int bits, int gqa) { return kCUs * mfma_blocks_per_cu(bits, gqa); }
 
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
-hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s);
-hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStream_t s);
-hipError_t launch_decode_partials(int bits, int group, const DecodeArgs& a, hipStream_t s);
+// bits / v_bits: key / value code widths (equal, or the K2V4 and K4V2 pairs
+// with G = 128)
+hipError_t launch_quantize(int bits, int v_bits, int group, const QuantArgs& a, hipStream_t s);
+hipError_t launch_dequantize(int bits, int v_bits, int group, const DequantArgs& a,
+                             hipStream_t s);
+hipError_t launch_decode_partials(int bits, int v_bits, int group, const DecodeArgs& a,
+                                  hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 // The merge of a decode step and the quantize of an appended group (both
 // small, latency-bound) as one launch; separate launches when the step has
 // more than kMergeAppendParts parts.
 constexpr int kMergeAppendParts = 32;
-hipError_t launch_merge_append(int bits, int group, const DecodeArgs& d, const QuantArgs& q,
-                               hipStream_t s);
+hipError_t launch_merge_append(int bits, int v_bits, int group, const DecodeArgs& d,
+                               const QuantArgs& q, hipStream_t s);
 hipError_t launch_decode_mfma(int bits, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t s);
 

@@ -5,8 +5,11 @@
 // keys per channel over G tokens, values per token over G channels.
 // KIVI page, Step 2 (`pack_tensor`): 32/bits codes per word, least
 // significant first.  Kitty page, sections 3.2 and 4.1: per key group the
-// n_boost channels of largest range get 4-bit codes, split into the dense
+// n_boost most important channels (largest range, or largest mean magnitude
+// over the group's tokens) get 4-bit codes, split into the dense
 // low-two-bit word, a compact word of high two bits and a channel index.
+// Keys and values may use different widths (Kitty page, section 3.1: K2V4,
+// K4V2): BITS is the key width, VB the value width.
 //
 // Exactness contract: fp32 range, IEEE fp32 division (hipcc's correctly
 // rounded division), fp16 scale rounded to nearest even, codes divide by the
@@ -35,6 +38,15 @@ __device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float
   float y = (x - mn) / s;
   y = fminf(fmaxf(y, 0.0f), maxq);
   return (uint32_t)__builtin_rintf(y);
+}
+
+// |x| of an fp16 value in units of 2^-24, exactly: a subnormal's fraction,
+// or the significand (implicit bit set) shifted by the biased exponent - 1.
+// A group's sum (at most 128 values below 2^40 units) fits 64 bits exactly,
+// so it does not depend on the order of the additions.
+__device__ __forceinline__ uint64_t mag_units(uint16_t h) {
+  const uint32_t e = (h >> 10) & 31u, f = h & 0x3FFu;
+  return e == 0 ? (uint64_t)f : (uint64_t)(f | 0x400u) << (e - 1);
 }
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t v, int width) {
@@ -124,6 +136,7 @@ __device__ void quantize_keys_kitty(const QuantArgs& a, int64_t head, int64_t gi
   __shared__ float s_mn[kD], s_sc[kD], s_mq[kD], s_rng[kD];
   __shared__ int s_flag[kD], s_chan_of_row[kD];
   __shared__ uint32_t s_red[2][kD];
+  __shared__ uint64_t s_mag[kD];   // sum of |x| over the group (units of 2^-24)
   const int tid = threadIdx.x;
   const int64_t gb = group_block(a.c, head, a.first_group + gi, G);
   if (gb < 0) return;
@@ -136,32 +149,47 @@ __device__ void quantize_keys_kitty(const QuantArgs& a, int64_t head, int64_t gi
   }
   __syncthreads();
   const int d = tid & (kD - 1), half = tid >> 7;
+  const bool by_mag = a.boost_score != 0;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  uint64_t mag = 0;
   for (int j = half * (G / 2); j < (half + 1) * (G / 2); ++j) {
-    const uint32_t k = order_key(tile[j * kD + d]);
+    const uint16_t x = tile[j * kD + d];
+    const uint32_t k = order_key(x);
     lo = min(lo, k);
     hi = max(hi, k);
+    if (by_mag) mag += mag_units(x);
   }
   if (half) {
     s_red[0][d] = lo;
     s_red[1][d] = hi;
+    s_mag[d] = mag;
   }
   __syncthreads();
   if (!half) {
     lo = min(lo, s_red[0][d]);
     hi = max(hi, s_red[1][d]);
+    s_mag[d] += mag;
     const float mn = h2f(from_order_key(lo));
     s_mn[d] = mn;
     s_rng[d] = h2f(from_order_key(hi)) - mn;
   }
   __syncthreads();
   if (!half) {
-    // rank by range, ties to the lower channel
-    const float r = s_rng[d];
+    // rank by range (or by the sum of |x|, the mean's order), ties to the
+    // lower channel
     int rank = 0;
-    for (int c = 0; c < kD; ++c) {
-      const float rc = s_rng[c];
-      rank += (rc > r) || (rc == r && c < d);
+    if (by_mag) {
+      const uint64_t v = s_mag[d];
+      for (int c = 0; c < kD; ++c) {
+        const uint64_t vc = s_mag[c];
+        rank += (vc > v) || (vc == v && c < d);
+      }
+    } else {
+      const float r = s_rng[d];
+      for (int c = 0; c < kD; ++c) {
+        const float rc = s_rng[c];
+        rank += (rc > r) || (rc == r && c < d);
+      }
     }
     s_flag[d] = rank < nb;
   }
@@ -281,14 +309,14 @@ __device__ void quantize_values_slice(const QuantArgs& a, int64_t head, int64_t 
 
 // grid: (heads * n_groups, 2 * kSlices): y < kSlices key slices (Kitty: the
 // whole key group in y == 0), then value slices
-template <int BITS, int G, bool KITTY>
+template <int BITS, int VB, int G, bool KITTY>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
   const int64_t blk = blockIdx.x;
   const int64_t head = blk / a.n_groups;
   const int64_t gi = blk % a.n_groups;
   const int y = blockIdx.y;
   if (y >= kSlices) {
-    if (y - kSlices < kValueSlices<BITS, G>) quantize_values_slice<BITS, G>(a, head, gi, y - kSlices);
+    if (y - kSlices < kValueSlices<VB, G>) quantize_values_slice<VB, G>(a, head, gi, y - kSlices);
   } else if constexpr (KITTY) {
     if (y == 0) quantize_keys_kitty<G>(a, head, gi);
   } else {
@@ -301,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 // (threads 0..127 and 128..255, one channel per thread); the blocks after
 // them are the quantize kernel's (group, slice) blocks.  The two jobs share
 // no memory (partials and output vs. residual rows and one cache group).
-template <int BITS, int G, bool KITTY, int NPM>
+template <int BITS, int VB, int G, bool KITTY, int NPM>
 __global__ __launch_bounds__(kThreads) void merge_append_kernel(DecodeArgs d, QuantArgs a,
                                                                int n_merge) {
   const int blk = blockIdx.x;
@@ -314,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void merge_append_kernel(DecodeArgs d, Qu
   const int64_t head = qb / (2 * kSlices);   // one group: (head, slice)
   const int y = qb % (2 * kSlices);
   if (y >= kSlices) {
-    if (y - kSlices < kValueSlices<BITS, G>) quantize_values_slice<BITS, G>(a, head, 0, y - kSlices);
+    if (y - kSlices < kValueSlices<VB, G>) quantize_values_slice<VB, G>(a, head, 0, y - kSlices);
   } else if constexpr (KITTY) {
     if (y == 0) quantize_keys_kitty<G>(a, head, 0);
   } else {
@@ -323,10 +351,10 @@ __global__ __launch_bounds__(kThreads) void merge_append_kernel(DecodeArgs d, Qu
 }
 
 // Dequantize: one thread per (token, channel) of keys and values.
-template <int BITS, int G>
+template <int BITS, int VB, int G>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
-  constexpr int FPI = 32 / BITS;
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  constexpr int FPI = 32 / BITS, VFPI = 32 / VB;
+  constexpr uint32_t MASK = (1u << BITS) - 1u, VMASK = (1u << VB) - 1u;
   const int64_t n_tok = a.n_groups * G;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t total = (int64_t)a.n_heads * n_tok * kD;
@@ -358,86 +386,114 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   }
   // value
   {
-    const uint32_t w = a.c.v_codes[(tb / FPI) * kD + d];
-    const uint32_t q = (w >> (BITS * (t % FPI))) & MASK;
+    const uint32_t w = a.c.v_codes[(tb / VFPI) * kD + d];
+    const uint32_t q = (w >> (VB * (t % VFPI))) & VMASK;
     const int64_t m_off = tb * (kD / G) + d / G;
     const float prod = (float)q * h2f(a.c.v_scale[m_off]);
     a.v_out[idx] = prod + h2f(a.c.v_min[m_off]);
   }
 }
 
-template <int BITS, bool KITTY>
+// Equal key and value widths are built for every group size, the mixed
+// pairs (K2V4, K4V2) for G = 128 only.
+template <int BITS, int VB, bool KITTY>
 hipError_t quantize_bits(int group, const QuantArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_heads * a.n_groups), 2 * kSlices);
-  switch (group) {
-    case 32: quantize_kernel<BITS, 32, KITTY><<<grid, kThreads, 0, s>>>(a); break;
-    case 64: quantize_kernel<BITS, 64, KITTY><<<grid, kThreads, 0, s>>>(a); break;
-    case 128: quantize_kernel<BITS, 128, KITTY><<<grid, kThreads, 0, s>>>(a); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (VB != BITS) {
+    if (group != 128) return hipErrorInvalidValue;
+    quantize_kernel<BITS, VB, 128, KITTY><<<grid, kThreads, 0, s>>>(a);
+  } else {
+    switch (group) {
+      case 32: quantize_kernel<BITS, VB, 32, KITTY><<<grid, kThreads, 0, s>>>(a); break;
+      case 64: quantize_kernel<BITS, VB, 64, KITTY><<<grid, kThreads, 0, s>>>(a); break;
+      case 128: quantize_kernel<BITS, VB, 128, KITTY><<<grid, kThreads, 0, s>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, int VB>
 hipError_t dequantize_bits(int group, const DequantArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.n_heads * a.n_groups * group * kD;
   const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
-  switch (group) {
-    case 32: dequantize_kernel<BITS, 32><<<grid, kThreads, 0, s>>>(a); break;
-    case 64: dequantize_kernel<BITS, 64><<<grid, kThreads, 0, s>>>(a); break;
-    case 128: dequantize_kernel<BITS, 128><<<grid, kThreads, 0, s>>>(a); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (VB != BITS) {
+    if (group != 128) return hipErrorInvalidValue;
+    dequantize_kernel<BITS, VB, 128><<<grid, kThreads, 0, s>>>(a);
+  } else {
+    switch (group) {
+      case 32: dequantize_kernel<BITS, VB, 32><<<grid, kThreads, 0, s>>>(a); break;
+      case 64: dequantize_kernel<BITS, VB, 64><<<grid, kThreads, 0, s>>>(a); break;
+      case 128: dequantize_kernel<BITS, VB, 128><<<grid, kThreads, 0, s>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
 
-template <int BITS, bool KITTY, int NPM>
+template <int BITS, int VB, bool KITTY, int NPM>
 hipError_t merge_append_bits(int group, const DecodeArgs& d, const QuantArgs& a, hipStream_t s) {
   const int n_merge = (int)(((int64_t)d.B * d.H_q + 1) / 2);
   const dim3 grid((unsigned)(n_merge + a.n_heads * 2 * kSlices));
-  switch (group) {
-    case 32: merge_append_kernel<BITS, 32, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge); break;
-    case 64: merge_append_kernel<BITS, 64, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge); break;
-    case 128: merge_append_kernel<BITS, 128, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (VB != BITS) {
+    if (group != 128) return hipErrorInvalidValue;
+    merge_append_kernel<BITS, VB, 128, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge);
+  } else {
+    switch (group) {
+      case 32: merge_append_kernel<BITS, VB, 32, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge); break;
+      case 64: merge_append_kernel<BITS, VB, 64, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge); break;
+      case 128: merge_append_kernel<BITS, VB, 128, KITTY, NPM><<<grid, kThreads, 0, s>>>(d, a, n_merge); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
 
-template <int BITS, bool KITTY>
+template <int BITS, int VB, bool KITTY>
 hipError_t merge_append_parts(int group, const DecodeArgs& d, const QuantArgs& a, hipStream_t s) {
-  if (d.n_parts <= 8) return merge_append_bits<BITS, KITTY, 8>(group, d, a, s);
-  if (d.n_parts <= 16) return merge_append_bits<BITS, KITTY, 16>(group, d, a, s);
-  return merge_append_bits<BITS, KITTY, kMergeAppendParts>(group, d, a, s);
+  if (d.n_parts <= 8) return merge_append_bits<BITS, VB, KITTY, 8>(group, d, a, s);
+  if (d.n_parts <= 16) return merge_append_bits<BITS, VB, KITTY, 16>(group, d, a, s);
+  return merge_append_bits<BITS, VB, KITTY, kMergeAppendParts>(group, d, a, s);
 }
 
 }  // namespace
 
-hipError_t launch_merge_append(int bits, int group, const DecodeArgs& d, const QuantArgs& a,
-                               hipStream_t s) {
+hipError_t launch_merge_append(int bits, int v_bits, int group, const DecodeArgs& d,
+                               const QuantArgs& a, hipStream_t s) {
   if (d.n_parts > kMergeAppendParts || a.n_groups != 1) {
     const hipError_t e = launch_merge(d, s);
-    return e != hipSuccess ? e : launch_quantize(bits, group, a, s);
+    return e != hipSuccess ? e : launch_quantize(bits, v_bits, group, a, s);
   }
+  if (bits == 2 && v_bits == 4) return merge_append_parts<2, 4, false>(group, d, a, s);
+  if (bits == 4 && v_bits == 2) return merge_append_parts<4, 2, false>(group, d, a, s);
+  if (bits != v_bits) return hipErrorInvalidValue;
   if (bits == 2)
-    return a.n_boost > 0 ? merge_append_parts<2, true>(group, d, a, s)
-                         : merge_append_parts<2, false>(group, d, a, s);
-  if (bits == 8) return merge_append_parts<8, false>(group, d, a, s);
-  return merge_append_parts<4, false>(group, d, a, s);
+    return a.n_boost > 0 ? merge_append_parts<2, 2, true>(group, d, a, s)
+                         : merge_append_parts<2, 2, false>(group, d, a, s);
+  if (bits == 8) return merge_append_parts<8, 8, false>(group, d, a, s);
+  return merge_append_parts<4, 4, false>(group, d, a, s);
 }
 
-hipError_t launch_quantize(int bits, int group, const QuantArgs& a, hipStream_t s) {
+hipError_t launch_quantize(int bits, int v_bits, int group, const QuantArgs& a, hipStream_t s) {
   if (a.n_groups == 0 || a.n_heads == 0) return hipSuccess;
+  if (bits == 2 && v_bits == 4) return quantize_bits<2, 4, false>(group, a, s);
+  if (bits == 4 && v_bits == 2) return quantize_bits<4, 2, false>(group, a, s);
+  if (bits != v_bits) return hipErrorInvalidValue;
   if (bits == 2)
-    return a.n_boost > 0 ? quantize_bits<2, true>(group, a, s) : quantize_bits<2, false>(group, a, s);
-  if (bits == 8) return quantize_bits<8, false>(group, a, s);
-  return quantize_bits<4, false>(group, a, s);
+    return a.n_boost > 0 ? quantize_bits<2, 2, true>(group, a, s)
+                         : quantize_bits<2, 2, false>(group, a, s);
+  if (bits == 8) return quantize_bits<8, 8, false>(group, a, s);
+  return quantize_bits<4, 4, false>(group, a, s);
 }
 
-hipError_t launch_dequantize(int bits, int group, const DequantArgs& a, hipStream_t s) {
+hipError_t launch_dequantize(int bits, int v_bits, int group, const DequantArgs& a,
+                             hipStream_t s) {
   if (a.n_groups == 0 || a.n_heads == 0) return hipSuccess;
-  if (bits == 8) return dequantize_bits<8>(group, a, s);
-  return bits == 2 ? dequantize_bits<2>(group, a, s) : dequantize_bits<4>(group, a, s);
+  if (bits == 2 && v_bits == 4) return dequantize_bits<2, 4>(group, a, s);
+  if (bits == 4 && v_bits == 2) return dequantize_bits<4, 2>(group, a, s);
+  if (bits != v_bits) return hipErrorInvalidValue;
+  if (bits == 8) return dequantize_bits<8, 8>(group, a, s);
+  return bits == 2 ? dequantize_bits<2, 2>(group, a, s) : dequantize_bits<4, 4>(group, a, s);
 }
 
 }  // namespace kvq

@@ -33,7 +33,8 @@
  *    the same dequantized cache within 2e-3 for the documented inputs.
  *
  * Cache layout (device memory owned by the caller).  head = b*H_kv + h,
- * fpi = 32/bits, D = head_dim, G = group, t_cap = token capacity per head:
+ * fpi = 32/bits (keys), v_fpi = 32/v_bits (values), D = head_dim, G = group,
+ * t_cap = token capacity per head:
  *    k_codes  [head][t_cap][D/fpi]       key codes packed along channels:
  *                                        word (t,w) holds channels w*fpi+j
  *    k_scale, k_min [head][t_cap/G][D]   fp16 bits per (group, channel)
@@ -41,8 +42,8 @@
  *                                        bits of boosted rows w*16+j
  *    k_bidx   [head][t_cap/G][D] uint8   Kitty: boosted row of channel d
  *                                        (ascending channel order) or n_boost
- *    v_codes  [head][t_cap/fpi][D]       value codes packed along tokens:
- *                                        word (w,d) holds tokens w*fpi+j
+ *    v_codes  [head][t_cap/v_fpi][D]     value codes packed along tokens:
+ *                                        word (w,d) holds tokens w*v_fpi+j
  *    v_scale, v_min [head][t_cap][D/G]   fp16 bits per (token, channel group)
  *  Keys are packed along the channel axis and values along the token axis:
  *  the contraction axis of q.K^T and p.V, so one word feeds one lane's
@@ -95,12 +96,23 @@ typedef enum kvq_status {
  *  group: G, one of 32, 64, 128; must divide head_dim.
  *  head_dim: D, 128.
  *  n_boost: 0 (plain KIVI) or, with bits == 2, a multiple of 16 up to D
- *        (Kitty boost; 16 of 128 channels is the 12.5% "Kitty" setting). */
+ *        (Kitty boost; 16 of 128 channels is the 12.5% "Kitty" setting).
+ *  v_bits: width of the value codes, 0 for the key width `bits`.  Mixed
+ *        widths are the Kitty page's K2V4 and K4V2 variants (section 3.1):
+ *        bits 2 with v_bits 4 or bits 4 with v_bits 2, G = 128 only (other
+ *        mixes: KVQ_ERR_UNSUPPORTED); they take the vector-ALU decode kernel.
+ *        With n_boost > 0, v_bits must be 0 or 2.
+ *  boost_score: how the Kitty boost ranks a group's key channels: 0 by range
+ *        (max - min over the group), 1 by mean magnitude over the group's
+ *        tokens (Kitty page, section 3.2's heuristic); ties go to the lower
+ *        channel.  Ignored when n_boost == 0. */
 typedef struct kvq_qcfg {
   int32_t bits;
   int32_t group;
   int32_t head_dim;
   int32_t n_boost;
+  int32_t v_bits;
+  int32_t boost_score;
 } kvq_qcfg;
 
 /* Packed cache, layout above.  k_hi / k_bidx may be NULL when n_boost == 0.

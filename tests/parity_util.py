@@ -17,7 +17,8 @@ TOL = 2e-3  # max-abs attention error vs the fp64 oracle
 
 def qcfg(w):
     import bit_kv_cache_amd as kvq
-    return kvq.QCfg(bits=w.bits, group=w.G, head_dim=w.D, n_boost=w.n_boost)
+    return kvq.QCfg(bits=w.bits, group=w.G, head_dim=w.D, n_boost=w.n_boost, v_bits=w.v_bits,
+                    boost_score=w.boost_score)
 
 
 def make_inputs(w, device="cuda", heads=None):
@@ -48,7 +49,8 @@ def gpu_quantize(w, inp, t_cap=None, stream=None):
 def oracle_quantize(w, inp, t_cap=None):
     t_cap = t_cap or (w.T + max(w.R, w.G))
     n = len(inp["heads"])
-    c = oracle.empty_cache(w.bits, w.G, w.D, w.n_boost, t_cap, n)
+    c = oracle.empty_cache(w.bits, w.G, w.D, w.n_boost, t_cap, n, v_bits=w.v_bits,
+                           score=w.boost_score)
     if w.T:
         oracle.quantize_pack(c, synth.as_bits(inp["k"]), synth.as_bits(inp["v"]), 0, w.T // w.G)
     return c
@@ -62,7 +64,7 @@ FIELDS = [("k_codes", "k_words"), ("k_scale", "k_scale"), ("k_min", "k_min"),
 def assert_cache_equal(gc, oc, tokens=None):
     """Bit-exact comparison of every cache array (optionally only the first
     ``tokens`` token slots)."""
-    G, fpi = oc.group, oc.fpi
+    G, v_fpi = oc.group, oc.v_fpi
     for gname, oname in FIELDS:
         g, o = getattr(gc, gname), getattr(oc, oname)
         if g is None or o is None:
@@ -71,7 +73,7 @@ def assert_cache_equal(gc, oc, tokens=None):
         gh = g.cpu().numpy().view(o.dtype)
         if tokens is not None:
             rows = {"k_codes": tokens, "k_hi": tokens, "k_scale": tokens // G,
-                    "k_min": tokens // G, "k_bidx": tokens // G, "v_codes": tokens // fpi,
+                    "k_min": tokens // G, "k_bidx": tokens // G, "v_codes": tokens // v_fpi,
                     "v_scale": tokens, "v_min": tokens}[gname]
             gh, o = gh[:, :rows], o[:, :rows]
         bad = np.argwhere(gh != o)

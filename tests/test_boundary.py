@@ -36,8 +36,8 @@ def test_status_strings():
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
 
 
-def _cfg(bits=2, group=128, D=128, nb=0):
-    return kvq.kvq_qcfg(bits, group, D, nb)
+def _cfg(bits=2, group=128, D=128, nb=0, vb=0, score=0):
+    return kvq.kvq_qcfg(bits, group, D, nb, vb, score)
 
 
 def _cache(t_cap=1024, align=0, hi=FAKE):
@@ -54,6 +54,12 @@ def _quant(cfg, cache, B=1, H=1, k=FAKE, v=FAKE, stride=128 * 128, fg=0, ng=1):
     (_cfg(bits=3), kvq.KVQ_ERR_ARG),
     (_cfg(bits=1), kvq.KVQ_ERR_ARG),
     (_cfg(bits=8, nb=16), kvq.KVQ_ERR_ARG),        # the boost is for 2-bit codes
+    (_cfg(vb=3), kvq.KVQ_ERR_ARG),
+    (_cfg(nb=16, vb=4), kvq.KVQ_ERR_ARG),          # Kitty values are 2-bit
+    (_cfg(score=2), kvq.KVQ_ERR_ARG),
+    (_cfg(vb=8), kvq.KVQ_ERR_UNSUPPORTED),         # mixed widths built: K2V4, K4V2
+    (_cfg(bits=4, vb=8), kvq.KVQ_ERR_UNSUPPORTED),
+    (_cfg(group=64, vb=4), kvq.KVQ_ERR_UNSUPPORTED),   # mixed widths: G = 128 only
     (_cfg(D=64), kvq.KVQ_ERR_UNSUPPORTED),
     (_cfg(group=48), kvq.KVQ_ERR_ARG),
     (_cfg(group=8), kvq.KVQ_ERR_ARG),

@@ -17,7 +17,7 @@ from test_gpu_parity import _w
 
 pytestmark = pytest.mark.gpu
 
-CASES = ["llama_2bit", "gqa8_2bit", "llama_4bit", "kitty_gqa4", "g32_8bit_gqa2"]
+CASES = ["llama_2bit", "gqa8_2bit", "llama_4bit", "kitty_gqa4", "g32_8bit_gqa2", "k2v4", "kitty_mag"]
 
 
 @pytest.fixture(scope="module")
@@ -39,7 +39,7 @@ def _gather(pool, table, n_groups):
     """The pool's pages in the contiguous layout ([heads][n_groups*G]...)."""
     import bit_kv_cache_amd as kvq
     cfg = pool.cfg
-    G, fpi = cfg.group, 32 // cfg.bits
+    G, fpi = cfg.group, 32 // cfg.vb
     idx = table[:, :n_groups].long().cpu()
     heads = idx.shape[0]
     n_pages = pool.t_cap // G

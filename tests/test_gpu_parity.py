@@ -39,6 +39,12 @@ CASES = {
     "llama_8bit": (W["llama3_8b_t8k_b32_4bit"], dict(B=2, T=11 * 128, bits=8)),
     "g32_8bit_gqa2": (synth.shrink(W["llama3_8b_t32k_2bit"], bits=8, H_q=16, G=32, T=23 * 32,
                                    B=1, R=32, S=3), {}),
+    # keys and values at different widths (Kitty page, section 3.1): the
+    # vector-ALU kernel
+    "k2v4": (synth.shrink(W["llama3_8b_t32k_2bit"], v_bits=4, B=1, T=9 * 128, S=3), {}),
+    "k4v2": (synth.shrink(W["llama3_8b_t8k_b32_4bit"], v_bits=2, B=1, T=10 * 128), {}),
+    # Kitty boost ranked by mean magnitude (Kitty page, section 3.2)
+    "kitty_mag": (synth.shrink(W["kitty_t128k_h64_boost16"], boost_score=1, B=1, T=8 * 128), {}),
 }
 
 
@@ -332,7 +338,7 @@ def test_quantize_rounding_ties_bit_exact(built):
 
 
 @pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "long_splitk", "llama_4bit", "kitty",
-                                  "llama_8bit"])
+                                  "llama_8bit", "k2v4", "k4v2", "kitty_mag"])
 def test_decode_step_with_append(built, name):
     """kvq_decode_step(append): the attention equals the oracle over the
     quantized tokens + the full fp16 residual group, and the residual group
@@ -379,3 +385,17 @@ def test_decode_step_append_rejects_short_residual(built):
     with pytest.raises(kvq.KvqError):
         kvq.kvq_decode_step(qcfg(w), gc, B, w.H_q, w.H_kv, inp["q"][:B].contiguous(), w.T, None,
                             kvq.window(inp["k_res"], inp["v_res"], w.G - 1), out, ws, True)
+
+
+def test_kitty_magnitude_score_changes_the_boosted_channels(built):
+    """The magnitude-ranked case is a real test of the score: on its inputs the
+    oracle boosts other channels than the range ranking would, and the GPU
+    cache matches the magnitude ranking."""
+    w = _w("kitty_mag")
+    inp = make_inputs(w)
+    oc_mag = oracle_quantize(w, inp)
+    oc_rng = oracle_quantize(synth.shrink(w, boost_score=0), inp)
+    assert not np.array_equal(oc_mag.k_bidx, oc_rng.k_bidx)
+    gc = gpu_quantize(w, inp)
+    torch.cuda.synchronize()
+    assert_cache_equal(gc, oc_mag, tokens=w.T)
