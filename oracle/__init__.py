@@ -83,6 +83,22 @@ def _load():
     lib.oracle_decode_attention.argtypes = [i32, i32, i32, i32, i32, i32, i64] + [P] * 8 + [
         i32, i32, i32, P, i64, P, P, i32, i32, P, P, i32, i32, f64, P, i32]
     lib.oracle_decode_attention.restype = i32
+    u8 = ctypes.c_uint8
+    lib.oracle_fp4_value.argtypes = [u8]
+    lib.oracle_fp4_value.restype = f64
+    lib.oracle_fp4_encode.argtypes = [f64]
+    lib.oracle_fp4_encode.restype = u8
+    lib.oracle_mx_exponent.argtypes = [P, i64, i64]
+    lib.oracle_mx_exponent.restype = i32
+    lib.oracle_mx_dequant.argtypes = [u8, u8]
+    lib.oracle_mx_dequant.restype = f32
+    lib.oracle_mx_quantize_pack.argtypes = [i32, i64, P, P, P, P, i64, P, P, i64, i64, i64, i32]
+    lib.oracle_mx_quantize_pack.restype = i32
+    lib.oracle_mx_dequantize.argtypes = [i32, i64, P, P, P, P, i64, i64, i64, P, P, i32]
+    lib.oracle_mx_dequantize.restype = i32
+    lib.oracle_mx_decode_attention.argtypes = [i32, i64, P, P, P, P, i32, i32, i32, P, i64, P,
+                                               P, i32, i32, P, P, i32, i32, f64, P, i32]
+    lib.oracle_mx_decode_attention.restype = i32
     _lib = lib
     return lib
 
@@ -267,4 +283,94 @@ def decode_attention(cache: Cache, B: int, H_q: int, H_kv: int, q: np.ndarray, n
                                          _ptr(vr), n_res, res_cap, sm, _ptr(out), n_threads)
     if rc:
         raise ValueError("oracle_decode_attention: bad configuration")
+    return out
+
+
+# --------------------------------------------------------------------------
+# MXFP4 cache (32-value blocks, E8M0 scale, E2M1 values); layout per head:
+#   k_words [t_cap][D/8] u32, k_scale [t_cap][D/32] u8 (blocks of 32 channels)
+#   v_words [t_cap/8][D] u32, v_scale [t_cap/32][D] u8 (blocks of 32 tokens)
+# --------------------------------------------------------------------------
+
+def fp4_value(code: int) -> float:
+    return float(_load().oracle_fp4_value(int(code)))
+
+
+def fp4_encode(v: float) -> int:
+    return int(_load().oracle_fp4_encode(float(v)))
+
+
+def mx_exponent(x_bits: np.ndarray) -> int:
+    """Shared exponent E of a block of fp16 values (bits)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    return int(_load().oracle_mx_exponent(_ptr(x), x.size, 1))
+
+
+def mx_dequant(code: int, e8m0: int) -> float:
+    return float(_load().oracle_mx_dequant(int(code), int(e8m0)))
+
+
+@dataclass
+class MxCache:
+    head_dim: int
+    t_cap: int
+    n_heads: int
+    k_words: np.ndarray
+    k_scale: np.ndarray
+    v_words: np.ndarray
+    v_scale: np.ndarray
+
+    def _args(self):
+        return [self.head_dim, self.t_cap, _ptr(self.k_words), _ptr(self.k_scale),
+                _ptr(self.v_words), _ptr(self.v_scale)]
+
+
+def mx_empty_cache(head_dim: int, t_cap: int, n_heads: int) -> MxCache:
+    H, T, D = n_heads, t_cap, head_dim
+    return MxCache(D, T, H, k_words=np.zeros((H, T, D // 8), np.uint32),
+                   k_scale=np.zeros((H, T, D // 32), np.uint8),
+                   v_words=np.zeros((H, T // 8, D), np.uint32),
+                   v_scale=np.zeros((H, T // 32, D), np.uint8))
+
+
+def mx_quantize_pack(cache: MxCache, k_src: np.ndarray, v_src: np.ndarray, t0: int, n: int,
+                     n_threads: int = 0) -> None:
+    """Quantize tokens [t0, t0+n) of every head from fp16 bits [heads][>= n][D]."""
+    k = np.ascontiguousarray(k_src, np.uint16)
+    v = np.ascontiguousarray(v_src, np.uint16)
+    assert k.shape == v.shape and k.shape[0] == cache.n_heads
+    rc = _load().oracle_mx_quantize_pack(*cache._args(), cache.n_heads, _ptr(k), _ptr(v),
+                                         k.shape[1] * k.shape[2], t0, n, n_threads)
+    if rc:
+        raise ValueError("oracle_mx_quantize_pack: bad configuration")
+
+
+def mx_dequantize(cache: MxCache, t0: int, n: int, n_threads: int = 0):
+    k = np.zeros((cache.n_heads, n, cache.head_dim), np.float32)
+    v = np.zeros_like(k)
+    rc = _load().oracle_mx_dequantize(*cache._args(), cache.n_heads, t0, n, _ptr(k), _ptr(v),
+                                      n_threads)
+    if rc:
+        raise ValueError("oracle_mx_dequantize: bad configuration")
+    return k, v
+
+
+def mx_decode_attention(cache: MxCache, B: int, H_q: int, H_kv: int, q: np.ndarray,
+                        n_quant: int, k_sink=None, v_sink=None, n_sink: int = 0, k_res=None,
+                        v_res=None, n_res: int = 0, sm: float = 0.0,
+                        n_threads: int = 0) -> np.ndarray:
+    """fp64 attention output ``[B][H_q][D]`` over the MXFP4 cache."""
+    D = cache.head_dim
+    q = np.ascontiguousarray(q, np.uint16)
+    ks = None if k_sink is None else np.ascontiguousarray(k_sink, np.uint16)
+    vs = None if v_sink is None else np.ascontiguousarray(v_sink, np.uint16)
+    kr = None if k_res is None else np.ascontiguousarray(k_res, np.uint16)
+    vr = None if v_res is None else np.ascontiguousarray(v_res, np.uint16)
+    out = np.zeros((B, H_q, D), np.float64)
+    rc = _load().oracle_mx_decode_attention(
+        *cache._args(), B, H_q, H_kv, _ptr(q), n_quant, _ptr(ks), _ptr(vs), n_sink,
+        0 if ks is None else ks.shape[1], _ptr(kr), _ptr(vr), n_res,
+        0 if kr is None else kr.shape[1], sm, _ptr(out), n_threads)
+    if rc:
+        raise ValueError("oracle_mx_decode_attention: bad configuration")
     return out

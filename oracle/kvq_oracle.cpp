@@ -529,6 +529,191 @@ int oracle_decode_attention(int32_t bits, int32_t v_bits, int32_t G, int32_t D, 
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 cache (BitDecoding page, section on native low-precision formats: its
+// Blackwell path runs the products on packed 4-bit data with block scale
+// factors, mxfp4 / nvfp4; the page gives no quantizer, so the format's own
+// definition is taken, the OCP microscaling one).  A block of 32 values
+// shares a scale 2^E, stored as the E8M0 byte E + 127; each value is an E2M1
+// number: sign, two exponent bits (bias 1, 0 = subnormal), one mantissa bit,
+// magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  E = floor(log2(max |x|)) - 2 (2 is
+// E2M1's largest exponent), so the largest magnitude lands in [4, 8) before
+// rounding; every value is rounded to the nearest E2M1 magnitude, ties to
+// the even mantissa bit, and magnitudes past 6 saturate to 6.  A block of
+// zeros has E = -127.  Blocks run along the contraction axis of each product:
+// 32 channels of one token for keys, 32 tokens of one channel for values.
+//
+// Layout per head, t_cap token slots (multiple of 32):
+//   K codes  [t_cap][D/8] u32   nibble j of word (t,w): channel 8w + j
+//   K scale  [t_cap][D/32] u8   E8M0 of channels 32c .. 32c + 31 of token t
+//   V codes  [t_cap/8][D] u32   nibble j of word (w,d): token 8w + j
+//   V scale  [t_cap/32][D] u8   E8M0 of tokens 32b .. 32b + 31 of channel d
+// ---------------------------------------------------------------------------
+
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+// value of a 4-bit E2M1 code
+double oracle_fp4_value(uint8_t code) {
+  const double m = kE2M1[code & 7];
+  return (code & 8) ? -m : m;
+}
+
+// nearest E2M1 code of v (ties to the even mantissa bit, i.e. the even index;
+// magnitudes past 6 saturate); the sign is v's, -0 included
+uint8_t oracle_fp4_encode(double v) {
+  const double a = std::fabs(v);
+  int best = 0;
+  for (int i = 1; i < 8; ++i) {
+    const double d = std::fabs(a - kE2M1[i]), db = std::fabs(a - kE2M1[best]);
+    if (d < db || (d == db && (i & 1) == 0)) best = i;
+  }
+  return (uint8_t)((std::signbit(v) ? 8 : 0) | best);
+}
+
+// shared exponent E of n fp16 values (stride apart)
+int32_t oracle_mx_exponent(const uint16_t* x, int64_t n, int64_t stride) {
+  double amax = 0.0;
+  for (int64_t i = 0; i < n; ++i) amax = std::max(amax, std::fabs(oracle_f16_to_f64(x[i * stride])));
+  if (amax == 0.0) return -127;
+  int e = 0;
+  std::frexp(amax, &e);            // amax = m 2^e, m in [0.5, 1): floor(log2 amax) = e - 1
+  return std::min(127, std::max(-127, (e - 1) - 2));
+}
+
+// codes of a block with shared exponent E (x / 2^E is exact in fp64)
+static void mx_block(const uint16_t* x, int64_t stride, int32_t E, uint8_t* codes) {
+  for (int64_t i = 0; i < 32; ++i)
+    codes[i] = oracle_fp4_encode(std::ldexp(oracle_f16_to_f64(x[i * stride]), -E));
+}
+
+// dequantized value: the E2M1 value times 2^E (exact in fp32 for fp16 inputs)
+float oracle_mx_dequant(uint8_t code, uint8_t e8m0) {
+  return (float)std::ldexp(oracle_fp4_value(code), (int)e8m0 - 127);
+}
+
+struct MxLayout {
+  int32_t D;
+  int64_t t_cap;
+  uint32_t* k_words;
+  uint8_t* k_scale;
+  uint32_t* v_words;
+  uint8_t* v_scale;
+  int64_t kw(int64_t hd, int64_t t, int64_t w) const { return (hd * t_cap + t) * (D / 8) + w; }
+  int64_t ks(int64_t hd, int64_t t, int64_t c) const { return (hd * t_cap + t) * (D / 32) + c; }
+  int64_t vw(int64_t hd, int64_t w, int64_t d) const { return (hd * (t_cap / 8) + w) * D + d; }
+  int64_t vs(int64_t hd, int64_t b, int64_t d) const { return (hd * (t_cap / 32) + b) * D + d; }
+};
+
+static float mx_key_at(const MxLayout& L, int64_t hd, int64_t t, int32_t d) {
+  const uint32_t w = L.k_words[L.kw(hd, t, d / 8)];
+  return oracle_mx_dequant((uint8_t)((w >> (4 * (d % 8))) & 15u), L.k_scale[L.ks(hd, t, d / 32)]);
+}
+
+static float mx_value_at(const MxLayout& L, int64_t hd, int64_t t, int32_t d) {
+  const uint32_t w = L.v_words[L.vw(hd, t / 8, d)];
+  return oracle_mx_dequant((uint8_t)((w >> (4 * (t % 8))) & 15u), L.v_scale[L.vs(hd, t / 32, d)]);
+}
+
+// Quantize tokens [t0, t0 + n) of every head (t0 and n multiples of 32) from
+// fp16 sources [head][n][D] with the given head stride (elements).
+int oracle_mx_quantize_pack(int32_t D, int64_t t_cap, uint32_t* k_words, uint8_t* k_scale,
+                            uint32_t* v_words, uint8_t* v_scale, int64_t n_heads,
+                            const uint16_t* k_src, const uint16_t* v_src,
+                            int64_t src_head_stride, int64_t t0, int64_t n, int32_t n_threads) {
+  if (D <= 0 || D % 32 || t_cap <= 0 || t_cap % 32) return -1;
+  if (t0 < 0 || n < 0 || t0 % 32 || n % 32 || t0 + n > t_cap) return -1;
+  MxLayout L{D, t_cap, k_words, k_scale, v_words, v_scale};
+  run_heads(n_heads, n_threads, [&](int64_t hd) {
+    const uint16_t* ks = k_src + hd * src_head_stride;
+    const uint16_t* vs = v_src + hd * src_head_stride;
+    uint8_t codes[32];
+    for (int64_t i = 0; i < n; ++i)            // keys: 32 channels of a token
+      for (int32_t c = 0; c < D / 32; ++c) {
+        const uint16_t* x = ks + i * D + 32 * c;
+        const int32_t E = oracle_mx_exponent(x, 32, 1);
+        mx_block(x, 1, E, codes);
+        L.k_scale[L.ks(hd, t0 + i, c)] = (uint8_t)(E + 127);
+        for (int32_t w = 0; w < 4; ++w) oracle_pack(codes + 8 * w, 8, 4, &L.k_words[L.kw(hd, t0 + i, 4 * c + w)]);
+      }
+    for (int64_t b = 0; b < n / 32; ++b)       // values: 32 tokens of a channel
+      for (int32_t d = 0; d < D; ++d) {
+        const uint16_t* x = vs + (32 * b) * D + d;
+        const int32_t E = oracle_mx_exponent(x, 32, D);
+        mx_block(x, D, E, codes);
+        L.v_scale[L.vs(hd, t0 / 32 + b, d)] = (uint8_t)(E + 127);
+        for (int32_t w = 0; w < 4; ++w)
+          oracle_pack(codes + 8 * w, 8, 4, &L.v_words[L.vw(hd, t0 / 8 + 4 * b + w, d)]);
+      }
+  });
+  return 0;
+}
+
+// fp32 dequantized K and V of tokens [t0, t0 + n), written [head][n][D].
+int oracle_mx_dequantize(int32_t D, int64_t t_cap, const uint32_t* k_words,
+                         const uint8_t* k_scale, const uint32_t* v_words,
+                         const uint8_t* v_scale, int64_t n_heads, int64_t t0, int64_t n,
+                         float* k_out, float* v_out, int32_t n_threads) {
+  if (D <= 0 || D % 32 || t_cap <= 0 || t_cap % 32 || t0 < 0 || n < 0 || t0 + n > t_cap)
+    return -1;
+  MxLayout L{D, t_cap, const_cast<uint32_t*>(k_words), const_cast<uint8_t*>(k_scale),
+             const_cast<uint32_t*>(v_words), const_cast<uint8_t*>(v_scale)};
+  run_heads(n_heads, n_threads, [&](int64_t hd) {
+    for (int64_t i = 0; i < n; ++i)
+      for (int32_t d = 0; d < D; ++d) {
+        k_out[(hd * n + i) * D + d] = mx_key_at(L, hd, t0 + i, d);
+        v_out[(hd * n + i) * D + d] = mx_value_at(L, hd, t0 + i, d);
+      }
+  });
+  return 0;
+}
+
+// Decode attention over the MXFP4 cache: as oracle_decode_attention, with the
+// quantized tokens [0, n_quant) dequantized as above (n_quant a multiple of 32).
+int oracle_mx_decode_attention(int32_t D, int64_t t_cap, const uint32_t* k_words,
+                               const uint8_t* k_scale, const uint32_t* v_words,
+                               const uint8_t* v_scale, int32_t B, int32_t H_q, int32_t H_kv,
+                               const uint16_t* q, int64_t n_quant, const uint16_t* k_sink,
+                               const uint16_t* v_sink, int32_t n_sink, int32_t sink_cap,
+                               const uint16_t* k_res, const uint16_t* v_res, int32_t n_res,
+                               int32_t res_cap, double sm, double* out, int32_t n_threads) {
+  if (D <= 0 || D % 32 || t_cap <= 0 || t_cap % 32) return -1;
+  if (B <= 0 || H_kv <= 0 || H_q % H_kv || n_quant < 0 || n_quant % 32 || n_quant > t_cap)
+    return -1;
+  if (n_sink < 0 || n_sink > sink_cap || n_res < 0 || n_res > res_cap) return -1;
+  MxLayout L{D, t_cap, const_cast<uint32_t*>(k_words), const_cast<uint8_t*>(k_scale),
+             const_cast<uint32_t*>(v_words), const_cast<uint8_t*>(v_scale)};
+  if (sm <= 0.0) sm = 1.0 / std::sqrt((double)D);
+  const int32_t gq = H_q / H_kv;
+  run_heads((int64_t)B * H_kv, n_threads, [&](int64_t hd) {
+    const int64_t n = n_sink + n_quant + n_res;
+    std::vector<double> K((size_t)n * D), V((size_t)n * D);
+    int64_t t = 0;
+    for (int32_t i = 0; i < n_sink; ++i, ++t)
+      for (int32_t d = 0; d < D; ++d) {
+        K[t * D + d] = oracle_f16_to_f64(k_sink[(hd * sink_cap + i) * D + d]);
+        V[t * D + d] = oracle_f16_to_f64(v_sink[(hd * sink_cap + i) * D + d]);
+      }
+    for (int64_t i = 0; i < n_quant; ++i, ++t)
+      for (int32_t d = 0; d < D; ++d) {
+        K[t * D + d] = mx_key_at(L, hd, i, d);
+        V[t * D + d] = mx_value_at(L, hd, i, d);
+      }
+    for (int32_t i = 0; i < n_res; ++i, ++t)
+      for (int32_t d = 0; d < D; ++d) {
+        K[t * D + d] = oracle_f16_to_f64(k_res[(hd * res_cap + i) * D + d]);
+        V[t * D + d] = oracle_f16_to_f64(v_res[(hd * res_cap + i) * D + d]);
+      }
+    const int64_t b = hd / H_kv, hk = hd % H_kv;
+    std::vector<double> qd(D);
+    for (int32_t j = 0; j < gq; ++j) {
+      const int64_t h = hk * gq + j;
+      for (int32_t d = 0; d < D; ++d) qd[d] = oracle_f16_to_f64(q[(b * H_q + h) * D + d]);
+      oracle_attention_fp64(qd.data(), K.data(), V.data(), n, D, sm, &out[(b * H_q + h) * D]);
+    }
+  });
+  return 0;
+}
+
 }  // extern "C"
 
 static void run_heads(int64_t n_heads, int32_t n_threads,
