@@ -34,13 +34,20 @@ KVQ_WS_COUNTER_BYTES = 262144
 EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_step",
             "kvq_decode_partials", "kvq_decode_merge", "kvq_dequantize",
-            "kvq_decode_attention_ragged", "kvq_decode_partials_ragged", "kvq_stream_read")
+            "kvq_decode_attention_ragged", "kvq_decode_partials_ragged", "kvq_stream_read",
+            "kvq_mx_quantize_pack", "kvq_mx_dequantize")
 
 
 class kvq_qcfg(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("n_boost", ctypes.c_int32),
                 ("v_bits", ctypes.c_int32), ("boost_score", ctypes.c_int32)]
+
+
+class kvq_mx_cache(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("t_cap", ctypes.c_int64)]
 
 
 class kvq_cache(ctypes.Structure):
@@ -86,6 +93,10 @@ _lib.kvq_decode_partials_ragged.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, 
 _lib.kvq_decode_partials_ragged.restype = ctypes.c_int
 _lib.kvq_dequantize.argtypes = [_P, _P, _i32, _i32, _i64, _i64, _P, _P, _P]
 _lib.kvq_stream_read.argtypes = [_P, _sz, _P, _i32, _i32, _i32, _P]
+_lib.kvq_mx_quantize_pack.argtypes = [_P, _i32, _i32, _P, _P, _i64, _i64, _i64, _P]
+_lib.kvq_mx_quantize_pack.restype = ctypes.c_int
+_lib.kvq_mx_dequantize.argtypes = [_P, _i32, _i32, _i64, _i64, _P, _P, _P]
+_lib.kvq_mx_dequantize.restype = ctypes.c_int
 _lib.kvq_stream_read.restype = ctypes.c_int
 _lib.kvq_dequantize.restype = ctypes.c_int
 
@@ -335,6 +346,48 @@ def kvq_dequantize(cfg: QCfg, cache: Cache, B: int, H_kv: int, first_group: int,
     _check(_lib.kvq_dequantize(ctypes.byref(c_cfg), ctypes.byref(c_cache), B, H_kv,
                                first_group, n_groups, _ptr(k_out), _ptr(v_out),
                                _stream(stream)), "kvq_dequantize")
+
+
+@dataclass
+class MxCache:
+    """MXFP4 cache tensors (layout in include/kvq.h), ``heads`` = B*H_kv."""
+    t_cap: int
+    heads: int
+    k_codes: torch.Tensor
+    k_scale: torch.Tensor
+    v_codes: torch.Tensor
+    v_scale: torch.Tensor
+
+    @staticmethod
+    def empty(heads: int, t_cap: int, head_dim: int = 128, device="cuda") -> "MxCache":
+        H, T, D = heads, t_cap, head_dim
+        z = dict(device=device)
+        return MxCache(t_cap, heads,
+                       k_codes=torch.zeros((H, T, D // 8), dtype=torch.int32, **z),
+                       k_scale=torch.zeros((H, T, D // 32), dtype=torch.uint8, **z),
+                       v_codes=torch.zeros((H, T // 8, D), dtype=torch.int32, **z),
+                       v_scale=torch.zeros((H, T // 32, D), dtype=torch.uint8, **z))
+
+    def c(self) -> kvq_mx_cache:
+        return kvq_mx_cache(_ptr(self.k_codes), _ptr(self.k_scale), _ptr(self.v_codes),
+                            _ptr(self.v_scale), self.t_cap)
+
+
+def kvq_mx_quantize_pack(cache: MxCache, B: int, H_kv: int, k_src: torch.Tensor,
+                         v_src: torch.Tensor, first_token: int, n_tokens: int,
+                         stream=None) -> None:
+    """k_src / v_src: fp16 ``[B*H_kv][>= n_tokens][D]``."""
+    c = cache.c()
+    _check(_lib.kvq_mx_quantize_pack(ctypes.byref(c), B, H_kv, _ptr(k_src), _ptr(v_src),
+                                     k_src.stride(0), first_token, n_tokens, _stream(stream)),
+           "kvq_mx_quantize_pack")
+
+
+def kvq_mx_dequantize(cache: MxCache, B: int, H_kv: int, first_token: int, n_tokens: int,
+                      k_out: torch.Tensor, v_out: torch.Tensor, stream=None) -> None:
+    c = cache.c()
+    _check(_lib.kvq_mx_dequantize(ctypes.byref(c), B, H_kv, first_token, n_tokens, _ptr(k_out),
+                                  _ptr(v_out), _stream(stream)), "kvq_mx_dequantize")
 
 
 def kvq_stream_read(src: torch.Tensor, sink: torch.Tensor, blocks: int, threads: int,

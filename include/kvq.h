@@ -289,6 +289,44 @@ kvq_status kvq_dequantize(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
                           int64_t first_group, int64_t n_groups, float* k_out, float* v_out,
                           void* stream);
 
+/* MXFP4 cache (BitDecoding page, section on native low-precision formats:
+ * mxfp4 / nvfp4 data with block scale factors in the layout the matrix units
+ * take; the format is the OCP microscaling one).  D = 128.  A block of 32
+ * values shares the scale 2^E, E = floor(log2 max|x|) - 2, stored as the E8M0
+ * byte E + 127 (a block of zeros: E = -127); each value is the nearest E2M1
+ * number to x / 2^E (0, 0.5, 1, 1.5, 2, 3, 4, 6 with a sign; ties to the even
+ * mantissa bit; magnitudes past 6 saturate), one nibble, least significant
+ * first.  Blocks run along each product's contraction axis.  Per head
+ * (b*H_kv + h), t_cap token slots (a multiple of 32):
+ *    k_codes  [head][t_cap][D/8]    nibble j of word (t,w): channel 8w+j
+ *    k_scale  [head][t_cap][D/32]   E8M0 of channels 32c..32c+31 of token t
+ *    v_codes  [head][t_cap/8][D]    nibble j of word (w,d): token 8w+j
+ *    v_scale  [head][t_cap/32][D]   E8M0 of tokens 32b..32b+31 of channel d
+ * Caller-owned device memory, 16-byte aligned. */
+typedef struct kvq_mx_cache {
+  int32_t* k_codes;
+  uint8_t* k_scale;
+  int32_t* v_codes;
+  uint8_t* v_scale;
+  int64_t t_cap;
+} kvq_mx_cache;
+
+/* Quantize tokens [first_token, first_token + n_tokens) of every head
+ * (both multiples of 32) from fp16 [head][n_tokens][D] with the given head
+ * stride (elements, a multiple of 8).  Writes those tokens' codes and
+ * scales only.  Errors: KVQ_ERR_ARG (bad sizes or range), KVQ_ERR_ALIGN. */
+kvq_status kvq_mx_quantize_pack(const kvq_mx_cache* cache, int32_t B, int32_t H_kv,
+                                const uint16_t* k_src, const uint16_t* v_src,
+                                int64_t src_head_stride, int64_t first_token, int64_t n_tokens,
+                                void* stream);
+
+/* Dequantize tokens [first_token, first_token + n_tokens) of every head to
+ * fp32 [head][n_tokens][D] (value = E2M1 value * 2^E, exact).  For checking
+ * the packed cache. */
+kvq_status kvq_mx_dequantize(const kvq_mx_cache* cache, int32_t B, int32_t H_kv,
+                             int64_t first_token, int64_t n_tokens, float* k_out, float* v_out,
+                             void* stream);
+
 /* Measurement aid, not part of the method: read `bytes` bytes at `src` once
  * (16-byte loads, `blocks` workgroups of `threads` lanes, each workgroup a
  * contiguous slice) and write nothing but a word that depends on every byte

@@ -211,3 +211,33 @@ def test_partials_reject_bad_arguments():
 ])
 def test_stream_read_validation(args, want):
     assert kvq.raw_call("kvq_stream_read", *args, None) == want
+
+
+def _mx(t_cap=1024, align=0):
+    p = FAKE + align
+    return kvq.kvq_mx_cache(p, p, p, p, t_cap)
+
+
+@pytest.mark.parametrize("cache,args,want", [
+    (None, (1, 1, FAKE, FAKE, 4096, 0, 32), kvq.KVQ_ERR_ARG),
+    (_mx(t_cap=1000), (1, 1, FAKE, FAKE, 4096, 0, 32), kvq.KVQ_ERR_ARG),
+    (_mx(align=4), (1, 1, FAKE, FAKE, 4096, 0, 32), kvq.KVQ_ERR_ALIGN),
+    (_mx(), (0, 1, FAKE, FAKE, 4096, 0, 32), kvq.KVQ_ERR_ARG),
+    (_mx(), (1, 1, FAKE, FAKE, 4096, 16, 32), kvq.KVQ_ERR_ARG),    # not a whole block
+    (_mx(), (1, 1, FAKE, FAKE, 4096, 0, 48), kvq.KVQ_ERR_ARG),
+    (_mx(), (1, 1, FAKE, FAKE, 4096, 1024, 32), kvq.KVQ_ERR_ARG),  # past t_cap
+    (_mx(), (1, 1, None, FAKE, 4096, 0, 32), kvq.KVQ_ERR_ARG),
+    (_mx(), (1, 1, FAKE, FAKE, 100, 0, 32), kvq.KVQ_ERR_ARG),      # stride below n*D
+    (_mx(), (1, 1, FAKE + 2, FAKE, 4096, 0, 32), kvq.KVQ_ERR_ALIGN),
+])
+def test_mx_quantize_validation(cache, args, want):
+    c = ctypes.byref(cache) if cache is not None else None
+    assert kvq.raw_call("kvq_mx_quantize_pack", c, *args, None) == want
+
+
+def test_mx_dequantize_validation():
+    c = _mx()
+    assert kvq.raw_call("kvq_mx_dequantize", ctypes.byref(c), 1, 1, 1000, 32, FAKE, FAKE,
+                        None) == kvq.KVQ_ERR_ARG
+    assert kvq.raw_call("kvq_mx_dequantize", ctypes.byref(c), 1, 1, 0, 32, FAKE + 8, FAKE,
+                        None) == kvq.KVQ_ERR_ALIGN

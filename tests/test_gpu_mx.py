@@ -1,0 +1,65 @@
+"""GPU parity of the MXFP4 cache (32-value blocks, E8M0 scale, E2M1 values):
+quantize + pack and dequantize through the C ABI against the CPU oracle on
+the same seeded inputs, bit for bit, including blocks of zeros, fp16
+subnormals, values near the fp16 maximum and exact rounding ties."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _inputs(heads, n, seed):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((heads, n, D)).astype(np.float32)
+    k[:, :, 3] *= 40.0                                   # an outlier channel
+    k[:, 5, :] = 0.0                                     # a token of zeros: key blocks of 0
+    k[:, 9, 64:96] *= 2.0 ** -20                         # fp16 subnormals
+    k[:, 11, :32] = rng.choice([-1, 1], 32) * 60000.0    # near the fp16 maximum
+    # exact ties: a block whose largest magnitude is 4 * 2^E and the rest midpoints
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.0])
+    k[:, 13, 32:64] = np.resize(np.concatenate([[4.0], mids]), 32) * 2.0 ** -3
+    v = (rng.standard_normal((heads, n, D)) * rng.uniform(0.05, 20.0, (1, 1, D))).astype(np.float32)
+    v[:, 32:64, 7] = 0.0                                 # a value block of zeros
+    v[:, 64:96, 8] = np.resize(np.concatenate([[6.0], -mids]), 32) * 2.0 ** 2
+    return k.astype(np.float16), v.astype(np.float16)
+
+
+def _compare(gc, oc, t_hi):
+    assert np.array_equal(gc.k_codes.cpu().numpy().view(np.uint32)[:, :t_hi], oc.k_words[:, :t_hi])
+    assert np.array_equal(gc.k_scale.cpu().numpy()[:, :t_hi], oc.k_scale[:, :t_hi])
+    assert np.array_equal(gc.v_codes.cpu().numpy().view(np.uint32)[:, : t_hi // 8],
+                          oc.v_words[:, : t_hi // 8])
+    assert np.array_equal(gc.v_scale.cpu().numpy()[:, : t_hi // 32], oc.v_scale[:, : t_hi // 32])
+
+
+@pytest.mark.parametrize("B,H_kv,n", [(1, 2, 256), (2, 3, 96)])
+def test_mx_quantize_append_dequantize_bit_exact(B, H_kv, n):
+    import bit_kv_cache_amd as kvq
+    heads = B * H_kv
+    t_cap = n + 64
+    k, v = _inputs(heads, n + 32, seed=31 + n)
+    kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    gc = kvq.MxCache.empty(heads, t_cap)
+    kvq.kvq_mx_quantize_pack(gc, B, H_kv, kt[:, :n], vt[:, :n], 0, n)
+    # the next 32 tokens appended as their own call
+    kvq.kvq_mx_quantize_pack(gc, B, H_kv, kt[:, n:], vt[:, n:], n, 32)
+    oc = oracle.mx_empty_cache(D, t_cap, heads)
+    oracle.mx_quantize_pack(oc, k.view(np.uint16)[:, :n], v.view(np.uint16)[:, :n], 0, n)
+    oracle.mx_quantize_pack(oc, k.view(np.uint16)[:, n:], v.view(np.uint16)[:, n:], n, 32)
+    torch.cuda.synchronize()
+    _compare(gc, oc, n + 32)
+    # slots past the appended block stay untouched
+    assert int(gc.k_codes[:, n + 32:].abs().sum()) == 0 and int(gc.k_scale[:, n + 32:].sum()) == 0
+    ko = torch.empty((heads, n + 32, D), dtype=torch.float32, device="cuda")
+    vo = torch.empty_like(ko)
+    kvq.kvq_mx_dequantize(gc, B, H_kv, 0, n + 32, ko, vo)
+    kr, vr = oracle.mx_dequantize(oc, 0, n + 32)
+    torch.cuda.synchronize()
+    assert np.array_equal(ko.cpu().numpy().view(np.uint32), kr.view(np.uint32))
+    assert np.array_equal(vo.cpu().numpy().view(np.uint32), vr.view(np.uint32))
