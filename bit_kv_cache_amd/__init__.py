@@ -35,7 +35,8 @@ EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_step",
             "kvq_decode_partials", "kvq_decode_merge", "kvq_dequantize",
             "kvq_decode_attention_ragged", "kvq_decode_partials_ragged", "kvq_stream_read",
-            "kvq_mx_quantize_pack", "kvq_mx_dequantize")
+            "kvq_mx_quantize_pack", "kvq_mx_dequantize", "kvq_mx_decode_plan",
+            "kvq_mx_decode_attention")
 
 
 class kvq_qcfg(ctypes.Structure):
@@ -97,6 +98,11 @@ _lib.kvq_mx_quantize_pack.argtypes = [_P, _i32, _i32, _P, _P, _i64, _i64, _i64, 
 _lib.kvq_mx_quantize_pack.restype = ctypes.c_int
 _lib.kvq_mx_dequantize.argtypes = [_P, _i32, _i32, _i64, _i64, _P, _P, _P]
 _lib.kvq_mx_dequantize.restype = ctypes.c_int
+_lib.kvq_mx_decode_plan.argtypes = [_i32, _i32, _i32, _i64, _i32, _P, _P]
+_lib.kvq_mx_decode_plan.restype = ctypes.c_int
+_lib.kvq_mx_decode_attention.argtypes = [_P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32, _P,
+                                         _sz, _P, _P]
+_lib.kvq_mx_decode_attention.restype = ctypes.c_int
 _lib.kvq_stream_read.restype = ctypes.c_int
 _lib.kvq_dequantize.restype = ctypes.c_int
 
@@ -388,6 +394,28 @@ def kvq_mx_dequantize(cache: MxCache, B: int, H_kv: int, first_token: int, n_tok
     c = cache.c()
     _check(_lib.kvq_mx_dequantize(ctypes.byref(c), B, H_kv, first_token, n_tokens, _ptr(k_out),
                                   _ptr(v_out), _stream(stream)), "kvq_mx_dequantize")
+
+
+def kvq_mx_decode_plan(B: int, H_q: int, H_kv: int, n_quant_tokens: int,
+                       n_chunks: int = 0) -> tuple[int, int]:
+    """(chunks per head, workspace bytes) of an MXFP4 decode."""
+    nc, ws = ctypes.c_int32(0), ctypes.c_size_t(0)
+    _check(_lib.kvq_mx_decode_plan(B, H_q, H_kv, n_quant_tokens, n_chunks, ctypes.byref(nc),
+                                   ctypes.byref(ws)), "kvq_mx_decode_plan")
+    return nc.value, ws.value
+
+
+def kvq_mx_decode_attention(cache: MxCache, B: int, H_q: int, H_kv: int, q: torch.Tensor,
+                            n_quant_tokens: int, sink, res, out: torch.Tensor,
+                            workspace: torch.Tensor, sm_scale: float = 0.0, n_chunks: int = 0,
+                            stream=None) -> None:
+    c = cache.c()
+    _check(_lib.kvq_mx_decode_attention(
+        ctypes.byref(c), B, H_q, H_kv, _ptr(q), n_quant_tokens,
+        ctypes.byref(sink) if sink is not None else None,
+        ctypes.byref(res) if res is not None else None, ctypes.c_float(sm_scale), n_chunks,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        _stream(stream)), "kvq_mx_decode_attention")
 
 
 def kvq_stream_read(src: torch.Tensor, sink: torch.Tensor, blocks: int, threads: int,

@@ -128,6 +128,132 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
   __syncthreads();
 }
 
+// --------------------------------------------------------- MXFP4 block
+// E2M1 value of a code (sign bit 3; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6)
+__device__ __forceinline__ float e2m1(uint32_t code) {
+  const uint32_t i = code & 7u;
+  const float mag = i < 4 ? 0.5f * (float)i : (float)(2u << ((i - 4) >> 1)) * (1.f + 0.5f * (i & 1u));
+  return (code & 8u) ? -mag : mag;
+}
+// 2^(e8m0 - 127) for the byte range a block exponent of fp16 data can take
+__device__ __forceinline__ float e8m0_scale(uint32_t e) { return ldexpf(1.f, (int)e - 127); }
+
+// Tokens [t0, t0+nt) of an MXFP4 cache head (t0, nt multiples of 32,
+// nt <= kBlockTok): key blocks of 32 channels per token, value blocks of 32
+// tokens per channel; each block's sum over its E2M1 values is scaled by 2^E
+// once (exact: a power of two).
+template <int GQA>
+__device__ void mx_block(const DecodeArgs& a, const kvq_mx_cache& mc, Lds<GQA>& s, int64_t head,
+                         int64_t t0, int nt, float (&acc)[GQA]) {
+  const int tid = threadIdx.x;
+  // q.k: thread (token t, channel half = two key blocks)
+  {
+    const int t = tid & (kBlockTok - 1), half = tid >> 7;
+    if (t < nt) {
+      const int64_t row = head * mc.t_cap + t0 + t;
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(mc.k_codes) + row * (kD / 8) + 8 * half;
+      float dot[GQA];
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) dot[h] = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int c0 = 64 * half + 32 * blk;
+        float part[GQA];
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) part[h] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t word = __builtin_nontemporal_load(kw + 4 * blk + w);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = e2m1((word >> (4 * j)) & 15u);
+#pragma unroll
+            for (int h = 0; h < GQA; ++h) part[h] = fmaf(s.q[h][c0 + 8 * w + j], x, part[h]);
+          }
+        }
+        const float sc = e8m0_scale(mc.k_scale[row * (kD / 32) + 2 * half + blk]);
+#pragma unroll
+        for (int h = 0; h < GQA; ++h) dot[h] = fmaf(part[h], sc, dot[h]);
+      }
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) s.part[half][h][t] = dot[h];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < GQA * nt; i += kThreads) {
+    const int h = i / nt, t = i % nt;
+    s.p[h][t] = s.part[0][h][t] + s.part[1][h][t];
+  }
+  __syncthreads();
+  softmax_block<GQA>(s, nt);
+  __syncthreads();
+  // p.v: thread (channel d, token half = two value blocks)
+  {
+    const int d = tid & (kD - 1), half = tid >> 7;
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) acc[h] *= s.alpha[h];
+    for (int blk = 0; blk < 2; ++blk) {
+      const int tb = 64 * half + 32 * blk;   // block's first token in the tile
+      if (tb >= nt) break;
+      const int64_t tg = t0 + tb;
+      float part[GQA];
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) part[h] = 0.f;
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(mc.v_codes) +
+                           (head * (mc.t_cap / 8) + tg / 8) * kD + d;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t word = __builtin_nontemporal_load(vw + w * kD);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = e2m1((word >> (4 * j)) & 15u);
+#pragma unroll
+          for (int h = 0; h < GQA; ++h) part[h] = fmaf(s.p[h][tb + 8 * w + j], x, part[h]);
+        }
+      }
+      const float sc = e8m0_scale(mc.v_scale[(head * (mc.t_cap / 32) + tg / 32) * kD + d]);
+#pragma unroll
+      for (int h = 0; h < GQA; ++h) acc[h] = fmaf(part[h], sc, acc[h]);
+    }
+  }
+  __syncthreads();
+}
+
+// grid: (n_chunks + 1, B * H_kv); part n_chunks is the fp16 windows.  A
+// chunk is groups_per_chunk blocks of 32 tokens.
+template <int GQA>
+__global__ __launch_bounds__(kThreads) void decode_mx_kernel(DecodeArgs a, kvq_mx_cache mc) {
+  __shared__ Lds<GQA> s;
+  const int tid = threadIdx.x;
+  const int part = blockIdx.x;
+  const int64_t head = blockIdx.y;
+  const int64_t b = head / a.H_kv, hk = head % a.H_kv;
+  for (int i = tid; i < GQA * kD; i += kThreads) {
+    const int h = i / kD, d = i % kD;
+    s.q[h][d] = h2f(a.q[((b * a.H_q) + hk * GQA + h) * kD + d]) * a.qscale;
+  }
+  if (tid < GQA) {
+    s.m[tid] = kNegInf;
+    s.l[tid] = 0.f;
+  }
+  if (tid == 0) s.bad = 0;
+  __syncthreads();
+  float acc[GQA];
+#pragma unroll
+  for (int h = 0; h < GQA; ++h) acc[h] = 0.f;
+  if (part < a.n_chunks) {
+    const int64_t tb = (int64_t)part * a.groups_per_chunk * 32;
+    const int64_t te = min<int64_t>(a.n_groups, (int64_t)(part + 1) * a.groups_per_chunk) * 32;
+    for (int64_t t = tb; t < te; t += kBlockTok)
+      mx_block<GQA>(a, mc, s, head, t, (int)min<int64_t>(kBlockTok, te - t), acc);
+  } else {
+    const int n_win = a.n_sink + a.n_res;
+    for (int u = 0; u < n_win; u += kBlockTok)
+      window_block<GQA>(a, s, head, u, min(kBlockTok, n_win - u), acc);
+  }
+  write_partial<GQA>(a, s, b, hk, part, acc);
+}
+
 // grid: (n_chunks + 1, B * H_kv); part n_chunks is the fp16 windows
 template <int BITS, int VB, int G, int GQA>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
@@ -276,6 +402,18 @@ hipError_t launch_decode_partials(int bits, int v_bits, int group, const DecodeA
              : (bits == 2   ? decode_bits<2, 2>(group, a, st)
                 : bits == 4 ? decode_bits<4, 4>(group, a, st)
                             : decode_bits<8, 8>(group, a, st));
+}
+
+hipError_t launch_decode_mx(const kvq_mx_cache& mc, const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.n_chunks + 1), (unsigned)(a.B * a.H_kv));
+  switch (a.gqa) {
+    case 1: decode_mx_kernel<1><<<grid, kThreads, 0, st>>>(a, mc); break;
+    case 2: decode_mx_kernel<2><<<grid, kThreads, 0, st>>>(a, mc); break;
+    case 4: decode_mx_kernel<4><<<grid, kThreads, 0, st>>>(a, mc); break;
+    case 8: decode_mx_kernel<8><<<grid, kThreads, 0, st>>>(a, mc); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st) {

@@ -3,6 +3,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "kvq.h"
 #include "kvq_internal.h"
 
@@ -407,6 +409,75 @@ kvq_status kvq_dequantize(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
                      cfg->n_boost};
   return hip_status(kvq::launch_dequantize(cfg->bits, vbits(cfg), cfg->group, a,
                                            static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_mx_decode_plan(int32_t B, int32_t H_q, int32_t H_kv, int64_t n_quant_tokens,
+                              int32_t n_chunks_req, int32_t* n_chunks, size_t* ws_bytes) {
+  if (B <= 0 || H_kv <= 0 || H_q <= 0 || H_q % H_kv) return KVQ_ERR_ARG;
+  const int32_t gqa = H_q / H_kv;
+  if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KVQ_ERR_UNSUPPORTED;
+  if (n_quant_tokens < 0 || n_quant_tokens % 32 || n_chunks_req < 0) return KVQ_ERR_ARG;
+  const int64_t heads = (int64_t)B * H_kv;
+  if (heads > 65535) return KVQ_ERR_ARG;
+  const int64_t blocks = n_quant_tokens / 32;
+  int64_t n = n_chunks_req;
+  if (n == 0) n = (512 + heads - 1) / heads;   // about two blocks per CU
+  n = std::max<int64_t>(1, std::min<int64_t>(n, std::max<int64_t>(1, blocks)));
+  if (n > 65535) return KVQ_ERR_ARG;
+  if (n_chunks) *n_chunks = (int32_t)n;
+  if (ws_bytes) *ws_bytes = workspace_bytes(B, H_q, n + 1);
+  return KVQ_OK;
+}
+
+kvq_status kvq_mx_decode_attention(const kvq_mx_cache* cache, int32_t B, int32_t H_q,
+                                   int32_t H_kv, const uint16_t* q, int64_t n_quant_tokens,
+                                   const kvq_window* sink, const kvq_window* res, float sm_scale,
+                                   int32_t n_chunks_req, void* workspace, size_t ws_bytes,
+                                   float* out, void* stream) {
+  if (!cache || !cache->k_codes || !cache->k_scale || !cache->v_codes || !cache->v_scale)
+    return KVQ_ERR_ARG;
+  if (cache->t_cap <= 0 || cache->t_cap % 32 || n_quant_tokens > cache->t_cap) return KVQ_ERR_ARG;
+  if (!aligned16(cache->k_codes) || !aligned16(cache->k_scale) || !aligned16(cache->v_codes) ||
+      !aligned16(cache->v_scale))
+    return KVQ_ERR_ALIGN;
+  int32_t nc = 0;
+  size_t need = 0;
+  kvq_status st = kvq_mx_decode_plan(B, H_q, H_kv, n_quant_tokens, n_chunks_req, &nc, &need);
+  if (st != KVQ_OK) return st;
+  if ((st = check_window(sink)) != KVQ_OK || (st = check_window(res)) != KVQ_OK) return st;
+  if (!q || !out) return KVQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (!(sm_scale > 0.f)) sm_scale = 1.0f / sqrtf((float)kD);
+  kvq::DecodeArgs a{};
+  a.q = q;
+  a.B = B;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.gqa = H_q / H_kv;
+  a.n_groups = n_quant_tokens / 32;
+  a.n_chunks = nc;
+  a.groups_per_chunk = (int32_t)((a.n_groups + nc - 1) / nc);
+  if (sink && sink->n > 0) {
+    a.k_sink = sink->k;
+    a.v_sink = sink->v;
+    a.n_sink = sink->n;
+    a.sink_cap = sink->cap;
+  }
+  if (res && res->n > 0) {
+    a.k_res = res->k;
+    a.v_res = res->v;
+    a.n_res = res->n;
+    a.res_cap = res->cap;
+  }
+  a.qscale = sm_scale * 1.4426950408889634f;
+  a.n_parts = nc + 1;
+  a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kvq::kCounterBytes);
+  a.out = out;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(kvq::launch_decode_mx(*cache, a, s))) != KVQ_OK) return st;
+  return hip_status(kvq::launch_merge(a, s));
 }
 
 }  // extern "C"

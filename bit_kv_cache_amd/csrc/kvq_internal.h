@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "kvq.h"
 #include <stdint.h>
 
 namespace kvq {
@@ -165,6 +167,10 @@ hipError_t launch_dequantize(int bits, int v_bits, int group, const DequantArgs&
 hipError_t launch_decode_partials(int bits, int v_bits, int group, const DecodeArgs& a,
                                   hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+// Split-K decode over an MXFP4 cache (vector ALU): a.n_groups counts blocks
+// of 32 tokens, a.groups_per_chunk too; parts n_chunks + 1 (the last is the
+// fp16 windows).
+hipError_t launch_decode_mx(const kvq_mx_cache& mc, const DecodeArgs& a, hipStream_t s);
 // The merge of a decode step and the quantize of an appended group (both
 // small, latency-bound) as one launch; separate launches when the step has
 // more than kMergeAppendParts parts.

@@ -327,6 +327,22 @@ kvq_status kvq_mx_dequantize(const kvq_mx_cache* cache, int32_t B, int32_t H_kv,
                              int64_t first_token, int64_t n_tokens, float* k_out, float* v_out,
                              void* stream);
 
+/* Decode attention over an MXFP4 cache: the same result as
+ * kvq_decode_attention (sink | tokens [0, n_quant_tokens) | residual, fp32
+ * output), the quantized keys and values read as E2M1 value * 2^E.
+ * n_quant_tokens a multiple of 32 (0 allowed).  Split-K over chunks of
+ * 32-token blocks on the vector ALU, then the log-sum-exp merge.
+ * kvq_mx_decode_plan gives the chunk count (n_chunks_req = 0: automatic) and
+ * the workspace size (arrival counters, then B*H_q*(n_chunks+1)*(D+2) fp32
+ * partials); errors as kvq_decode_attention. */
+kvq_status kvq_mx_decode_plan(int32_t B, int32_t H_q, int32_t H_kv, int64_t n_quant_tokens,
+                              int32_t n_chunks_req, int32_t* n_chunks, size_t* ws_bytes);
+kvq_status kvq_mx_decode_attention(const kvq_mx_cache* cache, int32_t B, int32_t H_q,
+                                   int32_t H_kv, const uint16_t* q, int64_t n_quant_tokens,
+                                   const kvq_window* sink, const kvq_window* res, float sm_scale,
+                                   int32_t n_chunks, void* workspace, size_t ws_bytes, float* out,
+                                   void* stream);
+
 /* Measurement aid, not part of the method: read `bytes` bytes at `src` once
  * (16-byte loads, `blocks` workgroups of `threads` lanes, each workgroup a
  * contiguous slice) and write nothing but a word that depends on every byte

@@ -241,3 +241,17 @@ def test_mx_dequantize_validation():
                         None) == kvq.KVQ_ERR_ARG
     assert kvq.raw_call("kvq_mx_dequantize", ctypes.byref(c), 1, 1, 0, 32, FAKE + 8, FAKE,
                         None) == kvq.KVQ_ERR_ALIGN
+
+
+def test_mx_decode_plan_validation():
+    def plan(*a):
+        n, w = ctypes.c_int32(0), ctypes.c_size_t(0)
+        return kvq.raw_call("kvq_mx_decode_plan", *a, ctypes.byref(n), ctypes.byref(w)), n.value
+    assert plan(1, 32, 8, 512, 0)[0] == kvq.KVQ_OK
+    assert plan(1, 32, 8, 500, 0)[0] == kvq.KVQ_ERR_ARG      # not whole 32-token blocks
+    assert plan(1, 48, 8, 512, 0)[0] == kvq.KVQ_ERR_UNSUPPORTED
+    assert plan(1, 30, 8, 512, 0)[0] == kvq.KVQ_ERR_ARG
+    assert plan(1, 32, 8, 512, 100)[1] == 16                # at most one chunk per block
+    c = _mx()
+    assert kvq.raw_call("kvq_mx_decode_attention", ctypes.byref(c), 1, 32, 8, FAKE, 512, None,
+                        None, ctypes.c_float(0.0), 0, FAKE, 16, FAKE, None) == kvq.KVQ_ERR_WORKSPACE

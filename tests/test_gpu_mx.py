@@ -63,3 +63,46 @@ def test_mx_quantize_append_dequantize_bit_exact(B, H_kv, n):
     torch.cuda.synchronize()
     assert np.array_equal(ko.cpu().numpy().view(np.uint32), kr.view(np.uint32))
     assert np.array_equal(vo.cpu().numpy().view(np.uint32), vr.view(np.uint32))
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,T,S,R", [(1, 32, 8, 512, 5, 40), (2, 16, 2, 224, 0, 17),
+                                              (1, 8, 8, 96, 3, 1), (1, 32, 8, 0, 4, 9)])
+def test_mx_decode_matches_oracle(B, H_q, H_kv, T, S, R):
+    """Decode over the MXFP4 cache (plus fp16 sink and residual windows) at
+    several chunk counts: max-abs within 2e-3 of the oracle's fp64 attention
+    over the same dequantized cache."""
+    import bit_kv_cache_amd as kvq
+    from parity_util import TOL
+    heads = B * H_kv
+    rng = np.random.default_rng(41 + T + H_q)
+    k = rng.standard_normal((heads, max(T, 32), D)).astype(np.float32)
+    k[:, :, 3] *= 10.0
+    v = rng.standard_normal((heads, max(T, 32), D)).astype(np.float32)
+    k, v = k.astype(np.float16), v.astype(np.float16)
+    ks = rng.standard_normal((heads, max(S, 1), D)).astype(np.float16)
+    vs = rng.standard_normal((heads, max(S, 1), D)).astype(np.float16)
+    kr = rng.standard_normal((heads, R + 3, D)).astype(np.float16)
+    vr = rng.standard_normal((heads, R + 3, D)).astype(np.float16)
+    q = rng.standard_normal((B, H_q, D)).astype(np.float16)
+    t_cap = max(T, 32) + 32
+    gc = kvq.MxCache.empty(heads, t_cap)
+    oc = oracle.mx_empty_cache(D, t_cap, heads)
+    if T:
+        kvq.kvq_mx_quantize_pack(gc, B, H_kv, torch.from_numpy(k).cuda(),
+                                 torch.from_numpy(v).cuda(), 0, T)
+        oracle.mx_quantize_pack(oc, k.view(np.uint16), v.view(np.uint16), 0, T)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    ks_d, vs_d, kr_d, vr_d, q_d = dev(ks), dev(vs), dev(kr), dev(vr), dev(q)
+    ref = oracle.mx_decode_attention(oc, B, H_q, H_kv, q.view(np.uint16), T,
+                                     k_sink=ks.view(np.uint16) if S else None,
+                                     v_sink=vs.view(np.uint16) if S else None, n_sink=S,
+                                     k_res=kr.view(np.uint16), v_res=vr.view(np.uint16), n_res=R)
+    for n_chunks in sorted({0, 1, 3, max(1, T // 32)}):
+        _, ws_bytes = kvq.kvq_mx_decode_plan(B, H_q, H_kv, T, n_chunks)
+        ws = kvq.decode_workspace(ws_bytes)
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device="cuda")
+        kvq.kvq_mx_decode_attention(gc, B, H_q, H_kv, q_d, T, kvq.window(ks_d, vs_d, S),
+                                    kvq.window(kr_d, vr_d, R), out, ws, n_chunks=n_chunks)
+        torch.cuda.synchronize()
+        err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
+        assert err <= TOL, f"n_chunks={n_chunks}: max-abs {err:.3g}"
