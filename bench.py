@@ -280,6 +280,9 @@ def main(argv=None):
                     help="after the run, stream 1 GiB in and 1 GiB out 5 times (counter scale)")
     ap.add_argument("--profile-step", action="store_true",
                     help="launch only the warm-up and timed steps (counter runs), then exit")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="time the MXFP4 cache's decode (kvq_mx_decode_attention) on the "
+                         "workload's shape instead")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "CMD"),
                     help="write the profiles/ traffic file from two counter runs and exit")
     args = ap.parse_args(argv)
@@ -304,6 +307,8 @@ def main(argv=None):
         return 2
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
+    if args.mxfp4:
+        return bench_mx(args, w, torch, kvq, synth)
     cache_bytes_one = None
 
     # packed caches (rotated) -----------------------------------------------------
@@ -572,6 +577,70 @@ def stream_read_ceiling(kvq, torch, nbytes, n_copies, stream, reps=50):
                             "loads": "non-temporal" if mode else "ordinary"},
             "sweep": "blocks 256..8192 x threads 256/512/1024 x ordinary/non-temporal loads, "
                      f"{reps} launches back to back per point"}
+
+
+def bench_mx(args, w, torch, kvq, synth):
+    """Decode over an MXFP4 cache of the workload's shape (32-value blocks,
+    E8M0 scales, E2M1 values), its keys and values from the same seeded
+    generator; one JSON line."""
+    D, T, heads = w.D, w.T, w.heads
+    per_head = T * (D // 8 * 4 + D // 32) * 2          # codes + scales, K and V
+    n_copies = min(16, args.copies or max(2, math.ceil(3 * MALL_BYTES / (per_head * heads)) + 1))
+    copies = [kvq.MxCache.empty(heads, T) for _ in range(n_copies)]
+    for h in range(heads):
+        k, v = synth.head_kv(w, h, "cuda")
+        for c in copies:
+            one = kvq.MxCache(T, 1, c.k_codes[h:h + 1], c.k_scale[h:h + 1], c.v_codes[h:h + 1],
+                              c.v_scale[h:h + 1])
+            kvq.kvq_mx_quantize_pack(one, 1, 1, k[None], v[None], 0, T)
+        del k, v
+    wins = [synth.head_windows(w, h, "cuda") for h in range(heads)]
+    k_res = torch.stack([x[2] for x in wins])
+    v_res = torch.stack([x[3] for x in wins])
+    res = kvq.window(k_res, v_res, w.R)
+    sink = None
+    if w.S:
+        sink = kvq.window(torch.stack([x[0] for x in wins]), torch.stack([x[1] for x in wins]), w.S)
+    q = synth.query(w, "cuda")
+    n_chunks, ws_bytes = kvq.kvq_mx_decode_plan(w.B, w.H_q, w.H_kv, T, args.n_chunks)
+    ws = kvq.decode_workspace(ws_bytes)
+    out = torch.empty((w.B, w.H_q, D), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kvq.kvq_mx_decode_attention(copies[i % n_copies], w.B, w.H_q, w.H_kv, q, T, sink, res,
+                                    out, ws, n_chunks=n_chunks, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    n_win = w.S + w.R
+    alg = heads * per_head + heads * n_win * D * 2 * 2 + w.B * w.H_q * D * (2 + 4)
+    gbps = alg / (us * 1e-6) / 1e9
+    sr = stream_read_ceiling(kvq, torch, alg, n_copies, stream)
+    print(json.dumps({
+        "metric": f"decode-attn us/step ({w.name} shape, MXFP4 cache)", "value": round(us, 3),
+        "unit": "us/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e2m1 codes + e8m0 block scales, fp32 math",
+        "data": "synthetic (seeded; the workload's generator)",
+        "config": {"workload": f"{w.name}_mxfp4", "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "D": D, "T": T, "R": w.R, "S": w.S, "block": 32, "n_chunks": n_chunks,
+                   "cache_copies": n_copies, "step": "decode (kvq_mx_decode_attention)"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "decode_mx_kernel + merge (kvq_mx_decode_attention, two launches)",
+                     "algorithmic_bytes": alg, "kernel_avg_us": round(us, 3),
+                     "frac_of_stream_read": round(gbps / sr["GBps"], 4)},
+        "stream_read": sr}), flush=True)
+    return 0
 
 
 def calib_copy(torch):

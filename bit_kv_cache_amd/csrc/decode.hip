@@ -74,9 +74,11 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
       float dot[GQA];
 #pragma unroll
       for (int h = 0; h < GQA; ++h) dot[h] = 0.f;
-#pragma unroll
+      // outer loops stay rolled: full unrolling keeps every product in
+      // registers (hundreds of VGPRs, one wave per SIMD)
+#pragma unroll 1
       for (int w = 0; w < WPT / 2; ++w) {
-        const uint32_t word = __builtin_nontemporal_load(kw + w);   // read once per step
+        const uint32_t word = kw[w];
 #pragma unroll
         for (int j = 0; j < FPI; ++j) {
           const int c = half * (kD / 2) + w * FPI + j;
@@ -129,6 +131,7 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
 }
 
 // --------------------------------------------------------- MXFP4 block
+typedef uint32_t mx_u32x4 __attribute__((ext_vector_type(4)));
 // E2M1 value of a code (sign bit 3; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6)
 __device__ __forceinline__ float e2m1(uint32_t code) {
   const uint32_t i = code & 7u;
@@ -151,19 +154,21 @@ __device__ void mx_block(const DecodeArgs& a, const kvq_mx_cache& mc, Lds<GQA>& 
     const int t = tid & (kBlockTok - 1), half = tid >> 7;
     if (t < nt) {
       const int64_t row = head * mc.t_cap + t0 + t;
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(mc.k_codes) + row * (kD / 8) + 8 * half;
+      // the token's 64 channels of this half: 8 words, two 16-byte loads
+      const mx_u32x4* kw = reinterpret_cast<const mx_u32x4*>(mc.k_codes + row * (kD / 8) + 8 * half);
       float dot[GQA];
 #pragma unroll
       for (int h = 0; h < GQA; ++h) dot[h] = 0.f;
-#pragma unroll
+#pragma unroll 1
       for (int blk = 0; blk < 2; ++blk) {
         const int c0 = 64 * half + 32 * blk;
         float part[GQA];
 #pragma unroll
         for (int h = 0; h < GQA; ++h) part[h] = 0.f;
-#pragma unroll
+        const mx_u32x4 words = kw[blk];
+#pragma unroll 1
         for (int w = 0; w < 4; ++w) {
-          const uint32_t word = __builtin_nontemporal_load(kw + 4 * blk + w);
+          const uint32_t word = words[w];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float x = e2m1((word >> (4 * j)) & 15u);
@@ -201,7 +206,7 @@ __device__ void mx_block(const DecodeArgs& a, const kvq_mx_cache& mc, Lds<GQA>& 
       for (int h = 0; h < GQA; ++h) part[h] = 0.f;
       const uint32_t* vw = reinterpret_cast<const uint32_t*>(mc.v_codes) +
                            (head * (mc.t_cap / 8) + tg / 8) * kD + d;
-#pragma unroll
+#pragma unroll 1
       for (int w = 0; w < 4; ++w) {
         const uint32_t word = __builtin_nontemporal_load(vw + w * kD);
 #pragma unroll

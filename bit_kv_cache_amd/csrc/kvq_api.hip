@@ -421,7 +421,9 @@ kvq_status kvq_mx_decode_plan(int32_t B, int32_t H_q, int32_t H_kv, int64_t n_qu
   if (heads > 65535) return KVQ_ERR_ARG;
   const int64_t blocks = n_quant_tokens / 32;
   int64_t n = n_chunks_req;
-  if (n == 0) n = (512 + heads - 1) / heads;   // about two blocks per CU
+  // automatic: about 16 blocks per CU (the vector-ALU kernel is bound by
+  // latency; 64 chunks per head ran the benchmark shape 1.7x faster than 8)
+  if (n == 0) n = (4096 + heads - 1) / heads;
   n = std::max<int64_t>(1, std::min<int64_t>(n, std::max<int64_t>(1, blocks)));
   if (n > 65535) return KVQ_ERR_ARG;
   if (n_chunks) *n_chunks = (int32_t)n;

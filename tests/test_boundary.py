@@ -252,6 +252,7 @@ def test_mx_decode_plan_validation():
     assert plan(1, 48, 8, 512, 0)[0] == kvq.KVQ_ERR_UNSUPPORTED
     assert plan(1, 30, 8, 512, 0)[0] == kvq.KVQ_ERR_ARG
     assert plan(1, 32, 8, 512, 100)[1] == 16                # at most one chunk per block
+    assert plan(8, 32, 8, 32768, 0)[1] == 64                # automatic: ~16 blocks per CU
     c = _mx()
     assert kvq.raw_call("kvq_mx_decode_attention", ctypes.byref(c), 1, 32, 8, FAKE, 512, None,
                         None, ctypes.c_float(0.0), 0, FAKE, 16, FAKE, None) == kvq.KVQ_ERR_WORKSPACE
