@@ -132,19 +132,26 @@ __device__ void quant_block(const DecodeArgs& a, Lds<GQA>& s, int64_t head, int6
 
 // --------------------------------------------------------- MXFP4 block
 typedef uint32_t mx_u32x4 __attribute__((ext_vector_type(4)));
-// E2M1 value of a code (sign bit 3; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6)
-__device__ __forceinline__ float e2m1(uint32_t code) {
-  const uint32_t i = code & 7u;
-  const float mag = i < 4 ? 0.5f * (float)i : (float)(2u << ((i - 4) >> 1)) * (1.f + 0.5f * (i & 1u));
-  return (code & 8u) ? -mag : mag;
-}
 // 2^(e8m0 - 127) for the byte range a block exponent of fp16 data can take
 __device__ __forceinline__ float e8m0_scale(uint32_t e) { return ldexpf(1.f, (int)e - 127); }
 
+// the eight E2M1 values of a word (nibble j -> x[j], least significant
+// first), each times sc, with gfx950's packed fp4 -> fp32 conversion (two
+// values per instruction, the scale applied in the conversion: exact for a
+// power of two)
+typedef float mx_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void e2m1x8(uint32_t word, float sc, float (&x)[8]) {
+  const mx_f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, sc, 0);
+  const mx_f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, sc, 1);
+  const mx_f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, sc, 2);
+  const mx_f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, sc, 3);
+  x[0] = a[0], x[1] = a[1], x[2] = b[0], x[3] = b[1];
+  x[4] = c[0], x[5] = c[1], x[6] = d[0], x[7] = d[1];
+}
+
 // Tokens [t0, t0+nt) of an MXFP4 cache head (t0, nt multiples of 32,
 // nt <= kBlockTok): key blocks of 32 channels per token, value blocks of 32
-// tokens per channel; each block's sum over its E2M1 values is scaled by 2^E
-// once (exact: a power of two).
+// tokens per channel, each value E2M1 * 2^E from the hardware conversion.
 template <int GQA>
 __device__ void mx_block(const DecodeArgs& a, const kvq_mx_cache& mc, Lds<GQA>& s, int64_t head,
                          int64_t t0, int nt, float (&acc)[GQA]) {
@@ -162,23 +169,17 @@ __device__ void mx_block(const DecodeArgs& a, const kvq_mx_cache& mc, Lds<GQA>& 
 #pragma unroll 1
       for (int blk = 0; blk < 2; ++blk) {
         const int c0 = 64 * half + 32 * blk;
-        float part[GQA];
-#pragma unroll
-        for (int h = 0; h < GQA; ++h) part[h] = 0.f;
+        const float sc = e8m0_scale(mc.k_scale[row * (kD / 32) + 2 * half + blk]);
         const mx_u32x4 words = kw[blk];
 #pragma unroll 1
         for (int w = 0; w < 4; ++w) {
-          const uint32_t word = words[w];
+          float x[8];
+          e2m1x8(words[w], sc, x);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float x = e2m1((word >> (4 * j)) & 15u);
+          for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int h = 0; h < GQA; ++h) part[h] = fmaf(s.q[h][c0 + 8 * w + j], x, part[h]);
-          }
+            for (int h = 0; h < GQA; ++h) dot[h] = fmaf(s.q[h][c0 + 8 * w + j], x[j], dot[h]);
         }
-        const float sc = e8m0_scale(mc.k_scale[row * (kD / 32) + 2 * half + blk]);
-#pragma unroll
-        for (int h = 0; h < GQA; ++h) dot[h] = fmaf(part[h], sc, dot[h]);
       }
 #pragma unroll
       for (int h = 0; h < GQA; ++h) s.part[half][h][t] = dot[h];
@@ -201,24 +202,18 @@ __device__ void mx_block(const DecodeArgs& a, const kvq_mx_cache& mc, Lds<GQA>& 
       const int tb = 64 * half + 32 * blk;   // block's first token in the tile
       if (tb >= nt) break;
       const int64_t tg = t0 + tb;
-      float part[GQA];
-#pragma unroll
-      for (int h = 0; h < GQA; ++h) part[h] = 0.f;
+      const float sc = e8m0_scale(mc.v_scale[(head * (mc.t_cap / 32) + tg / 32) * kD + d]);
       const uint32_t* vw = reinterpret_cast<const uint32_t*>(mc.v_codes) +
                            (head * (mc.t_cap / 8) + tg / 8) * kD + d;
 #pragma unroll 1
       for (int w = 0; w < 4; ++w) {
-        const uint32_t word = __builtin_nontemporal_load(vw + w * kD);
+        float x[8];
+        e2m1x8(__builtin_nontemporal_load(vw + w * kD), sc, x);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = e2m1((word >> (4 * j)) & 15u);
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-          for (int h = 0; h < GQA; ++h) part[h] = fmaf(s.p[h][tb + 8 * w + j], x, part[h]);
-        }
+          for (int h = 0; h < GQA; ++h) acc[h] = fmaf(s.p[h][tb + 8 * w + j], x[j], acc[h]);
       }
-      const float sc = e8m0_scale(mc.v_scale[(head * (mc.t_cap / 32) + tg / 32) * kD + d]);
-#pragma unroll
-      for (int h = 0; h < GQA; ++h) acc[h] = fmaf(part[h], sc, acc[h]);
     }
   }
   __syncthreads();
