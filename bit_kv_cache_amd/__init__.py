@@ -28,8 +28,10 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_ALIGN, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
-# arrival counters at the start of a decode workspace (zero between calls)
-KVQ_WS_COUNTER_BYTES = 262144
+# counter bytes at the start of a decode workspace: arrival counters (zero
+# between calls), then the status words at KVQ_WS_STATUS
+KVQ_WS_COUNTER_BYTES = 262400
+KVQ_WS_STATUS = 262144
 
 EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_step",
@@ -260,6 +262,18 @@ def decode_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A decode workspace of ``nbytes`` (from ``kvq_decode_plan``), allocated
     zeroed as the counter bytes at its start require."""
     return torch.zeros((nbytes + 3) // 4, dtype=torch.float32, device=device)
+
+
+def workspace_status(workspace: torch.Tensor):
+    """(stalled blocks, parts poisoned by a bad page) counted in a workspace's
+    status words since it was zeroed (synchronizes with the device)."""
+    w = workspace.view(torch.int32)[KVQ_WS_STATUS // 4: KVQ_WS_STATUS // 4 + 2].cpu()
+    return int(w[0]), int(w[1])
+
+
+def clear_workspace_status(workspace: torch.Tensor) -> None:
+    """Zero the status words of a workspace (asynchronous, on the current stream)."""
+    workspace.view(torch.int32)[KVQ_WS_STATUS // 4: KVQ_WS_STATUS // 4 + 2].zero_()
 
 
 def workspace_records(workspace: torch.Tensor, rows: int, n_parts: int, D: int = 128):

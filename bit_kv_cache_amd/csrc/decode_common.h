@@ -127,6 +127,7 @@ __device__ void write_partial(const DecodeArgs& a, Lds<GQA>& s, int64_t b, int64
     for (int h = 0; h < GQA; ++h) s.acc[h][d] = acc[h];
   }
   __syncthreads();
+  if (tid == 0 && s.bad) status_add(a.status, kStatusBadPage);
   if (!half) {
 #pragma unroll
     for (int h = 0; h < GQA; ++h) {

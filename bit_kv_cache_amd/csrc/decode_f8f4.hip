@@ -256,7 +256,7 @@ struct LdsF {
   int ready[R];     // chunk-relative group (mod kSeqLen) a slot holds once its data has arrived
   int empty[R];     // the group a slot may receive next (its previous one was copied out)
   int next_group;   // next group a consumer claims
-  int stalled;      // a wait ran past its spin limit
+  int stalled;      // bit 0: a wait ran past its spin limit; bit 1: a page outside the pool
   int last;         // this block is the last of its head to finish (in-launch merge)
   int next_item;    // next append item a consumer claims
 };
@@ -714,7 +714,9 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
     }
     vm_wait<0>();
-    if ((!ok || bad_page) && lane == 0) lds_store(&sh.stalled, 1);
+    if ((!ok || bad_page) && lane == 0)
+      __hip_atomic_fetch_or(&sh.stalled, (ok ? 0 : 1) | (bad_page ? 2 : 0), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
     // ---------------------------------------------------------- consumer waves
     __syncthreads();   // the loader has set up the ring's flags
@@ -802,8 +804,11 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     // q.K^T on fp16 matrix cores (raw keys as B), the online softmax, p.V
     // through an LDS transpose of the fp16 values into a natural-scale
     // accumulator, reduced to the lane's channels (wsum, rescaled with the
-    // softmax from here on).
+    // softmax from here on).  The query's fp16 hi/lo rows carry the same
+    // power of two as qv (largest entry below 2^8), so small entries stay
+    // normal fp16 numbers with their full precision; the logits drop it again.
     if (u_first < u1) {
+      const float wqs = a.qscale * exp2i(8 - e_q);
 #pragma unroll
       for (int H = 0; H < NH; ++H)
 #pragma unroll
@@ -814,7 +819,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
             unpack8(wq[H][c], v);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float x0 = v[2 * i] * a.qscale, x1 = v[2 * i + 1] * a.qscale;
+              const float x0 = v[2 * i] * wqs, x1 = v[2 * i + 1] * wqs;
               const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
               const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]);
               val[i] = __builtin_bit_cast(uint32_t, (m_row & 1) ? l : h);
@@ -846,7 +851,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
           f32x4 cw = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < 4; ++c) cw = mfma_f16(wq[H][c], wt.k[c], cw);
-          const float lg = valid ? cw[0] + cw[1] : kNegInfF;
+          const float lg = valid ? (cw[0] + cw[1]) * q_unscale : kNegInfF;
           const float v = row_max16(lg);
           const float m_new = fmaxf(m_run[H], v);   // finite: the tile has a valid token
           const float alpha = fexp2(m_run[H] - m_new);
@@ -1117,7 +1122,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       if (j >= ngc) break;
       const int s = j % R;
       if (!spin_until(&sh.ready[s], j & (kSeqLen - 1))) {
-        lds_store(&sh.stalled, 1);
+        if (lane == 0) __hip_atomic_fetch_or(&sh.stalled, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         break;
       }
       asm volatile("" ::: "memory");
@@ -1164,7 +1169,11 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   }
   __syncthreads();
   const int n_parts = a.n_parts;
-  const bool stalled = lds_load(&sh.stalled) != 0;
+  const int stall_bits = lds_load(&sh.stalled);
+  const bool stalled = stall_bits != 0;
+  // the reason a part is poisoned, counted in the workspace's status words
+  if (tid == 0 && (stall_bits & 1)) status_add(a.status, kStatusStalled);
+  if (tid == 0 && (stall_bits & 2)) status_add(a.status, kStatusBadPage);
   for (int i = tid; i < GQA * kD; i += kThreadsF) {
     const int h = i / kD, d = i % kD;
     // every wave's record read up front; empty ones (l = 0) are skipped by

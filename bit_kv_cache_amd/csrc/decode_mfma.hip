@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
 
   // this lane's A-prep heads (ph, ph + 4) and chunk (pc, pkq)
   // q * sm * log2e * 2^(24 - offset) of this lane's A-prep elements, in LDS
-  float qmax = 0.f;
+  float qmax = 0.f, qmax_n = 0.f;
 #pragma unroll
   for (int j = 0; j < NH; ++j) {
     float qh[8];
@@ -331,22 +331,32 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
       const float qv = h2f(qrow[(ph + 4 * j) * kD + ch]) * a.qscale;
       qh[e] = qv * exp2i(24 - code_offset<BITS>(ch));
       qmax = fmaxf(qmax, fabsf(qh[e]));
+      qmax_n = fmaxf(qmax_n, fabsf(qv));
     }
     L.qhat[j][lane][0] = f32x4{qh[0], qh[1], qh[2], qh[3]};
     L.qhat[j][lane][1] = f32x4{qh[4], qh[5], qh[6], qh[7]};
   }
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, o));
+  for (int o = 1; o < 64; o <<= 1) {
+    qmax = fmaxf(qmax, __shfl_xor(qmax, o));
+    qmax_n = fmaxf(qmax_n, __shfl_xor(qmax_n, o));
+  }
   const int e_q = ceil_exp(qmax);
+  // The bias / window operand below is q*sm*log2e times 2^(8 - e_n), its
+  // largest entry below 2^8, so that small entries stay normal fp16 numbers
+  // in the hi/lo split; products from it are scaled back by 2^(e_n - 8).
+  const int e_n = ceil_exp(qmax_n);
+  const float q_nat_unscale = exp2i(max(-126, min(127, e_n - 8)));
 
   // bias operand: hi/lo of q*sm*log2e in natural channel order, rows (head,
   // hi/lo); built once per block in LDS (wave w builds K-step w)
   {
     const int m = lane & 15, c = wave;
     const int h = (m % (2 * GQA)) >> 1, hl = m & 1;
+    const float qs = a.qscale * exp2i(max(-126, min(127, 8 - e_n)));
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = h2f(qrow[h * kD + 32 * c + 8 * kq + e]) * a.qscale;
+    for (int e = 0; e < 8; ++e) v[e] = h2f(qrow[h * kD + 32 * c + 8 * kq + e]) * qs;
     u32x4 hi, lo;
     split_hilo(v, hi, lo);
     sh.bias_a[c][kq][m] = hl ? lo : hi;
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
     f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) cb = mfma(sh.bias_a[c][kq][m_row], kl.kmin[c], cb);
-    const float biasA = cb[0] + cb[1], biasB = cb[2] + cb[3];
+    const float biasA = (cb[0] + cb[1]) * q_nat_unscale, biasB = (cb[2] + cb[3]) * q_nat_unscale;
 
     // ---- q.K^T
     const float ek = exp2i(max(-126, min(127, e_k)));
@@ -604,7 +614,7 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
       float alpha[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float lg = valid ? cw[2 * j] + cw[2 * j + 1] : kNegInfM;
+        const float lg = valid ? (cw[2 * j] + cw[2 * j + 1]) * q_nat_unscale : kNegInfM;
         float v = row_max16(lg);
         if (GQA == 4) v = fmaxf(v, xor32(v));
         const float m_new = fmaxf(m_run[j], v);   // finite: the tile has a valid token
@@ -702,6 +712,7 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
   }
   __syncthreads();
   const int n_parts = a.n_parts;
+  if (tid == 0 && sh.bad) status_add(a.status, kStatusBadPage);
   for (int i = tid; i < GQA * kD; i += kThreadsM) {
     const int h = i / kD, d = i % kD;
     // every wave's record read up front; empty ones (l = 0) are skipped by

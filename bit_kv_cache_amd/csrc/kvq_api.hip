@@ -243,6 +243,7 @@ kvq_status prepare_decode(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
   a->append = 0;
   a->seq_quant = nullptr;
   a->seq_res = nullptr;
+  a->status = static_cast<int32_t*>(workspace) + kvq::kStatusIndex;
   return KVQ_OK;
 }
 
@@ -476,6 +477,7 @@ kvq_status kvq_mx_decode_attention(const kvq_mx_cache* cache, int32_t B, int32_t
   a.qscale = sm_scale * 1.4426950408889634f;
   a.n_parts = nc + 1;
   a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kvq::kCounterBytes);
+  a.status = static_cast<int32_t*>(workspace) + kvq::kStatusIndex;
   a.out = out;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = hip_status(kvq::launch_decode_mx(*cache, a, s))) != KVQ_OK) return st;

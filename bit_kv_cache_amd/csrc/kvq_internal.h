@@ -108,6 +108,9 @@ struct DecodeArgs {
   // G / n_res): quantized tokens and residual tokens of sequence b.
   const int32_t* seq_quant;
   const int32_t* seq_res;
+  // Status words of the workspace (kStatusStalled, kStatusBadPage): a block
+  // that poisons its part adds 1 to the word naming why.
+  int32_t* status;
 };
 
 // Quantized groups and residual tokens of sequence b: the per-sequence
@@ -126,9 +129,20 @@ __device__ __forceinline__ int seq_res(const DecodeArgs& a, int64_t b) {
   return n < 0 ? 0 : (n > a.n_res ? a.n_res : n);
 }
 
-// Bytes of arrival counters at the start of a decode workspace (one int per
-// (batch, kv head) for up to 65536 of them); the partials follow.
-constexpr size_t kCounterBytes = 65536 * sizeof(int32_t);
+// Bytes of counters at the start of a decode workspace: one arrival counter
+// per (batch, kv head) for up to 65536 of them, then the status words (stalled
+// blocks, parts poisoned by a bad page) and reserved space; the partials
+// follow.
+constexpr size_t kCounterBytes = KVQ_WS_COUNTER_BYTES;
+constexpr size_t kStatusIndex = KVQ_WS_STATUS / sizeof(int32_t);
+static_assert(KVQ_WS_STATUS == 65536 * sizeof(int32_t), "status words follow the counters");
+constexpr int kStatusStalled = 0, kStatusBadPage = 1;
+
+// Adds to a status word of the workspace (device-scope vector atomic, one
+// lane of the calling block).
+__device__ __forceinline__ void status_add(int32_t* status, int which) {
+  if (status) __hip_atomic_fetch_add(status + which, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Parts the in-launch merge accepts (more take the merge kernel).
 constexpr int kFusedMergeParts = 8;
 

@@ -168,13 +168,25 @@ kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t 
                            int64_t n_quant_tokens, int32_t n_chunks_req, int32_t* n_chunks,
                            size_t* ws_bytes);
 
-/* Decode workspace layout: KVQ_WS_COUNTER_BYTES of int32 arrival counters
- * (one per (batch, kv head)), then the fp32 partial records.  The counter
- * bytes must be zero when a workspace is first used (allocate it zeroed);
- * every call leaves them zero, so a workspace stays valid across calls and
- * configurations.  The records need no initialization.  Calls that share a
- * workspace must not overlap in time. */
-#define KVQ_WS_COUNTER_BYTES 262144
+/* Decode workspace layout: KVQ_WS_COUNTER_BYTES of int32 counters, then the
+ * fp32 partial records.  The counter bytes are
+ *   [0, 262144)       arrival counters, one per (batch, kv head);
+ *   KVQ_WS_STATUS     int32 status[2]:
+ *     status[0]  blocks of a decode launch whose bounded wait for another
+ *                wave of the block ran out (the block then stops waiting and
+ *                poisons its part: NaN output for that head's query rows);
+ *                never expected, a symptom of a scheduling fault;
+ *     status[1]  parts poisoned because a page-table entry lay outside the
+ *                pool (an input error; NaN output for that head);
+ *   the rest up to KVQ_WS_COUNTER_BYTES is reserved (zero).
+ * The counter bytes must be zero when a workspace is first used (allocate it
+ * zeroed).  Every call leaves the arrival counters zero, so a workspace stays
+ * valid across calls and configurations; the status words only grow (device-
+ * scope atomic adds), so the caller reads them after a call and clears them
+ * when it wants a fresh count.  The records need no initialization.  Calls
+ * that share a workspace must not overlap in time. */
+#define KVQ_WS_COUNTER_BYTES 262400
+#define KVQ_WS_STATUS 262144
 
 /* Workspace bytes of kvq_decode_attention for the same arguments (0 on a bad
  * argument): the counter bytes plus fp32 partials (m, l, acc[D]) per (batch,

@@ -6,6 +6,8 @@ ever handed to the oracle."""
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -112,5 +114,14 @@ def oracle_decode(w, oc, inp, n_quant, n_res=None, n_sink=None):
         v_res=bits(inp["v_res"]) if n_res else None, n_res=n_res)
 
 
+# (test id, max-abs error) of every comparison made through max_err, printed
+# at the end of the session (tests/conftest.py) so that the margins below the
+# bar are on record even in a quiet run
+ERRORS = []
+
+
 def max_err(gpu_out, ref):
-    return float(np.max(np.abs(gpu_out.cpu().numpy().astype(np.float64) - ref)))
+    err = float(np.max(np.abs(gpu_out.cpu().numpy().astype(np.float64) - ref)))
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    ERRORS.append((test, err))
+    return err

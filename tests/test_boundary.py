@@ -27,6 +27,18 @@ def test_header_symbols_exported():
         assert hasattr(lib, n), n
 
 
+def test_header_workspace_constants_match_binding():
+    """The binding's workspace offsets are the header's: the status words sit
+    after the 65536 arrival counters and inside the counter bytes."""
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    consts = {m.group(1): int(m.group(2))
+              for m in re.finditer(r"#define\s+(KVQ_WS_[A-Z_]+)\s+(\d+)", src)}
+    assert consts["KVQ_WS_COUNTER_BYTES"] == kvq.KVQ_WS_COUNTER_BYTES
+    assert consts["KVQ_WS_STATUS"] == kvq.KVQ_WS_STATUS == 65536 * 4
+    assert kvq.KVQ_WS_STATUS + 8 <= kvq.KVQ_WS_COUNTER_BYTES
+    assert kvq.KVQ_WS_COUNTER_BYTES % 16 == 0   # the records stay 16-byte aligned
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5):
         assert kvq.kvq_status_string(s).startswith("KVQ_")

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from parity_util import TOL, assert_cache_equal, qcfg
+from parity_util import TOL, assert_cache_equal, max_err, qcfg
 
 pytestmark = pytest.mark.gpu
 
@@ -99,8 +99,7 @@ def test_full_size_sampled_heads(built, name):
         oracle.quantize_pack(oc, kR, vR, w.T // w.G, 1, n_threads=len(hs))
     for i, h in enumerate(hs):
         b, hk = divmod(h, w.H_kv)
-        got = out[b, hk * w.gqa:(hk + 1) * w.gqa].cpu().numpy().astype(np.float64)
-        err = float(np.max(np.abs(got - ref[i])))
+        err = max_err(out[b, hk * w.gqa:(hk + 1) * w.gqa], ref[i])
         print(f"  head {h}: max-abs {err:.3g}", flush=True)
         assert err <= TOL, f"{name} head {h}: max-abs {err:.3g}"
         one = oracle.empty_cache(w.bits, w.G, w.D, w.n_boost, w.T + w.G, 1)

@@ -114,11 +114,13 @@ def test_paged_quantize_decode_append(built, name):
     assert np.array_equal(vo.cpu().numpy().view(np.uint32), vr.view(np.uint32))
 
 
+@pytest.mark.bad_pages
 @pytest.mark.parametrize("name", ["llama_2bit", "llama_4bit", "g32_8bit_gqa2"])
 def test_paged_bad_entry_poisons_only_its_head(built, name):
     """A table entry outside the pool is never dereferenced: quantize skips the
     group, decode returns NaN for that head's query rows and the right
-    result for every other head."""
+    result for every other head, and the workspace's status words count one
+    poisoned part (the chunk holding the bad group) and no stalled block."""
     import bit_kv_cache_amd as kvq
     w = _w(name)
     inp = make_inputs(w)
@@ -151,6 +153,7 @@ def test_paged_bad_entry_poisons_only_its_head(built, name):
                                      kvq.window(inp["k_res"], inp["v_res"], w.R), out, ws,
                                      n_chunks=n_chunks)
             torch.cuda.synchronize()
+            assert kvq.workspace_status(ws) == (0, 1), (bad_page, n_chunks)
             o = out.view(n, w.gqa, w.D)
             assert torch.isnan(o[bad_head]).all(), (bad_page, n_chunks)
             good = [h for h in range(n) if h != bad_head]

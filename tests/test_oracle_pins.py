@@ -284,14 +284,155 @@ def test_append_matches_bulk():
 # Kitty channel-wise boost
 # --------------------------------------------------------------------------
 
-def test_kitty_boost_zero_is_plain_kivi():
-    rng = np.random.default_rng(5)
-    k, v = _rand_src(rng, 2, 128, 128, [(9, 20.0)])
-    a = oracle.empty_cache(2, 64, 128, 0, 128, 2)
-    oracle.quantize_pack(a, k, v, 0, 2)
-    b = oracle.empty_cache(2, 64, 128, 0, 128, 2)
-    oracle.quantize_pack(b, k, v, 0, 2)
-    assert np.array_equal(a.k_words, b.k_words) and np.array_equal(a.k_scale, b.k_scale)
+def _np_quant(xh, maxq):
+    """One min-max group restated in numpy, independently of the oracle (KIVI
+    page, Step 1, with the fp32 reading): min and max under the order
+    -0 < +0, range and quotient in IEEE fp32, the scale rounded to fp16, codes
+    round-half-even(clamp((x - min)/scale, 0, maxq)); a zero scale gives code 0.
+    Returns (min bits, scale bits, codes)."""
+    xh = np.asarray(xh, np.float16)
+    b = xh.view(np.uint16).astype(np.int64)
+    key = np.where(b & 0x8000, 0x7FFF - (b & 0x7FFF), 0x8000 + b)
+    mn, mx = xh[np.argmin(key)], xh[np.argmax(key)]
+    s = np.float16((np.float32(mx) - np.float32(mn)) / np.float32(maxq))
+    if s == 0:
+        codes = np.zeros(len(xh), np.uint8)
+    else:
+        y = (xh.astype(np.float32) - np.float32(mn)) / np.float32(s)
+        codes = np.rint(np.clip(y, np.float32(0), np.float32(maxq))).astype(np.uint8)
+    return int(np.array(mn).view(np.uint16)), int(np.array(s).view(np.uint16)), codes
+
+
+def _field(words, idx, bits):
+    """Code idx of a least-significant-first packed row (numpy shift-and-mask)."""
+    per = 32 // bits
+    return (words[..., idx // per] >> np.uint32(bits * (idx % per))) & np.uint32((1 << bits) - 1)
+
+
+@pytest.mark.parametrize("nb,G", [(0, 64), (0, 128), (16, 64), (16, 128), (32, 64), (32, 128)])
+def test_kitty_partial_boost_codes_high_bits_and_dequant(nb, G):
+    """Kitty page, 4.1 (a key page is a dense tensor of every channel's low two
+    bits, a compact (D_boost, G) tensor of the boosted channels' high two bits
+    and a per-channel index with a sentinel) and 4.2, Algorithm 1 (X = lo |
+    hi << 2, X * scale + zero), checked channel by channel against the numpy
+    restatement of the quantizer with 0 < n_boost < D, where a boosted row is
+    not its channel:
+      * the boosted set is the n_boost channels of largest fp32 range, ties to
+        the lower channel, and row r is the r-th of them in ascending order;
+      * each channel's scale and min are those of its own width (15 levels
+        boosted, 3 otherwise), and its dense 2-bit field holds code & 3;
+      * the high-bits word (t, r // 16) holds code >> 2 of row r's channel at
+        bit 2 (r % 16), for every token t of the group;
+      * the dequantized key is (lo | hi << 2) * scale + min in fp32.
+    n_boost = 0 is plain 2-bit KIVI: every channel against the same numpy
+    quantizer at 3 levels."""
+    rng = np.random.default_rng(40 + nb + G)
+    D, T, heads = 128, 256, 2
+    k, v = _rand_src(rng, heads, T, D, [(2, 20.0), (9, 15.0), (33, 18.0), (70, 12.0),
+                                        (101, 25.0), (126, 14.0)])
+    c = oracle.empty_cache(2, G, D, nb, T, heads)
+    oracle.quantize_pack(c, k, v, 0, T // G)
+    kk, vv = oracle.dequantize(c, 0, T // G)
+    kf = k.view(np.float16)
+    vf = v.view(np.float16)
+    for hd in range(heads):
+        for g in range(T // G):
+            blk = kf[hd, g * G:(g + 1) * G]
+            rng32 = blk.max(0).astype(np.float32) - blk.min(0).astype(np.float32)
+            boosted = sorted(sorted(range(D), key=lambda d: (-float(rng32[d]), d))[:nb])
+            rank = {d: r for r, d in enumerate(boosted)}
+            assert boosted != list(range(nb)) or nb == 0   # rows differ from channels
+            toks = slice(g * G, (g + 1) * G)
+            for d in range(D):
+                maxq = 15 if d in rank else 3
+                mn, s, q = _np_quant(blk[:, d], maxq)
+                assert (int(c.k_min[hd, g, d]), int(c.k_scale[hd, g, d])) == (mn, s), (hd, g, d)
+                lo = _field(c.k_words[hd, toks], d, 2)
+                assert np.array_equal(lo, q & 3), (hd, g, d)
+                code = lo.astype(np.uint32)
+                if nb:
+                    assert int(c.k_bidx[hd, g, d]) == rank.get(d, nb)
+                if d in rank:
+                    r = rank[d]
+                    hi = _field(c.k_hi[hd, toks], r, 2)
+                    assert np.array_equal(hi, q >> 2), (hd, g, d, r)
+                    code = code | (hi << np.uint32(2))
+                want = (code.astype(np.float32) * np.float16(np.uint16(s).view(np.float16)).astype(np.float32)
+                        + np.float32(np.uint16(mn).view(np.float16)))
+                assert np.array_equal(kk[hd, toks, d].view(np.uint32), want.view(np.uint32)), (hd, g, d)
+    # values stay plain 2-bit per token (Kitty page, 3.3: V2)
+    for hd in range(heads):
+        for t in (0, 77, T - 1):
+            for cg in range(D // G):
+                mn, s, q = _np_quant(vf[hd, t, cg * G:(cg + 1) * G], 3)
+                assert (int(c.v_min[hd, t, cg]), int(c.v_scale[hd, t, cg])) == (mn, s)
+                got = [int(_field(c.v_words[hd, :, d], t, 2)) for d in range(cg * G, (cg + 1) * G)]
+                assert got == list(q)
+
+
+def test_key_words_bridge_to_kivi_token_axis_packing():
+    """KIVI page, Step 2 packs key codes along tokens, [T/16, D] at 2 bits: word
+    (w, d) holds token 16 w + j of channel d at bit 2 j; Step 4's worked example
+    finds logical column 19 in word 1 at shift 6 (tests/golden/
+    kivi_unpack_example.txt).  The cache packs the same codes along channels.
+    Re-packing the cache's codes of each channel along tokens with the page's
+    shift-or (numpy) must give the page's words built from the numpy quantizer's
+    codes, and token 19 of every channel must sit in word 1 at shift 6: the
+    bit-exact words of the cache are a fixed transposition of the page's words,
+    with the same codes."""
+    (bits, idx, word, shift, mask), = [[int(x) for x in r] for r in _rows("kivi_unpack_example.txt")]
+    rng = np.random.default_rng(41)
+    D, G, T = 128, 32, 64
+    k, v = _rand_src(rng, 1, T, D, [(3, 15.0), (17, 15.0)])
+    c = oracle.empty_cache(bits, G, D, 0, T, 1)
+    oracle.quantize_pack(c, k, v, 0, T // G)
+    kf = k.view(np.float16)[0]
+    page_codes = np.zeros((T, D), np.uint32)           # quant_kcache's code[t][d]
+    for g in range(T // G):
+        for d in range(D):
+            page_codes[g * G:(g + 1) * G, d] = _np_quant(kf[g * G:(g + 1) * G, d], 3)[2]
+    per = 32 // bits
+
+    def pack_tokens(codes):                              # pack_tensor along tokens
+        w = np.zeros((T // per, D), np.uint32)
+        for j in range(per):
+            w |= codes[j::per] << np.uint32(bits * j)
+        return w
+
+    page_words = pack_tokens(page_codes)
+    cache_codes = np.stack([_field(c.k_words[0], d, bits) for d in range(D)], -1)   # [T][D]
+    assert np.array_equal(pack_tokens(cache_codes.astype(np.uint32)), page_words)
+    assert np.array_equal((page_words[word] >> np.uint32(shift)) & np.uint32(mask), page_codes[idx])
+    # the same code read straight from the cache's channel-axis word
+    for d in (0, 3, 17, 127):
+        assert (int(c.k_words[0, idx, d // per]) >> (bits * (d % per))) & mask == \
+            (int(page_words[word, d]) >> shift) & mask
+
+
+def test_value_words_bridge_to_channel_axis_packing():
+    """Values are quantized per token over G channels (KIVI page, Step 1) and
+    the cache packs them along tokens; re-packing its codes of each token along
+    channels (least significant first, as pack_tensor) gives the words built
+    from the numpy quantizer's per-token codes."""
+    rng = np.random.default_rng(42)
+    D, G, T = 128, 64, 64
+    for bits in (2, 4):
+        k, v = _rand_src(rng, 1, T, D)
+        c = oracle.empty_cache(bits, G, D, 0, T, 1)
+        oracle.quantize_pack(c, k, v, 0, T // G)
+        vf = v.view(np.float16)[0]
+        maxq = (1 << bits) - 1
+        page = np.concatenate([np.stack([_np_quant(vf[t, cg * G:(cg + 1) * G], maxq)[2]
+                                         for t in range(T)]) for cg in range(D // G)], 1)
+        cache_codes = np.stack([[int(_field(c.v_words[0, :, d], t, bits)) for d in range(D)]
+                                for t in range(T)])
+        assert np.array_equal(cache_codes, page.astype(np.int64))
+        per = 32 // bits
+        chan_words = np.zeros((T, D // per), np.uint32)
+        for j in range(per):
+            chan_words |= page[:, j::per].astype(np.uint32) << np.uint32(bits * j)
+        for t in range(T):
+            assert list(oracle.unpack(chan_words[t], D, bits)) == [int(x) for x in cache_codes[t]]
 
 
 def test_kitty_all_channels_boosted_equals_4bit():
