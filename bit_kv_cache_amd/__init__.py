@@ -38,7 +38,9 @@ EXPORTED = ("kvq_status_string", "kvq_quantize_pack", "kvq_decode_plan",
             "kvq_decode_partials", "kvq_decode_merge", "kvq_dequantize",
             "kvq_decode_attention_ragged", "kvq_decode_partials_ragged", "kvq_stream_read",
             "kvq_mx_quantize_pack", "kvq_mx_dequantize", "kvq_mx_decode_plan",
-            "kvq_mx_decode_attention")
+            "kvq_mx_decode_attention", "kvq_decode_step_noalloc")
+# workspace bytes of the no-allocation decode step's scratch array (per GPU)
+KVQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class kvq_qcfg(ctypes.Structure):
@@ -83,6 +85,9 @@ _lib.kvq_decode_attention.restype = ctypes.c_int
 _lib.kvq_decode_step.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32, _P,
                                  _sz, _P, _i32, _P]
 _lib.kvq_decode_step.restype = ctypes.c_int
+_lib.kvq_decode_step_noalloc.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32,
+                                         _P, _i32, _P]
+_lib.kvq_decode_step_noalloc.restype = ctypes.c_int
 _lib.kvq_decode_partials.argtypes = [_P, _P, _i32, _i32, _i32, _P, _i64, _P, _P, _f32, _i32,
                                      _P, _sz, _P, _P]
 _lib.kvq_decode_partials.restype = ctypes.c_int
@@ -316,6 +321,20 @@ def kvq_decode_step(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int, q: tor
         ctypes.byref(res) if res is not None else None, float(sm_scale), int(n_chunks),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
         1 if append else 0, _stream(stream)), "kvq_decode_step")
+
+
+def kvq_decode_step_noalloc(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int,
+                            q: torch.Tensor, n_quant_tokens: int, sink: kvq_window | None,
+                            res: kvq_window | None, out: torch.Tensor, append: bool,
+                            sm_scale: float = 0.0, n_chunks: int = 0, stream=None) -> None:
+    """kvq_decode_step on the library's own per-GPU scratch array (no
+    workspace argument; the call allocates nothing)."""
+    c_cfg, c_cache = cfg.c(), cache.c()
+    _check(_lib.kvq_decode_step_noalloc(
+        ctypes.byref(c_cfg), ctypes.byref(c_cache), B, H_q, H_kv, _ptr(q), n_quant_tokens,
+        ctypes.byref(sink) if sink is not None else None,
+        ctypes.byref(res) if res is not None else None, float(sm_scale), int(n_chunks),
+        _ptr(out), int(bool(append)), _stream(stream)), "kvq_decode_step_noalloc")
 
 
 def kvq_decode_partials(cfg: QCfg, cache: Cache, B: int, H_q: int, H_kv: int,

@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq.h"
 #include "kvq_internal.h"
@@ -280,14 +281,19 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
   return decode_and_merge(cfg, a, workspace, static_cast<hipStream_t>(stream));
 }
 
-kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,
-                           int32_t H_kv, const uint16_t* q, int64_t n_quant_tokens,
-                           const kvq_window* sink, const kvq_window* res, float sm_scale,
-                           int32_t n_chunks, void* workspace, size_t ws_bytes, float* out,
-                           int32_t append, void* stream) {
-  kvq::DecodeArgs a;
+}  // extern "C"
+
+namespace {
+
+// Validation of kvq_decode_step on a given workspace (the caller's, or the
+// no-allocation entry point's scratch array): fills the launch arguments.
+kvq_status prepare_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,
+                        int32_t H_kv, const uint16_t* q, int64_t n_quant_tokens,
+                        const kvq_window* sink, const kvq_window* res, float sm_scale,
+                        int32_t n_chunks, void* workspace, size_t ws_bytes, float* out,
+                        int32_t append, kvq::DecodeArgs* a) {
   kvq_status st = prepare_decode(cfg, cache, B, H_q, H_kv, q, n_quant_tokens, sink, res,
-                                 sm_scale, n_chunks, workspace, ws_bytes, &a);
+                                 sm_scale, n_chunks, workspace, ws_bytes, a);
   if (st != KVQ_OK) return st;
   if (!out) return KVQ_ERR_ARG;
   if (!aligned16(out)) return KVQ_ERR_ALIGN;
@@ -297,7 +303,16 @@ kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t 
     if (!res || res->n < G || !groups_fit(cache, G, n_quant_tokens / G + 1)) return KVQ_ERR_ARG;
     if ((int64_t)H_kv * B * 8 + (int64_t)B * H_q > 0x7FFFFFFF) return KVQ_ERR_ARG;
   }
-  a.out = out;
+  a->out = out;
+  return KVQ_OK;
+}
+
+// The launches of a validated kvq_decode_step.
+kvq_status launch_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_kv,
+                       int64_t n_quant_tokens, const kvq_window* res, void* workspace,
+                       int32_t append, kvq::DecodeArgs& a, void* stream) {
+  kvq_status st;
+  const int64_t G = cfg->group;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!append) return decode_and_merge(cfg, a, workspace, s);
   if (kvq::fused_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_parts,
@@ -315,6 +330,83 @@ kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t 
                           n_quant_tokens / G, 1,             (int32_t)heads, cfg->n_boost,
                           cfg->boost_score};
   return hip_status(kvq::launch_merge_append(cfg->bits, vbits(cfg), cfg->group, a, qa, s));
+}
+
+// ------------------------------------------------------------ no-allocation step
+//
+// The decode workspace of kvq_decode_step_noalloc: one array per GPU, in the
+// library's code object, holding the counter bytes and the partial records.
+// Its address on a device comes from hipGetSymbolAddress, taken once per
+// device with that device current (the array's name in host code is a
+// host-side stand-in, never a device address).
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's scratch address (resolved on the first call there).
+kvq_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KVQ_ERR_HIP;
+  if (dev >= kMaxDevices) return KVQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return KVQ_OK;
+}
+
+// Zeroes n int32 words (a kernel, not a memset, so a captured graph replays
+// it as an ordinary kernel node).
+__global__ void zero_words_kernel(int32_t* p, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,
+                           int32_t H_kv, const uint16_t* q, int64_t n_quant_tokens,
+                           const kvq_window* sink, const kvq_window* res, float sm_scale,
+                           int32_t n_chunks, void* workspace, size_t ws_bytes, float* out,
+                           int32_t append, void* stream) {
+  kvq::DecodeArgs a;
+  const kvq_status st = prepare_step(cfg, cache, B, H_q, H_kv, q, n_quant_tokens, sink, res,
+                                     sm_scale, n_chunks, workspace, ws_bytes, out, append, &a);
+  if (st != KVQ_OK) return st;
+  return launch_step(cfg, cache, B, H_kv, n_quant_tokens, res, workspace, append, a, stream);
+}
+
+kvq_status kvq_decode_step_noalloc(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                                   int32_t H_q, int32_t H_kv, const uint16_t* q,
+                                   int64_t n_quant_tokens, const kvq_window* sink,
+                                   const kvq_window* res, float sm_scale, int32_t n_chunks,
+                                   float* out, int32_t append, void* stream) {
+  // the workspace this call needs must fit the scratch array
+  size_t need = 0;
+  kvq_status st = kvq_decode_plan(cfg, B, H_q, H_kv, n_quant_tokens, n_chunks, nullptr, &need);
+  if (st != KVQ_OK) return st;
+  if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != KVQ_OK) return st;
+  kvq::DecodeArgs a;
+  if ((st = prepare_step(cfg, cache, B, H_q, H_kv, q, n_quant_tokens, sink, res, sm_scale,
+                         n_chunks, ws, KVQ_NOALLOC_SCRATCH_BYTES, out, append, &a)) != KVQ_OK)
+    return st;
+  // The array keeps the previous call's contents: zero the arrival counters
+  // of this call's heads and the status words before the step.
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t heads = B * H_kv;   // <= 65535: checked by kvq_decode_plan above
+  zero_words_kernel<<<(heads + 255) / 256, 256, 0, s>>>(static_cast<int32_t*>(ws), heads);
+  zero_words_kernel<<<1, 64, 0, s>>>(static_cast<int32_t*>(ws) + kvq::kStatusIndex, 2);
+  if ((st = hip_status(hipGetLastError())) != KVQ_OK) return st;
+  return launch_step(cfg, cache, B, H_kv, n_quant_tokens, res, ws, append, a, stream);
 }
 
 kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,

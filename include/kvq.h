@@ -237,6 +237,27 @@ kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t 
                            int32_t n_chunks, void* workspace, size_t ws_bytes, float* out,
                            int32_t append, void* stream);
 
+/* kvq_decode_step for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, result and kernels, without the workspace.  The workspace
+ * is an array of KVQ_NOALLOC_SCRATCH_BYTES in the library's code object, one
+ * per GPU, held until the process ends; the call uses the array of the
+ * current device (the stream must belong to it) and allocates nothing.
+ * Each call first zeroes its heads' arrival counters and the status words
+ * (two small kernels on `stream`), then runs the step.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialized by the caller.
+ * Errors: as kvq_decode_step; KVQ_ERR_WORKSPACE when the step needs more
+ * than KVQ_NOALLOC_SCRATCH_BYTES of workspace (KVQ_WS_COUNTER_BYTES plus
+ * B*H_q*parts*(D+2)*4: up to 15,627 (batch, query head, part) records), with
+ * nothing launched. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+kvq_status kvq_decode_step_noalloc(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
+                                   int32_t H_q, int32_t H_kv, const uint16_t* q,
+                                   int64_t n_quant_tokens, const kvq_window* sink,
+                                   const kvq_window* res, float sm_scale, int32_t n_chunks,
+                                   float* out, int32_t append, void* stream);
+
 /* The two phases of kvq_decode_attention, for callers that combine partial
  * results of several calls (for example a sequence split across devices, each
  * holding a token range of the same heads) or time the phases apart.

@@ -37,6 +37,8 @@ def test_header_workspace_constants_match_binding():
     assert consts["KVQ_WS_STATUS"] == kvq.KVQ_WS_STATUS == 65536 * 4
     assert kvq.KVQ_WS_STATUS + 8 <= kvq.KVQ_WS_COUNTER_BYTES
     assert kvq.KVQ_WS_COUNTER_BYTES % 16 == 0   # the records stay 16-byte aligned
+    m = re.search(r"#define\s+KVQ_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == kvq.KVQ_NOALLOC_SCRATCH_BYTES
 
 
 def test_status_strings():
@@ -268,3 +270,25 @@ def test_mx_decode_plan_validation():
     c = _mx()
     assert kvq.raw_call("kvq_mx_decode_attention", ctypes.byref(c), 1, 32, 8, FAKE, 512, None,
                         None, ctypes.c_float(0.0), 0, FAKE, 16, FAKE, None) == kvq.KVQ_ERR_WORKSPACE
+
+
+def test_noalloc_step_rejects_workspace_past_scratch():
+    """kvq_decode_step_noalloc refuses a step whose workspace would exceed
+    its scratch array (KVQ_ERR_WORKSPACE) before touching the GPU, and
+    validates its arguments like kvq_decode_step."""
+    def call(B, H_q, H_kv, T, n_chunks, cfg=None, cache=None, out=FAKE):
+        cfg = cfg or _cfg()
+        cache = cache or _cache(t_cap=1 << 20)
+        return kvq.raw_call("kvq_decode_step_noalloc", ctypes.byref(cfg), ctypes.byref(cache),
+                            B, H_q, H_kv, FAKE, T, None, None, ctypes.c_float(0.0), n_chunks,
+                            out, 0, None)
+    # 1024 x 64 query heads x 4 parts of (D + 2) floats: 136 MB > 8 MiB
+    _, need = kvq.kvq_decode_plan(kvq.QCfg(bits=2, group=128), 1024, 64, 8, 4 * 128, 4)
+    assert need > kvq.KVQ_NOALLOC_SCRATCH_BYTES
+    assert call(1024, 64, 8, 4 * 128, 4) == kvq.KVQ_ERR_WORKSPACE
+    # 1 x 32 query heads x 256 parts fits (the 1M-token split)
+    _, need = kvq.kvq_decode_plan(kvq.QCfg(bits=2, group=128), 1, 32, 8, 1 << 20, 256)
+    assert need <= kvq.KVQ_NOALLOC_SCRATCH_BYTES
+    assert call(1, 32, 8, 4 * 128, 4, cfg=_cfg(bits=3)) == kvq.KVQ_ERR_ARG
+    assert call(1, 32, 8, 100, 4) == kvq.KVQ_ERR_ARG          # not a multiple of G
+    assert call(1, 30, 8, 4 * 128, 4) == kvq.KVQ_ERR_ARG      # H_q % H_kv
