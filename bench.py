@@ -622,6 +622,12 @@ def bench_mx(args, w, torch, kvq, synth):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / args.steps * 1e3
     n_win = w.S + w.R
+    gqa = w.H_q // w.H_kv
+    if gqa in (4, 8) and T % 128 == 0:   # the block-scaled matrix-core kernel
+        kern = f"decode_f8f4_kernel<{gqa},mxfp4> (kvq_mx_decode_attention, " + (
+            "one launch, in-launch merge)" if n_chunks <= 8 else "+ merge launch)")
+    else:
+        kern = "decode_mx_kernel + merge (kvq_mx_decode_attention, two launches)"
     alg = heads * per_head + heads * n_win * D * 2 * 2 + w.B * w.H_q * D * (2 + 4)
     gbps = alg / (us * 1e-6) / 1e9
     sr = stream_read_ceiling(kvq, torch, alg, n_copies, stream)
@@ -636,7 +642,7 @@ def bench_mx(args, w, torch, kvq, synth):
                    "cache_copies": n_copies, "step": "decode (kvq_mx_decode_attention)"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "decode_mx_kernel + merge (kvq_mx_decode_attention, two launches)",
+                     "kernel": kern,
                      "algorithmic_bytes": alg, "kernel_avg_us": round(us, 3),
                      "frac_of_stream_read": round(gbps / sr["GBps"], 4)},
         "stream_read": sr}), flush=True)

@@ -54,6 +54,8 @@
 #include "merge_common.h"
 #include "quant_common.h"
 
+#include <type_traits>
+
 namespace kvq {
 namespace {
 
@@ -79,6 +81,12 @@ constexpr int kDigits = 4;        // fp8 digits of an A value
 // a row), B: fp4 e2m1 (format 4) with unit scale (127)
 __device__ __forceinline__ f32x4 mfma_f8f4(const v8i& a, const v8i& b, f32x4 c, int sa) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, 127);
+}
+
+// The same product with B's per-lane E8M0 block scale sb (the low byte of
+// the operand): an MXFP4 block's scale factor, as stored in the cache.
+__device__ __forceinline__ f32x4 mfma_f8f4_mx(const v8i& a, const v8i& b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
 }
 
 __device__ __forceinline__ f32x4 mfma_f16(const u32x4& a, const u32x4& b, f32x4 c) {
@@ -196,20 +204,28 @@ typedef uint8_t ATile[16][kRowBytes];
 
 // ------------------------------------------------------------------ LDS
 
-template <int GQA>
+template <int GQA, bool MX>
 struct WaveLdsF {
   static constexpr int NH = GQA / 4;
+  struct OpTiles {
+    ATile ak[NH];                                 // q.K^T A operand [half][row][g*32 + byte]
+    ATile av[NH];                                 // p.V A operand
+  };
+  // MXFP4: the q.K^T operand is built once per block, before the first p.V
+  // one, so the two tiles share their bytes
+  union OpShared {
+    ATile ak[NH];
+    ATile av[NH];
+  };
   union {
-    struct {
-      ATile ak[NH];                               // q.K^T A operand [half][row][g*32 + byte]
-      ATile av[NH];                               // p.V A operand
-    } op;
+    std::conditional_t<MX, OpShared, OpTiles> op;
     uint32_t vt[kD][10];                          // fp16 window tile, [channel][token pair]
                                                   // (rows padded to 40 bytes)
   };
   float p[GQA][16];                               // window-tile probabilities
-  float pt[GQA][kG + 4];                          // group probabilities [head][token]
-                                                  // (rows padded: 4 heads, 4 banks apart)
+  // group probabilities [head][token] (rows padded: 4 heads, 4 banks apart);
+  // the MXFP4 path keeps them in registers
+  float pt[MX ? 1 : GQA][MX ? 1 : kG + 4];
 };
 
 template <int GQA, int NW>
@@ -228,37 +244,46 @@ struct MergeLdsF {
 //   [9728, 9856)   boosted row of each channel (16 = not boosted), then pad
 constexpr int kSlotV = 4096, kSlotKs = 8192, kSlotKm = 8448, kSlotVs = 8704, kSlotVm = 8960;
 constexpr int kSlotHi = 9216, kSlotBidx = 9728;
-template <bool KITTY>
-constexpr int slot_bytes() { return KITTY ? 10240 : 9216; }
-template <bool KITTY>
-constexpr int dma_per_group() { return KITTY ? 10 : 9; }
-template <int GQA, bool KITTY>
-constexpr int ring_slots() { return GQA == 4 ? (KITTY ? 10 : 12) : 6; }
+//
+// MXFP4 cache (128 tokens of a head per group):
+//   [0, 8192)      key codes of the 128 tokens, 64 bytes each; row 16 i + k
+//                  holds token 8 k + i (the q.K^T tiles' column order)
+//   [8192, 16384)  value codes, 16 rows of 8 tokens x 128 channels, as in the cache
+//   [16384, 16896) key E8M0 scales of the 128 tokens (4 blocks of 32 channels each)
+//   [16896, 17408) value E8M0 scales, 4 rows (32-token blocks) of 128 channels
+constexpr int kMxV = 8192, kMxKs = 16384, kMxVs = 16896;
+template <bool KITTY, bool MX>
+constexpr int slot_bytes() { return MX ? 17408 : KITTY ? 10240 : 9216; }
+template <bool KITTY, bool MX>
+constexpr int dma_per_group() { return MX ? 17 : KITTY ? 10 : 9; }
+template <int GQA, bool KITTY, bool MX>
+constexpr int ring_slots() {
+  return MX ? (GQA == 4 ? 6 : 5) : GQA == 4 ? (KITTY ? 10 : 12) : 6;
+}
 // groups the loader keeps in flight: fewer than ring_slots, and (DF - 1)
 // groups of copies (plus each group's flag copy) within the vector-memory
 // counter's 63
-template <int GQA, bool KITTY>
+template <int GQA, bool KITTY, bool MX>
 constexpr int in_flight() {
-  return ring_slots<GQA, KITTY>() - 1 < 63 / (dma_per_group<KITTY>() + 1) + 1
-             ? ring_slots<GQA, KITTY>() - 1
-             : 63 / (dma_per_group<KITTY>() + 1) + 1;
+  constexpr int per = dma_per_group<KITTY, MX>() + 1;
+  return ring_slots<GQA, KITTY, MX>() - 1 < 63 / per + 1 ? ring_slots<GQA, KITTY, MX>() - 1
+                                                         : 63 / per + 1;
 }
 
-template <int GQA, bool KITTY>
+template <int GQA, bool KITTY, bool MX>
 struct LdsF {
-  static constexpr int R = ring_slots<GQA, KITTY>();
+  static constexpr int R = ring_slots<GQA, KITTY, MX>();
   static constexpr int NW = block_waves<GQA, KITTY>();
   union {
-    WaveLdsF<GQA> w[NW - 1];
+    WaveLdsF<GQA, MX> w[NW - 1];
     MergeLdsF<GQA, NW> merge;
   } u;
-  alignas(16) uint8_t ring[R][slot_bytes<KITTY>()];
+  alignas(16) uint8_t ring[R][slot_bytes<KITTY, MX>()];
   int ready[R];     // chunk-relative group (mod kSeqLen) a slot holds once its data has arrived
   int empty[R];     // the group a slot may receive next (its previous one was copied out)
   int next_group;   // next group a consumer claims
   int stalled;      // bit 0: a wait ran past its spin limit; bit 1: a page outside the pool
   int last;         // this block is the last of its head to finish (in-launch merge)
-  int next_item;    // next append item a consumer claims
 };
 
 struct Operands {
@@ -365,6 +390,30 @@ __device__ __forceinline__ void write_digits(ATile& tile, int hr, uint32_t off,
   }
 }
 
+// Byte offset, inside row 0 of an A-operand tile, of contraction elements
+// 8o..8o+7 when the B operand is fp4 in its plain order (nibble j of lane
+// group g is element 32g + j): by the A byte order above, element k sits at
+// byte 16(k/64) + k%16 of lane group (k%64)/16, and the octet stays whole.
+__device__ __forceinline__ uint32_t a_offset_nat(int o) {
+  return (uint32_t)(32 * ((o >> 1) & 3) + 16 * (o >> 3) + 8 * (o & 1));
+}
+
+// Digits of 8 values of consecutive contraction elements (bytes off..off+7
+// of rows 4*hr..4*hr+3, off from a_offset_nat): the MXFP4 operands, whose B
+// lane group g takes the 32 consecutive elements of block g as stored.
+__device__ __forceinline__ void write_digits_nat(ATile& tile, int hr, uint32_t off,
+                                                 const float (&x)[8], int eb) {
+  uint32_t lo[kDigits], hi[kDigits];
+  fp8_digits(x[0], x[1], x[2], x[3], eb, lo);
+  fp8_digits(x[4], x[5], x[6], x[7], eb, hi);
+  uint8_t* base = &tile[4 * hr][0] + off;
+#pragma unroll
+  for (int k = 0; k < kDigits; ++k) {
+    *reinterpret_cast<uint32_t*>(base + k * kRowBytes) = lo[k];
+    *reinterpret_cast<uint32_t*>(base + k * kRowBytes + 4) = hi[k];
+  }
+}
+
 __device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
   const u32x4* p = reinterpret_cast<const u32x4*>(&tile[m][32 * g]);
   const u32x4 lo = p[0], hi = p[1];
@@ -382,10 +431,11 @@ __device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
 // the quantize kernel (KIVI page, Steps 1-2): min and max by the total order
 // -0 < +0, scale fp16((max - min)/3), codes by quant_code_rcp.  The slice is
 // four self-contained items (16 key channels, or 16 value tokens, each with
-// its own statistics and whole packed words) that the first consumer waves
-// past the block barrier claim, while the first groups are still on their
-// way.  The appended group lies past
-// every group the launch reads.
+// its own statistics and whole packed words), item k taken by consumer wave
+// k + 1 right after the block barrier, while the first groups are still on
+// their way (a fixed assignment rather than a claim loop: the loop kept the
+// items' registers live across the group loop).  The appended group lies
+// past every group the launch reads.
 constexpr int kAppWpt = kD / 16;   // 2-bit key words per token
 constexpr int kAppItems = 4;       // items per slice
 
@@ -568,20 +618,29 @@ __device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int64_t b, 
 
 // ------------------------------------------------------------------ kernel
 
-template <int GQA, bool KITTY>
+// MX: the cache is an MXFP4 one (kvq_mx_cache in a.c: k_codes / v_codes its
+// code words, k_scale / v_scale its E8M0 bytes, no page table): keys and
+// values are E2M1 codes with a power-of-two scale per block of 32 along
+// each product's contraction axis, which the block-scaled matrix-core
+// product takes as they are (BitDecoding page, native mxfp4 data with block
+// scale factors).  The quantized part then has no per-group operand work on
+// the key side (the query's digits are built once) and no min terms.
+template <int GQA, bool KITTY, bool MX>
 __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8f4_kernel(DecodeArgs a) {
+  static_assert(!(KITTY && MX), "the Kitty boost is a min-max cache");
   constexpr int NH = GQA / 4;    // heads per lane (r and r + 4)
-  constexpr int R = ring_slots<GQA, KITTY>();
-  constexpr int DF = in_flight<GQA, KITTY>();
+  constexpr int R = ring_slots<GQA, KITTY, MX>();
+  constexpr int DF = in_flight<GQA, KITTY, MX>();
   constexpr int kWaves = block_waves<GQA, KITTY>();
   // wave 0 is the loader (the first wave of a block to start), 1.. consume
   constexpr int kConsumers = kWaves - 1, kLoader = 0;
   constexpr int kThreadsF = 64 * kWaves;
-  static_assert((dma_per_group<KITTY>() + 1) * (DF - 1) < 64, "vmcnt range");
+  static_assert((dma_per_group<KITTY, MX>() + 1) * (DF - 1) < 64, "vmcnt range");
   static_assert(R < kSeqLen, "ready tags must not repeat within the ring");
-  constexpr int SB = slot_bytes<KITTY>();
-  constexpr int NDMA = dma_per_group<KITTY>();
-  __shared__ LdsF<GQA, KITTY> sh;
+  static_assert(sizeof(LdsF<GQA, KITTY, MX>) <= 160 * 1024, "LDS per CU");
+  constexpr int SB = slot_bytes<KITTY, MX>();
+  constexpr int NDMA = dma_per_group<KITTY, MX>();
+  __shared__ LdsF<GQA, KITTY, MX> sh;
 
   // Every launch argument the first phase needs, fetched in one round trip
   // (the compiler would otherwise load each one just before its first use,
@@ -604,7 +663,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
   const int ngc = (int)max<int64_t>(0, min<int64_t>(seq_groups(a, b, kG), gb + a.groups_per_chunk) - gb);
   // slice of the appended group this block quantizes (-1: none)
-  const int app_slice = (!KITTY && a.append && chunk < 4) ? chunk : -1;
+  const int app_slice = (!KITTY && !MX && a.append && chunk < 4) ? chunk : -1;
 
   // The loader wave sets up the ring's flags and meets the other waves at the
   // block barrier before its first copy; past it, the loader waits for
@@ -638,7 +697,6 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     if (tid == 0) {
       sh.next_group = 0;
       sh.stalled = 0;
-      sh.next_item = 0;
     }
     // the flags are written before any copy can land on them
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -703,12 +761,33 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
           blk = 0;
         }
       }
+      if constexpr (MX) {
+        // the group's 128 tokens: key code rows (64 B each), value code rows
+        // (8 tokens x 128 channels, 512 B each), key scales (4 B per token;
+        // lanes 0..31) and value scales (128 B per 32 tokens; lanes 32..63)
+        // (key rows land transposed: slot row 16 i + k holds token 8 k + i)
+        const int64_t t0 = (gb + jo) * kG;
+        const char* kc = reinterpret_cast<const char*>(a.c.k_codes) + (head * a.c.t_cap + t0) * 64 +
+                         512 * (lane >> 2) + 16 * (lane & 3);
+        const char* vc = reinterpret_cast<const char*>(a.c.v_codes) +
+                         (head * (a.c.t_cap / 8) + t0 / 8) * (kD * 4) + 16 * lane;
+        const char* sc =
+            lane < 32 ? reinterpret_cast<const char*>(a.c.k_scale) + (head * a.c.t_cap + t0) * 4 + 16 * lane
+                      : reinterpret_cast<const char*>(a.c.v_scale) +
+                            (head * (a.c.t_cap / 32) + t0 / 32) * kD + 16 * (lane - 32);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma_1k(sl + 1024 * i, kp + blk * 4096 + 1024 * i);
+        for (int i = 0; i < 8; ++i) dma_1k(sl + 1024 * i, kc + 64 * i);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma_1k(sl + kSlotV + 1024 * i, vp + blk * 4096 + 1024 * i);
-      dma_1k(sl + kSlotKs, mp + blk * 256);
-      if constexpr (KITTY) dma_1k(sl + kSlotHi, xp + blk * xstep);
+        for (int i = 0; i < 8; ++i) dma_1k(sl + kMxV + 1024 * i, vc + 1024 * i);
+        dma_1k(sl + kMxKs, sc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma_1k(sl + 1024 * i, kp + blk * 4096 + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma_1k(sl + kSlotV + 1024 * i, vp + blk * 4096 + 1024 * i);
+        dma_1k(sl + kSlotKs, mp + blk * 256);
+        if constexpr (KITTY) dma_1k(sl + kSlotHi, xp + blk * xstep);
+      }
       if (lane == 0)
         dma_flag(__builtin_amdgcn_readfirstlane(ready0 + 4 * s), kSeq.v + (j & (kSeqLen - 1)));
       if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
@@ -797,8 +876,14 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
         for (int e = 0; e < 8; ++e) qv[j][e] *= qs;
     }
     const float q_unscale = exp2i(e_q - 8);
+    // channel of this lane's accumulator block blk (column n of a p.V product):
+    // the 2-bit value words give channels 4n.. and 64 + 4n..; MXFP4 value
+    // columns are 16 consecutive channels
+    auto chan = [&](int blk) -> int {
+      return MX ? 16 * blk + n : 64 * (blk >> 2) + 4 * n + (blk & 3);
+    };
 
-    WaveLdsF<GQA>& L = sh.u.w[cw];
+    WaveLdsF<GQA, MX>& L = sh.u.w[cw];
 
     // ------------------------------------------------------ fp16 window
     // q.K^T on fp16 matrix cores (raw keys as B), the online softmax, p.V
@@ -879,7 +964,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
           }
 #pragma unroll
           for (int blk = 0; blk < 8; ++blk) {
-            const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
+            const int d = chan(blk);
             u32x4 bv = u32x4{0u, 0u, 0u, 0u};
             if (kq < 2) {   // rows are 8-byte aligned: two 8-byte reads
               const u32x2 b0 = *reinterpret_cast<const u32x2*>(&L.vt[d][4 * kq]);
@@ -1005,16 +1090,10 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     };
 
     // logits of the group, softmax, value A operand and p.V
-    auto pv_step = [&](const Operands& pf) {
-      float logit[NH][8];
-      const float ek = exp2i(e_q - 8 + e_s + 1);   // fp4 codes are c/2
-#pragma unroll
-      for (int H = 0; H < NH; ++H)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          logit[H][t] =
-              fmaf((cq[H][t][0] + cq[H][t][1]) + (cq[H][t][2] + cq[H][t][3]), ek, bias[H]);
-      float alpha[NH];
+    // Online softmax over a group's logits (token 16t + n of head r + 4H in
+    // logit[H][t]): running max and sum, each head's rescale factor alpha,
+    // and p[H][e] = the probability of token 8n + e (through an LDS transpose).
+    auto softmax_group = [&](const float (&logit)[NH][8], float (&alpha)[NH], float (&p)[NH][8]) {
 #pragma unroll
       for (int H = 0; H < NH; ++H) {
         float v = logit[H][0];
@@ -1027,24 +1106,43 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
         float sum = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const float pe = fexp2(logit[H][t] - m_new);   // token 16t + n
-          L.pt[r + 4 * H][16 * t + n] = pe;
+          const float pe = fexp2(logit[H][t] - m_new);
+          if constexpr (MX) p[H][t] = pe;                  // token 8n + t
+          else L.pt[r + 4 * H][16 * t + n] = pe;           // token 16t + n
           sum += pe;
         }
         l_part[H] = fmaf(l_part[H], alpha[H], sum);
       }
-      wave_sync();
-      float p[NH][8];                // tokens 8n..8n+7 of head r + 4H
+      // the min-max path's logits are tokens 16t + n; its p.V digits want
+      // tokens 8n..8n+7 of the lane, hence a transpose through LDS (the
+      // MXFP4 path loads its key rows transposed instead)
+      if constexpr (!MX) {
+        wave_sync();
 #pragma unroll
-      for (int H = 0; H < NH; ++H) {
-        const f32x4* pp = reinterpret_cast<const f32x4*>(&L.pt[r + 4 * H][8 * n]);
-        const f32x4 p0 = pp[0], p1 = pp[1];
+        for (int H = 0; H < NH; ++H) {
+          const f32x4* pp = reinterpret_cast<const f32x4*>(&L.pt[r + 4 * H][8 * n]);
+          const f32x4 p0 = pp[0], p1 = pp[1];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[H][e] = p0[e];
-          p[H][4 + e] = p1[e];
+          for (int e = 0; e < 4; ++e) {
+            p[H][e] = p0[e];
+            p[H][4 + e] = p1[e];
+          }
         }
       }
+    };
+
+    auto pv_step = [&](const Operands& pf) {
+      float logit[NH][8];
+      const float ek = exp2i(e_q - 8 + e_s + 1);   // fp4 codes are c/2
+#pragma unroll
+      for (int H = 0; H < NH; ++H)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          logit[H][t] =
+              fmaf((cq[H][t][0] + cq[H][t][1]) + (cq[H][t][2] + cq[H][t][3]), ek, bias[H]);
+      float alpha[NH];
+      float p[NH][8];                // tokens 8n..8n+7 of head r + 4H
+      softmax_group(logit, alpha, p);
 
       // value A operand: digits of p s_t 2^(8 - e_v); min term
       const int e_v_new = max(e_v, row_exp_f16(pf.vs));
@@ -1097,17 +1195,11 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       }
     };
 
-    // the append's items first (the waves that get here first take them)
-    if (app_slice >= 0) {
-      for (;;) {
-        int kl = 0;
-        if (lane == 0) kl = atomicAdd(&sh.next_item, 1);
-        const int k = __builtin_amdgcn_readlane(kl, 0);
-        if (k >= kAppItems) break;
-        u32x4 app_x[4];
-        append_item_load(a, head, app_slice, k, lane, app_x);
-        append_item(a, head, app_slice, k, lane, app_x);
-      }
+    // the append's items first: item k by consumer k + 1 (waves 1..4)
+    if (app_slice >= 0 && wave - 1 < kAppItems) {
+      u32x4 app_x[4];
+      append_item_load(a, head, app_slice, wave - 1, lane, app_x);
+      append_item(a, head, app_slice, wave - 1, lane, app_x);
     }
 
     // Consumers claim the chunk's groups in order from a block counter and
@@ -1115,36 +1207,152 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     // Only the claim branches on the lane; every store in the loop is made
     // by all lanes with the same value (a lane-divergent store at the end of
     // the body lets the compiler split the wave across iterations).
-    for (;;) {
-      int jl = 0;
-      if (lane == 0) jl = atomicAdd(&sh.next_group, 1);
-      const int j = __builtin_amdgcn_readlane(jl, 0);
-      if (j >= ngc) break;
-      const int s = j % R;
-      if (!spin_until(&sh.ready[s], j & (kSeqLen - 1))) {
-        if (lane == 0) __hip_atomic_fetch_or(&sh.stalled, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        break;
+    if constexpr (!MX) {
+      for (;;) {
+        int jl = 0;
+        if (lane == 0) jl = atomicAdd(&sh.next_group, 1);
+        const int j = __builtin_amdgcn_readlane(jl, 0);
+        if (j >= ngc) break;
+        const int s = j % R;
+        if (!spin_until(&sh.ready[s], j & (kSeqLen - 1))) {
+          if (lane == 0) __hip_atomic_fetch_or(&sh.stalled, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          break;
+        }
+        asm volatile("" ::: "memory");
+        Operands pf;
+        read_slot(s, pf);
+        asm volatile("" ::: "memory");
+        // this wave's LDS reads complete in order before its next LDS write
+        lds_store(&sh.empty[s], j + R);
+        qk_issue(pf);
+        pv_step(pf);
       }
-      asm volatile("" ::: "memory");
-      Operands pf;
-      read_slot(s, pf);
-      asm volatile("" ::: "memory");
-      // this wave's LDS reads complete in order before its next LDS write
-      lds_store(&sh.empty[s], j + R);
-      qk_issue(pf);
-      pv_step(pf);
-    }
 
-    // fold the digit rows of the quantized p.V into the lane's channels
-    const float ev = exp2i(e_v - 8 + 1);   // p.V digits carry 2^(8 - e_v), codes are c/2
+      // fold the digit rows of the quantized p.V into the lane's channels
+      const float ev = exp2i(e_v - 8 + 1);   // p.V digits carry 2^(8 - e_v), codes are c/2
 #pragma unroll
-    for (int H = 0; H < NH; ++H) {
-      const float mts = row_sum16(mterm[H]);
+      for (int H = 0; H < NH; ++H) {
+        const float mts = row_sum16(mterm[H]);
 #pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
-        const f32x4 v = acc[H][blk];
-        wsum[H][blk] += fmaf((v[0] + v[1]) + (v[2] + v[3]), ev, mts);
+        for (int blk = 0; blk < 8; ++blk) {
+          const f32x4 v = acc[H][blk];
+          wsum[H][blk] += fmaf((v[0] + v[1]) + (v[2] + v[3]), ev, mts);
+        }
       }
+    } else {
+      // ---------------------------------------------------- MXFP4 groups
+      // Both products on the block-scaled matrix core with the cache's codes
+      // and E8M0 bytes as the B operand and its scales.  An fp4 B lane
+      // (n, g) holds contraction elements 32g..32g+31 and its scale byte
+      // covers them; block g of the cache (channels, resp. tokens,
+      // 32g..32g+31, in order) goes to lane group g, so a lane's B operand
+      // is one block as stored and its scale that block's.  The A digits
+      // follow the instruction's fp8 byte order (a_offset_nat).
+      //  q.K^T, tile t: column n is token 8n + t, so that a lane's eight
+      //    logits (tokens 8n..8n+7) are its p.V digit bytes 8n..8n+7 in
+      //    token order; lane (n, g) takes the 16 code bytes of that token,
+      //    channel block g, and k_scale[8n + t][g]; A = the query's fp8
+      //    digits (|qv| < 2^8), built once.
+      //  p.V, channel block blk (channels 16 blk..16 blk+15): lane (n, g)
+      //    takes code rows 4g..4g+3 (tokens 32g..32g+31) of channel
+      //    16 blk + n and v_scale[block g][16 blk + n]; A = digits of
+      //    2^8 p_t, tokens in order.
+      v8i aqm[NH];
+      const uint32_t a_nat = a_offset_nat(n);
+#pragma unroll
+      for (int H = 0; H < NH; ++H) write_digits_nat(L.op.av[H], r, a_nat, qv[H], 0);
+      wave_sync();
+#pragma unroll
+      for (int H = 0; H < NH; ++H) aqm[H] = read_a(L.op.av[H], lane & 15, lane >> 4);
+      wave_sync();   // the tile now takes the p.V digits
+      for (;;) {
+        int jl = 0;
+        if (lane == 0) jl = atomicAdd(&sh.next_group, 1);
+        const int j = __builtin_amdgcn_readlane(jl, 0);
+        if (j >= ngc) break;
+        const int s = j % R;
+        if (!spin_until(&sh.ready[s], j & (kSeqLen - 1))) {
+          if (lane == 0) __hip_atomic_fetch_or(&sh.stalled, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          break;
+        }
+        asm volatile("" ::: "memory");
+        const uint8_t* sp = &sh.ring[s][0];
+        u32x4 kc[8];
+        uint32_t ksc[8], vsc[8], vc[8][4];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          kc[t] = *reinterpret_cast<const u32x4*>(sp + (16 * t + n) * 64 + 16 * r);
+          ksc[t] = sp[kMxKs + (8 * n + t) * 4 + r];
+        }
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vc[blk][i] = *reinterpret_cast<const uint32_t*>(sp + kMxV + (4 * r + i) * (kD * 4) +
+                                                            (16 * blk + n) * 4);
+          vsc[blk] = sp[kMxVs + r * kD + 16 * blk + n];
+        }
+        asm volatile("" ::: "memory");
+        // this wave's LDS reads complete in order before its next LDS write
+        lds_store(&sh.empty[s], j + R);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const v8i bk = v8i{(int)kc[t][0], (int)kc[t][1], (int)kc[t][2], (int)kc[t][3], 0, 0, 0, 0};
+#pragma unroll
+          for (int H = 0; H < NH; ++H)
+            cq[H][t] = mfma_f8f4_mx(aqm[H], bk, f32x4{0.f, 0.f, 0.f, 0.f}, sa_digit, (int)ksc[t]);
+        }
+        float logit[NH][8];
+#pragma unroll
+        for (int H = 0; H < NH; ++H)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            logit[H][t] = ((cq[H][t][0] + cq[H][t][1]) + (cq[H][t][2] + cq[H][t][3])) * q_unscale;
+        float alpha[NH];
+        float p[NH][8];
+        softmax_group(logit, alpha, p);
+#pragma unroll
+        for (int H = 0; H < NH; ++H) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = p[H][e] * 256.f;
+          write_digits_nat(L.op.av[H], r, a_nat, x, 0);
+        }
+        wave_sync();
+        {
+          bool same = true;
+#pragma unroll
+          for (int H = 0; H < NH; ++H) same = same && alpha[H] == 1.f;
+          if (!__all(same)) {
+#pragma unroll
+            for (int H = 0; H < NH; ++H)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                acc[H][i] *= alpha[H];
+                wsum[H][i] *= alpha[H];
+              }
+          }
+        }
+#pragma unroll
+        for (int H = 0; H < NH; ++H) {
+          const v8i apv = read_a(L.op.av[H], lane & 15, lane >> 4);
+#pragma unroll
+          for (int blk = 0; blk < 8; ++blk)
+            acc[H][blk] = mfma_f8f4_mx(apv,
+                                       v8i{(int)vc[blk][0], (int)vc[blk][1], (int)vc[blk][2],
+                                           (int)vc[blk][3], 0, 0, 0, 0},
+                                       acc[H][blk], sa_digit, (int)vsc[blk]);
+        }
+        wave_sync();   // the digits are read before the next group writes them
+      }
+      // fold the digit rows (2^8 p) into the lane's channels
+#pragma unroll
+      for (int H = 0; H < NH; ++H)
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+          const f32x4 v = acc[H][blk];
+          wsum[H][blk] += ((v[0] + v[1]) + (v[2] + v[3])) * (1.f / 256.f);
+        }
     }
   }
 
@@ -1163,7 +1371,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     }
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
-      const int d = 64 * (blk >> 2) + 4 * n + (blk & 3);
+      const int d = MX ? 16 * blk + n : 64 * (blk >> 2) + 4 * n + (blk & 3);
       M.num[wave][h][d] = wsum[H][blk];
     }
   }
@@ -1224,12 +1432,28 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
 hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
   if (a.n_boost > 0) {
-    if (a.gqa == 4) decode_f8f4_kernel<4, true><<<grid, 64 * block_waves<4, true>(), 0, st>>>(a);
-    else decode_f8f4_kernel<8, true><<<grid, 64 * block_waves<8, true>(), 0, st>>>(a);
+    if (a.gqa == 4) decode_f8f4_kernel<4, true, false><<<grid, 64 * block_waves<4, true>(), 0, st>>>(a);
+    else decode_f8f4_kernel<8, true, false><<<grid, 64 * block_waves<8, true>(), 0, st>>>(a);
   } else {
-    if (a.gqa == 4) decode_f8f4_kernel<4, false><<<grid, 64 * block_waves<4, false>(), 0, st>>>(a);
-    else decode_f8f4_kernel<8, false><<<grid, 64 * block_waves<8, false>(), 0, st>>>(a);
+    if (a.gqa == 4) decode_f8f4_kernel<4, false, false><<<grid, 64 * block_waves<4, false>(), 0, st>>>(a);
+    else decode_f8f4_kernel<8, false, false><<<grid, 64 * block_waves<8, false>(), 0, st>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mx_mfma(const kvq_mx_cache& mc, const DecodeArgs& args, hipStream_t st) {
+  DecodeArgs a = args;
+  a.c = CacheArgs{};
+  a.c.k_codes = reinterpret_cast<uint32_t*>(mc.k_codes);
+  a.c.v_codes = reinterpret_cast<uint32_t*>(mc.v_codes);
+  a.c.k_scale = reinterpret_cast<uint16_t*>(mc.k_scale);   // E8M0 bytes
+  a.c.v_scale = reinterpret_cast<uint16_t*>(mc.v_scale);
+  a.c.t_cap = mc.t_cap;
+  a.c.pages = nullptr;
+  a.append = 0;
+  const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
+  if (a.gqa == 4) decode_f8f4_kernel<4, false, true><<<grid, 64 * block_waves<4, false>(), 0, st>>>(a);
+  else decode_f8f4_kernel<8, false, true><<<grid, 64 * block_waves<8, false>(), 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -512,6 +512,16 @@ kvq_status kvq_mx_decode_plan(int32_t B, int32_t H_q, int32_t H_kv, int64_t n_qu
   if (n_quant_tokens < 0 || n_quant_tokens % 32 || n_chunks_req < 0) return KVQ_ERR_ARG;
   const int64_t heads = (int64_t)B * H_kv;
   if (heads > 65535) return KVQ_ERR_ARG;
+  if (kvq::mx_mfma_supported(gqa, n_quant_tokens)) {
+    // matrix-core kernel: chunks of 128-token groups, one resident block per
+    // CU (the grid runs in one round), windows spread over the chunks
+    const int64_t groups = n_quant_tokens / 128;
+    int64_t n = n_chunks_req > 0 ? n_chunks_req : kvq::kCUs / heads;
+    n = std::max<int64_t>(1, std::min<int64_t>({n, std::max<int64_t>(1, groups), kMaxChunks}));
+    if (n_chunks) *n_chunks = (int32_t)n;
+    if (ws_bytes) *ws_bytes = workspace_bytes(B, H_q, n);
+    return KVQ_OK;
+  }
   const int64_t blocks = n_quant_tokens / 32;
   int64_t n = n_chunks_req;
   // automatic: about 16 blocks per CU (the vector-ALU kernel is bound by
@@ -572,6 +582,17 @@ kvq_status kvq_mx_decode_attention(const kvq_mx_cache* cache, int32_t B, int32_t
   a.status = static_cast<int32_t*>(workspace) + kvq::kStatusIndex;
   a.out = out;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kvq::mx_mfma_supported(a.gqa, n_quant_tokens)) {
+    a.n_groups = n_quant_tokens / 128;
+    a.groups_per_chunk = (int32_t)((a.n_groups + nc - 1) / nc);
+    a.n_parts = nc;
+    if (nc <= kvq::kFusedMergeParts) {   // one launch: the last block of a head merges
+      a.counters = static_cast<int32_t*>(workspace);
+      return hip_status(kvq::launch_decode_mx_mfma(*cache, a, s));
+    }
+    if ((st = hip_status(kvq::launch_decode_mx_mfma(*cache, a, s))) != KVQ_OK) return st;
+    return hip_status(kvq::launch_merge(a, s));
+  }
   if ((st = hip_status(kvq::launch_decode_mx(*cache, a, s))) != KVQ_OK) return st;
   return hip_status(kvq::launch_merge(a, s));
 }

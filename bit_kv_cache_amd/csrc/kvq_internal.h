@@ -193,5 +193,14 @@ hipError_t launch_merge_append(int bits, int v_bits, int group, const DecodeArgs
                                const QuantArgs& q, hipStream_t s);
 hipError_t launch_decode_mfma(int bits, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t s);
+// Split-K decode over an MXFP4 cache on the block-scaled matrix core (GQA 4
+// or 8, whole 128-token groups: a.n_groups counts them, a.groups_per_chunk
+// too; parts n_chunks, the windows spread over them; merges in the same
+// launch when a.counters is set).
+hipError_t launch_decode_mx_mfma(const kvq_mx_cache& mc, const DecodeArgs& a, hipStream_t s);
+// Whether that kernel serves an MXFP4 step.
+inline bool mx_mfma_supported(int gqa, int64_t n_quant_tokens) {
+  return (gqa == 4 || gqa == 8) && n_quant_tokens % 128 == 0;
+}
 
 }  // namespace kvq

@@ -265,8 +265,15 @@ def test_mx_decode_plan_validation():
     assert plan(1, 32, 8, 500, 0)[0] == kvq.KVQ_ERR_ARG      # not whole 32-token blocks
     assert plan(1, 48, 8, 512, 0)[0] == kvq.KVQ_ERR_UNSUPPORTED
     assert plan(1, 30, 8, 512, 0)[0] == kvq.KVQ_ERR_ARG
-    assert plan(1, 32, 8, 512, 100)[1] == 16                # at most one chunk per block
-    assert plan(8, 32, 8, 32768, 0)[1] == 64                # automatic: ~16 blocks per CU
+    # at most one chunk per unit of work: a 128-token group on the matrix-core
+    # path (GQA 4 / 8, whole groups), a 32-token block on the vector-ALU one
+    assert plan(1, 32, 8, 512, 100)[1] == 4
+    assert plan(1, 32, 8, 544, 100)[1] == 17
+    assert plan(1, 8, 8, 512, 100)[1] == 16
+    # automatic: one resident block per CU on the matrix-core path (256 / 64
+    # heads), about 16 blocks per CU on the vector-ALU one
+    assert plan(8, 32, 8, 32768, 0)[1] == 4
+    assert plan(8, 64, 64, 32768, 0)[1] == 8
     c = _mx()
     assert kvq.raw_call("kvq_mx_decode_attention", ctypes.byref(c), 1, 32, 8, FAKE, 512, None,
                         None, ctypes.c_float(0.0), 0, FAKE, 16, FAKE, None) == kvq.KVQ_ERR_WORKSPACE

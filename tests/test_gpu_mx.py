@@ -65,19 +65,37 @@ def test_mx_quantize_append_dequantize_bit_exact(B, H_kv, n):
     assert np.array_equal(vo.cpu().numpy().view(np.uint32), vr.view(np.uint32))
 
 
-@pytest.mark.parametrize("B,H_q,H_kv,T,S,R", [(1, 32, 8, 512, 5, 40), (2, 16, 2, 224, 0, 17),
-                                              (1, 8, 8, 96, 3, 1), (1, 32, 8, 0, 4, 9)])
-def test_mx_decode_matches_oracle(B, H_q, H_kv, T, S, R):
+# (B, H_q, H_kv, T, S, R): GQA 4 and 8 with whole 128-token groups take the
+# block-scaled matrix-core kernel (one launch up to 8 parts per head, a merge
+# launch past that); GQA 1 and 2 and token counts with a 32-token tail take
+# the vector-ALU kernel.
+MX_CASES = [(1, 32, 8, 512, 5, 40), (2, 16, 2, 224, 0, 17), (1, 8, 8, 96, 3, 1),
+            (1, 32, 8, 0, 4, 9), (2, 16, 2, 640, 3, 33), (1, 32, 8, 2048, 0, 128),
+            (3, 32, 4, 1152, 7, 64), (1, 64, 8, 896, 2, 5), (1, 16, 8, 256, 0, 3)]
+
+
+@pytest.mark.parametrize("edges", [False, True])
+@pytest.mark.parametrize("B,H_q,H_kv,T,S,R", MX_CASES)
+def test_mx_decode_matches_oracle(B, H_q, H_kv, T, S, R, edges):
     """Decode over the MXFP4 cache (plus fp16 sink and residual windows) at
     several chunk counts: max-abs within 2e-3 of the oracle's fp64 attention
-    over the same dequantized cache."""
+    over the same dequantized cache.  With edges, the cache also holds blocks
+    of zeros (E8M0 byte 0), fp16 subnormals and exact E2M1 ties."""
     import bit_kv_cache_amd as kvq
-    from parity_util import TOL
+    from parity_util import TOL, max_err
     heads = B * H_kv
     rng = np.random.default_rng(41 + T + H_q)
     k = rng.standard_normal((heads, max(T, 32), D)).astype(np.float32)
     k[:, :, 3] *= 10.0
     v = rng.standard_normal((heads, max(T, 32), D)).astype(np.float32)
+    if edges and T >= 128:
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.0])
+        k[:, 5, :] = 0.0                                  # a token of zero key blocks
+        k[:, 9, 64:96] *= 2.0 ** -20                      # fp16 subnormals
+        k[:, 13, 32:64] = np.resize(np.concatenate([[4.0], mids]), 32) * 2.0 ** -3
+        v[:, 32:64, 7] = 0.0                              # a value block of zeros
+        v[:, 64:96, 8] = np.resize(np.concatenate([[6.0], -mids]), 32) * 2.0 ** 2
+        v[:, 96:128, 20:40] *= 2.0 ** -18                 # value subnormals
     k, v = k.astype(np.float16), v.astype(np.float16)
     ks = rng.standard_normal((heads, max(S, 1), D)).astype(np.float16)
     vs = rng.standard_normal((heads, max(S, 1), D)).astype(np.float16)
@@ -97,12 +115,14 @@ def test_mx_decode_matches_oracle(B, H_q, H_kv, T, S, R):
                                      k_sink=ks.view(np.uint16) if S else None,
                                      v_sink=vs.view(np.uint16) if S else None, n_sink=S,
                                      k_res=kr.view(np.uint16), v_res=vr.view(np.uint16), n_res=R)
-    for n_chunks in sorted({0, 1, 3, max(1, T // 32)}):
+    for n_chunks in sorted({0, 1, 3, 7, 9, max(1, T // 128), max(1, T // 32)}):
         _, ws_bytes = kvq.kvq_mx_decode_plan(B, H_q, H_kv, T, n_chunks)
         ws = kvq.decode_workspace(ws_bytes)
         out = torch.empty((B, H_q, D), dtype=torch.float32, device="cuda")
         kvq.kvq_mx_decode_attention(gc, B, H_q, H_kv, q_d, T, kvq.window(ks_d, vs_d, S),
                                     kvq.window(kr_d, vr_d, R), out, ws, n_chunks=n_chunks)
         torch.cuda.synchronize()
-        err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
+        err = max_err(out, ref)
         assert err <= TOL, f"n_chunks={n_chunks}: max-abs {err:.3g}"
+        # the in-launch merge leaves the arrival counters zero
+        assert int(ws[: kvq.KVQ_WS_STATUS // 4].view(torch.int32).abs().sum().item()) == 0
