@@ -120,40 +120,71 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(w) -> str:
-    return os.path.join(ROOT, "profiles", f"hbm_traffic_{split_kernel(w)}_{w.name}.txt")
+def mx_kernel(w) -> str:
+    """Kernel name (with template arguments, as the profiler prints it) of the
+    MXFP4 decode for this workload."""
+    if w.gqa in (4, 8) and w.T % 128 == 0:
+        return f"decode_f8f4_kernel<{w.gqa}, false, true>"
+    return "decode_mx_kernel"
 
 
-def _counter_means(csv_path, counter, kernel):
+def traffic_file(w, mx: bool = False) -> str:
+    kern = "decode_f8f4_kernel_mxfp4" if mx else split_kernel(w)
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{kern}_{w.name}.txt")
+
+
+# kernels of the library (and the copy kernel) whose counters are recorded
+TRAFFIC_KERNELS = ("decode_", "merge_", "quantize_kernel", "mx_quantize_kernel")
+
+
+def _counter_means(csv_path, counter):
+    """Mean counter value per dispatch of every library kernel in the run, by
+    the kernel's name with template arguments."""
     import csv
+    import re
     per = {}
     with open(csv_path) as fh:
         for r in csv.DictReader(fh):
             if r["Counter_Name"] != counter:
                 continue
-            for key in (kernel, COPY_KERNEL):
-                if key in r["Kernel_Name"]:
-                    per.setdefault(key, []).append(float(r["Counter_Value"]))
+            name = r["Kernel_Name"]
+            if COPY_KERNEL in name:
+                key = COPY_KERNEL
+            else:
+                m = re.search(r"(\w+_kernel)(<[^()]*>)?\(", name)
+                if not m or not m.group(1).startswith(TRAFFIC_KERNELS):
+                    continue
+                key = m.group(1) + (m.group(2) or "")
+            per.setdefault(key, []).append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
-def write_traffic(w, fetch_csv: str, write_csv: str, command: str) -> dict:
-    """Turn the two counter runs into bytes per launch of the split-K kernel."""
-    kern = split_kernel(w)
-    fm, fn = _counter_means(fetch_csv, "FETCH_SIZE", kern)
-    wm, wn = _counter_means(write_csv, "WRITE_SIZE", kern)
+def write_traffic(w, fetch_csv: str, write_csv: str, command: str, mx: bool = False) -> dict:
+    """Turn the two counter runs into bytes per launch of the decode kernel
+    (and of every other library kernel the run launched)."""
+    want = mx_kernel(w) if mx else split_kernel(w)
+    fm, fn = _counter_means(fetch_csv, "FETCH_SIZE")
+    wm, wn = _counter_means(write_csv, "WRITE_SIZE")
     f_scale = CALIB_COPY_BYTES / (fm[COPY_KERNEL] * 1024)
     w_scale = CALIB_COPY_BYTES / (wm[COPY_KERNEL] * 1024)
+    # the decode kernel: the most-launched instantiation matching its name
+    kern = max((k for k in fm if k.startswith(want) or want.startswith(k)),
+               key=lambda k: fn[k])
     fetch = fm[kern] * 1024 * f_scale
     write = wm[kern] * 1024 * w_scale
-    rec = {"workload": w.name, "kernel": kern, "source_hash": kernel_source_hash(),
+    others = {k: {"fetch_bytes": round(fm[k] * 1024 * f_scale),
+                  "write_bytes": round(wm.get(k, 0.0) * 1024 * w_scale),
+                  "dispatches": fn[k]}
+              for k in sorted(fm) if k not in (kern, COPY_KERNEL)}
+    rec = {"workload": w.name + ("_mxfp4" if mx else ""), "kernel": kern,
+           "source_hash": kernel_source_hash(),
            "fetch_bytes": round(fetch), "write_bytes": round(write),
            "traffic_bytes": round(fetch + write),
            "raw_fetch_kib": round(fm[kern], 1), "raw_write_kib": round(wm[kern], 1),
            "copy_fetch_kib": round(fm[COPY_KERNEL], 1), "copy_write_kib": round(wm[COPY_KERNEL], 1),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-           "dispatches": {"fetch": fn, "write": wn}}
-    with open(traffic_file(w), "w") as fh:
+           "dispatches": {"fetch": fn, "write": wn}, "other_kernels": others}
+    with open(traffic_file(w, mx), "w") as fh:
         fh.write(f"# HBM traffic per launch of {kern}, workload {w.name}\n")
         fh.write(f"# counters: {command}\n")
         fh.write(f"# scale = {CALIB_COPY_BYTES} B copied / counter reading of the copy kernel\n")
@@ -162,12 +193,12 @@ def write_traffic(w, fetch_csv: str, write_csv: str, command: str) -> dict:
     return rec
 
 
-def read_traffic(w):
+def read_traffic(w, mx: bool = False):
     """Bytes per launch from the committed counter file, or None when absent or
     taken from other kernel sources."""
     try:
         rec = {}
-        with open(traffic_file(w)) as fh:
+        with open(traffic_file(w, mx)) as fh:
             for ln in fh:
                 if ln.startswith("#") or ":" not in ln:
                     continue
@@ -289,7 +320,8 @@ def main(argv=None):
 
     if args.write_traffic:
         import synth
-        print(json.dumps(write_traffic(synth.WORKLOADS[args.workload], *args.write_traffic)))
+        print(json.dumps(write_traffic(synth.WORKLOADS[args.workload], *args.write_traffic,
+                                       mx=args.mxfp4)))
         return 0
 
     if args.gpus != 1:
@@ -621,6 +653,12 @@ def bench_mx(args, w, torch, kvq, synth):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / args.steps * 1e3
+    if args.profile_step:
+        print(json.dumps({"profile_step": w.name + "_mxfp4", "steps": args.steps,
+                          "us_per_step": round(us, 3)}), flush=True)
+        if args.calib_copy:
+            calib_copy(torch)
+        return 0
     n_win = w.S + w.R
     gqa = w.H_q // w.H_kv
     if gqa in (4, 8) and T % 128 == 0:   # the block-scaled matrix-core kernel
@@ -641,7 +679,8 @@ def bench_mx(args, w, torch, kvq, synth):
                    "D": D, "T": T, "R": w.R, "S": w.S, "block": 32, "n_chunks": n_chunks,
                    "cache_copies": n_copies, "step": "decode (kvq_mx_decode_attention)"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": read_traffic(w, mx=True),
                      "kernel": kern,
                      "algorithmic_bytes": alg, "kernel_avg_us": round(us, 3),
                      "frac_of_stream_read": round(gbps / sr["GBps"], 4)},

@@ -225,8 +225,9 @@ template <int GQA>
 __global__ __launch_bounds__(kThreads) void decode_mx_kernel(DecodeArgs a, kvq_mx_cache mc) {
   __shared__ Lds<GQA> s;
   const int tid = threadIdx.x;
-  const int part = blockIdx.x;
-  const int64_t head = blockIdx.y;
+  int part, head32;
+  xcd_part_head(part, head32);
+  const int64_t head = head32;
   const int64_t b = head / a.H_kv, hk = head % a.H_kv;
   for (int i = tid; i < GQA * kD; i += kThreads) {
     const int h = i / kD, d = i % kD;
@@ -259,8 +260,9 @@ template <int BITS, int VB, int G, int GQA>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   __shared__ Lds<GQA> s;
   const int tid = threadIdx.x;
-  const int part = blockIdx.x;
-  const int64_t head = blockIdx.y;
+  int part, head32;
+  xcd_part_head(part, head32);
+  const int64_t head = head32;
   const int64_t b = head / a.H_kv, hk = head % a.H_kv;
   for (int i = tid; i < GQA * kD; i += kThreads) {
     const int h = i / kD, d = i % kD;

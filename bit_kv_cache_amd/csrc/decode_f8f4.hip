@@ -654,8 +654,8 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, r = lane >> 4;
-  const int chunk = blockIdx.x;
-  const int head32 = blockIdx.y;                 // < 65536 (checked on the host)
+  int chunk, head32;                             // head32 < 65536 (checked on the host)
+  xcd_part_head(chunk, head32);
   const int64_t head = head32;
   const int b32 = head32 / a.H_kv, hk32 = head32 - b32 * a.H_kv;   // 32-bit division
   const int64_t b = b32, hk = hk32;

@@ -274,8 +274,9 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, kq = lane >> 4;   // operand lane coordinates
-  const int chunk = blockIdx.x;
-  const int64_t head = blockIdx.y;
+  int chunk, head32;
+  xcd_part_head(chunk, head32);
+  const int64_t head = head32;
   const int64_t b = head / a.H_kv, hk = head % a.H_kv;
   const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
 

@@ -143,6 +143,26 @@ constexpr int kStatusStalled = 0, kStatusBadPage = 1;
 __device__ __forceinline__ void status_add(int32_t* status, int which) {
   if (status) __hip_atomic_fetch_add(status + which, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The chip hands a launch's workgroups to its 8 XCDs round-robin by linear
+// id (x fastest), and each XCD has an L2 of its own.  The decode kernels
+// renumber their (part, head) grid so that the parts of a head run on one
+// XCD: the partial records a head's last block merges, and the cache lines
+// that several parts of a head write (the appended group), then meet in one
+// L2 rather than being merged in memory.  The renumbering is a bijection
+// when the block count is a multiple of 8; otherwise the plain one is used.
+__device__ __forceinline__ void xcd_part_head(int& part, int& head) {
+  const int parts = (int)gridDim.x, nblk = (int)(gridDim.x * gridDim.y);
+  if ((nblk & 7) == 0) {
+    const int lin = (int)(blockIdx.x + blockIdx.y * gridDim.x);
+    const int g = (lin & 7) * (nblk >> 3) + (lin >> 3);
+    head = g / parts;
+    part = g - head * parts;
+  } else {
+    part = (int)blockIdx.x;
+    head = (int)blockIdx.y;
+  }
+}
+
 // Parts the in-launch merge accepts (more take the merge kernel).
 constexpr int kFusedMergeParts = 8;
 
