@@ -33,13 +33,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSlices = 4;
 
-__device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float maxq) {
-  if (s == 0.0f) return 0u;
-  float y = (x - mn) / s;
-  y = fminf(fmaxf(y, 0.0f), maxq);
-  return (uint32_t)__builtin_rintf(y);
-}
-
 // |x| of an fp16 value in units of 2^-24, exactly: a subnormal's fraction,
 // or the significand (implicit bit set) shifted by the biased exponent - 1.
 // A group's sum (at most 128 values below 2^40 units) fits 64 bits exactly,
@@ -128,77 +121,124 @@ __device__ void quantize_keys_slice(const QuantArgs& a, int64_t head, int64_t gi
 }
 
 // Keys of one whole group with the Kitty boost (2-bit, n_boost > 0).
+//  * min / max (and the sum of |x|) per channel: a thread takes a channel
+//    pair over a quarter of the tokens;
+//  * rank of each channel by range (or by the sum of |x|, the mean's order),
+//    ties to the lower channel: two threads per channel, half the channels
+//    each; a channel is boosted when fewer than n_boost channels precede it;
+//  * boosted row of a channel = number of boosted channels below it (rows
+//    ascend with the channel index), from the two waves' ballots;
+//  * codes: thread (token t, word w) codes channels 16w..16w+15 of token t
+//    from two 16-byte reads (the statistics of its 16 channels sit in
+//    registers), writes the low two bits as the packed word and ORs the high
+//    two bits of boosted channels into the token's high-bits words in LDS.
 template <int G>
 __device__ void quantize_keys_kitty(const QuantArgs& a, int64_t head, int64_t gi) {
   constexpr int BITS = 2, FPI = 16, WPT = kD / FPI;
   constexpr uint32_t MASK = 3u;
-  __shared__ uint16_t tile[G * kD];
-  __shared__ float s_mn[kD], s_sc[kD], s_mq[kD], s_rng[kD];
-  __shared__ int s_flag[kD], s_chan_of_row[kD];
-  __shared__ uint32_t s_red[2][kD];
-  __shared__ uint64_t s_mag[kD];   // sum of |x| over the group (units of 2^-24)
+  __shared__ alignas(16) uint16_t tile[G * kD];
+  __shared__ float s_mn[kD], s_sc[kD], s_rs[kD], s_mq[kD];
+  __shared__ alignas(16) float s_rng[kD];
+  __shared__ int s_row[kD], s_rank[2][kD];
+  __shared__ uint32_t s_lo4[4][kD], s_hi4[4][kD];
+  __shared__ alignas(16) uint64_t s_mag4[4][kD];   // sum of |x| per token quarter (units of 2^-24)
+  __shared__ alignas(16) uint64_t s_mag[kD];
+  __shared__ uint64_t s_ballot[2];
+  __shared__ uint32_t s_hi[G * (kD / 16)];     // high-bits words [token][n_boost / 16]
   const int tid = threadIdx.x;
   const int64_t gb = group_block(a.c, head, a.first_group + gi, G);
   if (gb < 0) return;
-  const int nb = a.n_boost;
+  const int nb = a.n_boost, hpt = nb / 16;
   const uint16_t* src = a.k_src + head * a.src_head_stride + gi * G * kD;
   {
     const uint4* s4 = reinterpret_cast<const uint4*>(src);
     uint4* t4 = reinterpret_cast<uint4*>(tile);
     for (int i = tid; i < G * kD / 8; i += kThreads) t4[i] = s4[i];
+    for (int i = tid; i < G * hpt; i += kThreads) s_hi[i] = 0u;
   }
   __syncthreads();
   const int d = tid & (kD - 1), half = tid >> 7;
   const bool by_mag = a.boost_score != 0;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  uint64_t mag = 0;
-  for (int j = half * (G / 2); j < (half + 1) * (G / 2); ++j) {
-    const uint16_t x = tile[j * kD + d];
-    const uint32_t k = order_key(x);
-    lo = min(lo, k);
-    hi = max(hi, k);
-    if (by_mag) mag += mag_units(x);
-  }
-  if (half) {
-    s_red[0][d] = lo;
-    s_red[1][d] = hi;
-    s_mag[d] = mag;
+  {
+    // channels 2 cp, 2 cp + 1 over tokens [32 qt, 32 qt + 32)
+    const int cp = tid & 63, qt = tid >> 6;
+    const uint32_t* t32 = reinterpret_cast<const uint32_t*>(tile);
+    uint32_t lo0 = 0xFFFFFFFFu, hi0 = 0u, lo1 = 0xFFFFFFFFu, hi1 = 0u;
+    uint64_t mag0 = 0, mag1 = 0;
+    for (int j = qt * (G / 4); j < (qt + 1) * (G / 4); ++j) {
+      const uint32_t x = t32[j * (kD / 2) + cp];
+      const uint16_t x0 = (uint16_t)(x & 0xFFFFu), x1 = (uint16_t)(x >> 16);
+      lo0 = min(lo0, order_key(x0));
+      hi0 = max(hi0, order_key(x0));
+      lo1 = min(lo1, order_key(x1));
+      hi1 = max(hi1, order_key(x1));
+      if (by_mag) {
+        mag0 += mag_units(x0);
+        mag1 += mag_units(x1);
+      }
+    }
+    s_lo4[qt][2 * cp] = lo0;
+    s_hi4[qt][2 * cp] = hi0;
+    s_lo4[qt][2 * cp + 1] = lo1;
+    s_hi4[qt][2 * cp + 1] = hi1;
+    s_mag4[qt][2 * cp] = mag0;
+    s_mag4[qt][2 * cp + 1] = mag1;
   }
   __syncthreads();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
   if (!half) {
-    lo = min(lo, s_red[0][d]);
-    hi = max(hi, s_red[1][d]);
-    s_mag[d] += mag;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lo = min(lo, s_lo4[q][d]);
+      hi = max(hi, s_hi4[q][d]);
+    }
+    s_mag[d] = (s_mag4[0][d] + s_mag4[1][d]) + (s_mag4[2][d] + s_mag4[3][d]);
     const float mn = h2f(from_order_key(lo));
     s_mn[d] = mn;
     s_rng[d] = h2f(from_order_key(hi)) - mn;
   }
   __syncthreads();
-  if (!half) {
-    // rank by range (or by the sum of |x|, the mean's order), ties to the
-    // lower channel
-    int rank = 0;
+  {
+    // channels of this thread's half that rank before channel d
+    int cnt = 0;
+    const int c0 = half * (kD / 2);
     if (by_mag) {
       const uint64_t v = s_mag[d];
-      for (int c = 0; c < kD; ++c) {
-        const uint64_t vc = s_mag[c];
-        rank += (vc > v) || (vc == v && c < d);
+      const ulonglong2* m2 = reinterpret_cast<const ulonglong2*>(s_mag + c0);
+      for (int c = 0; c < kD / 4; ++c) {
+        const ulonglong2 vc = m2[c];
+        const int ca = c0 + 2 * c;
+        cnt += (vc.x > v) || (vc.x == v && ca < d);
+        cnt += (vc.y > v) || (vc.y == v && ca + 1 < d);
       }
     } else {
       const float r = s_rng[d];
-      for (int c = 0; c < kD; ++c) {
-        const float rc = s_rng[c];
-        rank += (rc > r) || (rc == r && c < d);
+      const float4* r4 = reinterpret_cast<const float4*>(s_rng + c0);
+      for (int c = 0; c < kD / 8; ++c) {
+        const float4 rc = r4[c];
+        const int ca = c0 + 4 * c;
+        cnt += (rc.x > r) || (rc.x == r && ca < d);
+        cnt += (rc.y > r) || (rc.y == r && ca + 1 < d);
+        cnt += (rc.z > r) || (rc.z == r && ca + 2 < d);
+        cnt += (rc.w > r) || (rc.w == r && ca + 3 < d);
       }
     }
-    s_flag[d] = rank < nb;
+    s_rank[half][d] = cnt;
+  }
+  __syncthreads();
+  bool boosted = false;
+  if (!half) {
+    boosted = s_rank[0][d] + s_rank[1][d] < nb;
+    const uint64_t m = __ballot(boosted);   // waves 0 and 1: channels 0..63, 64..127
+    if ((tid & 63) == 0) s_ballot[tid >> 6] = m;
   }
   __syncthreads();
   if (!half) {
     int row = nb;  // sentinel: not boosted
-    if (s_flag[d]) {
-      row = 0;  // boosted rows ascend with the channel index
-      for (int c = 0; c < d; ++c) row += s_flag[c];
+    if (boosted) {
+      const int bit = d & 63;
+      const uint64_t below = bit ? (s_ballot[d >> 6] & ((1ull << bit) - 1ull)) : 0ull;
+      row = __popcll(below) + (d >= 64 ? __popcll(s_ballot[0]) : 0);
     }
     const float maxq = (row < nb) ? 15.0f : (float)MASK;
     const uint16_t sh = f2h(s_rng[d] / maxq);
@@ -207,35 +247,44 @@ __device__ void quantize_keys_kitty(const QuantArgs& a, int64_t head, int64_t gi
     a.c.k_min[m_off] = from_order_key(lo);
     a.c.k_bidx[m_off] = (uint8_t)row;
     s_sc[d] = h2f(sh);
+    s_rs[d] = 1.0f / h2f(sh);
     s_mq[d] = maxq;
-    if (row < nb) s_chan_of_row[row] = d;
+    s_row[d] = row;
   }
   __syncthreads();
+  // every thread codes the same 16 channels (kThreads is a multiple of WPT)
+  const int w = tid % WPT;
+  float mn[FPI], sc[FPI], rs[FPI], mq[FPI];
+  int rw[FPI];
+#pragma unroll
+  for (int j = 0; j < FPI; ++j) {
+    const int c = w * FPI + j;
+    mn[j] = s_mn[c];
+    sc[j] = s_sc[c];
+    rs[j] = s_rs[c];
+    mq[j] = s_mq[c];
+    rw[j] = s_row[c];
+  }
   uint32_t* kw = a.c.k_codes + gb * G * WPT;
   for (int i = tid; i < G * WPT; i += kThreads) {
-    const int t = i / WPT, w = i % WPT;
+    const int t = i / WPT;
+    const uint4* x4 = reinterpret_cast<const uint4*>(tile + t * kD + w * FPI);
+    const uint4 x0 = x4[0], x1 = x4[1];
+    const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     uint32_t word = 0u;
 #pragma unroll
     for (int j = 0; j < FPI; ++j) {
-      const int c = w * FPI + j;
-      const uint32_t q = quant_code(h2f(tile[t * kD + c]), s_mn[c], s_sc[c], s_mq[c]);
+      const uint16_t xh = (uint16_t)(xs[j >> 1] >> (16 * (j & 1)));
+      const uint32_t q = quant_code_rcp(h2f(xh), mn[j], sc[j], rs[j], mq[j]);
       word |= (q & MASK) << (BITS * j);
+      if (rw[j] < nb)
+        atomicOr(&s_hi[t * hpt + (rw[j] >> 4)], (q >> 2) << (2 * (rw[j] & 15)));
     }
     kw[i] = word;
   }
-  // high two bits of the boosted rows, 16 rows per word
-  const int hpt = nb / 16;
+  __syncthreads();
   uint32_t* hw = a.c.k_hi + gb * G * hpt;
-  for (int i = tid; i < G * hpt; i += kThreads) {
-    const int t = i / hpt, w = i % hpt;
-    uint32_t word = 0u;
-    for (int j = 0; j < 16; ++j) {
-      const int c = s_chan_of_row[w * 16 + j];
-      const uint32_t q = quant_code(h2f(tile[t * kD + c]), s_mn[c], s_sc[c], 15.0f);
-      word |= (q >> 2) << (2 * j);
-    }
-    hw[i] = word;
-  }
+  for (int i = tid; i < G * hpt; i += kThreads) hw[i] = s_hi[i];
 }
 
 // Value slices per group: whole packed words (FPI tokens) per slice.
