@@ -91,6 +91,19 @@ def split_kernel(w) -> str:
     return "decode_valu_kernel"
 
 
+def compute_dtype(w) -> str:
+    """The arithmetic the step's kernel computes in (not a precision claim)."""
+    kern = split_kernel(w)
+    if kern == "decode_f8f4_kernel":
+        return (f"u{w.bits} codes as the fp4 operand; dequantized query / probabilities as "
+                "4 fp8 digits (about 16 bits); fp16 windows on f16 matrix cores; fp32 "
+                "accumulate and softmax")
+    if kern == "decode_mfma_kernel":
+        return (f"u{w.bits} codes as subnormal fp16 operands; query / probabilities as fp16 "
+                "hi+lo (about 22 bits); fp32 accumulate and softmax")
+    return f"u{w.bits} codes, fp32 vector-ALU math"
+
+
 def fused_step(w, n_chunks: int) -> bool:
     """Whether the library runs a step with append as one launch (its dispatch
     rule: the 2-bit matrix-core kernel, plain codes, 4..8 chunks per head)."""
@@ -225,6 +238,16 @@ def _host_info():
                 model = ln.split(":", 1)[1].strip()
     except Exception:
         pass
+    try:   # the kernel's own name for the part, when lscpu's is generic
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    name = ln.split(":", 1)[1].strip()
+                    if len(name) > len(model):
+                        model = name
+                    break
+    except OSError:
+        pass
     return min(cores, aff), model
 
 
@@ -249,50 +272,72 @@ def build_caches(w, n_copies, kvq, synth, torch):
     return cfg, copies
 
 
-def cpu_baseline(w, max_heads, threads, min_seconds=10.0):
-    """Time the oracle (as it stands) on a bounded sample of heads: decode steps
-    plus the append-group quantize of those heads, repeated until at least
-    ``min_seconds`` of wall time; scale the mean step to the whole workload."""
+def cpu_baseline(w, max_heads, threads, one_thread_heads=4, reps=3):
+    """Time the oracle (as it stands) on bounded samples of the workload, each
+    figure the median of ``reps`` runs scaled to all kv heads:
+      * one decode step (attention over the whole cache and windows, plus the
+        quantize of the appended group) on all ``threads`` host threads over
+        up to ``max_heads`` kv heads, and on one thread over
+        ``one_thread_heads`` kv heads;
+      * quantize-all (the whole T-token cache) on the same two samples.
+    The headline ``value`` is the all-threads step."""
     import numpy as np
     import oracle
     import synth
 
-    heads = list(range(min(max_heads, w.heads)))
-    heads = heads[: (len(heads) // w.H_kv) * w.H_kv] or heads[:1]
-    B = max(1, len(heads) // w.H_kv)
-    H_kv = min(w.H_kv, len(heads))
-    oc = oracle.empty_cache(w.bits, w.G, w.D, w.n_boost, w.T + w.G, len(heads))
-    ks, vs, kr, vr, kS, vS = [], [], [], [], [], []
-    for h in heads:
-        k, v = synth.head_kv(w, h, "cpu")
-        a, b, c, d = synth.head_windows(w, h, "cpu")
-        ks.append(synth.as_bits(k)), vs.append(synth.as_bits(v))
-        kS.append(synth.as_bits(a)), vS.append(synth.as_bits(b))
-        kr.append(synth.as_bits(c)), vr.append(synth.as_bits(d))
-    k_src, v_src = np.stack(ks), np.stack(vs)
-    del ks, vs
-    oracle.quantize_pack(oc, k_src, v_src, 0, w.T // w.G, n_threads=threads)
-    del k_src, v_src
-    q = synth.as_bits(synth.query(w, "cpu"))[:B, : H_kv * w.gqa]
-    kS, vS, kr, vr = (np.stack(x) for x in (kS, vS, kr, vr))
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.decode_attention(oc, B, H_kv * w.gqa, H_kv, q, w.T, k_sink=kS if w.S else None,
-                                v_sink=vS if w.S else None, n_sink=w.S, k_res=kr, v_res=vr,
-                                n_res=w.R, n_threads=threads)
-        if w.R >= w.G:
-            oracle.quantize_pack(oc, kr, vr, w.T // w.G, 1, n_threads=threads)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    scale = w.heads / len(heads)
-    return {"value": round(dt / reps * scale * 1e6, 1), "unit": "us/step", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{len(heads)} of {w.heads} kv heads (all their query heads); {reps} "
-                      f"repetitions of one decode step + append quantize in {dt:.1f} s wall "
-                      f"on {threads} threads; mean step scaled x{scale:g}"}
+    def sample(n_heads):
+        heads = list(range(min(n_heads, w.heads)))
+        if len(heads) >= w.H_kv:
+            heads = heads[: (len(heads) // w.H_kv) * w.H_kv]
+        B = max(1, len(heads) // w.H_kv)
+        H_kv = min(w.H_kv, len(heads))
+        ks, vs, kr, vr, kS, vS = [], [], [], [], [], []
+        for h in heads:
+            k, v = synth.head_kv(w, h, "cpu")
+            a, b, c, d = synth.head_windows(w, h, "cpu")
+            ks.append(synth.as_bits(k)), vs.append(synth.as_bits(v))
+            kS.append(synth.as_bits(a)), vS.append(synth.as_bits(b))
+            kr.append(synth.as_bits(c)), vr.append(synth.as_bits(d))
+        q = synth.as_bits(synth.query(w, "cpu"))[:B, : H_kv * w.gqa]
+        return (heads, B, H_kv, np.stack(ks), np.stack(vs), q,
+                *(np.stack(x) for x in (kS, vS, kr, vr)))
+
+    def run(n_heads, n_threads):
+        heads, B, H_kv, k_src, v_src, q, kS, vS, kr, vr = sample(n_heads)
+        oc = oracle.empty_cache(w.bits, w.G, w.D, w.n_boost, w.T + w.G, len(heads))
+        quant, step = [], []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.quantize_pack(oc, k_src, v_src, 0, w.T // w.G, n_threads=n_threads)
+            quant.append(time.perf_counter() - t0)
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.decode_attention(oc, B, H_kv * w.gqa, H_kv, q, w.T,
+                                    k_sink=kS if w.S else None, v_sink=vS if w.S else None,
+                                    n_sink=w.S, k_res=kr, v_res=vr, n_res=w.R,
+                                    n_threads=n_threads)
+            if w.R >= w.G:
+                oracle.quantize_pack(oc, kr, vr, w.T // w.G, 1, n_threads=n_threads)
+            step.append(time.perf_counter() - t0)
+        scale = w.heads / len(heads)
+        us = lambda xs: sorted(round(x * scale * 1e6, 1) for x in xs)
+        return len(heads), us(step), us(quant)
+
+    n_all, step_all, quant_all = run(max_heads, threads)
+    n_one, step_one, quant_one = run(one_thread_heads, 1)
+    med = lambda xs: xs[len(xs) // 2]
+    return {"value": med(step_all), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"one decode step (attention + append quantize) over {n_all} of {w.heads} "
+                      f"kv heads on {threads} threads, median of {reps}, scaled x"
+                      f"{w.heads / n_all:g}",
+            "one_thread": {"value": med(step_one), "unit": "us/step", "cores": 1,
+                           "runs": step_one,
+                           "sample": f"{n_one} of {w.heads} kv heads, median of {reps}, scaled "
+                                     f"x{w.heads / n_one:g}"},
+            "all_threads_runs": step_all,
+            "quantize_all": {"unit": "us per whole-cache quantize (T tokens, all kv heads)",
+                             "all_threads": med(quant_all), "all_threads_runs": quant_all,
+                             "one_thread": med(quant_one), "one_thread_runs": quant_one}}
 
 
 def main(argv=None):
@@ -306,7 +351,6 @@ def main(argv=None):
     ap.add_argument("--n-chunks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=1 << 20, help="kv heads the oracle runs")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the run, stream 1 GiB in and 1 GiB out 5 times (counter scale)")
     ap.add_argument("--profile-step", action="store_true",
@@ -522,7 +566,7 @@ def main(argv=None):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"u{w.bits} codes, fp32 math",
+        "dtype": compute_dtype(w),
         "data": "synthetic (seeded; K outlier channels, see synth/)",
         "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "D": w.D,
                    "T": w.T, "R": w.R, "S": w.S, "bits": w.bits, "G": w.G,
@@ -563,7 +607,7 @@ def main(argv=None):
     result["roofline"]["frac_of_stream_read"] = round(achieved / sr["GBps"], 4)
     if not args.no_cpu_baseline:
         cores, model = _host_info()
-        cb = cpu_baseline(w, args.cpu_heads, cores, args.cpu_seconds)
+        cb = cpu_baseline(w, args.cpu_heads, cores)
         cb["cpu_model"] = model
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
@@ -673,7 +717,12 @@ def bench_mx(args, w, torch, kvq, synth):
         "metric": f"decode-attn us/step ({w.name} shape, MXFP4 cache)", "value": round(us, 3),
         "unit": "us/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(us / 1e3, 5), "higher_is_better": False, "scaling": "weak",
-        "vs_baseline": None, "dtype": "e2m1 codes + e8m0 block scales, fp32 math",
+        "vs_baseline": None,
+        "dtype": ("e2m1 codes with e8m0 block scales as the fp4 operand; query and "
+                  "probabilities as 4 fp8 digits (about 16 bits); fp16 windows on f16 "
+                  "matrix cores; fp32 accumulate and softmax"
+                  if gqa in (4, 8) and T % 128 == 0 else
+                  "e2m1 codes with e8m0 block scales, fp32 vector-ALU math"),
         "data": "synthetic (seeded; the workload's generator)",
         "config": {"workload": f"{w.name}_mxfp4", "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
                    "D": D, "T": T, "R": w.R, "S": w.S, "block": 32, "n_chunks": n_chunks,

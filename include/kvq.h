@@ -194,10 +194,16 @@ kvq_status kvq_decode_plan(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t 
 size_t kvq_decode_workspace_bytes(const kvq_qcfg* cfg, int32_t B, int32_t H_q, int32_t H_kv,
                                   int64_t n_quant_tokens, int32_t n_chunks_req);
 
-/* One decode step: for batch b and query head h (kv head h / (H_q/H_kv)),
+/* One decode step (BitDecoding page, section II: single-query attention over
+ * a low-bit cache; KIVI page, Step 4: the quantized keys and values read as
+ * code*scale + min; Kitty page, section 4.2, Algorithm 1 for boosted key
+ * channels; KIVI page, Step 3 and Kitty page, section 3.1 for the fp16
+ * windows): for batch b and query head h (kv head h / (H_q/H_kv)),
  *   out[b][h] = softmax(sm * q[b][h] . K^T) V
  * over the sink window, the first n_quant_tokens cached tokens and the
- * residual window (which holds the current token).
+ * residual window (which holds the current token).  Split-K over token
+ * chunks, the chunks combined by the log-sum-exp identity (the merge of
+ * kvq_decode_merge).
  *  q: fp16 [B][H_q][D].  out: fp32 [B][H_q][D].
  *  n_quant_tokens: multiple of G, 0 <= n_quant_tokens <= t_cap.
  *  sink, res: may be NULL (no tokens).
@@ -276,7 +282,9 @@ kvq_status kvq_decode_step_noalloc(const kvq_qcfg* cfg, const kvq_cache* cache, 
  *
  * kvq_decode_merge: out[b][h] = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
  * over the parts with l_p > 0 (M the largest such m_p); 0 when every part is
- * empty.  Reads workspace laid out as above with 1 <= n_parts <= 1024 and
+ * empty.  This is the log-sum-exp identity: the softmax over the union of the
+ * parts' tokens (BitDecoding page, section II, normalizes over the whole
+ * sequence) rebuilt from each part's max, sum and weighted value sum.  Reads workspace laid out as above with 1 <= n_parts <= 1024 and
  * ws_bytes >= KVQ_WS_COUNTER_BYTES + B*H_q*n_parts*(D+2)*4.  Neither call
  * touches the counter bytes. */
 kvq_status kvq_decode_partials(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
@@ -363,11 +371,20 @@ kvq_status kvq_mx_dequantize(const kvq_mx_cache* cache, int32_t B, int32_t H_kv,
 /* Decode attention over an MXFP4 cache: the same result as
  * kvq_decode_attention (sink | tokens [0, n_quant_tokens) | residual, fp32
  * output), the quantized keys and values read as E2M1 value * 2^E.
- * n_quant_tokens a multiple of 32 (0 allowed).  Split-K over chunks of
- * 32-token blocks on the vector ALU, then the log-sum-exp merge.
- * kvq_mx_decode_plan gives the chunk count (n_chunks_req = 0: automatic) and
- * the workspace size (arrival counters, then B*H_q*(n_chunks+1)*(D+2) fp32
- * partials); errors as kvq_decode_attention. */
+ * n_quant_tokens a multiple of 32 (0 allowed).  With GQA 4 or 8 and
+ * n_quant_tokens a multiple of 128 the split-K kernel runs both products on
+ * the block-scaled matrix cores (the E2M1 codes as the B operand and the E8M0
+ * bytes as its block scales, the query and probabilities as fp8 digit rows),
+ * one part per chunk, the fp16 windows shared among the chunks, merged in the
+ * same launch when there are at most 8 chunks (as kvq_decode_attention);
+ * otherwise the vector-ALU kernel runs over chunks of 32-token blocks plus a
+ * window part, followed by the merge launch.  kvq_mx_decode_plan gives the
+ * chunk count (n_chunks_req = 0: automatic; n_chunks_req > 0 is honoured up
+ * to one chunk per 128-token group on the matrix-core path, at most 1023,
+ * and one per 32-token block on the vector-ALU path) and the workspace size
+ * (the counter bytes, then B*H_q*parts*(D+2) fp32 partials, parts = chunks
+ * on the matrix-core path and chunks + 1 otherwise); errors as
+ * kvq_decode_attention. */
 kvq_status kvq_mx_decode_plan(int32_t B, int32_t H_q, int32_t H_kv, int64_t n_quant_tokens,
                               int32_t n_chunks_req, int32_t* n_chunks, size_t* ws_bytes);
 kvq_status kvq_mx_decode_attention(const kvq_mx_cache* cache, int32_t B, int32_t H_q,

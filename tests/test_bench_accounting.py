@@ -41,3 +41,27 @@ def test_decode_bytes_of_workloads():
     assert bench.decode_bytes(W["long_t1m_2bit_splitk"]) == 604_528_640
     assert bench.decode_bytes(W["llama3_8b_t8k_b32_4bit"]) == 302_776_320
     assert bench.decode_bytes(W["kitty_t128k_h64_boost16"]) == 1_303_117_824
+
+
+def test_counter_csv_parse_and_copy_scale(tmp_path):
+    # the counter files rocprofv3 writes name kernels with their namespaces,
+    # template arguments and parameter lists; the copy kernel's reading gives
+    # the scale (a 1 GiB pass read 2x too low by FETCH_SIZE on this chip)
+    hdr = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+    rows = [
+        (1, "void kvq::(anonymous namespace)::decode_f8f4_kernel<4, false, false>(kvq::DecodeArgs)", 100.0),
+        (2, "void kvq::(anonymous namespace)::decode_f8f4_kernel<4, false, false>(kvq::DecodeArgs)", 110.0),
+        (3, "kvq::(anonymous namespace)::merge_kernel(kvq::DecodeArgs)", 4.0),
+        (4, "void at::native::vectorized_elementwise_kernel<4, at::native::bitwise_not_kernel_cuda"
+            "(at::TensorIteratorBase&)::{lambda(int)#1}, std::array<char*, 2ul> >(int, x)",
+         bench.CALIB_COPY_BYTES / 1024 / 2),
+        (5, "void at::native::unrelated_kernel<float>(float*)", 7.0),
+    ]
+    f = tmp_path / "fetch.csv"
+    f.write_text(hdr + "".join(f'{i},"{n}",FETCH_SIZE,{v}\n' for i, n, v in rows))
+    means, counts = bench._counter_means(str(f), "FETCH_SIZE")
+    assert counts["decode_f8f4_kernel<4, false, false>"] == 2
+    assert means["decode_f8f4_kernel<4, false, false>"] == 105.0
+    assert means["merge_kernel"] == 4.0
+    assert bench.COPY_KERNEL in means and "unrelated_kernel<float>" not in means
+    assert bench.CALIB_COPY_BYTES / (means[bench.COPY_KERNEL] * 1024) == 2.0
