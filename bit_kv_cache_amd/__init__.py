@@ -17,7 +17,9 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+# KVQ_LIB names another build of the same sources (the sanitizer test's
+# host-instrumented one); there is no other implementation to fall back on
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

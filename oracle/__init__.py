@@ -30,6 +30,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.cpp")
 _LIB_PATH = os.path.join(_HERE, "liboracle_kvq.so")
+# another build of the same source (the sanitizer test's ASan/UBSan build)
+_LOAD_PATH = os.environ.get("KVQ_ORACLE_LIB") or _LIB_PATH
 _lib = None
 
 BUILD_CMD = [
@@ -48,9 +50,9 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    if _LOAD_PATH == _LIB_PATH and not os.path.exists(_LIB_PATH):
         build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(_LOAD_PATH)
     P = ctypes.c_void_p
     i32, i64, u16, f32, f64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint16,
                                ctypes.c_float, ctypes.c_double)
