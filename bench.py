@@ -104,20 +104,27 @@ def compute_dtype(w) -> str:
     return f"u{w.bits} codes, fp32 vector-ALU math"
 
 
+def split_append(w, n_chunks: int) -> bool:
+    """Whether the split-K launch also quantizes the appended group (the
+    library's dispatch rule: the 2-bit matrix-core kernel, plain codes, at
+    least 4 chunks)."""
+    return split_kernel(w) == "decode_f8f4_kernel" and w.n_boost == 0 and n_chunks >= 4
+
+
 def fused_step(w, n_chunks: int) -> bool:
-    """Whether the library runs a step with append as one launch (its dispatch
-    rule: the 2-bit matrix-core kernel, plain codes, 4..8 chunks per head)."""
-    return split_kernel(w) == "decode_f8f4_kernel" and w.n_boost == 0 and 4 <= n_chunks <= 8
+    """Whether the library runs a step with append as one launch (split-K with
+    the append, and the merge in the same launch: at most 8 parts)."""
+    return split_append(w, n_chunks) and n_chunks <= 8
 
 
 def launches_per_step(w, n_chunks: int, append: bool) -> int:
     """Kernel launches of one kvq_decode_step call (the library's dispatch)."""
     mfma = split_kernel(w) != "decode_valu_kernel"
     n_parts = n_chunks if mfma else n_chunks + 1
-    in_launch_merge = split_kernel(w) == "decode_f8f4_kernel" and n_parts <= 8
+    in_launch_merge = mfma and n_parts <= 8
     if append:
-        if fused_step(w, n_chunks):
-            return 1
+        if split_append(w, n_chunks):
+            return 1 if in_launch_merge else 2
         return 2 if n_parts <= 32 else 3
     return 1 if in_launch_merge else 2
 

@@ -51,6 +51,7 @@
 // waves merge in LDS and the block writes its partial (m, l, acc).
 
 #include "kvq_internal.h"
+#include "append_common.h"
 #include "merge_common.h"
 #include "quant_common.h"
 
@@ -424,197 +425,15 @@ __device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
 
 // ------------------------------------------------------------------ fused append
 //
-// With DecodeArgs::append the block also quantizes its share of the group
-// that has filled the residual window (rows 0..127 of the head's residual
-// buffer) into cache group n_groups: slice s = chunk of four (key channels
-// [32 s, 32 s + 32), value tokens [32 s, 32 s + 32)), with the arithmetic of
-// the quantize kernel (KIVI page, Steps 1-2): min and max by the total order
-// -0 < +0, scale fp16((max - min)/3), codes by quant_code_rcp.  The slice is
-// four self-contained items (16 key channels, or 16 value tokens, each with
-// its own statistics and whole packed words), item k taken by consumer wave
-// k + 1 right after the block barrier, while the first groups are still on
-// their way (a fixed assignment rather than a claim loop: the loop kept the
-// items' registers live across the group loop).  The appended group lies
-// past every group the launch reads.
-constexpr int kAppWpt = kD / 16;   // 2-bit key words per token
-constexpr int kAppItems = 4;       // items per slice
-
-// min / max (as order keys) of the fp16 value e of a u32x4 of 8 halves
-__device__ __forceinline__ uint32_t half_key(const u32x4& v, int e) {
-  return order_key((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
-}
-__device__ __forceinline__ uint16_t half_of(const u32x4& v, int e) {
-  return (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-}
-
-// Item k of slice s.  k < 2: key channels c0 = 32 s + 16 k .. c0 + 15 over
-// the 128 tokens, one packed word per token (lane: tokens lane / 2 + 32 i,
-// channels c0 + 8 (lane % 2) ..); k >= 2: value tokens t0 = 32 s + 16 (k - 2)
-// .. t0 + 15 over the 128 channels, one packed word per channel (lane: tokens
-// t0 + lane / 16 + 4 i, channels 8 (lane % 16) ..).
-__device__ __forceinline__ void append_item_load(const DecodeArgs& a, int64_t head, int s, int k,
-                                                 int lane, u32x4 (&x)[4]) {
-  if (k < 2) {
-    const uint16_t* src = a.k_res + head * a.res_cap * kD + 32 * s + 16 * k + 8 * (lane & 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[i] = *reinterpret_cast<const u32x4*>(src + ((lane >> 1) + 32 * i) * kD);
-  } else {
-    const uint16_t* src =
-        a.v_res + (head * a.res_cap + 32 * s + 16 * (k - 2) + (lane >> 4)) * kD + 8 * (lane & 15);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const u32x4*>(src + 4 * i * kD);
-  }
-}
-
-__device__ __forceinline__ void append_item(const DecodeArgs& a, int64_t head, int s, int k,
-                                            int lane, const u32x4 (&x)[4]) {
-  const int64_t blk = group_block(a.c, head, a.n_groups, kG);   // the appended group's block
-  if (blk < 0) return;   // a page outside the pool: nothing is written
-  if (k < 2) {
-    const int c0 = 32 * s + 16 * k, q = lane & 1;
-    // per channel over the 128 tokens: the lane's 4, then the 32 lanes with
-    // the same q
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo[e] = half_key(x[0], e);
-      hi[e] = lo[e];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        lo[e] = min(lo[e], half_key(x[i], e));
-        hi[e] = max(hi[e], half_key(x[i], e));
-      }
-    }
-#pragma unroll
-    for (int o = 2; o < 64; o <<= 1)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        lo[e] = min(lo[e], (uint32_t)__shfl_xor((int)lo[e], o));
-        hi[e] = max(hi[e], (uint32_t)__shfl_xor((int)hi[e], o));
-      }
-    float mn[8], sc[8], rs[8];
-    uint32_t shw[4], mnw[4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t l16 = from_order_key(lo[e]);
-      const uint16_t sh = group_scale(h2f(l16), h2f(from_order_key(hi[e])), 3.0f);
-      mn[e] = h2f(l16);
-      sc[e] = h2f(sh);
-      rs[e] = 1.0f / sc[e];
-      if (e & 1) {
-        shw[e >> 1] |= (uint32_t)sh << 16;
-        mnw[e >> 1] |= (uint32_t)l16 << 16;
-      } else {
-        shw[e >> 1] = sh;
-        mnw[e >> 1] = l16;
-      }
-    }
-    if (lane < 2) {
-      const int64_t m_off = blk * kD + c0 + 8 * q;
-      *reinterpret_cast<u32x4*>(a.c.k_scale + m_off) = u32x4{shw[0], shw[1], shw[2], shw[3]};
-      *reinterpret_cast<u32x4*>(a.c.k_min + m_off) = u32x4{mnw[0], mnw[1], mnw[2], mnw[3]};
-    }
-    // codes: channels c0 + 8 q + e at bits 2 (8 q + e) of the token's word
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t part = 0u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        part |= quant_code_rcp(h2f(half_of(x[i], e)), mn[e], sc[e], rs[e], 3.0f)
-                << (2 * (8 * q + e));
-      const uint32_t word = part | (uint32_t)__shfl_xor((int)part, 1);
-      if (q == 0) {
-        const int t = (lane >> 1) + 32 * i;
-        a.c.k_codes[(blk * kG + t) * kAppWpt + 2 * s + k] = word;
-      }
-    }
-  } else {
-    const int t0 = 32 * s + 16 * (k - 2), r = lane >> 4, q = lane & 15;
-    // per token over the 128 channels: the lane's 8, then the 16 lanes with
-    // the same r
-    uint32_t lo[4], hi[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo[i] = half_key(x[i], 0);
-      hi[i] = lo[i];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) {
-        lo[i] = min(lo[i], half_key(x[i], e));
-        hi[i] = max(hi[i], half_key(x[i], e));
-      }
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = min(lo[i], (uint32_t)__shfl_xor((int)lo[i], o));
-        hi[i] = max(hi[i], (uint32_t)__shfl_xor((int)hi[i], o));
-      }
-    float mn[4], sc[4], rs[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t l16 = from_order_key(lo[i]);
-      const uint16_t sh = group_scale(h2f(l16), h2f(from_order_key(hi[i])), 3.0f);
-      mn[i] = h2f(l16);
-      sc[i] = h2f(sh);
-      rs[i] = 1.0f / sc[i];
-      if (q == 0) {
-        const int64_t m_off = blk * kG + t0 + r + 4 * i;
-        a.c.v_scale[m_off] = sh;
-        a.c.v_min[m_off] = l16;
-      }
-    }
-    // codes: token t0 + r + 4 i at bits 2 (r + 4 i) of the channel's word
-    uint32_t wd[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t part = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        part |= quant_code_rcp(h2f(half_of(x[i], e)), mn[i], sc[i], rs[i], 3.0f)
-                << (2 * (r + 4 * i));
-      part |= (uint32_t)__shfl_xor((int)part, 16);
-      wd[e] = part | (uint32_t)__shfl_xor((int)part, 32);
-    }
-    if (r == 0) {
-      uint32_t* dst = a.c.v_codes + (blk * (kG / 16) + t0 / 16) * kD + 8 * q;
-      *reinterpret_cast<u32x4*>(dst) = u32x4{wd[0], wd[1], wd[2], wd[3]};
-      *reinterpret_cast<u32x4*>(dst + 4) = u32x4{wd[4], wd[5], wd[6], wd[7]};
-    }
-  }
-}
-
-// ------------------------------------------------------------------ in-launch merge
-
-// After a block has written its partial records (device-scope stores): its
-// arrival on the head's counter, and, in the last block of the head to
-// arrive, the log-sum-exp merge of the head's query rows into the output.
-// No block waits for another, so the order in which blocks run is free.  The
-// last block resets the counter, leaving it zero for the next call.
-template <int GQA>
-__device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int64_t b, int64_t hk,
-                                                int head32, int& last_flag) {
-  // this thread's stores have completed (they are visible device-wide)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(a.counters + head32, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == a.n_chunks - 1;
-    if (last) __hip_atomic_store(a.counters + head32, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = last;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  const int np = a.n_parts;
-  for (int i = threadIdx.x; i < GQA * kD; i += blockDim.x) {
-    const int64_t bh = b * a.H_q + hk * GQA + i / kD;
-    const int d = i % kD;
-    if (np <= 4) merge_row<4, true>(a.ws, np, a.out, bh, d);
-    else merge_row<8, true>(a.ws, np, a.out, bh, d);
-  }
-}
+// With DecodeArgs::append the blocks of a head also quantize the group that
+// has filled the residual window (append_common.h): its 16 items go to
+// consumer waves 1..kItemWaves of the head's blocks (slot = chunk *
+// kItemWaves + wave - 1), taken right after the block barrier while the
+// first groups are on their way.  The step takes this path with 4 or more
+// chunks per head, so a slot has at most one item.  The items run before
+// the group loop, so their registers are dead by then (inside the loop they
+// made the GQA-8 kernel spill).
+constexpr int kItemWaves = 4;
 
 // ------------------------------------------------------------------ kernel
 
@@ -662,8 +481,8 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
   const int ngc = (int)max<int64_t>(0, min<int64_t>(seq_groups(a, b, kG), gb + a.groups_per_chunk) - gb);
-  // slice of the appended group this block quantizes (-1: none)
-  const int app_slice = (!KITTY && !MX && a.append && chunk < 4) ? chunk : -1;
+  // this block's waves take items of the appended group (2-bit min-max cache)
+  const bool app_on = !KITTY && !MX && a.append;
 
   // The loader wave sets up the ring's flags and meets the other waves at the
   // block barrier before its first copy; past it, the loader waits for
@@ -1195,12 +1014,9 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       }
     };
 
-    // the append's items first: item k by consumer k + 1 (waves 1..4)
-    if (app_slice >= 0 && wave - 1 < kAppItems) {
-      u32x4 app_x[4];
-      append_item_load(a, head, app_slice, wave - 1, lane, app_x);
-      append_item(a, head, app_slice, wave - 1, lane, app_x);
-    }
+    // the append's items first (consumer waves 1..kItemWaves)
+    if (app_on && wave - 1 < kItemWaves)
+      app::run_items<2, 1>(a, head, chunk * kItemWaves + wave - 1, a.n_chunks * kItemWaves, lane);
 
     // Consumers claim the chunk's groups in order from a block counter and
     // take each from the ring as soon as the loader has published it.
@@ -1376,7 +1192,6 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     }
   }
   __syncthreads();
-  const int n_parts = a.n_parts;
   const int stall_bits = lds_load(&sh.stalled);
   const bool stalled = stall_bits != 0;
   // the reason a part is poisoned, counted in the workspace's status words
@@ -1408,21 +1223,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       den = 1.f;
       mm = 0.f;
     }
-    float* wp = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + chunk) * (kD + 2);
-    if (a.counters) {
-      // read by another block of this launch: device-scope stores
-      __hip_atomic_store(wp + 2 + d, num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (d == 0) {
-        __hip_atomic_store(wp, mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(wp + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    } else {
-      wp[2 + d] = num;
-      if (d == 0) {
-        wp[0] = mm;
-        wp[1] = den;
-      }
-    }
+    store_record(a, (b * a.H_q) + hk * GQA + h, chunk, d, mm, den, num);
   }
   if (a.counters) merge_in_launch<GQA>(a, b, hk, head32, sh.last);
 }

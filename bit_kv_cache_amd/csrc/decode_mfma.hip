@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "kvq_internal.h"
+#include "merge_common.h"
 
 namespace kvq {
 namespace {
@@ -261,6 +262,7 @@ struct MfmaLds {
   } u;
   u32x4 bias_a[4][4][16];                          // bias A operand [c][kq][row]
   int bad;                                         // a group's page lies outside the pool
+  int last;                                        // last block of its head (in-launch merge)
 };
 
 template <int BITS, int GQA>
@@ -712,7 +714,6 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
     }
   }
   __syncthreads();
-  const int n_parts = a.n_parts;
   if (tid == 0 && sh.bad) status_add(a.status, kStatusBadPage);
   for (int i = tid; i < GQA * kD; i += kThreadsM) {
     const int h = i / kD, d = i % kD;
@@ -740,13 +741,9 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
       den = 1.f;
       mm = 0.f;
     }
-    float* wp = a.ws + (((b * a.H_q) + hk * GQA + h) * n_parts + chunk) * (kD + 2);
-    wp[2 + d] = num;
-    if (d == 0) {
-      wp[0] = mm;
-      wp[1] = den;
-    }
+    store_record(a, (b * a.H_q) + hk * GQA + h, chunk, d, mm, den, num);
   }
+  if (a.counters) merge_in_launch<GQA>(a, b, hk, head32, sh.last);
 
 }
 

@@ -315,12 +315,18 @@ kvq_status launch_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, i
   const int64_t G = cfg->group;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!append) return decode_and_merge(cfg, a, workspace, s);
-  if (kvq::fused_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_parts,
-                                  a.n_chunks)) {
-    // one launch: split-K, the append's quantize and the merge
-    a.counters = static_cast<int32_t*>(workspace);
+  if (kvq::split_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_chunks)) {
+    // the split-K launch also quantizes the appended group; the merge runs in
+    // the same launch (at most 8 parts) or in one launch after it
     a.append = 1;
-    return hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s));
+    if (kvq::fused_merge_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_parts)) {
+      a.counters = static_cast<int32_t*>(workspace);
+      return hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s));
+    }
+    if ((st = hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s))) !=
+        KVQ_OK)
+      return st;
+    return hip_status(kvq::launch_merge(a, s));
   }
   if ((st = hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s))) !=
       KVQ_OK)

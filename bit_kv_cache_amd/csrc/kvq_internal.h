@@ -173,17 +173,19 @@ inline bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
   return group == 128 && (gqa == 4 || gqa == 8) &&
          ((bits == 2 && (n_boost == 0 || n_boost == 16)) || (bits == 4 && n_boost == 0));
 }
-// The 2-bit matrix-core kernel merges its parts in the same launch when a
-// head has at most kFusedMergeParts of them.
+// The matrix-core kernels (one part per block) merge their parts in the same
+// launch when a head has at most kFusedMergeParts of them.
 inline bool fused_merge_supported(int bits, int group, int gqa, int n_boost, int n_parts) {
-  return bits == 2 && mfma_decode_supported(bits, group, gqa, n_boost) &&
-         n_parts <= kFusedMergeParts;
+  return mfma_decode_supported(bits, group, gqa, n_boost) && n_parts <= kFusedMergeParts;
 }
-// The same kernel also runs the append of a full residual group (plain
-// 2-bit codes, at least 4 chunks: chunk c quantizes slice c of 4).
-inline bool fused_append_supported(int bits, int group, int gqa, int n_boost, int n_parts,
-                                   int n_chunks) {
-  return fused_merge_supported(bits, group, gqa, n_boost, n_parts) && n_boost == 0 &&
+// The 2-bit matrix-core kernel also runs the append of a full residual group
+// (plain codes, at least 4 chunks: one of the group's 16 items per consumer
+// wave of the head's first four blocks, append_common.h), with the merge in
+// the same launch or in a merge launch after it.  (The 4-bit kernel has no
+// loader wave: items there delay every wave's first loads, and the step ran
+// slower than with the append in the merge's launch.)
+inline bool split_append_supported(int bits, int group, int gqa, int n_boost, int n_chunks) {
+  return bits == 2 && mfma_decode_supported(bits, group, gqa, n_boost) && n_boost == 0 &&
          n_chunks >= 4;
 }
 // Resident blocks per CU of the matrix-core kernels: two waves per SIMD,

@@ -50,4 +50,56 @@ __device__ __forceinline__ void merge_row(const float* ws, int np, float* out, i
   out[bh * kD + d] = L > 0.f ? o / L : 0.f;
 }
 
+// A block's record (m, l, acc[d]) of part `part` of row bh, stored for the
+// in-launch merge (device-scope stores, read by another block of the launch)
+// or for a merge launch (plain stores).
+__device__ __forceinline__ void store_record(const DecodeArgs& a, int64_t bh, int part, int d,
+                                             float m, float l, float v) {
+  float* wp = a.ws + (bh * a.n_parts + part) * (kD + 2);
+  if (a.counters) {
+    __hip_atomic_store(wp + 2 + d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      __hip_atomic_store(wp, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(wp + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    wp[2 + d] = v;
+    if (d == 0) {
+      wp[0] = m;
+      wp[1] = l;
+    }
+  }
+}
+
+// In-launch merge (decode kernels with one part per block, at most 8 parts):
+// after a block has stored its records with store_record, its arrival on the
+// head's counter, and in the last block of the head to arrive, the
+// log-sum-exp merge of the head's GQA query rows into the output.  No block
+// waits for another, so the order in which blocks run is free.  The last
+// block resets the counter, leaving it zero for the next call.  last_flag is
+// an LDS word of the block.
+template <int GQA>
+__device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int64_t b, int64_t hk,
+                                                int head32, int& last_flag) {
+  // this thread's stores have completed (they are visible device-wide)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(a.counters + head32, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == a.n_chunks - 1;
+    if (last) __hip_atomic_store(a.counters + head32, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = last;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  const int np = a.n_parts;
+  for (int i = threadIdx.x; i < GQA * kD; i += blockDim.x) {
+    const int64_t bh = b * a.H_q + hk * GQA + i / kD;
+    const int d = i % kD;
+    if (np <= 4) merge_row<4, true>(a.ws, np, a.out, bh, d);
+    else merge_row<8, true>(a.ws, np, a.out, bh, d);
+  }
+}
+
 }  // namespace kvq

@@ -213,8 +213,9 @@ size_t kvq_decode_workspace_bytes(const kvq_qcfg* cfg, int32_t B, int32_t H_q, i
  *      kvq_decode_workspace_bytes(...) bytes, 16-byte aligned, counter bytes
  *      zero (layout above).
  *  H_q / H_kv must be 1..8.
- *  2-bit codes with G = 128, GQA 4 or 8 and at most 8 parts per head run
- *  as one launch: the last block of each head to finish merges the head's
+ *  The matrix-core kernels (2-bit codes plain or with 16 boosted channels,
+ *  4-bit codes; G = 128, GQA 4 or 8) with at most 8 parts per head run as
+ *  one launch: the last block of each head to finish merges the head's
  *  partial records (device-scope stores and loads, one arrival counter per
  *  head); other configurations launch the merge separately. */
 kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
@@ -231,10 +232,11 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
  * step still attends to in fp16.  The cache contents equal those of
  * kvq_quantize_pack(cfg, cache, B, H_kv, res->k, res->v, res->cap * D,
  * n_quant_tokens / G, 1), bit for bit.  Plain 2-bit codes with G = 128,
- * GQA 4 or 8 and 4 to 8 chunks run the whole step as one launch (each of the
- * first four blocks of a head quantizes a quarter of the group, the last
- * block to finish merges); otherwise the quantization shares the merge's
- * launch (separate launches past 32 parts).
+ * GQA 4 or 8 and at least 4 chunks quantize the group in the split-K launch
+ * (the first four blocks of a head take a quarter of it each): with at most
+ * 8 chunks the whole step is that one launch (the last block to finish
+ * merges), with more a merge launch follows.  Otherwise the quantization
+ * shares the merge's launch (separate launches past 32 parts).
  *  append != 0 requires res->n >= G and n_quant_tokens + G <= t_cap
  *  (else KVQ_ERR_ARG, nothing launched). */
 kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,

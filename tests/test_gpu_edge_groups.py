@@ -14,8 +14,8 @@ channels) are planted, on a fixed pattern, with:
 Every quantize path of the library sees them: kvq_quantize_pack on a
 contiguous and on a paged cache, and the streaming append inside
 kvq_decode_step -- the one-launch step of the 2-bit kernel (4 and 7 chunks)
-and the merge + quantize launch of the other kernels (3 chunks; Kitty,
-4-bit, 8-bit).  Codes, scales, mins, Kitty high words / indices and
+and the merge + quantize launch of the other kernels (Kitty, 4-bit, 8-bit,
+G 32).  Codes, scales, mins, Kitty high words / indices and
 dequantized values must equal the oracle bit for bit.
 
 Attention over such a cache must stay within 2e-3 of the oracle.  Keys near

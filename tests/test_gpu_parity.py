@@ -342,9 +342,10 @@ def test_quantize_rounding_ties_bit_exact(built):
 def test_decode_step_with_append(built, name):
     """kvq_decode_step(append): the attention equals the oracle over the
     quantized tokens + the full fp16 residual group, and the residual group
-    lands in cache group T/G bit-exact.  Chunk counts 4..8 take the one-launch
-    path for plain 2-bit codes (split-K, append and merge in one kernel);
-    others quantize in the merge's launch, or in launches of their own."""
+    lands in cache group T/G bit-exact.  Plain 2-bit codes at GQA 4/8 with 4
+    or more chunks quantize in the split-K launch (4..8 chunks: the whole
+    step is one launch; more: a merge launch follows); others quantize in the
+    merge's launch, or in launches of their own."""
     import bit_kv_cache_amd as kvq
     w = _w(name)
     w = synth.shrink(w, R=w.G)
@@ -355,7 +356,7 @@ def test_decode_step_with_append(built, name):
     oracle.quantize_pack(oc, synth.as_bits(inp["k_res"]), synth.as_bits(inp["v_res"]),
                          w.T // w.G, 1)
     B = len(inp["heads"]) // w.H_kv
-    for n_chunks in (0, 3, 4, 7):
+    for n_chunks in (0, 1, 2, 3, 4, 7, 16, 40):
         gc = gpu_quantize(w, inp, t_cap)   # a fresh cache: each append is checked alone
         _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), B, w.H_q, w.H_kv, w.T, n_chunks)
         ws = kvq.decode_workspace(ws_bytes)
