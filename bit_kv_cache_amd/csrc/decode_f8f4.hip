@@ -15,14 +15,17 @@
 //    (KIVI page Step 4, x = code*scale + min spread over the dot product):
 //        q.k_t = sum_d (q_d s_d) code_td + sum_d q_d mn_d
 //        p.v_d = sum_t (p_t s_t) code_td + sum_t p_t mn_t
-//    Each A value is scaled by a power of two per group to below 2^8 and
-//    written as the sum of fp8 (e4m3) digits, each the round-to-nearest fp8
-//    value of the remaining residual (about four significant bits per
-//    digit).  The digits are A rows of the same head, so one MFMA per 16
-//    tokens (or 16 channels) serves four heads and the output rows of a head
-//    are summed afterwards.  Four digits carry about 16 bits; each digit's
-//    conversion is scaled by 2^-4k (undone by the MFMA's per-row E8M0 block
-//    scale) so small residuals never fall into fp8's subnormal range.
+//    Each A value is written as four fp8 (e4m3) digits in four A rows of the
+//    same head, so one MFMA per 16 tokens (or 16 channels) serves four heads
+//    and the output rows of a head are summed afterwards.  Key side: q_d s_d,
+//    scaled by a power of two per group to below 2^8, digit k the
+//    round-to-nearest fp8 value of the remaining residual over 2^-4k (about
+//    four significant bits each, 16 in all, relative to each value; the
+//    MFMA's per-row E8M0 scale undoes the 2^-4k).  Value side: p_t s_t >= 0
+//    as a 16-bit fixed-point number relative to its 32-token block's largest,
+//    digit k its k-th nibble from the top (fp8 bytes 0..15 are exactly
+//    b 2^-9, so no conversion), the block's power of two in the per-row,
+//    per-block E8M0 scale.
 //  * sum_d q_d mn_d is a vector-ALU dot product in the A-prep lanes; sum_t
 //    p_t mn_t is a per-head scalar kept beside the accumulator.
 //
@@ -75,6 +78,7 @@ constexpr int block_waves() { return 8; }
 constexpr uint32_t kNib = 0x33333333u;
 constexpr float kNegInfF = -__builtin_inff();
 constexpr int kDigits = 4;        // fp8 digits of an A value
+constexpr float kFixMax = 65535.f; // value-side fixed point: M = round(x 65535 / 2^eb) <= 65535
 
 // ------------------------------------------------------------------ helpers
 
@@ -391,6 +395,45 @@ __device__ __forceinline__ void write_digits(ATile& tile, int hr, uint32_t off,
   }
 }
 
+// Fixed-point digits of four non-negative values (x0..x3 -> bytes 0..3 of each
+// digit word): M = round(x S) with x S < 65535.5 (an integer in the low
+// mantissa bits of x S + 2^23), and digit k is nibble 3 - k of M as an fp8
+// byte.  The e4m3 bytes 0..15 are the values b 2^-9 (subnormals, then the
+// first binade), so a nibble is its own fp8 encoding and no conversion is
+// needed; the matrix-core row of digit k carries 2^(12 - 4k) in its scale.
+__device__ __forceinline__ void fixed_digits(float x0, float x1, float x2, float x3, float S,
+                                             uint32_t (&d)[kDigits]) {
+  constexpr float kRound = 8388608.f;   // 2^23
+  const uint32_t u0 = __builtin_bit_cast(uint32_t, fmaf(x0, S, kRound));
+  const uint32_t u1 = __builtin_bit_cast(uint32_t, fmaf(x1, S, kRound));
+  const uint32_t u2 = __builtin_bit_cast(uint32_t, fmaf(x2, S, kRound));
+  const uint32_t u3 = __builtin_bit_cast(uint32_t, fmaf(x3, S, kRound));
+  // the four 16-bit M side by side, then their nibbles spread into bytes
+  const uint32_t p01 = __builtin_amdgcn_perm(u1, u0, 0x05040100u);
+  const uint32_t p23 = __builtin_amdgcn_perm(u3, u2, 0x05040100u);
+  const uint32_t lo01 = p01 & 0x0F0F0F0Fu, hi01 = (p01 >> 4) & 0x0F0F0F0Fu;
+  const uint32_t lo23 = p23 & 0x0F0F0F0Fu, hi23 = (p23 >> 4) & 0x0F0F0F0Fu;
+  d[0] = __builtin_amdgcn_perm(hi23, hi01, 0x07050301u);   // bits 12..15 of each M
+  d[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07050301u);   // bits 8..11
+  d[2] = __builtin_amdgcn_perm(hi23, hi01, 0x06040200u);   // bits 4..7
+  d[3] = __builtin_amdgcn_perm(lo23, lo01, 0x06040200u);   // bits 0..3
+}
+
+// Fixed-point digits of 8 non-negative values (items 8o..8o+7) into rows
+// 4*hr..4*hr+3 of an A tile, at the byte positions write_digits uses.
+__device__ __forceinline__ void write_fixed_digits(ATile& tile, int hr, uint32_t off,
+                                                   const float (&x)[8], float S) {
+  uint32_t de[kDigits], dodd[kDigits];
+  fixed_digits(x[0], x[2], x[4], x[6], S, de);
+  fixed_digits(x[1], x[3], x[5], x[7], S, dodd);
+  uint8_t* base = &tile[4 * hr][0] + off;
+#pragma unroll
+  for (int k = 0; k < kDigits; ++k) {
+    *reinterpret_cast<uint32_t*>(base + k * kRowBytes) = de[k];
+    *reinterpret_cast<uint32_t*>(base + k * kRowBytes + 8) = dodd[k];
+  }
+}
+
 // Byte offset, inside row 0 of an A-operand tile, of contraction elements
 // 8o..8o+7 when the B operand is fp4 in its plain order (nibble j of lane
 // group g is element 32g + j): by the A byte order above, element k sits at
@@ -494,7 +537,6 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   float m_run[NH], l_part[NH], mterm[NH];
   float wsum[NH][8];                 // fp16-window p.V, channels of this lane
   f32x4 acc[NH][8];                  // quantized p.V: [head half][channel block], 4 digit rows
-  int e_v = -1000;                   // running value-side exponent of acc
 #pragma unroll
   for (int H = 0; H < NH; ++H) {
     m_run[H] = kNegInfF;
@@ -804,6 +846,9 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     // ------------------------------------------------------ groups
     const uint32_t a_off = a_offset(n);
     const int sa_digit = 127 - 4 * (lane & 3);   // A row m = lane & 15 holds digit m % 4
+    // byte address of the lane holding the value-side exponent of this lane's
+    // A-scale row (m = lane & 15) and block (g = lane >> 4)
+    const int blk_src = 4 * (16 * ((lane & 15) >> 2) + 4 * (lane >> 4));
     int e_s = 0;                   // key exponent of the current group
     float bias[NH];                // its q . key-min terms
     f32x4 cq[NH][8];               // its q.K^T digit rows, per tile
@@ -963,10 +1008,10 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       float p[NH][8];                // tokens 8n..8n+7 of head r + 4H
       softmax_group(logit, alpha, p);
 
-      // value A operand: digits of p s_t 2^(8 - e_v); min term
-      const int e_v_new = max(e_v, row_exp_f16(pf.vs));
-      const float vshift = exp2i(e_v - e_v_new);
-      e_v = e_v_new;
+      // value A operand: fixed-point digits of p s_t, one power of two per
+      // head and 32-token block (lanes n = 4b..4b+3 of a row hold block b);
+      // min term
+      int sav[NH];   // the p.V product's A scale of this lane's row and block
 #pragma unroll
       for (int H = 0; H < NH; ++H) {
         float x[8];
@@ -979,22 +1024,32 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
           mt = fmaf(p[H][2 * i + 1], h2f_hi(pf.vmn[i]), mt);
         }
         mterm[H] = fmaf(mterm[H], alpha[H], mt);
-        write_digits(L.op.av[H], r, a_off, x, e_v - 8);
+        float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        bm = fmaxf(bm, dpp<kQuadXor1>(bm));
+        bm = fmaxf(bm, dpp<kQuadXor2>(bm));
+        // x < 2^eb for the whole block; blocks below 2^-100 (all but zero
+        // weight) keep that exponent, so every scale stays in E8M0's range
+        const int eb = max(ceil_exp(bm), -100);
+        write_fixed_digits(L.op.av[H], r, a_off, x, kFixMax * exp2i(-eb));
+        // row m = lane & 15 (head m / 4, digit m % 4), block g = lane >> 4:
+        // the exponent of lane 16 (m / 4) + 4 g, and 2^(eb - 16) M =
+        // sum_k nibble_k 2^-9 2^(eb + 5 - 4k)
+        sav[H] = 132 - 4 * (lane & 3) + __builtin_amdgcn_ds_bpermute(blk_src, eb);
       }
       wave_sync();
 
-      // rescale the accumulators (alpha and the exponent change)
+      // rescale the accumulators by the softmax's alpha
       {
         bool same = true;
 #pragma unroll
-        for (int H = 0; H < NH; ++H) same = same && alpha[H] * vshift == 1.f;
+        for (int H = 0; H < NH; ++H) same = same && alpha[H] == 1.f;
         if (!__all(same)) {
 #pragma unroll
           for (int H = 0; H < NH; ++H) {
-            const float f = alpha[H] * vshift;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              acc[H][i] *= f;
+              acc[H][i] *= alpha[H];
               wsum[H][i] *= alpha[H];
             }
           }
@@ -1009,7 +1064,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
         for (int blk = 0; blk < 8; ++blk) {
           const int hb = blk >> 2, comp = blk & 3;
           acc[H][blk] = mfma_f8f4(apv, fp4_operand(pf.vw[0][hb][comp], pf.vw[1][hb][comp]),
-                                  acc[H][blk], sa_digit);
+                                  acc[H][blk], sav[H]);
         }
       }
     };
@@ -1045,7 +1100,8 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       }
 
       // fold the digit rows of the quantized p.V into the lane's channels
-      const float ev = exp2i(e_v - 8 + 1);   // p.V digits carry 2^(8 - e_v), codes are c/2
+      // p.V digits carry 65535 / 65536 of p s_t, codes are c/2
+      constexpr float ev = 2.f * 65536.f / 65535.f;
 #pragma unroll
       for (int H = 0; H < NH; ++H) {
         const float mts = row_sum16(mterm[H]);

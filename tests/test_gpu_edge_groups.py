@@ -23,8 +23,8 @@ Attention over such a cache must stay within 2e-3 of the oracle.  Keys near
 their logits stay O(1): an fp32 kernel cannot resolve logits of order 1e4
 to 2e-3 (their rounding alone is of that size), while the fp64 oracle can.
 Values near +-65504 are a separate case: every error term of the output
-scales with the values' magnitude (the p.V operand's fp8 digits, 2^-16 of
-p_t * scale_t; the fp32 rounding of the logits, which moves the weights of
+scales with the values' magnitude (the p.V operand's fixed-point digits,
+2^-17 of the largest p_t * scale_t of a 32-token block; the fp32 rounding of the logits, which moves the weights of
 values of that size; the fp32 accumulation), so that case is held to the
 bar relative to the values' scale, 2e-3 * max(1, |v|max / 4), as the
 scaled-input parity tests are (N(0,1) values reach |v| of about 4).
