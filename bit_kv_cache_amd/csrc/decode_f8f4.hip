@@ -72,9 +72,10 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kG = 128;          // tokens per group
 // One block per CU: 8 waves (two per SIMD), the first the loader, the
-// others consumers.
-template <int GQA, bool KITTY>
-constexpr int block_waves() { return 8; }
+// others consumers; with one chunk per consumer wave (PW), 9 waves: the
+// loader and 8 consumers, two per SIMD.
+template <int GQA, bool KITTY, bool PW = false>
+constexpr int block_waves() { return PW ? 9 : 8; }
 constexpr uint32_t kNib = 0x33333333u;
 constexpr float kNegInfF = -__builtin_inff();
 constexpr int kDigits = 4;        // fp8 digits of an A value
@@ -261,24 +262,24 @@ template <bool KITTY, bool MX>
 constexpr int slot_bytes() { return MX ? 17408 : KITTY ? 10240 : 9216; }
 template <bool KITTY, bool MX>
 constexpr int dma_per_group() { return MX ? 17 : KITTY ? 10 : 9; }
-template <int GQA, bool KITTY, bool MX>
+template <int GQA, bool KITTY, bool MX, bool PW = false>
 constexpr int ring_slots() {
-  return MX ? (GQA == 4 ? 6 : 5) : GQA == 4 ? (KITTY ? 10 : 12) : 6;
+  return PW ? 11 : MX ? (GQA == 4 ? 6 : 5) : GQA == 4 ? (KITTY ? 10 : 12) : 6;
 }
 // groups the loader keeps in flight: fewer than ring_slots, and (DF - 1)
 // groups of copies (plus each group's flag copy) within the vector-memory
 // counter's 63
-template <int GQA, bool KITTY, bool MX>
+template <int GQA, bool KITTY, bool MX, bool PW = false>
 constexpr int in_flight() {
   constexpr int per = dma_per_group<KITTY, MX>() + 1;
-  return ring_slots<GQA, KITTY, MX>() - 1 < 63 / per + 1 ? ring_slots<GQA, KITTY, MX>() - 1
-                                                         : 63 / per + 1;
+  constexpr int rs = ring_slots<GQA, KITTY, MX, PW>();
+  return rs - 1 < 63 / per + 1 ? rs - 1 : 63 / per + 1;
 }
 
-template <int GQA, bool KITTY, bool MX>
+template <int GQA, bool KITTY, bool MX, bool PW = false>
 struct LdsF {
-  static constexpr int R = ring_slots<GQA, KITTY, MX>();
-  static constexpr int NW = block_waves<GQA, KITTY>();
+  static constexpr int R = ring_slots<GQA, KITTY, MX, PW>();
+  static constexpr int NW = block_waves<GQA, KITTY, PW>();
   union {
     WaveLdsF<GQA, MX> w[NW - 1];
     MergeLdsF<GQA, NW> merge;
@@ -289,6 +290,7 @@ struct LdsF {
   int next_group;   // next group a consumer claims
   int stalled;      // bit 0: a wait ran past its spin limit; bit 1: a page outside the pool
   int last;         // this block is the last of its head to finish (in-launch merge)
+  int bad_chunks;   // PW: bit w set when a group of the block's chunk w lies outside the pool
 };
 
 struct Operands {
@@ -478,6 +480,14 @@ __device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
 // made the GQA-8 kernel spill).
 constexpr int kItemWaves = 4;
 
+// Channel of accumulator block blk in lane (n, r): column n of a p.V product;
+// the 2-bit value words give channels 4n.. and 64 + 4n..; MXFP4 value
+// columns are 16 consecutive channels.
+template <bool MX>
+__device__ __forceinline__ int lane_chan(int blk, int n) {
+  return MX ? 16 * blk + n : 64 * (blk >> 2) + 4 * n + (blk & 3);
+}
+
 // ------------------------------------------------------------------ kernel
 
 // MX: the cache is an MXFP4 one (kvq_mx_cache in a.c: k_codes / v_codes its
@@ -487,22 +497,31 @@ constexpr int kItemWaves = 4;
 // product takes as they are (BitDecoding page, native mxfp4 data with block
 // scale factors).  The quantized part then has no per-group operand work on
 // the key side (the query's digits are built once) and no min terms.
-template <int GQA, bool KITTY, bool MX>
-__global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8f4_kernel(DecodeArgs a) {
+//
+// PW (one chunk per consumer wave, plain 2-bit codes at GQA 4, for steps of
+// many chunks with no in-launch merge): a block takes the 8 chunks c0..c0+7,
+// the loader streams them interleaved (block group j is group j / 8 of chunk
+// c0 + j % 8) and consumer wave w + 1 takes every group of chunk c0 + w in
+// order, with its window slice.  The wave's softmax state is then the
+// chunk's partial, written without a block merge, and a launch of n_chunks
+// chunks needs n_chunks / 8 blocks per head.
+template <int GQA, bool KITTY, bool MX, bool PW>
+__global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decode_f8f4_kernel(DecodeArgs a) {
   static_assert(!(KITTY && MX), "the Kitty boost is a min-max cache");
+  static_assert(!PW || (GQA == 4 && !KITTY && !MX), "one chunk per wave: plain 2-bit codes, GQA 4");
   constexpr int NH = GQA / 4;    // heads per lane (r and r + 4)
-  constexpr int R = ring_slots<GQA, KITTY, MX>();
-  constexpr int DF = in_flight<GQA, KITTY, MX>();
-  constexpr int kWaves = block_waves<GQA, KITTY>();
+  constexpr int R = ring_slots<GQA, KITTY, MX, PW>();
+  constexpr int DF = in_flight<GQA, KITTY, MX, PW>();
+  constexpr int kWaves = block_waves<GQA, KITTY, PW>();
   // wave 0 is the loader (the first wave of a block to start), 1.. consume
   constexpr int kConsumers = kWaves - 1, kLoader = 0;
   constexpr int kThreadsF = 64 * kWaves;
   static_assert((dma_per_group<KITTY, MX>() + 1) * (DF - 1) < 64, "vmcnt range");
   static_assert(R < kSeqLen, "ready tags must not repeat within the ring");
-  static_assert(sizeof(LdsF<GQA, KITTY, MX>) <= 160 * 1024, "LDS per CU");
+  static_assert(sizeof(LdsF<GQA, KITTY, MX, PW>) <= 160 * 1024, "LDS per CU");
   constexpr int SB = slot_bytes<KITTY, MX>();
   constexpr int NDMA = dma_per_group<KITTY, MX>();
-  __shared__ LdsF<GQA, KITTY, MX> sh;
+  __shared__ LdsF<GQA, KITTY, MX, PW> sh;
 
   // Every launch argument the first phase needs, fetched in one round trip
   // (the compiler would otherwise load each one just before its first use,
@@ -516,14 +535,23 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, r = lane >> 4;
-  int chunk, head32;                             // head32 < 65536 (checked on the host)
-  xcd_part_head(chunk, head32);
+  int bpart, head32;                             // head32 < 65536 (checked on the host)
+  xcd_part_head(bpart, head32);
   const int64_t head = head32;
   const int b32 = head32 / a.H_kv, hk32 = head32 - b32 * a.H_kv;   // 32-bit division
   const int64_t b = b32, hk = hk32;
   const uint16_t* qrow = a.q + ((b * a.H_q) + hk * GQA) * kD;
+  // the block's chunk, or (PW) its first chunk c0 and this wave's chunk
+  const int c0 = PW ? bpart * kConsumers : bpart;
+  const int chunk = PW ? c0 + max(wave - 1, 0) : bpart;
+  const int64_t seq_g = seq_groups(a, b, kG);
+  auto chunk_groups = [&](int c) -> int {   // groups of chunk c in this sequence
+    const int64_t g0 = (int64_t)c * a.groups_per_chunk;
+    return (int)max<int64_t>(0, min<int64_t>(seq_g, g0 + a.groups_per_chunk) - g0);
+  };
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
-  const int ngc = (int)max<int64_t>(0, min<int64_t>(seq_groups(a, b, kG), gb + a.groups_per_chunk) - gb);
+  const int ngc = chunk_groups(chunk);
+  bool own_stall = false;   // PW: this consumer's wait for a group ran out
   // this block's waves take items of the appended group (2-bit min-max cache)
   const bool app_on = !KITTY && !MX && a.append;
 
@@ -558,6 +586,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     if (tid == 0) {
       sh.next_group = 0;
       sh.stalled = 0;
+      sh.bad_chunks = 0;
     }
     // the flags are written before any copy can land on them
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -582,13 +611,12 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     const char* xp = lane < 32 ? reinterpret_cast<const char*>(a.c.k_hi) + 16 * lane
                                : reinterpret_cast<const char*>(a.c.k_bidx) + 16 * ((lane - 32) & 7);
     const int64_t xstep = lane < 32 ? kG * 4 : kD;
-    // block of the chunk's group gb + jo: head-major, or the page table's entry
+    // block of the head's group gi: head-major, or the page table's entry
     // (read through the constant address space: scalar loads, which the
     // vector-memory counter the copies rely on does not see)
-    const int64_t blk0 = head * (a.c.t_cap / kG) + gb;
     const int64_t pool = a.c.t_cap / kG;
     typedef __attribute__((address_space(4))) const int32_t* PagePtr;
-    const PagePtr pt = a.c.pages ? (PagePtr)(uintptr_t)(a.c.pages + head * a.c.pt_stride + gb)
+    const PagePtr pt = a.c.pages ? (PagePtr)(uintptr_t)(a.c.pages + head * a.c.pt_stride)
                                  : (PagePtr) nullptr;
     bool bad_page = false;
     // LDS byte address of the ring (address-space cast of the generic pointer)
@@ -605,7 +633,9 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     // of their heads (and on the same memory channels).
     const int rot = ngc > 0 ? (int)((head32 * 37 + chunk * 17) % ngc) : 0;
     bool ok = true;
-    for (int j = 0; j < ngc; ++j) {
+    // PW: the chunks are in token order, so the first has the most groups
+    const int n_iter = PW ? kConsumers * chunk_groups(c0) : ngc;
+    for (int j = 0; j < n_iter; ++j) {
       const int s = j % R;
       if (!spin_until(&sh.empty[s], j)) {
         ok = false;
@@ -613,13 +643,33 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       }
       asm volatile("" ::: "memory");
       const uint32_t sl = __builtin_amdgcn_readfirstlane(ring0 + s * SB);
-      const int64_t jo = j + rot < ngc ? j + rot : j + rot - ngc;
-      int64_t blk = blk0 + jo;
+      int64_t gi;   // the group's index in the head
+      int w = 0;    // PW: its chunk c0 + w
+      if constexpr (PW) {
+        w = j % kConsumers;
+        const int g = j / kConsumers;
+        if (g >= chunk_groups(c0 + w)) {   // past a shorter chunk's end: the slot passes on
+          lds_store(&sh.empty[s], j + R);
+          continue;
+        }
+        gi = (int64_t)(c0 + w) * a.groups_per_chunk + g;
+      } else {
+        gi = gb + (j + rot < ngc ? j + rot : j + rot - ngc);
+      }
+      int64_t blk = head * pool + gi;
       if (pt) {
-        blk = pt[jo];
+        blk = pt[gi];
         if (blk < 0 || blk >= pool) {   // a page outside the pool: copy block 0, poison
-          bad_page = true;
           blk = 0;
+          if constexpr (PW) {
+            // marked before the group is published, so its consumer sees it
+            if (lane == 0)
+              __hip_atomic_fetch_or(&sh.bad_chunks, 1 << w, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          } else {
+            bad_page = true;
+          }
         }
       }
       if constexpr (MX) {
@@ -627,7 +677,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
         // (8 tokens x 128 channels, 512 B each), key scales (4 B per token;
         // lanes 0..31) and value scales (128 B per 32 tokens; lanes 32..63)
         // (key rows land transposed: slot row 16 i + k holds token 8 k + i)
-        const int64_t t0 = (gb + jo) * kG;
+        const int64_t t0 = gi * kG;
         const char* kc = reinterpret_cast<const char*>(a.c.k_codes) + (head * a.c.t_cap + t0) * 64 +
                          512 * (lane >> 2) + 16 * (lane & 3);
         const char* vc = reinterpret_cast<const char*>(a.c.v_codes) +
@@ -654,9 +704,12 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
     }
     vm_wait<0>();
-    if ((!ok || bad_page) && lane == 0)
+    if constexpr (PW) {
+      if (!ok && lane == 0) status_add(a.status, kStatusStalled);
+    } else if ((!ok || bad_page) && lane == 0) {
       __hip_atomic_fetch_or(&sh.stalled, (ok ? 0 : 1) | (bad_page ? 2 : 0), __ATOMIC_RELAXED,
                             __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
   } else {
     // ---------------------------------------------------------- consumer waves
     __syncthreads();   // the loader has set up the ring's flags
@@ -673,7 +726,10 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     const int u0 = min(n_win, chunk * wpc), u1 = min(n_win, u0 + wpc);
     const int kq = lane >> 4, m_row = lane & 15;
     const int cw = wave - 1;   // consumer index
-    const int u_first = u0 + 16 * cw;
+    // window tiles of the wave: every kConsumers-th of the block's slice, or
+    // (PW) every tile of its chunk's slice
+    const int u_first = PW ? u0 : u0 + 16 * cw;
+    constexpr int kWinStep = 16 * (PW ? 1 : kConsumers);
     auto win_row = [&](const uint16_t* sink, const uint16_t* res, int u) -> const uint16_t* {
       return u < a.n_sink ? sink + (head * a.sink_cap + u) * kD
                           : res + (head * a.res_cap + (u - a.n_sink)) * kD;
@@ -737,12 +793,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
         for (int e = 0; e < 8; ++e) qv[j][e] *= qs;
     }
     const float q_unscale = exp2i(e_q - 8);
-    // channel of this lane's accumulator block blk (column n of a p.V product):
-    // the 2-bit value words give channels 4n.. and 64 + 4n..; MXFP4 value
-    // columns are 16 consecutive channels
-    auto chan = [&](int blk) -> int {
-      return MX ? 16 * blk + n : 64 * (blk >> 2) + 4 * n + (blk & 3);
-    };
+    auto chan = [&](int blk) -> int { return lane_chan<MX>(blk, n); };
 
     WaveLdsF<GQA, MX>& L = sh.u.w[cw];
 
@@ -778,7 +829,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
       for (int H = 0; H < NH; ++H)
 #pragma unroll
         for (int i = 0; i < 8; ++i) wacc[H][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int u = u_first; u < u1; u += 16 * kConsumers) {
+      for (int u = u_first; u < u1; u += kWinStep) {
         if (u != u_first) load_win(u, wt);
         const int nt = min(16, u1 - u);
         {
@@ -1071,7 +1122,8 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
 
     // the append's items first (consumer waves 1..kItemWaves)
     if (app_on && wave - 1 < kItemWaves)
-      app::run_items<2, 1>(a, head, chunk * kItemWaves + wave - 1, a.n_chunks * kItemWaves, lane);
+      app::run_items<2, 1>(a, head, bpart * kItemWaves + wave - 1, (int)gridDim.x * kItemWaves,
+                           lane);
 
     // Consumers claim the chunk's groups in order from a block counter and
     // take each from the ring as soon as the loader has published it.
@@ -1079,14 +1131,21 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     // by all lanes with the same value (a lane-divergent store at the end of
     // the body lets the compiler split the wave across iterations).
     if constexpr (!MX) {
-      for (;;) {
-        int jl = 0;
-        if (lane == 0) jl = atomicAdd(&sh.next_group, 1);
-        const int j = __builtin_amdgcn_readlane(jl, 0);
-        if (j >= ngc) break;
+      for (int it = 0;; ++it) {
+        int j;
+        if constexpr (PW) {   // the wave's own chunk, in order
+          if (it >= ngc) break;
+          j = cw + kConsumers * it;
+        } else {
+          int jl = 0;
+          if (lane == 0) jl = atomicAdd(&sh.next_group, 1);
+          j = __builtin_amdgcn_readlane(jl, 0);
+          if (j >= ngc) break;
+        }
         const int s = j % R;
         if (!spin_until(&sh.ready[s], j & (kSeqLen - 1))) {
           if (lane == 0) __hip_atomic_fetch_or(&sh.stalled, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          own_stall = true;
           break;
         }
         asm volatile("" ::: "memory");
@@ -1228,6 +1287,24 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     }
   }
 
+  if constexpr (PW) {
+    // ------------------------------------------------------------ chunk partial
+    // the consumer's state is its chunk's partial (poisoned when its wait ran
+    // out or a group of the chunk lies outside the pool); no block merge
+    if (wave == kLoader) return;
+    const bool bad = (lds_load(&sh.bad_chunks) >> (wave - 1)) & 1;
+    if (lane == 0 && own_stall) status_add(a.status, kStatusStalled);
+    if (lane == 0 && bad) status_add(a.status, kStatusBadPage);
+    const bool poison = own_stall || bad;
+    const int64_t bh = (b * a.H_q) + hk * GQA + r;
+    const float lsum = row_sum16(l_part[0]);
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk)
+      store_record(a, bh, chunk, lane_chan<MX>(blk, n), poison ? 0.f : m_run[0],
+                   poison ? 1.f : lsum, poison ? __builtin_nanf("") : wsum[0][blk]);
+    return;
+  }
+
   // ---------------------------------------------------------------- block merge
   float lsum[NH];
 #pragma unroll
@@ -1243,8 +1320,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
     }
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
-      const int d = MX ? 16 * blk + n : 64 * (blk >> 2) + 4 * n + (blk & 3);
-      M.num[wave][h][d] = wsum[H][blk];
+      M.num[wave][h][lane_chan<MX>(blk, n)] = wsum[H][blk];
     }
   }
   __syncthreads();
@@ -1288,12 +1364,15 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY>()), 1) void decode_f8
 
 hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
-  if (a.n_boost > 0) {
-    if (a.gqa == 4) decode_f8f4_kernel<4, true, false><<<grid, 64 * block_waves<4, true>(), 0, st>>>(a);
-    else decode_f8f4_kernel<8, true, false><<<grid, 64 * block_waves<8, true>(), 0, st>>>(a);
+  if (pw_decode_supported(a.n_boost, a.gqa, a.counters != nullptr, a.n_chunks, a.B * a.H_kv)) {
+    const dim3 gpw((unsigned)(a.n_chunks / kPwChunks), (unsigned)(a.B * a.H_kv));
+    decode_f8f4_kernel<4, false, false, true><<<gpw, 64 * block_waves<4, false, true>(), 0, st>>>(a);
+  } else if (a.n_boost > 0) {
+    if (a.gqa == 4) decode_f8f4_kernel<4, true, false, false><<<grid, 64 * block_waves<4, true>(), 0, st>>>(a);
+    else decode_f8f4_kernel<8, true, false, false><<<grid, 64 * block_waves<8, true>(), 0, st>>>(a);
   } else {
-    if (a.gqa == 4) decode_f8f4_kernel<4, false, false><<<grid, 64 * block_waves<4, false>(), 0, st>>>(a);
-    else decode_f8f4_kernel<8, false, false><<<grid, 64 * block_waves<8, false>(), 0, st>>>(a);
+    if (a.gqa == 4) decode_f8f4_kernel<4, false, false, false><<<grid, 64 * block_waves<4, false>(), 0, st>>>(a);
+    else decode_f8f4_kernel<8, false, false, false><<<grid, 64 * block_waves<8, false>(), 0, st>>>(a);
   }
   return hipGetLastError();
 }
@@ -1309,8 +1388,8 @@ hipError_t launch_decode_mx_mfma(const kvq_mx_cache& mc, const DecodeArgs& args,
   a.c.pages = nullptr;
   a.append = 0;
   const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
-  if (a.gqa == 4) decode_f8f4_kernel<4, false, true><<<grid, 64 * block_waves<4, false>(), 0, st>>>(a);
-  else decode_f8f4_kernel<8, false, true><<<grid, 64 * block_waves<8, false>(), 0, st>>>(a);
+  if (a.gqa == 4) decode_f8f4_kernel<4, false, true, false><<<grid, 64 * block_waves<4, false>(), 0, st>>>(a);
+  else decode_f8f4_kernel<8, false, true, false><<<grid, 64 * block_waves<8, false>(), 0, st>>>(a);
   return hipGetLastError();
 }
 

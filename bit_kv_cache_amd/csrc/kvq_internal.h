@@ -188,6 +188,18 @@ inline bool split_append_supported(int bits, int group, int gqa, int n_boost, in
   return bits == 2 && mfma_decode_supported(bits, group, gqa, n_boost) && n_boost == 0 &&
          n_chunks >= 4;
 }
+// The 2-bit kernel's one-chunk-per-wave geometry (kPwChunks consumer waves
+// per block, each with a whole chunk): plain codes at GQA 4 with no in-launch
+// merge, when the chunks fill every CU in one round of blocks.  It removes
+// the block merge and the per-block start and tail that a step of hundreds
+// of one-chunk blocks per head pays in every round.
+constexpr int kPwChunks = 8;
+inline bool pw_decode_supported(int n_boost, int gqa, bool in_launch_merge, int n_chunks,
+                                int64_t heads) {
+  return n_boost == 0 && gqa == 4 && !in_launch_merge && n_chunks % kPwChunks == 0 &&
+         n_chunks >= 4 * kPwChunks &&   // at least 4 blocks per head: the append's 16 items
+         (int64_t)(n_chunks / kPwChunks) * heads >= 256;
+}
 // Resident blocks per CU of the matrix-core kernels: two waves per SIMD,
 // as one block of 8 waves (2-bit, fp8 x fp4 kernel) or two of 4 (4-bit).
 constexpr int mfma_blocks_per_cu(int bits, int) { return bits == 2 ? 1 : 2; }
