@@ -460,6 +460,21 @@ __device__ __forceinline__ void write_digits_nat(ATile& tile, int hr, uint32_t o
   }
 }
 
+// Fixed-point digits (fixed_digits) of 8 non-negative values of consecutive
+// contraction elements, at the byte positions write_digits_nat uses.
+__device__ __forceinline__ void write_fixed_digits_nat(ATile& tile, int hr, uint32_t off,
+                                                       const float (&x)[8], float S) {
+  uint32_t lo[kDigits], hi[kDigits];
+  fixed_digits(x[0], x[1], x[2], x[3], S, lo);
+  fixed_digits(x[4], x[5], x[6], x[7], S, hi);
+  uint8_t* base = &tile[4 * hr][0] + off;
+#pragma unroll
+  for (int k = 0; k < kDigits; ++k) {
+    *reinterpret_cast<uint32_t*>(base + k * kRowBytes) = lo[k];
+    *reinterpret_cast<uint32_t*>(base + k * kRowBytes + 4) = hi[k];
+  }
+}
+
 __device__ __forceinline__ v8i read_a(const ATile& tile, int m, int g) {
   const u32x4* p = reinterpret_cast<const u32x4*>(&tile[m][32 * g]);
   const u32x4 lo = p[0], hi = p[1];
@@ -1242,12 +1257,18 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
         float alpha[NH];
         float p[NH][8];
         softmax_group(logit, alpha, p);
+        // fixed-point digits of p, one power of two per head and 32-token
+        // block (lanes n = 4b..4b+3 of a row), as on the min-max path
+        int sav[NH];
 #pragma unroll
         for (int H = 0; H < NH; ++H) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = p[H][e] * 256.f;
-          write_digits_nat(L.op.av[H], r, a_nat, x, 0);
+          float bm = fmaxf(fmaxf(fmaxf(p[H][0], p[H][1]), fmaxf(p[H][2], p[H][3])),
+                           fmaxf(fmaxf(p[H][4], p[H][5]), fmaxf(p[H][6], p[H][7])));
+          bm = fmaxf(bm, dpp<kQuadXor1>(bm));
+          bm = fmaxf(bm, dpp<kQuadXor2>(bm));
+          const int eb = max(ceil_exp(bm), -100);
+          write_fixed_digits_nat(L.op.av[H], r, a_nat, p[H], kFixMax * exp2i(-eb));
+          sav[H] = 132 - 4 * (lane & 3) + __builtin_amdgcn_ds_bpermute(blk_src, eb);
         }
         wave_sync();
         {
@@ -1272,17 +1293,17 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
             acc[H][blk] = mfma_f8f4_mx(apv,
                                        v8i{(int)vc[blk][0], (int)vc[blk][1], (int)vc[blk][2],
                                            (int)vc[blk][3], 0, 0, 0, 0},
-                                       acc[H][blk], sa_digit, (int)vsc[blk]);
+                                       acc[H][blk], sav[H], (int)vsc[blk]);
         }
         wave_sync();   // the digits are read before the next group writes them
       }
-      // fold the digit rows (2^8 p) into the lane's channels
+      // fold the digit rows (65535 / 65536 of p) into the lane's channels
 #pragma unroll
       for (int H = 0; H < NH; ++H)
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
           const f32x4 v = acc[H][blk];
-          wsum[H][blk] += ((v[0] + v[1]) + (v[2] + v[3])) * (1.f / 256.f);
+          wsum[H][blk] += ((v[0] + v[1]) + (v[2] + v[3])) * (65536.f / 65535.f);
         }
     }
   }
