@@ -3,7 +3,7 @@
 // that has filled up (rows 0..127 of the head's residual buffer) into cache
 // group n_groups, with the arithmetic of the quantize kernel (KIVI page,
 // Steps 1-2): min and max by the total order -0 < +0, scale
-// fp16((max - min) / maxq), codes by quant_code_rcp, least significant code
+// fp16((max - min) / maxq), codes as quant_code_rcp gives them, least significant code
 // first.  The codes are bit-identical to kvq_quantize_pack's.
 //
 // The group is cut into 16 self-contained items: items 0..7 are key channels
@@ -49,7 +49,27 @@ __device__ __forceinline__ void item_load(const DecodeArgs& a, int64_t head, int
   }
 }
 
-template <int BITS>
+// Code of x in a group (mn, s, rs) as quant_code_rcp computes it, in two
+// parts: quot() is the quotient by the reciprocal, or (exact) by the IEEE
+// division, and near() says whether the former lies within quant_code_rcp's
+// tie window.  An item first codes every value by the reciprocal and notes
+// whether any value of the wave lies within the window; only then does it
+// code the item again by the IEEE quotient, so the window costs no branch
+// per value (ONE_CHECK; otherwise quant_code_rcp itself, value by value,
+// which keeps fewer registers live).  Outside the window both quotients give
+// the same code, so the codes are quant_code_rcp's either way.
+__device__ __forceinline__ float quot(float x, float mn, float s, float rs, bool exact) {
+#pragma clang fp contract(off)
+  return exact ? (x - mn) / s : (x - mn) * rs;
+}
+__device__ __forceinline__ bool near_tie(float y) {
+  return __builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-16f;
+}
+__device__ __forceinline__ uint32_t code_of(float y, float s, float maxq) {
+  return s == 0.0f ? 0u : (uint32_t)__builtin_rintf(fminf(fmaxf(y, 0.0f), maxq));
+}
+
+template <int BITS, bool ONE_CHECK>
 __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, int item, int lane,
                                            const u32x4 (&x)[4]) {
   static_assert(BITS == 2 || BITS == 4, "2- or 4-bit codes");
@@ -104,14 +124,33 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
     }
     // codes of token t: channel c0 + 8q + e at bits BITS (c0 + 8q + e) mod
     // 32 of key word (c0 + 8q + e) / kFpi
+    uint32_t parts[4];
+    bool near = false;
+    auto pack = [&](bool exact) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        parts[i] = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xv = h2f(half_of(x[i], e));
+          uint32_t c;
+          if constexpr (ONE_CHECK) {
+            const float y = quot(xv, mn[e], sc[e], rs[e], exact);
+            if (!exact) near = near || near_tie(y);
+            c = code_of(y, sc[e], kMaxq);
+          } else {
+            c = quant_code_rcp(xv, mn[e], sc[e], rs[e], kMaxq);
+          }
+          parts[i] |= c << (BITS * ((8 * q + e) % kFpi));
+        }
+      }
+    };
+    pack(false);
+    if (ONE_CHECK && __any(near)) pack(true);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = (lane >> 1) + 32 * i;
-      uint32_t part = 0u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        part |= quant_code_rcp(h2f(half_of(x[i], e)), mn[e], sc[e], rs[e], kMaxq)
-                << (BITS * ((8 * q + e) % kFpi));
+      const uint32_t part = parts[i];
       if constexpr (BITS == 2) {
         // the two lanes of a token hold the two halves of one word
         const uint32_t word = part | (uint32_t)__shfl_xor((int)part, 1);
@@ -160,22 +199,38 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
     // (t0 + j) / kFpi of its channel; the 4 lanes with the same q hold the
     // item's 16 tokens of a channel
     constexpr int kRows = 16 / kFpi;   // word rows of the item (1 or 2)
+    uint32_t part[8][kRows];           // this lane's codes of channel 8q + e
+    bool near = false;
+    auto pack = [&](bool exact) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+#pragma unroll
+        for (int w = 0; w < kRows; ++w) part[e][w] = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = r + 4 * i;
+          const float xv = h2f(half_of(x[i], e));
+          uint32_t c;
+          if constexpr (ONE_CHECK) {
+            const float y = quot(xv, mn[i], sc[i], rs[i], exact);
+            if (!exact) near = near || near_tie(y);
+            c = code_of(y, sc[i], kMaxq);
+          } else {
+            c = quant_code_rcp(xv, mn[i], sc[i], rs[i], kMaxq);
+          }
+          // i is a compile-time index: j / kFpi == (4 i) / kFpi for r < 4
+          part[e][(4 * i) / kFpi] |= c << (BITS * (j % kFpi));
+        }
+      }
+    };
+    pack(false);
+    if (ONE_CHECK && __any(near)) pack(true);
     uint32_t wd[kRows][8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint32_t part[kRows];
-#pragma unroll
-      for (int w = 0; w < kRows; ++w) part[w] = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = r + 4 * i;
-        const uint32_t c = quant_code_rcp(h2f(half_of(x[i], e)), mn[i], sc[i], rs[i], kMaxq);
-        // i is a compile-time index: j / kFpi == (4 i) / kFpi for r < 4
-        part[(4 * i) / kFpi] |= c << (BITS * (j % kFpi));
-      }
 #pragma unroll
       for (int w = 0; w < kRows; ++w) {
-        uint32_t p = part[w] | (uint32_t)__shfl_xor((int)part[w], 16);
+        uint32_t p = part[e][w] | (uint32_t)__shfl_xor((int)part[e][w], 16);
         wd[w][e] = p | (uint32_t)__shfl_xor((int)p, 32);
       }
     }
@@ -195,7 +250,7 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
 // n_slots, ... (n_slots >= 16 / MAXI).  Every item's inputs are requested
 // before any is computed, so the wave waits for memory once.  Unrolled with
 // guards: a loop here kept registers live into the decode loop and spilled.
-template <int BITS, int MAXI>
+template <int BITS, int MAXI, bool ONE_CHECK = false>
 __device__ __forceinline__ void run_items(const DecodeArgs& a, int64_t head, int slot,
                                           int n_slots, int lane) {
   u32x4 x[MAXI][4];
@@ -204,7 +259,8 @@ __device__ __forceinline__ void run_items(const DecodeArgs& a, int64_t head, int
     if (slot + k * n_slots < kItems) item_load(a, head, slot + k * n_slots, lane, x[k]);
 #pragma unroll
   for (int k = 0; k < MAXI; ++k)
-    if (slot + k * n_slots < kItems) item_store<BITS>(a, head, slot + k * n_slots, lane, x[k]);
+    if (slot + k * n_slots < kItems)
+      item_store<BITS, ONE_CHECK>(a, head, slot + k * n_slots, lane, x[k]);
 }
 
 }  // namespace app

@@ -36,6 +36,7 @@
 
 #include "kvq_internal.h"
 #include "merge_common.h"
+#include "append_common.h"
 
 namespace kvq {
 namespace {
@@ -744,7 +745,15 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
     store_record(a, (b * a.H_q) + hk * GQA + h, chunk, d, mm, den, num);
   }
   if (a.counters) merge_in_launch<GQA>(a, b, hk, head32, sh.last);
-
+  // With DecodeArgs::append the blocks of a head then quantize the group
+  // that has filled the residual window: its 16 items (append_common.h), item
+  // slot chunk * 4 + wave and every n_chunks * 4-th after it, with no
+  // barrier.  At the end of the block they no longer delay its first loads,
+  // and the head's blocks share one XCD, so the items' stores into the same
+  // cache lines meet in one L2.
+  if (a.append)
+    app::run_items<BITS, 4, true>(a, head, chunk * (kThreadsM / 64) + wave,
+                            a.n_chunks * (kThreadsM / 64), lane);
 }
 
 }  // namespace

@@ -315,9 +315,11 @@ kvq_status launch_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, i
   const int64_t G = cfg->group;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!append) return decode_and_merge(cfg, a, workspace, s);
-  if (kvq::split_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_chunks)) {
-    // the split-K launch also quantizes the appended group; the merge runs in
-    // the same launch (at most 8 parts) or in one launch after it
+  if (kvq::split_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_chunks) ||
+      kvq::tail_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost)) {
+    // the split-K launch also quantizes the appended group (2-bit: in its
+    // consumer waves; 4-bit: in blocks after its decode grid); the merge runs
+    // in the same launch (at most 8 parts) or in one launch after it
     a.append = 1;
     if (kvq::fused_merge_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_parts)) {
       a.counters = static_cast<int32_t*>(workspace);

@@ -150,8 +150,9 @@ __device__ __forceinline__ void status_add(int32_t* status, int which) {
 // that several parts of a head write (the appended group), then meet in one
 // L2 rather than being merged in memory.  The renumbering is a bijection
 // when the block count is a multiple of 8; otherwise the plain one is used.
-__device__ __forceinline__ void xcd_part_head(int& part, int& head) {
-  const int parts = (int)gridDim.x, nblk = (int)(gridDim.x * gridDim.y);
+// nblk: the blocks so numbered (the first nblk of the grid in linear order).
+__device__ __forceinline__ void xcd_part_head(int& part, int& head, int nblk) {
+  const int parts = (int)gridDim.x;
   if ((nblk & 7) == 0) {
     const int lin = (int)(blockIdx.x + blockIdx.y * gridDim.x);
     const int g = (lin & 7) * (nblk >> 3) + (lin >> 3);
@@ -161,6 +162,9 @@ __device__ __forceinline__ void xcd_part_head(int& part, int& head) {
     part = (int)blockIdx.x;
     head = (int)blockIdx.y;
   }
+}
+__device__ __forceinline__ void xcd_part_head(int& part, int& head) {
+  xcd_part_head(part, head, (int)(gridDim.x * gridDim.y));
 }
 
 // Parts the in-launch merge accepts (more take the merge kernel).
@@ -199,6 +203,11 @@ inline bool pw_decode_supported(int n_boost, int gqa, bool in_launch_merge, int 
   return n_boost == 0 && gqa == 4 && !in_launch_merge && n_chunks % kPwChunks == 0 &&
          n_chunks >= 4 * kPwChunks &&   // at least 4 blocks per head: the append's 16 items
          (int64_t)(n_chunks / kPwChunks) * heads >= 256;
+}
+// The 4-bit matrix-core kernel runs the append of a full residual group at
+// the end of its blocks (after the in-launch merge).
+inline bool tail_append_supported(int bits, int group, int gqa, int n_boost) {
+  return bits == 4 && mfma_decode_supported(bits, group, gqa, n_boost);
 }
 // Resident blocks per CU of the matrix-core kernels: two waves per SIMD,
 // as one block of 8 waves (2-bit, fp8 x fp4 kernel) or two of 4 (4-bit).

@@ -24,6 +24,7 @@
 #include "kvq_internal.h"
 #include "quant_common.h"
 #include "merge_common.h"
+#include "append_common.h"
 
 #pragma clang fp contract(off)
 
@@ -399,6 +400,26 @@ __global__ __launch_bounds__(kThreads) void merge_append_kernel(DecodeArgs d, Qu
   }
 }
 
+// The merge of a decode step and the append of its full residual group as
+// the split-K kernel's append items (append_common.h: 8 key items of 16
+// channels and 8 value items of 16 tokens, each self-contained in one wave,
+// with no LDS and no barrier): blocks [0, n_merge) merge 8 (batch, query
+// head) rows each, one channel per thread; each block after them runs the 16
+// items of one head, one per wave, so the stores of a head's group (each
+// item writes part of the same cache lines) meet in one CU and one L2.
+// Plain 2- or 4-bit codes of equal widths, G = 128.
+template <int BITS, int NPM>
+__global__ __launch_bounds__(1024) void merge_items_kernel(DecodeArgs d, int n_merge) {
+  const int blk = blockIdx.x;
+  if (blk < n_merge) {
+    const int64_t bh = 8 * (int64_t)blk + (threadIdx.x >> 7);
+    if (bh < (int64_t)d.B * d.H_q) merge_row<NPM>(d.ws, d.n_parts, d.out, bh, threadIdx.x & 127);
+    return;
+  }
+  app::run_items<BITS, 1, true>(d, (int64_t)(blk - n_merge), (int)(threadIdx.x >> 6), app::kItems,
+                          (int)(threadIdx.x & 63));
+}
+
 // Dequantize: one thread per (token, channel) of keys and values.
 template <int BITS, int VB, int G>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
@@ -498,6 +519,14 @@ hipError_t merge_append_bits(int group, const DecodeArgs& d, const QuantArgs& a,
   return hipGetLastError();
 }
 
+template <int BITS, int NPM>
+hipError_t merge_items_bits(const DecodeArgs& d, hipStream_t s) {
+  const int n_merge = (int)(((int64_t)d.B * d.H_q + 7) / 8);
+  const dim3 grid((unsigned)(n_merge + (int64_t)d.B * d.H_kv));
+  merge_items_kernel<BITS, NPM><<<grid, 1024, 0, s>>>(d, n_merge);
+  return hipGetLastError();
+}
+
 template <int BITS, int VB, bool KITTY>
 hipError_t merge_append_parts(int group, const DecodeArgs& d, const QuantArgs& a, hipStream_t s) {
   if (d.n_parts <= 8) return merge_append_bits<BITS, VB, KITTY, 8>(group, d, a, s);
@@ -512,6 +541,13 @@ hipError_t launch_merge_append(int bits, int v_bits, int group, const DecodeArgs
   if (d.n_parts > kMergeAppendParts || a.n_groups != 1) {
     const hipError_t e = launch_merge(d, s);
     return e != hipSuccess ? e : launch_quantize(bits, v_bits, group, a, s);
+  }
+  if (bits == v_bits && (bits == 2 || bits == 4) && group == 128 && a.n_boost == 0 &&
+      d.n_parts <= 16 && d.res_cap >= 128) {
+    // the merge and the append's items (one item per wave, no barriers)
+    if (bits == 2)
+      return d.n_parts <= 8 ? merge_items_bits<2, 8>(d, s) : merge_items_bits<2, 16>(d, s);
+    return d.n_parts <= 8 ? merge_items_bits<4, 8>(d, s) : merge_items_bits<4, 16>(d, s);
   }
   if (bits == 2 && v_bits == 4) return merge_append_parts<2, 4, false>(group, d, a, s);
   if (bits == 4 && v_bits == 2) return merge_append_parts<4, 2, false>(group, d, a, s);

@@ -337,15 +337,16 @@ def test_quantize_rounding_ties_bit_exact(built):
         assert_cache_equal(gc, oc, tokens=w.T)
 
 
-@pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "long_splitk", "llama_4bit", "kitty",
-                                  "llama_8bit", "k2v4", "k4v2", "kitty_mag"])
+@pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "long_splitk", "llama_4bit",
+                                  "gqa8_4bit", "kitty", "llama_8bit", "k2v4", "k4v2", "kitty_mag"])
 def test_decode_step_with_append(built, name):
     """kvq_decode_step(append): the attention equals the oracle over the
     quantized tokens + the full fp16 residual group, and the residual group
     lands in cache group T/G bit-exact.  Plain 2-bit codes at GQA 4/8 with 4
-    or more chunks quantize in the split-K launch (4..8 chunks: the whole
-    step is one launch; more: a merge launch follows); others quantize in the
-    merge's launch, or in launches of their own."""
+    or more chunks quantize in the split-K launch's consumer waves, 4-bit
+    codes at GQA 4/8 in blocks after its decode grid (up to 8 chunks: the
+    whole step is one launch; more: a merge launch follows); others quantize
+    in the merge's launch, or in launches of their own."""
     import bit_kv_cache_amd as kvq
     w = _w(name)
     w = synth.shrink(w, R=w.G)
