@@ -34,6 +34,14 @@ __device__ __forceinline__ uint32_t half_key(const u32x4& v, int e) {
   return order_key(half_of(v, e));
 }
 
+// A lane of the same row of 16 lanes (DPP): row rotations by 8 and 4, and
+// the quad swaps of lanes 2 and 1 apart.
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_lane(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kRor8 = 0x128, kRor4 = 0x124, kXor2 = 0x4E, kXor1 = 0xB1;
+
 __device__ __forceinline__ void item_load(const DecodeArgs& a, int64_t head, int item, int lane,
                                           u32x4 (&x)[4]) {
   if (item < 8) {
@@ -93,8 +101,18 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
         hi[e] = max(hi[e], half_key(x[i], e));
       }
     }
+    // the 8 lanes of the row with this q (DPP), then the four rows
 #pragma unroll
-    for (int o = 2; o < 64; o <<= 1)
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = min(lo[e], row_lane<kRor8>(lo[e]));
+      hi[e] = max(hi[e], row_lane<kRor8>(hi[e]));
+      lo[e] = min(lo[e], row_lane<kRor4>(lo[e]));
+      hi[e] = max(hi[e], row_lane<kRor4>(hi[e]));
+      lo[e] = min(lo[e], row_lane<kXor2>(lo[e]));
+      hi[e] = max(hi[e], row_lane<kXor2>(hi[e]));
+    }
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         lo[e] = min(lo[e], (uint32_t)__shfl_xor((int)lo[e], o));
@@ -108,7 +126,7 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
       const uint16_t sh = group_scale(h2f(l16), h2f(from_order_key(hi[e])), kMaxq);
       mn[e] = h2f(l16);
       sc[e] = h2f(sh);
-      rs[e] = 1.0f / sc[e];
+      rs[e] = __builtin_amdgcn_rcpf(sc[e]);   // within an ulp: enough (quant_code_rcp)
       if (e & 1) {
         shw[e >> 1] |= (uint32_t)sh << 16;
         mnw[e >> 1] |= (uint32_t)l16 << 16;
@@ -153,7 +171,7 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
       const uint32_t part = parts[i];
       if constexpr (BITS == 2) {
         // the two lanes of a token hold the two halves of one word
-        const uint32_t word = part | (uint32_t)__shfl_xor((int)part, 1);
+        const uint32_t word = part | row_lane<kXor1>(part);
         if (q == 0) a.c.k_codes[(blk * kG + t) * kWpt + item] = word;
       } else {
         a.c.k_codes[(blk * kG + t) * kWpt + 2 * item + q] = part;
@@ -174,13 +192,18 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
         hi[i] = max(hi[i], half_key(x[i], e));
       }
     }
+    // the 16 lanes of the row (DPP)
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = min(lo[i], (uint32_t)__shfl_xor((int)lo[i], o));
-        hi[i] = max(hi[i], (uint32_t)__shfl_xor((int)hi[i], o));
-      }
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = min(lo[i], row_lane<kRor8>(lo[i]));
+      hi[i] = max(hi[i], row_lane<kRor8>(hi[i]));
+      lo[i] = min(lo[i], row_lane<kRor4>(lo[i]));
+      hi[i] = max(hi[i], row_lane<kRor4>(hi[i]));
+      lo[i] = min(lo[i], row_lane<kXor2>(lo[i]));
+      hi[i] = max(hi[i], row_lane<kXor2>(hi[i]));
+      lo[i] = min(lo[i], row_lane<kXor1>(lo[i]));
+      hi[i] = max(hi[i], row_lane<kXor1>(hi[i]));
+    }
     float mn[4], sc[4], rs[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -188,7 +211,7 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
       const uint16_t sh = group_scale(h2f(l16), h2f(from_order_key(hi[i])), kMaxq);
       mn[i] = h2f(l16);
       sc[i] = h2f(sh);
-      rs[i] = 1.0f / sc[i];
+      rs[i] = __builtin_amdgcn_rcpf(sc[i]);
       if (q == 0) {
         const int64_t m_off = blk * kG + t0 + r + 4 * i;
         a.c.v_scale[m_off] = sh;

@@ -6,19 +6,20 @@
 
 namespace kvq {
 
-// Code of x in a group with min mn and stored scale s (rs = 1/s rounded):
-// round-half-even(clamp((x - mn)/s, 0, maxq)) with the IEEE fp32 quotient
-// (KIVI page, Step 1).  The quotient is taken as (x - mn) * rs, falling
-// back to the IEEE division near a rounding tie.  Exact: the range fits
-// (x - mn)/s <= 1.5 maxq (s is the fp16-rounded range/maxq, at least 2^-24
-// when nonzero).  The product is within a relative 2^-23 of the true
-// quotient and the IEEE quotient within half an ulp of it, so the two differ
-// by less than 2^-18 for maxq <= 15 (quotients <= 22.5) and less than 2^-14
-// for maxq = 255 (quotients <= 383); round-half-even of two values that close
-// differs only when a half-integer lies between them, so the fallback window
-// is 2^-16 for 2- and 4-bit codes and 2^-12 for 8-bit ones.  The clamp
-// bounds are integers and cannot change that.  s == 0 (max == min, or a
-// range whose scale underflows fp16) gives code 0.
+// Code of x in a group with min mn and stored scale s (rs within one ulp of
+// 1/s: the IEEE reciprocal, or v_rcp_f32): round-half-even(clamp((x - mn)/s,
+// 0, maxq)) with the IEEE fp32 quotient (KIVI page, Step 1).  The quotient
+// is taken as (x - mn) * rs, falling back to the IEEE division near a
+// rounding tie.  Exact: the range fits (x - mn)/s <= 1.5 maxq (s is the
+// fp16-rounded range/maxq, at least 2^-24 when nonzero).  The product is
+// within a relative 1.5 * 2^-23 of the true quotient (2^-23 from rs, 2^-24
+// from its own rounding) and the IEEE quotient within half an ulp of it, so
+// the two differ by less than 2^-17 for maxq <= 15 (quotients <= 22.5) and
+// less than 2^-13 for maxq = 255 (quotients <= 383); round-half-even of two
+// values that close differs only when a half-integer lies between them, so
+// the fallback window is 2^-16 for 2- and 4-bit codes and 2^-12 for 8-bit
+// ones.  The clamp bounds are integers and cannot change that.  s == 0 (max
+// == min, or a range whose scale underflows fp16) gives code 0.
 __device__ __forceinline__ uint32_t quant_code_rcp(float x, float mn, float s, float rs,
                                                    float maxq) {
 #pragma clang fp contract(off)

@@ -337,6 +337,56 @@ def test_quantize_rounding_ties_bit_exact(built):
         assert_cache_equal(gc, oc, tokens=w.T)
 
 
+def _tie_grid(heads, bits, seed):
+    """[heads][128][128] fp16 rows of multiples of 1/2 in [0, maxq], a third
+    of them nudged one fp16 step up or down, with every 128-row key group
+    (channel) and value group (token) pinned to min 0 and max maxq, so the
+    scale is 1 and the quotients land on and next to half-integers."""
+    maxq = (1 << bits) - 1
+    gen = torch.Generator().manual_seed(seed)
+    n = heads * 128 * 128
+    x = (torch.randint(0, 2 * maxq + 1, (n,), generator=gen).float() * 0.5).half()
+    bits16 = x.view(torch.int16)
+    sel = torch.randint(0, 3, (n,), generator=gen)
+    bits16 = torch.where((sel == 1) & (x > 0), bits16 + 1, bits16)
+    bits16 = torch.where((sel == 2) & (x > 0), bits16 - 1, bits16)
+    x = bits16.view(torch.float16).view(heads, 128, 128).clone()
+    x[:, 0, :] = 0.0
+    x[:, 1, :] = float(maxq)
+    x[:, :, 0] = 0.0
+    x[:, :, 1] = float(maxq)
+    return x
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_append_rounding_ties_bit_exact(built, bits):
+    """The step's append quantizes a residual group of rounding ties (the tie
+    grid above) bit-exact on every path that runs it: 2-bit at 1 chunk (the
+    merge launch's items), 2 and 4 chunks (4: the split-K launch's consumer
+    waves); 4-bit at 1, 2 and 4 chunks (the ends of the split-K blocks)."""
+    import bit_kv_cache_amd as kvq
+    w = synth.shrink(W["llama3_8b_t32k_2bit"], B=1, H_kv=2, H_q=8, T=4 * 128, bits=bits)
+    inp = make_inputs(w)
+    x = _tie_grid(w.heads, bits, 91 + bits)
+    inp["k_res"], inp["v_res"] = x.cuda(), x.flip(1).contiguous().cuda()
+    t_cap = w.T + w.G
+    oc = oracle_quantize(w, inp, t_cap)
+    oracle.quantize_pack(oc, synth.as_bits(inp["k_res"]), synth.as_bits(inp["v_res"]),
+                         w.T // w.G, 1)
+    for n_chunks in (1, 2, 4):
+        gc = gpu_quantize(w, inp, t_cap)
+        _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), w.B, w.H_q, w.H_kv, w.T, n_chunks)
+        ws = kvq.decode_workspace(ws_bytes)
+        out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+        kvq.kvq_decode_step(qcfg(w), gc, w.B, w.H_q, w.H_kv, inp["q"][:w.B].contiguous(), w.T,
+                            kvq.window(inp["k_sink"], inp["v_sink"], w.S),
+                            kvq.window(inp["k_res"], inp["v_res"], w.R), out, ws, True,
+                            n_chunks=n_chunks)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all(), n_chunks
+        assert_cache_equal(gc, oc, tokens=t_cap)
+
+
 @pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "long_splitk", "llama_4bit",
                                   "gqa8_4bit", "kitty", "llama_8bit", "k2v4", "k4v2", "kitty_mag"])
 def test_decode_step_with_append(built, name):
