@@ -27,11 +27,26 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kItems = 16;
 constexpr int kG = 128;
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Order keys (order_key) of the two fp16 values of a word, side by side: an
+// fp16 value h maps to h XOR 0xFFFF when negative and h XOR 0x8000
+// otherwise, which orders -0 < +0 and every finite value as its number.
+__device__ __forceinline__ uint32_t order_keys2(uint32_t w) {
+  return w ^ (((w >> 15) & 0x00010001u) * 0x7FFFu) ^ 0x80008000u;
+}
+// min / max of two words of side-by-side 16-bit keys (packed integer ops)
+__device__ __forceinline__ uint32_t min2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                 __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t max2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                 __builtin_bit_cast(u16x2, b)));
+}
+
 __device__ __forceinline__ uint16_t half_of(const u32x4& v, int e) {
   return (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-}
-__device__ __forceinline__ uint32_t half_key(const u32x4& v, int e) {
-  return order_key(half_of(v, e));
 }
 
 // A lane of the same row of 16 lanes (DPP): row rotations by 8 and 4, and
@@ -70,11 +85,14 @@ __device__ __forceinline__ float quot(float x, float mn, float s, float rs, bool
 #pragma clang fp contract(off)
   return exact ? (x - mn) / s : (x - mn) * rs;
 }
-__device__ __forceinline__ bool near_tie(float y) {
-  return __builtin_fabsf((y - __builtin_floorf(y)) - 0.5f) < 0x1p-16f;
+// With r = rint(y): y lies within the window of a half-integer exactly when
+// |y - r| > 1/2 - 2^-16 (both differences are exact), and clamping r to
+// [0, maxq] gives rint of the clamped y, the bounds being integers.
+__device__ __forceinline__ bool near_tie(float y, float r) {
+  return __builtin_fabsf(y - r) > 0.5f - 0x1p-16f;
 }
-__device__ __forceinline__ uint32_t code_of(float y, float s, float maxq) {
-  return s == 0.0f ? 0u : (uint32_t)__builtin_rintf(fminf(fmaxf(y, 0.0f), maxq));
+__device__ __forceinline__ uint32_t code_of(float r, float s, float maxq) {
+  return s == 0.0f ? 0u : (uint32_t)fminf(fmaxf(r, 0.0f), maxq);
 }
 
 template <int BITS, bool ONE_CHECK>
@@ -88,36 +106,39 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
   if (blk < 0) return;   // a page outside the pool: nothing is written
   if (item < 8) {
     const int c0 = 16 * item, q = lane & 1;
-    // per channel over the 128 tokens: the lane's 4, then the 32 lanes with
-    // the same q
-    uint32_t lo[8], hi[8];
+    // per channel over the 128 tokens, as order keys of channel pairs
+    // (2p, 2p + 1) side by side: the lane's 4 tokens, the 8 lanes of the row
+    // with this q (DPP), then the four rows
+    uint32_t lo2[4], hi2[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo[e] = half_key(x[0], e);
-      hi[e] = lo[e];
+    for (int p = 0; p < 4; ++p) {
+      lo2[p] = hi2[p] = order_keys2(x[0][p]);
 #pragma unroll
       for (int i = 1; i < 4; ++i) {
-        lo[e] = min(lo[e], half_key(x[i], e));
-        hi[e] = max(hi[e], half_key(x[i], e));
+        const uint32_t k = order_keys2(x[i][p]);
+        lo2[p] = min2(lo2[p], k);
+        hi2[p] = max2(hi2[p], k);
       }
-    }
-    // the 8 lanes of the row with this q (DPP), then the four rows
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo[e] = min(lo[e], row_lane<kRor8>(lo[e]));
-      hi[e] = max(hi[e], row_lane<kRor8>(hi[e]));
-      lo[e] = min(lo[e], row_lane<kRor4>(lo[e]));
-      hi[e] = max(hi[e], row_lane<kRor4>(hi[e]));
-      lo[e] = min(lo[e], row_lane<kXor2>(lo[e]));
-      hi[e] = max(hi[e], row_lane<kXor2>(hi[e]));
+      lo2[p] = min2(lo2[p], row_lane<kRor8>(lo2[p]));
+      hi2[p] = max2(hi2[p], row_lane<kRor8>(hi2[p]));
+      lo2[p] = min2(lo2[p], row_lane<kRor4>(lo2[p]));
+      hi2[p] = max2(hi2[p], row_lane<kRor4>(hi2[p]));
+      lo2[p] = min2(lo2[p], row_lane<kXor2>(lo2[p]));
+      hi2[p] = max2(hi2[p], row_lane<kXor2>(hi2[p]));
     }
 #pragma unroll
     for (int o = 16; o < 64; o <<= 1)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        lo[e] = min(lo[e], (uint32_t)__shfl_xor((int)lo[e], o));
-        hi[e] = max(hi[e], (uint32_t)__shfl_xor((int)hi[e], o));
+      for (int p = 0; p < 4; ++p) {
+        lo2[p] = min2(lo2[p], (uint32_t)__shfl_xor((int)lo2[p], o));
+        hi2[p] = max2(hi2[p], (uint32_t)__shfl_xor((int)hi2[p], o));
       }
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = (lo2[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      hi[e] = (hi2[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    }
     float mn[8], sc[8], rs[8];
     uint32_t shw[4], mnw[4];
 #pragma unroll
@@ -154,8 +175,9 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
           uint32_t c;
           if constexpr (ONE_CHECK) {
             const float y = quot(xv, mn[e], sc[e], rs[e], exact);
-            if (!exact) near = near || near_tie(y);
-            c = code_of(y, sc[e], kMaxq);
+            const float rn = __builtin_rintf(y);
+            if (!exact) near = near || near_tie(y, rn);
+            c = code_of(rn, sc[e], kMaxq);
           } else {
             c = quant_code_rcp(xv, mn[e], sc[e], rs[e], kMaxq);
           }
@@ -179,30 +201,39 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
     }
   } else {
     const int t0 = 16 * (item - 8), r = lane >> 4, q = lane & 15;
-    // per token over the 128 channels: the lane's 8, then the 16 lanes with
-    // the same r
+    // per token over the 128 channels, as order keys of token pairs
+    // (2u, 2u + 1) side by side: the lane's 8 channels (two per word, then
+    // the word's halves), then the 16 lanes of the row (DPP)
+    uint32_t lo2[2], hi2[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t ml[2], mh[2];   // token 2u + k: even channels low, odd high
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const u32x4& v = x[2 * u + k];
+        const uint32_t k0 = order_keys2(v[0]), k1 = order_keys2(v[1]);
+        const uint32_t k2 = order_keys2(v[2]), k3 = order_keys2(v[3]);
+        ml[k] = min2(min2(k0, k1), min2(k2, k3));
+        mh[k] = max2(max2(k0, k1), max2(k2, k3));
+      }
+      lo2[u] = min2(__builtin_amdgcn_perm(ml[1], ml[0], 0x05040100u),
+                    __builtin_amdgcn_perm(ml[1], ml[0], 0x07060302u));
+      hi2[u] = max2(__builtin_amdgcn_perm(mh[1], mh[0], 0x05040100u),
+                    __builtin_amdgcn_perm(mh[1], mh[0], 0x07060302u));
+      lo2[u] = min2(lo2[u], row_lane<kRor8>(lo2[u]));
+      hi2[u] = max2(hi2[u], row_lane<kRor8>(hi2[u]));
+      lo2[u] = min2(lo2[u], row_lane<kRor4>(lo2[u]));
+      hi2[u] = max2(hi2[u], row_lane<kRor4>(hi2[u]));
+      lo2[u] = min2(lo2[u], row_lane<kXor2>(lo2[u]));
+      hi2[u] = max2(hi2[u], row_lane<kXor2>(hi2[u]));
+      lo2[u] = min2(lo2[u], row_lane<kXor1>(lo2[u]));
+      hi2[u] = max2(hi2[u], row_lane<kXor1>(hi2[u]));
+    }
     uint32_t lo[4], hi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lo[i] = half_key(x[i], 0);
-      hi[i] = lo[i];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) {
-        lo[i] = min(lo[i], half_key(x[i], e));
-        hi[i] = max(hi[i], half_key(x[i], e));
-      }
-    }
-    // the 16 lanes of the row (DPP)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo[i] = min(lo[i], row_lane<kRor8>(lo[i]));
-      hi[i] = max(hi[i], row_lane<kRor8>(hi[i]));
-      lo[i] = min(lo[i], row_lane<kRor4>(lo[i]));
-      hi[i] = max(hi[i], row_lane<kRor4>(hi[i]));
-      lo[i] = min(lo[i], row_lane<kXor2>(lo[i]));
-      hi[i] = max(hi[i], row_lane<kXor2>(hi[i]));
-      lo[i] = min(lo[i], row_lane<kXor1>(lo[i]));
-      hi[i] = max(hi[i], row_lane<kXor1>(hi[i]));
+      lo[i] = (lo2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      hi[i] = (hi2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
     }
     float mn[4], sc[4], rs[4];
 #pragma unroll
@@ -236,8 +267,9 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
           uint32_t c;
           if constexpr (ONE_CHECK) {
             const float y = quot(xv, mn[i], sc[i], rs[i], exact);
-            if (!exact) near = near || near_tie(y);
-            c = code_of(y, sc[i], kMaxq);
+            const float rn = __builtin_rintf(y);
+            if (!exact) near = near || near_tie(y, rn);
+            c = code_of(rn, sc[i], kMaxq);
           } else {
             c = quant_code_rcp(xv, mn[i], sc[i], rs[i], kMaxq);
           }
