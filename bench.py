@@ -95,9 +95,10 @@ def compute_dtype(w) -> str:
     """The arithmetic the step's kernel computes in (not a precision claim)."""
     kern = split_kernel(w)
     if kern == "decode_f8f4_kernel":
-        return (f"u{w.bits} codes as the fp4 operand; dequantized query / probabilities as "
-                "4 fp8 digits (about 16 bits); fp16 windows on f16 matrix cores; fp32 "
-                "accumulate and softmax")
+        return (f"u{w.bits} codes as the fp4 operand; dequantized query as 4 fp8 digits "
+                "(about 16 bits of each value), probabilities as 16-bit fixed point per "
+                "32-token block in 4 fp8 nibble digits; fp16 windows on f16 matrix cores; "
+                "fp32 accumulate and softmax")
     if kern == "decode_mfma_kernel":
         return (f"u{w.bits} codes as subnormal fp16 operands; query / probabilities as fp16 "
                 "hi+lo (about 22 bits); fp32 accumulate and softmax")
@@ -106,9 +107,11 @@ def compute_dtype(w) -> str:
 
 def split_append(w, n_chunks: int) -> bool:
     """Whether the split-K launch also quantizes the appended group (the
-    library's dispatch rule: the 2-bit matrix-core kernel, plain codes, at
-    least 4 chunks)."""
-    return split_kernel(w) == "decode_f8f4_kernel" and w.n_boost == 0 and n_chunks >= 4
+    library's dispatch rule: the 2-bit matrix-core kernel with plain codes and
+    at least 4 chunks, or the 4-bit matrix-core kernel)."""
+    kern = split_kernel(w)
+    return ((kern == "decode_f8f4_kernel" and w.n_boost == 0 and n_chunks >= 4)
+            or kern == "decode_mfma_kernel")
 
 
 def fused_step(w, n_chunks: int) -> bool:
@@ -144,7 +147,7 @@ def mx_kernel(w) -> str:
     """Kernel name (with template arguments, as the profiler prints it) of the
     MXFP4 decode for this workload."""
     if w.gqa in (4, 8) and w.T % 128 == 0:
-        return f"decode_f8f4_kernel<{w.gqa}, false, true>"
+        return f"decode_f8f4_kernel<{w.gqa}, false, true, false>"
     return "decode_mx_kernel"
 
 
