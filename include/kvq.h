@@ -231,12 +231,13 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
  * up (KIVI page, Step 3; Kitty page, section 4.3, stage 3), whose tokens this
  * step still attends to in fp16.  The cache contents equal those of
  * kvq_quantize_pack(cfg, cache, B, H_kv, res->k, res->v, res->cap * D,
- * n_quant_tokens / G, 1), bit for bit.  Plain 2-bit codes with G = 128,
- * GQA 4 or 8 and at least 4 chunks quantize the group in the split-K launch
- * (the first four blocks of a head take a quarter of it each): with at most
- * 8 chunks the whole step is that one launch (the last block to finish
- * merges), with more a merge launch follows.  Otherwise the quantization
- * shares the merge's launch (separate launches past 32 parts).
+ * n_quant_tokens / G, 1), bit for bit.  With G = 128 and GQA 4 or 8, plain
+ * 2-bit codes with at least 4 chunks and 4-bit codes quantize the group in
+ * the split-K launch (16 items per head, taken by the head's blocks: 2-bit
+ * before their group loops, 4-bit after their merge): with at most 8 chunks
+ * the whole step is that one launch (the last block to finish merges), with
+ * more a merge launch follows.  Otherwise the quantization shares the
+ * merge's launch (separate launches past 32 parts).
  *  append != 0 requires res->n >= G and n_quant_tokens + G <= t_cap
  *  (else KVQ_ERR_ARG, nothing launched). */
 kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,
