@@ -264,7 +264,7 @@ template <bool KITTY, bool MX>
 constexpr int dma_per_group() { return MX ? 17 : KITTY ? 10 : 9; }
 template <int GQA, bool KITTY, bool MX, bool PW = false>
 constexpr int ring_slots() {
-  return PW ? 11 : MX ? (GQA == 4 ? 6 : 5) : GQA == 4 ? (KITTY ? 10 : 12) : 6;
+  return PW ? 8 : MX ? (GQA == 4 ? 6 : 5) : GQA == 4 ? (KITTY ? 10 : 12) : 6;
 }
 // groups the loader keeps in flight: fewer than ring_slots, and (DF - 1)
 // groups of copies (plus each group's flag copy) within the vector-memory
@@ -596,7 +596,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
     // ---------------------------------------------------------- loader wave
     if (tid < R) {
       sh.ready[tid] = -1;
-      sh.empty[tid] = tid;
+      sh.empty[tid] = PW ? 0 : tid;   // PW: slot w's next group of chunk c0 + w
     }
     if (tid == 0) {
       sh.next_group = 0;
@@ -648,29 +648,10 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
     // of their heads (and on the same memory channels).
     const int rot = ngc > 0 ? (int)((head32 * 37 + chunk * 17) % ngc) : 0;
     bool ok = true;
-    // PW: the chunks are in token order, so the first has the most groups
-    const int n_iter = PW ? kConsumers * chunk_groups(c0) : ngc;
-    for (int j = 0; j < n_iter; ++j) {
-      const int s = j % R;
-      if (!spin_until(&sh.empty[s], j)) {
-        ok = false;
-        break;
-      }
-      asm volatile("" ::: "memory");
+    // Copies group gi of the head (of the block's chunk c0 + w with PW) into
+    // ring slot s, then the sequence table's tag into ready[s].
+    auto issue = [&](int s, int64_t gi, int w, int tag) {
       const uint32_t sl = __builtin_amdgcn_readfirstlane(ring0 + s * SB);
-      int64_t gi;   // the group's index in the head
-      int w = 0;    // PW: its chunk c0 + w
-      if constexpr (PW) {
-        w = j % kConsumers;
-        const int g = j / kConsumers;
-        if (g >= chunk_groups(c0 + w)) {   // past a shorter chunk's end: the slot passes on
-          lds_store(&sh.empty[s], j + R);
-          continue;
-        }
-        gi = (int64_t)(c0 + w) * a.groups_per_chunk + g;
-      } else {
-        gi = gb + (j + rot < ngc ? j + rot : j + rot - ngc);
-      }
       int64_t blk = head * pool + gi;
       if (pt) {
         blk = pt[gi];
@@ -715,8 +696,57 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
         if constexpr (KITTY) dma_1k(sl + kSlotHi, xp + blk * xstep);
       }
       if (lane == 0)
-        dma_flag(__builtin_amdgcn_readfirstlane(ready0 + 4 * s), kSeq.v + (j & (kSeqLen - 1)));
-      if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
+        dma_flag(__builtin_amdgcn_readfirstlane(ready0 + 4 * s), kSeq.v + (tag & (kSeqLen - 1)));
+    };
+    if constexpr (PW) {
+      // One ring slot per consumer: slot w takes the groups of chunk c0 + w
+      // in order, each as soon as consumer w has copied the previous one out
+      // (empty[w] == its index), so a consumer that falls behind holds up
+      // only its own chunk.  The loader polls the slots in turn.
+      int nxt[kConsumers], ng[kConsumers];
+      int left = 0;
+#pragma unroll
+      for (int w = 0; w < kConsumers; ++w) {
+        nxt[w] = 0;
+        ng[w] = chunk_groups(c0 + w);
+        left += ng[w];
+      }
+      int issued = 0;
+      uint32_t idle = 0;
+      while (left > 0) {
+        bool any = false;
+#pragma unroll
+        for (int w = 0; w < kConsumers; ++w) {
+          if (nxt[w] < ng[w] && __builtin_amdgcn_readfirstlane(lds_load(&sh.empty[w])) == nxt[w]) {
+            asm volatile("" ::: "memory");
+            issue(w, (int64_t)(c0 + w) * a.groups_per_chunk + nxt[w], w, nxt[w]);
+            ++nxt[w];
+            --left;
+            any = true;
+            if (++issued >= DF) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 in flight
+          }
+        }
+        if (!any) {
+          if (++idle >= kSpinLimit) {   // a consumer stopped taking its groups
+            ok = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        } else {
+          idle = 0;
+        }
+      }
+    } else {
+      for (int j = 0; j < ngc; ++j) {
+        const int s = j % R;
+        if (!spin_until(&sh.empty[s], j)) {
+          ok = false;
+          break;
+        }
+        asm volatile("" ::: "memory");
+        issue(s, gb + (j + rot < ngc ? j + rot : j + rot - ngc), 0, j);
+        if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
+      }
     }
     vm_wait<0>();
     if constexpr (PW) {
@@ -1148,16 +1178,16 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
     if constexpr (!MX) {
       for (int it = 0;; ++it) {
         int j;
-        if constexpr (PW) {   // the wave's own chunk, in order
+        if constexpr (PW) {   // the wave's own chunk, in order, through its own slot
           if (it >= ngc) break;
-          j = cw + kConsumers * it;
+          j = it;
         } else {
           int jl = 0;
           if (lane == 0) jl = atomicAdd(&sh.next_group, 1);
           j = __builtin_amdgcn_readlane(jl, 0);
           if (j >= ngc) break;
         }
-        const int s = j % R;
+        const int s = PW ? cw : j % R;
         if (!spin_until(&sh.ready[s], j & (kSeqLen - 1))) {
           if (lane == 0) __hip_atomic_fetch_or(&sh.stalled, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           own_stall = true;
@@ -1168,7 +1198,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
         read_slot(s, pf);
         asm volatile("" ::: "memory");
         // this wave's LDS reads complete in order before its next LDS write
-        lds_store(&sh.empty[s], j + R);
+        lds_store(&sh.empty[s], PW ? j + 1 : j + R);
         qk_issue(pf);
         pv_step(pf);
       }
