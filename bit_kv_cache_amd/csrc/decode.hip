@@ -304,12 +304,17 @@ __global__ __launch_bounds__(kD) void merge_small_kernel(DecodeArgs a) {
 
 // Log-sum-exp merge of the parts: one block per (batch, query head).
 // Parts' (m, l) are read in parallel (one per thread), the weights
-// 2^(m_p - M) / L go to LDS, then each thread sums one channel over the parts
-// with its loads batched.
-constexpr int kMergeThreads = 256;
+// 2^(m_p - M) / L go to LDS, then thread (channel d, phase ph) sums channel d
+// over the parts ph, ph + 8, ... with 16 loads in flight at a time, and the
+// 8 phases' sums are added through LDS.  (The partials come from another
+// launch and sit in the caches or in memory: batching the loads, rather
+// than one dependent round trip per few parts, is what sets the time.)
+constexpr int kMergeThreads = 1024;
+constexpr int kMergePhases = kMergeThreads / kD;
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   __shared__ float s_w[kMaxParts];
   __shared__ float s_red[kMergeThreads / 64];
+  static_assert(kMaxParts >= kMergePhases * kD, "the phases' sums reuse s_w");
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int np = a.n_parts;
@@ -344,22 +349,27 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   float Ls = 0.f;
 #pragma unroll
   for (int i = 0; i < kMergeThreads / 64; ++i) Ls += s_red[i];
-  // numerators: thread (channel d, part phase), batched independent loads
-  const int d = tid & (kD - 1), ph = tid >> 7;
+  // numerators: thread (channel d, phase ph), 16 independent loads at a time
+  const int d = tid & (kD - 1), ph = tid / kD;
   float o = 0.f;
   int p = ph;
-  for (; p + 14 < np; p += 16) {
-    float v[8];
+  for (; p + kMergePhases * 15 < np; p += kMergePhases * 16) {
+    float v[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = w[(p + 2 * j) * (kD + 2) + 2 + d];
+    for (int j = 0; j < 16; ++j) v[j] = w[(p + kMergePhases * j) * (kD + 2) + 2 + d];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o = fmaf(v[j], s_w[p + 2 * j], o);
+    for (int j = 0; j < 16; ++j) o = fmaf(v[j], s_w[p + kMergePhases * j], o);
   }
-  for (; p < np; p += 2) o = fmaf(w[p * (kD + 2) + 2 + d], s_w[p], o);
+  for (; p < np; p += kMergePhases) o = fmaf(w[p * (kD + 2) + 2 + d], s_w[p], o);
   __syncthreads();
-  if (ph) s_w[d] = o;   // s_w is free again: park the odd-phase sums
+  s_w[ph * kD + d] = o;   // s_w is free again: the phases' sums
   __syncthreads();
-  if (!ph) a.out[bh * kD + d] = Ls > 0.f ? (o + s_w[d]) / Ls : 0.f;
+  if (ph == 0) {
+    float t = s_w[d];
+#pragma unroll
+    for (int q = 1; q < kMergePhases; ++q) t += s_w[q * kD + d];
+    a.out[bh * kD + d] = Ls > 0.f ? t / Ls : 0.f;
+  }
 }
 
 template <int BITS, int VB, int G>
