@@ -95,6 +95,44 @@ __device__ __forceinline__ uint32_t code_of(float r, float s, float maxq) {
   return s == 0.0f ? 0u : (uint32_t)fminf(fmaxf(r, 0.0f), maxq);
 }
 
+// Minimum and maximum, as order keys, of the 8 channels c0 + 8(l%2) + e of a
+// key item over its 128 tokens (lane layout above): order keys of channel
+// pairs (2p, 2p + 1) side by side, over the lane's 4 tokens, the 8 lanes of
+// its row with the same l%2 (DPP), then the four rows.  Every lane with the
+// same l%2 ends with the same values.
+__device__ __forceinline__ void key_extrema(const u32x4 (&x)[4], uint32_t (&lo)[8],
+                                            uint32_t (&hi)[8]) {
+  uint32_t lo2[4], hi2[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    lo2[p] = hi2[p] = order_keys2(x[0][p]);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      const uint32_t k = order_keys2(x[i][p]);
+      lo2[p] = min2(lo2[p], k);
+      hi2[p] = max2(hi2[p], k);
+    }
+    lo2[p] = min2(lo2[p], row_lane<kRor8>(lo2[p]));
+    hi2[p] = max2(hi2[p], row_lane<kRor8>(hi2[p]));
+    lo2[p] = min2(lo2[p], row_lane<kRor4>(lo2[p]));
+    hi2[p] = max2(hi2[p], row_lane<kRor4>(hi2[p]));
+    lo2[p] = min2(lo2[p], row_lane<kXor2>(lo2[p]));
+    hi2[p] = max2(hi2[p], row_lane<kXor2>(hi2[p]));
+  }
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      lo2[p] = min2(lo2[p], (uint32_t)__shfl_xor((int)lo2[p], o));
+      hi2[p] = max2(hi2[p], (uint32_t)__shfl_xor((int)hi2[p], o));
+    }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lo[e] = (lo2[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    hi[e] = (hi2[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+  }
+}
+
 template <int BITS, bool ONE_CHECK>
 __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, int item, int lane,
                                            const u32x4 (&x)[4]) {
@@ -106,39 +144,8 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
   if (blk < 0) return;   // a page outside the pool: nothing is written
   if (item < 8) {
     const int c0 = 16 * item, q = lane & 1;
-    // per channel over the 128 tokens, as order keys of channel pairs
-    // (2p, 2p + 1) side by side: the lane's 4 tokens, the 8 lanes of the row
-    // with this q (DPP), then the four rows
-    uint32_t lo2[4], hi2[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      lo2[p] = hi2[p] = order_keys2(x[0][p]);
-#pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        const uint32_t k = order_keys2(x[i][p]);
-        lo2[p] = min2(lo2[p], k);
-        hi2[p] = max2(hi2[p], k);
-      }
-      lo2[p] = min2(lo2[p], row_lane<kRor8>(lo2[p]));
-      hi2[p] = max2(hi2[p], row_lane<kRor8>(hi2[p]));
-      lo2[p] = min2(lo2[p], row_lane<kRor4>(lo2[p]));
-      hi2[p] = max2(hi2[p], row_lane<kRor4>(hi2[p]));
-      lo2[p] = min2(lo2[p], row_lane<kXor2>(lo2[p]));
-      hi2[p] = max2(hi2[p], row_lane<kXor2>(hi2[p]));
-    }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        lo2[p] = min2(lo2[p], (uint32_t)__shfl_xor((int)lo2[p], o));
-        hi2[p] = max2(hi2[p], (uint32_t)__shfl_xor((int)hi2[p], o));
-      }
     uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo[e] = (lo2[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      hi[e] = (hi2[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-    }
+    key_extrema(x, lo, hi);
     float mn[8], sc[8], rs[8];
     uint32_t shw[4], mnw[4];
 #pragma unroll
@@ -316,6 +323,147 @@ __device__ __forceinline__ void run_items(const DecodeArgs& a, int64_t head, int
   for (int k = 0; k < MAXI; ++k)
     if (slot + k * n_slots < kItems)
       item_store<BITS, ONE_CHECK>(a, head, slot + k * n_slots, lane, x[k]);
+}
+
+// ------------------------------------------------------------ Kitty key items
+//
+// The Kitty page's key groups with boosted channels (sections 3.2 and 4.1):
+// the n_boost channels of largest range (ties to the lower channel) take
+// 4-bit codes, split into the low two bits in the dense 2-bit word and the
+// high two bits in a compact word per token (boosted row r at bits 2(r%16)
+// of word r/16, rows ascending with the channel), and k_bidx names each
+// channel's row (n_boost: not boosted).  The 8 key items of a group run in
+// the waves of one block and meet in LDS three times: their channels'
+// ranges (kitty_stats), the boosted channels of each item (kitty_rank), and
+// the high-bits words, which collect bits from every item (kitty_codes).
+// Scales, minima and codes follow the quantize kernel's arithmetic.
+struct KittyLds {
+  alignas(16) float rng[kD];         // range (max - min in fp32) of every channel
+  uint32_t bmask[8];                 // item w: bit j set when channel 16w + j is boosted
+  uint32_t hi[kG * (kD / 16)];       // high-bits words [token][n_boost / 16]
+};
+struct KittyKey {
+  uint32_t lo[8];                    // order keys of the minima of the lane's 8 channels
+  float mn[8], rng[8];
+};
+
+// Extrema and ranges of the item's channels (the lane's 8: c0 + 8(l%2) + e);
+// lanes 0 and 1 put the ranges in LDS.
+__device__ __forceinline__ void kitty_stats(const u32x4 (&x)[4], int item, int lane,
+                                            KittyKey& k, KittyLds& s) {
+#pragma clang fp contract(off)
+  uint32_t hi[8];
+  key_extrema(x, k.lo, hi);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    k.mn[e] = h2f(from_order_key(k.lo[e]));
+    k.rng[e] = h2f(from_order_key(hi[e])) - k.mn[e];
+  }
+  if (lane < 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s.rng[16 * item + 8 * lane + e] = k.rng[e];
+  }
+}
+
+// Rank of each of the item's 16 channels among all 128 (channels with a
+// larger range, or an equal one and a lower index): lane l counts channel
+// 16 item + l%16 against channels 32(l/16) .. +31, the four counts add up
+// over the lanes 16 apart; lane 0 puts the item's boosted set in LDS.
+__device__ __forceinline__ void kitty_rank(int item, int lane, int n_boost, KittyLds& s) {
+  const int d = 16 * item + (lane & 15), part = lane >> 4;
+  const float r = s.rng[d];
+  const float4* r4 = reinterpret_cast<const float4*>(s.rng + 32 * part);
+  int cnt = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float4 rc = r4[c];
+    const int ca = 32 * part + 4 * c;
+    cnt += (rc.x > r) || (rc.x == r && ca < d);
+    cnt += (rc.y > r) || (rc.y == r && ca + 1 < d);
+    cnt += (rc.z > r) || (rc.z == r && ca + 2 < d);
+    cnt += (rc.w > r) || (rc.w == r && ca + 3 < d);
+  }
+  cnt += __shfl_xor(cnt, 16);
+  cnt += __shfl_xor(cnt, 32);
+  const uint64_t m = __ballot(cnt < n_boost);
+  if (lane == 0) s.bmask[item] = (uint32_t)(m & 0xFFFFu);
+}
+
+// Scales, minima, indices and codes of the item's channels in cache block
+// blk: the dense words go to memory, the high two bits of boosted codes are
+// ORed into the LDS words (each bit pair has one writer; the block stores
+// the words after its next barrier).  Codes as item_store computes them.
+__device__ __forceinline__ void kitty_codes(const DecodeArgs& a, int64_t blk, int item, int lane,
+                                            const u32x4 (&x)[4], const KittyKey& k,
+                                            KittyLds& s, int n_boost) {
+#pragma clang fp contract(off)
+  constexpr int kWpt = kD / 16;              // dense key words per token
+  const int c0 = 16 * item, q = lane & 1, hpt = n_boost >> 4;
+  const uint32_t m16 = s.bmask[item];
+  int base = 0;                              // boosted channels of the items before
+  for (int w = 0; w < item; ++w) base += __popc(s.bmask[w]);
+  float sc[8], rs[8], mq[8];
+  int row[8];
+  uint32_t shw[4], mnw[4], bw[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = 8 * q + e;
+    const bool boosted = (m16 >> j) & 1u;
+    row[e] = boosted ? base + __popc(m16 & ((1u << j) - 1u)) : n_boost;
+    mq[e] = boosted ? 15.0f : 3.0f;
+    const uint16_t sh = f2h(k.rng[e] / mq[e]);
+    const uint16_t l16 = from_order_key(k.lo[e]);
+    sc[e] = h2f(sh);
+    rs[e] = __builtin_amdgcn_rcpf(sc[e]);   // within an ulp: enough (quant_code_rcp)
+    if (e & 1) {
+      shw[e >> 1] |= (uint32_t)sh << 16;
+      mnw[e >> 1] |= (uint32_t)l16 << 16;
+    } else {
+      shw[e >> 1] = sh;
+      mnw[e >> 1] = l16;
+    }
+    bw[e >> 2] |= (uint32_t)row[e] << (8 * (e & 3));
+  }
+  if (lane < 2) {
+    const int64_t m_off = blk * kD + c0 + 8 * q;
+    *reinterpret_cast<u32x4*>(a.c.k_scale + m_off) = u32x4{shw[0], shw[1], shw[2], shw[3]};
+    *reinterpret_cast<u32x4*>(a.c.k_min + m_off) = u32x4{mnw[0], mnw[1], mnw[2], mnw[3]};
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2*>(a.c.k_bidx + m_off) = u32x2{bw[0], bw[1]};
+  }
+  // nibble e of nib[i]: the code of channel c0 + 8q + e at token l/2 + 32i
+  uint32_t nib[4];
+  bool near = false;
+  auto pack = [&](bool exact) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nib[i] = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = quot(h2f(half_of(x[i], e)), k.mn[e], sc[e], rs[e], exact);
+        const float rn = __builtin_rintf(y);
+        if (!exact) near = near || near_tie(y, rn);
+        nib[i] |= code_of(rn, sc[e], mq[e]) << (4 * e);
+      }
+    }
+  };
+  pack(false);
+  if (__any(near)) pack(true);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = (lane >> 1) + 32 * i;
+    uint32_t part = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part |= ((nib[i] >> (4 * e)) & 3u) << (2 * (8 * q + e));
+    // the two lanes of a token hold the two halves of one word
+    const uint32_t word = part | row_lane<kXor1>(part);
+    if (q == 0) a.c.k_codes[(blk * kG + t) * kWpt + item] = word;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (row[e] < n_boost)
+        atomicOr(&s.hi[t * hpt + (row[e] >> 4)], ((nib[i] >> (4 * e + 2)) & 3u)
+                                                     << (2 * (row[e] & 15)));
+  }
 }
 
 }  // namespace app

@@ -421,6 +421,38 @@ __global__ __launch_bounds__(1024) void merge_items_kernel(DecodeArgs d, int n_m
 }
 
 // Dequantize: one thread per (token, channel) of keys and values.
+// The same for Kitty caches (2-bit codes with boosted key channels, G =
+// 128, boosted channels ranked by range): each block after the merge rows
+// runs one head's group as 16 waves, the 8 key items of the Kitty ranking
+// (append_common.h, three barriers) and the 8 plain 2-bit value items.
+template <int NPM>
+__global__ __launch_bounds__(1024) void merge_kitty_items_kernel(DecodeArgs d, int n_merge) {
+  __shared__ app::KittyLds s;
+  const int blk = blockIdx.x;
+  if (blk < n_merge) {
+    const int64_t bh = 8 * (int64_t)blk + (threadIdx.x >> 7);
+    if (bh < (int64_t)d.B * d.H_q) merge_row<NPM>(d.ws, d.n_parts, d.out, bh, threadIdx.x & 127);
+    return;
+  }
+  const int64_t head = blk - n_merge;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t gb = group_block(d.c, head, d.n_groups, app::kG);
+  if (gb < 0) return;   // a page outside the pool: the whole block writes nothing
+  const int nb = d.n_boost, n_hi = app::kG * (nb >> 4);
+  app::u32x4 x[4];
+  app::item_load(d, head, wave, lane, x);
+  if (tid < n_hi) s.hi[tid] = 0u;
+  app::KittyKey k;
+  if (wave < 8) app::kitty_stats(x, wave, lane, k, s);
+  else app::item_store<2, true>(d, head, wave, lane, x);
+  __syncthreads();
+  if (wave < 8) app::kitty_rank(wave, lane, nb, s);
+  __syncthreads();
+  if (wave < 8) app::kitty_codes(d, gb, wave, lane, x, k, s, nb);
+  __syncthreads();
+  if (tid < n_hi) d.c.k_hi[gb * n_hi + tid] = s.hi[tid];
+}
+
 template <int BITS, int VB, int G>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs a) {
   constexpr int FPI = 32 / BITS, VFPI = 32 / VB;
@@ -527,6 +559,14 @@ hipError_t merge_items_bits(const DecodeArgs& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NPM>
+hipError_t merge_kitty_items(const DecodeArgs& d, hipStream_t s) {
+  const int n_merge = (int)(((int64_t)d.B * d.H_q + 7) / 8);
+  const dim3 grid((unsigned)(n_merge + (int64_t)d.B * d.H_kv));
+  merge_kitty_items_kernel<NPM><<<grid, 1024, 0, s>>>(d, n_merge);
+  return hipGetLastError();
+}
+
 template <int BITS, int VB, bool KITTY>
 hipError_t merge_append_parts(int group, const DecodeArgs& d, const QuantArgs& a, hipStream_t s) {
   if (d.n_parts <= 8) return merge_append_bits<BITS, VB, KITTY, 8>(group, d, a, s);
@@ -549,6 +589,9 @@ hipError_t launch_merge_append(int bits, int v_bits, int group, const DecodeArgs
       return d.n_parts <= 8 ? merge_items_bits<2, 8>(d, s) : merge_items_bits<2, 16>(d, s);
     return d.n_parts <= 8 ? merge_items_bits<4, 8>(d, s) : merge_items_bits<4, 16>(d, s);
   }
+  if (bits == 2 && v_bits == 2 && group == 128 && a.n_boost > 0 && a.n_boost == d.n_boost &&
+      a.boost_score == 0 && d.n_parts <= 16 && d.res_cap >= 128)
+    return d.n_parts <= 8 ? merge_kitty_items<8>(d, s) : merge_kitty_items<16>(d, s);
   if (bits == 2 && v_bits == 4) return merge_append_parts<2, 4, false>(group, d, a, s);
   if (bits == 4 && v_bits == 2) return merge_append_parts<4, 2, false>(group, d, a, s);
   if (bits != v_bits) return hipErrorInvalidValue;

@@ -45,6 +45,12 @@ CASES = {
     "k4v2": (synth.shrink(W["llama3_8b_t8k_b32_4bit"], v_bits=2, B=1, T=10 * 128), {}),
     # Kitty boost ranked by mean magnitude (Kitty page, section 3.2)
     "kitty_mag": (synth.shrink(W["kitty_t128k_h64_boost16"], boost_score=1, B=1, T=8 * 128), {}),
+    # 32 and all 128 key channels boosted at G 128 (two and eight high-bits
+    # words per token)
+    "kitty_boost32_g128": (synth.shrink(W["kitty_t128k_h64_boost16"], n_boost=32, H_q=32, B=1,
+                                        T=5 * 128), {}),
+    "kitty_boost128": (synth.shrink(W["kitty_t128k_h64_boost16"], n_boost=128, H_q=32, B=1,
+                                    T=4 * 128), {}),
 }
 
 
@@ -388,15 +394,17 @@ def test_append_rounding_ties_bit_exact(built, bits):
 
 
 @pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "long_splitk", "llama_4bit",
-                                  "gqa8_4bit", "kitty", "llama_8bit", "k2v4", "k4v2", "kitty_mag"])
+                                  "gqa8_4bit", "kitty", "kitty_gqa4", "kitty_boost32_g128",
+                                  "kitty_boost128", "llama_8bit", "k2v4", "k4v2", "kitty_mag"])
 def test_decode_step_with_append(built, name):
     """kvq_decode_step(append): the attention equals the oracle over the
     quantized tokens + the full fp16 residual group, and the residual group
     lands in cache group T/G bit-exact.  Plain 2-bit codes at GQA 4/8 with 4
     or more chunks quantize in the split-K launch's consumer waves, 4-bit
-    codes at GQA 4/8 in blocks after its decode grid (up to 8 chunks: the
-    whole step is one launch; more: a merge launch follows); others quantize
-    in the merge's launch, or in launches of their own."""
+    codes at GQA 4/8 at the ends of its blocks (up to 8 chunks: the whole
+    step is one launch; more: a merge launch follows); Kitty caches ranked by
+    range at G 128 as items in the merge's launch (up to 16 parts); others
+    quantize in the merge's launch, or in launches of their own."""
     import bit_kv_cache_amd as kvq
     w = _w(name)
     w = synth.shrink(w, R=w.G)
@@ -423,6 +431,43 @@ def test_decode_step_with_append(built, name):
     # the next step reads the appended group like any other
     out = gpu_decode(w, gc, inp, t_cap, n_res=0)
     assert max_err(out, oracle_decode(w, oc, inp, t_cap, n_res=0)) <= TOL
+
+
+def test_kitty_append_rounding_ties_bit_exact(built):
+    """The Kitty append (boosted key channels ranked by range) on a residual
+    group of rounding ties: key channel c is the tie grid at 4 bits times
+    2^(c%3 - 1), so the 16 boosted channels (among those of the largest
+    range, where the grid's nudged maxima and then the channel index break
+    ties) spread over several key items, every boosted and plain channel's
+    quotients land on and next to half-integers, and the values are the
+    2-bit tie grid.  Bit-exact at 1, 2,
+    4 and 16 chunks (the merge launch's items with 8 and 16 parts) and at 40
+    (the quantize kernel's Kitty blocks)."""
+    import bit_kv_cache_amd as kvq
+    w = synth.shrink(W["kitty_t128k_h64_boost16"], B=1, H_kv=2, H_q=16, T=4 * 128, S=0)
+    inp = make_inputs(w)
+    mult = torch.tensor([2.0 ** (c % 3 - 1) for c in range(w.D)], dtype=torch.float32)
+    k = (_tie_grid(w.heads, 4, 93).float() * mult).half()
+    inp["k_res"], inp["v_res"] = k.cuda(), _tie_grid(w.heads, 2, 94).cuda()
+    t_cap = w.T + w.G
+    oc = oracle_quantize(w, inp, t_cap)
+    oracle.quantize_pack(oc, synth.as_bits(inp["k_res"]), synth.as_bits(inp["v_res"]),
+                         w.T // w.G, 1)
+    bidx = oc.k_bidx.reshape(w.heads, t_cap // w.G, w.D)[:, w.T // w.G]
+    for h in range(w.heads):   # the boosted channels of every head span several key items
+        boosted = np.nonzero(bidx[h] < w.n_boost)[0]
+        assert len(boosted) == w.n_boost and len(set(boosted // 16)) >= 3, boosted
+    for n_chunks in (1, 2, 4, 16, 40):
+        gc = gpu_quantize(w, inp, t_cap)
+        _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), w.B, w.H_q, w.H_kv, w.T, n_chunks)
+        ws = kvq.decode_workspace(ws_bytes)
+        out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+        kvq.kvq_decode_step(qcfg(w), gc, w.B, w.H_q, w.H_kv, inp["q"][:w.B].contiguous(), w.T,
+                            None, kvq.window(inp["k_res"], inp["v_res"], w.R), out, ws, True,
+                            n_chunks=n_chunks)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all(), n_chunks
+        assert_cache_equal(gc, oc, tokens=t_cap)
 
 
 def test_decode_step_append_rejects_short_residual(built):
