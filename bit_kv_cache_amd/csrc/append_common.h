@@ -33,7 +33,10 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // fp16 value h maps to h XOR 0xFFFF when negative and h XOR 0x8000
 // otherwise, which orders -0 < +0 and every finite value as its number.
 __device__ __forceinline__ uint32_t order_keys2(uint32_t w) {
-  return w ^ (((w >> 15) & 0x00010001u) * 0x7FFFu) ^ 0x80008000u;
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  // each half's sign bit spread over the half (0xFFFF when negative)
+  const uint32_t m = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, w) >> (short)15);
+  return w ^ (m | 0x80008000u);
 }
 // min / max of two words of side-by-side 16-bit keys (packed integer ops)
 __device__ __forceinline__ uint32_t min2(uint32_t a, uint32_t b) {
@@ -72,27 +75,79 @@ __device__ __forceinline__ void item_load(const DecodeArgs& a, int64_t head, int
   }
 }
 
-// Code of x in a group (mn, s, rs) as quant_code_rcp computes it, in two
-// parts: quot() is the quotient by the reciprocal, or (exact) by the IEEE
-// division, and near() says whether the former lies within quant_code_rcp's
-// tie window.  An item first codes every value by the reciprocal and notes
-// whether any value of the wave lies within the window; only then does it
-// code the item again by the IEEE quotient, so the window costs no branch
-// per value (ONE_CHECK; otherwise quant_code_rcp itself, value by value,
-// which keeps fewer registers live).  Outside the window both quotients give
-// the same code, so the codes are quant_code_rcp's either way.
-__device__ __forceinline__ float quot(float x, float mn, float s, float rs, bool exact) {
+// Code of x in a group (mn, s, rs) as quant_code_rcp computes it.  quot() is
+// the quotient by the reciprocal, or (exact) by the IEEE division; the code
+// is rint of the quotient clamped to maxq.  An item first codes every value
+// by the reciprocal and notes whether any value of the wave lies within
+// quant_code_rcp's tie window (|y - rint(y)| > 1/2 - 2^-16, both differences
+// exact); only then does it code the item again by the IEEE quotient, so the
+// window costs no branch per value (ONE_CHECK; otherwise quant_code_rcp
+// itself, value by value, which keeps fewer registers live).  Outside the
+// window both quotients give the same code, so the codes are
+// quant_code_rcp's either way.  Clamping before rounding gives the same code
+// (the bound is an integer), and a clamped quotient is never in the window
+// unless the unclamped one is.  The groups' reciprocals are 0 for a zero
+// scale (group_stat), so the quotient is 0 there and the code 0, the guard,
+// with no select per value; x >= mn makes every quotient >= 0, so only the
+// upper clamp remains.
+//
+// x is half `hi` of the fp16 word w; x - mn is taken by one v_fma_mix_f32
+// (x converted exactly, times 1, minus mn, rounded once): the value of the
+// fp32 subtraction, without a conversion of its own.
+__device__ __forceinline__ float quot(uint32_t w, bool hi, float mn, float s, float rs,
+                                      bool exact) {
 #pragma clang fp contract(off)
-  return exact ? (x - mn) / s : (x - mn) * rs;
+  float d;
+  if (hi)
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(mn));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(mn));
+  return exact ? (s == 0.0f ? 0.0f : d / s) : d * rs;
 }
-// With r = rint(y): y lies within the window of a half-integer exactly when
-// |y - r| > 1/2 - 2^-16 (both differences are exact), and clamping r to
-// [0, maxq] gives rint of the clamped y, the bounds being integers.
-__device__ __forceinline__ bool near_tie(float y, float r) {
-  return __builtin_fabsf(y - r) > 0.5f - 0x1p-16f;
+
+// Rounding by the magic number 1.5 * 2^23: for 0 <= yc <= 15, yc + 1.5 * 2^23
+// lies in [2^23, 2^24), where the float spacing is 1, so the addition
+// rounds yc to the nearest integer, ties to even (the even last mantissa
+// bit), and the sum's bits are kRoundMagicBits + rint(yc).  Codes packed as
+// sums of such bits, each shifted to its field, carry a constant
+// (magic_sum) that one subtraction per word removes.  dev keeps the
+// largest |yc - rint(yc)| (exact), tested against the window once.
+constexpr float kRoundMagic = 12582912.0f;
+constexpr uint32_t kRoundMagicBits = 0x4B400000u;
+constexpr uint32_t magic_sum(int step, int n) {
+  uint32_t s = 0u;
+  for (int k = 0; k < n; ++k) s += kRoundMagicBits << (step * k);
+  return s;
 }
-__device__ __forceinline__ uint32_t code_of(float r, float s, float maxq) {
-  return s == 0.0f ? 0u : (uint32_t)fminf(fmaxf(r, 0.0f), maxq);
+__device__ __forceinline__ uint32_t round_bits(float yc, float& dev) {
+#pragma clang fp contract(off)
+  const float t = yc + kRoundMagic;
+  dev = fmaxf(dev, __builtin_fabsf(yc - (t - kRoundMagic)));
+  return __builtin_bit_cast(uint32_t, t);
+}
+constexpr float kTieWindow = 0.5f - 0x1p-16f;   // near a tie: dev above this
+
+// Scale and minimum of a group from the order keys of its extrema: pk holds
+// the fp16 minimum (low half) and scale (high half), rs the scale's
+// reciprocal (v_rcp_f32, within an ulp: enough for quant_code_rcp), or 0
+// for a zero scale.
+__device__ __forceinline__ void group_stat(uint32_t lo_key, uint32_t hi_key, float maxq,
+                                           uint32_t& pk, float& rs) {
+  const uint16_t l16 = from_order_key(lo_key);
+  const uint16_t sh = group_scale(h2f(l16), h2f(from_order_key(hi_key)), maxq);
+  const float sc = h2f(sh);
+  rs = sc == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sc);
+  pk = (uint32_t)l16 | ((uint32_t)sh << 16);
+}
+// The statistics (group_stat) that lane `src` computed, fetched by every
+// lane: minimum and scale as floats, the reciprocal, and the packed halves.
+__device__ __forceinline__ void fetch_stat(int src, uint32_t pk, float rs, uint32_t& pk_out,
+                                           float& mn_out, float& sc_out, float& rs_out) {
+  pk_out = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)pk);
+  rs_out = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * src,
+                                                                  __builtin_bit_cast(int, rs)));
+  mn_out = h2f((uint16_t)(pk_out & 0xFFFFu));
+  sc_out = h2f((uint16_t)(pk_out >> 16));
 }
 
 // Minimum and maximum, as order keys, of the 8 channels c0 + 8(l%2) + e of a
@@ -147,50 +202,69 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
     uint32_t lo[8], hi[8];
     key_extrema(x, lo, hi);
     float mn[8], sc[8], rs[8];
-    uint32_t shw[4], mnw[4];
+    uint32_t pk[8];
+    if constexpr (ONE_CHECK) {
+      // Statistics one channel per lane: lane l takes channel c0 + 8q + es,
+      // es = (l/2)%8 (lanes 16 apart repeat it), then every lane fetches its 8
+      // channels' from lanes 2e + q of its row.
+      const int es = (lane >> 1) & 7;
+      uint32_t los = lo[0], his = hi[0];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t l16 = from_order_key(lo[e]);
-      const uint16_t sh = group_scale(h2f(l16), h2f(from_order_key(hi[e])), kMaxq);
-      mn[e] = h2f(l16);
-      sc[e] = h2f(sh);
-      rs[e] = __builtin_amdgcn_rcpf(sc[e]);   // within an ulp: enough (quant_code_rcp)
-      if (e & 1) {
-        shw[e >> 1] |= (uint32_t)sh << 16;
-        mnw[e >> 1] |= (uint32_t)l16 << 16;
-      } else {
-        shw[e >> 1] = sh;
-        mnw[e >> 1] = l16;
+      for (int e = 1; e < 8; ++e) {
+        los = es == e ? lo[e] : los;
+        his = es == e ? hi[e] : his;
+      }
+      uint32_t pk0;
+      float rs0;
+      group_stat(los, his, kMaxq, pk0, rs0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        fetch_stat((lane & 48) + 2 * e + q, pk0, rs0, pk[e], mn[e], sc[e], rs[e]);
+    } else {
+      // every lane its own 8 (no LDS traffic: this form runs beside the
+      // decode's LDS ring)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        group_stat(lo[e], hi[e], kMaxq, pk[e], rs[e]);
+        mn[e] = h2f((uint16_t)(pk[e] & 0xFFFFu));
+        sc[e] = h2f((uint16_t)(pk[e] >> 16));
       }
     }
     if (lane < 2) {
       const int64_t m_off = blk * kD + c0 + 8 * q;
-      *reinterpret_cast<u32x4*>(a.c.k_scale + m_off) = u32x4{shw[0], shw[1], shw[2], shw[3]};
-      *reinterpret_cast<u32x4*>(a.c.k_min + m_off) = u32x4{mnw[0], mnw[1], mnw[2], mnw[3]};
+      u32x4 shw, mnw;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        shw[k] = __builtin_amdgcn_perm(pk[2 * k + 1], pk[2 * k], 0x07060302u);
+        mnw[k] = __builtin_amdgcn_perm(pk[2 * k + 1], pk[2 * k], 0x05040100u);
+      }
+      *reinterpret_cast<u32x4*>(a.c.k_scale + m_off) = shw;
+      *reinterpret_cast<u32x4*>(a.c.k_min + m_off) = mnw;
     }
     // codes of token t: channel c0 + 8q + e at bits BITS (c0 + 8q + e) mod
     // 32 of key word (c0 + 8q + e) / kFpi
     uint32_t parts[4];
     bool near = false;
     auto pack = [&](bool exact) {
+      float dev = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        parts[i] = 0u;
+        uint32_t acc = 0u;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float xv = h2f(half_of(x[i], e));
-          uint32_t c;
           if constexpr (ONE_CHECK) {
-            const float y = quot(xv, mn[e], sc[e], rs[e], exact);
-            const float rn = __builtin_rintf(y);
-            if (!exact) near = near || near_tie(y, rn);
-            c = code_of(rn, sc[e], kMaxq);
+            const float y = quot(x[i][e >> 1], e & 1, mn[e], sc[e], rs[e], exact);
+            acc += round_bits(fminf(y, kMaxq), dev) << (BITS * e);
           } else {
-            c = quant_code_rcp(xv, mn[e], sc[e], rs[e], kMaxq);
+            const float xv = h2f(half_of(x[i], e));
+            acc |= quant_code_rcp(xv, mn[e], sc[e], rs[e], kMaxq) << (BITS * e);
           }
-          parts[i] |= c << (BITS * ((8 * q + e) % kFpi));
         }
+        if constexpr (ONE_CHECK) acc -= magic_sum(BITS, 8);
+        // (8q + e) mod kFpi is e (4-bit) or 8q + e (2-bit)
+        parts[i] = BITS == 2 ? acc << (16 * q) : acc;
       }
+      if (!exact) near = dev > kTieWindow;
     };
     pack(false);
     if (ONE_CHECK && __any(near)) pack(true);
@@ -243,17 +317,43 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
       hi[i] = (hi2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
     }
     float mn[4], sc[4], rs[4];
+    if constexpr (ONE_CHECK) {
+      // Statistics one token per lane: lane l takes token t0 + r + 4 is, is =
+      // l%4 (every 4 lanes of the row repeat them), stores them from the
+      // first four lanes of its row, and every lane fetches its 4 tokens'
+      // from lanes 16r + i.
+      const int is = lane & 3;
+      uint32_t los = lo[0], his = hi[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t l16 = from_order_key(lo[i]);
-      const uint16_t sh = group_scale(h2f(l16), h2f(from_order_key(hi[i])), kMaxq);
-      mn[i] = h2f(l16);
-      sc[i] = h2f(sh);
-      rs[i] = __builtin_amdgcn_rcpf(sc[i]);
-      if (q == 0) {
-        const int64_t m_off = blk * kG + t0 + r + 4 * i;
-        a.c.v_scale[m_off] = sh;
-        a.c.v_min[m_off] = l16;
+      for (int i = 1; i < 4; ++i) {
+        los = is == i ? lo[i] : los;
+        his = is == i ? hi[i] : his;
+      }
+      uint32_t pk0;
+      float rs0;
+      group_stat(los, his, kMaxq, pk0, rs0);
+      if (q < 4) {
+        const int64_t m_off = blk * kG + t0 + r + 4 * is;
+        a.c.v_scale[m_off] = (uint16_t)(pk0 >> 16);
+        a.c.v_min[m_off] = (uint16_t)(pk0 & 0xFFFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t pk;
+        fetch_stat((lane & 48) + i, pk0, rs0, pk, mn[i], sc[i], rs[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t pk;
+        group_stat(lo[i], hi[i], kMaxq, pk, rs[i]);
+        mn[i] = h2f((uint16_t)(pk & 0xFFFFu));
+        sc[i] = h2f((uint16_t)(pk >> 16));
+        if (q == 0) {
+          const int64_t m_off = blk * kG + t0 + r + 4 * i;
+          a.c.v_scale[m_off] = (uint16_t)(pk >> 16);
+          a.c.v_min[m_off] = (uint16_t)(pk & 0xFFFFu);
+        }
       }
     }
     // codes: token t0 + j (j = r + 4i) at bits BITS (j mod kFpi) of word row
@@ -263,27 +363,32 @@ __device__ __forceinline__ void item_store(const DecodeArgs& a, int64_t head, in
     uint32_t part[8][kRows];           // this lane's codes of channel 8q + e
     bool near = false;
     auto pack = [&](bool exact) {
+      float dev = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        uint32_t acc[kRows];
 #pragma unroll
-        for (int w = 0; w < kRows; ++w) part[e][w] = 0u;
+        for (int w = 0; w < kRows; ++w) acc[w] = 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = r + 4 * i;
-          const float xv = h2f(half_of(x[i], e));
-          uint32_t c;
+          // token j = r + 4i (i a compile-time index, r < 4): word row
+          // (4 i) / kFpi, field j mod kFpi = r + (4 i) mod kFpi
+          const int sh = BITS * ((4 * i) % kFpi);
           if constexpr (ONE_CHECK) {
-            const float y = quot(xv, mn[i], sc[i], rs[i], exact);
-            const float rn = __builtin_rintf(y);
-            if (!exact) near = near || near_tie(y, rn);
-            c = code_of(rn, sc[i], kMaxq);
+            const float y = quot(x[i][e >> 1], e & 1, mn[i], sc[i], rs[i], exact);
+            acc[(4 * i) / kFpi] += round_bits(fminf(y, kMaxq), dev) << sh;
           } else {
-            c = quant_code_rcp(xv, mn[i], sc[i], rs[i], kMaxq);
+            const float xv = h2f(half_of(x[i], e));
+            acc[(4 * i) / kFpi] |= quant_code_rcp(xv, mn[i], sc[i], rs[i], kMaxq) << sh;
           }
-          // i is a compile-time index: j / kFpi == (4 i) / kFpi for r < 4
-          part[e][(4 * i) / kFpi] |= c << (BITS * (j % kFpi));
+        }
+#pragma unroll
+        for (int w = 0; w < kRows; ++w) {
+          if constexpr (ONE_CHECK) acc[w] -= magic_sum(4 * BITS, 4 / kRows);
+          part[e][w] = acc[w] << (BITS * r);
         }
       }
+      if (!exact) near = dev > kTieWindow;
     };
     pack(false);
     if (ONE_CHECK && __any(near)) pack(true);
@@ -414,7 +519,7 @@ __device__ __forceinline__ void kitty_codes(const DecodeArgs& a, int64_t blk, in
     const uint16_t sh = f2h(k.rng[e] / mq[e]);
     const uint16_t l16 = from_order_key(k.lo[e]);
     sc[e] = h2f(sh);
-    rs[e] = __builtin_amdgcn_rcpf(sc[e]);   // within an ulp: enough (quant_code_rcp)
+    rs[e] = sc[e] == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sc[e]);   // as group_stat
     if (e & 1) {
       shw[e >> 1] |= (uint32_t)sh << 16;
       mnw[e >> 1] |= (uint32_t)l16 << 16;
@@ -435,17 +540,18 @@ __device__ __forceinline__ void kitty_codes(const DecodeArgs& a, int64_t blk, in
   uint32_t nib[4];
   bool near = false;
   auto pack = [&](bool exact) {
+    float dev = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      nib[i] = 0u;
+      uint32_t acc = 0u;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float y = quot(h2f(half_of(x[i], e)), k.mn[e], sc[e], rs[e], exact);
-        const float rn = __builtin_rintf(y);
-        if (!exact) near = near || near_tie(y, rn);
-        nib[i] |= code_of(rn, sc[e], mq[e]) << (4 * e);
+        const float yc = fminf(quot(x[i][e >> 1], e & 1, k.mn[e], sc[e], rs[e], exact), mq[e]);
+        acc += round_bits(yc, dev) << (4 * e);
       }
+      nib[i] = acc - magic_sum(4, 8);
     }
+    if (!exact) near = dev > kTieWindow;
   };
   pack(false);
   if (__any(near)) pack(true);

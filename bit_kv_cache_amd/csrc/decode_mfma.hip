@@ -750,10 +750,11 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
   // slot chunk * 4 + wave and every n_chunks * 4-th after it, with no
   // barrier.  At the end of the block they no longer delay its first loads,
   // and the head's blocks share one XCD, so the items' stores into the same
-  // cache lines meet in one L2.
+  // cache lines meet in one L2.  (Requesting their inputs before the block
+  // merge instead measured slower.)
   if (a.append)
     app::run_items<BITS, 4, true>(a, head, chunk * (kThreadsM / 64) + wave,
-                            a.n_chunks * (kThreadsM / 64), lane);
+                                  a.n_chunks * (kThreadsM / 64), lane);
 }
 
 }  // namespace
