@@ -241,7 +241,8 @@ struct MergeLdsF {
 };
 
 // Ring of group records filled by the loader wave: slot layout (bytes)
-//   [0, 4096)      key words of the 128 tokens, as in the cache (token-major)
+//   [0, 4096)      key words of the 128 tokens in 16-token tiles of 512 B,
+//                  each the first 16-B halves of its tokens, then the second
 //   [4096, 8192)   value words, 8 rows of 128 channels, as in the cache
 //   [8192, 8448)   key scale of the 128 channels (fp16), then key min,
 //   [8704, 8960)   value scale of the 128 tokens, then value min
@@ -615,7 +616,13 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
     // index blk has its key words at k_codes + 4096 blk bytes, its value words
     // at v_codes + 4096 blk, its scales and mins at + 256 blk in each of the
     // four arrays (Kitty: high-bits words + 512 blk, boosted rows + 128 blk).
-    const char* kp = reinterpret_cast<const char*>(a.c.k_codes) + 16 * lane;
+    // Key words land in the slot half-token-major per 16-token tile: the 16-B
+    // halves h of tokens 16t + n at 512 t + 256 h + 16 n, so a consumer's 32
+    // lanes of one half read 256 contiguous bytes (token-major, their 8-B
+    // reads 32 B apart hit the same banks two or four times).  Lane L of a
+    // 1-KB copy takes tile L / 32, token L % 16, half (L / 16) % 2.
+    const char* kp = reinterpret_cast<const char*>(a.c.k_codes) + 512 * (lane >> 5) +
+                     32 * (lane & 15) + 16 * ((lane >> 4) & 1);
     const char* vp = reinterpret_cast<const char*>(a.c.v_codes) + 16 * lane;
     // metadata lanes: key scale, key min, value scale, value min (256 B each)
     const uint16_t* marr = part == 0 ? a.c.k_scale : part == 1 ? a.c.k_min
@@ -972,7 +979,8 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
       const uint8_t* sp = &sh.ring[s][0];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(sp + 512 * t + 32 * n + 8 * r);
+        const u32x2 v =
+            *reinterpret_cast<const u32x2*>(sp + 512 * t + 256 * (r >> 1) + 16 * n + 8 * (r & 1));
         f.kw[t][0] = v[0];
         f.kw[t][1] = v[1];
       }
