@@ -267,14 +267,19 @@ template <int GQA, bool KITTY, bool MX, bool PW = false>
 constexpr int ring_slots() {
   return PW ? 8 : MX ? (GQA == 4 ? 6 : 5) : GQA == 4 ? (KITTY ? 10 : 12) : 6;
 }
-// groups the loader keeps in flight: fewer than ring_slots, and (DF - 1)
-// groups of copies (plus each group's flag copy) within the vector-memory
-// counter's 63
+// groups the loader keeps in flight: fewer than ring_slots, (DF - 1) groups
+// of copies (plus each group's flag copy) within the vector-memory counter's
+// 63, and for plain codes fewer still, as measured: 4 with one chunk per
+// block (the 32K step 0.75 us faster than with 7) and 3 with one chunk per
+// consumer wave (the 1M-token step 5 us faster than with 7; 2 is 10 us
+// slower).
 template <int GQA, bool KITTY, bool MX, bool PW = false>
 constexpr int in_flight() {
   constexpr int per = dma_per_group<KITTY, MX>() + 1;
   constexpr int rs = ring_slots<GQA, KITTY, MX, PW>();
-  return rs - 1 < 63 / per + 1 ? rs - 1 : 63 / per + 1;
+  constexpr int cap = rs - 1 < 63 / per + 1 ? rs - 1 : 63 / per + 1;
+  constexpr int want = PW ? 3 : (KITTY || MX) ? cap : 4;
+  return want < cap ? want : cap;
 }
 
 template <int GQA, bool KITTY, bool MX, bool PW = false>
