@@ -233,17 +233,23 @@ __device__ __forceinline__ float chunk_elem(const u32x2 (&run)[2], int e) {
 template <int GQA>
 struct WaveLds {
   static constexpr int ROWS = 2 * GQA;             // A rows: (head, hi/lo)
+  // rows padded by one: the A-prep lanes of one write pass differ in c and
+  // kq, which would otherwise put their 16-byte writes 512 bytes apart, on
+  // the same LDS banks
+  static constexpr int RS = ROWS + 1;
   union {
     struct {
-      u32x4 ak[4][4][ROWS];                        // key A operand [c][kq][row]
-      u32x4 av[4][4][ROWS];                        // value A operand [c][kq][row]
+      u32x4 ak[4][4][RS];                          // key A operand [c][kq][row]
+      u32x4 av[4][4][RS];                          // value A operand [c][kq][row]
     } op;
     uint32_t vt[kD][8];                            // fp16 window tile, transposed:
                                                    // [channel][token pair]
   };
-  float p[GQA][kG];                                // probabilities of the group
+  float p[GQA][kG + 4];                            // probabilities of the group (rows
+                                                   // padded: heads 4 banks apart)
   float alpha[GQA];
-  f32x4 qhat[GQA / 4][64][2];                      // scaled query of the A-prep lanes
+  f32x4 qhat[GQA / 4][2][64];                      // scaled query of the A-prep lanes
+                                                   // (lane-minor: 16-byte lane stride)
 };
 
 template <int GQA>
@@ -337,8 +343,8 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
       qmax = fmaxf(qmax, fabsf(qh[e]));
       qmax_n = fmaxf(qmax_n, fabsf(qv));
     }
-    L.qhat[j][lane][0] = f32x4{qh[0], qh[1], qh[2], qh[3]};
-    L.qhat[j][lane][1] = f32x4{qh[4], qh[5], qh[6], qh[7]};
+    L.qhat[j][0][lane] = f32x4{qh[0], qh[1], qh[2], qh[3]};
+    L.qhat[j][1][lane] = f32x4{qh[4], qh[5], qh[6], qh[7]};
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -388,11 +394,11 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
   for (int slot = 0; slot < TPC; ++slot) {
     const bool mine = TPC == 1 || (m_row >> 3) == slot;
     ak_ptr[slot] = mine ? &L.op.ak[0][kq][TPC == 1 ? m_row : (m_row & 7)] : &sh.u.main.zero;
-    ak_step[slot] = mine ? 4 * WaveLds<GQA>::ROWS : 0;
+    ak_step[slot] = mine ? 4 * WaveLds<GQA>::RS : 0;
   }
   const bool av_mine = m_row < 2 * GQA;
   const u32x4* av_ptr = av_mine ? &L.op.av[0][kq][m_row] : &sh.u.main.zero;
-  const int av_step = av_mine ? 4 * WaveLds<GQA>::ROWS : 0;
+  const int av_step = av_mine ? 4 * WaveLds<GQA>::RS : 0;
   __syncthreads();
 
   // One group of this wave.  With PREFETCH the next group's keys are fetched
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(kThreadsM, mfma_blocks_per_cu(BITS, GQA)) void deco
     const float sk = exp2i(max(-126, min(127, -e_k)));
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
-      const f32x4 q0 = L.qhat[j][lane][0], q1 = L.qhat[j][lane][1];
+      const f32x4 q0 = L.qhat[j][0][lane], q1 = L.qhat[j][1][lane];
       const float qh[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
       float v[8];
 #pragma unroll
