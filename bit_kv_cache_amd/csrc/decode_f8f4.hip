@@ -80,6 +80,7 @@ constexpr uint32_t kNib = 0x33333333u;
 constexpr float kNegInfF = -__builtin_inff();
 constexpr int kDigits = 4;        // fp8 digits of an A value
 constexpr float kFixMax = 65535.f; // value-side fixed point: M = round(x 65535 / 2^eb) <= 65535
+constexpr float kLazyMax = 8.f;    // log2 of the largest probability a group may carry
 
 // ------------------------------------------------------------------ helpers
 
@@ -1079,7 +1080,11 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
 #pragma unroll
         for (int t = 1; t < 8; ++t) v = fmaxf(v, logit[H][t]);
         v = row_max16(v);
-        const float m_new = fmaxf(m_run[H], v);
+        // The reference moves only when the group's largest logit passes it
+        // by more than kLazyMax, so most groups keep it and skip the
+        // accumulators' rescale (probabilities then reach 2^kLazyMax, which
+        // the fixed-point value digits and fp32 sums take as they come).
+        const float m_new = v > m_run[H] + kLazyMax ? v : m_run[H];
         alpha[H] = fexp2(m_run[H] - m_new);
         m_run[H] = m_new;
         float sum = 0.f;
