@@ -114,22 +114,41 @@ def split_append(w, n_chunks: int) -> bool:
             or kern == "decode_mfma_kernel")
 
 
+def per_wave_chunks(w, n_chunks: int) -> bool:
+    """Whether the 2-bit kernel runs one chunk per consumer wave (plain codes,
+    GQA 4, a multiple of 8 chunks, at least 32, and at least 256 blocks of 8
+    chunks over all heads): its parts are then blocks of 8 chunks."""
+    return (split_kernel(w) == "decode_f8f4_kernel" and w.n_boost == 0 and w.gqa == 4
+            and n_chunks % 8 == 0 and n_chunks >= 32 and (n_chunks // 8) * w.heads >= 256)
+
+
+def in_launch_merge(w, n_chunks: int) -> bool:
+    """Whether the split-K launch merges its parts in place (matrix-core
+    kernels: at most 8 parts, or 32 blocks of 8 chunks)."""
+    if split_kernel(w) == "decode_valu_kernel":
+        return False
+    if per_wave_chunks(w, n_chunks):
+        return n_chunks // 8 <= 32
+    return n_chunks <= 8
+
+
 def fused_step(w, n_chunks: int) -> bool:
     """Whether the library runs a step with append as one launch (split-K with
-    the append, and the merge in the same launch: at most 8 parts)."""
-    return split_append(w, n_chunks) and n_chunks <= 8
+    the append, and the merge in the same launch)."""
+    return split_append(w, n_chunks) and in_launch_merge(w, n_chunks)
 
 
 def launches_per_step(w, n_chunks: int, append: bool) -> int:
     """Kernel launches of one kvq_decode_step call (the library's dispatch)."""
     mfma = split_kernel(w) != "decode_valu_kernel"
-    n_parts = n_chunks if mfma else n_chunks + 1
-    in_launch_merge = mfma and n_parts <= 8
+    n_parts = (n_chunks // 8 if per_wave_chunks(w, n_chunks) else n_chunks) if mfma \
+        else n_chunks + 1
+    merged = in_launch_merge(w, n_chunks)
     if append:
         if split_append(w, n_chunks):
-            return 1 if in_launch_merge else 2
+            return 1 if merged else 2
         return 2 if n_parts <= 32 else 3
-    return 1 if in_launch_merge else 2
+    return 1 if merged else 2
 
 
 def kernel_source_hash() -> str:

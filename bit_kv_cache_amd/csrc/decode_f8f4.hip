@@ -297,7 +297,6 @@ struct LdsF {
   int next_group;   // next group a consumer claims
   int stalled;      // bit 0: a wait ran past its spin limit; bit 1: a page outside the pool
   int last;         // this block is the last of its head to finish (in-launch merge)
-  int bad_chunks;   // PW: bit w set when a group of the block's chunk w lies outside the pool
 };
 
 struct Operands {
@@ -521,12 +520,13 @@ __device__ __forceinline__ int lane_chan(int blk, int n) {
 // the key side (the query's digits are built once) and no min terms.
 //
 // PW (one chunk per consumer wave, plain 2-bit codes at GQA 4, for steps of
-// many chunks with no in-launch merge): a block takes the 8 chunks c0..c0+7,
-// the loader streams them interleaved (block group j is group j / 8 of chunk
-// c0 + j % 8) and consumer wave w + 1 takes every group of chunk c0 + w in
-// order, with its window slice.  The wave's softmax state is then the
-// chunk's partial, written without a block merge, and a launch of n_chunks
-// chunks needs n_chunks / 8 blocks per head.
+// many chunks): a block takes the 8 chunks c0..c0+7, the loader streams them
+// interleaved (block group j is group j / 8 of chunk c0 + j % 8) and
+// consumer wave w + 1 takes every group of chunk c0 + w in order, with its
+// window slice.  The wave's softmax state is then its chunk's partial; the
+// block merges the 8 in LDS and writes one part, so a launch of n_chunks
+// chunks has n_chunks / 8 blocks and parts per head (merged in the same
+// launch up to kPwFusedMergeParts of them).
 template <int GQA, bool KITTY, bool MX, bool PW>
 __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decode_f8f4_kernel(DecodeArgs a) {
   static_assert(!(KITTY && MX), "the Kitty boost is a min-max cache");
@@ -573,7 +573,6 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
   };
   const int64_t gb = (int64_t)chunk * a.groups_per_chunk;
   const int ngc = chunk_groups(chunk);
-  bool own_stall = false;   // PW: this consumer's wait for a group ran out
   // this block's waves take items of the appended group (2-bit min-max cache)
   const bool app_on = !KITTY && !MX && a.append;
 
@@ -608,7 +607,6 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
     if (tid == 0) {
       sh.next_group = 0;
       sh.stalled = 0;
-      sh.bad_chunks = 0;
     }
     // the flags are written before any copy can land on them
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -667,24 +665,16 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
                     : (KITTY || MX) ? (int)((head32 * 37 + chunk * 17) % ngc)
                                     : (int)((head32 * 7 + chunk * (ngc / 4)) % ngc);
     bool ok = true;
-    // Copies group gi of the head (of the block's chunk c0 + w with PW) into
-    // ring slot s, then the sequence table's tag into ready[s].
-    auto issue = [&](int s, int64_t gi, int w, int tag) {
+    // Copies group gi of the head into ring slot s, then the sequence
+    // table's tag into ready[s].
+    auto issue = [&](int s, int64_t gi, int tag) {
       const uint32_t sl = __builtin_amdgcn_readfirstlane(ring0 + s * SB);
       int64_t blk = head * pool + gi;
       if (pt) {
         blk = pt[gi];
         if (blk < 0 || blk >= pool) {   // a page outside the pool: copy block 0, poison
           blk = 0;
-          if constexpr (PW) {
-            // marked before the group is published, so its consumer sees it
-            if (lane == 0)
-              __hip_atomic_fetch_or(&sh.bad_chunks, 1 << w, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_WORKGROUP);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          } else {
-            bad_page = true;
-          }
+          bad_page = true;
         }
       }
       if constexpr (MX) {
@@ -738,7 +728,7 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
         for (int w = 0; w < kConsumers; ++w) {
           if (nxt[w] < ng[w] && __builtin_amdgcn_readfirstlane(lds_load(&sh.empty[w])) == nxt[w]) {
             asm volatile("" ::: "memory");
-            issue(w, (int64_t)(c0 + w) * a.groups_per_chunk + nxt[w], w, nxt[w]);
+            issue(w, (int64_t)(c0 + w) * a.groups_per_chunk + nxt[w], nxt[w]);
             ++nxt[w];
             --left;
             any = true;
@@ -763,14 +753,12 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
           break;
         }
         asm volatile("" ::: "memory");
-        issue(s, gb + (j + rot < ngc ? j + rot : j + rot - ngc), 0, j);
+        issue(s, gb + (j + rot < ngc ? j + rot : j + rot - ngc), j);
         if (j >= DF - 1) vm_wait<(NDMA + 1) * (DF - 1)>();   // at most DF - 1 groups in flight
       }
     }
     vm_wait<0>();
-    if constexpr (PW) {
-      if (!ok && lane == 0) status_add(a.status, kStatusStalled);
-    } else if ((!ok || bad_page) && lane == 0) {
+    if ((!ok || bad_page) && lane == 0) {
       __hip_atomic_fetch_or(&sh.stalled, (ok ? 0 : 1) | (bad_page ? 2 : 0), __ATOMIC_RELAXED,
                             __HIP_MEMORY_SCOPE_WORKGROUP);
     }
@@ -1214,7 +1202,6 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
         const int s = PW ? cw : j % R;
         if (!spin_until(&sh.ready[s], j & (kSeqLen - 1))) {
           if (lane == 0) __hip_atomic_fetch_or(&sh.stalled, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          own_stall = true;
           break;
         }
         asm volatile("" ::: "memory");
@@ -1362,25 +1349,9 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
     }
   }
 
-  if constexpr (PW) {
-    // ------------------------------------------------------------ chunk partial
-    // the consumer's state is its chunk's partial (poisoned when its wait ran
-    // out or a group of the chunk lies outside the pool); no block merge
-    if (wave == kLoader) return;
-    const bool bad = (lds_load(&sh.bad_chunks) >> (wave - 1)) & 1;
-    if (lane == 0 && own_stall) status_add(a.status, kStatusStalled);
-    if (lane == 0 && bad) status_add(a.status, kStatusBadPage);
-    const bool poison = own_stall || bad;
-    const int64_t bh = (b * a.H_q) + hk * GQA + r;
-    const float lsum = row_sum16(l_part[0]);
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk)
-      store_record(a, bh, chunk, lane_chan<MX>(blk, n), poison ? 0.f : m_run[0],
-                   poison ? 1.f : lsum, poison ? __builtin_nanf("") : wsum[0][blk]);
-    return;
-  }
-
   // ---------------------------------------------------------------- block merge
+  // (PW: the consumers' states are their chunks' partials; the block's part
+  // is their merge, one per block of 8 chunks)
   float lsum[NH];
 #pragma unroll
   for (int H = 0; H < NH; ++H) lsum[H] = row_sum16(l_part[H]);
@@ -1430,16 +1401,17 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
       den = 1.f;
       mm = 0.f;
     }
-    store_record(a, (b * a.H_q) + hk * GQA + h, chunk, d, mm, den, num);
+    store_record(a, (b * a.H_q) + hk * GQA + h, bpart, d, mm, den, num);
   }
-  if (a.counters) merge_in_launch<GQA>(a, b, hk, head32, sh.last);
+  if (a.counters)
+    merge_in_launch<GQA, PW ? kPwFusedMergeParts : kFusedMergeParts>(a, b, hk, head32, sh.last);
 }
 
 }  // namespace
 
 hipError_t launch_decode_f8f4(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.B * a.H_kv));
-  if (pw_decode_supported(a.n_boost, a.gqa, a.counters != nullptr, a.n_chunks, a.B * a.H_kv)) {
+  if (pw_decode_supported(a.n_boost, a.gqa, a.n_chunks, a.B * a.H_kv)) {
     const dim3 gpw((unsigned)(a.n_chunks / kPwChunks), (unsigned)(a.B * a.H_kv));
     decode_f8f4_kernel<4, false, false, true><<<gpw, 64 * block_waves<4, false, true>(), 0, st>>>(a);
   } else if (a.n_boost > 0) {

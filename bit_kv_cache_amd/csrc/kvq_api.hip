@@ -237,9 +237,8 @@ kvq_status prepare_decode(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
   }
   a->qscale = sm_scale * 1.4426950408889634f;
   a->ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kvq::kCounterBytes);
-  a->n_parts = kvq::mfma_decode_supported(same_bits(cfg), cfg->group, a->gqa, cfg->n_boost)
-                    ? nc
-                    : nc + 1;
+  a->n_parts = kvq::decode_parts(same_bits(cfg), cfg->group, a->gqa, cfg->n_boost, nc,
+                                 (int64_t)B * H_kv);
   a->counters = nullptr;
   a->append = 0;
   a->seq_quant = nullptr;
@@ -252,7 +251,8 @@ kvq_status prepare_decode(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B
 // place, else the split-K launch and the merge launch.
 kvq_status decode_and_merge(const kvq_qcfg* cfg, kvq::DecodeArgs& a, void* workspace,
                             hipStream_t s) {
-  if (kvq::fused_merge_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_parts)) {
+  if (kvq::fused_merge_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_chunks,
+                                 (int64_t)a.B * a.H_kv)) {
     a.counters = static_cast<int32_t*>(workspace);
     return hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s));
   }
@@ -321,7 +321,8 @@ kvq_status launch_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, i
     // consumer waves; 4-bit: in blocks after its decode grid); the merge runs
     // in the same launch (at most 8 parts) or in one launch after it
     a.append = 1;
-    if (kvq::fused_merge_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_parts)) {
+    if (kvq::fused_merge_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_chunks,
+                                 (int64_t)a.B * a.H_kv)) {
       a.counters = static_cast<int32_t*>(workspace);
       return hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s));
     }

@@ -167,8 +167,11 @@ __device__ __forceinline__ void xcd_part_head(int& part, int& head) {
   xcd_part_head(part, head, (int)(gridDim.x * gridDim.y));
 }
 
-// Parts the in-launch merge accepts (more take the merge kernel).
+// Parts the in-launch merge accepts (more take the merge kernel); the
+// one-chunk-per-wave geometry (below), whose parts are whole blocks of 8
+// chunks, accepts up to kPwFusedMergeParts.
 constexpr int kFusedMergeParts = 8;
+constexpr int kPwFusedMergeParts = 32;
 
 // The matrix-core decode kernels serve GQA groups of 4 or 8 heads with
 // G = 128: 2-bit codes plain or with the 16-channel Kitty boost, 4-bit codes
@@ -177,10 +180,38 @@ inline bool mfma_decode_supported(int bits, int group, int gqa, int n_boost) {
   return group == 128 && (gqa == 4 || gqa == 8) &&
          ((bits == 2 && (n_boost == 0 || n_boost == 16)) || (bits == 4 && n_boost == 0));
 }
+// The 2-bit kernel's one-chunk-per-wave geometry (kPwChunks consumer waves
+// per block, each with a whole chunk): plain codes at GQA 4, when the chunks
+// fill every CU in one round of blocks.  It removes the per-block start and
+// tail that a step of hundreds of one-chunk blocks per head pays in every
+// round.  The block merges its 8 chunks' states in LDS and writes one part.
+constexpr int kPwChunks = 8;
+inline bool pw_decode_supported(int n_boost, int gqa, int n_chunks, int64_t heads) {
+  return n_boost == 0 && gqa == 4 && n_chunks % kPwChunks == 0 &&
+         n_chunks >= 4 * kPwChunks &&   // at least 4 blocks per head: the append's 16 items
+         (int64_t)(n_chunks / kPwChunks) * heads >= 256;
+}
+inline bool pw_step(int bits, int group, int gqa, int n_boost, int n_chunks, int64_t heads) {
+  return bits == 2 && mfma_decode_supported(bits, group, gqa, n_boost) &&
+         pw_decode_supported(n_boost, gqa, n_chunks, heads);
+}
+// Parts per (batch, query head) of a decode step over n_chunks chunks: one
+// per chunk, one per block of kPwChunks chunks in the one-chunk-per-wave
+// geometry, one more for the fp16 window on the vector-ALU path.
+inline int decode_parts(int bits, int group, int gqa, int n_boost, int n_chunks,
+                        int64_t heads) {
+  if (!mfma_decode_supported(bits, group, gqa, n_boost)) return n_chunks + 1;
+  return pw_step(bits, group, gqa, n_boost, n_chunks, heads) ? n_chunks / kPwChunks : n_chunks;
+}
 // The matrix-core kernels (one part per block) merge their parts in the same
-// launch when a head has at most kFusedMergeParts of them.
-inline bool fused_merge_supported(int bits, int group, int gqa, int n_boost, int n_parts) {
-  return mfma_decode_supported(bits, group, gqa, n_boost) && n_parts <= kFusedMergeParts;
+// launch when a head has at most kFusedMergeParts of them (kPwFusedMergeParts
+// in the one-chunk-per-wave geometry).
+inline bool fused_merge_supported(int bits, int group, int gqa, int n_boost, int n_chunks,
+                                  int64_t heads) {
+  if (!mfma_decode_supported(bits, group, gqa, n_boost)) return false;
+  if (pw_step(bits, group, gqa, n_boost, n_chunks, heads))
+    return n_chunks / kPwChunks <= kPwFusedMergeParts;
+  return n_chunks <= kFusedMergeParts;
 }
 // The 2-bit matrix-core kernel also runs the append of a full residual group
 // (plain codes, at least 4 chunks: one of the group's 16 items per consumer
@@ -191,18 +222,6 @@ inline bool fused_merge_supported(int bits, int group, int gqa, int n_boost, int
 inline bool split_append_supported(int bits, int group, int gqa, int n_boost, int n_chunks) {
   return bits == 2 && mfma_decode_supported(bits, group, gqa, n_boost) && n_boost == 0 &&
          n_chunks >= 4;
-}
-// The 2-bit kernel's one-chunk-per-wave geometry (kPwChunks consumer waves
-// per block, each with a whole chunk): plain codes at GQA 4 with no in-launch
-// merge, when the chunks fill every CU in one round of blocks.  It removes
-// the block merge and the per-block start and tail that a step of hundreds
-// of one-chunk blocks per head pays in every round.
-constexpr int kPwChunks = 8;
-inline bool pw_decode_supported(int n_boost, int gqa, bool in_launch_merge, int n_chunks,
-                                int64_t heads) {
-  return n_boost == 0 && gqa == 4 && !in_launch_merge && n_chunks % kPwChunks == 0 &&
-         n_chunks >= 4 * kPwChunks &&   // at least 4 blocks per head: the append's 16 items
-         (int64_t)(n_chunks / kPwChunks) * heads >= 256;
 }
 // The 4-bit matrix-core kernel runs the append of a full residual group at
 // the end of its blocks (after the in-launch merge).

@@ -27,12 +27,25 @@ __device__ __forceinline__ void merge_row(const float* ws, int np, float* out, i
       return *p;
   };
   float m[NPM], l[NPM], v[NPM];
+  if constexpr (NPM <= 8) {
 #pragma unroll
-  for (int j = 0; j < NPM; ++j) {
-    const float* wp = w + (int64_t)min(j, np - 1) * (kD + 2);
-    m[j] = ld(wp);
-    l[j] = ld(wp + 1);
-    v[j] = ld(wp + 2 + d);
+    for (int j = 0; j < NPM; ++j) {
+      const float* wp = w + (int64_t)min(j, np - 1) * (kD + 2);
+      m[j] = ld(wp);
+      l[j] = ld(wp + 1);
+      v[j] = ld(wp + 2 + d);
+    }
+  } else {
+    // the same loads with a per-lane pointer stepped part by part (many
+    // parts' wave-uniform offsets would otherwise crowd the scalar registers)
+    const float* wp = w;
+#pragma unroll
+    for (int j = 0; j < NPM; ++j) {
+      m[j] = ld(wp);
+      l[j] = ld(wp + 1);
+      v[j] = ld(wp + 2 + d);
+      wp += j + 1 < np ? kD + 2 : 0;
+    }
   }
   float M = -__builtin_inff();
 #pragma unroll
@@ -71,14 +84,14 @@ __device__ __forceinline__ void store_record(const DecodeArgs& a, int64_t bh, in
   }
 }
 
-// In-launch merge (decode kernels with one part per block, at most 8 parts):
+// In-launch merge (decode kernels with one part per block, at most 32 parts):
 // after a block has stored its records with store_record, its arrival on the
 // head's counter, and in the last block of the head to arrive, the
 // log-sum-exp merge of the head's GQA query rows into the output.  No block
 // waits for another, so the order in which blocks run is free.  The last
 // block resets the counter, leaving it zero for the next call.  last_flag is
 // an LDS word of the block.
-template <int GQA>
+template <int GQA, int MAXP = kFusedMergeParts>
 __device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int64_t b, int64_t hk,
                                                 int head32, int& last_flag) {
   // this thread's stores have completed (they are visible device-wide)
@@ -87,7 +100,7 @@ __device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int64_t b, 
   if (threadIdx.x == 0) {
     const int old = __hip_atomic_fetch_add(a.counters + head32, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == a.n_chunks - 1;
+    const int last = old == a.n_parts - 1;   // a head's blocks, one part each
     if (last) __hip_atomic_store(a.counters + head32, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = last;
   }
@@ -97,8 +110,14 @@ __device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int64_t b, 
   for (int i = threadIdx.x; i < GQA * kD; i += blockDim.x) {
     const int64_t bh = b * a.H_q + hk * GQA + i / kD;
     const int d = i % kD;
-    if (np <= 4) merge_row<4, true>(a.ws, np, a.out, bh, d);
-    else merge_row<8, true>(a.ws, np, a.out, bh, d);
+    if constexpr (MAXP <= 8) {
+      if (np <= 4) merge_row<4, true>(a.ws, np, a.out, bh, d);
+      else merge_row<8, true>(a.ws, np, a.out, bh, d);
+    } else {
+      static_assert(MAXP == kPwFusedMergeParts, "up to 32 parts");
+      if (np <= 16) merge_row<16, true>(a.ws, np, a.out, bh, d);
+      else merge_row<32, true>(a.ws, np, a.out, bh, d);
+    }
   }
 }
 

@@ -214,10 +214,11 @@ size_t kvq_decode_workspace_bytes(const kvq_qcfg* cfg, int32_t B, int32_t H_q, i
  *      zero (layout above).
  *  H_q / H_kv must be 1..8.
  *  The matrix-core kernels (2-bit codes plain or with 16 boosted channels,
- *  4-bit codes; G = 128, GQA 4 or 8) with at most 8 parts per head run as
- *  one launch: the last block of each head to finish merges the head's
- *  partial records (device-scope stores and loads, one arrival counter per
- *  head); other configurations launch the merge separately. */
+ *  4-bit codes; G = 128, GQA 4 or 8) with at most 8 parts per head, and the
+ *  one-chunk-per-wave geometry (below) with at most 32, run as one launch:
+ *  the last block of each head to finish merges the head's partial records
+ *  (device-scope stores and loads, one arrival counter per head); other
+ *  configurations launch the merge separately. */
 kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B,
                                 int32_t H_q, int32_t H_kv, const uint16_t* q,
                                 int64_t n_quant_tokens, const kvq_window* sink,
@@ -234,9 +235,9 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
  * n_quant_tokens / G, 1), bit for bit.  With G = 128 and GQA 4 or 8, plain
  * 2-bit codes with at least 4 chunks and 4-bit codes quantize the group in
  * the split-K launch (16 items per head, taken by the head's blocks: 2-bit
- * before their group loops, 4-bit after their merge): with at most 8 chunks
- * the whole step is that one launch (the last block to finish merges), with
- * more a merge launch follows.  Otherwise the quantization shares the
+ * before their group loops, 4-bit after their merge): when the merge runs in
+ * place (as for kvq_decode_attention) the whole step is that one launch,
+ * otherwise a merge launch follows.  Otherwise the quantization shares the
  * merge's launch (separate launches past 32 parts).
  *  append != 0 requires res->n >= G and n_quant_tokens + G <= t_cap
  *  (else KVQ_ERR_ARG, nothing launched). */
@@ -280,8 +281,13 @@ kvq_status kvq_decode_step_noalloc(const kvq_qcfg* cfg, const kvq_cache* cache, 
  * the log-sum-exp merge): with x_t = sm*log2(e)*(q . k_t) over the range's
  * tokens, m = max x_t, l = sum 2^(x_t - m), acc = sum 2^(x_t - m) v_t.  An
  * empty range has l = 0 (m is then meaningless).  *n_parts receives the
- * number of parts per (b, h): the chunk count of kvq_decode_plan, plus one
- * window part when GQA is 1 or 2, or G != 128, or n_boost > 0.
+ * number of parts per (b, h): the chunk count of kvq_decode_plan; an eighth
+ * of it in the one-chunk-per-wave geometry (plain 2-bit codes, G = 128,
+ * GQA 4, a chunk count that is a multiple of 8, at least 32, with at least
+ * 256 blocks of 8 chunks over all heads), whose parts are the merged states
+ * of 8 consecutive chunks; one more (the fp16 windows) on the vector-ALU path
+ * (GQA 1 or 2, G != 128, 8-bit codes, n_boost other than 0 or 16, or keys
+ * and values at different widths).
  *
  * kvq_decode_merge: out[b][h] = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
  * over the parts with l_p > 0 (M the largest such m_p); 0 when every part is

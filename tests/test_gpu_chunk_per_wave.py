@@ -1,16 +1,18 @@
 """GPU parity of the 2-bit kernel's one-chunk-per-wave geometry.
 
-A step of many chunks per head (plain 2-bit codes at GQA 4, 8 or more
+A step of many chunks per head (plain 2-bit codes at GQA 4, 4 or more
 blocks' worth of chunks per head, enough chunks to fill every CU in one
-round, no in-launch merge) runs with blocks of one loader and 8 consumer
-waves, each consumer taking one whole chunk; its softmax state is the
-chunk's partial, with no block merge.  These cases take that path (256
+round) runs with blocks of one loader and 8 consumer waves, each consumer
+taking one whole chunk; the block merges its 8 chunks' softmax states into
+one part, and with at most 32 such parts per head the last block of the
+head merges them in the same launch.  These cases take that path (256
 chunks over 8 kv heads, or 128 over 16) and check it against the oracle:
 every chunk full; chunks of two groups with the last 106 chunks empty (so
 a block holds both full and empty chunks); three groups with one partial
 chunk; ragged sequence lengths, contiguous and paged; a bad page-table entry
-(its chunk's part is poisoned and counted once); and the step with the
-append, whose group must land bit-exact."""
+(its block's part is poisoned and counted once); the step with the append,
+whose group must land bit-exact; and the two phases apart (32 parts, then
+the merge launch)."""
 
 import numpy as np
 import pytest
@@ -66,8 +68,9 @@ def test_chunk_per_wave_decode(built, n_groups, S):
 
 
 def test_chunk_per_wave_step_with_append(built):
-    """kvq_decode_step at 256 chunks: the split-K launch (one chunk per wave)
-    also quantizes the full residual group, a merge launch follows."""
+    """kvq_decode_step at 256 chunks: one launch (one chunk per wave, 32
+    parts of 8 chunks merged in place) that also quantizes the full residual
+    group."""
     import bit_kv_cache_amd as kvq
     w = _shape(300)
     inp = make_inputs(w)
@@ -132,8 +135,8 @@ def test_chunk_per_wave_ragged(built, paged):
 
 @pytest.mark.bad_pages
 def test_chunk_per_wave_bad_page_poisons_its_chunk(built):
-    """A table entry outside the pool poisons the part of the chunk holding
-    it (NaN for that head, counted once) and nothing else."""
+    """A table entry outside the pool poisons the part (block of 8 chunks)
+    holding it (NaN for that head, counted once) and nothing else."""
     import bit_kv_cache_amd as kvq
     w = _shape(256)
     inp = make_inputs(w)
@@ -159,3 +162,28 @@ def test_chunk_per_wave_bad_page_poisons_its_chunk(built):
     ref = oracle_decode(w, oc, inp, w.T).reshape(n, w.gqa, w.D)
     err = float(np.max(np.abs(o[good].cpu().numpy().astype(np.float64) - ref[good])))
     assert err <= TOL, err
+
+
+def test_chunk_per_wave_partials_then_merge(built):
+    """kvq_decode_partials at 256 chunks gives 32 parts per (batch, query
+    head), each the merged state of 8 chunks; kvq_decode_merge over them
+    equals the one-launch call and the oracle."""
+    import bit_kv_cache_amd as kvq
+    w = _shape(300)
+    inp = make_inputs(w)
+    gc = gpu_quantize(w, inp)
+    ref = oracle_decode(w, oracle_quantize(w, inp), inp, w.T)
+    one, ws1 = _decode(w, gc, inp, 256)
+    _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), w.B, w.H_q, w.H_kv, w.T, 256)
+    ws = kvq.decode_workspace(ws_bytes)
+    sink = kvq.window(inp["k_sink"], inp["v_sink"], w.S)
+    res = kvq.window(inp["k_res"], inp["v_res"], w.R)
+    n_parts = kvq.kvq_decode_partials(qcfg(w), gc, w.B, w.H_q, w.H_kv, inp["q"].contiguous(),
+                                      w.T, sink, res, ws, n_chunks=256)
+    assert n_parts == 256 // 8
+    out = torch.empty((w.B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_merge(w.B, w.H_q, n_parts, ws, out)
+    torch.cuda.synchronize()
+    assert kvq.workspace_status(ws) == (0, 0) and kvq.workspace_status(ws1) == (0, 0)
+    assert max_err(out, ref) <= TOL
+    assert float((out - one).abs().max()) <= 1e-4
