@@ -108,10 +108,12 @@ def compute_dtype(w) -> str:
 def split_append(w, n_chunks: int) -> bool:
     """Whether the split-K launch also quantizes the appended group (the
     library's dispatch rule: the 2-bit matrix-core kernel with plain codes and
-    at least 4 chunks, or the 4-bit matrix-core kernel)."""
+    at least 4 chunks, or with the 16-channel Kitty boost when it merges in
+    place, or the 4-bit matrix-core kernel)."""
     kern = split_kernel(w)
-    return ((kern == "decode_f8f4_kernel" and w.n_boost == 0 and n_chunks >= 4)
-            or kern == "decode_mfma_kernel")
+    if kern == "decode_f8f4_kernel":
+        return n_chunks >= 4 if w.n_boost == 0 else in_launch_merge(w, n_chunks)
+    return kern == "decode_mfma_kernel"
 
 
 def per_wave_chunks(w, n_chunks: int) -> bool:

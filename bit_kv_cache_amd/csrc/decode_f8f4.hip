@@ -290,6 +290,7 @@ struct LdsF {
   union {
     WaveLdsF<GQA, MX> w[NW - 1];
     MergeLdsF<GQA, NW> merge;
+    app::KittyLds kitty;      // the Kitty append's key items, after the merge
   } u;
   alignas(16) uint8_t ring[R][slot_bytes<KITTY, MX>()];
   int ready[R];     // chunk-relative group (mod kSeqLen) a slot holds once its data has arrived
@@ -1405,6 +1406,42 @@ __global__ __launch_bounds__((64 * block_waves<GQA, KITTY, PW>()), 1) void decod
   }
   if (a.counters)
     merge_in_launch<GQA, PW ? kPwFusedMergeParts : kFusedMergeParts>(a, b, hk, head32, sh.last);
+
+  // Kitty append (the group that has filled the residual window, Kitty page
+  // 4.3 stage 3): block 0 of the head runs its 8 key items (one per wave,
+  // meeting in LDS for the boosted channels' ranking), the next block (or
+  // block 0 again when the head has one) its 8 value items.  At the end of
+  // the blocks they delay no stream, and the head's blocks share one XCD, so
+  // the items' stores into the same cache lines meet in one L2.
+  if constexpr (KITTY) {
+    if (a.append) {
+      static_assert(block_waves<GQA, KITTY, PW>() == 8, "one Kitty item per wave");
+      if (bpart == 0) {
+        const int64_t gb = group_block(a.c, head, a.n_groups, kG);
+        if (gb >= 0) {   // a page outside the pool: the head's group is not written
+          app::KittyLds& ks = sh.u.kitty;
+          const int n_hi = kG * (a.n_boost >> 4);
+          app::u32x4 x[4];
+          app::item_load(a, head, wave, lane, x);
+          __syncthreads();   // the merge's LDS is free
+          if (tid < n_hi) ks.hi[tid] = 0u;
+          app::KittyKey k;
+          app::kitty_stats(x, wave, lane, k, ks);
+          __syncthreads();
+          app::kitty_rank(wave, lane, a.n_boost, ks);
+          __syncthreads();
+          app::kitty_codes(a, gb, wave, lane, x, k, ks, a.n_boost);
+          __syncthreads();
+          if (tid < n_hi) a.c.k_hi[gb * n_hi + tid] = ks.hi[tid];
+        }
+      }
+      if (bpart == min(1, (int)gridDim.x - 1)) {
+        app::u32x4 x[4];
+        app::item_load(a, head, 8 + wave, lane, x);
+        app::item_store<2, true>(a, head, 8 + wave, lane, x);
+      }
+    }
+  }
 }
 
 }  // namespace

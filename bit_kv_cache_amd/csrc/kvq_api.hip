@@ -315,6 +315,14 @@ kvq_status launch_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, i
   const int64_t G = cfg->group;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!append) return decode_and_merge(cfg, a, workspace, s);
+  if (kvq::kitty_tail_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost,
+                                       cfg->boost_score, a.n_chunks, (int64_t)B * H_kv)) {
+    // one launch: the split-K kernel merges in place, then its blocks
+    // quantize the appended group (Kitty key items, value items)
+    a.append = 1;
+    a.counters = static_cast<int32_t*>(workspace);
+    return hip_status(kvq::launch_decode_partials(cfg->bits, vbits(cfg), cfg->group, a, s));
+  }
   if (kvq::split_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost, a.n_chunks) ||
       kvq::tail_append_supported(same_bits(cfg), cfg->group, a.gqa, cfg->n_boost)) {
     // the split-K launch also quantizes the appended group (2-bit: in its

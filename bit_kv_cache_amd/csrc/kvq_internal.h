@@ -223,6 +223,16 @@ inline bool split_append_supported(int bits, int group, int gqa, int n_boost, in
   return bits == 2 && mfma_decode_supported(bits, group, gqa, n_boost) && n_boost == 0 &&
          n_chunks >= 4;
 }
+// The 2-bit kernel with the 16-channel Kitty boost (boosted channels ranked
+// by range) runs the append of a full residual group at the end of its
+// blocks, after the in-launch merge: the 8 key items in the head's first
+// block, the 8 value items in the next.
+inline bool kitty_tail_append_supported(int bits, int group, int gqa, int n_boost,
+                                        int boost_score, int n_chunks, int64_t heads) {
+  return bits == 2 && n_boost == 16 && boost_score == 0 &&
+         mfma_decode_supported(bits, group, gqa, n_boost) &&
+         fused_merge_supported(bits, group, gqa, n_boost, n_chunks, heads);
+}
 // The 4-bit matrix-core kernel runs the append of a full residual group at
 // the end of its blocks (after the in-launch merge).
 inline bool tail_append_supported(int bits, int group, int gqa, int n_boost) {

@@ -237,8 +237,11 @@ kvq_status kvq_decode_attention(const kvq_qcfg* cfg, const kvq_cache* cache, int
  * the split-K launch (16 items per head, taken by the head's blocks: 2-bit
  * before their group loops, 4-bit after their merge): when the merge runs in
  * place (as for kvq_decode_attention) the whole step is that one launch,
- * otherwise a merge launch follows.  Otherwise the quantization shares the
- * merge's launch (separate launches past 32 parts).
+ * otherwise a merge launch follows.  2-bit codes with 16 boosted channels
+ * ranked by range do the same when the merge runs in place (the head's first
+ * block runs the 8 key items after the merge, the next block the 8 value
+ * items).  Otherwise the quantization shares the merge's launch (separate
+ * launches past 32 parts).
  *  append != 0 requires res->n >= G and n_quant_tokens + G <= t_cap
  *  (else KVQ_ERR_ARG, nothing launched). */
 kvq_status kvq_decode_step(const kvq_qcfg* cfg, const kvq_cache* cache, int32_t B, int32_t H_q,

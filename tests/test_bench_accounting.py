@@ -70,13 +70,14 @@ def test_counter_csv_parse_and_copy_scale(tmp_path):
 def test_launches_per_step_of_workloads():
     # the library's dispatch: one launch where the split-K kernel quantizes
     # the appended group and merges in place (at most 8 parts, or 32 blocks
-    # of 8 chunks in the one-chunk-per-wave geometry); Kitty's append shares
-    # the merge's launch
+    # of 8 chunks in the one-chunk-per-wave geometry); Kitty's append runs at
+    # the end of the blocks of a step that merges in place
     W = synth.WORKLOADS
     assert bench.launches_per_step(W["llama3_8b_t32k_2bit"], 4, True) == 1
     assert bench.launches_per_step(W["llama3_8b_t8k_b32_4bit"], 2, True) == 1
     assert bench.per_wave_chunks(W["long_t1m_2bit_splitk"], 256)
     assert bench.launches_per_step(W["long_t1m_2bit_splitk"], 256, True) == 1
     assert bench.launches_per_step(W["long_t1m_2bit_splitk"], 512, True) == 2
-    assert bench.launches_per_step(W["kitty_t128k_h64_boost16"], 2, True) == 2
+    assert bench.launches_per_step(W["kitty_t128k_h64_boost16"], 2, True) == 1
+    assert bench.launches_per_step(W["kitty_t128k_h64_boost16"], 16, True) == 2
     assert bench.launches_per_step(W["kitty_t128k_h64_boost16"], 2, False) == 1
