@@ -571,11 +571,19 @@ def main(argv=None):
         if st:
             raise kvq.KvqError(st, "kvq_decode_step")
 
-    step_avg = back_to_back(step)
-    attn_avg = back_to_back(attention)
-    part_avg = back_to_back(partials)
-    merge_avg = back_to_back(lambda i: merge())
-    app_avg = back_to_back(quant) if append else 0.0
+    # three interleaved rounds of each, the median of each kept (one pass in a
+    # fixed order let the figure measured right after a long run of another
+    # launch read a few microseconds high)
+    legs = [("step", step), ("attention", attention), ("partials", partials),
+            ("merge", lambda i: merge())] + ([("quant", quant)] if append else [])
+    runs = {name: [] for name, _ in legs}
+    for _ in range(3):
+        for name, fn in legs:
+            runs[name].append(back_to_back(fn))
+    med = {name: sorted(v)[1] for name, v in runs.items()}
+    step_avg, attn_avg, part_avg, merge_avg = (med["step"], med["attention"], med["partials"],
+                                               med["merge"])
+    app_avg = med["quant"] if append else 0.0
 
     alg = decode_bytes(w)
     alg_split = alg - w.B * w.H_q * w.D * 4   # the split-K phase does not write O
@@ -626,8 +634,8 @@ def main(argv=None):
                       "split_kernel_isolated_avg": round(part_iso * 1e3, 3),
                       "merge_kernel_isolated_avg": round(merge_iso * 1e3, 3),
                       "timing": "*_avg: n launches back to back between two HIP events on the "
-                                "launch stream; *_isolated_*: an event pair around every "
-                                "launch"},
+                                "launch stream, the median of three interleaved rounds; "
+                                "*_isolated_*: an event pair around every launch"},
         "append_quant_us": round(app_avg * 1e3, 3) if append else None,
         "step_as_three_launches_us": round(ms_unfused * 1e3, 3),
         "split_phase": {"kernel": f"{split_kernel(w)} (kvq_decode_partials)",
