@@ -515,6 +515,54 @@ hipError_t quantize_bits(int group, const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Quantize + pack of whole groups as the decode step's append items
+// (append_common.h: 8 key items of 16 channels and 8 value items of 16
+// tokens, each in one wave, reading whole 32-byte pieces of the source rows
+// and writing whole packed words).  Plain codes: four 4-wave blocks per
+// (head, group), block j running items 4j..4j+3 (the key items of channels
+// 0..63, of 64..127, the value items of tokens 0..63, of 64..127), so every
+// 128-byte line of a group's rows is read by one block.  With KITTY (2-bit
+// codes, 16 boosted channels ranked by range) one 16-wave block per (head,
+// group), waves 0..7 running the Kitty key items, which meet in LDS three
+// times.  The items' arithmetic is the quantize kernel's (quant_common.h),
+// so the codes are the same bit for bit.  Equal widths, G = 128, a source
+// head stride that is a whole number of rows.
+template <int BITS, bool KITTY>
+__global__ __launch_bounds__(KITTY ? 1024 : 256) void items_quantize_kernel(QuantArgs q) {
+  __shared__ app::KittyLds ks;
+  constexpr int kBlocksPerGroup = KITTY ? 1 : 4;
+  const int64_t hg = blockIdx.x / kBlocksPerGroup;
+  const int64_t head = hg / q.n_groups, gi = hg - head * q.n_groups;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (tid >> 6) + (KITTY ? 0 : 4 * (int)(blockIdx.x % kBlocksPerGroup));
+  DecodeArgs d{};
+  d.c = q.c;
+  d.n_boost = q.n_boost;
+  d.res_cap = (int32_t)(q.src_head_stride / kD);   // rows per source head
+  d.k_res = q.k_src + gi * app::kG * kD;            // the group's first row of head 0
+  d.v_res = q.v_src + gi * app::kG * kD;
+  d.n_groups = q.first_group + gi;                  // the cache group the items write
+  app::u32x4 x[4];
+  app::item_load(d, head, wave, lane, x);
+  if constexpr (KITTY) {
+    const int64_t gb = group_block(d.c, head, d.n_groups, app::kG);
+    if (gb < 0) return;   // a page outside the pool: the whole block writes nothing
+    const int n_hi = app::kG * (q.n_boost >> 4);
+    if (tid < n_hi) ks.hi[tid] = 0u;
+    app::KittyKey k;
+    if (wave < 8) app::kitty_stats(x, wave, lane, k, ks);
+    else app::item_store<2, true>(d, head, wave, lane, x);
+    __syncthreads();
+    if (wave < 8) app::kitty_rank(wave, lane, q.n_boost, ks);
+    __syncthreads();
+    if (wave < 8) app::kitty_codes(d, gb, wave, lane, x, k, ks, q.n_boost);
+    __syncthreads();
+    if (tid < n_hi) d.c.k_hi[gb * n_hi + tid] = ks.hi[tid];
+  } else {
+    app::item_store<BITS, true>(d, head, wave, lane, x);
+  }
+}
+
 template <int BITS, int VB>
 hipError_t dequantize_bits(int group, const DequantArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.n_heads * a.n_groups * group * kD;
@@ -604,6 +652,23 @@ hipError_t launch_merge_append(int bits, int v_bits, int group, const DecodeArgs
 
 hipError_t launch_quantize(int bits, int v_bits, int group, const QuantArgs& a, hipStream_t s) {
   if (a.n_groups == 0 || a.n_heads == 0) return hipSuccess;
+  if (bits == v_bits && group == 128 && a.src_head_stride % kD == 0 &&
+      a.src_head_stride / kD <= INT32_MAX && 4 * (int64_t)a.n_heads * a.n_groups <= INT32_MAX) {
+    const int64_t groups = (int64_t)a.n_heads * a.n_groups;
+    const dim3 grid4((unsigned)(4 * groups)), grid1((unsigned)groups);
+    if (bits == 2 && a.n_boost == 0) {
+      items_quantize_kernel<2, false><<<grid4, 256, 0, s>>>(a);
+      return hipGetLastError();
+    }
+    if (bits == 4 && a.n_boost == 0) {
+      items_quantize_kernel<4, false><<<grid4, 256, 0, s>>>(a);
+      return hipGetLastError();
+    }
+    if (bits == 2 && a.n_boost == 16 && a.boost_score == 0) {
+      items_quantize_kernel<2, true><<<grid1, 1024, 0, s>>>(a);
+      return hipGetLastError();
+    }
+  }
   if (bits == 2 && v_bits == 4) return quantize_bits<2, 4, false>(group, a, s);
   if (bits == 4 && v_bits == 2) return quantize_bits<4, 2, false>(group, a, s);
   if (bits != v_bits) return hipErrorInvalidValue;
