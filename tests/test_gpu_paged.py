@@ -213,3 +213,73 @@ def test_ragged_batch(built, name, paged):
         for b in range(w.B):
             err = max_err(out[b:b + 1], refs[b])
             assert err <= TOL, f"{name} paged={paged} n_chunks={n_chunks} seq {b}: {err:.3g}"
+
+
+
+@pytest.mark.bad_pages
+@pytest.mark.parametrize("name", ["llama_2bit", "gqa8_2bit", "llama_4bit", "kitty", "kitty_gqa4"])
+def test_paged_bad_append_page_writes_nothing(built, name):
+    """A table entry outside the pool for the group being appended: the step
+    (4 chunks: one launch, the append inside it) and the quantize of that
+    group alone write nothing for that head and nothing outside the other
+    heads' pages for the group, the other heads' appended group is
+    bit-exact, and the attention over the cached groups is the oracle's
+    with no part poisoned (the decode never reads the appended group)."""
+    import bit_kv_cache_amd as kvq
+    from parity_util import FIELDS
+    w = _w(name)
+    w = synth.shrink(w, R=w.G)
+    inp = make_inputs(w)
+    n = len(inp["heads"])
+    B = n // w.H_kv
+    ng = w.T // w.G
+    bad = n // 2
+    table, n_pages = _table(n, ng + 1, extra=5, seed=17)
+    t_bad = table.clone()
+    t_bad[bad, ng] = n_pages + 3
+    pool = kvq.Cache.pool(qcfg(w), n_pages, t_bad.cuda())
+    kvq.kvq_quantize_pack(qcfg(w), pool, 1, n, inp["k"], inp["v"], 0, ng)
+    torch.cuda.synchronize()
+    names = [f for f in kvq.Cache.FIELDS if getattr(pool, f) is not None and f != "page_table"]
+    before = {f: getattr(pool, f).clone() for f in names}
+    oc = oracle_quantize(w, inp, w.T + w.G)
+    oracle.quantize_pack(oc, synth.as_bits(inp["k_res"]), synth.as_bits(inp["v_res"]), ng, 1)
+    ref = oracle_decode(w, oracle_quantize(w, inp), inp, w.T)
+    written = {int(t_bad[h, ng]) for h in range(n) if h != bad}
+    good = [h for h in range(n) if h != bad]
+
+    def check():
+        # the good heads' groups (appended one included) through the valid table
+        g = _gather(pool, table, ng + 1)
+        for gname, oname in FIELDS:
+            gv, ov = getattr(g, gname), getattr(oc, oname)
+            if gv is None:
+                continue
+            gh = gv.cpu().numpy().view(ov.dtype)
+            assert np.array_equal(gh[good], ov[good]), gname
+        # every page but the good heads' appended ones is as before
+        for f in names:
+            now, was = getattr(pool, f), before[f]
+            rows = now.shape[1] // n_pages
+            for p in range(n_pages):
+                if p not in written:
+                    assert torch.equal(now[0, p * rows:(p + 1) * rows],
+                                       was[0, p * rows:(p + 1) * rows]), (f, p)
+
+    # one step with the append
+    _, ws_bytes = kvq.kvq_decode_plan(qcfg(w), B, w.H_q, w.H_kv, w.T, 4)
+    ws = kvq.decode_workspace(ws_bytes)
+    out = torch.empty((B, w.H_q, w.D), dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_step(qcfg(w), pool, B, w.H_q, w.H_kv, inp["q"][:B].contiguous(), w.T,
+                        kvq.window(inp["k_sink"], inp["v_sink"], w.S),
+                        kvq.window(inp["k_res"], inp["v_res"], w.R), out, ws, True, n_chunks=4)
+    torch.cuda.synchronize()
+    assert max_err(out, ref) <= TOL
+    assert kvq.workspace_status(ws) == (0, 0)
+    check()
+    # the quantize of the appended group alone, from the restored pool
+    for f in names:
+        getattr(pool, f).copy_(before[f])
+    kvq.kvq_quantize_pack(qcfg(w), pool, 1, n, inp["k_res"], inp["v_res"], ng, 1)
+    torch.cuda.synchronize()
+    check()
